@@ -1,0 +1,220 @@
+"""ctypes binding of libhalo.so (include/halo.h), same names as the C-ABI.
+
+Argument marshalling only: every step of the exchange runs in the HIP library.
+PyTorch supplies device memory (torch.cuda tensors) and streams. If the
+library has not been built, every call raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libhalo.so")
+
+STATUS = {0: "HALO_OK", -1: "HALO_ERR_ARG", -2: "HALO_ERR_GEOMETRY", -3: "HALO_ERR_RANGE",
+          -4: "HALO_ERR_HIP", -5: "HALO_ERR_TIMEOUT", -6: "HALO_ERR_STATE", -7: "HALO_ERR_NOMEM"}
+
+# Every symbol include/halo.h declares, with (restype, argtypes).
+_vp, _i32, _i64, _u32, _f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                               ctypes.c_float)
+_P = ctypes.POINTER
+_st = ctypes.c_int
+SIGNATURES = {
+    "halo_plan_create": (_st, [_vp, _i64, _vp, _vp, _f32, _P(_vp)]),
+    "halo_plan_destroy": (None, [_vp]),
+    "halo_last_error": (ctypes.c_char_p, []),
+    "halo_plan_total_slots": (_i64, [_vp]),
+    "halo_plan_num_domains": (_i32, [_vp]),
+    "halo_plan_num_pulses": (_i32, [_vp]),
+    "halo_plan_num_entries": (_i64, [_vp]),
+    "halo_plan_num_items": (_i32, [_vp]),
+    "halo_plan_pulse_dim": (_st, [_vp, _i32, _P(_i32), _P(_i32)]),
+    "halo_plan_domain": (_st, [_vp, _i32, _P(_i64), _P(_i32), _P(_i32)]),
+    "halo_plan_home_slots": (_st, [_vp, _vp]),
+    "halo_plan_pulse": (_st, [_vp, _i32, _i32, _P(_i32), _P(_i32), _P(_i32), _P(_i32), _P(_i32),
+                              _P(_i32), _P(_i32), _vp, _vp]),
+    "halo_plan_upload": (_st, [_vp]),
+    "halo_exchange_x": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_f": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_x_pulsewise": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_f_pulsewise": (_st, [_vp, _vp, _vp]),
+    "halo_plan_sync": (_st, [_vp, _vp]),
+    "halo_plan_reset": (_st, [_vp]),
+    "halo_plan_set_spin_limit": (_st, [_vp, _u32]),
+    "halo_plan_debug_withhold": (_st, [_vp, _i32]),
+}
+
+_lib = None
+
+
+class HaloError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libhalo.so; raise if it is missing (build it with build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build the HIP library first "
+                           "(python -m domain_decomposition_halo_fusedpackx_amd.build)")
+    # PyTorch ships its own HIP runtime under the same soname as the one the
+    # library links against; loading torch first makes the library bind to it,
+    # so that device pointers and streams from torch are valid for it.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(code: int):
+    if code != 0:
+        raise HaloError(code, load_library().halo_last_error().decode())
+
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class HaloPlan:
+    """An exchange plan (halo_plan_create) and its two exchanges."""
+
+    def __init__(self, positions, box, grid, cutoff):
+        lib = load_library()
+        pos = np.ascontiguousarray(np.asarray(positions, dtype=np.float32).reshape(-1, 3))
+        self._box = np.ascontiguousarray(box, dtype=np.float32)
+        self._grid = np.ascontiguousarray(grid, dtype=np.int32)
+        if self._box.shape != (3,) or self._grid.shape != (3,):
+            raise ValueError("box and grid need three entries")
+        h = ctypes.c_void_p()
+        _check(lib.halo_plan_create(_np_ptr(pos) if pos.size else None, pos.shape[0],
+                                    _np_ptr(self._box), _np_ptr(self._grid),
+                                    ctypes.c_float(cutoff), ctypes.byref(h)))
+        self._h = h
+        self.n_atoms = pos.shape[0]
+        self.total_slots = lib.halo_plan_total_slots(h)
+        self.num_domains = lib.halo_plan_num_domains(h)
+        self.num_pulses = lib.halo_plan_num_pulses(h)
+        self.num_entries = lib.halo_plan_num_entries(h)
+        self.num_items = lib.halo_plan_num_items(h)
+
+    def close(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            load_library().halo_plan_destroy(h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- read-out -------------------------------------------------------------
+    def pulse_dim(self, p: int):
+        d, k = ctypes.c_int32(), ctypes.c_int32()
+        _check(load_library().halo_plan_pulse_dim(self._h, p, ctypes.byref(d), ctypes.byref(k)))
+        return d.value, k.value
+
+    def domains(self):
+        lib = load_library()
+        n = self.num_domains
+        base = np.zeros(n, np.int64)
+        n_home = np.zeros(n, np.int32)
+        n_halo = np.zeros(n, np.int32)
+        for d in range(n):
+            b, h, m = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+            _check(lib.halo_plan_domain(self._h, d, ctypes.byref(b), ctypes.byref(h),
+                                        ctypes.byref(m)))
+            base[d], n_home[d], n_halo[d] = b.value, h.value, m.value
+        return base, n_home, n_halo
+
+    def home_slots(self) -> np.ndarray:
+        out = np.zeros(max(self.n_atoms, 1), np.int64)
+        _check(load_library().halo_plan_home_slots(self._h, _np_ptr(out)))
+        return out[:self.n_atoms]
+
+    def pulse(self, p: int, d: int) -> dict:
+        lib = load_library()
+        v = [ctypes.c_int32() for _ in range(7)]
+        shift = np.zeros(3, np.float32)
+        _check(lib.halo_plan_pulse(self._h, p, d, *[ctypes.byref(x) for x in v], _np_ptr(shift),
+                                   None))
+        im = np.zeros(max(v[1].value, 1), np.int32)
+        _check(lib.halo_plan_pulse(self._h, p, d, None, None, None, None, None, None, None, None,
+                                   _np_ptr(im)))
+        return dict(send_to=v[0].value, send_size=v[1].value, recv_from=v[2].value,
+                    recv_size=v[3].value, atom_offset=v[4].value, dep_start=v[5].value,
+                    items=v[6].value, shift=shift, index_map=im[:v[1].value].copy())
+
+    # -- device side ------------------------------------------------------------
+    def _buf(self, t):
+        import torch
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("exchange buffers must be torch.cuda tensors")
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError("exchange buffers must be contiguous float32")
+        if t.numel() != 3 * self.total_slots:
+            raise ValueError(f"buffer holds {t.numel()} floats, the plan needs "
+                             f"{3 * self.total_slots} (total_slots x 3)")
+        if t.data_ptr() % 4:
+            raise ValueError("buffer must be 4-byte aligned")
+        return ctypes.c_void_p(t.data_ptr())
+
+    def upload(self):
+        _check(load_library().halo_plan_upload(self._h))
+
+    def exchange_x(self, x, stream=None):
+        _check(load_library().halo_exchange_x(self._h, self._buf(x), _stream_handle(stream)))
+
+    def exchange_f(self, f, stream=None):
+        _check(load_library().halo_exchange_f(self._h, self._buf(f), _stream_handle(stream)))
+
+    def exchange_x_pulsewise(self, x, stream=None):
+        _check(load_library().halo_exchange_x_pulsewise(self._h, self._buf(x),
+                                                        _stream_handle(stream)))
+
+    def exchange_f_pulsewise(self, f, stream=None):
+        _check(load_library().halo_exchange_f_pulsewise(self._h, self._buf(f),
+                                                        _stream_handle(stream)))
+
+    def sync(self, stream=None):
+        _check(load_library().halo_plan_sync(self._h, _stream_handle(stream)))
+
+    def reset(self):
+        _check(load_library().halo_plan_reset(self._h))
+
+    def set_spin_limit(self, polls: int):
+        _check(load_library().halo_plan_set_spin_limit(self._h, polls))
+
+    def debug_withhold(self, segment: int):
+        _check(load_library().halo_plan_debug_withhold(self._h, segment))
+
+    # -- inputs in this layout ----------------------------------------------------
+    def home_filled(self, positions, fill=float("nan")) -> np.ndarray:
+        """Host array in this plan's slot layout: positions in home slots."""
+        x = np.full((self.total_slots, 3), fill, dtype=np.float32)
+        x[self.home_slots()] = np.asarray(positions, np.float32).reshape(-1, 3)
+        return x

@@ -1,0 +1,75 @@
+"""Compile the HIP library (libhalo.so) in-tree for gfx950.
+
+    python -m domain_decomposition_halo_fusedpackx_amd.build
+
+Host code (the plan builder) is compiled with g++; the kernels and the C-ABI
+with hipcc. Floating point: no FMA contraction, subnormals kept, and packed
+fp32 instructions disabled for the device code.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libhalo.so")
+BUILD_DIR = os.path.join(PKG, "_build")
+
+ARCH = os.environ.get("HALO_OFFLOAD_ARCH", "gfx950")
+
+HIP_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+              "-Wextra", "-pthread"]
+
+
+def _hipcc() -> str:
+    h = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(h):
+        raise RuntimeError("hipcc not found: the HIP library cannot be built")
+    return h
+
+
+def _run(cmd):
+    print("+", " ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile libhalo.so (always recompiles). Returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    plan_o = os.path.join(BUILD_DIR, "plan.o")
+    api_o = os.path.join(BUILD_DIR, "halo_api.o")
+    _run(["g++", *HOST_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o])
+    _run([_hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, "halo_api.hip"), "-o",
+          api_o])
+    tmp = LIB + ".tmp"
+    _run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, api_o,
+          plan_o])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def asm(out_path: str | None = None) -> str:
+    """Write the gfx950 assembly of the kernels (for inspection)."""
+    out_path = out_path or os.path.join(BUILD_DIR, "halo_api.s")
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    _run([_hipcc(), *HIP_FLAGS, "-I", INCLUDE, "--cuda-device-only", "-S",
+          os.path.join(CSRC, "halo_api.hip"), "-o", out_path])
+    return out_path
+
+
+if __name__ == "__main__":
+    if len(sys.argv) > 1 and sys.argv[1] == "asm":
+        print(asm(sys.argv[2] if len(sys.argv) > 2 else None))
+    else:
+        print(build())

@@ -1,0 +1,642 @@
+// halo_api.hip -- the exchange kernels for gfx950 and the C-ABI of include/halo.h.
+//
+// Method: "Redesigning GROMACS Halo Exchange" (paper review):
+//   Algorithm 3 FusedPackCommX  -> k_pack<FUSED=true>: every pulse in one
+//     launch; blocks take work items (a run of one pulse's indexMap for one
+//     sending domain) and store x[indexMap[i]] + coordShift straight into the
+//     receiver's region (the pages' NVLink zero-copy store: here the receiver
+//     is another region of the same HBM buffer);
+//   Algorithm 4 packWithDeps    -> the item's entries below depOffset are
+//     stored at once; the rest wait for the regions they forward;
+//   Algorithm 5 syncAndCommWithDeps -> block barrier + one release atomic per
+//     item on the (pulse, sender) completion counter;
+//   Algorithm 6 FusedCommUnpackF -> k_unpack<FUSED=true>: pulses in reverse;
+//     the forces of the receiver's region are added onto the sender's
+//     indexMap targets.
+// "GPU-Initiated Halo Exchange Cuts CPU Bottlenecks in GROMACS", "Fusing
+// pack, put, and wait into one kernel": the per-pulse first design is kept as
+// k_pack / k_unpack <FUSED=false>, one launch per pulse in stream order.
+//
+// Everything is float32 and every add is a single IEEE add (no FMA, no flush
+// of subnormals: the build passes -ffp-contract=off and keeps denormals).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/halo.h"
+#include "plan.hpp"
+#include "sync.hpp"
+
+using halo::WorkItem;
+
+namespace {
+
+constexpr int kThreads = 256;             // 4 waves of 64 per workgroup
+constexpr int32_t kDefaultItemEntries = 1024;
+
+thread_local std::string g_last_error;
+
+halo_status fail(halo_status st, const std::string &msg)
+{
+    g_last_error = msg;
+    return st;
+}
+
+// ---- buffer addressing ----------------------------------------------------
+// x, f and the indexMap are read and written through buffer descriptors: one
+// 12-byte float triple per buffer_load/store_dwordx3, 32-bit byte offsets, and
+// hardware range checking (an offset past the end returns zeros on a load and
+// drops a store). kInvalid is such an offset; the plan keeps every buffer
+// below 2 GiB so that it is never in range.
+typedef float f3v __attribute__((ext_vector_type(3)));
+constexpr uint32_t kInvalid = 0x80000000u;
+constexpr int kPlain = 0;      // cached access
+constexpr int kShared = 16;    // sc1: agent-coherent access, bypasses the XCD-private caches
+constexpr int32_t kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, kRsrcWord3);
+}
+
+template <int AUX>
+__device__ __forceinline__ f3v load3(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b96(r, byte_off, 0, AUX);
+}
+
+template <int AUX>
+__device__ __forceinline__ void store3(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f3v v)
+{
+    __builtin_amdgcn_raw_buffer_store_b96(v, r, byte_off, 0, AUX);
+}
+
+// indexMap entry e, or 0 when !ok (the load is issued either way, so that no
+// branch separates the loads of one thread).
+__device__ __forceinline__ uint32_t load_index(__amdgpu_buffer_rsrc_t r, int32_t e, bool ok)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, ok ? (uint32_t)e * 4u : kInvalid, 0, kPlain);
+}
+
+// Gather x[idx[map_begin + e]] + shift and store it at slot region_begin + e,
+// for e in [lo, hi), hi - lo <= EPT * kThreads. Branch-free: lanes past hi
+// load slot 0 and store to kInvalid. All index loads are issued first, then
+// all gathers, then all stores.
+template <int EPT, int LD, int ST>
+__device__ __forceinline__ void pack_span(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t ridx,
+                                          int32_t map_begin, int32_t region_begin, int32_t lo,
+                                          int32_t hi, f3v shift)
+{
+    uint32_t src[EPT], dst[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = lo + (int32_t)threadIdx.x + j * kThreads;
+        const bool ok = e < hi;
+        src[j] = load_index(ridx, map_begin + e, ok) * 12u;
+        dst[j] = ok ? (uint32_t)(region_begin + e) * 12u : kInvalid;
+    }
+    f3v v[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) v[j] = load3<LD>(rx, src[j]);
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) store3<ST>(rx, dst[j], v[j] + shift);
+}
+
+// ---- work items ------------------------------------------------------------
+
+// One coordinate-direction item of the fused exchange (Algorithms 3 and 4):
+// the entries below depOffset are stored at once; the rest wait for the
+// regions they forward. Home slots are never written during the launch and
+// are read through the caches; every forwarded region is stored and read
+// with sc1 accesses.
+template <int EPT>
+__device__ __forceinline__ void pack_item_fused(const WorkItem *it, __amdgpu_buffer_rsrc_t rx,
+                                                __amdgpu_buffer_rsrc_t ridx, const int32_t *xwaits,
+                                                const uint32_t *seg_items, uint32_t *state,
+                                                int32_t n_seg, uint32_t epoch,
+                                                uint32_t spin_limit, uint32_t *err_word,
+                                                int32_t withhold)
+{
+    const int32_t map_begin = it->map_begin;
+    const int32_t n_indep = it->n_indep;
+    const int32_t n_total = it->n_total;
+    const int32_t region_begin = it->region_begin;
+    const f3v shift = {it->shift[0], it->shift[1], it->shift[2]};
+    const bool st_shared = (it->flags & halo::kItemXStoreShared) != 0;
+    if (n_indep > 0) {
+        if (st_shared)
+            pack_span<EPT, kPlain, kShared>(rx, ridx, map_begin, region_begin, 0, n_indep, shift);
+        else
+            pack_span<EPT, kPlain, kPlain>(rx, ridx, map_begin, region_begin, 0, n_indep, shift);
+    }
+    if (n_total > n_indep) {
+        halo::wait_segments(xwaits + it->xwait_begin, it->xwait_count, seg_items, state, n_seg,
+                            false, epoch, spin_limit, err_word);
+        if (st_shared)
+            pack_span<EPT, kShared, kShared>(rx, ridx, map_begin, region_begin, n_indep, n_total,
+                                             shift);
+        else
+            pack_span<EPT, kShared, kPlain>(rx, ridx, map_begin, region_begin, n_indep, n_total,
+                                            shift);
+    }
+    halo::signal_done(halo::counter_x(state, it->seg), it->seg == withhold);
+}
+
+// f[idx[map_begin + e]] += f[region_begin + e] for e < n; the index loads were
+// issued before the dependency wait.
+template <int EPT, int LD, int ST>
+__device__ __forceinline__ void unpack_span(__amdgpu_buffer_rsrc_t rf, const uint32_t *tgt,
+                                            int32_t region_begin, int32_t n)
+{
+    f3v add[EPT], cur[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        add[j] = load3<LD>(rf, e < n ? (uint32_t)(region_begin + e) * 12u : kInvalid);
+        cur[j] = load3<LD>(rf, tgt[j]);  // kInvalid reads zeros
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) store3<ST>(rf, tgt[j], cur[j] + add[j]);
+}
+
+template <int EPT>
+__device__ __forceinline__ void load_targets(__amdgpu_buffer_rsrc_t ridx, int32_t map_begin,
+                                             int32_t n_total, uint32_t *tgt)
+{
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        const bool ok = e < n_total;
+        const uint32_t t = load_index(ridx, map_begin + e, ok) * 12u;
+        tgt[j] = ok ? t : kInvalid;
+    }
+}
+
+// One force-direction item of the fused exchange (Algorithm 6): wait until
+// pulse p+1 is finished for the sender and its receiver, then add.
+template <int EPT>
+__device__ __forceinline__ void unpack_item_fused(const WorkItem *it, __amdgpu_buffer_rsrc_t rf,
+                                                  __amdgpu_buffer_rsrc_t ridx,
+                                                  const uint32_t *seg_items, uint32_t *state,
+                                                  int32_t n_seg, uint32_t epoch,
+                                                  uint32_t spin_limit, uint32_t *err_word,
+                                                  int32_t withhold)
+{
+    const int32_t n_total = it->n_total;
+    const int32_t region_begin = it->region_begin;
+    // The indexMap is read-only during the exchange: load it before waiting.
+    uint32_t tgt[EPT];
+    load_targets<EPT>(ridx, it->map_begin, n_total, tgt);
+    if (it->fwait[0] >= 0) {
+        const int32_t nw = it->fwait[1] >= 0 && it->fwait[1] != it->fwait[0] ? 2 : 1;
+        halo::wait_segments(it->fwait, nw, seg_items, state, n_seg, true, epoch, spin_limit,
+                            err_word);
+    }
+    const int32_t fl = it->flags;
+    if (fl & halo::kItemFLoadShared) {
+        if (fl & halo::kItemFStoreShared)
+            unpack_span<EPT, kShared, kShared>(rf, tgt, region_begin, n_total);
+        else
+            unpack_span<EPT, kShared, kPlain>(rf, tgt, region_begin, n_total);
+    } else {
+        if (fl & halo::kItemFStoreShared)
+            unpack_span<EPT, kPlain, kShared>(rf, tgt, region_begin, n_total);
+        else
+            unpack_span<EPT, kPlain, kPlain>(rf, tgt, region_begin, n_total);
+    }
+    halo::signal_done(halo::counter_f(state, n_seg, it->seg), it->seg == withhold);
+}
+
+// ---- kernels -----------------------------------------------------------------
+
+// Fused coordinate exchange: ONE launch for all pulses, one item per
+// workgroup, items in pulse-major order of the workgroup index. An item only
+// waits on items of earlier pulses, i.e. on workgroups with smaller indices.
+// The hardware hands workgroups of a grid to the XCDs round-robin and each
+// XCD dispatches its share in increasing index order, so the smallest
+// unfinished item is always resident or next in line: every wait ends. The
+// spin limit turns a violation of that order into HALO_ERR_TIMEOUT, not a
+// hang. (No atomic ticket: 2560 same-address device atomics serialise for
+// about 20 us on MI355X; and no cooperative launch, which idles the GPU for
+// about 20 us before each launch.)
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_pack_fused(
+    float *x, uint32_t x_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
+    const WorkItem *__restrict__ items, const int32_t *__restrict__ xwaits,
+    const uint32_t *__restrict__ seg_items, uint32_t *state, int32_t n_seg, uint32_t epoch,
+    uint32_t spin_limit, uint32_t *err_word, int32_t withhold)
+{
+    pack_item_fused<EPT>(items + blockIdx.x, make_rsrc(x, x_bytes), make_rsrc(idx, idx_bytes),
+                         xwaits, seg_items, state, n_seg, epoch, spin_limit, err_word, withhold);
+}
+
+// Fused force exchange: ONE launch, workgroup b takes item n_items-1-b, so
+// the last pulse comes first; same progress argument.
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_unpack_fused(
+    float *f, uint32_t f_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
+    const WorkItem *__restrict__ items, const uint32_t *__restrict__ seg_items, uint32_t *state,
+    int32_t n_seg, uint32_t n_items, uint32_t epoch, uint32_t spin_limit, uint32_t *err_word,
+    int32_t withhold)
+{
+    unpack_item_fused<EPT>(items + (n_items - 1u - blockIdx.x), make_rsrc(f, f_bytes),
+                           make_rsrc(idx, idx_bytes), seg_items, state, n_seg, epoch, spin_limit,
+                           err_word, withhold);
+}
+
+// Per-pulse baseline: one launch per pulse, one item per workgroup, no
+// counters; the kernel boundary orders the pulses, so every access is cached.
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_pack_pulse(float *x, uint32_t x_bytes,
+                                                         const int32_t *__restrict__ idx,
+                                                         uint32_t idx_bytes,
+                                                         const WorkItem *__restrict__ items,
+                                                         int32_t item_base)
+{
+    const WorkItem *it = items + item_base + blockIdx.x;
+    const f3v shift = {it->shift[0], it->shift[1], it->shift[2]};
+    pack_span<EPT, kPlain, kPlain>(make_rsrc(x, x_bytes), make_rsrc(idx, idx_bytes),
+                                   it->map_begin, it->region_begin, 0, it->n_total, shift);
+}
+
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_unpack_pulse(float *f, uint32_t f_bytes,
+                                                           const int32_t *__restrict__ idx,
+                                                           uint32_t idx_bytes,
+                                                           const WorkItem *__restrict__ items,
+                                                           int32_t item_base)
+{
+    const WorkItem *it = items + item_base + blockIdx.x;
+    uint32_t tgt[EPT];
+    load_targets<EPT>(make_rsrc(idx, idx_bytes), it->map_begin, it->n_total, tgt);
+    unpack_span<EPT, kPlain, kPlain>(make_rsrc(f, f_bytes), tgt, it->region_begin, it->n_total);
+}
+
+}  // namespace
+
+struct halo_plan {
+    halo::HostPlan h;
+    int device = -1;
+    bool uploaded = false;
+    bool poisoned = false;
+    int32_t *d_idx = nullptr;
+    WorkItem *d_items = nullptr;
+    int32_t *d_xwaits = nullptr;
+    uint32_t *d_seg_items = nullptr;
+    uint32_t *d_state = nullptr;
+    size_t state_words = 0;
+    uint32_t *h_err = nullptr;  // pinned host word, written by kernels on a timeout
+    uint32_t *d_err = nullptr;  // its device address
+    uint32_t epoch_x = 0, epoch_f = 0;
+    uint32_t spin_limit = 1u << 20;
+    int32_t withhold = -1;
+};
+
+namespace {
+
+halo_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(HALO_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void free_device(halo_plan *p)
+{
+    if (p->d_idx) (void)hipFree(p->d_idx);
+    if (p->d_items) (void)hipFree(p->d_items);
+    if (p->d_xwaits) (void)hipFree(p->d_xwaits);
+    if (p->d_seg_items) (void)hipFree(p->d_seg_items);
+    if (p->d_state) (void)hipFree(p->d_state);
+    if (p->h_err) (void)hipHostFree(p->h_err);
+    p->d_idx = nullptr;
+    p->d_items = nullptr;
+    p->d_xwaits = nullptr;
+    p->d_seg_items = nullptr;
+    p->d_state = nullptr;
+    p->h_err = p->d_err = nullptr;
+    p->uploaded = false;
+}
+
+template <class T>
+hipError_t upload_vec(T **dst, const std::vector<T> &v)
+{
+    size_t bytes = std::max<size_t>(v.size() * sizeof(T), 16);
+    hipError_t e = hipMalloc((void **)dst, bytes);
+    if (e != hipSuccess) return e;
+    if (!v.empty()) e = hipMemcpy(*dst, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice);
+    return e;
+}
+
+int ept_for(int32_t item_entries)
+{
+    const int e = (item_entries + kThreads - 1) / kThreads;
+    return e <= 1 ? 1 : e <= 2 ? 2 : e <= 4 ? 4 : 8;
+}
+
+// Kernel entry points for the plan's items-per-thread.
+struct Kernels {
+    const void *pack_fused, *unpack_fused, *pack_pulse, *unpack_pulse;
+};
+
+template <int EPT>
+Kernels kernels_for()
+{
+    return {(const void *)&k_pack_fused<EPT>, (const void *)&k_unpack_fused<EPT>,
+            (const void *)&k_pack_pulse<EPT>, (const void *)&k_unpack_pulse<EPT>};
+}
+
+Kernels kernels(int32_t item_entries)
+{
+    switch (ept_for(item_entries)) {
+    case 1: return kernels_for<1>();
+    case 2: return kernels_for<2>();
+    case 4: return kernels_for<4>();
+    default: return kernels_for<8>();
+    }
+}
+
+hipError_t launch_fused(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
+{
+    const halo::HostPlan &h = p->h;
+    int32_t n_seg = (int32_t)h.seg.size();
+    uint32_t n_items = (uint32_t)h.items.size();
+    uint32_t bytes = (uint32_t)(h.total_slots * 12);
+    uint32_t idx_bytes = (uint32_t)(h.abs_map.size() * 4);
+    uint32_t epoch = force_dir ? p->epoch_f : p->epoch_x;
+    const Kernels k = kernels(h.item_entries);
+    if (force_dir) {
+        void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_seg_items,
+                        &p->d_state, &n_seg, &n_items, &epoch, &p->spin_limit, &p->d_err,
+                        &p->withhold};
+        return hipLaunchKernel(k.unpack_fused, dim3(n_items), dim3(kThreads), args, 0, s);
+    }
+    void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_xwaits,
+                    &p->d_seg_items, &p->d_state, &n_seg, &epoch, &p->spin_limit, &p->d_err,
+                    &p->withhold};
+    return hipLaunchKernel(k.pack_fused, dim3(n_items), dim3(kThreads), args, 0, s);
+}
+
+hipError_t launch_pulse(halo_plan *p, bool force_dir, float *buf, hipStream_t s, int32_t q)
+{
+    const halo::HostPlan &h = p->h;
+    uint32_t bytes = (uint32_t)(h.total_slots * 12);
+    uint32_t idx_bytes = (uint32_t)(h.abs_map.size() * 4);
+    int32_t base = h.pulse_item_off[q];
+    const uint32_t n = (uint32_t)(h.pulse_item_off[q + 1] - base);
+    const Kernels k = kernels(h.item_entries);
+    void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &base};
+    return hipLaunchKernel(force_dir ? k.unpack_pulse : k.pack_pulse, dim3(n), dim3(kThreads),
+                           args, 0, s);
+}
+
+halo_status ensure_uploaded(halo_plan *p)
+{
+    if (p->uploaded) return HALO_OK;
+    hipError_t e;
+    if ((e = hipGetDevice(&p->device)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+    const halo::HostPlan &h = p->h;
+    if ((e = upload_vec(&p->d_idx, h.abs_map)) != hipSuccess ||
+        (e = upload_vec(&p->d_items, h.items)) != hipSuccess ||
+        (e = upload_vec(&p->d_xwaits, h.xwaits)) != hipSuccess ||
+        (e = upload_vec(&p->d_seg_items, h.seg_items)) != hipSuccess) {
+        free_device(p);
+        return hip_fail(e, "halo_plan_upload");
+    }
+    p->state_words = (size_t)halo::kCountersBegin + 2 * h.seg.size() * halo::kCounterStride;
+    if ((e = hipMalloc((void **)&p->d_state, p->state_words * 4)) != hipSuccess ||
+        (e = hipMemset(p->d_state, 0, p->state_words * 4)) != hipSuccess ||
+        (e = hipHostMalloc((void **)&p->h_err, 64, hipHostMallocMapped)) != hipSuccess ||
+        (e = hipHostGetDevicePointer((void **)&p->d_err, p->h_err, 0)) != hipSuccess ||
+        (e = hipDeviceSynchronize()) != hipSuccess) {
+        free_device(p);
+        return hip_fail(e, "halo_plan_upload");
+    }
+    std::memset(p->h_err, 0, 64);
+    p->epoch_x = p->epoch_f = 0;
+    p->uploaded = true;
+    return HALO_OK;
+}
+
+halo_status check_exchange(halo_plan *p, float *buf, const char *what)
+{
+    if (!p) return fail(HALO_ERR_ARG, std::string(what) + ": NULL plan");
+    if (!buf && p->h.total_slots > 0) return fail(HALO_ERR_ARG, std::string(what) + ": NULL buffer");
+    if (p->uploaded && p->h_err && __atomic_load_n(p->h_err, __ATOMIC_ACQUIRE) != 0)
+        p->poisoned = true;
+    if (p->poisoned)
+        return fail(HALO_ERR_STATE, std::string(what) +
+                                        ": plan poisoned by an in-kernel wait timeout; call "
+                                        "halo_plan_reset");
+    halo_status st = ensure_uploaded(p);
+    if (st != HALO_OK) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != p->device)
+        return fail(HALO_ERR_ARG, std::string(what) + ": current device differs from the plan's");
+    return HALO_OK;
+}
+
+int32_t item_entries_from_env()
+{
+    const char *v = std::getenv("HALO_ITEM_ENTRIES");
+    if (!v) return kDefaultItemEntries;
+    long n = std::strtol(v, nullptr, 10);
+    if (n < 1) n = 1;
+    if (n > 8 * kThreads) n = 8 * kThreads;
+    return (int32_t)n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *halo_last_error(void) { return g_last_error.c_str(); }
+
+halo_status halo_plan_create(const float *positions, int64_t n_atoms, const float *box,
+                             const int32_t *grid, float cutoff, halo_plan **out)
+{
+    if (!out) return fail(HALO_ERR_ARG, "halo_plan_create: NULL output pointer");
+    *out = nullptr;
+    halo_plan *p = new (std::nothrow) halo_plan();
+    if (!p) return fail(HALO_ERR_NOMEM, "halo_plan_create: out of host memory");
+    std::string msg;
+    int rc;
+    try {
+        rc = halo::build_plan(positions, n_atoms, box, grid, cutoff, item_entries_from_env(), p->h,
+                              msg);
+    } catch (const std::bad_alloc &) {
+        rc = halo::kErrNoMem;
+        msg = "halo_plan_create: out of host memory";
+    }
+    if (rc != halo::kOk) {
+        delete p;
+        return fail((halo_status)rc, msg);
+    }
+    *out = p;
+    return HALO_OK;
+}
+
+void halo_plan_destroy(halo_plan *plan)
+{
+    if (!plan) return;
+    free_device(plan);
+    delete plan;
+}
+
+int64_t halo_plan_total_slots(const halo_plan *p) { return p ? p->h.total_slots : -1; }
+int32_t halo_plan_num_domains(const halo_plan *p) { return p ? p->h.n_dom : -1; }
+int32_t halo_plan_num_pulses(const halo_plan *p) { return p ? p->h.n_pulse : -1; }
+int64_t halo_plan_num_entries(const halo_plan *p) { return p ? (int64_t)p->h.abs_map.size() : -1; }
+int32_t halo_plan_num_items(const halo_plan *p) { return p ? (int32_t)p->h.items.size() : -1; }
+
+halo_status halo_plan_pulse_dim(const halo_plan *p, int32_t pulse, int32_t *dim, int32_t *k)
+{
+    if (!p || pulse < 0 || pulse >= p->h.n_pulse)
+        return fail(HALO_ERR_ARG, "halo_plan_pulse_dim: no such pulse");
+    if (dim) *dim = p->h.pulse_dim[pulse];
+    if (k) *k = p->h.pulse_k[pulse];
+    return HALO_OK;
+}
+
+halo_status halo_plan_domain(const halo_plan *p, int32_t d, int64_t *base, int32_t *n_home,
+                             int32_t *n_halo)
+{
+    if (!p || d < 0 || d >= p->h.n_dom) return fail(HALO_ERR_ARG, "halo_plan_domain: no such domain");
+    if (base) *base = p->h.base[d];
+    if (n_home) *n_home = p->h.n_home[d];
+    if (n_halo) *n_halo = p->h.n_halo[d];
+    return HALO_OK;
+}
+
+halo_status halo_plan_home_slots(const halo_plan *p, int64_t *slot_of_atom)
+{
+    if (!p || (!slot_of_atom && p->h.n_atoms > 0))
+        return fail(HALO_ERR_ARG, "halo_plan_home_slots: NULL argument");
+    if (p->h.n_atoms > 0)
+        std::memcpy(slot_of_atom, p->h.home_slot.data(), (size_t)p->h.n_atoms * sizeof(int64_t));
+    return HALO_OK;
+}
+
+halo_status halo_plan_pulse(const halo_plan *p, int32_t pulse, int32_t d, int32_t *send_to,
+                            int32_t *send_size, int32_t *recv_from, int32_t *recv_size,
+                            int32_t *atom_offset, int32_t *dep_start, int32_t *items, float *shift,
+                            int32_t *index_map)
+{
+    if (!p || pulse < 0 || pulse >= p->h.n_pulse || d < 0 || d >= p->h.n_dom)
+        return fail(HALO_ERR_ARG, "halo_plan_pulse: no such pulse or domain");
+    const halo::Segment &s = p->h.at(pulse, d);
+    if (send_to) *send_to = s.send_to;
+    if (send_size) *send_size = s.send_size;
+    if (recv_from) *recv_from = s.recv_from;
+    if (recv_size) *recv_size = s.recv_size;
+    if (atom_offset) *atom_offset = s.atom_offset;
+    if (dep_start) *dep_start = s.dep_start;
+    if (items) *items = s.n_items;
+    if (shift)
+        for (int c = 0; c < 3; ++c) shift[c] = s.shift[c];
+    if (index_map && s.send_size > 0)
+        std::memcpy(index_map, p->h.local_map.data() + s.map_off, (size_t)s.send_size * 4);
+    return HALO_OK;
+}
+
+halo_status halo_plan_upload(halo_plan *p)
+{
+    if (!p) return fail(HALO_ERR_ARG, "halo_plan_upload: NULL plan");
+    return ensure_uploaded(p);
+}
+
+halo_status halo_exchange_x(halo_plan *p, float *x, void *stream)
+{
+    halo_status st = check_exchange(p, x, "halo_exchange_x");
+    if (st != HALO_OK) return st;
+    if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
+    p->epoch_x += 1;
+    hipError_t e = launch_fused(p, false, x, (hipStream_t)stream);
+    return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_x launch");
+}
+
+halo_status halo_exchange_f(halo_plan *p, float *f, void *stream)
+{
+    halo_status st = check_exchange(p, f, "halo_exchange_f");
+    if (st != HALO_OK) return st;
+    if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
+    p->epoch_f += 1;
+    hipError_t e = launch_fused(p, true, f, (hipStream_t)stream);
+    return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_f launch");
+}
+
+halo_status halo_exchange_x_pulsewise(halo_plan *p, float *x, void *stream)
+{
+    halo_status st = check_exchange(p, x, "halo_exchange_x_pulsewise");
+    if (st != HALO_OK) return st;
+    const halo::HostPlan &h = p->h;
+    if (h.total_slots == 0) return HALO_OK;
+    for (int32_t q = 0; q < h.n_pulse; ++q) {
+        hipError_t e = launch_pulse(p, false, x, (hipStream_t)stream, q);
+        if (e != hipSuccess) return hip_fail(e, "halo_exchange_x_pulsewise launch");
+    }
+    return HALO_OK;
+}
+
+halo_status halo_exchange_f_pulsewise(halo_plan *p, float *f, void *stream)
+{
+    halo_status st = check_exchange(p, f, "halo_exchange_f_pulsewise");
+    if (st != HALO_OK) return st;
+    const halo::HostPlan &h = p->h;
+    if (h.total_slots == 0) return HALO_OK;
+    for (int32_t q = h.n_pulse - 1; q >= 0; --q) {
+        hipError_t e = launch_pulse(p, true, f, (hipStream_t)stream, q);
+        if (e != hipSuccess) return hip_fail(e, "halo_exchange_f_pulsewise launch");
+    }
+    return HALO_OK;
+}
+
+halo_status halo_plan_sync(halo_plan *p, void *stream)
+{
+    if (!p) return fail(HALO_ERR_ARG, "halo_plan_sync: NULL plan");
+    if (!p->uploaded) return HALO_OK;
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "halo_plan_sync");
+    if (__atomic_load_n(p->h_err, __ATOMIC_ACQUIRE) != 0) {
+        p->poisoned = true;
+        return fail(HALO_ERR_TIMEOUT, "halo_plan_sync: an in-kernel dependency wait timed out");
+    }
+    return HALO_OK;
+}
+
+halo_status halo_plan_reset(halo_plan *p)
+{
+    if (!p) return fail(HALO_ERR_ARG, "halo_plan_reset: NULL plan");
+    if (!p->uploaded) {
+        p->poisoned = false;
+        return HALO_OK;
+    }
+    hipError_t e;
+    if ((e = hipDeviceSynchronize()) != hipSuccess ||
+        (e = hipMemset(p->d_state, 0, p->state_words * 4)) != hipSuccess ||
+        (e = hipDeviceSynchronize()) != hipSuccess)
+        return hip_fail(e, "halo_plan_reset");
+    std::memset(p->h_err, 0, 64);
+    p->epoch_x = p->epoch_f = 0;
+    p->poisoned = false;
+    return HALO_OK;
+}
+
+halo_status halo_plan_set_spin_limit(halo_plan *p, uint32_t polls)
+{
+    if (!p || polls == 0) return fail(HALO_ERR_ARG, "halo_plan_set_spin_limit: bad argument");
+    p->spin_limit = polls;
+    return HALO_OK;
+}
+
+halo_status halo_plan_debug_withhold(halo_plan *p, int32_t segment)
+{
+    if (!p || segment < -1 || segment >= (int32_t)p->h.seg.size())
+        return fail(HALO_ERR_ARG, "halo_plan_debug_withhold: no such segment");
+    p->withhold = segment;
+    return HALO_OK;
+}
+
+}  // extern "C"

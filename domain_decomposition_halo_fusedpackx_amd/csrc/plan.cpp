@@ -1,0 +1,318 @@
+// plan.cpp -- build the exchange plan on the host.
+//
+// Method: "Redesigning GROMACS Halo Exchange" (paper review), s.3 "GROMACS
+// domain decomposition halo exchange" (domains own home atoms; atoms within
+// the cutoff are forwarded through intermediate domains in pulses along z,
+// then y, then x), Algorithm 1 (PulseData) and Algorithm 4 (depOffset).
+//
+// Choices where the pages are silent (also stated in include/halo.h):
+// pulses per dimension ceil(cutoff / w); data flows to the lower neighbour
+// with +L on a periodic wrap; an atom is sent when its original position,
+// in units of w and in double precision, lies less than cutoff / w above the
+// receiver's upper face; home atoms in ascending id; indexMap ascending;
+// slots of a domain = [home | region per pulse], domains in id order.
+//
+// The build runs the pulses on index lists only (no coordinates are moved):
+// every pulse first lets each domain pick its sends from its slots as they
+// were before the pulse, then appends each pick to the receiver. Domains are
+// independent within each phase, so both phases run in parallel.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <limits>
+#include <thread>
+
+namespace halo {
+namespace {
+
+template <class F>
+void parallel_for(int32_t n, F &&fn)
+{
+    unsigned hw = std::thread::hardware_concurrency();
+    int32_t workers = (int32_t)std::min<unsigned>(hw ? hw : 1, 16);
+    workers = std::min(workers, std::max<int32_t>(1, n / 4));
+    if (workers <= 1) {
+        for (int32_t i = 0; i < n; ++i) fn(i);
+        return;
+    }
+    std::atomic<int32_t> next{0};
+    std::vector<std::thread> pool;
+    pool.reserve(workers);
+    for (int32_t w = 0; w < workers; ++w)
+        pool.emplace_back([&] {
+            for (int32_t i = next.fetch_add(1); i < n; i = next.fetch_add(1)) fn(i);
+        });
+    for (auto &t : pool) t.join();
+}
+
+struct Cell3 {
+    int32_t c[3];
+};
+
+inline Cell3 cell_of_domain(const int32_t *grid, int32_t id)
+{
+    Cell3 r;
+    r.c[0] = id % grid[0];
+    r.c[1] = (id / grid[0]) % grid[1];
+    r.c[2] = id / (grid[0] * grid[1]);
+    return r;
+}
+
+inline int32_t domain_of_cell(const int32_t *grid, const int32_t *c)
+{
+    return c[0] + grid[0] * (c[1] + grid[1] * c[2]);
+}
+
+}  // namespace
+
+int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,
+               float cutoff, int32_t item_entries, HostPlan &P, std::string &msg)
+{
+    if (n_atoms < 0 || !box || !grid || (n_atoms > 0 && !pos)) {
+        msg = "halo_plan_create: NULL pointer or negative atom count";
+        return kErrArg;
+    }
+    P = HostPlan();
+    P.n_atoms = n_atoms;
+    P.cutoff = cutoff;
+    for (int d = 0; d < 3; ++d) {
+        P.box[d] = box[d];
+        P.grid[d] = grid[d];
+        if (!(box[d] > 0.f) || !std::isfinite(box[d]) || grid[d] < 1) {
+            msg = "halo_plan_create: box lengths must be finite and > 0, grid counts >= 1";
+            return kErrGeometry;
+        }
+    }
+    if (!(cutoff > 0.f) || !std::isfinite(cutoff)) {
+        msg = "halo_plan_create: cutoff must be finite and > 0";
+        return kErrGeometry;
+    }
+    for (int d = 0; d < 3; ++d) {
+        P.width[d] = (double)box[d] / (double)grid[d];
+        P.reach[d] = (double)cutoff / P.width[d];
+        P.pulses_in[d] = 0;
+        if (grid[d] > 1) {
+            double np = std::ceil(P.reach[d]);
+            if (np > (double)(grid[d] - 1)) {
+                msg = "halo_plan_create: cutoff needs " + std::to_string((long long)np) +
+                      " pulses in dimension " + std::to_string(d) + " but the grid allows only " +
+                      std::to_string(grid[d] - 1);
+                return kErrGeometry;
+            }
+            P.pulses_in[d] = (int32_t)np;
+        }
+    }
+    for (int64_t a = 0; a < n_atoms; ++a)
+        for (int d = 0; d < 3; ++d) {
+            float v = pos[3 * a + d];
+            if (!std::isfinite(v) || !(v >= 0.f) || !(v < box[d])) {
+                msg = "halo_plan_create: atom " + std::to_string((long long)a) +
+                      " lies outside [0, L) or is not finite";
+                return kErrRange;
+            }
+        }
+    int64_t nd = (int64_t)grid[0] * grid[1] * grid[2];
+    if (nd > std::numeric_limits<int32_t>::max() / 64) {
+        msg = "halo_plan_create: too many domains";
+        return kErrGeometry;
+    }
+    P.n_dom = (int32_t)nd;
+    for (int dim = 2; dim >= 0; --dim)
+        for (int32_t k = 0; k < P.pulses_in[dim]; ++k) {
+            P.pulse_dim.push_back(dim);
+            P.pulse_k.push_back(k);
+        }
+    P.n_pulse = (int32_t)P.pulse_dim.size();
+
+    // Position in units of the domain width; a rounding up to n is pulled
+    // back below n so that the cell index stays in range.
+    std::vector<double> scaled((size_t)n_atoms * 3);
+    std::vector<int32_t> owner((size_t)n_atoms);
+    {
+        double top[3];
+        for (int d = 0; d < 3; ++d) top[d] = std::nextafter((double)grid[d], 0.0);
+        for (int64_t a = 0; a < n_atoms; ++a) {
+            int32_t c[3];
+            for (int d = 0; d < 3; ++d) {
+                double s = (double)pos[3 * a + d] / P.width[d];
+                if (s > top[d]) s = top[d];
+                scaled[3 * a + d] = s;
+                c[d] = (int32_t)std::floor(s);
+            }
+            owner[a] = domain_of_cell(grid, c);
+        }
+    }
+
+    // Home atoms by stable counting sort: ascending id within each domain.
+    std::vector<std::vector<int64_t>> slot_atom(P.n_dom);
+    P.n_home.assign(P.n_dom, 0);
+    for (int64_t a = 0; a < n_atoms; ++a) P.n_home[owner[a]] += 1;
+    for (int32_t d = 0; d < P.n_dom; ++d) slot_atom[d].reserve((size_t)P.n_home[d] * 2 + 8);
+    for (int64_t a = 0; a < n_atoms; ++a) slot_atom[owner[a]].push_back(a);
+
+    // Pulses.
+    P.seg.assign((size_t)P.n_pulse * P.n_dom, Segment());
+    std::vector<std::vector<int32_t>> picks((size_t)P.n_pulse * P.n_dom);
+    std::vector<std::vector<int64_t>> moving(P.n_dom);
+    for (int32_t p = 0; p < P.n_pulse; ++p) {
+        const int dim = P.pulse_dim[p];
+        const int32_t k = P.pulse_k[p];
+        const int32_t n = grid[dim];
+        const double reach = P.reach[dim];
+        Segment *row = &P.seg[(size_t)p * P.n_dom];
+        std::vector<int32_t> *prow = &picks[(size_t)p * P.n_dom];
+
+        // Phase 1 reads only the sender's own slots.
+        parallel_for(P.n_dom, [&](int32_t D) {
+            Cell3 cd = cell_of_domain(grid, D);
+            int32_t cr[3] = {cd.c[0], cd.c[1], cd.c[2]};
+            cr[dim] = cd.c[dim] == 0 ? n - 1 : cd.c[dim] - 1;
+            Segment &s = row[D];
+            s.send_to = domain_of_cell(grid, cr);
+            s.shift[0] = s.shift[1] = s.shift[2] = 0.f;
+            if (cd.c[dim] == 0) s.shift[dim] = box[dim];
+            // Candidate slots: all of them on the first pulse of a dimension,
+            // otherwise only what arrived in the previous pulse.
+            int32_t first = 0, last = (int32_t)slot_atom[D].size();
+            if (k > 0) {
+                const Segment &prev = P.seg[(size_t)(p - 1) * P.n_dom + D];
+                first = prev.atom_offset;
+                last = prev.atom_offset + prev.recv_size;
+            }
+            const double face = (double)(cr[dim] + 1);
+            std::vector<int32_t> &out = prow[D];
+            std::vector<int64_t> &mv = moving[D];
+            mv.clear();
+            const std::vector<int64_t> &sa = slot_atom[D];
+            for (int32_t slot = first; slot < last; ++slot) {
+                double above = scaled[3 * sa[slot] + dim] - face;
+                if (above < 0.0) above += (double)n;
+                if (above < reach) {
+                    out.push_back(slot);
+                    mv.push_back(sa[slot]);
+                }
+            }
+            s.send_size = (int32_t)out.size();
+            s.dep_start = (int32_t)(std::lower_bound(out.begin(), out.end(), P.n_home[D]) -
+                                    out.begin());
+        });
+
+        // Phase 2 writes only the receiver's slots; each receiver has exactly
+        // one sender per pulse.
+        parallel_for(P.n_dom, [&](int32_t D) {
+            const Segment &s = row[D];
+            Segment &r = row[s.send_to];
+            std::vector<int64_t> &dst = slot_atom[s.send_to];
+            r.recv_from = D;
+            r.recv_size = s.send_size;
+            r.atom_offset = (int32_t)dst.size();
+            dst.insert(dst.end(), moving[D].begin(), moving[D].end());
+        });
+    }
+
+    // Layout.
+    P.base.assign(P.n_dom, 0);
+    P.n_halo.assign(P.n_dom, 0);
+    int64_t acc = 0;
+    for (int32_t d = 0; d < P.n_dom; ++d) {
+        P.base[d] = acc;
+        P.n_halo[d] = (int32_t)slot_atom[d].size() - P.n_home[d];
+        acc += (int64_t)slot_atom[d].size();
+    }
+    P.total_slots = acc;
+    if (acc > kMaxSlots) {
+        msg = "halo_plan_create: more than " + std::to_string((long long)kMaxSlots) +
+              " slots (2 GiB of float triples) in one plan";
+        return kErrRange;
+    }
+    P.home_slot.assign((size_t)n_atoms, 0);
+    for (int32_t d = 0; d < P.n_dom; ++d)
+        for (int32_t s = 0; s < P.n_home[d]; ++s) P.home_slot[slot_atom[d][s]] = P.base[d] + s;
+
+    // Concatenated indexMap, pulse-major then domain.
+    int64_t entries = 0;
+    for (auto &s : P.seg) {
+        s.map_off = entries;
+        entries += s.send_size;
+    }
+    P.local_map.resize((size_t)entries);
+    P.abs_map.resize((size_t)entries);
+    for (int32_t p = 0; p < P.n_pulse; ++p)
+        for (int32_t D = 0; D < P.n_dom; ++D) {
+            const Segment &s = P.seg[(size_t)p * P.n_dom + D];
+            const std::vector<int32_t> &pk = picks[(size_t)p * P.n_dom + D];
+            for (int32_t i = 0; i < s.send_size; ++i) {
+                P.local_map[s.map_off + i] = pk[i];
+                P.abs_map[s.map_off + i] = (int32_t)(P.base[D] + pk[i]);
+            }
+        }
+    make_items(P, item_entries);
+    return kOk;
+}
+
+void make_items(HostPlan &P, int32_t item_entries)
+{
+    P.item_entries = item_entries;
+    P.items.clear();
+    P.xwaits.clear();
+    P.seg_items.assign(P.seg.size(), 0);
+    P.pulse_item_off.assign(P.n_pulse + 1, 0);
+    for (int32_t p = 0; p < P.n_pulse; ++p) {
+        P.pulse_item_off[p] = (int32_t)P.items.size();
+        for (int32_t D = 0; D < P.n_dom; ++D) {
+            Segment &s = P.seg[(size_t)p * P.n_dom + D];
+            const Segment &rs = P.at(p, s.send_to);
+            const int32_t n = std::max<int32_t>(1, (s.send_size + item_entries - 1) / item_entries);
+            s.item_off = (int32_t)P.items.size();
+            s.n_items = n;
+            P.seg_items[(size_t)p * P.n_dom + D] = (uint32_t)n;
+            for (int32_t j = 0; j < n; ++j) {
+                const int32_t b = (int32_t)((int64_t)s.send_size * j / n);
+                const int32_t e = (int32_t)((int64_t)s.send_size * (j + 1) / n);
+                WorkItem it{};
+                it.map_begin = (int32_t)(s.map_off + b);
+                it.n_total = e - b;
+                it.n_indep = std::min(std::max(s.dep_start - b, 0), it.n_total);
+                it.region_begin = (int32_t)(P.base[s.send_to] + rs.atom_offset + b);
+                for (int c = 0; c < 3; ++c) it.shift[c] = s.shift[c];
+                it.seg = p * P.n_dom + D;
+                // Coordinate direction: wait for exactly the regions that the
+                // dependent entries read (each was filled by one sender in an
+                // earlier pulse).
+                it.xwait_begin = (int32_t)P.xwaits.size();
+                int32_t last_r = -1;
+                for (int32_t i = b + it.n_indep; i < e; ++i) {
+                    const int32_t slot = P.local_map[s.map_off + i];
+                    int32_t r = last_r < 0 ? 0 : last_r;
+                    while (r < p && !(slot >= P.at(r, D).atom_offset &&
+                                      slot < P.at(r, D).atom_offset + P.at(r, D).recv_size))
+                        ++r;
+                    if (r < p && r != last_r) {
+                        P.xwaits.push_back(r * P.n_dom + P.at(r, D).recv_from);
+                        last_r = r;
+                    }
+                }
+                it.xwait_count = (int32_t)P.xwaits.size() - it.xwait_begin;
+                // Force direction: pulse p+1 finished for D and for its receiver.
+                it.fwait[0] = it.fwait[1] = -1;
+                if (p + 1 < P.n_pulse) {
+                    it.fwait[0] = (p + 1) * P.n_dom + D;
+                    it.fwait[1] = (p + 1) * P.n_dom + s.send_to;
+                }
+                // Regions of every pulse but the last are candidates of a
+                // later pulse; in the force direction the last pulse runs
+                // first (reads untouched slots) and pulse 0 runs last (its
+                // sums are read by nobody in the same launch).
+                it.flags = 0;
+                if (p + 1 < P.n_pulse) it.flags |= kItemXStoreShared | kItemFLoadShared;
+                if (p > 0) it.flags |= kItemFStoreShared;
+                P.items.push_back(it);
+            }
+        }
+    }
+    P.pulse_item_off[P.n_pulse] = (int32_t)P.items.size();
+}
+
+}  // namespace halo

@@ -1,0 +1,103 @@
+// plan.hpp -- host-side exchange plan: PulseData per (pulse, domain) and the
+// work items the fused kernels run.
+//
+// "Redesigning GROMACS Halo Exchange" (paper review), Algorithm 1 (PulseData:
+// sendSize, recvSize, atomOffset, coordShift, indexMap, blocksForPulse) and
+// Algorithm 4 (depOffset split). The plan is rebuilt whenever the atoms are
+// redistributed (the pages' domain decomposition / neighbour search step).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace halo {
+
+// Work-item flags: which accesses of the item touch slots that another item
+// of the same launch writes or reads, and so must be coherent across XCDs.
+enum : int32_t {
+    kItemXStoreShared = 1,  // X: the region stored is forwarded by a later pulse
+    kItemFLoadShared = 2,   // F: the slots read were updated by a later pulse
+    kItemFStoreShared = 4,  // F: the slots written are read by an earlier pulse
+};
+
+// One work item = one workgroup of the fused kernels: a contiguous run of the
+// indexMap of one (pulse, sending domain) segment. 64 bytes, read with scalar
+// loads.
+struct alignas(16) WorkItem {
+    int32_t map_begin;     // first entry (index into the concatenated indexMap)
+    int32_t n_indep;       // leading entries below depOffset: no wait needed
+    int32_t n_total;       // entries in this item
+    int32_t region_begin;  // receiver-region slot of the first entry (X: store, F: load)
+    float shift[3];        // coordShift of the segment
+    int32_t seg;           // segment id = pulse * n_domains + sending domain
+    int32_t xwait_begin;   // coordinate direction: segments whose arrival the
+    int32_t xwait_count;   //   dependent entries need (list in xwaits)
+    int32_t fwait[2];      // force direction: (p+1, D) and (p+1, receiver); -1 = none
+    int32_t flags;         // kItem* bits
+    int32_t pad[3];
+};
+static_assert(sizeof(WorkItem) == 64, "WorkItem layout");
+
+struct Segment {
+    int32_t send_to = 0;
+    int32_t send_size = 0;
+    int32_t recv_from = 0;
+    int32_t recv_size = 0;
+    int32_t atom_offset = 0;  // local slot where this domain's region of the pulse starts
+    int32_t dep_start = 0;
+    float shift[3] = {0.f, 0.f, 0.f};
+    int64_t map_off = 0;      // first entry in the concatenated indexMap
+    int32_t item_off = 0;     // first work item (pulse-major item order)
+    int32_t n_items = 0;
+};
+
+struct HostPlan {
+    // inputs
+    int64_t n_atoms = 0;
+    float box[3] = {0, 0, 0};
+    int32_t grid[3] = {1, 1, 1};
+    float cutoff = 0;
+    // geometry
+    double width[3] = {0, 0, 0};
+    double reach[3] = {0, 0, 0};  // cutoff / width
+    int32_t pulses_in[3] = {0, 0, 0};
+    int32_t n_dom = 0;
+    int32_t n_pulse = 0;
+    std::vector<int32_t> pulse_dim, pulse_k;
+    // layout
+    std::vector<int64_t> base;
+    std::vector<int32_t> n_home, n_halo;
+    int64_t total_slots = 0;
+    std::vector<int64_t> home_slot;        // per atom
+    // pulses
+    std::vector<Segment> seg;              // [n_pulse * n_dom]
+    std::vector<int32_t> local_map;        // concatenated indexMap, local slots
+    std::vector<int32_t> abs_map;          // same entries as absolute slots
+    // work items
+    int32_t item_entries = 0;
+    std::vector<WorkItem> items;
+    std::vector<int32_t> xwaits;
+    std::vector<uint32_t> seg_items;       // items per segment
+    std::vector<int32_t> pulse_item_off;   // [n_pulse + 1]
+
+    const Segment &at(int32_t p, int32_t d) const { return seg[(size_t)p * n_dom + d]; }
+};
+
+// Largest slot count of one plan: byte offsets of float triples stay below
+// 2^31, so the kernels address x and f with 32-bit buffer offsets and use
+// 0x80000000 as an always-out-of-range offset.
+constexpr int64_t kMaxSlots = ((int64_t)1 << 31) / 12 - 1;
+
+// Status codes shared with halo.h.
+enum : int { kOk = 0, kErrArg = -1, kErrGeometry = -2, kErrRange = -3, kErrNoMem = -7 };
+
+// Build the plan; returns a status code and a message on failure.
+int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,
+               float cutoff, int32_t item_entries, HostPlan &out, std::string &msg);
+
+// Cut every segment into work items of at most item_entries entries and
+// compute their wait lists.
+void make_items(HostPlan &plan, int32_t item_entries);
+
+}  // namespace halo

@@ -1,0 +1,176 @@
+/*
+ * halo.h -- eighth-shell halo exchange over virtual domains on one MI355X.
+ *
+ * The method is the GPU-resident GROMACS domain-decomposition halo exchange:
+ *   "Redesigning GROMACS Halo Exchange: Improving Strong Scaling with
+ *    GPU-initiated NVSHMEM" (paper review), s.3 "GROMACS domain decomposition
+ *    halo exchange", Algorithms 1-6, s.4 "Core formulas";
+ *   "GPU-Initiated Halo Exchange Cuts CPU Bottlenecks in GROMACS", "Fusing
+ *    pack, put, and wait into one kernel".
+ *
+ * A periodic rectangular box is cut into nx*ny*nz domains. Every domain holds
+ * its home atoms and, after a coordinate exchange, a halo: the atoms within the
+ * cutoff above its upper faces (the eighth shell), delivered by forwarding
+ * pulses in z, then y, then x. All domains live in one device buffer, so the
+ * pages' remote store into a peer's coordinate array is a store into another
+ * domain's region of the same allocation.
+ *
+ * Conventions fixed by this library where the pages leave them open:
+ *  - pulses per dimension: ceil(cutoff / w_d) for a decomposed dimension
+ *    (n_d > 1), none otherwise; it may not exceed n_d - 1;
+ *  - a domain sends to its lower neighbour (periodic); a send from cell 0 of
+ *    the pulse's dimension wraps and adds +L_d (coordShift);
+ *  - an atom is sent in pulse (d, k) iff, measured from its original position
+ *    in double precision in units of w_d, it lies less than cutoff/w_d above
+ *    the receiver's upper face; candidates are all local slots for k = 0 and
+ *    the region received in pulse (d, k-1) for k >= 1;
+ *  - domain id = cx + nx*(cy + ny*cz); home atoms in ascending atom id; indexMap
+ *    ascending; a domain's slots are [home | region of pulse 0 | pulse 1 | ...]
+ *    and domains follow one another in id order ("slots" below);
+ *  - force exchange: pulses strictly in reverse order, one fp32 add per
+ *    component, so results are bitwise deterministic.
+ *
+ * Coordinates and forces are float32 triples (x, y, z), 12 bytes per slot,
+ * packed without padding.
+ *
+ * Errors: every call returns a halo_status; halo_last_error() gives a message
+ * for the calling thread's last failure. Argument and geometry errors return
+ * synchronously with no side effect. A wait inside a kernel that exceeds its
+ * spin limit sets the plan's device error word; halo_plan_sync() or the next
+ * exchange reports HALO_ERR_TIMEOUT, and the plan refuses exchanges until
+ * halo_plan_reset().
+ */
+#ifndef HALO_H
+#define HALO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct halo_plan halo_plan; /* opaque; created and freed by the library */
+
+typedef enum {
+    HALO_OK = 0,
+    HALO_ERR_ARG = -1,      /* NULL pointer, negative count, index out of range   */
+    HALO_ERR_GEOMETRY = -2, /* box/grid/cutoff not positive and finite, or more
+                               pulses in a dimension than n_d - 1                */
+    HALO_ERR_RANGE = -3,    /* a position not finite or outside [0, L); more
+                               slots than fit a 32-bit index                      */
+    HALO_ERR_HIP = -4,      /* a HIP runtime call failed                          */
+    HALO_ERR_TIMEOUT = -5,  /* an in-kernel dependency wait exceeded its limit    */
+    HALO_ERR_STATE = -6,    /* plan poisoned by an earlier timeout                */
+    HALO_ERR_NOMEM = -7     /* host allocation failed                             */
+} halo_status;
+
+/* Build the exchange plan (the pages' PulseData per pulse and domain,
+ * Algorithm 1) from the atom positions. Host only: no HIP call is made; device
+ * metadata is uploaded by halo_plan_upload() or by the first exchange.
+ *   positions : host, n_atoms*3 float32 (x,y,z per atom), each in [0, L_d)
+ *   n_atoms   : >= 0 (positions may be NULL when 0)
+ *   box       : host, 3 float32, periodic box lengths Lx, Ly, Lz > 0
+ *   grid      : host, 3 int32, domains per dimension nx, ny, nz >= 1
+ *   cutoff    : > 0, in the units of box
+ *   out       : receives the plan; set to NULL on error
+ * The caller keeps ownership of every input; the plan copies what it needs. */
+halo_status halo_plan_create(const float *positions, int64_t n_atoms, const float *box,
+                             const int32_t *grid, float cutoff, halo_plan **out);
+
+/* Free the plan and its device metadata (NULL is accepted). Waits for nothing:
+ * the caller must make sure no exchange on the plan is still running. */
+void halo_plan_destroy(halo_plan *plan);
+
+/* Message describing the calling thread's most recent error ("" if none). */
+const char *halo_last_error(void);
+
+/* ---- plan read-out ----------------------------------------------------------------- */
+
+int64_t halo_plan_total_slots(const halo_plan *plan);  /* slots in x and f; -1 on NULL */
+int32_t halo_plan_num_domains(const halo_plan *plan);  /* nx*ny*nz; -1 on NULL        */
+int32_t halo_plan_num_pulses(const halo_plan *plan);   /* np(x)+np(y)+np(z); -1 on NULL */
+int64_t halo_plan_num_entries(const halo_plan *plan);  /* indexMap entries, all pulses */
+int32_t halo_plan_num_items(const halo_plan *plan);    /* work items (workgroups) per exchange */
+
+/* Dimension (0 = x, 1 = y, 2 = z) and number within that dimension of pulse p. */
+halo_status halo_plan_pulse_dim(const halo_plan *plan, int32_t p, int32_t *dim, int32_t *k);
+
+/* Layout of domain d: first slot, home count, halo count (outputs may be NULL). */
+halo_status halo_plan_domain(const halo_plan *plan, int32_t d, int64_t *base, int32_t *n_home,
+                             int32_t *n_halo);
+
+/* Home slot of every atom: slot_of_atom is host memory of n_atoms int64. */
+halo_status halo_plan_home_slots(const halo_plan *plan, int64_t *slot_of_atom);
+
+/* PulseData of pulse p for sending domain d (Algorithm 1); outputs may be NULL.
+ *   send_to     : the receiving domain
+ *   send_size   : indexMap length
+ *   recv_from   : the domain that sends to d in this pulse
+ *   recv_size   : entries d receives in this pulse
+ *   atom_offset : first local slot of d's region for this pulse
+ *   dep_start   : entries of indexMap below depOffset (= d's home count): the
+ *                 independent prefix of Algorithm 4
+ *   items       : work items the plan cut this (pulse, domain) into
+ *   shift       : 3 float32, coordShift
+ *   index_map   : host, send_size int32 local slots of d, ascending */
+halo_status halo_plan_pulse(const halo_plan *plan, int32_t p, int32_t d, int32_t *send_to,
+                            int32_t *send_size, int32_t *recv_from, int32_t *recv_size,
+                            int32_t *atom_offset, int32_t *dep_start, int32_t *items, float *shift,
+                            int32_t *index_map);
+
+/* ---- device side ------------------------------------------------------------------- */
+
+/* Allocate and upload the device metadata on the current HIP device (blocking).
+ * Called implicitly by the first exchange. */
+halo_status halo_plan_upload(halo_plan *plan);
+
+/* Coordinate exchange, Algorithms 3-5 fused into ONE kernel launch on
+ * `stream` (a hipStream_t; NULL = default stream). All pulses run at once:
+ * the entries of each indexMap below depOffset are packed immediately; entries
+ * that forward atoms received in earlier pulses wait, inside the kernel, on
+ * the arrival counters of exactly the regions they read.
+ *   x : device, total_slots*3 float32, 4-byte aligned. Home slots are read;
+ *       every halo slot is overwritten with x[indexMap[i]] + coordShift.
+ * Asynchronous; exchanges of one plan must be ordered on one stream. */
+halo_status halo_exchange_x(halo_plan *plan, float *x, void *stream);
+
+/* Force exchange, Algorithm 6 in ONE kernel launch: pulses from last to
+ * first; for every sender d of pulse p, f[indexMap[i]] += f[receiver's region
+ * of pulse p][i]. A (pulse, domain) waits, inside the kernel, until pulse p+1
+ * is finished for itself and for its receiver, which keeps the per-slot order
+ * of additions of the serial reverse-pulse loop.
+ *   f : device, total_slots*3 float32, updated in place. On return home slots
+ *       hold the accumulated forces; forwarding halo slots hold partial sums.
+ * Asynchronous; exchanges of one plan must be ordered on one stream. */
+halo_status halo_exchange_f(halo_plan *plan, float *f, void *stream);
+
+/* The same two exchanges as one kernel launch per pulse, with no in-kernel
+ * waits: stream order between the launches carries the dependencies (the
+ * per-pulse "first design" of the NVIDIA guide, "Fusing pack, put, and wait
+ * into one kernel"). Results are bitwise identical to the fused calls. */
+halo_status halo_exchange_x_pulsewise(halo_plan *plan, float *x, void *stream);
+halo_status halo_exchange_f_pulsewise(halo_plan *plan, float *f, void *stream);
+
+/* Wait for the plan's work on `stream` and report a timeout raised inside a
+ * kernel (HALO_ERR_TIMEOUT); poisons the plan in that case. */
+halo_status halo_plan_sync(halo_plan *plan, void *stream);
+
+/* Clear a poisoned plan: zero the device counters and the error word (blocking,
+ * device-wide synchronisation). */
+halo_status halo_plan_reset(halo_plan *plan);
+
+/* Bound on the polls of one in-kernel dependency wait (default 1<<20, each
+ * separated by a short sleep). A debugging and testing knob. */
+halo_status halo_plan_set_spin_limit(halo_plan *plan, uint32_t polls);
+
+/* Testing hook: when `segment` >= 0, the fused kernels skip the completion
+ * signal of that (pulse * num_domains + domain) segment, so that its
+ * dependents run into their spin limit and the timeout path is exercised.
+ * -1 (the default) disables it. */
+halo_status halo_plan_debug_withhold(halo_plan *plan, int32_t segment);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HALO_H */

@@ -1,0 +1,246 @@
+"""GPU parity: the HIP exchanges against the serial oracle, bit for bit.
+
+Every test calls the library through the C-ABI (ctypes binding) on device
+buffers and compares the whole slot array (home and halo slots) with the
+oracle run on the same seeded inputs. Coordinates must match bitwise; fp32
+forces too, because both sides add in the same reverse-pulse order. Halo slots
+start as NaN, so a slot the kernel fails to write cannot pass.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from domain_decomposition_halo_fusedpackx_amd import HaloError, HaloPlan
+from domain_decomposition_halo_fusedpackx_amd import workloads as W
+
+from .test_oracle_pins import TINY
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU visible")
+    return t
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+def assert_bitwise(got, want, what):
+    g, w = bits(got), bits(want)
+    bad = np.flatnonzero((g != w).any(axis=1))
+    assert bad.size == 0, (f"{what}: {bad.size} slots differ, first {bad[:5].tolist()}: "
+                           f"got {got[bad[:3]].tolist()} want {want[bad[:3]].tolist()}")
+
+
+def setup_case(oracle_mod, pos, box, grid, rc):
+    plan = HaloPlan(pos, box, grid, rc)
+    o = oracle_mod.Oracle(pos, box, grid, rc)
+    assert plan.total_slots == o.total_slots
+    for a, b in zip(plan.domains(), o.domains()):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(plan.home_slots(), o.home_slots())
+    return plan, o
+
+
+def run_x(torch, plan, x_host, impl, stream=None):
+    x = torch.from_numpy(x_host.copy()).cuda()
+    if impl == "fused":
+        plan.exchange_x(x, stream)
+    else:
+        plan.exchange_x_pulsewise(x, stream)
+    torch.cuda.synchronize()
+    plan.sync(stream)
+    return x.cpu().numpy()
+
+
+def run_f(torch, plan, f_host, impl, stream=None):
+    f = torch.from_numpy(f_host.copy()).cuda()
+    if impl == "fused":
+        plan.exchange_f(f, stream)
+    else:
+        plan.exchange_f_pulsewise(f, stream)
+    torch.cuda.synchronize()
+    plan.sync(stream)
+    return f.cpu().numpy()
+
+
+def check_both(torch, oracle_mod, plan, o, seed, impl, tag):
+    x0 = o.home_filled(np.nan)
+    want_x = o.exchange_x(x0.copy())
+    say(f"{tag} {impl} exchange_x slots={o.total_slots}")
+    assert_bitwise(run_x(torch, plan, x0, impl), want_x, f"{tag} {impl} x")
+    base, n_home, n_halo = o.domains()
+    f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, seed)
+    want_f = o.exchange_f(f0.copy())
+    say(f"{tag} {impl} exchange_f")
+    assert_bitwise(run_f(torch, plan, f0, impl), want_f, f"{tag} {impl} f")
+
+
+@pytest.mark.parametrize("impl", ["fused", "pulsewise"])
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_parity_workloads(torch, oracle_mod, wid, impl):
+    w = W.WORKLOADS[wid]
+    pos = W.workload_positions(w)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    check_both(torch, oracle_mod, plan, o, w.seed, impl, w.name)
+
+
+@pytest.mark.parametrize("case", TINY, ids=lambda c: "x".join(map(str, c[1])))
+def test_parity_tiny_boxes(torch, oracle_mod, case):
+    box, grid, rc, n = case
+    pos = W.positions(box, n, 7)
+    plan, o = setup_case(oracle_mod, pos, box, grid, rc)
+    for impl in ("fused", "pulsewise"):
+        check_both(torch, oracle_mod, plan, o, 7, impl, "tiny" + "x".join(map(str, grid)))
+
+
+@pytest.mark.parametrize("entries", [64, 200, 256, 2048])
+@pytest.mark.parametrize("wid", [3, 4])
+def test_parity_item_sizes(torch, oracle_mod, monkeypatch, wid, entries):
+    """Items smaller and larger than one workgroup pass, ragged tails."""
+    monkeypatch.setenv("HALO_ITEM_ENTRIES", str(entries))
+    w = W.WORKLOADS[wid]
+    pos = W.workload_positions(w)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    check_both(torch, oracle_mod, plan, o, w.seed, "fused", f"{w.name} items={entries}")
+
+
+def test_edge_cases(torch, oracle_mod):
+    cases = [
+        ("empty", np.zeros((0, 3), np.float32), (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
+        ("one-domain", W.positions((2.0, 2.0, 2.0), 50, 3), (2.0, 2.0, 2.0), (1, 1, 1), 0.9),
+        ("all-in-one-domain", W.positions((1.0, 1.0, 1.0), 64, 4) + np.float32(2.5),
+         (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
+        ("one-atom", np.array([[0.1, 0.1, 0.1]], np.float32), (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
+    ]
+    for name, pos, box, grid, rc in cases:
+        plan, o = setup_case(oracle_mod, pos, box, grid, rc)
+        if o.total_slots == 0:
+            say(f"{name}: zero slots, exchanges are no-ops")
+            x = torch.zeros((0, 3), device="cuda")
+            plan.exchange_x(x)
+            plan.exchange_f(x)
+            plan.exchange_x_pulsewise(x)
+            plan.exchange_f_pulsewise(x)
+            torch.cuda.synchronize()
+            plan.sync()
+            continue
+        for impl in ("fused", "pulsewise"):
+            check_both(torch, oracle_mod, plan, o, 9, impl, name)
+
+
+@pytest.mark.parametrize("wid", [2, 4])
+def test_repeats_are_deterministic(torch, oracle_mod, wid):
+    """Many exchanges in a row (epochs advance, counters never reset)."""
+    w = W.WORKLOADS[wid]
+    pos = W.workload_positions(w)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    x0 = o.home_filled(np.nan)
+    want_x = o.exchange_x(x0.copy())
+    base, n_home, n_halo = o.domains()
+    f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, w.seed)
+    want_f = o.exchange_f(f0.copy())
+    x = torch.from_numpy(x0).cuda()
+    f_init = torch.from_numpy(f0).cuda()
+    f = torch.empty_like(f_init)
+    say(f"{w.name}: 60 alternating fused/pulsewise exchanges")
+    for r in range(30):
+        plan.exchange_x(x)
+        f.copy_(f_init)
+        plan.exchange_f(f)
+        if r % 10 == 9:
+            torch.cuda.synchronize()
+            assert_bitwise(x.cpu().numpy(), want_x, f"repeat {r} x")
+            assert_bitwise(f.cpu().numpy(), want_f, f"repeat {r} f")
+        plan.exchange_x_pulsewise(x)
+        f.copy_(f_init)
+        plan.exchange_f_pulsewise(f)
+    torch.cuda.synchronize()
+    plan.sync()
+    assert_bitwise(f.cpu().numpy(), want_f, "final f")
+
+
+def test_side_stream(torch, oracle_mod):
+    w = W.WORKLOADS[2]
+    pos = W.workload_positions(w)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    s = torch.cuda.Stream()
+    x0 = o.home_filled(np.nan)
+    want = o.exchange_x(x0.copy())
+    say("exchange on a side stream")
+    with torch.cuda.stream(s):
+        x = torch.from_numpy(x0).cuda()
+        plan.exchange_x(x)          # current stream = s
+        plan.exchange_x(x, s)       # explicit stream
+    s.synchronize()
+    plan.sync(s)
+    assert_bitwise(x.cpu().numpy(), want, "side stream x")
+
+
+def test_forced_timeout_poisons_and_reset_recovers(torch, oracle_mod):
+    """A withheld completion signal makes its dependents hit a tiny spin limit.
+
+    Every wait still ends (the limit is small), the kernel drains, the error
+    word surfaces as HALO_ERR_TIMEOUT, the plan refuses work until reset, and
+    after the reset results are exact again.
+    """
+    w = W.WORKLOADS[2]
+    pos = W.workload_positions(w)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    x0 = o.home_filled(np.nan)
+    want = o.exchange_x(x0.copy())
+    x = torch.from_numpy(x0).cuda()
+    plan.set_spin_limit(2000)
+    plan.debug_withhold(0)  # z0 of domain 0: the y0 items of domain 4 wait on it
+    say("forced timeout, coordinate direction")
+    plan.exchange_x(x)
+    torch.cuda.synchronize()
+    with pytest.raises(HaloError) as e:
+        plan.sync()
+    assert e.value.code == -5
+    with pytest.raises(HaloError) as e:
+        plan.exchange_x(x)
+    assert e.value.code == -6
+    plan.debug_withhold(-1)
+    plan.reset()
+    plan.set_spin_limit(1 << 20)
+    say("after reset")
+    x.copy_(torch.from_numpy(x0))
+    plan.exchange_x(x)
+    torch.cuda.synchronize()
+    plan.sync()
+    assert_bitwise(x.cpu().numpy(), want, "x after reset")
+
+    # force direction: withhold the last pulse of domain 0
+    base, n_home, n_halo = o.domains()
+    f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, 1)
+    want_f = o.exchange_f(f0.copy())
+    f = torch.from_numpy(f0).cuda()
+    plan.set_spin_limit(2000)
+    plan.debug_withhold((plan.num_pulses - 1) * plan.num_domains)
+    say("forced timeout, force direction")
+    plan.exchange_f(f)
+    torch.cuda.synchronize()
+    with pytest.raises(HaloError) as e:
+        plan.sync()
+    assert e.value.code == -5
+    plan.debug_withhold(-1)
+    plan.reset()
+    plan.set_spin_limit(1 << 20)
+    f.copy_(torch.from_numpy(f0))
+    plan.exchange_f(f)
+    torch.cuda.synchronize()
+    plan.sync()
+    assert_bitwise(f.cpu().numpy(), want_f, "f after reset")

@@ -1,0 +1,104 @@
+"""The library's host plan builder against the oracle (CPU only).
+
+The plan is host logic; its layout, home slots and every PulseData field
+(sendSize, recvSize, atomOffset, coordShift, indexMap, depOffset split) must
+equal the oracle's on every workload and on the tiny multi-pulse boxes.
+"""
+import numpy as np
+import pytest
+
+from domain_decomposition_halo_fusedpackx_amd import HaloError, HaloPlan
+from domain_decomposition_halo_fusedpackx_amd import workloads as W
+
+from .test_oracle_pins import TINY
+
+
+def compare_plans(plan, o):
+    assert plan.total_slots == o.total_slots
+    assert plan.num_domains == o.n_dom
+    assert plan.num_pulses == o.n_pulse
+    for a, b in zip(plan.domains(), o.domains()):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(plan.home_slots(), o.home_slots())
+    entries = 0
+    for p in range(o.n_pulse):
+        assert plan.pulse_dim(p) == o.pulse_dims()[p]
+        for d in range(o.n_dom):
+            a, b = plan.pulse(p, d), o.pulse(p, d)
+            for key in ("send_to", "send_size", "recv_from", "recv_size", "atom_offset",
+                        "dep_start"):
+                assert a[key] == b[key], (p, d, key)
+            np.testing.assert_array_equal(a["shift"].view(np.uint32), b["shift"].view(np.uint32))
+            np.testing.assert_array_equal(a["index_map"], b["index_map"])
+            assert a["items"] >= 1
+            entries += a["send_size"]
+    assert plan.num_entries == entries
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_plan_equals_oracle_on_workloads(oracle_mod, wid):
+    w = W.WORKLOADS[wid]
+    pos = W.workload_positions(w)
+    plan = HaloPlan(pos, w.box, w.grid, w.cutoff)
+    o = oracle_mod.Oracle(pos, w.box, w.grid, w.cutoff)
+    compare_plans(plan, o)
+
+
+@pytest.mark.parametrize("case", TINY, ids=lambda c: "x".join(map(str, c[1])))
+def test_plan_equals_oracle_on_tiny_boxes(oracle_mod, case):
+    box, grid, rc, n = case
+    for seed in (1, 2):
+        pos = W.positions(box, n, seed)
+        compare_plans(HaloPlan(pos, box, grid, rc), oracle_mod.Oracle(pos, box, grid, rc))
+
+
+def test_plan_edge_cases(oracle_mod):
+    # empty system, one domain, all atoms in one domain
+    cases = [
+        (np.zeros((0, 3), np.float32), (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
+        (W.positions((2.0, 2.0, 2.0), 50, 3), (2.0, 2.0, 2.0), (1, 1, 1), 0.9),
+        (W.positions((1.0, 1.0, 1.0), 64, 4) + np.float32(2.5), (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
+    ]
+    for pos, box, grid, rc in cases:
+        compare_plans(HaloPlan(pos, box, grid, rc), oracle_mod.Oracle(pos, box, grid, rc))
+
+
+@pytest.mark.parametrize("args", [
+    ((2.0, 2.0, 2.0), (2, 2, 2), 1.5),
+    ((2.0, 2.0, 2.0), (1, 1, 1), 0.0),
+    ((2.0, 2.0, 2.0), (1, 1, 1), float("nan")),
+    ((2.0, 0.0, 2.0), (1, 1, 1), 0.5),
+    ((2.0, 2.0, 2.0), (1, 0, 1), 0.5),
+])
+def test_error_codes_match_oracle(oracle_mod, args):
+    pos = W.positions((2.0, 2.0, 2.0), 10, 1)
+    want = oracle_mod.try_build(pos, *args)
+    with pytest.raises(HaloError) as e:
+        HaloPlan(pos, *args)
+    assert e.value.code == want
+
+
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -0.5, 2.0, 7.0])
+def test_position_errors_match_oracle(oracle_mod, bad):
+    pos = W.positions((2.0, 2.0, 2.0), 10, 1)
+    pos[3, 1] = bad
+    want = oracle_mod.try_build(pos, (2.0, 2.0, 2.0), (2, 2, 2), 0.5)
+    with pytest.raises(HaloError) as e:
+        HaloPlan(pos, (2.0, 2.0, 2.0), (2, 2, 2), 0.5)
+    assert e.value.code == want == -3
+
+
+def test_item_cutting(monkeypatch):
+    """Work items cover every entry once, with at least one per (pulse, domain)."""
+    w = W.WORKLOADS[4]
+    pos = W.workload_positions(w)
+    for n in (64, 300, 1024, 2048):
+        monkeypatch.setenv("HALO_ITEM_ENTRIES", str(n))
+        plan = HaloPlan(pos, w.box, w.grid, w.cutoff)
+        tot = 0
+        for p in range(plan.num_pulses):
+            for d in range(plan.num_domains):
+                q = plan.pulse(p, d)
+                assert q["items"] == max(1, -(-q["send_size"] // n))
+                tot += q["items"]
+        assert tot == plan.num_items
