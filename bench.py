@@ -115,6 +115,9 @@ def main():
     ap.add_argument("--no-ablation", action="store_true", help="skip the per-pulse baseline")
     ap.add_argument("--cpu-seconds", type=float, default=3.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device-to-device 3 times (a plain copy kernel of "
+                         "known size, for scaling hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -129,6 +132,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 18  # float32 elements in MIB MiB
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: 3 x {args.calibrate_copy} MiB")
+        del src, dst
     w = W.WORKLOADS[args.config]
     pos = W.workload_positions(w)
     log(f"workload {w.describe()}")

@@ -108,11 +108,60 @@ __device__ __forceinline__ void pack_span(__amdgpu_buffer_rsrc_t rx, __amdgpu_bu
 
 // ---- work items ------------------------------------------------------------
 
-// One coordinate-direction item of the fused exchange (Algorithms 3 and 4):
-// the entries below depOffset are stored at once; the rest wait for the
-// regions they forward. Home slots are never written during the launch and
-// are read through the caches; every forwarded region is stored and read
-// with sc1 accesses.
+// One coordinate-direction item of the fused exchange (Algorithms 3 and 4).
+// Thread t owns entries t, t+256, ... of the item. All index loads are
+// issued first (the indexMap is read-only), then the entries below depOffset
+// are gathered and stored at once; the rest wait for the regions they
+// forward. Lanes outside a phase use kInvalid offsets, so the code has no
+// branches between the loads of one thread. Home slots are never written
+// during the launch and are read through the caches; forwarded regions are
+// stored and read with sc1 accesses.
+template <int EPT, int ST>
+__device__ __forceinline__ void pack_item_fused_st(const WorkItem *it, __amdgpu_buffer_rsrc_t rx,
+                                                   __amdgpu_buffer_rsrc_t ridx,
+                                                   const int32_t *xwaits, const uint32_t *seg_items,
+                                                   uint32_t *state, int32_t n_seg, uint32_t epoch,
+                                                   uint32_t spin_limit, uint32_t *err_word)
+{
+    const int32_t n_indep = it->n_indep;
+    const int32_t n_total = it->n_total;
+    const int32_t region_begin = it->region_begin;
+    const f3v shift = {it->shift[0], it->shift[1], it->shift[2]};
+    uint32_t src[EPT], dst[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        const bool ok = e < n_total;
+        src[j] = load_index(ridx, it->map_begin + e, ok) * 12u;
+        dst[j] = ok ? (uint32_t)(region_begin + e) * 12u : kInvalid;
+    }
+    f3v v[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const bool ind = (int32_t)threadIdx.x + j * kThreads < n_indep;
+        v[j] = load3<kPlain>(rx, ind ? src[j] : kInvalid);
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const bool ind = (int32_t)threadIdx.x + j * kThreads < n_indep;
+        store3<ST>(rx, ind ? dst[j] : kInvalid, v[j] + shift);
+    }
+    if (n_total > n_indep) {
+        halo::wait_segments(xwaits + it->xwait_begin, it->xwait_count, seg_items, state, n_seg,
+                            false, epoch, spin_limit, err_word);
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const bool dep = (int32_t)threadIdx.x + j * kThreads >= n_indep;
+            v[j] = load3<kShared>(rx, dep ? src[j] : kInvalid);
+        }
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const bool dep = (int32_t)threadIdx.x + j * kThreads >= n_indep;
+            store3<ST>(rx, dep ? dst[j] : kInvalid, v[j] + shift);
+        }
+    }
+}
+
 template <int EPT>
 __device__ __forceinline__ void pack_item_fused(const WorkItem *it, __amdgpu_buffer_rsrc_t rx,
                                                 __amdgpu_buffer_rsrc_t ridx, const int32_t *xwaits,
@@ -121,28 +170,12 @@ __device__ __forceinline__ void pack_item_fused(const WorkItem *it, __amdgpu_buf
                                                 uint32_t spin_limit, uint32_t *err_word,
                                                 int32_t withhold)
 {
-    const int32_t map_begin = it->map_begin;
-    const int32_t n_indep = it->n_indep;
-    const int32_t n_total = it->n_total;
-    const int32_t region_begin = it->region_begin;
-    const f3v shift = {it->shift[0], it->shift[1], it->shift[2]};
-    const bool st_shared = (it->flags & halo::kItemXStoreShared) != 0;
-    if (n_indep > 0) {
-        if (st_shared)
-            pack_span<EPT, kPlain, kShared>(rx, ridx, map_begin, region_begin, 0, n_indep, shift);
-        else
-            pack_span<EPT, kPlain, kPlain>(rx, ridx, map_begin, region_begin, 0, n_indep, shift);
-    }
-    if (n_total > n_indep) {
-        halo::wait_segments(xwaits + it->xwait_begin, it->xwait_count, seg_items, state, n_seg,
-                            false, epoch, spin_limit, err_word);
-        if (st_shared)
-            pack_span<EPT, kShared, kShared>(rx, ridx, map_begin, region_begin, n_indep, n_total,
-                                             shift);
-        else
-            pack_span<EPT, kShared, kPlain>(rx, ridx, map_begin, region_begin, n_indep, n_total,
-                                            shift);
-    }
+    if (it->flags & halo::kItemXStoreShared)
+        pack_item_fused_st<EPT, kShared>(it, rx, ridx, xwaits, seg_items, state, n_seg, epoch,
+                                         spin_limit, err_word);
+    else
+        pack_item_fused_st<EPT, kPlain>(it, rx, ridx, xwaits, seg_items, state, n_seg, epoch,
+                                        spin_limit, err_word);
     halo::signal_done(halo::counter_x(state, it->seg), it->seg == withhold);
 }
 
