@@ -39,6 +39,10 @@ SIGNATURES = {
     "halo_plan_upload": (_st, [_vp]),
     "halo_exchange_x": (_st, [_vp, _vp, _vp]),
     "halo_exchange_f": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_x_indexmap": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_f_indexmap": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_x_transposed": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_f_transposed": (_st, [_vp, _vp, _vp]),
     "halo_exchange_x_pulsewise": (_st, [_vp, _vp, _vp]),
     "halo_exchange_f_pulsewise": (_st, [_vp, _vp, _vp]),
     "halo_plan_sync": (_st, [_vp, _vp]),
@@ -191,6 +195,22 @@ class HaloPlan:
 
     def exchange_f(self, f, stream=None):
         _check(load_library().halo_exchange_f(self._h, self._buf(f), _stream_handle(stream)))
+
+    def exchange_x_indexmap(self, x, stream=None):
+        _check(load_library().halo_exchange_x_indexmap(self._h, self._buf(x),
+                                                       _stream_handle(stream)))
+
+    def exchange_f_indexmap(self, f, stream=None):
+        _check(load_library().halo_exchange_f_indexmap(self._h, self._buf(f),
+                                                       _stream_handle(stream)))
+
+    def exchange_x_transposed(self, x, stream=None):
+        _check(load_library().halo_exchange_x_transposed(self._h, self._buf(x),
+                                                         _stream_handle(stream)))
+
+    def exchange_f_transposed(self, f, stream=None):
+        _check(load_library().halo_exchange_f_transposed(self._h, self._buf(f),
+                                                         _stream_handle(stream)))
 
     def exchange_x_pulsewise(self, x, stream=None):
         _check(load_library().halo_exchange_x_pulsewise(self._h, self._buf(x),

@@ -281,6 +281,213 @@ __global__ __launch_bounds__(kThreads) void k_unpack_fused(
                            err_word, withhold);
 }
 
+// ---- transposed form: per-slot pulse masks --------------------------------
+
+// Pulse ranks of one chunk. Thread t owns slots first + t + j*256 (j < EPT),
+// i.e. slot order is row-major over (j, wave, lane). For pulse p the slot's
+// entry of indexMap_p is chunk.rank[p] plus the number of earlier slots of
+// the chunk with bit p: a wave ballot gives the count within the wave, and an
+// exclusive prefix over (row, wave) in LDS, built once per pulse, the rest.
+template <int EPT>
+struct Ranks {
+    uint32_t cnt[halo::kMaxMaskPulses][EPT * 4];
+    uint32_t off[halo::kMaxMaskPulses][EPT * 4];
+};
+
+// Count, per pulse and (row, wave), the slots with the pulse's bit, then turn
+// the counts into exclusive prefixes (thread k computes entry k of pulse
+// k / (EPT*4) from up to EPT*4 independent LDS reads). Ends with a workgroup
+// barrier.
+template <int EPT>
+__device__ __forceinline__ void build_ranks(Ranks<EPT> &sh, const uint32_t *m, uint32_t umask,
+                                            int32_t n_pulse)
+{
+    constexpr int kRow = EPT * 4;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int32_t p = 0; p < n_pulse; ++p) {
+        if (!((umask >> p) & 1u)) continue;
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const uint64_t b = __ballot((m[j] >> p) & 1u);
+            if (lane == 0) sh.cnt[p][j * 4 + wave] = (uint32_t)__popcll(b);
+        }
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < n_pulse * kRow; k += kThreads) {
+        const int p = k / kRow, e = k % kRow;
+        if (!((umask >> p) & 1u)) continue;
+        uint32_t acc = 0;
+#pragma unroll
+        for (int q = 0; q < kRow; ++q)
+            if (q < e) acc += sh.cnt[p][q];
+        sh.off[p][e] = acc;
+    }
+    __syncthreads();
+}
+
+// Position among the chunk's bit-p slots of this thread's row-j slot.
+template <int EPT>
+__device__ __forceinline__ uint32_t rank_in_chunk(const Ranks<EPT> &sh, int32_t p, int j, bool bit)
+{
+    const uint64_t b = __ballot(bit);
+    return sh.off[p][j * 4 + (threadIdx.x >> 6)] +
+           __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
+
+// Fused coordinate exchange, transposed form (Algorithms 3 and 4): one
+// workgroup per chunk, chunks in zone order (home slots of every domain,
+// then the region of pulse 0, pulse 1, ...). A home chunk never waits (its
+// entries are the independent ones below depOffset); a region chunk waits for
+// the arrival of its region, then forwards it. Each slot is read once and
+// stored, plus coordShift, to every pulse whose bit it carries.
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_push_x(
+    float *x, uint32_t x_bytes, const uint8_t *__restrict__ slot_mask,
+    const halo::Chunk *__restrict__ chunks, const int32_t *__restrict__ dest_start,
+    const float4 *__restrict__ shift4, const uint32_t *__restrict__ x_arrivals, uint32_t *state,
+    int32_t n_dom, int32_t n_pulse, uint32_t epoch, uint32_t spin_limit, uint32_t *err_word,
+    int32_t withhold)
+{
+    __shared__ Ranks<EPT> sh;
+    const halo::Chunk *c = chunks + blockIdx.x;
+    const int32_t first = c->first, count = c->count, D = c->domain;
+    const uint32_t umask = c->mask;
+    const auto rx = make_rsrc(x, x_bytes);
+
+    uint32_t m[EPT], off[EPT];
+    f3v v[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        m[j] = e < count ? (uint32_t)slot_mask[first + e] : 0u;
+        off[j] = e < count ? (uint32_t)(first + e) * 12u : kInvalid;
+    }
+    if (c->zone < 0) {
+        // home slots are final before the launch: load them with the masks
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) v[j] = load3<kPlain>(rx, off[j]);
+    }
+    build_ranks<EPT>(sh, m, umask, n_pulse);
+    if (c->zone >= 0) {
+        // region slots are filled by another domain in this launch
+        halo::wait_one(c->xwait, x_arrivals, state, n_dom * n_pulse, false, epoch, spin_limit,
+                       err_word);
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) v[j] = load3<kShared>(rx, m[j] ? off[j] : kInvalid);
+    }
+    for (int32_t p = 0; p < n_pulse; ++p) {
+        if (!((umask >> p) & 1u)) continue;
+        const int32_t base = dest_start[p * n_dom + D] + c->rank[p];
+        const float4 sh4 = shift4[p * n_dom + D];
+        const f3v s3 = {sh4.x, sh4.y, sh4.z};
+        uint32_t dst[EPT];
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const bool bit = (m[j] >> p) & 1u;
+            const uint32_t r = rank_in_chunk<EPT>(sh, p, j, bit);
+            dst[j] = bit ? (uint32_t)(base + (int32_t)r) * 12u : kInvalid;
+        }
+        if (p + 1 < n_pulse) {
+            // the region may be forwarded by a later pulse of this launch
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) store3<kShared>(rx, dst[j], v[j] + s3);
+        } else {
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) store3<kPlain>(rx, dst[j], v[j] + s3);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    halo::wait_vmem();
+    __syncthreads();
+    if (threadIdx.x < (unsigned)n_pulse && ((umask >> threadIdx.x) & 1u)) {
+        const int32_t seg = (int32_t)threadIdx.x * n_dom + D;
+        if (seg != withhold)
+            __hip_atomic_fetch_add(halo::counter_x(state, seg), 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Fused force exchange, transposed form (Algorithm 6): one workgroup per
+// chunk, regions of later pulses first, home slots last. Every thread keeps
+// the running sum of its target slot in registers and adds the sources of
+// its pulses in strict reverse order; before pulse p it waits until the
+// sources (the receiver's region of pulse p) hold their final sums. Each
+// target slot is read once and written once.
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_pull_f(
+    float *f, uint32_t f_bytes, const uint8_t *__restrict__ slot_mask,
+    const halo::Chunk *__restrict__ chunks, const int32_t *__restrict__ forder,
+    const int32_t *__restrict__ dest_start, const int32_t *__restrict__ send_to,
+    const uint32_t *__restrict__ zone_chunks, uint32_t *state, int32_t n_dom, int32_t n_pulse,
+    uint32_t epoch, uint32_t spin_limit, uint32_t *err_word, int32_t withhold)
+{
+    __shared__ Ranks<EPT> sh;
+    const halo::Chunk *c = chunks + forder[blockIdx.x];
+    const int32_t first = c->first, count = c->count, D = c->domain, zone = c->zone;
+    const uint32_t umask = c->mask;
+    const auto rf = make_rsrc(f, f_bytes);
+    const int32_t n_seg = n_dom * n_pulse;
+
+    uint32_t m[EPT], off[EPT];
+    f3v v[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        m[j] = e < count ? (uint32_t)slot_mask[first + e] : 0u;
+        off[j] = e < count ? (uint32_t)(first + e) * 12u : kInvalid;
+    }
+    // Only this workgroup writes these slots, and nobody before it in this
+    // launch: cached loads, issued together with the masks.
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) v[j] = load3<kPlain>(rf, off[j]);
+    build_ranks<EPT>(sh, m, umask, n_pulse);
+    for (int32_t p = n_pulse - 1; p >= 0; --p) {
+        if (!((umask >> p) & 1u)) continue;
+        const int32_t R = send_to[p * n_dom + D];
+        const int32_t zseg = p * n_dom + R;
+        if (zone_chunks[zseg] > 0)
+            halo::wait_one(zseg, zone_chunks, state, n_seg, true, epoch, spin_limit, err_word);
+        const int32_t base = dest_start[p * n_dom + D] + c->rank[p];
+        uint32_t src[EPT];
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const bool bit = (m[j] >> p) & 1u;
+            const uint32_t r = rank_in_chunk<EPT>(sh, p, j, bit);
+            src[j] = bit ? (uint32_t)(base + (int32_t)r) * 12u : kInvalid;
+        }
+        f3v add[EPT];
+        if (zone_chunks[zseg] > 0) {
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) add[j] = load3<kShared>(rf, src[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) add[j] = load3<kPlain>(rf, src[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < EPT; ++j)
+            if (src[j] != kInvalid) v[j] = v[j] + add[j];
+    }
+    uint32_t dst[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) dst[j] = m[j] ? off[j] : kInvalid;
+    if (zone >= 0) {
+        // region sums are read by another domain in this launch
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) store3<kShared>(rf, dst[j], v[j]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        halo::wait_vmem();
+        __syncthreads();
+        const int32_t seg = zone * n_dom + D;
+        if (threadIdx.x == 0 && seg != withhold)
+            __hip_atomic_fetch_add(halo::counter_f(state, n_seg, seg), 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) store3<kPlain>(rf, dst[j], v[j]);
+    }
+}
+
 // Per-pulse baseline: one launch per pulse, one item per workgroup, no
 // counters; the kernel boundary orders the pulses, so every access is cached.
 template <int EPT>
@@ -324,7 +531,18 @@ struct halo_plan {
     size_t state_words = 0;
     uint32_t *h_err = nullptr;  // pinned host word, written by kernels on a timeout
     uint32_t *d_err = nullptr;  // its device address
-    uint32_t epoch_x = 0, epoch_f = 0;
+    // transposed form
+    uint8_t *d_mask = nullptr;
+    halo::Chunk *d_chunks = nullptr;
+    int32_t *d_forder = nullptr;
+    int32_t *d_dest_start = nullptr;
+    int32_t *d_send_to = nullptr;
+    float *d_shift4 = nullptr;
+    uint32_t *d_x_arrivals = nullptr;
+    uint32_t *d_zone_chunks = nullptr;
+    // epochs: work-item kernels (x, f) and chunk kernels (xc, fc); each family
+    // counts in its own block of state
+    uint32_t epoch_x = 0, epoch_f = 0, epoch_xc = 0, epoch_fc = 0;
     uint32_t spin_limit = 1u << 20;
     int32_t withhold = -1;
 };
@@ -344,6 +562,15 @@ void free_device(halo_plan *p)
     if (p->d_seg_items) (void)hipFree(p->d_seg_items);
     if (p->d_state) (void)hipFree(p->d_state);
     if (p->h_err) (void)hipHostFree(p->h_err);
+    for (void *q : {(void *)p->d_mask, (void *)p->d_chunks, (void *)p->d_forder,
+                    (void *)p->d_dest_start, (void *)p->d_send_to, (void *)p->d_shift4,
+                    (void *)p->d_x_arrivals, (void *)p->d_zone_chunks})
+        if (q) (void)hipFree(q);
+    p->d_mask = nullptr;
+    p->d_chunks = nullptr;
+    p->d_forder = p->d_dest_start = p->d_send_to = nullptr;
+    p->d_shift4 = nullptr;
+    p->d_x_arrivals = p->d_zone_chunks = nullptr;
     p->d_idx = nullptr;
     p->d_items = nullptr;
     p->d_xwaits = nullptr;
@@ -371,14 +598,15 @@ int ept_for(int32_t item_entries)
 
 // Kernel entry points for the plan's items-per-thread.
 struct Kernels {
-    const void *pack_fused, *unpack_fused, *pack_pulse, *unpack_pulse;
+    const void *pack_fused, *unpack_fused, *pack_pulse, *unpack_pulse, *push_x, *pull_f;
 };
 
 template <int EPT>
 Kernels kernels_for()
 {
     return {(const void *)&k_pack_fused<EPT>, (const void *)&k_unpack_fused<EPT>,
-            (const void *)&k_pack_pulse<EPT>, (const void *)&k_unpack_pulse<EPT>};
+            (const void *)&k_pack_pulse<EPT>, (const void *)&k_unpack_pulse<EPT>,
+            (const void *)&k_push_x<EPT>,     (const void *)&k_pull_f<EPT>};
 }
 
 Kernels kernels(int32_t item_entries)
@@ -412,6 +640,29 @@ hipError_t launch_fused(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
     return hipLaunchKernel(k.pack_fused, dim3(n_items), dim3(kThreads), args, 0, s);
 }
 
+// Transposed-form kernels: counters in the second block of state.
+hipError_t launch_chunks(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
+{
+    const halo::HostPlan &h = p->h;
+    int32_t n_dom = h.n_dom, n_pulse = h.n_pulse;
+    uint32_t bytes = (uint32_t)(h.total_slots * 12);
+    uint32_t *state = p->d_state + 2 * h.seg.size() * halo::kCounterStride;
+    const uint32_t n = (uint32_t)h.chunks.size();
+    const Kernels k = kernels(h.chunk_slots);
+    if (force_dir) {
+        uint32_t epoch = p->epoch_fc;
+        void *args[] = {&buf, &bytes, &p->d_mask, &p->d_chunks, &p->d_forder, &p->d_dest_start,
+                        &p->d_send_to, &p->d_zone_chunks, &state, &n_dom, &n_pulse, &epoch,
+                        &p->spin_limit, &p->d_err, &p->withhold};
+        return hipLaunchKernel(k.pull_f, dim3(n), dim3(kThreads), args, 0, s);
+    }
+    uint32_t epoch = p->epoch_xc;
+    void *args[] = {&buf, &bytes, &p->d_mask, &p->d_chunks, &p->d_dest_start, &p->d_shift4,
+                    &p->d_x_arrivals, &state, &n_dom, &n_pulse, &epoch, &p->spin_limit,
+                    &p->d_err, &p->withhold};
+    return hipLaunchKernel(k.push_x, dim3(n), dim3(kThreads), args, 0, s);
+}
+
 hipError_t launch_pulse(halo_plan *p, bool force_dir, float *buf, hipStream_t s, int32_t q)
 {
     const halo::HostPlan &h = p->h;
@@ -438,7 +689,20 @@ halo_status ensure_uploaded(halo_plan *p)
         free_device(p);
         return hip_fail(e, "halo_plan_upload");
     }
-    p->state_words = (size_t)halo::kCountersBegin + 2 * h.seg.size() * halo::kCounterStride;
+    if (h.has_chunks &&
+        ((e = upload_vec(&p->d_mask, h.slot_mask)) != hipSuccess ||
+         (e = upload_vec(&p->d_chunks, h.chunks)) != hipSuccess ||
+         (e = upload_vec(&p->d_forder, h.chunk_forder)) != hipSuccess ||
+         (e = upload_vec(&p->d_dest_start, h.dest_start)) != hipSuccess ||
+         (e = upload_vec(&p->d_send_to, h.send_to)) != hipSuccess ||
+         (e = upload_vec(&p->d_shift4, h.shift4)) != hipSuccess ||
+         (e = upload_vec(&p->d_x_arrivals, h.x_arrivals)) != hipSuccess ||
+         (e = upload_vec(&p->d_zone_chunks, h.zone_chunks)) != hipSuccess)) {
+        free_device(p);
+        return hip_fail(e, "halo_plan_upload");
+    }
+    // two counter blocks (work items, chunks), each X then F, 128 B per counter
+    p->state_words = 4 * h.seg.size() * halo::kCounterStride + halo::kCounterStride;
     if ((e = hipMalloc((void **)&p->d_state, p->state_words * 4)) != hipSuccess ||
         (e = hipMemset(p->d_state, 0, p->state_words * 4)) != hipSuccess ||
         (e = hipHostMalloc((void **)&p->h_err, 64, hipHostMallocMapped)) != hipSuccess ||
@@ -448,7 +712,7 @@ halo_status ensure_uploaded(halo_plan *p)
         return hip_fail(e, "halo_plan_upload");
     }
     std::memset(p->h_err, 0, 64);
-    p->epoch_x = p->epoch_f = 0;
+    p->epoch_x = p->epoch_f = p->epoch_xc = p->epoch_fc = 0;
     p->uploaded = true;
     return HALO_OK;
 }
@@ -502,6 +766,9 @@ halo_status halo_plan_create(const float *positions, int64_t n_atoms, const floa
     } catch (const std::bad_alloc &) {
         rc = halo::kErrNoMem;
         msg = "halo_plan_create: out of host memory";
+    } catch (const std::exception &ex) {
+        rc = halo::kErrArg;
+        msg = std::string("halo_plan_create: internal error: ") + ex.what();
     }
     if (rc != halo::kOk) {
         delete p;
@@ -580,24 +847,64 @@ halo_status halo_plan_upload(halo_plan *p)
     return ensure_uploaded(p);
 }
 
+// The fused defaults take, per direction, the form that measured fastest on
+// the 8x8x8 workload: the index-list kernel for coordinates, the transposed
+// kernel for forces (index-list form when a plan has more than 8 pulses).
 halo_status halo_exchange_x(halo_plan *p, float *x, void *stream)
 {
-    halo_status st = check_exchange(p, x, "halo_exchange_x");
-    if (st != HALO_OK) return st;
-    if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
-    p->epoch_x += 1;
-    hipError_t e = launch_fused(p, false, x, (hipStream_t)stream);
-    return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_x launch");
+    return halo_exchange_x_indexmap(p, x, stream);
 }
 
 halo_status halo_exchange_f(halo_plan *p, float *f, void *stream)
 {
-    halo_status st = check_exchange(p, f, "halo_exchange_f");
+    if (p && !p->h.has_chunks) return halo_exchange_f_indexmap(p, f, stream);
+    return halo_exchange_f_transposed(p, f, stream);
+}
+
+halo_status halo_exchange_x_transposed(halo_plan *p, float *x, void *stream)
+{
+    halo_status st = check_exchange(p, x, "halo_exchange_x_transposed");
+    if (st != HALO_OK) return st;
+    if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
+    if (!p->h.has_chunks)
+        return fail(HALO_ERR_ARG, "halo_exchange_x_transposed: plan has more than 8 pulses");
+    if (p->h.chunks.empty()) return HALO_OK;
+    p->epoch_xc += 1;
+    hipError_t e = launch_chunks(p, false, x, (hipStream_t)stream);
+    return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_x_transposed launch");
+}
+
+halo_status halo_exchange_f_transposed(halo_plan *p, float *f, void *stream)
+{
+    halo_status st = check_exchange(p, f, "halo_exchange_f_transposed");
+    if (st != HALO_OK) return st;
+    if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
+    if (!p->h.has_chunks)
+        return fail(HALO_ERR_ARG, "halo_exchange_f_transposed: plan has more than 8 pulses");
+    if (p->h.chunks.empty()) return HALO_OK;
+    p->epoch_fc += 1;
+    hipError_t e = launch_chunks(p, true, f, (hipStream_t)stream);
+    return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_f_transposed launch");
+}
+
+halo_status halo_exchange_x_indexmap(halo_plan *p, float *x, void *stream)
+{
+    halo_status st = check_exchange(p, x, "halo_exchange_x_indexmap");
+    if (st != HALO_OK) return st;
+    if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
+    p->epoch_x += 1;
+    hipError_t e = launch_fused(p, false, x, (hipStream_t)stream);
+    return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_x_indexmap launch");
+}
+
+halo_status halo_exchange_f_indexmap(halo_plan *p, float *f, void *stream)
+{
+    halo_status st = check_exchange(p, f, "halo_exchange_f_indexmap");
     if (st != HALO_OK) return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
     p->epoch_f += 1;
     hipError_t e = launch_fused(p, true, f, (hipStream_t)stream);
-    return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_f launch");
+    return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_f_indexmap launch");
 }
 
 halo_status halo_exchange_x_pulsewise(halo_plan *p, float *x, void *stream)
@@ -652,7 +959,7 @@ halo_status halo_plan_reset(halo_plan *p)
         (e = hipDeviceSynchronize()) != hipSuccess)
         return hip_fail(e, "halo_plan_reset");
     std::memset(p->h_err, 0, 64);
-    p->epoch_x = p->epoch_f = 0;
+    p->epoch_x = p->epoch_f = p->epoch_xc = p->epoch_fc = 0;
     p->poisoned = false;
     return HALO_OK;
 }

@@ -22,6 +22,8 @@
 #include <atomic>
 #include <cmath>
 #include <limits>
+#include <cstdlib>
+#include <stdexcept>
 #include <thread>
 
 namespace halo {
@@ -46,6 +48,18 @@ void parallel_for(int32_t n, F &&fn)
         });
     for (auto &t : pool) t.join();
 }
+
+}  // namespace
+
+// XCD-aware item order (on by default; HALO_XCD_ORDER=0 turns it off for
+// comparisons).
+bool xcd_ordering_enabled()
+{
+    const char *v = std::getenv("HALO_XCD_ORDER");
+    return !(v && v[0] == '0');
+}
+
+namespace {
 
 struct Cell3 {
     int32_t c[3];
@@ -249,7 +263,35 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
             }
         }
     make_items(P, item_entries);
+    make_chunks(P, item_entries);
     return kOk;
+}
+
+// Reorder the items of one pulse so that the items of domain D sit at
+// positions whose index is D mod 8 (mod 8) where possible. Workgroups of a
+// grid go to the 8 XCDs of an MI355X round-robin, so all pulses of a domain
+// then run on one XCD and re-read its home slots from that XCD's L2. Items of
+// one pulse never wait on each other, so any order within a pulse is valid.
+static void xcd_order(std::vector<WorkItem> &items, size_t begin, int32_t n_dom)
+{
+    constexpr int kXcds = 8;
+    const size_t n = items.size() - begin;
+    std::vector<std::vector<WorkItem>> bucket(kXcds);
+    for (size_t i = begin; i < items.size(); ++i)
+        bucket[(items[i].seg % n_dom) % kXcds].push_back(items[i]);
+    std::vector<size_t> head(kXcds, 0);
+    for (size_t k = 0; k < n; ++k) {
+        int want = (int)((begin + k) % kXcds);
+        if (head[want] == bucket[want].size()) {
+            size_t best = 0;
+            for (int c = 0; c < kXcds; ++c)
+                if (bucket[c].size() - head[c] > best) {
+                    best = bucket[c].size() - head[c];
+                    want = c;
+                }
+        }
+        items[begin + k] = bucket[want][head[want]++];
+    }
 }
 
 void make_items(HostPlan &P, int32_t item_entries)
@@ -311,8 +353,88 @@ void make_items(HostPlan &P, int32_t item_entries)
                 P.items.push_back(it);
             }
         }
+        if (xcd_ordering_enabled()) xcd_order(P.items, (size_t)P.pulse_item_off[p], P.n_dom);
     }
     P.pulse_item_off[P.n_pulse] = (int32_t)P.items.size();
+}
+
+void make_chunks(HostPlan &P, int32_t chunk_slots)
+{
+    P.chunk_slots = chunk_slots;
+    P.chunks.clear();
+    P.chunk_forder.clear();
+    P.has_chunks = P.n_pulse > 0 && P.n_pulse <= kMaxMaskPulses && P.total_slots > 0;
+    if (!P.has_chunks) return;
+    const int32_t nd = P.n_dom, np = P.n_pulse;
+    P.slot_mask.assign((size_t)P.total_slots, 0);
+    P.dest_start.assign((size_t)np * nd, 0);
+    P.send_to.assign((size_t)np * nd, 0);
+    P.shift4.assign((size_t)np * nd * 4, 0.f);
+    P.x_arrivals.assign((size_t)np * nd, 0);
+    P.zone_chunks.assign((size_t)np * nd, 0);
+    for (int32_t p = 0; p < np; ++p)
+        for (int32_t D = 0; D < nd; ++D) {
+            const Segment &s = P.at(p, D);
+            const Segment &r = P.at(p, s.send_to);
+            P.dest_start[(size_t)p * nd + D] = (int32_t)(P.base[s.send_to] + r.atom_offset);
+            P.send_to[(size_t)p * nd + D] = s.send_to;
+            for (int c = 0; c < 3; ++c) P.shift4[((size_t)p * nd + D) * 4 + c] = s.shift[c];
+            for (int32_t i = 0; i < s.send_size; ++i)
+                P.slot_mask[(size_t)(P.base[D] + P.local_map[s.map_off + i])] |= (uint8_t)(1u << p);
+        }
+    // Zones of every domain in slot order: home, then the region of each pulse.
+    // zone_chunks_by_zone[z] collects the chunks of zone z (-1 -> index 0).
+    std::vector<std::vector<Chunk>> by_zone(np + 1);
+    for (int32_t D = 0; D < nd; ++D) {
+        int32_t rank[kMaxMaskPulses] = {0};
+        for (int32_t z = -1; z < np; ++z) {
+            int32_t lo, hi;
+            if (z < 0) {
+                lo = 0;
+                hi = P.n_home[D];
+            } else {
+                lo = P.at(z, D).atom_offset;
+                hi = lo + P.at(z, D).recv_size;
+            }
+            const int32_t len = hi - lo;
+            const int32_t pieces = len > 0 ? (len + chunk_slots - 1) / chunk_slots : 0;
+            for (int32_t k = 0; k < pieces; ++k) {
+                const int32_t a = lo + (int32_t)((int64_t)len * k / pieces);
+                const int32_t b = lo + (int32_t)((int64_t)len * (k + 1) / pieces);
+                Chunk c{};
+                c.first = (int32_t)(P.base[D] + a);
+                c.count = b - a;
+                c.domain = D;
+                c.zone = z;
+                c.mask = 0;
+                for (int32_t q = 0; q < kMaxMaskPulses; ++q) c.rank[q] = rank[q];
+                for (int32_t sl = a; sl < b; ++sl) {
+                    const uint32_t m = P.slot_mask[(size_t)(P.base[D] + sl)];
+                    c.mask |= m;
+                    for (int32_t q = 0; q < np; ++q) rank[q] += (m >> q) & 1u;
+                }
+                c.xwait = z < 0 ? -1 : z * nd + P.at(z, D).recv_from;
+                if (c.mask == 0) continue;  // nothing to send from or add into
+                by_zone[z + 1].push_back(c);
+            }
+        }
+        for (int32_t q = 0; q < np; ++q) {
+            if (rank[q] != P.at(q, D).send_size) throw std::logic_error("mask ranks disagree");
+        }
+    }
+    for (int32_t z = 0; z <= np; ++z)
+        for (const Chunk &c : by_zone[z]) {
+            P.chunks.push_back(c);
+            for (int32_t q = 0; q < np; ++q)
+                if ((c.mask >> q) & 1u) P.x_arrivals[(size_t)q * nd + c.domain] += 1;
+            if (c.zone >= 0) P.zone_chunks[(size_t)c.zone * nd + c.domain] += 1;
+        }
+    // Force direction: regions of later pulses first (their sums feed earlier
+    // pulses), home slots last.
+    std::vector<int32_t> zone_off(np + 2, 0);
+    for (int32_t z = 0; z <= np; ++z) zone_off[z + 1] = zone_off[z] + (int32_t)by_zone[z].size();
+    for (int32_t z = np; z >= 0; --z)
+        for (int32_t i = zone_off[z]; i < zone_off[z + 1]; ++i) P.chunk_forder.push_back(i);
 }
 
 }  // namespace halo

@@ -39,6 +39,24 @@ struct alignas(16) WorkItem {
 };
 static_assert(sizeof(WorkItem) == 64, "WorkItem layout");
 
+// Transposed form of the indexMaps: one chunk = a run of consecutive local
+// slots of one domain inside one zone (the home slots, or the region received
+// in one pulse). For every pulse p the chunk's slots whose mask has bit p are
+// exactly the entries rank[p], rank[p]+1, ... of indexMap_p(domain), in order.
+constexpr int kMaxMaskPulses = 8;
+
+struct alignas(16) Chunk {
+    int32_t first;        // absolute first slot
+    int32_t count;        // slots in the chunk
+    int32_t domain;
+    int32_t zone;         // -1: home slots; r >= 0: region received in pulse r
+    uint32_t mask;        // union of the pulse masks of the chunk's slots
+    int32_t xwait;        // X: segment (r * n_dom + sender) that fills this region; -1 for home
+    int32_t pad[2];
+    int32_t rank[kMaxMaskPulses];  // entries of indexMap_p(domain) before the chunk
+};
+static_assert(sizeof(Chunk) == 64, "Chunk layout");
+
 struct Segment {
     int32_t send_to = 0;
     int32_t send_size = 0;
@@ -80,6 +98,17 @@ struct HostPlan {
     std::vector<int32_t> xwaits;
     std::vector<uint32_t> seg_items;       // items per segment
     std::vector<int32_t> pulse_item_off;   // [n_pulse + 1]
+    // transposed form (only when n_pulse <= kMaxMaskPulses)
+    bool has_chunks = false;
+    int32_t chunk_slots = 0;
+    std::vector<uint8_t> slot_mask;        // per slot: pulses that send it
+    std::vector<Chunk> chunks;             // zone-major: home, region 0, region 1, ...
+    std::vector<int32_t> chunk_forder;     // force-direction order: last region first, home last
+    std::vector<int32_t> dest_start;       // [p][D]: first slot of the receiver's region of pulse p
+    std::vector<int32_t> send_to;          // [p][D]: receiver of D in pulse p
+    std::vector<float> shift4;             // [p][D][4]: coordShift of (p, D)
+    std::vector<uint32_t> x_arrivals;      // [p][D]: chunks of D that send in pulse p
+    std::vector<uint32_t> zone_chunks;     // [r][D]: chunks in region zone r of D
 
     const Segment &at(int32_t p, int32_t d) const { return seg[(size_t)p * n_dom + d]; }
 };
@@ -91,6 +120,12 @@ constexpr int64_t kMaxSlots = ((int64_t)1 << 31) / 12 - 1;
 
 // Status codes shared with halo.h.
 enum : int { kOk = 0, kErrArg = -1, kErrGeometry = -2, kErrRange = -3, kErrNoMem = -7 };
+
+// Whether make_items places the items of one domain on one XCD.
+bool xcd_ordering_enabled();
+
+// Build the transposed form (masks and chunks of at most chunk_slots slots).
+void make_chunks(HostPlan &plan, int32_t chunk_slots);
 
 // Build the plan; returns a status code and a message on failure.
 int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,

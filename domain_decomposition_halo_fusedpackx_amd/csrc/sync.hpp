@@ -35,18 +35,17 @@ namespace halo {
 
 constexpr int kCounterStride = 32;  // uint32 words: one 128-byte line per counter
 
-// State block layout (uint32 words), one allocation per plan: the counters
-// of the coordinate direction, then those of the force direction.
-constexpr int kCountersBegin = 0;
-
+// A counter block holds n_seg counters of the coordinate direction, then
+// n_seg of the force direction. The plan keeps one block per kernel family,
+// each with its own epochs, so that the families never mix their counts.
 __device__ __forceinline__ uint32_t *counter_x(uint32_t *state, int32_t seg)
 {
-    return state + kCountersBegin + (size_t)seg * kCounterStride;
+    return state + (size_t)seg * kCounterStride;
 }
 
 __device__ __forceinline__ uint32_t *counter_f(uint32_t *state, int32_t n_seg, int32_t seg)
 {
-    return state + kCountersBegin + ((size_t)n_seg + seg) * kCounterStride;
+    return state + ((size_t)n_seg + seg) * kCounterStride;
 }
 
 // s_waitcnt with vmcnt(0) only (gfx9 encoding: expcnt and lgkmcnt left at max).
@@ -91,6 +90,29 @@ __device__ __forceinline__ void wait_segments(const int32_t *list, int32_t n, co
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
+        }
+        wait_vmem();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+    __syncthreads();
+}
+
+// The same wait for one segment, polled by lane 0 of wave 0.
+__device__ __forceinline__ void wait_one(int32_t s, const uint32_t *seg_items, uint32_t *state,
+                                         int32_t n_seg, bool force_dir, uint32_t epoch,
+                                         uint32_t spin_limit, uint32_t *err_word)
+{
+    if (threadIdx.x == 0) {
+        uint32_t *ctr = force_dir ? counter_f(state, n_seg, s) : counter_x(state, s);
+        const uint32_t target = epoch * seg_items[s];
+        uint32_t polls = 0;
+        while ((int32_t)(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                         target) < 0) {
+            if (++polls > spin_limit) {
+                __hip_atomic_store(err_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
         }
         wait_vmem();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");

@@ -126,9 +126,10 @@ halo_status halo_plan_upload(halo_plan *plan);
 
 /* Coordinate exchange, Algorithms 3-5 fused into ONE kernel launch on
  * `stream` (a hipStream_t; NULL = default stream). All pulses run at once:
- * the entries of each indexMap below depOffset are packed immediately; entries
- * that forward atoms received in earlier pulses wait, inside the kernel, on
- * the arrival counters of exactly the regions they read.
+ * the entries of each indexMap below depOffset (home slots) are packed
+ * immediately; entries that forward atoms received in earlier pulses wait,
+ * inside the kernel, on the arrival counters of exactly the regions they
+ * read. Runs the index-list form (halo_exchange_x_indexmap).
  *   x : device, total_slots*3 float32, 4-byte aligned. Home slots are read;
  *       every halo slot is overwritten with x[indexMap[i]] + coordShift.
  * Asynchronous; exchanges of one plan must be ordered on one stream. */
@@ -136,13 +137,34 @@ halo_status halo_exchange_x(halo_plan *plan, float *x, void *stream);
 
 /* Force exchange, Algorithm 6 in ONE kernel launch: pulses from last to
  * first; for every sender d of pulse p, f[indexMap[i]] += f[receiver's region
- * of pulse p][i]. A (pulse, domain) waits, inside the kernel, until pulse p+1
- * is finished for itself and for its receiver, which keeps the per-slot order
- * of additions of the serial reverse-pulse loop.
+ * of pulse p][i], with the per-slot order of additions of the serial
+ * reverse-pulse loop, so results are bitwise deterministic. Runs the
+ * transposed form (halo_exchange_f_transposed), or the index-list form when
+ * the plan has more than 8 pulses.
  *   f : device, total_slots*3 float32, updated in place. On return home slots
  *       hold the accumulated forces; forwarding halo slots hold partial sums.
  * Asynchronous; exchanges of one plan must be ordered on one stream. */
 halo_status halo_exchange_f(halo_plan *plan, float *f, void *stream);
+
+/* Index-list form of the fused exchanges: one work item (workgroup) per run
+ * of an indexMap, in pulse-major order (reverse for forces); entries below
+ * depOffset first, the rest after a wait on the (pulse, sender) counters of
+ * the regions they read; forces added with one read-modify-write per entry,
+ * an item waiting until pulse p+1 is finished for its sender and receiver. */
+halo_status halo_exchange_x_indexmap(halo_plan *plan, float *x, void *stream);
+halo_status halo_exchange_f_indexmap(halo_plan *plan, float *f, void *stream);
+
+/* Transposed form of the fused exchanges: the indexMaps stored as one pulse
+ * mask per slot; a workgroup takes a run of slots of one domain inside one
+ * zone (home slots, or the region of one pulse). Coordinates: each slot is
+ * read once and stored, plus coordShift, to every pulse it carries, at the
+ * rank given by a wave-ballot prefix count; region runs wait for their
+ * region to arrive. Forces: each target slot keeps its running sum in a
+ * register and adds its pulses' sources in strict reverse order, waiting
+ * until each source holds its final sum; every target is read and written
+ * once. HALO_ERR_ARG for plans with more than 8 pulses. */
+halo_status halo_exchange_x_transposed(halo_plan *plan, float *x, void *stream);
+halo_status halo_exchange_f_transposed(halo_plan *plan, float *f, void *stream);
 
 /* The same two exchanges as one kernel launch per pulse, with no in-kernel
  * waits: stream order between the launches carries the dependencies (the

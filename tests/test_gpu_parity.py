@@ -54,12 +54,21 @@ def setup_case(oracle_mod, pos, box, grid, rc):
     return plan, o
 
 
+IMPLS = ["fused", "indexmap", "transposed", "pulsewise"]
+
+
+def exchange(plan, impl, direction, buf, stream=None):
+    if impl == "transposed" and plan.num_pulses > 8:
+        impl = "indexmap"  # the transposed form refuses plans with more than 8 pulses
+    name = {"fused": "exchange_{}", "indexmap": "exchange_{}_indexmap",
+            "transposed": "exchange_{}_transposed",
+            "pulsewise": "exchange_{}_pulsewise"}[impl].format(direction)
+    getattr(plan, name)(buf, stream)
+
+
 def run_x(torch, plan, x_host, impl, stream=None):
     x = torch.from_numpy(x_host.copy()).cuda()
-    if impl == "fused":
-        plan.exchange_x(x, stream)
-    else:
-        plan.exchange_x_pulsewise(x, stream)
+    exchange(plan, impl, "x", x, stream)
     torch.cuda.synchronize()
     plan.sync(stream)
     return x.cpu().numpy()
@@ -67,10 +76,7 @@ def run_x(torch, plan, x_host, impl, stream=None):
 
 def run_f(torch, plan, f_host, impl, stream=None):
     f = torch.from_numpy(f_host.copy()).cuda()
-    if impl == "fused":
-        plan.exchange_f(f, stream)
-    else:
-        plan.exchange_f_pulsewise(f, stream)
+    exchange(plan, impl, "f", f, stream)
     torch.cuda.synchronize()
     plan.sync(stream)
     return f.cpu().numpy()
@@ -88,7 +94,7 @@ def check_both(torch, oracle_mod, plan, o, seed, impl, tag):
     assert_bitwise(run_f(torch, plan, f0, impl), want_f, f"{tag} {impl} f")
 
 
-@pytest.mark.parametrize("impl", ["fused", "pulsewise"])
+@pytest.mark.parametrize("impl", IMPLS)
 @pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
 def test_parity_workloads(torch, oracle_mod, wid, impl):
     w = W.WORKLOADS[wid]
@@ -102,7 +108,7 @@ def test_parity_tiny_boxes(torch, oracle_mod, case):
     box, grid, rc, n = case
     pos = W.positions(box, n, 7)
     plan, o = setup_case(oracle_mod, pos, box, grid, rc)
-    for impl in ("fused", "pulsewise"):
+    for impl in IMPLS:
         check_both(torch, oracle_mod, plan, o, 7, impl, "tiny" + "x".join(map(str, grid)))
 
 
@@ -114,7 +120,8 @@ def test_parity_item_sizes(torch, oracle_mod, monkeypatch, wid, entries):
     w = W.WORKLOADS[wid]
     pos = W.workload_positions(w)
     plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
-    check_both(torch, oracle_mod, plan, o, w.seed, "fused", f"{w.name} items={entries}")
+    for impl in ("indexmap", "transposed"):
+        check_both(torch, oracle_mod, plan, o, w.seed, impl, f"{w.name} items={entries}")
 
 
 def test_edge_cases(torch, oracle_mod):
@@ -130,14 +137,13 @@ def test_edge_cases(torch, oracle_mod):
         if o.total_slots == 0:
             say(f"{name}: zero slots, exchanges are no-ops")
             x = torch.zeros((0, 3), device="cuda")
-            plan.exchange_x(x)
-            plan.exchange_f(x)
-            plan.exchange_x_pulsewise(x)
-            plan.exchange_f_pulsewise(x)
+            for impl in IMPLS:
+                exchange(plan, impl, "x", x)
+                exchange(plan, impl, "f", x)
             torch.cuda.synchronize()
             plan.sync()
             continue
-        for impl in ("fused", "pulsewise"):
+        for impl in IMPLS:
             check_both(torch, oracle_mod, plan, o, 9, impl, name)
 
 
@@ -155,18 +161,16 @@ def test_repeats_are_deterministic(torch, oracle_mod, wid):
     x = torch.from_numpy(x0).cuda()
     f_init = torch.from_numpy(f0).cuda()
     f = torch.empty_like(f_init)
-    say(f"{w.name}: 60 alternating fused/pulsewise exchanges")
+    say(f"{w.name}: 90 exchanges, the three implementations interleaved")
     for r in range(30):
-        plan.exchange_x(x)
-        f.copy_(f_init)
-        plan.exchange_f(f)
-        if r % 10 == 9:
-            torch.cuda.synchronize()
-            assert_bitwise(x.cpu().numpy(), want_x, f"repeat {r} x")
-            assert_bitwise(f.cpu().numpy(), want_f, f"repeat {r} f")
-        plan.exchange_x_pulsewise(x)
-        f.copy_(f_init)
-        plan.exchange_f_pulsewise(f)
+        for impl in IMPLS:
+            exchange(plan, impl, "x", x)
+            f.copy_(f_init)
+            exchange(plan, impl, "f", f)
+            if r % 10 == 9:
+                torch.cuda.synchronize()
+                assert_bitwise(x.cpu().numpy(), want_x, f"repeat {r} {impl} x")
+                assert_bitwise(f.cpu().numpy(), want_f, f"repeat {r} {impl} f")
     torch.cuda.synchronize()
     plan.sync()
     assert_bitwise(f.cpu().numpy(), want_f, "final f")
@@ -189,7 +193,8 @@ def test_side_stream(torch, oracle_mod):
     assert_bitwise(x.cpu().numpy(), want, "side stream x")
 
 
-def test_forced_timeout_poisons_and_reset_recovers(torch, oracle_mod):
+@pytest.mark.parametrize("impl", ["indexmap", "transposed"])
+def test_forced_timeout_poisons_and_reset_recovers(torch, oracle_mod, impl):
     """A withheld completion signal makes its dependents hit a tiny spin limit.
 
     Every wait still ends (the limit is small), the kernel drains, the error
@@ -203,35 +208,36 @@ def test_forced_timeout_poisons_and_reset_recovers(torch, oracle_mod):
     want = o.exchange_x(x0.copy())
     x = torch.from_numpy(x0).cuda()
     plan.set_spin_limit(2000)
-    plan.debug_withhold(0)  # z0 of domain 0: the y0 items of domain 4 wait on it
-    say("forced timeout, coordinate direction")
-    plan.exchange_x(x)
+    plan.debug_withhold(0)  # z0 of domain 0: the forwarding of domain 4's z0 region waits on it
+    say(f"forced timeout, coordinate direction, {impl}")
+    exchange(plan, impl, "x", x)
     torch.cuda.synchronize()
     with pytest.raises(HaloError) as e:
         plan.sync()
     assert e.value.code == -5
     with pytest.raises(HaloError) as e:
-        plan.exchange_x(x)
+        exchange(plan, impl, "x", x)
     assert e.value.code == -6
     plan.debug_withhold(-1)
     plan.reset()
     plan.set_spin_limit(1 << 20)
     say("after reset")
     x.copy_(torch.from_numpy(x0))
-    plan.exchange_x(x)
+    exchange(plan, impl, "x", x)
     torch.cuda.synchronize()
     plan.sync()
     assert_bitwise(x.cpu().numpy(), want, "x after reset")
 
-    # force direction: withhold the last pulse of domain 0
+    # force direction: withhold pulse y0 of domain 0 (the force sums of its
+    # y0 region, or its y0 completion, are waited on by z0)
     base, n_home, n_halo = o.domains()
     f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, 1)
     want_f = o.exchange_f(f0.copy())
     f = torch.from_numpy(f0).cuda()
     plan.set_spin_limit(2000)
-    plan.debug_withhold((plan.num_pulses - 1) * plan.num_domains)
-    say("forced timeout, force direction")
-    plan.exchange_f(f)
+    plan.debug_withhold((plan.num_pulses - 2) * plan.num_domains)
+    say(f"forced timeout, force direction, {impl}")
+    exchange(plan, impl, "f", f)
     torch.cuda.synchronize()
     with pytest.raises(HaloError) as e:
         plan.sync()
@@ -240,7 +246,7 @@ def test_forced_timeout_poisons_and_reset_recovers(torch, oracle_mod):
     plan.reset()
     plan.set_spin_limit(1 << 20)
     f.copy_(torch.from_numpy(f0))
-    plan.exchange_f(f)
+    exchange(plan, impl, "f", f)
     torch.cuda.synchronize()
     plan.sync()
     assert_bitwise(f.cpu().numpy(), want_f, "f after reset")
