@@ -111,7 +111,9 @@ def main():
     ap.add_argument("--config", type=int, default=5, help="workload 1..5 (default 5: 8x8x8)")
     ap.add_argument("--replicas", type=int, default=0,
                     help="rotated copies of plan/x/f (0: enough to exceed 2x the 256 MB cache)")
-    ap.add_argument("--impl", choices=["fused", "pulsewise"], default="fused")
+    ap.add_argument("--impl", choices=["fused", "indexmap", "transposed", "pulsewise"],
+                    default="fused", help="fused = the library's defaults (index-list "
+                    "coordinates, transposed forces)")
     ap.add_argument("--no-ablation", action="store_true", help="skip the per-pulse baseline")
     ap.add_argument("--cpu-seconds", type=float, default=3.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -162,8 +164,9 @@ def main():
     torch.cuda.synchronize()
 
     fused = args.impl == "fused"
-    ex_x = (lambda p, x: p.exchange_x(x)) if fused else (lambda p, x: p.exchange_x_pulsewise(x))
-    ex_f = (lambda p, f: p.exchange_f(f)) if fused else (lambda p, f: p.exchange_f_pulsewise(f))
+    suffix = "" if fused else "_" + args.impl
+    ex_x = lambda p, x: getattr(p, "exchange_x" + suffix)(x)  # noqa: E731
+    ex_f = lambda p, f: getattr(p, "exchange_f" + suffix)(f)  # noqa: E731
 
     def step(i):
         r = i % R
@@ -186,9 +189,13 @@ def main():
 
     gbs_x = E * BYTES_X / (ms_x * 1e-3) / 1e9
     gbs_f = E * BYTES_F / (ms_f * 1e-3) / 1e9
-    dom = "f" if ms_f * BYTES_F >= 0 and ms_f >= ms_x else "x"
+    dom = "f" if ms_f >= ms_x else "x"
     sha = kernel_source_sha()
-    kname = ("unpack" if dom == "f" else "pack") + ("_fused" if fused else "_pulsewise")
+    kernel_of = {("fused", "x"): "pack_fused", ("fused", "f"): "pull_f",
+                 ("indexmap", "x"): "pack_fused", ("indexmap", "f"): "unpack_fused",
+                 ("transposed", "x"): "push_x", ("transposed", "f"): "pull_f",
+                 ("pulsewise", "x"): "pack_pulse", ("pulsewise", "f"): "unpack_pulse"}
+    kname = kernel_of[(args.impl, dom)]
     achieved = gbs_f if dom == "f" else gbs_x
     traffic = read_traffic(w.name, kname, sha)
 

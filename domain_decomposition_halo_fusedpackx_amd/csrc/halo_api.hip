@@ -170,13 +170,15 @@ __device__ __forceinline__ void pack_item_fused(const WorkItem *it, __amdgpu_buf
                                                 uint32_t spin_limit, uint32_t *err_word,
                                                 int32_t withhold)
 {
-    if (it->flags & halo::kItemXStoreShared)
+    if (it->flags & halo::kItemXStoreShared) {
         pack_item_fused_st<EPT, kShared>(it, rx, ridx, xwaits, seg_items, state, n_seg, epoch,
                                          spin_limit, err_word);
-    else
+        halo::signal_done(halo::counter_x(state, it->seg), it->seg == withhold);
+    } else {
+        // last pulse: no later pulse forwards its region, nobody waits on it
         pack_item_fused_st<EPT, kPlain>(it, rx, ridx, xwaits, seg_items, state, n_seg, epoch,
                                         spin_limit, err_word);
-    halo::signal_done(halo::counter_x(state, it->seg), it->seg == withhold);
+    }
 }
 
 // f[idx[map_begin + e]] += f[region_begin + e] for e < n; the index loads were
@@ -241,7 +243,9 @@ __device__ __forceinline__ void unpack_item_fused(const WorkItem *it, __amdgpu_b
         else
             unpack_span<EPT, kPlain, kPlain>(rf, tgt, region_begin, n_total);
     }
-    halo::signal_done(halo::counter_f(state, n_seg, it->seg), it->seg == withhold);
+    // pulse 0 runs last: nobody waits on its completion
+    if (fl & halo::kItemFStoreShared)
+        halo::signal_done(halo::counter_f(state, n_seg, it->seg), it->seg == withhold);
 }
 
 // ---- kernels -----------------------------------------------------------------
@@ -389,22 +393,23 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
             dst[j] = bit ? (uint32_t)(base + (int32_t)r) * 12u : kInvalid;
         }
         if (p + 1 < n_pulse) {
-            // the region may be forwarded by a later pulse of this launch
+            // the region may be forwarded by a later pulse of this launch:
+            // store coherently and signal its arrival as soon as it is
+            // complete, before the stores of later pulses
 #pragma unroll
             for (int j = 0; j < EPT; ++j) store3<kShared>(rx, dst[j], v[j] + s3);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            halo::wait_vmem();
+            __syncthreads();
+            const int32_t seg = p * n_dom + D;
+            if (threadIdx.x == 0 && seg != withhold)
+                __hip_atomic_fetch_add(halo::counter_x(state, seg), 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
         } else {
+            // last pulse: nobody forwards this region, nobody waits on it
 #pragma unroll
             for (int j = 0; j < EPT; ++j) store3<kPlain>(rx, dst[j], v[j] + s3);
         }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    halo::wait_vmem();
-    __syncthreads();
-    if (threadIdx.x < (unsigned)n_pulse && ((umask >> threadIdx.x) & 1u)) {
-        const int32_t seg = (int32_t)threadIdx.x * n_dom + D;
-        if (seg != withhold)
-            __hip_atomic_fetch_add(halo::counter_x(state, seg), 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -294,6 +294,68 @@ static void xcd_order(std::vector<WorkItem> &items, size_t begin, int32_t n_dom)
     }
 }
 
+// Work items of the index-list kernels. Every segment (pulse p, sender D) is
+// cut into items of at most item_entries entries, separately for its
+// independent span (entries below depOffset) and its dependent span, and
+// every segment has at least one item (its counter must advance). Launch
+// order, which is also the dependency order: for every pulse the independent
+// items, then the dependent ones; for the last pulse, whose completion nobody
+// waits for, the dependent items come first and its independent bulk last,
+// so that the forwarding chain meets less memory traffic.
+static void cut_span(HostPlan &P, int32_t p, int32_t D, int32_t lo, int32_t hi,
+                     int32_t item_entries, bool keep_empty)
+{
+    Segment &s = P.seg[(size_t)p * P.n_dom + D];
+    const Segment &rs = P.at(p, s.send_to);
+    const int32_t len = hi - lo;
+    int32_t n = (len + item_entries - 1) / item_entries;
+    if (n == 0 && keep_empty) n = 1;
+    for (int32_t j = 0; j < n; ++j) {
+        const int32_t b = lo + (int32_t)((int64_t)len * j / n);
+        const int32_t e = lo + (int32_t)((int64_t)len * (j + 1) / n);
+        WorkItem it{};
+        it.map_begin = (int32_t)(s.map_off + b);
+        it.n_total = e - b;
+        it.n_indep = std::min(std::max(s.dep_start - b, 0), it.n_total);
+        it.region_begin = (int32_t)(P.base[s.send_to] + rs.atom_offset + b);
+        for (int c = 0; c < 3; ++c) it.shift[c] = s.shift[c];
+        it.seg = p * P.n_dom + D;
+        // Coordinate direction: wait for exactly the regions that the
+        // dependent entries read (each was filled by one sender in an
+        // earlier pulse).
+        it.xwait_begin = (int32_t)P.xwaits.size();
+        int32_t last_r = -1;
+        for (int32_t i = b + it.n_indep; i < e; ++i) {
+            const int32_t slot = P.local_map[s.map_off + i];
+            int32_t r = last_r < 0 ? 0 : last_r;
+            while (r < p && !(slot >= P.at(r, D).atom_offset &&
+                              slot < P.at(r, D).atom_offset + P.at(r, D).recv_size))
+                ++r;
+            if (r < p && r != last_r) {
+                P.xwaits.push_back(r * P.n_dom + P.at(r, D).recv_from);
+                last_r = r;
+            }
+        }
+        it.xwait_count = (int32_t)P.xwaits.size() - it.xwait_begin;
+        // Force direction: pulse p+1 finished for D and for its receiver.
+        it.fwait[0] = it.fwait[1] = -1;
+        if (p + 1 < P.n_pulse) {
+            it.fwait[0] = (p + 1) * P.n_dom + D;
+            it.fwait[1] = (p + 1) * P.n_dom + s.send_to;
+        }
+        // Regions of every pulse but the last are candidates of a later
+        // pulse; in the force direction the last pulse runs first (reads
+        // untouched slots) and pulse 0 runs last (its sums are read by nobody
+        // in the same launch).
+        it.flags = 0;
+        if (p + 1 < P.n_pulse) it.flags |= kItemXStoreShared | kItemFLoadShared;
+        if (p > 0) it.flags |= kItemFStoreShared;
+        P.items.push_back(it);
+        s.n_items += 1;
+        P.seg_items[(size_t)p * P.n_dom + D] += 1;
+    }
+}
+
 void make_items(HostPlan &P, int32_t item_entries)
 {
     P.item_entries = item_entries;
@@ -301,59 +363,27 @@ void make_items(HostPlan &P, int32_t item_entries)
     P.xwaits.clear();
     P.seg_items.assign(P.seg.size(), 0);
     P.pulse_item_off.assign(P.n_pulse + 1, 0);
+    for (auto &s : P.seg) {
+        s.n_items = 0;
+        s.item_off = 0;
+    }
     for (int32_t p = 0; p < P.n_pulse; ++p) {
         P.pulse_item_off[p] = (int32_t)P.items.size();
-        for (int32_t D = 0; D < P.n_dom; ++D) {
-            Segment &s = P.seg[(size_t)p * P.n_dom + D];
-            const Segment &rs = P.at(p, s.send_to);
-            const int32_t n = std::max<int32_t>(1, (s.send_size + item_entries - 1) / item_entries);
-            s.item_off = (int32_t)P.items.size();
-            s.n_items = n;
-            P.seg_items[(size_t)p * P.n_dom + D] = (uint32_t)n;
-            for (int32_t j = 0; j < n; ++j) {
-                const int32_t b = (int32_t)((int64_t)s.send_size * j / n);
-                const int32_t e = (int32_t)((int64_t)s.send_size * (j + 1) / n);
-                WorkItem it{};
-                it.map_begin = (int32_t)(s.map_off + b);
-                it.n_total = e - b;
-                it.n_indep = std::min(std::max(s.dep_start - b, 0), it.n_total);
-                it.region_begin = (int32_t)(P.base[s.send_to] + rs.atom_offset + b);
-                for (int c = 0; c < 3; ++c) it.shift[c] = s.shift[c];
-                it.seg = p * P.n_dom + D;
-                // Coordinate direction: wait for exactly the regions that the
-                // dependent entries read (each was filled by one sender in an
-                // earlier pulse).
-                it.xwait_begin = (int32_t)P.xwaits.size();
-                int32_t last_r = -1;
-                for (int32_t i = b + it.n_indep; i < e; ++i) {
-                    const int32_t slot = P.local_map[s.map_off + i];
-                    int32_t r = last_r < 0 ? 0 : last_r;
-                    while (r < p && !(slot >= P.at(r, D).atom_offset &&
-                                      slot < P.at(r, D).atom_offset + P.at(r, D).recv_size))
-                        ++r;
-                    if (r < p && r != last_r) {
-                        P.xwaits.push_back(r * P.n_dom + P.at(r, D).recv_from);
-                        last_r = r;
-                    }
-                }
-                it.xwait_count = (int32_t)P.xwaits.size() - it.xwait_begin;
-                // Force direction: pulse p+1 finished for D and for its receiver.
-                it.fwait[0] = it.fwait[1] = -1;
-                if (p + 1 < P.n_pulse) {
-                    it.fwait[0] = (p + 1) * P.n_dom + D;
-                    it.fwait[1] = (p + 1) * P.n_dom + s.send_to;
-                }
-                // Regions of every pulse but the last are candidates of a
-                // later pulse; in the force direction the last pulse runs
-                // first (reads untouched slots) and pulse 0 runs last (its
-                // sums are read by nobody in the same launch).
-                it.flags = 0;
-                if (p + 1 < P.n_pulse) it.flags |= kItemXStoreShared | kItemFLoadShared;
-                if (p > 0) it.flags |= kItemFStoreShared;
-                P.items.push_back(it);
+        const bool last = p + 1 == P.n_pulse;
+        for (int pass = 0; pass < 2; ++pass) {
+            const bool indep = (pass == 0) != last;
+            const size_t group = P.items.size();
+            for (int32_t D = 0; D < P.n_dom; ++D) {
+                const Segment &s = P.seg[(size_t)p * P.n_dom + D];
+                // an empty segment keeps one (empty) item in its first group
+                const bool keep_empty = s.send_size == 0 && pass == 0;
+                if (indep)
+                    cut_span(P, p, D, 0, s.dep_start, item_entries, keep_empty);
+                else
+                    cut_span(P, p, D, s.dep_start, s.send_size, item_entries, keep_empty);
             }
+            if (xcd_ordering_enabled()) xcd_order(P.items, group, P.n_dom);
         }
-        if (xcd_ordering_enabled()) xcd_order(P.items, (size_t)P.pulse_item_off[p], P.n_dom);
     }
     P.pulse_item_off[P.n_pulse] = (int32_t)P.items.size();
 }

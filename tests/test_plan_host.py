@@ -89,7 +89,8 @@ def test_position_errors_match_oracle(oracle_mod, bad):
 
 
 def test_item_cutting(monkeypatch):
-    """Work items cover every entry once, with at least one per (pulse, domain)."""
+    """Work items cut the independent and the dependent span of every
+    (pulse, domain) separately, with at least one item per (pulse, domain)."""
     w = W.WORKLOADS[4]
     pos = W.workload_positions(w)
     for n in (64, 300, 1024, 2048):
@@ -99,6 +100,7 @@ def test_item_cutting(monkeypatch):
         for p in range(plan.num_pulses):
             for d in range(plan.num_domains):
                 q = plan.pulse(p, d)
-                assert q["items"] == max(1, -(-q["send_size"] // n))
+                dep = q["send_size"] - q["dep_start"]
+                assert q["items"] == max(1, -(-q["dep_start"] // n) + -(-dep // n))
                 tot += q["items"]
         assert tot == plan.num_items
