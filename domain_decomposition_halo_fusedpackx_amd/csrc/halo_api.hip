@@ -54,7 +54,8 @@ halo_status fail(halo_status st, const std::string &msg)
 // below 2 GiB so that it is never in range.
 typedef float f3v __attribute__((ext_vector_type(3)));
 constexpr uint32_t kInvalid = 0x80000000u;
-constexpr int kPlain = 0;      // cached access
+constexpr int kPlain = 0;      // cached: data another access of this XCD may reuse
+constexpr int kStream = 2;     // nt: touched once in this launch, streamed past the caches
 constexpr int kShared = 16;    // sc1: agent-coherent access, bypasses the XCD-private caches
 constexpr int32_t kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
 
@@ -79,7 +80,7 @@ __device__ __forceinline__ void store3(__amdgpu_buffer_rsrc_t r, uint32_t byte_o
 // branch separates the loads of one thread).
 __device__ __forceinline__ uint32_t load_index(__amdgpu_buffer_rsrc_t r, int32_t e, bool ok)
 {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, ok ? (uint32_t)e * 4u : kInvalid, 0, kPlain);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, ok ? (uint32_t)e * 4u : kInvalid, 0, kStream);
 }
 
 // Gather x[idx[map_begin + e]] + shift and store it at slot region_begin + e,
@@ -176,7 +177,7 @@ __device__ __forceinline__ void pack_item_fused(const WorkItem *it, __amdgpu_buf
         halo::signal_done(halo::counter_x(state, it->seg), it->seg == withhold);
     } else {
         // last pulse: no later pulse forwards its region, nobody waits on it
-        pack_item_fused_st<EPT, kPlain>(it, rx, ridx, xwaits, seg_items, state, n_seg, epoch,
+        pack_item_fused_st<EPT, kStream>(it, rx, ridx, xwaits, seg_items, state, n_seg, epoch,
                                         spin_limit, err_word);
     }
 }
@@ -236,12 +237,12 @@ __device__ __forceinline__ void unpack_item_fused(const WorkItem *it, __amdgpu_b
         if (fl & halo::kItemFStoreShared)
             unpack_span<EPT, kShared, kShared>(rf, tgt, region_begin, n_total);
         else
-            unpack_span<EPT, kShared, kPlain>(rf, tgt, region_begin, n_total);
+            unpack_span<EPT, kShared, kStream>(rf, tgt, region_begin, n_total);
     } else {
         if (fl & halo::kItemFStoreShared)
-            unpack_span<EPT, kPlain, kShared>(rf, tgt, region_begin, n_total);
+            unpack_span<EPT, kStream, kShared>(rf, tgt, region_begin, n_total);
         else
-            unpack_span<EPT, kPlain, kPlain>(rf, tgt, region_begin, n_total);
+            unpack_span<EPT, kStream, kStream>(rf, tgt, region_begin, n_total);
     }
     // pulse 0 runs last: nobody waits on its completion
     if (fl & halo::kItemFStoreShared)
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
     if (c->zone < 0) {
         // home slots are final before the launch: load them with the masks
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) v[j] = load3<kPlain>(rx, off[j]);
+        for (int j = 0; j < EPT; ++j) v[j] = load3<kStream>(rx, off[j]);
     }
     build_ranks<EPT>(sh, m, umask, n_pulse);
     if (c->zone >= 0) {
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
         } else {
             // last pulse: nobody forwards this region, nobody waits on it
 #pragma unroll
-            for (int j = 0; j < EPT; ++j) store3<kPlain>(rx, dst[j], v[j] + s3);
+            for (int j = 0; j < EPT; ++j) store3<kStream>(rx, dst[j], v[j] + s3);
         }
     }
 }
@@ -445,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
     // Only this workgroup writes these slots, and nobody before it in this
     // launch: cached loads, issued together with the masks.
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) v[j] = load3<kPlain>(rf, off[j]);
+    for (int j = 0; j < EPT; ++j) v[j] = load3<kStream>(rf, off[j]);
     build_ranks<EPT>(sh, m, umask, n_pulse);
     for (int32_t p = n_pulse - 1; p >= 0; --p) {
         if (!((umask >> p) & 1u)) continue;
@@ -467,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
             for (int j = 0; j < EPT; ++j) add[j] = load3<kShared>(rf, src[j]);
         } else {
 #pragma unroll
-            for (int j = 0; j < EPT; ++j) add[j] = load3<kPlain>(rf, src[j]);
+            for (int j = 0; j < EPT; ++j) add[j] = load3<kStream>(rf, src[j]);
         }
 #pragma unroll
         for (int j = 0; j < EPT; ++j)
@@ -489,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
                                    __HIP_MEMORY_SCOPE_AGENT);
     } else {
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) store3<kPlain>(rf, dst[j], v[j]);
+        for (int j = 0; j < EPT; ++j) store3<kStream>(rf, dst[j], v[j]);
     }
 }
 
