@@ -191,7 +191,8 @@ def main():
     gbs_f = E * BYTES_F / (ms_f * 1e-3) / 1e9
     dom = "f" if ms_f >= ms_x else "x"
     sha = kernel_source_sha()
-    kernel_of = {("fused", "x"): "pack_fused", ("fused", "f"): "pull_f",
+    f_default = "pull_f" if E >= (1 << 18) else "unpack_fused"
+    kernel_of = {("fused", "x"): "pack_fused", ("fused", "f"): f_default,
                  ("indexmap", "x"): "pack_fused", ("indexmap", "f"): "unpack_fused",
                  ("transposed", "x"): "push_x", ("transposed", "f"): "pull_f",
                  ("pulsewise", "x"): "pack_pulse", ("pulsewise", "f"): "unpack_pulse"}
@@ -226,14 +227,22 @@ def main():
     }
 
     if fused and not args.no_ablation:
-        log("per-pulse baseline")
-        ms_px = time_loop(torch, lambda i: plans[i % R].exchange_x_pulsewise(xs[i % R]),
-                          args.steps)
-        ms_pf = time_loop(torch, lambda i: plans[i % R].exchange_f_pulsewise(fs[i % R]),
-                          args.steps)
-        out["pulsewise"] = {"us_x": ms_px * 1e3, "us_f": ms_pf * 1e3,
-                            "launches_per_exchange": plan0.num_pulses,
-                            "speedup_fused_x": ms_px / ms_x, "speedup_fused_f": ms_pf / ms_f}
+        # the other forms of the same two exchanges, same replicas
+        forms = {}
+        for form in ("indexmap", "transposed", "pulsewise"):
+            log(f"form {form}")
+            fx = getattr(HaloPlan, "exchange_x_" + form)
+            ff = getattr(HaloPlan, "exchange_f_" + form)
+            ux = time_loop(torch, lambda i: fx(plans[i % R], xs[i % R]), args.steps) * 1e3
+            uf = time_loop(torch, lambda i: ff(plans[i % R], fs[i % R]), args.steps) * 1e3
+            forms[form] = {"us_x": ux, "us_f": uf,
+                           "launches_per_exchange": plan0.num_pulses if form == "pulsewise" else 1}
+        for p in plans:
+            p.sync()
+        out["forms"] = forms
+        out["pulsewise"] = dict(forms["pulsewise"],
+                                speedup_fused_x=forms["pulsewise"]["us_x"] / (ms_x * 1e3),
+                                speedup_fused_f=forms["pulsewise"]["us_f"] / (ms_f * 1e3))
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

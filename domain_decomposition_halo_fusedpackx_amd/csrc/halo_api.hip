@@ -853,9 +853,12 @@ halo_status halo_plan_upload(halo_plan *p)
     return ensure_uploaded(p);
 }
 
-// The fused defaults take, per direction, the form that measured fastest on
-// the 8x8x8 workload: the index-list kernel for coordinates, the transposed
-// kernel for forces (index-list form when a plan has more than 8 pulses).
+// The fused defaults take, per direction, the form that measured fastest:
+// the index-list kernel for coordinates at every size; for forces the
+// transposed kernel from 2^18 entries up (4x4x4 and 8x8x8 boxes), the
+// index-list kernel below that and for plans with more than 8 pulses.
+constexpr int64_t kTransposedForceMinEntries = 1 << 18;
+
 halo_status halo_exchange_x(halo_plan *p, float *x, void *stream)
 {
     return halo_exchange_x_indexmap(p, x, stream);
@@ -863,7 +866,8 @@ halo_status halo_exchange_x(halo_plan *p, float *x, void *stream)
 
 halo_status halo_exchange_f(halo_plan *p, float *f, void *stream)
 {
-    if (p && !p->h.has_chunks) return halo_exchange_f_indexmap(p, f, stream);
+    if (p && (!p->h.has_chunks || (int64_t)p->h.abs_map.size() < kTransposedForceMinEntries))
+        return halo_exchange_f_indexmap(p, f, stream);
     return halo_exchange_f_transposed(p, f, stream);
 }
 
