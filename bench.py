@@ -32,6 +32,7 @@ HBM_PEAK_GBS = 8000.0
 BYTES_X = 28  # per entry: 4 B index + 12 B gathered source + 12 B store
 BYTES_F = 40  # per entry: 4 B index + 12 B region read + 12 B target read + 12 B target write
 MALL_BYTES = 256 << 20
+MAX_REPLICAS = 128
 KERNEL_SOURCES = ["domain_decomposition_halo_fusedpackx_amd/csrc/halo_api.hip",
                   "domain_decomposition_halo_fusedpackx_amd/csrc/sync.hpp"]
 
@@ -75,18 +76,24 @@ def cpu_baseline(w, pos, seconds: float):
     x = o.home_filled(np.nan)
     base, n_home, n_halo = o.domains()
     f = W.halo_forces(o.total_slots, base, n_home, n_halo, w.seed)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        o.exchange_x(x)
-        o.exchange_f(f)
-        reps += 1
-        el = time.perf_counter() - t0
-        if (el >= seconds and reps >= 3) or reps >= 10000:
-            break
-    return {"value": entries * reps / el, "unit": "halo atoms/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole {w.name} workload ({entries} halo entries), {reps} steps of one "
-                      f"coordinate + one force exchange, serial C (gcc -O2), 1 thread, "
-                      f"{el:.2f} s",
+
+    def timed(fn, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if (el >= budget and reps >= 3) or reps >= 10000:
+                return reps, el
+
+    rx, tx = timed(lambda: o.exchange_x(x), seconds / 2)
+    rf, tf = timed(lambda: o.exchange_f(f), seconds / 2)
+    us_x, us_f = tx / rx * 1e6, tf / rf * 1e6
+    return {"value": entries / ((us_x + us_f) * 1e-6), "unit": "halo atoms/s", "cores": 1,
+            "kind": "oracle", "us_per_exchange": {"x": us_x, "f": us_f},
+            "sample": f"whole {w.name} workload ({entries} halo entries): {rx} coordinate "
+                      f"exchanges in {tx:.2f} s, then {rf} force exchanges in {tf:.2f} s; "
+                      f"serial C (gcc -O2), 1 thread",
             "host_cpus": os.cpu_count(), "host_cpu": platform.processor() or platform.machine()}
 
 
@@ -103,6 +110,114 @@ def time_loop(torch, fn, n):
     return e0.elapsed_time(e1) / n  # ms
 
 
+def launch_floor_us(torch, n):
+    """Back-to-back launches of a one-element kernel on the same stream
+    (after a warm-up that loads the kernel)."""
+    t = torch.zeros(1, device="cuda")
+    for _ in range(20):
+        t.add_(1.0)
+    return time_loop(torch, lambda i: t.add_(1.0), n) * 1e3
+
+
+def host_call_us(torch, fn, n):
+    """Host time to issue one call (no synchronisation inside the loop): when
+    it exceeds the GPU time of the call, back-to-back timings measure the
+    host, not the kernel."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        fn(i)
+    el = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    return el / n * 1e6
+
+
+def cold_exchange_us(torch, plan, x, f, f_init, suffix, reps):
+    """Median time of one exchange per direction with cold caches: before each
+    timed exchange a 1 GiB device write evicts L2 and the 256 MB cache (the
+    force array is restored before that write)."""
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    ex_x = getattr(plan, "exchange_x" + suffix)
+    ex_f = getattr(plan, "exchange_f" + suffix)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(2 * reps)]
+    for r in range(reps):
+        scratch.fill_(float(r))
+        ev[2 * r][0].record(s)
+        ex_x(x)
+        ev[2 * r][1].record(s)
+        f.copy_(f_init)
+        scratch.fill_(float(r) + 0.5)
+        ev[2 * r + 1][0].record(s)
+        ex_f(f)
+        ev[2 * r + 1][1].record(s)
+    torch.cuda.synchronize()
+    plan.sync()
+    tx = [ev[2 * r][0].elapsed_time(ev[2 * r][1]) * 1e3 for r in range(reps)]
+    tf = [ev[2 * r + 1][0].elapsed_time(ev[2 * r + 1][1]) * 1e3 for r in range(reps)]
+    del scratch
+    return {"us_x": float(np.median(tx)), "us_f": float(np.median(tf))}
+
+
+def overlap(torch, plan, x, f, reps):
+    """The pages' overlap measurement with a synthetic local workload.
+
+    Local work: a bf16 GEMM (4096 x 4096 by 4096 x 2048) on its own stream,
+    standing in for the local non-bonded kernel. Non-local work: the
+    coordinate exchange followed by the force exchange on the launch stream.
+    Both start together after a common event. Local = start to end of the GEMM;
+    non-local = start of the coordinate exchange to end of the force exchange;
+    non-overlap = end of the GEMM to end of the force exchange, clamped at 0.
+    Medians over reps; the same quantities with each side alone for
+    reference."""
+    a = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(4096, 2048, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(4096, 2048, device="cuda", dtype=torch.bfloat16)
+    main = torch.cuda.current_stream()
+    loc = torch.cuda.Stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def run(do_local, do_nonlocal):
+        rec = []
+        for _ in range(reps):
+            go, l0, l1, n0, n1 = ev(), ev(), ev(), ev(), ev()
+            go.record(main)
+            loc.wait_event(go)
+            if do_local:
+                l0.record(loc)
+                with torch.cuda.stream(loc):
+                    torch.mm(a, b, out=c)
+                l1.record(loc)
+            if do_nonlocal:
+                n0.record(main)
+                plan.exchange_x(x)
+                plan.exchange_f(f)
+                n1.record(main)
+            main.wait_stream(loc)
+            rec.append((l0, l1, n0, n1))
+        torch.cuda.synchronize()
+        plan.sync()
+        out = {}
+        if do_local:
+            out["local_us"] = float(np.median([l0.elapsed_time(l1) for l0, l1, _, _ in rec])) * 1e3
+        if do_nonlocal:
+            out["nonlocal_us"] = float(np.median([n0.elapsed_time(n1) for _, _, n0, n1 in rec])) * 1e3
+        if do_local and do_nonlocal:
+            out["non_overlap_us"] = float(np.median(
+                [max(0.0, l1.elapsed_time(n1)) for _, l1, _, n1 in rec])) * 1e3
+        return out
+
+    run(True, True)  # warm-up
+    alone_l, alone_n, both = run(True, False), run(False, True), run(True, True)
+    return {"local_work": "bf16 GEMM 4096x4096 @ 4096x2048 on a second stream",
+            "nonlocal_work": "halo_exchange_x + halo_exchange_f",
+            "local_alone_us": alone_l["local_us"], "nonlocal_alone_us": alone_n["nonlocal_us"],
+            **both, "reps": reps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,8 +230,12 @@ def main():
                     default="fused", help="fused = the library's defaults (index-list "
                     "coordinates, transposed forces)")
     ap.add_argument("--no-ablation", action="store_true", help="skip the per-pulse baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=3.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time budget of the oracle baseline (split over both directions)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=50)
+    ap.add_argument("--no-overlap", action="store_true")
+    ap.add_argument("--overlap-reps", type=int, default=50)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device 3 times (a plain copy kernel of "
                          "known size, for scaling hardware byte counters)")
@@ -151,7 +270,9 @@ def main():
     E = plan0.num_entries
     S = plan0.total_slots
     per_rep_bytes = S * 12 + E * 4
-    R = args.replicas or max(1, -(-2 * MALL_BYTES // per_rep_bytes))
+    # Small workloads are capped at MAX_REPLICAS: their whole footprint then
+    # stays in the 256 MB cache, as it would in a real run.
+    R = args.replicas or min(MAX_REPLICAS, max(1, -(-2 * MALL_BYTES // per_rep_bytes)))
     log(f"entries={E} slots={S} items={plan0.num_items} replicas={R}")
     plans = [plan0] + [HaloPlan(pos, w.box, w.grid, w.cutoff) for _ in range(R - 1)]
     x_home = torch.from_numpy(plan0.home_filled(pos, 0.0)).cuda()
@@ -229,20 +350,34 @@ def main():
     if fused and not args.no_ablation:
         # the other forms of the same two exchanges, same replicas
         forms = {}
-        for form in ("indexmap", "transposed", "pulsewise"):
+        for form in ("indexmap", "transposed", "pulsewise", "staged", "atomic"):
             log(f"form {form}")
-            fx = getattr(HaloPlan, "exchange_x_" + form)
+            fx = getattr(HaloPlan, "exchange_x_" + form, None)
             ff = getattr(HaloPlan, "exchange_f_" + form)
-            ux = time_loop(torch, lambda i: fx(plans[i % R], xs[i % R]), args.steps) * 1e3
+            ux = (time_loop(torch, lambda i: fx(plans[i % R], xs[i % R]), args.steps) * 1e3
+                  if fx else None)
             uf = time_loop(torch, lambda i: ff(plans[i % R], fs[i % R]), args.steps) * 1e3
-            forms[form] = {"us_x": ux, "us_f": uf,
-                           "launches_per_exchange": plan0.num_pulses if form == "pulsewise" else 1}
+            launches = {"pulsewise": plan0.num_pulses, "staged": 2 * plan0.num_pulses}
+            forms[form] = {"us_x": ux, "us_f": uf, "launches_per_exchange": launches.get(form, 1)}
         for p in plans:
             p.sync()
         out["forms"] = forms
         out["pulsewise"] = dict(forms["pulsewise"],
                                 speedup_fused_x=forms["pulsewise"]["us_x"] / (ms_x * 1e3),
                                 speedup_fused_f=forms["pulsewise"]["us_f"] / (ms_f * 1e3))
+        out["launch_floor_us"] = launch_floor_us(torch, args.steps)
+        out["host_us_per_call"] = {
+            "x": host_call_us(torch, lambda i: ex_x(plans[i % R], xs[i % R]), args.steps),
+            "f": host_call_us(torch, lambda i: ex_f(plans[i % R], fs[i % R]), args.steps)}
+        log("cold exchanges")
+        out["cold"] = {form: cold_exchange_us(torch, plans[0], xs[0], fs[0], f_init, suffix,
+                                              args.cold_reps)
+                       for form, suffix in (("fused", ""), ("pulsewise", "_pulsewise"))}
+        out["cold"]["method"] = (f"median of {args.cold_reps} single exchanges, each after a 1 GiB "
+                                 f"device write that evicts L2 and the 256 MB cache")
+        if not args.no_overlap:
+            log("overlap with local work")
+            out["overlap"] = overlap(torch, plans[0], xs[0], fs[0], args.overlap_reps)
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

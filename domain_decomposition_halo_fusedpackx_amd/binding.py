@@ -45,6 +45,9 @@ SIGNATURES = {
     "halo_exchange_f_transposed": (_st, [_vp, _vp, _vp]),
     "halo_exchange_x_pulsewise": (_st, [_vp, _vp, _vp]),
     "halo_exchange_f_pulsewise": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_f_atomic": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_x_staged": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_f_staged": (_st, [_vp, _vp, _vp]),
     "halo_plan_sync": (_st, [_vp, _vp]),
     "halo_plan_reset": (_st, [_vp]),
     "halo_plan_set_spin_limit": (_st, [_vp, _u32]),
@@ -93,10 +96,14 @@ def _np_ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _stream_handle(stream):
+def _stream_handle(stream, device: int = -1):
+    """HIP stream handle: the caller's stream object or raw handle, else torch's
+    current stream on `device` (the buffer's device)."""
     if stream is None:
         import torch
-        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if device < 0:
+            device = torch.cuda.current_device()
+        return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(device))
     if isinstance(stream, int):
         return ctypes.c_void_p(stream)
     return ctypes.c_void_p(stream.cuda_stream)
@@ -175,6 +182,7 @@ class HaloPlan:
 
     # -- device side ------------------------------------------------------------
     def _buf(self, t):
+        """Validate an exchange buffer; returns (pointer, device index)."""
         import torch
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise TypeError("exchange buffers must be torch.cuda tensors")
@@ -183,42 +191,50 @@ class HaloPlan:
         if t.numel() != 3 * self.total_slots:
             raise ValueError(f"buffer holds {t.numel()} floats, the plan needs "
                              f"{3 * self.total_slots} (total_slots x 3)")
-        if t.data_ptr() % 4:
+        ptr = t.data_ptr()
+        if ptr % 4:
             raise ValueError("buffer must be 4-byte aligned")
-        return ctypes.c_void_p(t.data_ptr())
+        return ctypes.c_void_p(ptr), t.get_device()
+
+    def _call(self, name, t, stream):
+        ptr, dev = self._buf(t)
+        _check(getattr(load_library(), name)(self._h, ptr, _stream_handle(stream, dev)))
 
     def upload(self):
         _check(load_library().halo_plan_upload(self._h))
 
     def exchange_x(self, x, stream=None):
-        _check(load_library().halo_exchange_x(self._h, self._buf(x), _stream_handle(stream)))
+        self._call("halo_exchange_x", x, stream)
 
     def exchange_f(self, f, stream=None):
-        _check(load_library().halo_exchange_f(self._h, self._buf(f), _stream_handle(stream)))
+        self._call("halo_exchange_f", f, stream)
 
     def exchange_x_indexmap(self, x, stream=None):
-        _check(load_library().halo_exchange_x_indexmap(self._h, self._buf(x),
-                                                       _stream_handle(stream)))
+        self._call("halo_exchange_x_indexmap", x, stream)
 
     def exchange_f_indexmap(self, f, stream=None):
-        _check(load_library().halo_exchange_f_indexmap(self._h, self._buf(f),
-                                                       _stream_handle(stream)))
+        self._call("halo_exchange_f_indexmap", f, stream)
 
     def exchange_x_transposed(self, x, stream=None):
-        _check(load_library().halo_exchange_x_transposed(self._h, self._buf(x),
-                                                         _stream_handle(stream)))
+        self._call("halo_exchange_x_transposed", x, stream)
 
     def exchange_f_transposed(self, f, stream=None):
-        _check(load_library().halo_exchange_f_transposed(self._h, self._buf(f),
-                                                         _stream_handle(stream)))
+        self._call("halo_exchange_f_transposed", f, stream)
 
     def exchange_x_pulsewise(self, x, stream=None):
-        _check(load_library().halo_exchange_x_pulsewise(self._h, self._buf(x),
-                                                        _stream_handle(stream)))
+        self._call("halo_exchange_x_pulsewise", x, stream)
 
     def exchange_f_pulsewise(self, f, stream=None):
-        _check(load_library().halo_exchange_f_pulsewise(self._h, self._buf(f),
-                                                        _stream_handle(stream)))
+        self._call("halo_exchange_f_pulsewise", f, stream)
+
+    def exchange_f_atomic(self, f, stream=None):
+        self._call("halo_exchange_f_atomic", f, stream)
+
+    def exchange_x_staged(self, x, stream=None):
+        self._call("halo_exchange_x_staged", x, stream)
+
+    def exchange_f_staged(self, f, stream=None):
+        self._call("halo_exchange_f_staged", f, stream)
 
     def sync(self, stream=None):
         _check(load_library().halo_plan_sync(self._h, _stream_handle(stream)))

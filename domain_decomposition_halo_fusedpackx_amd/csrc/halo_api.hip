@@ -249,6 +249,56 @@ __device__ __forceinline__ void unpack_item_fused(const WorkItem *it, __amdgpu_b
         halo::signal_done(halo::counter_f(state, n_seg, it->seg), it->seg == withhold);
 }
 
+// One force-direction item with atomic accumulation: Algorithm 6 as the
+// pages print it, with the items of every pulse in flight together and the
+// adds done by atomicAdd. The item waits only until the slots it reads (the
+// receiver's region of its pulse) hold their final sums, i.e. for the
+// later-pulse segments that add into them; its own targets may take adds of
+// other pulses at the same time. The order of the adds onto one slot is not
+// fixed, so the result equals the ordered exchange up to rounding, and
+// exactly whenever every partial sum is exact (small integers, for example).
+template <int EPT>
+__device__ __forceinline__ void unpack_item_atomic(const WorkItem *it, float *f,
+                                                   __amdgpu_buffer_rsrc_t rf,
+                                                   __amdgpu_buffer_rsrc_t ridx,
+                                                   const int32_t *awaits,
+                                                   const uint32_t *seg_items, uint32_t *state,
+                                                   int32_t n_seg, uint32_t epoch,
+                                                   uint32_t spin_limit, uint32_t *err_word,
+                                                   int32_t withhold)
+{
+    const int32_t n_total = it->n_total;
+    const int32_t region_begin = it->region_begin;
+    uint32_t tgt[EPT], src[EPT];
+    load_targets<EPT>(ridx, it->map_begin, n_total, tgt);
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        src[j] = e < n_total ? (uint32_t)(region_begin + e) * 12u : kInvalid;
+    }
+    f3v add[EPT];
+    if (it->await_count > 0) {
+        halo::wait_segments(awaits + it->await_begin, it->await_count, seg_items, state, n_seg,
+                            true, epoch, spin_limit, err_word);
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) add[j] = load3<kShared>(rf, src[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) add[j] = load3<kStream>(rf, src[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        if (tgt[j] == kInvalid) continue;
+        float *t = f + tgt[j] / 4u;
+        __hip_atomic_fetch_add(t + 0, add[j].x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(t + 1, add[j].y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(t + 2, add[j].z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the targets of a pulse p > 0 may be the sources of an earlier pulse
+    if (it->flags & halo::kItemFStoreShared)
+        halo::signal_done(halo::counter_f(state, n_seg, it->seg), it->seg == withhold);
+}
+
 // ---- kernels -----------------------------------------------------------------
 
 // Fused coordinate exchange: ONE launch for all pulses, one item per
@@ -284,6 +334,20 @@ __global__ __launch_bounds__(kThreads) void k_unpack_fused(
     unpack_item_fused<EPT>(items + (n_items - 1u - blockIdx.x), make_rsrc(f, f_bytes),
                            make_rsrc(idx, idx_bytes), seg_items, state, n_seg, epoch, spin_limit,
                            err_word, withhold);
+}
+
+// Fused force exchange with atomic adds: ONE launch, last pulse first; an item
+// waits only on segments of later pulses, i.e. on smaller workgroup indices.
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_unpack_atomic(
+    float *f, uint32_t f_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
+    const WorkItem *__restrict__ items, const int32_t *__restrict__ awaits,
+    const uint32_t *__restrict__ seg_items, uint32_t *state, int32_t n_seg, uint32_t n_items,
+    uint32_t epoch, uint32_t spin_limit, uint32_t *err_word, int32_t withhold)
+{
+    unpack_item_atomic<EPT>(items + (n_items - 1u - blockIdx.x), f, make_rsrc(f, f_bytes),
+                            make_rsrc(idx, idx_bytes), awaits, seg_items, state, n_seg, epoch,
+                            spin_limit, err_word, withhold);
 }
 
 // ---- transposed form: per-slot pulse masks --------------------------------
@@ -522,6 +586,87 @@ __global__ __launch_bounds__(kThreads) void k_unpack_pulse(float *f, uint32_t f_
     unpack_span<EPT, kPlain, kPlain>(make_rsrc(f, f_bytes), tgt, it->region_begin, it->n_total);
 }
 
+// Staged baseline (the message-passing design the pages compare against): a
+// pulse first packs into a staging buffer, entry e of the concatenated
+// indexMap at stage[e], and a second launch moves the staged run into the
+// receiver's region; forces go the other way round (region -> stage, then
+// the scatter-add from stage). Two launches per pulse and 24 bytes more per
+// entry than the zero-copy store.
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_stage_pack(
+    float *x, uint32_t x_bytes, float *stage, uint32_t stage_bytes,
+    const int32_t *__restrict__ idx, uint32_t idx_bytes, const WorkItem *__restrict__ items,
+    int32_t item_base)
+{
+    const WorkItem *it = items + item_base + blockIdx.x;
+    const f3v shift = {it->shift[0], it->shift[1], it->shift[2]};
+    const auto rx = make_rsrc(x, x_bytes), rs = make_rsrc(stage, stage_bytes);
+    const auto ridx = make_rsrc(idx, idx_bytes);
+    uint32_t src[EPT], dst[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        const bool ok = e < it->n_total;
+        src[j] = load_index(ridx, it->map_begin + e, ok) * 12u;
+        dst[j] = ok ? (uint32_t)(it->map_begin + e) * 12u : kInvalid;
+    }
+    f3v v[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) v[j] = load3<kPlain>(rx, src[j]);
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) store3<kPlain>(rs, dst[j], v[j] + shift);
+}
+
+// to_region != 0: buf[region_begin + e] = stage[map_begin + e] (coordinates);
+// to_region == 0: stage[map_begin + e] = buf[region_begin + e] (forces).
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_stage_move(float *buf, uint32_t buf_bytes,
+                                                         float *stage, uint32_t stage_bytes,
+                                                         const WorkItem *__restrict__ items,
+                                                         int32_t item_base, int32_t to_region)
+{
+    const WorkItem *it = items + item_base + blockIdx.x;
+    const auto rb = make_rsrc(buf, buf_bytes), rs = make_rsrc(stage, stage_bytes);
+    const auto rsrc = to_region ? rs : rb, rdst = to_region ? rb : rs;
+    uint32_t src[EPT], dst[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        const bool ok = e < it->n_total;
+        const uint32_t so = ok ? (uint32_t)(it->map_begin + e) * 12u : kInvalid;
+        const uint32_t ro = ok ? (uint32_t)(it->region_begin + e) * 12u : kInvalid;
+        src[j] = to_region ? so : ro;
+        dst[j] = to_region ? ro : so;
+    }
+    f3v v[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) v[j] = load3<kPlain>(rsrc, src[j]);
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) store3<kPlain>(rdst, dst[j], v[j]);
+}
+
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_stage_unpack(
+    float *f, uint32_t f_bytes, float *stage, uint32_t stage_bytes,
+    const int32_t *__restrict__ idx, uint32_t idx_bytes, const WorkItem *__restrict__ items,
+    int32_t item_base)
+{
+    const WorkItem *it = items + item_base + blockIdx.x;
+    const auto rf = make_rsrc(f, f_bytes), rs = make_rsrc(stage, stage_bytes);
+    uint32_t tgt[EPT];
+    load_targets<EPT>(make_rsrc(idx, idx_bytes), it->map_begin, it->n_total, tgt);
+    f3v add[EPT], cur[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        add[j] = load3<kPlain>(rs, e < it->n_total ? (uint32_t)(it->map_begin + e) * 12u
+                                                   : kInvalid);
+        cur[j] = load3<kPlain>(rf, tgt[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) store3<kPlain>(rf, tgt[j], cur[j] + add[j]);
+}
+
 }  // namespace
 
 struct halo_plan {
@@ -532,6 +677,7 @@ struct halo_plan {
     int32_t *d_idx = nullptr;
     WorkItem *d_items = nullptr;
     int32_t *d_xwaits = nullptr;
+    int32_t *d_awaits = nullptr;
     uint32_t *d_seg_items = nullptr;
     uint32_t *d_state = nullptr;
     size_t state_words = 0;
@@ -546,6 +692,8 @@ struct halo_plan {
     float *d_shift4 = nullptr;
     uint32_t *d_x_arrivals = nullptr;
     uint32_t *d_zone_chunks = nullptr;
+    // staged baseline: one float triple per indexMap entry, allocated on first use
+    float *d_stage = nullptr;
     // epochs: work-item kernels (x, f) and chunk kernels (xc, fc); each family
     // counts in its own block of state
     uint32_t epoch_x = 0, epoch_f = 0, epoch_xc = 0, epoch_fc = 0;
@@ -565,6 +713,8 @@ void free_device(halo_plan *p)
     if (p->d_idx) (void)hipFree(p->d_idx);
     if (p->d_items) (void)hipFree(p->d_items);
     if (p->d_xwaits) (void)hipFree(p->d_xwaits);
+    if (p->d_awaits) (void)hipFree(p->d_awaits);
+    if (p->d_stage) (void)hipFree(p->d_stage);
     if (p->d_seg_items) (void)hipFree(p->d_seg_items);
     if (p->d_state) (void)hipFree(p->d_state);
     if (p->h_err) (void)hipHostFree(p->h_err);
@@ -579,7 +729,8 @@ void free_device(halo_plan *p)
     p->d_x_arrivals = p->d_zone_chunks = nullptr;
     p->d_idx = nullptr;
     p->d_items = nullptr;
-    p->d_xwaits = nullptr;
+    p->d_xwaits = p->d_awaits = nullptr;
+    p->d_stage = nullptr;
     p->d_seg_items = nullptr;
     p->d_state = nullptr;
     p->h_err = p->d_err = nullptr;
@@ -604,15 +755,18 @@ int ept_for(int32_t item_entries)
 
 // Kernel entry points for the plan's items-per-thread.
 struct Kernels {
-    const void *pack_fused, *unpack_fused, *pack_pulse, *unpack_pulse, *push_x, *pull_f;
+    const void *pack_fused, *unpack_fused, *pack_pulse, *unpack_pulse, *push_x, *pull_f,
+        *unpack_atomic, *stage_pack, *stage_move, *stage_unpack;
 };
 
 template <int EPT>
 Kernels kernels_for()
 {
-    return {(const void *)&k_pack_fused<EPT>, (const void *)&k_unpack_fused<EPT>,
-            (const void *)&k_pack_pulse<EPT>, (const void *)&k_unpack_pulse<EPT>,
-            (const void *)&k_push_x<EPT>,     (const void *)&k_pull_f<EPT>};
+    return {(const void *)&k_pack_fused<EPT>,    (const void *)&k_unpack_fused<EPT>,
+            (const void *)&k_pack_pulse<EPT>,    (const void *)&k_unpack_pulse<EPT>,
+            (const void *)&k_push_x<EPT>,        (const void *)&k_pull_f<EPT>,
+            (const void *)&k_unpack_atomic<EPT>, (const void *)&k_stage_pack<EPT>,
+            (const void *)&k_stage_move<EPT>,    (const void *)&k_stage_unpack<EPT>};
 }
 
 Kernels kernels(int32_t item_entries)
@@ -682,6 +836,46 @@ hipError_t launch_pulse(halo_plan *p, bool force_dir, float *buf, hipStream_t s,
                            args, 0, s);
 }
 
+hipError_t launch_atomic(halo_plan *p, float *buf, hipStream_t s)
+{
+    const halo::HostPlan &h = p->h;
+    int32_t n_seg = (int32_t)h.seg.size();
+    uint32_t n_items = (uint32_t)h.items.size();
+    uint32_t bytes = (uint32_t)(h.total_slots * 12);
+    uint32_t idx_bytes = (uint32_t)(h.abs_map.size() * 4);
+    uint32_t epoch = p->epoch_f;
+    const Kernels k = kernels(h.item_entries);
+    void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_awaits,
+                    &p->d_seg_items, &p->d_state, &n_seg, &n_items, &epoch, &p->spin_limit,
+                    &p->d_err, &p->withhold};
+    return hipLaunchKernel(k.unpack_atomic, dim3(n_items), dim3(kThreads), args, 0, s);
+}
+
+// One pulse of the staged baseline: two launches.
+hipError_t launch_staged(halo_plan *p, bool force_dir, float *buf, hipStream_t s, int32_t q)
+{
+    const halo::HostPlan &h = p->h;
+    uint32_t bytes = (uint32_t)(h.total_slots * 12);
+    uint32_t idx_bytes = (uint32_t)(h.abs_map.size() * 4);
+    uint32_t stage_bytes = (uint32_t)(h.abs_map.size() * 12);
+    int32_t base = h.pulse_item_off[q];
+    const uint32_t n = (uint32_t)(h.pulse_item_off[q + 1] - base);
+    const Kernels k = kernels(h.item_entries);
+    int32_t to_region = force_dir ? 0 : 1;
+    void *args_io[] = {&buf, &bytes, &p->d_stage, &stage_bytes, &p->d_idx, &idx_bytes,
+                       &p->d_items, &base};
+    void *args_mv[] = {&buf, &bytes, &p->d_stage, &stage_bytes, &p->d_items, &base, &to_region};
+    hipError_t e;
+    if (!force_dir) {
+        e = hipLaunchKernel(k.stage_pack, dim3(n), dim3(kThreads), args_io, 0, s);
+        if (e == hipSuccess) e = hipLaunchKernel(k.stage_move, dim3(n), dim3(kThreads), args_mv, 0, s);
+    } else {
+        e = hipLaunchKernel(k.stage_move, dim3(n), dim3(kThreads), args_mv, 0, s);
+        if (e == hipSuccess) e = hipLaunchKernel(k.stage_unpack, dim3(n), dim3(kThreads), args_io, 0, s);
+    }
+    return e;
+}
+
 halo_status ensure_uploaded(halo_plan *p)
 {
     if (p->uploaded) return HALO_OK;
@@ -691,6 +885,7 @@ halo_status ensure_uploaded(halo_plan *p)
     if ((e = upload_vec(&p->d_idx, h.abs_map)) != hipSuccess ||
         (e = upload_vec(&p->d_items, h.items)) != hipSuccess ||
         (e = upload_vec(&p->d_xwaits, h.xwaits)) != hipSuccess ||
+        (e = upload_vec(&p->d_awaits, h.awaits)) != hipSuccess ||
         (e = upload_vec(&p->d_seg_items, h.seg_items)) != hipSuccess) {
         free_device(p);
         return hip_fail(e, "halo_plan_upload");
@@ -941,6 +1136,50 @@ halo_status halo_exchange_f_pulsewise(halo_plan *p, float *f, void *stream)
         if (e != hipSuccess) return hip_fail(e, "halo_exchange_f_pulsewise launch");
     }
     return HALO_OK;
+}
+
+halo_status halo_exchange_f_atomic(halo_plan *p, float *f, void *stream)
+{
+    halo_status st = check_exchange(p, f, "halo_exchange_f_atomic");
+    if (st != HALO_OK) return st;
+    if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
+    // shares the index-list force counters: both kernels advance the same
+    // counters by the same counts per exchange
+    p->epoch_f += 1;
+    hipError_t e = launch_atomic(p, f, (hipStream_t)stream);
+    return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_f_atomic launch");
+}
+
+static halo_status exchange_staged(halo_plan *p, bool force_dir, float *buf, void *stream,
+                                   const char *what)
+{
+    halo_status st = check_exchange(p, buf, what);
+    if (st != HALO_OK) return st;
+    const halo::HostPlan &h = p->h;
+    if (h.total_slots == 0 || h.abs_map.empty()) return HALO_OK;
+    if (!p->d_stage) {
+        hipError_t e = hipMalloc((void **)&p->d_stage, h.abs_map.size() * 12);
+        if (e != hipSuccess) {
+            p->d_stage = nullptr;
+            return hip_fail(e, what);
+        }
+    }
+    for (int32_t i = 0; i < h.n_pulse; ++i) {
+        const int32_t q = force_dir ? h.n_pulse - 1 - i : i;
+        hipError_t e = launch_staged(p, force_dir, buf, (hipStream_t)stream, q);
+        if (e != hipSuccess) return hip_fail(e, what);
+    }
+    return HALO_OK;
+}
+
+halo_status halo_exchange_x_staged(halo_plan *p, float *x, void *stream)
+{
+    return exchange_staged(p, false, x, stream, "halo_exchange_x_staged");
+}
+
+halo_status halo_exchange_f_staged(halo_plan *p, float *f, void *stream)
+{
+    return exchange_staged(p, true, f, stream, "halo_exchange_f_staged");
 }
 
 halo_status halo_plan_sync(halo_plan *p, void *stream)

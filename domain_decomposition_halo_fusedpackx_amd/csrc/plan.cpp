@@ -302,6 +302,25 @@ static void xcd_order(std::vector<WorkItem> &items, size_t begin, int32_t n_dom)
 // items, then the dependent ones; for the last pulse, whose completion nobody
 // waits for, the dependent items come first and its independent bulk last,
 // so that the forwarding chain meets less memory traffic.
+// Force direction with atomic adds: the segments of later pulses whose
+// targets lie in the region that segment (p, D) reads (the receiver's region
+// of pulse p). Only those write the item's sources during the launch.
+static std::vector<int32_t> atomic_force_waits(const HostPlan &P, int32_t p, int32_t D)
+{
+    std::vector<int32_t> out;
+    const int32_t R = P.at(p, D).send_to;
+    const Segment &rs = P.at(p, R);
+    const int32_t lo = rs.atom_offset, hi = rs.atom_offset + rs.recv_size;
+    if (lo == hi) return out;
+    for (int32_t q = p + 1; q < P.n_pulse; ++q) {
+        const Segment &w = P.at(q, R);
+        const int32_t *m = P.local_map.data() + w.map_off;
+        const int32_t *it = std::lower_bound(m, m + w.send_size, lo);
+        if (it != m + w.send_size && *it < hi) out.push_back(q * P.n_dom + R);
+    }
+    return out;
+}
+
 static void cut_span(HostPlan &P, int32_t p, int32_t D, int32_t lo, int32_t hi,
                      int32_t item_entries, bool keep_empty)
 {
@@ -310,6 +329,7 @@ static void cut_span(HostPlan &P, int32_t p, int32_t D, int32_t lo, int32_t hi,
     const int32_t len = hi - lo;
     int32_t n = (len + item_entries - 1) / item_entries;
     if (n == 0 && keep_empty) n = 1;
+    const std::vector<int32_t> aw = n > 0 ? atomic_force_waits(P, p, D) : std::vector<int32_t>();
     for (int32_t j = 0; j < n; ++j) {
         const int32_t b = lo + (int32_t)((int64_t)len * j / n);
         const int32_t e = lo + (int32_t)((int64_t)len * (j + 1) / n);
@@ -343,6 +363,9 @@ static void cut_span(HostPlan &P, int32_t p, int32_t D, int32_t lo, int32_t hi,
             it.fwait[0] = (p + 1) * P.n_dom + D;
             it.fwait[1] = (p + 1) * P.n_dom + s.send_to;
         }
+        it.await_begin = (int32_t)P.awaits.size();
+        it.await_count = (int32_t)aw.size();
+        P.awaits.insert(P.awaits.end(), aw.begin(), aw.end());
         // Regions of every pulse but the last are candidates of a later
         // pulse; in the force direction the last pulse runs first (reads
         // untouched slots) and pulse 0 runs last (its sums are read by nobody
@@ -361,6 +384,7 @@ void make_items(HostPlan &P, int32_t item_entries)
     P.item_entries = item_entries;
     P.items.clear();
     P.xwaits.clear();
+    P.awaits.clear();
     P.seg_items.assign(P.seg.size(), 0);
     P.pulse_item_off.assign(P.n_pulse + 1, 0);
     for (auto &s : P.seg) {

@@ -35,7 +35,9 @@ struct alignas(16) WorkItem {
     int32_t xwait_count;   //   dependent entries need (list in xwaits)
     int32_t fwait[2];      // force direction: (p+1, D) and (p+1, receiver); -1 = none
     int32_t flags;         // kItem* bits
-    int32_t pad[3];
+    int32_t await_begin;   // atomic force direction: segments of later pulses that
+    int32_t await_count;   //   add into the slots this item reads (list in awaits)
+    int32_t pad;
 };
 static_assert(sizeof(WorkItem) == 64, "WorkItem layout");
 
@@ -96,6 +98,7 @@ struct HostPlan {
     int32_t item_entries = 0;
     std::vector<WorkItem> items;
     std::vector<int32_t> xwaits;
+    std::vector<int32_t> awaits;
     std::vector<uint32_t> seg_items;       // items per segment
     std::vector<int32_t> pulse_item_off;   // [n_pulse + 1]
     // transposed form (only when n_pulse <= kMaxMaskPulses)

@@ -174,6 +174,32 @@ halo_status halo_exchange_f_transposed(halo_plan *plan, float *f, void *stream);
 halo_status halo_exchange_x_pulsewise(halo_plan *plan, float *x, void *stream);
 halo_status halo_exchange_f_pulsewise(halo_plan *plan, float *f, void *stream);
 
+/* Force exchange with atomic accumulation, as "Redesigning GROMACS Halo
+ * Exchange" (paper review), Algorithm 6, prints it: one launch, the items of
+ * every pulse in flight together, each adding its received forces onto its
+ * indexMap targets with atomicAdd. An item waits only until the slots it
+ * reads (the receiver's region of its pulse) hold their final sums. The order
+ * of the adds onto one slot is not fixed, so the result matches
+ * halo_exchange_f only up to fp32 rounding: per slot, at most
+ * 2 * (n - 1) * 2^-24 * (sum of |terms|) apart, n being the number of values
+ * summed into the slot; it is bitwise equal whenever every partial sum is
+ * exact (small integers, for example). Same arguments, ownership and errors
+ * as halo_exchange_f. Shares the index-list force counters; do not overlap it
+ * with halo_exchange_f on the same plan. */
+halo_status halo_exchange_f_atomic(halo_plan *plan, float *f, void *stream);
+
+/* Staged baseline (the message-passing design that the pages measure the
+ * zero-copy exchange against, "GPU-Initiated Halo Exchange Cuts CPU
+ * Bottlenecks in GROMACS"): per pulse, one launch packs x[indexMap] +
+ * coordShift into a staging buffer owned by the plan, and a second launch
+ * moves the staged entries into the receiver's region; for forces the region
+ * is first copied out to the staging buffer and then scatter-added onto the
+ * targets. 2 * num_pulses launches per exchange, bitwise identical results.
+ * The first staged call on a plan allocates the staging buffer
+ * (num_entries * 12 bytes; HALO_ERR_HIP if that fails). */
+halo_status halo_exchange_x_staged(halo_plan *plan, float *x, void *stream);
+halo_status halo_exchange_f_staged(halo_plan *plan, float *f, void *stream);
+
 /* Wait for the plan's work on `stream` and report a timeout raised inside a
  * kernel (HALO_ERR_TIMEOUT); poisons the plan in that case. */
 halo_status halo_plan_sync(halo_plan *plan, void *stream);
