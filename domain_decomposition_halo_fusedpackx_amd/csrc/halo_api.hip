@@ -120,8 +120,9 @@ __device__ __forceinline__ void pack_span(__amdgpu_buffer_rsrc_t rx, __amdgpu_bu
 template <int EPT, int ST>
 __device__ __forceinline__ void pack_item_fused_st(const WorkItem *it, __amdgpu_buffer_rsrc_t rx,
                                                    __amdgpu_buffer_rsrc_t ridx,
-                                                   const int32_t *xwaits, const uint32_t *seg_items,
-                                                   uint32_t *state, int32_t n_seg, uint32_t epoch,
+                                                   const int32_t *recv_from,
+                                                   const uint32_t *seg_items, uint32_t *state,
+                                                   int32_t n_dom, uint32_t epoch,
                                                    uint32_t spin_limit, uint32_t *err_word)
 {
     const int32_t n_indep = it->n_indep;
@@ -148,8 +149,17 @@ __device__ __forceinline__ void pack_item_fused_st(const WorkItem *it, __amdgpu_
         store3<ST>(rx, ind ? dst[j] : kInvalid, v[j] + shift);
     }
     if (n_total > n_indep) {
-        halo::wait_segments(xwaits + it->xwait_begin, it->xwait_count, seg_items, state, n_seg,
-                            false, epoch, spin_limit, err_word);
+        // lane r of wave 0 polls the arrival of the region the sender
+        // received in pulse r, if the dependent entries read it
+        const uint32_t lane = threadIdx.x & 63u, wmask = it->xwait_mask;
+        uint32_t *ctr = nullptr;
+        uint32_t target = 0;
+        if (lane < 32u && ((wmask >> lane) & 1u)) {
+            const int32_t s = (int32_t)lane * n_dom + recv_from[(int32_t)lane * n_dom + it->domain];
+            ctr = halo::counter_x(state, s);
+            target = epoch * seg_items[s];
+        }
+        halo::wait_lanes(ctr, target, spin_limit, err_word);
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
             const bool dep = (int32_t)threadIdx.x + j * kThreads >= n_indep;
@@ -165,19 +175,20 @@ __device__ __forceinline__ void pack_item_fused_st(const WorkItem *it, __amdgpu_
 
 template <int EPT>
 __device__ __forceinline__ void pack_item_fused(const WorkItem *it, __amdgpu_buffer_rsrc_t rx,
-                                                __amdgpu_buffer_rsrc_t ridx, const int32_t *xwaits,
+                                                __amdgpu_buffer_rsrc_t ridx,
+                                                const int32_t *recv_from,
                                                 const uint32_t *seg_items, uint32_t *state,
-                                                int32_t n_seg, uint32_t epoch,
+                                                int32_t n_dom, uint32_t epoch,
                                                 uint32_t spin_limit, uint32_t *err_word,
                                                 int32_t withhold)
 {
     if (it->flags & halo::kItemXStoreShared) {
-        pack_item_fused_st<EPT, kShared>(it, rx, ridx, xwaits, seg_items, state, n_seg, epoch,
+        pack_item_fused_st<EPT, kShared>(it, rx, ridx, recv_from, seg_items, state, n_dom, epoch,
                                          spin_limit, err_word);
         halo::signal_done(halo::counter_x(state, it->seg), it->seg == withhold);
     } else {
         // last pulse: no later pulse forwards its region, nobody waits on it
-        pack_item_fused_st<EPT, kStream>(it, rx, ridx, xwaits, seg_items, state, n_seg, epoch,
+        pack_item_fused_st<EPT, kStream>(it, rx, ridx, recv_from, seg_items, state, n_dom, epoch,
                                         spin_limit, err_word);
     }
 }
@@ -261,9 +272,8 @@ template <int EPT>
 __device__ __forceinline__ void unpack_item_atomic(const WorkItem *it, float *f,
                                                    __amdgpu_buffer_rsrc_t rf,
                                                    __amdgpu_buffer_rsrc_t ridx,
-                                                   const int32_t *awaits,
                                                    const uint32_t *seg_items, uint32_t *state,
-                                                   int32_t n_seg, uint32_t epoch,
+                                                   int32_t n_seg, int32_t n_dom, uint32_t epoch,
                                                    uint32_t spin_limit, uint32_t *err_word,
                                                    int32_t withhold)
 {
@@ -277,9 +287,18 @@ __device__ __forceinline__ void unpack_item_atomic(const WorkItem *it, float *f,
         src[j] = e < n_total ? (uint32_t)(region_begin + e) * 12u : kInvalid;
     }
     f3v add[EPT];
-    if (it->await_count > 0) {
-        halo::wait_segments(awaits + it->await_begin, it->await_count, seg_items, state, n_seg,
-                            true, epoch, spin_limit, err_word);
+    const uint32_t amask = it->await_mask;
+    if (amask) {
+        // lane q of wave 0 polls segment (q, receiver)
+        const uint32_t lane = threadIdx.x & 63u;
+        uint32_t *ctr = nullptr;
+        uint32_t target = 0;
+        if (lane < 32u && ((amask >> lane) & 1u)) {
+            const int32_t s = (int32_t)lane * n_dom + it->receiver;
+            ctr = halo::counter_f(state, n_seg, s);
+            target = epoch * seg_items[s];
+        }
+        halo::wait_lanes(ctr, target, spin_limit, err_word);
 #pragma unroll
         for (int j = 0; j < EPT; ++j) add[j] = load3<kShared>(rf, src[j]);
     } else {
@@ -314,12 +333,13 @@ __device__ __forceinline__ void unpack_item_atomic(const WorkItem *it, float *f,
 template <int EPT>
 __global__ __launch_bounds__(kThreads) void k_pack_fused(
     float *x, uint32_t x_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
-    const WorkItem *__restrict__ items, const int32_t *__restrict__ xwaits,
-    const uint32_t *__restrict__ seg_items, uint32_t *state, int32_t n_seg, uint32_t epoch,
+    const WorkItem *__restrict__ items, const int32_t *__restrict__ recv_from,
+    const uint32_t *__restrict__ seg_items, uint32_t *state, int32_t n_dom, uint32_t epoch,
     uint32_t spin_limit, uint32_t *err_word, int32_t withhold)
 {
     pack_item_fused<EPT>(items + blockIdx.x, make_rsrc(x, x_bytes), make_rsrc(idx, idx_bytes),
-                         xwaits, seg_items, state, n_seg, epoch, spin_limit, err_word, withhold);
+                         recv_from, seg_items, state, n_dom, epoch, spin_limit, err_word,
+                         withhold);
 }
 
 // Fused force exchange: ONE launch, workgroup b takes item n_items-1-b, so
@@ -341,12 +361,12 @@ __global__ __launch_bounds__(kThreads) void k_unpack_fused(
 template <int EPT>
 __global__ __launch_bounds__(kThreads) void k_unpack_atomic(
     float *f, uint32_t f_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
-    const WorkItem *__restrict__ items, const int32_t *__restrict__ awaits,
-    const uint32_t *__restrict__ seg_items, uint32_t *state, int32_t n_seg, uint32_t n_items,
-    uint32_t epoch, uint32_t spin_limit, uint32_t *err_word, int32_t withhold)
+    const WorkItem *__restrict__ items, const uint32_t *__restrict__ seg_items, uint32_t *state,
+    int32_t n_seg, int32_t n_dom, uint32_t n_items, uint32_t epoch, uint32_t spin_limit,
+    uint32_t *err_word, int32_t withhold)
 {
     unpack_item_atomic<EPT>(items + (n_items - 1u - blockIdx.x), f, make_rsrc(f, f_bytes),
-                            make_rsrc(idx, idx_bytes), awaits, seg_items, state, n_seg, epoch,
+                            make_rsrc(idx, idx_bytes), seg_items, state, n_seg, n_dom, epoch,
                             spin_limit, err_word, withhold);
 }
 
@@ -676,8 +696,8 @@ struct halo_plan {
     bool poisoned = false;
     int32_t *d_idx = nullptr;
     WorkItem *d_items = nullptr;
-    int32_t *d_xwaits = nullptr;
-    int32_t *d_awaits = nullptr;
+    int32_t *d_recv_from = nullptr;
+    int32_t *d_send_to = nullptr;
     uint32_t *d_seg_items = nullptr;
     uint32_t *d_state = nullptr;
     size_t state_words = 0;
@@ -688,7 +708,6 @@ struct halo_plan {
     halo::Chunk *d_chunks = nullptr;
     int32_t *d_forder = nullptr;
     int32_t *d_dest_start = nullptr;
-    int32_t *d_send_to = nullptr;
     float *d_shift4 = nullptr;
     uint32_t *d_x_arrivals = nullptr;
     uint32_t *d_zone_chunks = nullptr;
@@ -712,24 +731,24 @@ void free_device(halo_plan *p)
 {
     if (p->d_idx) (void)hipFree(p->d_idx);
     if (p->d_items) (void)hipFree(p->d_items);
-    if (p->d_xwaits) (void)hipFree(p->d_xwaits);
-    if (p->d_awaits) (void)hipFree(p->d_awaits);
+    if (p->d_recv_from) (void)hipFree(p->d_recv_from);
+    if (p->d_send_to) (void)hipFree(p->d_send_to);
     if (p->d_stage) (void)hipFree(p->d_stage);
     if (p->d_seg_items) (void)hipFree(p->d_seg_items);
     if (p->d_state) (void)hipFree(p->d_state);
     if (p->h_err) (void)hipHostFree(p->h_err);
     for (void *q : {(void *)p->d_mask, (void *)p->d_chunks, (void *)p->d_forder,
-                    (void *)p->d_dest_start, (void *)p->d_send_to, (void *)p->d_shift4,
+                    (void *)p->d_dest_start, (void *)p->d_shift4,
                     (void *)p->d_x_arrivals, (void *)p->d_zone_chunks})
         if (q) (void)hipFree(q);
     p->d_mask = nullptr;
     p->d_chunks = nullptr;
-    p->d_forder = p->d_dest_start = p->d_send_to = nullptr;
+    p->d_forder = p->d_dest_start = nullptr;
     p->d_shift4 = nullptr;
     p->d_x_arrivals = p->d_zone_chunks = nullptr;
     p->d_idx = nullptr;
     p->d_items = nullptr;
-    p->d_xwaits = p->d_awaits = nullptr;
+    p->d_recv_from = p->d_send_to = nullptr;
     p->d_stage = nullptr;
     p->d_seg_items = nullptr;
     p->d_state = nullptr;
@@ -785,7 +804,7 @@ hipError_t launch_fused(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
     int32_t n_seg = (int32_t)h.seg.size();
     uint32_t n_items = (uint32_t)h.items.size();
     uint32_t bytes = (uint32_t)(h.total_slots * 12);
-    uint32_t idx_bytes = (uint32_t)(h.abs_map.size() * 4);
+    uint32_t idx_bytes = (uint32_t)(h.n_entries * 4);
     uint32_t epoch = force_dir ? p->epoch_f : p->epoch_x;
     const Kernels k = kernels(h.item_entries);
     if (force_dir) {
@@ -794,8 +813,9 @@ hipError_t launch_fused(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
                         &p->withhold};
         return hipLaunchKernel(k.unpack_fused, dim3(n_items), dim3(kThreads), args, 0, s);
     }
-    void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_xwaits,
-                    &p->d_seg_items, &p->d_state, &n_seg, &epoch, &p->spin_limit, &p->d_err,
+    int32_t n_dom = h.n_dom;
+    void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_recv_from,
+                    &p->d_seg_items, &p->d_state, &n_dom, &epoch, &p->spin_limit, &p->d_err,
                     &p->withhold};
     return hipLaunchKernel(k.pack_fused, dim3(n_items), dim3(kThreads), args, 0, s);
 }
@@ -827,7 +847,7 @@ hipError_t launch_pulse(halo_plan *p, bool force_dir, float *buf, hipStream_t s,
 {
     const halo::HostPlan &h = p->h;
     uint32_t bytes = (uint32_t)(h.total_slots * 12);
-    uint32_t idx_bytes = (uint32_t)(h.abs_map.size() * 4);
+    uint32_t idx_bytes = (uint32_t)(h.n_entries * 4);
     int32_t base = h.pulse_item_off[q];
     const uint32_t n = (uint32_t)(h.pulse_item_off[q + 1] - base);
     const Kernels k = kernels(h.item_entries);
@@ -842,12 +862,13 @@ hipError_t launch_atomic(halo_plan *p, float *buf, hipStream_t s)
     int32_t n_seg = (int32_t)h.seg.size();
     uint32_t n_items = (uint32_t)h.items.size();
     uint32_t bytes = (uint32_t)(h.total_slots * 12);
-    uint32_t idx_bytes = (uint32_t)(h.abs_map.size() * 4);
+    uint32_t idx_bytes = (uint32_t)(h.n_entries * 4);
     uint32_t epoch = p->epoch_f;
     const Kernels k = kernels(h.item_entries);
-    void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_awaits,
-                    &p->d_seg_items, &p->d_state, &n_seg, &n_items, &epoch, &p->spin_limit,
-                    &p->d_err, &p->withhold};
+    int32_t n_dom = h.n_dom;
+    void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_seg_items,
+                    &p->d_state, &n_seg, &n_dom, &n_items, &epoch, &p->spin_limit, &p->d_err,
+                    &p->withhold};
     return hipLaunchKernel(k.unpack_atomic, dim3(n_items), dim3(kThreads), args, 0, s);
 }
 
@@ -856,8 +877,8 @@ hipError_t launch_staged(halo_plan *p, bool force_dir, float *buf, hipStream_t s
 {
     const halo::HostPlan &h = p->h;
     uint32_t bytes = (uint32_t)(h.total_slots * 12);
-    uint32_t idx_bytes = (uint32_t)(h.abs_map.size() * 4);
-    uint32_t stage_bytes = (uint32_t)(h.abs_map.size() * 12);
+    uint32_t idx_bytes = (uint32_t)(h.n_entries * 4);
+    uint32_t stage_bytes = (uint32_t)(h.n_entries * 12);
     int32_t base = h.pulse_item_off[q];
     const uint32_t n = (uint32_t)(h.pulse_item_off[q + 1] - base);
     const Kernels k = kernels(h.item_entries);
@@ -884,8 +905,8 @@ halo_status ensure_uploaded(halo_plan *p)
     const halo::HostPlan &h = p->h;
     if ((e = upload_vec(&p->d_idx, h.abs_map)) != hipSuccess ||
         (e = upload_vec(&p->d_items, h.items)) != hipSuccess ||
-        (e = upload_vec(&p->d_xwaits, h.xwaits)) != hipSuccess ||
-        (e = upload_vec(&p->d_awaits, h.awaits)) != hipSuccess ||
+        (e = upload_vec(&p->d_recv_from, h.recv_from)) != hipSuccess ||
+        (e = upload_vec(&p->d_send_to, h.send_to)) != hipSuccess ||
         (e = upload_vec(&p->d_seg_items, h.seg_items)) != hipSuccess) {
         free_device(p);
         return hip_fail(e, "halo_plan_upload");
@@ -895,7 +916,6 @@ halo_status ensure_uploaded(halo_plan *p)
          (e = upload_vec(&p->d_chunks, h.chunks)) != hipSuccess ||
          (e = upload_vec(&p->d_forder, h.chunk_forder)) != hipSuccess ||
          (e = upload_vec(&p->d_dest_start, h.dest_start)) != hipSuccess ||
-         (e = upload_vec(&p->d_send_to, h.send_to)) != hipSuccess ||
          (e = upload_vec(&p->d_shift4, h.shift4)) != hipSuccess ||
          (e = upload_vec(&p->d_x_arrivals, h.x_arrivals)) != hipSuccess ||
          (e = upload_vec(&p->d_zone_chunks, h.zone_chunks)) != hipSuccess)) {
@@ -989,7 +1009,7 @@ void halo_plan_destroy(halo_plan *plan)
 int64_t halo_plan_total_slots(const halo_plan *p) { return p ? p->h.total_slots : -1; }
 int32_t halo_plan_num_domains(const halo_plan *p) { return p ? p->h.n_dom : -1; }
 int32_t halo_plan_num_pulses(const halo_plan *p) { return p ? p->h.n_pulse : -1; }
-int64_t halo_plan_num_entries(const halo_plan *p) { return p ? (int64_t)p->h.abs_map.size() : -1; }
+int64_t halo_plan_num_entries(const halo_plan *p) { return p ? (int64_t)p->h.n_entries : -1; }
 int32_t halo_plan_num_items(const halo_plan *p) { return p ? (int32_t)p->h.items.size() : -1; }
 
 halo_status halo_plan_pulse_dim(const halo_plan *p, int32_t pulse, int32_t *dim, int32_t *k)
@@ -1061,7 +1081,7 @@ halo_status halo_exchange_x(halo_plan *p, float *x, void *stream)
 
 halo_status halo_exchange_f(halo_plan *p, float *f, void *stream)
 {
-    if (p && (!p->h.has_chunks || (int64_t)p->h.abs_map.size() < kTransposedForceMinEntries))
+    if (p && (!p->h.has_chunks || (int64_t)p->h.n_entries < kTransposedForceMinEntries))
         return halo_exchange_f_indexmap(p, f, stream);
     return halo_exchange_f_transposed(p, f, stream);
 }
@@ -1156,9 +1176,9 @@ static halo_status exchange_staged(halo_plan *p, bool force_dir, float *buf, voi
     halo_status st = check_exchange(p, buf, what);
     if (st != HALO_OK) return st;
     const halo::HostPlan &h = p->h;
-    if (h.total_slots == 0 || h.abs_map.empty()) return HALO_OK;
+    if (h.total_slots == 0 || h.n_entries == 0) return HALO_OK;
     if (!p->d_stage) {
-        hipError_t e = hipMalloc((void **)&p->d_stage, h.abs_map.size() * 12);
+        hipError_t e = hipMalloc((void **)&p->d_stage, h.n_entries * 12);
         if (e != hipSuccess) {
             p->d_stage = nullptr;
             return hip_fail(e, what);

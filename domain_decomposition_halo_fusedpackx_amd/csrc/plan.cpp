@@ -139,6 +139,11 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
             P.pulse_k.push_back(k);
         }
     P.n_pulse = (int32_t)P.pulse_dim.size();
+    if (P.n_pulse > kMaxPulses) {
+        msg = "halo_plan_create: the cutoff needs " + std::to_string(P.n_pulse) +
+              " pulses; at most " + std::to_string(kMaxPulses) + " are supported";
+        return kErrGeometry;
+    }
 
     // Position in units of the domain width; a rounding up to n is pulled
     // back below n so that the cell index stays in range.
@@ -251,8 +256,15 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
         s.map_off = entries;
         entries += s.send_size;
     }
+    P.n_entries = entries;
     P.local_map.resize((size_t)entries);
     P.abs_map.resize((size_t)entries);
+    P.send_to.assign(P.seg.size(), 0);
+    P.recv_from.assign(P.seg.size(), 0);
+    for (size_t i = 0; i < P.seg.size(); ++i) {
+        P.send_to[i] = P.seg[i].send_to;
+        P.recv_from[i] = P.seg[i].recv_from;
+    }
     for (int32_t p = 0; p < P.n_pulse; ++p)
         for (int32_t D = 0; D < P.n_dom; ++D) {
             const Segment &s = P.seg[(size_t)p * P.n_dom + D];
@@ -302,12 +314,12 @@ static void xcd_order(std::vector<WorkItem> &items, size_t begin, int32_t n_dom)
 // items, then the dependent ones; for the last pulse, whose completion nobody
 // waits for, the dependent items come first and its independent bulk last,
 // so that the forwarding chain meets less memory traffic.
-// Force direction with atomic adds: the segments of later pulses whose
-// targets lie in the region that segment (p, D) reads (the receiver's region
-// of pulse p). Only those write the item's sources during the launch.
-static std::vector<int32_t> atomic_force_waits(const HostPlan &P, int32_t p, int32_t D)
+// Force direction with atomic adds: the later pulses q whose segment (q, R)
+// has targets in the region that segment (p, D) reads (R's region of pulse
+// p, R the receiver). Only those write the item's sources during the launch.
+static uint32_t atomic_force_waits(const HostPlan &P, int32_t p, int32_t D)
 {
-    std::vector<int32_t> out;
+    uint32_t out = 0;
     const int32_t R = P.at(p, D).send_to;
     const Segment &rs = P.at(p, R);
     const int32_t lo = rs.atom_offset, hi = rs.atom_offset + rs.recv_size;
@@ -316,7 +328,7 @@ static std::vector<int32_t> atomic_force_waits(const HostPlan &P, int32_t p, int
         const Segment &w = P.at(q, R);
         const int32_t *m = P.local_map.data() + w.map_off;
         const int32_t *it = std::lower_bound(m, m + w.send_size, lo);
-        if (it != m + w.send_size && *it < hi) out.push_back(q * P.n_dom + R);
+        if (it != m + w.send_size && *it < hi) out |= 1u << q;
     }
     return out;
 }
@@ -329,7 +341,7 @@ static void cut_span(HostPlan &P, int32_t p, int32_t D, int32_t lo, int32_t hi,
     const int32_t len = hi - lo;
     int32_t n = (len + item_entries - 1) / item_entries;
     if (n == 0 && keep_empty) n = 1;
-    const std::vector<int32_t> aw = n > 0 ? atomic_force_waits(P, p, D) : std::vector<int32_t>();
+    const uint32_t aw = n > 0 ? atomic_force_waits(P, p, D) : 0u;
     for (int32_t j = 0; j < n; ++j) {
         const int32_t b = lo + (int32_t)((int64_t)len * j / n);
         const int32_t e = lo + (int32_t)((int64_t)len * (j + 1) / n);
@@ -343,29 +355,24 @@ static void cut_span(HostPlan &P, int32_t p, int32_t D, int32_t lo, int32_t hi,
         // Coordinate direction: wait for exactly the regions that the
         // dependent entries read (each was filled by one sender in an
         // earlier pulse).
-        it.xwait_begin = (int32_t)P.xwaits.size();
-        int32_t last_r = -1;
+        it.xwait_mask = 0;
+        int32_t r = 0;
         for (int32_t i = b + it.n_indep; i < e; ++i) {
             const int32_t slot = P.local_map[s.map_off + i];
-            int32_t r = last_r < 0 ? 0 : last_r;
             while (r < p && !(slot >= P.at(r, D).atom_offset &&
                               slot < P.at(r, D).atom_offset + P.at(r, D).recv_size))
                 ++r;
-            if (r < p && r != last_r) {
-                P.xwaits.push_back(r * P.n_dom + P.at(r, D).recv_from);
-                last_r = r;
-            }
+            if (r < p) it.xwait_mask |= 1u << r;
         }
-        it.xwait_count = (int32_t)P.xwaits.size() - it.xwait_begin;
+        it.domain = D;
+        it.receiver = s.send_to;
         // Force direction: pulse p+1 finished for D and for its receiver.
         it.fwait[0] = it.fwait[1] = -1;
         if (p + 1 < P.n_pulse) {
             it.fwait[0] = (p + 1) * P.n_dom + D;
             it.fwait[1] = (p + 1) * P.n_dom + s.send_to;
         }
-        it.await_begin = (int32_t)P.awaits.size();
-        it.await_count = (int32_t)aw.size();
-        P.awaits.insert(P.awaits.end(), aw.begin(), aw.end());
+        it.await_mask = aw;
         // Regions of every pulse but the last are candidates of a later
         // pulse; in the force direction the last pulse runs first (reads
         // untouched slots) and pulse 0 runs last (its sums are read by nobody
@@ -383,8 +390,6 @@ void make_items(HostPlan &P, int32_t item_entries)
 {
     P.item_entries = item_entries;
     P.items.clear();
-    P.xwaits.clear();
-    P.awaits.clear();
     P.seg_items.assign(P.seg.size(), 0);
     P.pulse_item_off.assign(P.n_pulse + 1, 0);
     for (auto &s : P.seg) {
@@ -422,7 +427,6 @@ void make_chunks(HostPlan &P, int32_t chunk_slots)
     const int32_t nd = P.n_dom, np = P.n_pulse;
     P.slot_mask.assign((size_t)P.total_slots, 0);
     P.dest_start.assign((size_t)np * nd, 0);
-    P.send_to.assign((size_t)np * nd, 0);
     P.shift4.assign((size_t)np * nd * 4, 0.f);
     P.x_arrivals.assign((size_t)np * nd, 0);
     P.zone_chunks.assign((size_t)np * nd, 0);
@@ -431,7 +435,6 @@ void make_chunks(HostPlan &P, int32_t chunk_slots)
             const Segment &s = P.at(p, D);
             const Segment &r = P.at(p, s.send_to);
             P.dest_start[(size_t)p * nd + D] = (int32_t)(P.base[s.send_to] + r.atom_offset);
-            P.send_to[(size_t)p * nd + D] = s.send_to;
             for (int c = 0; c < 3; ++c) P.shift4[((size_t)p * nd + D) * 4 + c] = s.shift[c];
             for (int32_t i = 0; i < s.send_size; ++i)
                 P.slot_mask[(size_t)(P.base[D] + P.local_map[s.map_off + i])] |= (uint8_t)(1u << p);

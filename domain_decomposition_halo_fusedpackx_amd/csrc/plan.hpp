@@ -31,12 +31,14 @@ struct alignas(16) WorkItem {
     int32_t region_begin;  // receiver-region slot of the first entry (X: store, F: load)
     float shift[3];        // coordShift of the segment
     int32_t seg;           // segment id = pulse * n_domains + sending domain
-    int32_t xwait_begin;   // coordinate direction: segments whose arrival the
-    int32_t xwait_count;   //   dependent entries need (list in xwaits)
+    uint32_t xwait_mask;   // coordinate direction: bit r = the dependent entries read
+                           //   the region the sender received in pulse r
+    int32_t domain;        // sending domain
     int32_t fwait[2];      // force direction: (p+1, D) and (p+1, receiver); -1 = none
     int32_t flags;         // kItem* bits
-    int32_t await_begin;   // atomic force direction: segments of later pulses that
-    int32_t await_count;   //   add into the slots this item reads (list in awaits)
+    uint32_t await_mask;   // atomic force direction: bit q = segment (q, receiver) adds
+                           //   into the region this item reads
+    int32_t receiver;      // receiving domain
     int32_t pad;
 };
 static_assert(sizeof(WorkItem) == 64, "WorkItem layout");
@@ -92,13 +94,14 @@ struct HostPlan {
     std::vector<int64_t> home_slot;        // per atom
     // pulses
     std::vector<Segment> seg;              // [n_pulse * n_dom]
+    int64_t n_entries = 0;                 // entries of all indexMaps
     std::vector<int32_t> local_map;        // concatenated indexMap, local slots
     std::vector<int32_t> abs_map;          // same entries as absolute slots
+    std::vector<int32_t> send_to;          // [p][D]: receiver of D in pulse p
+    std::vector<int32_t> recv_from;        // [p][D]: sender to D in pulse p
     // work items
     int32_t item_entries = 0;
     std::vector<WorkItem> items;
-    std::vector<int32_t> xwaits;
-    std::vector<int32_t> awaits;
     std::vector<uint32_t> seg_items;       // items per segment
     std::vector<int32_t> pulse_item_off;   // [n_pulse + 1]
     // transposed form (only when n_pulse <= kMaxMaskPulses)
@@ -108,13 +111,16 @@ struct HostPlan {
     std::vector<Chunk> chunks;             // zone-major: home, region 0, region 1, ...
     std::vector<int32_t> chunk_forder;     // force-direction order: last region first, home last
     std::vector<int32_t> dest_start;       // [p][D]: first slot of the receiver's region of pulse p
-    std::vector<int32_t> send_to;          // [p][D]: receiver of D in pulse p
     std::vector<float> shift4;             // [p][D][4]: coordShift of (p, D)
     std::vector<uint32_t> x_arrivals;      // [p][D]: chunks of D that send in pulse p
     std::vector<uint32_t> zone_chunks;     // [r][D]: chunks in region zone r of D
 
     const Segment &at(int32_t p, int32_t d) const { return seg[(size_t)p * n_dom + d]; }
 };
+
+// Most pulses of one plan: the work items keep per-pulse wait sets as 32-bit
+// masks.
+constexpr int32_t kMaxPulses = 32;
 
 // Largest slot count of one plan: byte offsets of float triples stay below
 // 2^31, so the kernels address x and f with 32-bit buffer offsets and use

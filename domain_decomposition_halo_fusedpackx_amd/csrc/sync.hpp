@@ -120,6 +120,34 @@ __device__ __forceinline__ void wait_one(int32_t s, const uint32_t *seg_items, u
     __syncthreads();
 }
 
+// Wave 0 waits until the counter that each of its lanes names (ctr; nullptr:
+// none) reaches that lane's target; the workgroup then meets at a barrier.
+// One round of polls covers up to 64 counters.
+__device__ __forceinline__ void wait_lanes(uint32_t *ctr, uint32_t target, uint32_t spin_limit,
+                                           uint32_t *err_word)
+{
+    if (threadIdx.x < 64) {
+        uint32_t polls = 0;
+        while (true) {
+            bool ok = true;
+            if (ctr) {
+                const uint32_t c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = (int32_t)(c - target) >= 0;
+            }
+            if (__all(ok)) break;
+            if (++polls > spin_limit) {
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(err_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        wait_vmem();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+    __syncthreads();
+}
+
 // Completion of one work item: every wave waits until its stores are
 // complete, the workgroup meets at a barrier, and one thread adds 1 to the
 // segment's counter.
