@@ -24,6 +24,7 @@ _P = ctypes.POINTER
 _st = ctypes.c_int
 SIGNATURES = {
     "halo_plan_create": (_st, [_vp, _i64, _vp, _vp, _f32, _P(_vp)]),
+    "halo_plan_create_device": (_st, [_vp, _i64, _vp, _vp, _f32, _vp, _P(_vp)]),
     "halo_plan_destroy": (None, [_vp]),
     "halo_last_error": (ctypes.c_char_p, []),
     "halo_plan_total_slots": (_i64, [_vp]),
@@ -36,6 +37,7 @@ SIGNATURES = {
     "halo_plan_home_slots": (_st, [_vp, _vp]),
     "halo_plan_pulse": (_st, [_vp, _i32, _i32, _P(_i32), _P(_i32), _P(_i32), _P(_i32), _P(_i32),
                               _P(_i32), _P(_i32), _vp, _vp]),
+    "halo_plan_item_waits": (_st, [_vp, _i32, _P(_i32), _P(_u32), _P(_u32)]),
     "halo_plan_upload": (_st, [_vp]),
     "halo_exchange_x": (_st, [_vp, _vp, _vp]),
     "halo_exchange_f": (_st, [_vp, _vp, _vp]),
@@ -123,8 +125,38 @@ class HaloPlan:
         _check(lib.halo_plan_create(_np_ptr(pos) if pos.size else None, pos.shape[0],
                                     _np_ptr(self._box), _np_ptr(self._grid),
                                     ctypes.c_float(cutoff), ctypes.byref(h)))
+        self._finish(h, pos.shape[0])
+
+    @classmethod
+    def on_device(cls, positions, box, grid, cutoff, stream=None):
+        """Build the plan on the GPU (halo_plan_create_device) from a
+        contiguous float32 torch.cuda tensor of shape (n_atoms, 3)."""
+        import torch
+        if not isinstance(positions, torch.Tensor) or not positions.is_cuda:
+            raise TypeError("positions must be a torch.cuda tensor")
+        if positions.dtype != torch.float32 or not positions.is_contiguous():
+            raise TypeError("positions must be contiguous float32")
+        if positions.numel() % 3:
+            raise ValueError("positions must hold 3 floats per atom")
+        self = cls.__new__(cls)
+        lib = load_library()
+        self._box = np.ascontiguousarray(box, dtype=np.float32)
+        self._grid = np.ascontiguousarray(grid, dtype=np.int32)
+        if self._box.shape != (3,) or self._grid.shape != (3,):
+            raise ValueError("box and grid need three entries")
+        n = positions.numel() // 3
+        h = ctypes.c_void_p()
+        _check(lib.halo_plan_create_device(
+            ctypes.c_void_p(positions.data_ptr()) if n else None, n, _np_ptr(self._box),
+            _np_ptr(self._grid), ctypes.c_float(cutoff),
+            _stream_handle(stream, positions.get_device()), ctypes.byref(h)))
+        self._finish(h, n)
+        return self
+
+    def _finish(self, h, n_atoms):
+        lib = load_library()
         self._h = h
-        self.n_atoms = pos.shape[0]
+        self.n_atoms = n_atoms
         self.total_slots = lib.halo_plan_total_slots(h)
         self.num_domains = lib.halo_plan_num_domains(h)
         self.num_pulses = lib.halo_plan_num_pulses(h)
@@ -179,6 +211,17 @@ class HaloPlan:
         return dict(send_to=v[0].value, send_size=v[1].value, recv_from=v[2].value,
                     recv_size=v[3].value, atom_offset=v[4].value, dep_start=v[5].value,
                     items=v[6].value, shift=shift, index_map=im[:v[1].value].copy())
+
+    def item_waits(self):
+        """(segment, xwait_mask, await_mask) of every work item, launch order."""
+        lib = load_library()
+        out = np.zeros((self.num_items, 3), np.int64)
+        sg, xm, am = ctypes.c_int32(), ctypes.c_uint32(), ctypes.c_uint32()
+        for i in range(self.num_items):
+            _check(lib.halo_plan_item_waits(self._h, i, ctypes.byref(sg), ctypes.byref(xm),
+                                            ctypes.byref(am)))
+            out[i] = (sg.value, xm.value, am.value)
+        return out
 
     # -- device side ------------------------------------------------------------
     def _buf(self, t):

@@ -52,19 +52,22 @@ def build(verbose: bool = True) -> str:
     _run(["g++", *HOST_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o])
     _run([_hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, "halo_api.hip"), "-o",
           api_o])
+    dev_o = os.path.join(BUILD_DIR, "plan_device.o")
+    _run([_hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, "plan_device.hip"), "-o",
+          dev_o])
     tmp = LIB + ".tmp"
     _run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, api_o,
-          plan_o])
+          dev_o, plan_o])
     os.replace(tmp, LIB)
     return LIB
 
 
-def asm(out_path: str | None = None) -> str:
-    """Write the gfx950 assembly of the kernels (for inspection)."""
-    out_path = out_path or os.path.join(BUILD_DIR, "halo_api.s")
+def asm(out_path: str | None = None, source: str = "halo_api.hip") -> str:
+    """Write the gfx950 assembly of one source's kernels (for inspection)."""
+    out_path = out_path or os.path.join(BUILD_DIR, source.replace(".hip", ".s"))
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     _run([_hipcc(), *HIP_FLAGS, "-I", INCLUDE, "--cuda-device-only", "-S",
-          os.path.join(CSRC, "halo_api.hip"), "-o", out_path])
+          os.path.join(CSRC, source), "-o", out_path])
     return out_path
 
 

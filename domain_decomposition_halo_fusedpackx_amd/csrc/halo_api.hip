@@ -29,6 +29,7 @@
 
 #include "../../include/halo.h"
 #include "plan.hpp"
+#include "plan_state.hpp"
 #include "sync.hpp"
 
 using halo::WorkItem;
@@ -689,36 +690,6 @@ __global__ __launch_bounds__(kThreads) void k_stage_unpack(
 
 }  // namespace
 
-struct halo_plan {
-    halo::HostPlan h;
-    int device = -1;
-    bool uploaded = false;
-    bool poisoned = false;
-    int32_t *d_idx = nullptr;
-    WorkItem *d_items = nullptr;
-    int32_t *d_recv_from = nullptr;
-    int32_t *d_send_to = nullptr;
-    uint32_t *d_seg_items = nullptr;
-    uint32_t *d_state = nullptr;
-    size_t state_words = 0;
-    uint32_t *h_err = nullptr;  // pinned host word, written by kernels on a timeout
-    uint32_t *d_err = nullptr;  // its device address
-    // transposed form
-    uint8_t *d_mask = nullptr;
-    halo::Chunk *d_chunks = nullptr;
-    int32_t *d_forder = nullptr;
-    int32_t *d_dest_start = nullptr;
-    float *d_shift4 = nullptr;
-    uint32_t *d_x_arrivals = nullptr;
-    uint32_t *d_zone_chunks = nullptr;
-    // staged baseline: one float triple per indexMap entry, allocated on first use
-    float *d_stage = nullptr;
-    // epochs: work-item kernels (x, f) and chunk kernels (xc, fc); each family
-    // counts in its own block of state
-    uint32_t epoch_x = 0, epoch_f = 0, epoch_xc = 0, epoch_fc = 0;
-    uint32_t spin_limit = 1u << 20;
-    int32_t withhold = -1;
-};
 
 namespace {
 
@@ -729,36 +700,32 @@ halo_status hip_fail(hipError_t e, const char *what)
 
 void free_device(halo_plan *p)
 {
-    if (p->d_idx) (void)hipFree(p->d_idx);
-    if (p->d_items) (void)hipFree(p->d_items);
-    if (p->d_recv_from) (void)hipFree(p->d_recv_from);
-    if (p->d_send_to) (void)hipFree(p->d_send_to);
-    if (p->d_stage) (void)hipFree(p->d_stage);
-    if (p->d_seg_items) (void)hipFree(p->d_seg_items);
-    if (p->d_state) (void)hipFree(p->d_state);
-    if (p->h_err) (void)hipHostFree(p->h_err);
-    for (void *q : {(void *)p->d_mask, (void *)p->d_chunks, (void *)p->d_forder,
-                    (void *)p->d_dest_start, (void *)p->d_shift4,
-                    (void *)p->d_x_arrivals, (void *)p->d_zone_chunks})
+    for (void *q : {(void *)p->d_idx, (void *)p->d_items, (void *)p->d_recv_from,
+                    (void *)p->d_send_to, (void *)p->d_stage, (void *)p->d_seg_items,
+                    (void *)p->d_state, (void *)p->d_mask, (void *)p->d_chunks,
+                    (void *)p->d_forder, (void *)p->d_dest_start, (void *)p->d_shift4,
+                    (void *)p->d_x_arrivals, (void *)p->d_zone_chunks, (void *)p->d_local_map,
+                    (void *)p->d_home_slot})
         if (q) (void)hipFree(q);
+    if (p->h_err) (void)hipHostFree(p->h_err);
+    p->d_idx = p->d_recv_from = p->d_send_to = p->d_forder = p->d_dest_start = nullptr;
+    p->d_local_map = nullptr;
+    p->d_home_slot = nullptr;
+    p->d_items = nullptr;
+    p->d_stage = p->d_shift4 = nullptr;
+    p->d_seg_items = p->d_state = p->d_x_arrivals = p->d_zone_chunks = nullptr;
     p->d_mask = nullptr;
     p->d_chunks = nullptr;
-    p->d_forder = p->d_dest_start = nullptr;
-    p->d_shift4 = nullptr;
-    p->d_x_arrivals = p->d_zone_chunks = nullptr;
-    p->d_idx = nullptr;
-    p->d_items = nullptr;
-    p->d_recv_from = p->d_send_to = nullptr;
-    p->d_stage = nullptr;
-    p->d_seg_items = nullptr;
-    p->d_state = nullptr;
     p->h_err = p->d_err = nullptr;
     p->uploaded = false;
 }
 
+// Copy v to a new device array at *dst, unless *dst already exists (arrays a
+// device-side build produced in place).
 template <class T>
 hipError_t upload_vec(T **dst, const std::vector<T> &v)
 {
+    if (*dst) return hipSuccess;
     size_t bytes = std::max<size_t>(v.size() * sizeof(T), 16);
     hipError_t e = hipMalloc((void **)dst, bytes);
     if (e != hipSuccess) return e;
@@ -902,6 +869,8 @@ halo_status ensure_uploaded(halo_plan *p)
     if (p->uploaded) return HALO_OK;
     hipError_t e;
     if ((e = hipGetDevice(&p->device)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (p->built_on_device && !p->d_idx)
+        return fail(HALO_ERR_STATE, "halo_plan_upload: device-built plan lost its device arrays");
     const halo::HostPlan &h = p->h;
     if ((e = upload_vec(&p->d_idx, h.abs_map)) != hipSuccess ||
         (e = upload_vec(&p->d_items, h.items)) != hipSuccess ||
@@ -937,6 +906,12 @@ halo_status ensure_uploaded(halo_plan *p)
     p->uploaded = true;
     return HALO_OK;
 }
+
+}  // namespace
+
+int halo::plan_upload(halo_plan *p) { return ensure_uploaded(p); }
+
+namespace {
 
 halo_status check_exchange(halo_plan *p, float *buf, const char *what)
 {
@@ -999,6 +974,37 @@ halo_status halo_plan_create(const float *positions, int64_t n_atoms, const floa
     return HALO_OK;
 }
 
+halo_status halo_plan_create_device(const float *positions, int64_t n_atoms, const float *box,
+                                    const int32_t *grid, float cutoff, void *stream,
+                                    halo_plan **out)
+{
+    if (!out) return fail(HALO_ERR_ARG, "halo_plan_create_device: NULL output pointer");
+    *out = nullptr;
+    halo_plan *p = new (std::nothrow) halo_plan();
+    if (!p) return fail(HALO_ERR_NOMEM, "halo_plan_create_device: out of host memory");
+    std::string msg;
+    int rc;
+    g_last_error.clear();
+    try {
+        rc = halo::build_plan_device(p, positions, n_atoms, box, grid, cutoff,
+                                     item_entries_from_env(), (hipStream_t)stream, msg);
+    } catch (const std::bad_alloc &) {
+        rc = halo::kErrNoMem;
+        msg = "halo_plan_create_device: out of host memory";
+    } catch (const std::exception &ex) {
+        rc = halo::kErrArg;
+        msg = std::string("halo_plan_create_device: internal error: ") + ex.what();
+    }
+    if (rc != halo::kOk) {
+        free_device(p);
+        delete p;
+        // an upload failure has already set the message
+        return msg.empty() ? (halo_status)rc : fail((halo_status)rc, msg);
+    }
+    *out = p;
+    return HALO_OK;
+}
+
 void halo_plan_destroy(halo_plan *plan)
 {
     if (!plan) return;
@@ -1031,10 +1037,38 @@ halo_status halo_plan_domain(const halo_plan *p, int32_t d, int64_t *base, int32
     return HALO_OK;
 }
 
+// Host copies of a device-built plan's indexMap and home slots, fetched on
+// first use (a blocking copy).
+static halo_status ensure_host_maps(const halo_plan *cp)
+{
+    halo_plan *p = const_cast<halo_plan *>(cp);
+    halo::HostPlan &h = p->h;
+    if (!p->built_on_device) return HALO_OK;
+    hipError_t e;
+    if ((int64_t)h.local_map.size() != h.n_entries) {
+        std::vector<int32_t> m((size_t)h.n_entries);
+        if (h.n_entries > 0 &&
+            (e = hipMemcpy(m.data(), p->d_local_map, m.size() * 4, hipMemcpyDeviceToHost)) !=
+                hipSuccess)
+            return hip_fail(e, "fetching the indexMap");
+        h.local_map.swap(m);
+    }
+    if ((int64_t)h.home_slot.size() != h.n_atoms) {
+        std::vector<int64_t> hs((size_t)h.n_atoms);
+        if (h.n_atoms > 0 &&
+            (e = hipMemcpy(hs.data(), p->d_home_slot, hs.size() * 8, hipMemcpyDeviceToHost)) !=
+                hipSuccess)
+            return hip_fail(e, "fetching the home slots");
+        h.home_slot.swap(hs);
+    }
+    return HALO_OK;
+}
+
 halo_status halo_plan_home_slots(const halo_plan *p, int64_t *slot_of_atom)
 {
     if (!p || (!slot_of_atom && p->h.n_atoms > 0))
         return fail(HALO_ERR_ARG, "halo_plan_home_slots: NULL argument");
+    if (halo_status st = ensure_host_maps(p); st != HALO_OK) return st;
     if (p->h.n_atoms > 0)
         std::memcpy(slot_of_atom, p->h.home_slot.data(), (size_t)p->h.n_atoms * sizeof(int64_t));
     return HALO_OK;
@@ -1057,8 +1091,27 @@ halo_status halo_plan_pulse(const halo_plan *p, int32_t pulse, int32_t d, int32_
     if (items) *items = s.n_items;
     if (shift)
         for (int c = 0; c < 3; ++c) shift[c] = s.shift[c];
-    if (index_map && s.send_size > 0)
+    if (index_map && s.send_size > 0) {
+        if (halo_status st = ensure_host_maps(p); st != HALO_OK) return st;
         std::memcpy(index_map, p->h.local_map.data() + s.map_off, (size_t)s.send_size * 4);
+    }
+    return HALO_OK;
+}
+
+halo_status halo_plan_item_waits(const halo_plan *p, int32_t item, int32_t *segment,
+                                 uint32_t *xwait_mask, uint32_t *await_mask)
+{
+    if (!p || item < 0 || item >= (int32_t)p->h.items.size())
+        return fail(HALO_ERR_ARG, "halo_plan_item_waits: no such work item");
+    halo::WorkItem it = p->h.items[item];
+    if (p->built_on_device) {
+        // the wait masks were computed on the device
+        hipError_t e = hipMemcpy(&it, p->d_items + item, sizeof(it), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "halo_plan_item_waits");
+    }
+    if (segment) *segment = it.seg;
+    if (xwait_mask) *xwait_mask = it.xwait_mask;
+    if (await_mask) *await_mask = it.await_mask;
     return HALO_OK;
 }
 

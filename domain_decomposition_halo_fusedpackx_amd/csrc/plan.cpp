@@ -81,13 +81,9 @@ inline int32_t domain_of_cell(const int32_t *grid, const int32_t *c)
 
 }  // namespace
 
-int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,
-               float cutoff, int32_t item_entries, HostPlan &P, std::string &msg)
+int plan_geometry(int64_t n_atoms, const float *box, const int32_t *grid, float cutoff,
+                  HostPlan &P, std::string &msg)
 {
-    if (n_atoms < 0 || !box || !grid || (n_atoms > 0 && !pos)) {
-        msg = "halo_plan_create: NULL pointer or negative atom count";
-        return kErrArg;
-    }
     P = HostPlan();
     P.n_atoms = n_atoms;
     P.cutoff = cutoff;
@@ -118,15 +114,6 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
             P.pulses_in[d] = (int32_t)np;
         }
     }
-    for (int64_t a = 0; a < n_atoms; ++a)
-        for (int d = 0; d < 3; ++d) {
-            float v = pos[3 * a + d];
-            if (!std::isfinite(v) || !(v >= 0.f) || !(v < box[d])) {
-                msg = "halo_plan_create: atom " + std::to_string((long long)a) +
-                      " lies outside [0, L) or is not finite";
-                return kErrRange;
-            }
-        }
     int64_t nd = (int64_t)grid[0] * grid[1] * grid[2];
     if (nd > std::numeric_limits<int32_t>::max() / 64) {
         msg = "halo_plan_create: too many domains";
@@ -144,6 +131,42 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
               " pulses; at most " + std::to_string(kMaxPulses) + " are supported";
         return kErrGeometry;
     }
+    // Receiver and sender of every (pulse, domain): data flows to the lower
+    // neighbour along the pulse's dimension, periodically.
+    P.send_to.assign((size_t)P.n_pulse * P.n_dom, 0);
+    P.recv_from.assign((size_t)P.n_pulse * P.n_dom, 0);
+    for (int32_t p = 0; p < P.n_pulse; ++p) {
+        const int dim = P.pulse_dim[p];
+        for (int32_t D = 0; D < P.n_dom; ++D) {
+            Cell3 cd = cell_of_domain(grid, D);
+            int32_t cr[3] = {cd.c[0], cd.c[1], cd.c[2]};
+            cr[dim] = cd.c[dim] == 0 ? grid[dim] - 1 : cd.c[dim] - 1;
+            const int32_t R = domain_of_cell(grid, cr);
+            P.send_to[(size_t)p * P.n_dom + D] = R;
+            P.recv_from[(size_t)p * P.n_dom + R] = D;
+        }
+    }
+    return kOk;
+}
+
+int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,
+               float cutoff, int32_t item_entries, HostPlan &P, std::string &msg)
+{
+    if (n_atoms < 0 || !box || !grid || (n_atoms > 0 && !pos)) {
+        msg = "halo_plan_create: NULL pointer or negative atom count";
+        return kErrArg;
+    }
+    int rc = plan_geometry(n_atoms, box, grid, cutoff, P, msg);
+    if (rc != kOk) return rc;
+    for (int64_t a = 0; a < n_atoms; ++a)
+        for (int d = 0; d < 3; ++d) {
+            float v = pos[3 * a + d];
+            if (!std::isfinite(v) || !(v >= 0.f) || !(v < box[d])) {
+                msg = "halo_plan_create: atom " + std::to_string((long long)a) +
+                      " lies outside [0, L) or is not finite";
+                return kErrRange;
+            }
+        }
 
     // Position in units of the domain width; a rounding up to n is pulled
     // back below n so that the cell index stays in range.
@@ -186,10 +209,9 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
         // Phase 1 reads only the sender's own slots.
         parallel_for(P.n_dom, [&](int32_t D) {
             Cell3 cd = cell_of_domain(grid, D);
-            int32_t cr[3] = {cd.c[0], cd.c[1], cd.c[2]};
-            cr[dim] = cd.c[dim] == 0 ? n - 1 : cd.c[dim] - 1;
             Segment &s = row[D];
-            s.send_to = domain_of_cell(grid, cr);
+            s.send_to = P.send_to[(size_t)p * P.n_dom + D];
+            const int32_t c_recv = cell_of_domain(grid, s.send_to).c[dim];
             s.shift[0] = s.shift[1] = s.shift[2] = 0.f;
             if (cd.c[dim] == 0) s.shift[dim] = box[dim];
             // Candidate slots: all of them on the first pulse of a dimension,
@@ -200,7 +222,7 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
                 first = prev.atom_offset;
                 last = prev.atom_offset + prev.recv_size;
             }
-            const double face = (double)(cr[dim] + 1);
+            const double face = (double)(c_recv + 1);
             std::vector<int32_t> &out = prow[D];
             std::vector<int64_t> &mv = moving[D];
             mv.clear();
@@ -259,12 +281,7 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
     P.n_entries = entries;
     P.local_map.resize((size_t)entries);
     P.abs_map.resize((size_t)entries);
-    P.send_to.assign(P.seg.size(), 0);
-    P.recv_from.assign(P.seg.size(), 0);
-    for (size_t i = 0; i < P.seg.size(); ++i) {
-        P.send_to[i] = P.seg[i].send_to;
-        P.recv_from[i] = P.seg[i].recv_from;
-    }
+
     for (int32_t p = 0; p < P.n_pulse; ++p)
         for (int32_t D = 0; D < P.n_dom; ++D) {
             const Segment &s = P.seg[(size_t)p * P.n_dom + D];
@@ -334,14 +351,14 @@ static uint32_t atomic_force_waits(const HostPlan &P, int32_t p, int32_t D)
 }
 
 static void cut_span(HostPlan &P, int32_t p, int32_t D, int32_t lo, int32_t hi,
-                     int32_t item_entries, bool keep_empty)
+                     int32_t item_entries, bool keep_empty, bool with_masks)
 {
     Segment &s = P.seg[(size_t)p * P.n_dom + D];
     const Segment &rs = P.at(p, s.send_to);
     const int32_t len = hi - lo;
     int32_t n = (len + item_entries - 1) / item_entries;
     if (n == 0 && keep_empty) n = 1;
-    const uint32_t aw = n > 0 ? atomic_force_waits(P, p, D) : 0u;
+    const uint32_t aw = n > 0 && with_masks ? atomic_force_waits(P, p, D) : 0u;
     for (int32_t j = 0; j < n; ++j) {
         const int32_t b = lo + (int32_t)((int64_t)len * j / n);
         const int32_t e = lo + (int32_t)((int64_t)len * (j + 1) / n);
@@ -357,7 +374,7 @@ static void cut_span(HostPlan &P, int32_t p, int32_t D, int32_t lo, int32_t hi,
         // earlier pulse).
         it.xwait_mask = 0;
         int32_t r = 0;
-        for (int32_t i = b + it.n_indep; i < e; ++i) {
+        for (int32_t i = b + it.n_indep; with_masks && i < e; ++i) {
             const int32_t slot = P.local_map[s.map_off + i];
             while (r < p && !(slot >= P.at(r, D).atom_offset &&
                               slot < P.at(r, D).atom_offset + P.at(r, D).recv_size))
@@ -386,7 +403,7 @@ static void cut_span(HostPlan &P, int32_t p, int32_t D, int32_t lo, int32_t hi,
     }
 }
 
-void make_items(HostPlan &P, int32_t item_entries)
+void make_items(HostPlan &P, int32_t item_entries, bool with_masks)
 {
     P.item_entries = item_entries;
     P.items.clear();
@@ -407,9 +424,10 @@ void make_items(HostPlan &P, int32_t item_entries)
                 // an empty segment keeps one (empty) item in its first group
                 const bool keep_empty = s.send_size == 0 && pass == 0;
                 if (indep)
-                    cut_span(P, p, D, 0, s.dep_start, item_entries, keep_empty);
+                    cut_span(P, p, D, 0, s.dep_start, item_entries, keep_empty, with_masks);
                 else
-                    cut_span(P, p, D, s.dep_start, s.send_size, item_entries, keep_empty);
+                    cut_span(P, p, D, s.dep_start, s.send_size, item_entries, keep_empty,
+                             with_masks);
             }
             if (xcd_ordering_enabled()) xcd_order(P.items, group, P.n_dom);
         }
@@ -417,34 +435,16 @@ void make_items(HostPlan &P, int32_t item_entries)
     P.pulse_item_off[P.n_pulse] = (int32_t)P.items.size();
 }
 
-void make_chunks(HostPlan &P, int32_t chunk_slots)
+bool plan_has_chunks(const HostPlan &P)
 {
-    P.chunk_slots = chunk_slots;
-    P.chunks.clear();
-    P.chunk_forder.clear();
-    P.has_chunks = P.n_pulse > 0 && P.n_pulse <= kMaxMaskPulses && P.total_slots > 0;
-    if (!P.has_chunks) return;
-    const int32_t nd = P.n_dom, np = P.n_pulse;
-    P.slot_mask.assign((size_t)P.total_slots, 0);
-    P.dest_start.assign((size_t)np * nd, 0);
-    P.shift4.assign((size_t)np * nd * 4, 0.f);
-    P.x_arrivals.assign((size_t)np * nd, 0);
-    P.zone_chunks.assign((size_t)np * nd, 0);
-    for (int32_t p = 0; p < np; ++p)
-        for (int32_t D = 0; D < nd; ++D) {
-            const Segment &s = P.at(p, D);
-            const Segment &r = P.at(p, s.send_to);
-            P.dest_start[(size_t)p * nd + D] = (int32_t)(P.base[s.send_to] + r.atom_offset);
-            for (int c = 0; c < 3; ++c) P.shift4[((size_t)p * nd + D) * 4 + c] = s.shift[c];
-            for (int32_t i = 0; i < s.send_size; ++i)
-                P.slot_mask[(size_t)(P.base[D] + P.local_map[s.map_off + i])] |= (uint8_t)(1u << p);
-        }
-    // Zones of every domain in slot order: home, then the region of each pulse.
-    // zone_chunks_by_zone[z] collects the chunks of zone z (-1 -> index 0).
-    std::vector<std::vector<Chunk>> by_zone(np + 1);
-    for (int32_t D = 0; D < nd; ++D) {
-        int32_t rank[kMaxMaskPulses] = {0};
-        for (int32_t z = -1; z < np; ++z) {
+    return P.n_pulse > 0 && P.n_pulse <= kMaxMaskPulses && P.total_slots > 0;
+}
+
+std::vector<Piece> chunk_pieces(const HostPlan &P, int32_t chunk_slots)
+{
+    std::vector<Piece> out;
+    for (int32_t D = 0; D < P.n_dom; ++D)
+        for (int32_t z = -1; z < P.n_pulse; ++z) {
             int32_t lo, hi;
             if (z < 0) {
                 lo = 0;
@@ -458,27 +458,60 @@ void make_chunks(HostPlan &P, int32_t chunk_slots)
             for (int32_t k = 0; k < pieces; ++k) {
                 const int32_t a = lo + (int32_t)((int64_t)len * k / pieces);
                 const int32_t b = lo + (int32_t)((int64_t)len * (k + 1) / pieces);
-                Chunk c{};
-                c.first = (int32_t)(P.base[D] + a);
-                c.count = b - a;
-                c.domain = D;
-                c.zone = z;
-                c.mask = 0;
-                for (int32_t q = 0; q < kMaxMaskPulses; ++q) c.rank[q] = rank[q];
-                for (int32_t sl = a; sl < b; ++sl) {
-                    const uint32_t m = P.slot_mask[(size_t)(P.base[D] + sl)];
-                    c.mask |= m;
-                    for (int32_t q = 0; q < np; ++q) rank[q] += (m >> q) & 1u;
-                }
-                c.xwait = z < 0 ? -1 : z * nd + P.at(z, D).recv_from;
-                if (c.mask == 0) continue;  // nothing to send from or add into
-                by_zone[z + 1].push_back(c);
+                out.push_back(Piece{(int32_t)(P.base[D] + a), b - a, D, z});
             }
         }
-        for (int32_t q = 0; q < np; ++q) {
-            if (rank[q] != P.at(q, D).send_size) throw std::logic_error("mask ranks disagree");
+    return out;
+}
+
+void finish_chunks(HostPlan &P, int32_t chunk_slots, const std::vector<Piece> &pieces,
+                   const std::vector<PieceStats> &stats)
+{
+    const int32_t nd = P.n_dom, np = P.n_pulse;
+    P.chunk_slots = chunk_slots;
+    P.dest_start.assign((size_t)np * nd, 0);
+    P.shift4.assign((size_t)np * nd * 4, 0.f);
+    P.x_arrivals.assign((size_t)np * nd, 0);
+    P.zone_chunks.assign((size_t)np * nd, 0);
+    for (int32_t p = 0; p < np; ++p)
+        for (int32_t D = 0; D < nd; ++D) {
+            const Segment &s = P.at(p, D);
+            const Segment &r = P.at(p, s.send_to);
+            P.dest_start[(size_t)p * nd + D] = (int32_t)(P.base[s.send_to] + r.atom_offset);
+            for (int c = 0; c < 3; ++c) P.shift4[((size_t)p * nd + D) * 4 + c] = s.shift[c];
         }
+    // Pieces come per domain in slot order (home, then the region of each
+    // pulse); a chunk's rank[q] counts the bit-q slots of its domain before it.
+    std::vector<std::vector<Chunk>> by_zone(np + 1);
+    int32_t rank[kMaxMaskPulses] = {0};
+    int32_t cur = -1;
+    for (size_t i = 0; i < pieces.size(); ++i) {
+        const Piece &pc = pieces[i];
+        if (pc.domain != cur) {
+            if (cur >= 0)
+                for (int32_t q = 0; q < np; ++q)
+                    if (rank[q] != P.at(q, cur).send_size)
+                        throw std::logic_error("mask ranks disagree");
+            cur = pc.domain;
+            for (int32_t q = 0; q < kMaxMaskPulses; ++q) rank[q] = 0;
+        }
+        Chunk c{};
+        c.first = pc.first;
+        c.count = pc.count;
+        c.domain = pc.domain;
+        c.zone = pc.zone;
+        c.mask = stats[i].mask;
+        for (int32_t q = 0; q < kMaxMaskPulses; ++q) c.rank[q] = rank[q];
+        for (int32_t q = 0; q < np; ++q) rank[q] += stats[i].count[q];
+        c.xwait = pc.zone < 0 ? -1 : pc.zone * nd + P.at(pc.zone, pc.domain).recv_from;
+        if (c.mask == 0) continue;  // nothing to send from or add into
+        by_zone[pc.zone + 1].push_back(c);
     }
+    if (cur >= 0)
+        for (int32_t q = 0; q < np; ++q)
+            if (rank[q] != P.at(q, cur).send_size) throw std::logic_error("mask ranks disagree");
+    P.chunks.clear();
+    P.chunk_forder.clear();
     for (int32_t z = 0; z <= np; ++z)
         for (const Chunk &c : by_zone[z]) {
             P.chunks.push_back(c);
@@ -492,6 +525,35 @@ void make_chunks(HostPlan &P, int32_t chunk_slots)
     for (int32_t z = 0; z <= np; ++z) zone_off[z + 1] = zone_off[z] + (int32_t)by_zone[z].size();
     for (int32_t z = np; z >= 0; --z)
         for (int32_t i = zone_off[z]; i < zone_off[z + 1]; ++i) P.chunk_forder.push_back(i);
+}
+
+void make_chunks(HostPlan &P, int32_t chunk_slots)
+{
+    P.chunk_slots = chunk_slots;
+    P.chunks.clear();
+    P.chunk_forder.clear();
+    P.has_chunks = plan_has_chunks(P);
+    if (!P.has_chunks) return;
+    P.slot_mask.assign((size_t)P.total_slots, 0);
+    for (int32_t p = 0; p < P.n_pulse; ++p)
+        for (int32_t D = 0; D < P.n_dom; ++D) {
+            const Segment &s = P.at(p, D);
+            for (int32_t i = 0; i < s.send_size; ++i)
+                P.slot_mask[(size_t)(P.base[D] + P.local_map[s.map_off + i])] |= (uint8_t)(1u << p);
+        }
+    const std::vector<Piece> pieces = chunk_pieces(P, chunk_slots);
+    std::vector<PieceStats> stats(pieces.size());
+    for (size_t i = 0; i < pieces.size(); ++i) {
+        PieceStats &st = stats[i];
+        st.mask = 0;
+        for (int32_t q = 0; q < kMaxMaskPulses; ++q) st.count[q] = 0;
+        for (int32_t sl = pieces[i].first; sl < pieces[i].first + pieces[i].count; ++sl) {
+            const uint32_t m = P.slot_mask[(size_t)sl];
+            st.mask |= m;
+            for (int32_t q = 0; q < P.n_pulse; ++q) st.count[q] += (int32_t)((m >> q) & 1u);
+        }
+    }
+    finish_chunks(P, chunk_slots, pieces, stats);
 }
 
 }  // namespace halo

@@ -128,7 +128,7 @@ constexpr int32_t kMaxPulses = 32;
 constexpr int64_t kMaxSlots = ((int64_t)1 << 31) / 12 - 1;
 
 // Status codes shared with halo.h.
-enum : int { kOk = 0, kErrArg = -1, kErrGeometry = -2, kErrRange = -3, kErrNoMem = -7 };
+enum : int { kOk = 0, kErrArg = -1, kErrGeometry = -2, kErrRange = -3, kErrHip = -4, kErrNoMem = -7 };
 
 // Whether make_items places the items of one domain on one XCD.
 bool xcd_ordering_enabled();
@@ -136,12 +136,40 @@ bool xcd_ordering_enabled();
 // Build the transposed form (masks and chunks of at most chunk_slots slots).
 void make_chunks(HostPlan &plan, int32_t chunk_slots);
 
+// The transposed form exists for plans with 1..kMaxMaskPulses pulses.
+bool plan_has_chunks(const HostPlan &plan);
+
+// Chunk candidates: every zone of every domain cut into balanced pieces of
+// at most chunk_slots slots, per domain in slot order.
+struct Piece {
+    int32_t first;   // absolute first slot
+    int32_t count;
+    int32_t domain;
+    int32_t zone;    // -1 home, r >= 0 region of pulse r
+};
+struct PieceStats {
+    uint32_t mask;                   // union of the slots' pulse masks
+    int32_t count[kMaxMaskPulses];   // slots with bit q
+};
+std::vector<Piece> chunk_pieces(const HostPlan &plan, int32_t chunk_slots);
+
+// Chunks, ranks, per-zone counts and the force-direction order from the
+// pieces and their statistics (pieces with an empty mask are dropped).
+void finish_chunks(HostPlan &plan, int32_t chunk_slots, const std::vector<Piece> &pieces,
+                   const std::vector<PieceStats> &stats);
+
+// Geometry of a plan: validates box, grid and cutoff and fills widths,
+// reaches, the pulse list and the send/receive tables.
+int plan_geometry(int64_t n_atoms, const float *box, const int32_t *grid, float cutoff,
+                  HostPlan &plan, std::string &msg);
+
 // Build the plan; returns a status code and a message on failure.
 int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,
                float cutoff, int32_t item_entries, HostPlan &out, std::string &msg);
 
-// Cut every segment into work items of at most item_entries entries and
-// compute their wait lists.
-void make_items(HostPlan &plan, int32_t item_entries);
+// Cut every segment into work items of at most item_entries entries and,
+// with with_masks, compute their wait masks from the indexMaps (without, the
+// masks are left 0 for the caller to fill).
+void make_items(HostPlan &plan, int32_t item_entries, bool with_masks = true);
 
 }  // namespace halo

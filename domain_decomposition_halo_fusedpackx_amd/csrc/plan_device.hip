@@ -1,0 +1,725 @@
+// plan_device.hip -- build the exchange plan on the GPU from device-resident
+// positions, for repartitioning steps.
+//
+// Same plan as plan.cpp, and the same readings of "Redesigning GROMACS Halo
+// Exchange" (paper review), s.3 and Algorithms 1 and 4: the domain of an atom
+// is floor(min(x / w, nextafter(n, 0))) per dimension in double precision;
+// home atoms in ascending id; pulses z, then y, then x; an atom is sent when
+// its original position lies less than cutoff / w above the receiver's upper
+// face (periodically); candidates are all slots on the first pulse of a
+// dimension and the previous pulse's region otherwise; indexMap ascending;
+// slots of a domain = [home | region per pulse], domains in id order.
+//
+// The work that grows with the atoms and the entries runs in kernels:
+//   k_owner          domain of every atom, range check, per-tile histogram
+//   k_tile_scan      per domain, exclusive scan of the tile histogram
+//   k_home_scatter   stable counting sort: home atoms of every domain in
+//                    ascending id (wave-level key grouping, waves in order)
+//   k_select<false>  per (pulse, domain): how many candidates are sent, and
+//                    how many of them are home slots (depOffset split)
+//   k_select<true>   the same selection writing the indexMap (local slots)
+//                    and the id of every sent atom, by stable compaction
+//   k_abs_map        indexMap entries as absolute slots
+//   k_home_slot      slot of every atom
+//   k_mask           per-slot pulse masks of the transposed form
+//   k_item_masks     wait masks of the work items
+//   k_piece_stats    union mask and per-pulse counts of every chunk candidate
+// and the host keeps the O(domains x pulses + items + chunks) bookkeeping:
+// prefix sums over domains, the receivers' region offsets, the layout, the
+// work items and the chunk order. The host reads back a few small tables
+// (one synchronisation per pulse, one for the layout, one for the chunks).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <limits>
+#include <string>
+#include <vector>
+
+#include "plan.hpp"
+#include "plan_state.hpp"
+
+namespace halo {
+namespace {
+
+constexpr int kBT = 256;                 // threads per block
+constexpr int kTile = 2048;              // atoms per histogram tile (8 per thread)
+constexpr int32_t kMaxDeviceDomains = 8192;  // LDS histogram of 32 KiB
+
+struct Geom {
+    double width[3];
+    double top[3];  // nextafter(n_d, 0): scaled positions are clamped below n_d
+    float box[3];
+    int32_t grid[3];
+};
+
+__device__ __forceinline__ double scaled(float v, double width, double top)
+{
+    double s = (double)v / width;
+    return s > top ? top : s;
+}
+
+// Exclusive prefix of v over the block's threads (in thread order); total
+// receives the block sum. Every thread of the block must call it.
+__device__ uint32_t block_scan_excl(uint32_t v, uint32_t &total)
+{
+    __shared__ uint32_t ws[kBT / 64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) ws[w] = x;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kBT / 64; ++i) {
+        if (i < w) off += ws[i];
+        tot += ws[i];
+    }
+    __syncthreads();
+    total = tot;
+    return off + x - v;
+}
+
+__device__ __forceinline__ uint64_t lanes_below(int lane)
+{
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Position of the thread among the block's threads with flag set (thread
+// order); total receives their number.
+__device__ uint32_t block_rank(bool flag, uint32_t &total)
+{
+    __shared__ uint32_t wc[kBT / 64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint64_t b = __ballot(flag);
+    if (lane == 0) wc[w] = (uint32_t)__popcll(b);
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kBT / 64; ++i) {
+        if (i < w) off += wc[i];
+        tot += wc[i];
+    }
+    __syncthreads();
+    total = tot;
+    return off + (uint32_t)__popcll(b & lanes_below(lane));
+}
+
+// Domain of every atom (0 for an atom out of range, whose smallest index goes
+// to *bad) and the tile's histogram over domains, stored domain-major.
+__global__ __launch_bounds__(kBT) void k_owner(const float *__restrict__ pos, int64_t n_atoms,
+                                               Geom g, int32_t n_dom, int32_t n_tiles,
+                                               int32_t *__restrict__ owner,
+                                               uint32_t *__restrict__ tile_hist,
+                                               unsigned long long *bad)
+{
+    extern __shared__ uint32_t hist[];
+    for (int32_t d = threadIdx.x; d < n_dom; d += kBT) hist[d] = 0;
+    __syncthreads();
+    const int64_t t0 = (int64_t)blockIdx.x * kTile;
+    for (int j = 0; j < kTile / kBT; ++j) {
+        const int64_t a = t0 + j * kBT + threadIdx.x;
+        if (a < n_atoms) {
+            bool ok = true;
+            int32_t c[3];
+#pragma unroll
+            for (int d = 0; d < 3; ++d) {
+                const float v = pos[3 * a + d];
+                if (!(__builtin_isfinite(v) && v >= 0.f && v < g.box[d])) ok = false;
+                c[d] = ok ? (int32_t)floor(scaled(v, g.width[d], g.top[d])) : 0;
+            }
+            const int32_t dom = ok ? c[0] + g.grid[0] * (c[1] + g.grid[1] * c[2]) : 0;
+            if (!ok) atomicMin(bad, (unsigned long long)a);
+            owner[a] = dom;
+            atomicAdd(&hist[dom], 1u);
+        }
+    }
+    __syncthreads();
+    for (int32_t d = threadIdx.x; d < n_dom; d += kBT)
+        tile_hist[(size_t)d * n_tiles + blockIdx.x] = hist[d];
+}
+
+// Block d: exclusive scan over the tiles of domain d's histogram row (in
+// place); n_home[d] = the row total.
+__global__ __launch_bounds__(kBT) void k_tile_scan(uint32_t *__restrict__ tile_hist,
+                                                   int32_t n_tiles, int32_t *__restrict__ n_home)
+{
+    uint32_t *row = tile_hist + (size_t)blockIdx.x * n_tiles;
+    uint32_t carry = 0;
+    for (int32_t b = 0; b < n_tiles; b += kBT) {
+        const int32_t t = b + threadIdx.x;
+        const uint32_t v = t < n_tiles ? row[t] : 0u;
+        uint32_t tot;
+        const uint32_t ex = block_scan_excl(v, tot);
+        if (t < n_tiles) row[t] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) n_home[blockIdx.x] = (int32_t)carry;
+}
+
+// Stable counting sort of the atoms by domain. Block = tile; LDS counters
+// start at the tile's offsets within each domain. In each round of 256 atoms
+// a wave groups its lanes by domain (a lane's rank = lanes below it with the
+// same domain), then the waves add their group sizes to the counters one
+// after the other, so that lower ids get lower ranks.
+__global__ __launch_bounds__(kBT) void k_home_scatter(const int32_t *__restrict__ owner,
+                                                      int64_t n_atoms, int32_t n_dom,
+                                                      int32_t n_tiles,
+                                                      const uint32_t *__restrict__ tile_off,
+                                                      const int32_t *__restrict__ home_start,
+                                                      int32_t *__restrict__ home_gid,
+                                                      int32_t *__restrict__ home_rank)
+{
+    extern __shared__ uint32_t cnt[];
+    for (int32_t d = threadIdx.x; d < n_dom; d += kBT)
+        cnt[d] = tile_off[(size_t)d * n_tiles + blockIdx.x];
+    __syncthreads();
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int j = 0; j < kTile / kBT; ++j) {
+        const int64_t a = (int64_t)blockIdx.x * kTile + j * kBT + threadIdx.x;
+        const bool valid = a < n_atoms;
+        const int32_t key = valid ? owner[a] : -1;
+        uint64_t todo = __ballot(valid);
+        uint32_t my_rank = 0, grp = 0;
+        int my_leader = 0;
+        while (todo) {
+            const int leader = __ffsll((unsigned long long)todo) - 1;
+            const int32_t k = __shfl(key, leader, 64);
+            const bool mine = valid && key == k;
+            const uint64_t m = __ballot(mine);
+            if (mine) {
+                my_rank = (uint32_t)__popcll(m & lanes_below(lane));
+                my_leader = leader;
+                grp = (uint32_t)__popcll(m);
+            }
+            todo &= ~m;
+        }
+        uint32_t base = 0;
+        for (int t = 0; t < kBT / 64; ++t) {
+            if (w == t && valid && lane == my_leader) {
+                base = cnt[key];
+                cnt[key] = base + grp;
+            }
+            __syncthreads();
+        }
+        base = (uint32_t)__shfl((int)base, my_leader, 64);
+        if (valid) {
+            const uint32_t r = base + my_rank;
+            home_gid[home_start[key] + (int32_t)r] = (int32_t)a;
+            home_rank[a] = (int32_t)r;
+        }
+    }
+}
+
+// Device copy of the segment table, [pulse][domain] arrays.
+struct SegTable {
+    int32_t *send_size, *dep_start, *recv_size, *atom_offset, *map_off;
+};
+
+// Selection of pulse p for domain D = blockIdx.x. Candidates in ascending
+// local slot: the home slots and every region received so far (k == 0), or
+// the region of the previous pulse (k > 0). A candidate is sent when its
+// atom's original position lies less than reach above the receiver's upper
+// face. WRITE == false: store the send count and how many candidates were
+// home slots; WRITE == true: store the indexMap (local slots) and the sent
+// atoms' ids from map_off on, in candidate order.
+template <bool WRITE>
+__global__ __launch_bounds__(kBT) void k_select(
+    const float *__restrict__ pos, int32_t p, int32_t dim, int32_t k, int32_t n_dom, Geom g,
+    double reach, const int32_t *__restrict__ send_to, const int32_t *__restrict__ recv_from,
+    const int32_t *__restrict__ n_home, const int32_t *__restrict__ home_start,
+    const int32_t *__restrict__ home_gid, SegTable seg, const int32_t *entry_gid,
+    int32_t *__restrict__ local_map, int32_t *gid_out)
+{
+    const int32_t D = blockIdx.x;
+    const int32_t R = send_to[p * n_dom + D];
+    int32_t c_r;  // receiver's cell index along dim
+    if (dim == 0)
+        c_r = R % g.grid[0];
+    else if (dim == 1)
+        c_r = (R / g.grid[0]) % g.grid[1];
+    else
+        c_r = R / (g.grid[0] * g.grid[1]);
+    const double face = (double)(c_r + 1);
+    const double ncell = (double)g.grid[dim];
+    const int32_t out0 = WRITE ? seg.map_off[p * n_dom + D] : 0;
+    const int32_t limit = WRITE ? seg.send_size[p * n_dom + D] : 0;
+    uint32_t count = 0, dep = 0;
+    const int32_t zfirst = k == 0 ? -1 : p - 1;
+    for (int32_t z = zfirst; z < p; ++z) {
+        int32_t len, slot0;
+        const int32_t *gids;
+        if (z < 0) {
+            len = n_home[D];
+            slot0 = 0;
+            gids = home_gid + home_start[D];
+        } else {
+            const int32_t S = recv_from[z * n_dom + D];
+            len = seg.recv_size[z * n_dom + D];
+            slot0 = seg.atom_offset[z * n_dom + D];
+            gids = entry_gid + seg.map_off[z * n_dom + S];
+        }
+        for (int32_t b = 0; b < len; b += kBT) {
+            const int32_t i = b + (int32_t)threadIdx.x;
+            bool flag = false;
+            int32_t gid = 0;
+            if (i < len) {
+                gid = gids[i];
+                double above = scaled(pos[3 * (int64_t)gid + dim], g.width[dim], g.top[dim]) - face;
+                if (above < 0.0) above += ncell;
+                flag = above < reach;
+            }
+            uint32_t tot;
+            const uint32_t r = block_rank(flag, tot);
+            if (WRITE && flag && (int32_t)(count + r) < limit) {
+                local_map[out0 + (int32_t)(count + r)] = slot0 + i;
+                gid_out[out0 + (int32_t)(count + r)] = gid;
+            }
+            count += tot;
+            if (z < 0) dep += tot;
+        }
+    }
+    if (!WRITE && threadIdx.x == 0) {
+        seg.send_size[p * n_dom + D] = (int32_t)count;
+        seg.dep_start[p * n_dom + D] = (int32_t)dep;
+    }
+}
+
+// Block = segment (pulse-major): absolute slots of its indexMap entries.
+__global__ __launch_bounds__(kBT) void k_abs_map(const int32_t *__restrict__ local_map,
+                                                 SegTable seg, int32_t n_dom,
+                                                 const int64_t *__restrict__ base,
+                                                 int32_t *__restrict__ abs_map)
+{
+    const int32_t s = blockIdx.x;
+    const int32_t D = s % n_dom;
+    const int32_t m0 = seg.map_off[s], n = seg.send_size[s];
+    const int64_t b = base[D];
+    for (int32_t i = threadIdx.x; i < n; i += kBT) abs_map[m0 + i] = (int32_t)(b + local_map[m0 + i]);
+}
+
+__global__ __launch_bounds__(kBT) void k_home_slot(const int32_t *__restrict__ owner,
+                                                   const int32_t *__restrict__ home_rank,
+                                                   const int64_t *__restrict__ base,
+                                                   int64_t n_atoms, int64_t *__restrict__ slot)
+{
+    const int64_t a = (int64_t)blockIdx.x * kBT + threadIdx.x;
+    if (a < n_atoms) slot[a] = base[owner[a]] + home_rank[a];
+}
+
+// Bit p on the slots sent in pulse p (entries [e0, e1)). A slot appears at
+// most once per pulse, and pulses run as separate launches.
+__global__ __launch_bounds__(kBT) void k_mask(const int32_t *__restrict__ abs_map, int32_t e0,
+                                              int32_t e1, int32_t p, uint8_t *__restrict__ mask)
+{
+    const int32_t e = e0 + (int32_t)(blockIdx.x * kBT + threadIdx.x);
+    if (e < e1) {
+        const int32_t s = abs_map[e];
+        mask[s] = (uint8_t)(mask[s] | (1u << p));
+    }
+}
+
+// Block = work item: the pulses whose regions its dependent entries read
+// (coordinate direction) and, for the atomic force exchange, the later pulses
+// q whose segment (q, receiver) has targets in the region the item reads.
+__global__ __launch_bounds__(kBT) void k_item_masks(WorkItem *__restrict__ items,
+                                                    const int32_t *__restrict__ local_map,
+                                                    SegTable seg, int32_t n_dom,
+                                                    int32_t n_pulse)
+{
+    __shared__ uint32_t xm;
+    WorkItem *it = items + blockIdx.x;
+    const int32_t s = it->seg, p = s / n_dom, D = s % n_dom, R = it->receiver;
+    if (threadIdx.x == 0) xm = 0;
+    __syncthreads();
+    uint32_t mine = 0;
+    for (int32_t i = it->n_indep + (int32_t)threadIdx.x; i < it->n_total; i += kBT) {
+        const int32_t slot = local_map[it->map_begin + i];
+        for (int32_t r = 0; r < p; ++r) {
+            const int32_t lo = seg.atom_offset[r * n_dom + D];
+            if (slot >= lo && slot < lo + seg.recv_size[r * n_dom + D]) {
+                mine |= 1u << r;
+                break;
+            }
+        }
+    }
+    if (mine) atomicOr(&xm, mine);
+    // the item's sources: R's region of pulse p
+    const int32_t lo = seg.atom_offset[p * n_dom + R];
+    const int32_t hi = lo + seg.recv_size[p * n_dom + R];
+    uint32_t am = 0;
+    const int32_t q = p + 1 + (int32_t)threadIdx.x;
+    if (q < n_pulse && lo < hi) {
+        const int32_t *m = local_map + seg.map_off[q * n_dom + R];
+        int32_t a = 0, b = seg.send_size[q * n_dom + R];
+        while (a < b) {  // first entry >= lo
+            const int32_t mid = a + (b - a) / 2;
+            if (m[mid] < lo)
+                a = mid + 1;
+            else
+                b = mid;
+        }
+        if (a < seg.send_size[q * n_dom + R] && m[a] < hi) am = 1u << q;
+    }
+    __shared__ uint32_t amask;
+    if (threadIdx.x == 0) amask = 0;
+    __syncthreads();
+    if (am) atomicOr(&amask, am);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        it->xwait_mask = xm;
+        it->await_mask = amask;
+    }
+}
+
+// Block = chunk candidate: union of its slots' masks and the number of slots
+// with each pulse bit.
+__global__ __launch_bounds__(kBT) void k_piece_stats(const Piece *__restrict__ pieces,
+                                                     const uint8_t *__restrict__ mask,
+                                                     int32_t n_pulse,
+                                                     PieceStats *__restrict__ stats)
+{
+    __shared__ uint32_t um;
+    __shared__ int32_t cnt[kMaxMaskPulses];
+    if (threadIdx.x == 0) um = 0;
+    if (threadIdx.x < kMaxMaskPulses) cnt[threadIdx.x] = 0;
+    __syncthreads();
+    const Piece pc = pieces[blockIdx.x];
+    uint32_t u = 0;
+    int32_t c[kMaxMaskPulses] = {0};
+    for (int32_t i = threadIdx.x; i < pc.count; i += kBT) {
+        const uint32_t m = mask[pc.first + i];
+        u |= m;
+#pragma unroll
+        for (int q = 0; q < kMaxMaskPulses; ++q) c[q] += (int32_t)((m >> q) & 1u);
+    }
+    if (u) atomicOr(&um, u);
+#pragma unroll
+    for (int q = 0; q < kMaxMaskPulses; ++q)
+        if (q < n_pulse && c[q]) atomicAdd(&cnt[q], c[q]);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        stats[blockIdx.x].mask = um;
+        for (int q = 0; q < kMaxMaskPulses; ++q) stats[blockIdx.x].count[q] = cnt[q];
+    }
+}
+
+// Device arrays of one build; freed on every exit unless released.
+struct DevArrays {
+    std::vector<void *> owned;
+    template <class T>
+    hipError_t alloc(T **p, size_t n)
+    {
+        *p = nullptr;
+        hipError_t e = hipMalloc((void **)p, std::max<size_t>(n, 1) * sizeof(T));
+        if (e == hipSuccess) owned.push_back((void *)*p);
+        return e;
+    }
+    void release(void *p)
+    {
+        for (auto &q : owned)
+            if (q == p) q = nullptr;
+    }
+    ~DevArrays()
+    {
+        for (void *p : owned)
+            if (p) (void)hipFree(p);
+    }
+};
+
+unsigned grid_for(int64_t n, int per_block) { return (unsigned)((n + per_block - 1) / per_block); }
+
+}  // namespace
+
+int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const float *box,
+                      const int32_t *grid, float cutoff, int32_t item_entries, hipStream_t st,
+                      std::string &msg)
+{
+    if (n_atoms < 0 || !box || !grid || (n_atoms > 0 && !pos)) {
+        msg = "halo_plan_create_device: NULL pointer or negative atom count";
+        return kErrArg;
+    }
+    HostPlan &P = pl->h;
+    int rc = plan_geometry(n_atoms, box, grid, cutoff, P, msg);
+    if (rc != kOk) return rc;
+    if (P.n_dom > kMaxDeviceDomains) {
+        msg = "halo_plan_create_device: at most " + std::to_string(kMaxDeviceDomains) +
+              " domains (use halo_plan_create)";
+        return kErrGeometry;
+    }
+    if (n_atoms > kMaxSlots) {
+        msg = "halo_plan_create_device: too many atoms for one plan";
+        return kErrRange;
+    }
+    const int32_t nd = P.n_dom, np = P.n_pulse;
+    Geom g;
+    for (int d = 0; d < 3; ++d) {
+        g.width[d] = P.width[d];
+        g.top[d] = std::nextafter((double)grid[d], 0.0);
+        g.box[d] = box[d];
+        g.grid[d] = grid[d];
+    }
+    DevArrays A;
+    hipError_t e = hipSuccess;
+    auto hip_err = [&](const char *what) {
+        msg = std::string("halo_plan_create_device: ") + what + ": " + hipGetErrorString(e);
+        return kErrHip;
+    };
+#define HALO_TRY(call, what)            \
+    do {                                \
+        if ((e = (call)) != hipSuccess) \
+            return hip_err(what);       \
+    } while (0)
+
+    // -- domains and home order ------------------------------------------------
+    const int32_t n_tiles = (int32_t)std::max<int64_t>(1, (n_atoms + kTile - 1) / kTile);
+    int32_t *owner, *home_rank, *home_gid, *d_n_home, *d_home_start;
+    uint32_t *tile_hist;
+    unsigned long long *bad;
+    HALO_TRY(A.alloc(&owner, n_atoms), "hipMalloc");
+    HALO_TRY(A.alloc(&home_rank, n_atoms), "hipMalloc");
+    HALO_TRY(A.alloc(&home_gid, n_atoms), "hipMalloc");
+    HALO_TRY(A.alloc(&d_n_home, nd), "hipMalloc");
+    HALO_TRY(A.alloc(&d_home_start, nd), "hipMalloc");
+    HALO_TRY(A.alloc(&tile_hist, (size_t)nd * n_tiles), "hipMalloc");
+    HALO_TRY(A.alloc(&bad, 1), "hipMalloc");
+    const unsigned long long none = ~0ull;
+    HALO_TRY(hipMemcpyAsync(bad, &none, sizeof(none), hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+    const size_t lds = (size_t)nd * sizeof(uint32_t);
+    if (n_atoms > 0) {
+        k_owner<<<n_tiles, kBT, lds, st>>>(pos, n_atoms, g, nd, n_tiles, owner, tile_hist, bad);
+    } else {
+        HALO_TRY(hipMemsetAsync(tile_hist, 0, (size_t)nd * n_tiles * 4, st), "hipMemsetAsync");
+    }
+    k_tile_scan<<<nd, kBT, 0, st>>>(tile_hist, n_tiles, d_n_home);
+    HALO_TRY(hipGetLastError(), "launch");
+    unsigned long long first_bad = 0;
+    P.n_home.assign(nd, 0);
+    HALO_TRY(hipMemcpyAsync(&first_bad, bad, sizeof(first_bad), hipMemcpyDeviceToHost, st),
+             "hipMemcpyAsync");
+    HALO_TRY(hipMemcpyAsync(P.n_home.data(), d_n_home, (size_t)nd * 4, hipMemcpyDeviceToHost, st),
+             "hipMemcpyAsync");
+    HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
+    if (first_bad != none) {
+        msg = "halo_plan_create: atom " + std::to_string(first_bad) +
+              " lies outside [0, L) or is not finite";
+        return kErrRange;
+    }
+    std::vector<int32_t> home_start(nd, 0);
+    {
+        int64_t acc = 0;
+        for (int32_t d = 0; d < nd; ++d) {
+            home_start[d] = (int32_t)acc;
+            acc += P.n_home[d];
+        }
+        if (acc != n_atoms) {
+            msg = "halo_plan_create_device: internal error: home counts do not add up";
+            return kErrArg;
+        }
+    }
+    HALO_TRY(hipMemcpyAsync(d_home_start, home_start.data(), (size_t)nd * 4,
+                            hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+    if (n_atoms > 0)
+        k_home_scatter<<<n_tiles, kBT, lds, st>>>(owner, n_atoms, nd, n_tiles, tile_hist,
+                                                  d_home_start, home_gid, home_rank);
+    HALO_TRY(hipGetLastError(), "launch");
+
+    // -- pulses -------------------------------------------------------------------
+    const size_t nseg = (size_t)np * nd;
+    P.seg.assign(nseg, Segment());
+    SegTable sg;
+    int32_t *d_send_to, *d_recv_from, *local_map, *entry_gid;
+    HALO_TRY(A.alloc(&sg.send_size, nseg), "hipMalloc");
+    HALO_TRY(A.alloc(&sg.dep_start, nseg), "hipMalloc");
+    HALO_TRY(A.alloc(&sg.recv_size, nseg), "hipMalloc");
+    HALO_TRY(A.alloc(&sg.atom_offset, nseg), "hipMalloc");
+    HALO_TRY(A.alloc(&sg.map_off, nseg), "hipMalloc");
+    HALO_TRY(A.alloc(&d_send_to, nseg), "hipMalloc");
+    HALO_TRY(A.alloc(&d_recv_from, nseg), "hipMalloc");
+    HALO_TRY(hipMemcpyAsync(d_send_to, P.send_to.data(), nseg * 4, hipMemcpyHostToDevice, st),
+             "hipMemcpyAsync");
+    HALO_TRY(hipMemcpyAsync(d_recv_from, P.recv_from.data(), nseg * 4, hipMemcpyHostToDevice, st),
+             "hipMemcpyAsync");
+    // entry arrays grow with the pulses (sizes become known pulse by pulse)
+    size_t cap = std::max<size_t>(1024, (size_t)n_atoms * 2);
+    HALO_TRY(A.alloc(&local_map, cap), "hipMalloc");
+    HALO_TRY(A.alloc(&entry_gid, cap), "hipMalloc");
+    std::vector<int32_t> cur(P.n_home.begin(), P.n_home.end());
+    std::vector<int32_t> send_size(nd), dep_start(nd), row_map(nd), row_recv(nd), row_off(nd);
+    int64_t entries = 0;
+    for (int32_t p = 0; p < np; ++p) {
+        const int dim = P.pulse_dim[p];
+        const int32_t k = P.pulse_k[p];
+        const size_t r0 = (size_t)p * nd;
+        k_select<false><<<nd, kBT, 0, st>>>(pos, p, dim, k, nd, g, P.reach[dim], d_send_to,
+                                            d_recv_from, d_n_home, d_home_start, home_gid, sg,
+                                            entry_gid, local_map, entry_gid);
+        HALO_TRY(hipGetLastError(), "launch");
+        HALO_TRY(hipMemcpyAsync(send_size.data(), sg.send_size + r0, (size_t)nd * 4,
+                                hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
+        HALO_TRY(hipMemcpyAsync(dep_start.data(), sg.dep_start + r0, (size_t)nd * 4,
+                                hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
+        HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
+        // map offsets (pulse-major, then domain) and the receivers' regions
+        const int64_t entries_before = entries;
+        for (int32_t D = 0; D < nd; ++D) {
+            Segment &s = P.seg[r0 + D];
+            s.send_to = P.send_to[r0 + D];
+            s.send_size = send_size[D];
+            s.dep_start = dep_start[D];
+            s.map_off = entries;
+            row_map[D] = (int32_t)entries;
+            entries += send_size[D];
+            const int32_t cd = dim == 0   ? D % grid[0]
+                               : dim == 1 ? (D / grid[0]) % grid[1]
+                                          : D / (grid[0] * grid[1]);
+            s.shift[0] = s.shift[1] = s.shift[2] = 0.f;
+            if (cd == 0) s.shift[dim] = box[dim];
+        }
+        if (entries > kMaxSlots) {
+            msg = "halo_plan_create_device: too many halo entries for one plan";
+            return kErrRange;
+        }
+        for (int32_t D = 0; D < nd; ++D) {
+            const int32_t R = P.send_to[r0 + D];
+            Segment &r = P.seg[r0 + R];
+            r.recv_from = D;
+            r.recv_size = send_size[D];
+            r.atom_offset = cur[R];
+            cur[R] += send_size[D];
+        }
+        for (int32_t D = 0; D < nd; ++D) {
+            row_recv[D] = P.seg[r0 + D].recv_size;
+            row_off[D] = P.seg[r0 + D].atom_offset;
+        }
+        HALO_TRY(hipMemcpyAsync(sg.map_off + r0, row_map.data(), (size_t)nd * 4,
+                                hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+        HALO_TRY(hipMemcpyAsync(sg.recv_size + r0, row_recv.data(), (size_t)nd * 4,
+                                hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+        HALO_TRY(hipMemcpyAsync(sg.atom_offset + r0, row_off.data(), (size_t)nd * 4,
+                                hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+        if ((size_t)entries > cap) {
+            const size_t ncap = std::max<size_t>((size_t)entries, cap * 2);
+            int32_t *nl, *ng;
+            HALO_TRY(A.alloc(&nl, ncap), "hipMalloc");
+            HALO_TRY(A.alloc(&ng, ncap), "hipMalloc");
+            const size_t used = (size_t)entries_before;
+            if (used > 0) {
+                HALO_TRY(hipMemcpyAsync(nl, local_map, used * 4, hipMemcpyDeviceToDevice, st),
+                         "hipMemcpyAsync");
+                HALO_TRY(hipMemcpyAsync(ng, entry_gid, used * 4, hipMemcpyDeviceToDevice, st),
+                         "hipMemcpyAsync");
+            }
+            HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
+            A.release(local_map);
+            A.release(entry_gid);
+            (void)hipFree(local_map);
+            (void)hipFree(entry_gid);
+            local_map = nl;
+            entry_gid = ng;
+            cap = ncap;
+        }
+        k_select<true><<<nd, kBT, 0, st>>>(pos, p, dim, k, nd, g, P.reach[dim], d_send_to,
+                                           d_recv_from, d_n_home, d_home_start, home_gid, sg,
+                                           entry_gid, local_map, entry_gid);
+        HALO_TRY(hipGetLastError(), "launch");
+    }
+
+    // -- layout ---------------------------------------------------------------------
+    P.base.assign(nd, 0);
+    P.n_halo.assign(nd, 0);
+    int64_t acc = 0;
+    for (int32_t d = 0; d < nd; ++d) {
+        P.base[d] = acc;
+        P.n_halo[d] = cur[d] - P.n_home[d];
+        acc += cur[d];
+    }
+    P.total_slots = acc;
+    if (acc > kMaxSlots) {
+        msg = "halo_plan_create: more than " + std::to_string((long long)kMaxSlots) +
+              " slots (2 GiB of float triples) in one plan";
+        return kErrRange;
+    }
+    P.n_entries = entries;
+    int64_t *d_base, *home_slot;
+    int32_t *abs_map;
+    HALO_TRY(A.alloc(&d_base, nd), "hipMalloc");
+    HALO_TRY(A.alloc(&home_slot, n_atoms), "hipMalloc");
+    HALO_TRY(A.alloc(&abs_map, entries), "hipMalloc");
+    HALO_TRY(hipMemcpyAsync(d_base, P.base.data(), (size_t)nd * 8, hipMemcpyHostToDevice, st),
+             "hipMemcpyAsync");
+    if (nseg > 0) k_abs_map<<<(unsigned)nseg, kBT, 0, st>>>(local_map, sg, nd, d_base, abs_map);
+    if (n_atoms > 0)
+        k_home_slot<<<grid_for(n_atoms, kBT), kBT, 0, st>>>(owner, home_rank, d_base, n_atoms,
+                                                            home_slot);
+    HALO_TRY(hipGetLastError(), "launch");
+
+    // -- work items (host order, device wait masks) -----------------------------------
+    make_items(P, item_entries, false);
+    WorkItem *items;
+    HALO_TRY(A.alloc(&items, P.items.size()), "hipMalloc");
+    if (!P.items.empty()) {
+        HALO_TRY(hipMemcpyAsync(items, P.items.data(), P.items.size() * sizeof(WorkItem),
+                                hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+        k_item_masks<<<(unsigned)P.items.size(), kBT, 0, st>>>(items, local_map, sg, nd, np);
+        HALO_TRY(hipGetLastError(), "launch");
+    }
+
+    // -- transposed form -----------------------------------------------------------------
+    uint8_t *mask = nullptr;
+    P.has_chunks = plan_has_chunks(P);
+    P.chunk_slots = item_entries;
+    if (P.has_chunks) {
+        HALO_TRY(A.alloc(&mask, (size_t)P.total_slots), "hipMalloc");
+        HALO_TRY(hipMemsetAsync(mask, 0, (size_t)P.total_slots, st), "hipMemsetAsync");
+        for (int32_t p = 0; p < np; ++p) {
+            const int32_t e0 = (int32_t)P.at(p, 0).map_off;
+            const int32_t e1 = p + 1 < np ? (int32_t)P.at(p + 1, 0).map_off : (int32_t)entries;
+            if (e1 > e0) k_mask<<<grid_for(e1 - e0, kBT), kBT, 0, st>>>(abs_map, e0, e1, p, mask);
+        }
+        const std::vector<Piece> pieces = chunk_pieces(P, item_entries);
+        std::vector<PieceStats> stats(pieces.size());
+        if (!pieces.empty()) {
+            Piece *d_pieces;
+            PieceStats *d_stats;
+            HALO_TRY(A.alloc(&d_pieces, pieces.size()), "hipMalloc");
+            HALO_TRY(A.alloc(&d_stats, pieces.size()), "hipMalloc");
+            HALO_TRY(hipMemcpyAsync(d_pieces, pieces.data(), pieces.size() * sizeof(Piece),
+                                    hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+            k_piece_stats<<<(unsigned)pieces.size(), kBT, 0, st>>>(d_pieces, mask, np, d_stats);
+            HALO_TRY(hipGetLastError(), "launch");
+            HALO_TRY(hipMemcpyAsync(stats.data(), d_stats, stats.size() * sizeof(PieceStats),
+                                    hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
+        }
+        HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
+        try {
+            finish_chunks(P, item_entries, pieces, stats);
+        } catch (const std::exception &ex) {
+            msg = std::string("halo_plan_create_device: internal error: ") + ex.what();
+            return kErrArg;
+        }
+    }
+    HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
+
+    // hand the device arrays to the plan
+    pl->d_idx = abs_map;
+    pl->d_items = items;
+    pl->d_mask = mask;
+    pl->d_local_map = local_map;
+    pl->d_home_slot = home_slot;
+    pl->d_send_to = d_send_to;
+    pl->d_recv_from = d_recv_from;
+    for (void *q : {(void *)abs_map, (void *)items, (void *)mask, (void *)local_map,
+                    (void *)home_slot, (void *)d_send_to, (void *)d_recv_from})
+        A.release(q);
+    pl->built_on_device = true;
+#undef HALO_TRY
+    return plan_upload(pl);
+}
+
+}  // namespace halo

@@ -1,0 +1,59 @@
+// plan_state.hpp -- what a halo_plan holds: the host-side plan and its device
+// copy (shared by the C-ABI and the device-side plan builder).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "plan.hpp"
+
+struct halo_plan {
+    halo::HostPlan h;
+    int device = -1;
+    bool uploaded = false;
+    bool poisoned = false;
+    bool built_on_device = false;  // host copies of the maps are fetched on first use
+    int32_t *d_idx = nullptr;      // concatenated indexMap, absolute slots
+    halo::WorkItem *d_items = nullptr;
+    int32_t *d_recv_from = nullptr;
+    int32_t *d_send_to = nullptr;
+    uint32_t *d_seg_items = nullptr;
+    uint32_t *d_state = nullptr;
+    size_t state_words = 0;
+    uint32_t *h_err = nullptr;  // pinned host word, written by kernels on a timeout
+    uint32_t *d_err = nullptr;  // its device address
+    // transposed form
+    uint8_t *d_mask = nullptr;
+    halo::Chunk *d_chunks = nullptr;
+    int32_t *d_forder = nullptr;
+    int32_t *d_dest_start = nullptr;
+    float *d_shift4 = nullptr;
+    uint32_t *d_x_arrivals = nullptr;
+    uint32_t *d_zone_chunks = nullptr;
+    // staged baseline: one float triple per indexMap entry, allocated on first use
+    float *d_stage = nullptr;
+    // device-built plans: local-slot indexMap and home slot of every atom
+    int32_t *d_local_map = nullptr;
+    int64_t *d_home_slot = nullptr;
+    // epochs: work-item kernels (x, f) and chunk kernels (xc, fc); each family
+    // counts in its own block of state
+    uint32_t epoch_x = 0, epoch_f = 0, epoch_xc = 0, epoch_fc = 0;
+    uint32_t spin_limit = 1u << 20;
+    int32_t withhold = -1;
+};
+
+namespace halo {
+
+// Allocate and fill whatever device copy of the plan is still missing (arrays
+// already on the device are kept), the counters and the error word.
+// Returns a halo_status code; the message goes to halo_last_error.
+int plan_upload(halo_plan *p);
+
+// Build p->h and its device arrays on the GPU from device-resident positions
+// (plan_device.hip). Returns a status code and a message on failure.
+int build_plan_device(halo_plan *p, const float *pos, int64_t n_atoms, const float *box,
+                      const int32_t *grid, float cutoff, int32_t item_entries, hipStream_t stream,
+                      std::string &msg);
+
+}  // namespace halo

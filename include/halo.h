@@ -77,6 +77,25 @@ typedef enum {
 halo_status halo_plan_create(const float *positions, int64_t n_atoms, const float *box,
                              const int32_t *grid, float cutoff, halo_plan **out);
 
+/* Build the same plan on the GPU from device-resident positions, for
+ * repartitioning steps of a GPU-resident simulation (the pages rebuild the
+ * halo metadata at every domain-decomposition / neighbour-search step; see
+ * "Redesigning GROMACS Halo Exchange", s.3 and Algorithms 1 and 4). The
+ * result is identical to halo_plan_create on the same positions: layout,
+ * home slots, every PulseData field and the exchanges' results.
+ *   positions : DEVICE, n_atoms*3 float32 on the current device, read on
+ *               `stream` (so work queued there before the call is seen)
+ *   stream    : a hipStream_t; the call synchronises it a few times (it reads
+ *               back per-pulse sizes) and returns with the plan uploaded
+ *   others    : as halo_plan_create.
+ * Limits: at most 8192 domains (HALO_ERR_GEOMETRY beyond). A position not
+ * finite or outside [0, L) gives HALO_ERR_RANGE naming the first such atom.
+ * The host copies of the indexMaps and home slots (halo_plan_pulse's
+ * index_map, halo_plan_home_slots) are fetched from the device on first use. */
+halo_status halo_plan_create_device(const float *positions, int64_t n_atoms, const float *box,
+                                    const int32_t *grid, float cutoff, void *stream,
+                                    halo_plan **out);
+
 /* Free the plan and its device metadata (NULL is accepted). Waits for nothing:
  * the caller must make sure no exchange on the plan is still running. */
 void halo_plan_destroy(halo_plan *plan);
@@ -119,6 +138,16 @@ halo_status halo_plan_pulse(const halo_plan *plan, int32_t p, int32_t d, int32_t
                             int32_t *index_map);
 
 /* ---- device side ------------------------------------------------------------------- */
+
+/* Work item `item` (0 <= item < halo_plan_num_items) of the index-list
+ * kernels, in launch order: its segment (pulse * num_domains + sending
+ * domain); the pulses whose regions its dependent entries read (bit r: the
+ * region the sender received in pulse r; the coordinate exchange waits for
+ * their arrival, Algorithm 4); and, for halo_exchange_f_atomic, the later
+ * pulses q whose segment (q, receiver) adds into the region the item reads.
+ * Any output may be NULL. A read-out for tests and tools. */
+halo_status halo_plan_item_waits(const halo_plan *plan, int32_t item, int32_t *segment,
+                                 uint32_t *xwait_mask, uint32_t *await_mask);
 
 /* Allocate and upload the device metadata on the current HIP device (blocking).
  * Called implicitly by the first exchange. */

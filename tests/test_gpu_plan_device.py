@@ -1,0 +1,127 @@
+"""The plan built on the GPU (halo_plan_create_device) against the oracle.
+
+A device-built plan must be the same plan: layout, home slots, every
+PulseData field (sendSize, recvSize, atomOffset, coordShift, indexMap,
+depOffset split) equal to the oracle's, the same work items with the same
+wait masks as the host-built plan, and exchanges bitwise equal to the
+oracle's.
+"""
+import numpy as np
+import pytest
+
+from domain_decomposition_halo_fusedpackx_amd import HaloError, HaloPlan
+from domain_decomposition_halo_fusedpackx_amd import workloads as W
+
+from .test_gpu_parity import IMPLS, assert_bitwise, exchange, say, torch  # noqa: F401
+from .test_oracle_pins import TINY
+from .test_plan_host import compare_plans
+
+pytestmark = pytest.mark.gpu
+
+
+def device_plan(torch, pos, box, grid, rc):
+    t = torch.from_numpy(np.ascontiguousarray(pos, np.float32).reshape(-1, 3)).cuda()
+    return HaloPlan.on_device(t, box, grid, rc)
+
+
+def check_same_plan(torch, oracle_mod, pos, box, grid, rc, tag):
+    say(f"{tag}: device plan build")
+    dp = device_plan(torch, pos, box, grid, rc)
+    o = oracle_mod.Oracle(pos, box, grid, rc)
+    compare_plans(dp, o)
+    hp = HaloPlan(pos, box, grid, rc)
+    assert dp.num_items == hp.num_items
+    for p in range(o.n_pulse):
+        for d in range(o.n_dom):
+            assert dp.pulse(p, d)["items"] == hp.pulse(p, d)["items"]
+    np.testing.assert_array_equal(dp.item_waits(), hp.item_waits())
+    return dp, o
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_device_plan_equals_oracle_on_workloads(torch, oracle_mod, wid):
+    w = W.WORKLOADS[wid]
+    check_same_plan(torch, oracle_mod, W.workload_positions(w), w.box, w.grid, w.cutoff, w.name)
+
+
+@pytest.mark.parametrize("case", TINY, ids=lambda c: "x".join(map(str, c[1])))
+def test_device_plan_equals_oracle_on_tiny_boxes(torch, oracle_mod, case):
+    box, grid, rc, n = case
+    for seed in (1, 2):
+        check_same_plan(torch, oracle_mod, W.positions(box, n, seed), box, grid, rc,
+                        "tiny" + "x".join(map(str, grid)))
+
+
+def test_device_plan_edge_cases(torch, oracle_mod):
+    cases = [
+        ("empty", np.zeros((0, 3), np.float32), (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
+        ("one-domain", W.positions((2.0, 2.0, 2.0), 50, 3), (2.0, 2.0, 2.0), (1, 1, 1), 0.9),
+        ("all-in-one-domain", W.positions((1.0, 1.0, 1.0), 64, 4) + np.float32(2.5),
+         (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
+        ("one-atom", np.array([[0.1, 0.1, 0.1]], np.float32), (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
+        ("on-faces", np.array([[0.0, 0.0, 0.0], [2.0, 2.0, 2.0], [1.0, 3.0, 2.0],
+                               [np.nextafter(np.float32(4), np.float32(0))] * 3], np.float32),
+         (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
+        ("more-atoms-than-a-tile", W.positions((6.0, 6.0, 6.0), 5000, 8), (6.0, 6.0, 6.0),
+         (3, 2, 1), 1.0),
+    ]
+    for name, pos, box, grid, rc in cases:
+        check_same_plan(torch, oracle_mod, pos, box, grid, rc, name)
+
+
+@pytest.mark.parametrize("wid", [2, 4, 5])
+def test_exchanges_on_device_plans(torch, oracle_mod, wid):
+    w = W.WORKLOADS[wid]
+    pos = W.workload_positions(w)
+    dp = device_plan(torch, pos, w.box, w.grid, w.cutoff)
+    o = oracle_mod.Oracle(pos, w.box, w.grid, w.cutoff)
+    x0 = o.home_filled(np.nan)
+    want_x = o.exchange_x(x0.copy())
+    base, n_home, n_halo = o.domains()
+    f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, w.seed)
+    want_f = o.exchange_f(f0.copy())
+    for impl in IMPLS:
+        say(f"{w.name} device plan, {impl}")
+        x = torch.from_numpy(x0.copy()).cuda()
+        exchange(dp, impl, "x", x)
+        f = torch.from_numpy(f0.copy()).cuda()
+        exchange(dp, impl, "f", f)
+        torch.cuda.synchronize()
+        dp.sync()
+        assert_bitwise(x.cpu().numpy(), want_x, f"{impl} x")
+        assert_bitwise(f.cpu().numpy(), want_f, f"{impl} f")
+
+
+def test_repartition_sequence(torch, oracle_mod):
+    """Rebuild on the device for new positions (a repartitioning step) several
+    times; every plan equals the oracle's for its positions."""
+    w = W.WORKLOADS[3]
+    for seed in (11, 12, 13):
+        pos = W.positions(w.box, w.n_atoms, seed)
+        check_same_plan(torch, oracle_mod, pos, w.box, w.grid, w.cutoff, f"repartition {seed}")
+
+
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -0.5, 2.0, 7.0])
+def test_device_plan_range_errors(torch, oracle_mod, bad):
+    pos = W.positions((2.0, 2.0, 2.0), 10, 1)
+    pos[7, 0] = bad
+    pos[3, 2] = bad
+    want = oracle_mod.try_build(pos, (2.0, 2.0, 2.0), (2, 2, 2), 0.5)
+    with pytest.raises(HaloError) as e:
+        device_plan(torch, pos, (2.0, 2.0, 2.0), (2, 2, 2), 0.5)
+    assert e.value.code == want == -3
+    assert "atom 3 " in str(e.value)
+
+
+@pytest.mark.parametrize("args", [
+    ((2.0, 2.0, 2.0), (2, 2, 2), 1.5),
+    ((2.0, 2.0, 2.0), (1, 1, 1), 0.0),
+    ((2.0, 0.0, 2.0), (1, 1, 1), 0.5),
+    ((2.0, 2.0, 2.0), (1, 0, 1), 0.5),
+])
+def test_device_plan_geometry_errors(torch, oracle_mod, args):
+    pos = W.positions((2.0, 2.0, 2.0), 10, 1)
+    want = oracle_mod.try_build(pos, *args)
+    with pytest.raises(HaloError) as e:
+        device_plan(torch, pos, *args)
+    assert e.value.code == want

@@ -104,3 +104,46 @@ def test_item_cutting(monkeypatch):
                 assert q["items"] == max(1, -(-q["dep_start"] // n) + -(-dep // n))
                 tot += q["items"]
         assert tot == plan.num_items
+
+
+def _region_of(o, p, d, slot):
+    for r in range(p):
+        q = o.pulse(r, d)
+        if q["atom_offset"] <= slot < q["atom_offset"] + q["recv_size"]:
+            return r
+    return None
+
+
+@pytest.mark.parametrize("wid", [2, 4])
+def test_item_wait_masks(oracle_mod, wid):
+    """Every work item's wait masks follow from the oracle's PulseData: the
+    regions its dependent entries read, and the later pulses of the receiver
+    that add into the region it reads."""
+    w = W.WORKLOADS[wid]
+    pos = W.workload_positions(w)
+    plan = HaloPlan(pos, w.box, w.grid, w.cutoff)
+    o = oracle_mod.Oracle(pos, w.box, w.grid, w.cutoff)
+    seen = {}
+    waits = plan.item_waits()
+    for seg, xm, am in waits:
+        p, d = divmod(int(seg), plan.num_domains)
+        seen.setdefault((p, d), []).append((xm, am))
+    for (p, d), lst in seen.items():
+        q = o.pulse(p, d)
+        dep = q["index_map"][q["dep_start"]:]
+        regions = {_region_of(o, p, d, int(s)) for s in dep}
+        assert None not in regions
+        union = 0
+        for xm, _ in lst:
+            union |= int(xm)
+        assert union == sum(1 << r for r in regions), (p, d)
+        r = q["send_to"]
+        rr = o.pulse(p, r)
+        lo, hi = rr["atom_offset"], rr["atom_offset"] + rr["recv_size"]
+        want_am = 0
+        for qq in range(p + 1, o.n_pulse):
+            m = o.pulse(qq, r)["index_map"]
+            if np.any((m >= lo) & (m < hi)):
+                want_am |= 1 << qq
+        for _, am in lst:
+            assert int(am) == want_am, (p, d)
