@@ -160,6 +160,40 @@ def cold_exchange_us(torch, plan, x, f, f_init, suffix, reps):
     return {"us_x": float(np.median(tx)), "us_f": float(np.median(tf))}
 
 
+def plan_build_ms(torch, HaloPlan, w, pos, reps):
+    """Wall time of building the plan on the host (halo_plan_create from host
+    positions, then the upload) and on the GPU (halo_plan_create_device from
+    device positions), median of reps, after one warm-up build each."""
+    pos_d = torch.from_numpy(pos).cuda()
+
+    def host():
+        p = HaloPlan(pos, w.box, w.grid, w.cutoff)
+        p.upload()
+        torch.cuda.synchronize()
+        return p
+
+    def dev():
+        p = HaloPlan.on_device(pos_d, w.box, w.grid, w.cutoff)
+        torch.cuda.synchronize()
+        return p
+
+    out = {}
+    for name, fn in (("host_ms", host), ("device_ms", dev)):
+        fn().close()
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            p = fn()
+            ts.append((time.perf_counter() - t0) * 1e3)
+            p.close()
+        out[name] = float(np.median(ts))
+    out["speedup"] = out["host_ms"] / out["device_ms"]
+    out["reps"] = reps
+    out["host_threads"] = min(os.cpu_count() or 1, 16)
+    return out
+
+
 def overlap(torch, plan, x, f, reps):
     """The pages' overlap measurement with a synthetic local workload.
 
@@ -235,6 +269,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=50)
     ap.add_argument("--no-overlap", action="store_true")
+    ap.add_argument("--build-reps", type=int, default=5)
     ap.add_argument("--overlap-reps", type=int, default=50)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device 3 times (a plain copy kernel of "
@@ -375,6 +410,8 @@ def main():
                        for form, suffix in (("fused", ""), ("pulsewise", "_pulsewise"))}
         out["cold"]["method"] = (f"median of {args.cold_reps} single exchanges, each after a 1 GiB "
                                  f"device write that evicts L2 and the 256 MB cache")
+        log("plan builds")
+        out["plan_build"] = plan_build_ms(torch, HaloPlan, w, pos, args.build_reps)
         if not args.no_overlap:
             log("overlap with local work")
             out["overlap"] = overlap(torch, plans[0], xs[0], fs[0], args.overlap_reps)
