@@ -65,6 +65,16 @@ def workload_positions(w: Workload) -> np.ndarray:
     return positions(w.box, w.n_atoms, w.seed)
 
 
+def cell_sorted(pos: np.ndarray, box, cell: float = 0.5) -> np.ndarray:
+    """The same atoms renumbered in the order of a grid of `cell`-sized cubes
+    (z slowest, then y, then x; stable within a cube), the spatial order in
+    which MD codes keep their atoms. Only the numbering changes."""
+    n = np.maximum(1, np.floor(np.asarray(box, np.float64) / cell)).astype(np.int64)
+    c = np.minimum((pos.astype(np.float64) / cell).astype(np.int64), n - 1)
+    key = (c[:, 2] * n[1] + c[:, 1]) * n[0] + c[:, 0]
+    return np.ascontiguousarray(pos[np.argsort(key, kind="stable")])
+
+
 def halo_forces(total_slots: int, bases, n_home, n_halo, seed: int) -> np.ndarray:
     """Forces for a slot layout: N(0,1) float32 on halo slots, 0 on home slots.
 

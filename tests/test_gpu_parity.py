@@ -251,3 +251,13 @@ def test_forced_timeout_poisons_and_reset_recovers(torch, oracle_mod, impl):
     torch.cuda.synchronize()
     plan.sync()
     assert_bitwise(f.cpu().numpy(), want_f, "f after reset")
+
+
+@pytest.mark.parametrize("wid", [3, 5])
+def test_parity_cell_sorted_input(torch, oracle_mod, wid):
+    """The secondary input: the same atoms numbered in 0.5 nm cell order."""
+    w = W.WORKLOADS[wid]
+    pos = W.cell_sorted(W.workload_positions(w), w.box)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    for impl in ("fused", "transposed"):
+        check_both(torch, oracle_mod, plan, o, w.seed, impl, f"{w.name} cell-sorted")

@@ -389,3 +389,15 @@ def test_planted_selection_mistake_is_caught(oracle_mod):
     base, n_home, n_halo = o.domains()
     d1 = gids[base[1] + n_home[1]: base[1] + n_home[1] + n_halo[1]]
     assert 2 not in d1.tolist()
+
+
+def test_cell_sorted_is_a_renumbering():
+    """The cell-sorted input holds the same atoms, in cell order."""
+    w = W.WORKLOADS[2]
+    pos = W.workload_positions(w)
+    sp = W.cell_sorted(pos, w.box)
+    assert sp.shape == pos.shape and sp.dtype == pos.dtype
+    assert sorted(map(tuple, sp.tolist())) == sorted(map(tuple, pos.tolist()))
+    c = np.minimum((sp.astype(np.float64) / 0.5).astype(np.int64), 11)
+    key = (c[:, 2] * 12 + c[:, 1]) * 12 + c[:, 0]
+    assert np.all(np.diff(key) >= 0)
