@@ -1,24 +1,7 @@
-// halo_api.hip -- the exchange kernels for gfx950 and the C-ABI of include/halo.h.
+// halo_api.hip -- the C-ABI of include/halo.h: plans, uploads, launches.
 //
-// Method: "Redesigning GROMACS Halo Exchange" (paper review):
-//   Algorithm 3 FusedPackCommX  -> k_pack<FUSED=true>: every pulse in one
-//     launch; blocks take work items (a run of one pulse's indexMap for one
-//     sending domain) and store x[indexMap[i]] + coordShift straight into the
-//     receiver's region (the pages' NVLink zero-copy store: here the receiver
-//     is another region of the same HBM buffer);
-//   Algorithm 4 packWithDeps    -> the item's entries below depOffset are
-//     stored at once; the rest wait for the regions they forward;
-//   Algorithm 5 syncAndCommWithDeps -> block barrier + one release atomic per
-//     item on the (pulse, sender) completion counter;
-//   Algorithm 6 FusedCommUnpackF -> k_unpack<FUSED=true>: pulses in reverse;
-//     the forces of the receiver's region are added onto the sender's
-//     indexMap targets.
-// "GPU-Initiated Halo Exchange Cuts CPU Bottlenecks in GROMACS", "Fusing
-// pack, put, and wait into one kernel": the per-pulse first design is kept as
-// k_pack / k_unpack <FUSED=false>, one launch per pulse in stream order.
-//
-// Everything is float32 and every add is a single IEEE add (no FMA, no flush
-// of subnormals: the build passes -ffp-contract=off and keeps denormals).
+// The kernels are in exchange_kernels.hpp (included below); the host plan
+// builder in plan.cpp, the device plan builder in plan_device.hip.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -36,7 +19,6 @@ using halo::WorkItem;
 
 namespace {
 
-constexpr int kThreads = 256;             // 4 waves of 64 per workgroup
 constexpr int32_t kDefaultItemEntries = 1024;
 
 thread_local std::string g_last_error;
@@ -47,649 +29,11 @@ halo_status fail(halo_status st, const std::string &msg)
     return st;
 }
 
-// ---- buffer addressing ----------------------------------------------------
-// x, f and the indexMap are read and written through buffer descriptors: one
-// 12-byte float triple per buffer_load/store_dwordx3, 32-bit byte offsets, and
-// hardware range checking (an offset past the end returns zeros on a load and
-// drops a store). kInvalid is such an offset; the plan keeps every buffer
-// below 2 GiB so that it is never in range.
-typedef float f3v __attribute__((ext_vector_type(3)));
-constexpr uint32_t kInvalid = 0x80000000u;
-constexpr int kPlain = 0;      // cached: data another access of this XCD may reuse
-constexpr int kStream = 2;     // nt: touched once in this launch, streamed past the caches
-constexpr int kShared = 16;    // sc1: agent-coherent access, bypasses the XCD-private caches
-constexpr int32_t kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, kRsrcWord3);
-}
-
-template <int AUX>
-__device__ __forceinline__ f3v load3(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
-{
-    return __builtin_amdgcn_raw_buffer_load_b96(r, byte_off, 0, AUX);
-}
-
-template <int AUX>
-__device__ __forceinline__ void store3(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f3v v)
-{
-    __builtin_amdgcn_raw_buffer_store_b96(v, r, byte_off, 0, AUX);
-}
-
-// indexMap entry e, or 0 when !ok (the load is issued either way, so that no
-// branch separates the loads of one thread).
-__device__ __forceinline__ uint32_t load_index(__amdgpu_buffer_rsrc_t r, int32_t e, bool ok)
-{
-    return __builtin_amdgcn_raw_buffer_load_b32(r, ok ? (uint32_t)e * 4u : kInvalid, 0, kStream);
-}
-
-// Gather x[idx[map_begin + e]] + shift and store it at slot region_begin + e,
-// for e in [lo, hi), hi - lo <= EPT * kThreads. Branch-free: lanes past hi
-// load slot 0 and store to kInvalid. All index loads are issued first, then
-// all gathers, then all stores.
-template <int EPT, int LD, int ST>
-__device__ __forceinline__ void pack_span(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t ridx,
-                                          int32_t map_begin, int32_t region_begin, int32_t lo,
-                                          int32_t hi, f3v shift)
-{
-    uint32_t src[EPT], dst[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int32_t e = lo + (int32_t)threadIdx.x + j * kThreads;
-        const bool ok = e < hi;
-        src[j] = load_index(ridx, map_begin + e, ok) * 12u;
-        dst[j] = ok ? (uint32_t)(region_begin + e) * 12u : kInvalid;
-    }
-    f3v v[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) v[j] = load3<LD>(rx, src[j]);
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) store3<ST>(rx, dst[j], v[j] + shift);
-}
-
-// ---- work items ------------------------------------------------------------
-
-// One coordinate-direction item of the fused exchange (Algorithms 3 and 4).
-// Thread t owns entries t, t+256, ... of the item. All index loads are
-// issued first (the indexMap is read-only), then the entries below depOffset
-// are gathered and stored at once; the rest wait for the regions they
-// forward. Lanes outside a phase use kInvalid offsets, so the code has no
-// branches between the loads of one thread. Home slots are never written
-// during the launch and are read through the caches; forwarded regions are
-// stored and read with sc1 accesses.
-template <int EPT, int ST>
-__device__ __forceinline__ void pack_item_fused_st(const WorkItem *it, __amdgpu_buffer_rsrc_t rx,
-                                                   __amdgpu_buffer_rsrc_t ridx,
-                                                   const int32_t *recv_from,
-                                                   const uint32_t *seg_items, uint32_t *state,
-                                                   int32_t n_dom, uint32_t epoch,
-                                                   uint32_t spin_limit, uint32_t *err_word)
-{
-    const int32_t n_indep = it->n_indep;
-    const int32_t n_total = it->n_total;
-    const int32_t region_begin = it->region_begin;
-    const f3v shift = {it->shift[0], it->shift[1], it->shift[2]};
-    uint32_t src[EPT], dst[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
-        const bool ok = e < n_total;
-        src[j] = load_index(ridx, it->map_begin + e, ok) * 12u;
-        dst[j] = ok ? (uint32_t)(region_begin + e) * 12u : kInvalid;
-    }
-    f3v v[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const bool ind = (int32_t)threadIdx.x + j * kThreads < n_indep;
-        v[j] = load3<kPlain>(rx, ind ? src[j] : kInvalid);
-    }
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const bool ind = (int32_t)threadIdx.x + j * kThreads < n_indep;
-        store3<ST>(rx, ind ? dst[j] : kInvalid, v[j] + shift);
-    }
-    if (n_total > n_indep) {
-        // lane r of wave 0 polls the arrival of the region the sender
-        // received in pulse r, if the dependent entries read it
-        const uint32_t lane = threadIdx.x & 63u, wmask = it->xwait_mask;
-        uint32_t *ctr = nullptr;
-        uint32_t target = 0;
-        if (lane < 32u && ((wmask >> lane) & 1u)) {
-            const int32_t s = (int32_t)lane * n_dom + recv_from[(int32_t)lane * n_dom + it->domain];
-            ctr = halo::counter_x(state, s);
-            target = epoch * seg_items[s];
-        }
-        halo::wait_lanes(ctr, target, spin_limit, err_word);
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const bool dep = (int32_t)threadIdx.x + j * kThreads >= n_indep;
-            v[j] = load3<kShared>(rx, dep ? src[j] : kInvalid);
-        }
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const bool dep = (int32_t)threadIdx.x + j * kThreads >= n_indep;
-            store3<ST>(rx, dep ? dst[j] : kInvalid, v[j] + shift);
-        }
-    }
-}
-
-template <int EPT>
-__device__ __forceinline__ void pack_item_fused(const WorkItem *it, __amdgpu_buffer_rsrc_t rx,
-                                                __amdgpu_buffer_rsrc_t ridx,
-                                                const int32_t *recv_from,
-                                                const uint32_t *seg_items, uint32_t *state,
-                                                int32_t n_dom, uint32_t epoch,
-                                                uint32_t spin_limit, uint32_t *err_word,
-                                                int32_t withhold)
-{
-    if (it->flags & halo::kItemXStoreShared) {
-        pack_item_fused_st<EPT, kShared>(it, rx, ridx, recv_from, seg_items, state, n_dom, epoch,
-                                         spin_limit, err_word);
-        halo::signal_done(halo::counter_x(state, it->seg), it->seg == withhold);
-    } else {
-        // last pulse: no later pulse forwards its region, nobody waits on it
-        pack_item_fused_st<EPT, kStream>(it, rx, ridx, recv_from, seg_items, state, n_dom, epoch,
-                                        spin_limit, err_word);
-    }
-}
-
-// f[idx[map_begin + e]] += f[region_begin + e] for e < n; the index loads were
-// issued before the dependency wait.
-template <int EPT, int LD, int ST>
-__device__ __forceinline__ void unpack_span(__amdgpu_buffer_rsrc_t rf, const uint32_t *tgt,
-                                            int32_t region_begin, int32_t n)
-{
-    f3v add[EPT], cur[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
-        add[j] = load3<LD>(rf, e < n ? (uint32_t)(region_begin + e) * 12u : kInvalid);
-        cur[j] = load3<LD>(rf, tgt[j]);  // kInvalid reads zeros
-    }
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) store3<ST>(rf, tgt[j], cur[j] + add[j]);
-}
-
-template <int EPT>
-__device__ __forceinline__ void load_targets(__amdgpu_buffer_rsrc_t ridx, int32_t map_begin,
-                                             int32_t n_total, uint32_t *tgt)
-{
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
-        const bool ok = e < n_total;
-        const uint32_t t = load_index(ridx, map_begin + e, ok) * 12u;
-        tgt[j] = ok ? t : kInvalid;
-    }
-}
-
-// One force-direction item of the fused exchange (Algorithm 6): wait until
-// pulse p+1 is finished for the sender and its receiver, then add.
-template <int EPT>
-__device__ __forceinline__ void unpack_item_fused(const WorkItem *it, __amdgpu_buffer_rsrc_t rf,
-                                                  __amdgpu_buffer_rsrc_t ridx,
-                                                  const uint32_t *seg_items, uint32_t *state,
-                                                  int32_t n_seg, uint32_t epoch,
-                                                  uint32_t spin_limit, uint32_t *err_word,
-                                                  int32_t withhold)
-{
-    const int32_t n_total = it->n_total;
-    const int32_t region_begin = it->region_begin;
-    // The indexMap is read-only during the exchange: load it before waiting.
-    uint32_t tgt[EPT];
-    load_targets<EPT>(ridx, it->map_begin, n_total, tgt);
-    if (it->fwait[0] >= 0) {
-        const int32_t nw = it->fwait[1] >= 0 && it->fwait[1] != it->fwait[0] ? 2 : 1;
-        halo::wait_segments(it->fwait, nw, seg_items, state, n_seg, true, epoch, spin_limit,
-                            err_word);
-    }
-    const int32_t fl = it->flags;
-    if (fl & halo::kItemFLoadShared) {
-        if (fl & halo::kItemFStoreShared)
-            unpack_span<EPT, kShared, kShared>(rf, tgt, region_begin, n_total);
-        else
-            unpack_span<EPT, kShared, kStream>(rf, tgt, region_begin, n_total);
-    } else {
-        if (fl & halo::kItemFStoreShared)
-            unpack_span<EPT, kStream, kShared>(rf, tgt, region_begin, n_total);
-        else
-            unpack_span<EPT, kStream, kStream>(rf, tgt, region_begin, n_total);
-    }
-    // pulse 0 runs last: nobody waits on its completion
-    if (fl & halo::kItemFStoreShared)
-        halo::signal_done(halo::counter_f(state, n_seg, it->seg), it->seg == withhold);
-}
-
-// One force-direction item with atomic accumulation: Algorithm 6 as the
-// pages print it, with the items of every pulse in flight together and the
-// adds done by atomicAdd. The item waits only until the slots it reads (the
-// receiver's region of its pulse) hold their final sums, i.e. for the
-// later-pulse segments that add into them; its own targets may take adds of
-// other pulses at the same time. The order of the adds onto one slot is not
-// fixed, so the result equals the ordered exchange up to rounding, and
-// exactly whenever every partial sum is exact (small integers, for example).
-template <int EPT>
-__device__ __forceinline__ void unpack_item_atomic(const WorkItem *it, float *f,
-                                                   __amdgpu_buffer_rsrc_t rf,
-                                                   __amdgpu_buffer_rsrc_t ridx,
-                                                   const uint32_t *seg_items, uint32_t *state,
-                                                   int32_t n_seg, int32_t n_dom, uint32_t epoch,
-                                                   uint32_t spin_limit, uint32_t *err_word,
-                                                   int32_t withhold)
-{
-    const int32_t n_total = it->n_total;
-    const int32_t region_begin = it->region_begin;
-    uint32_t tgt[EPT], src[EPT];
-    load_targets<EPT>(ridx, it->map_begin, n_total, tgt);
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
-        src[j] = e < n_total ? (uint32_t)(region_begin + e) * 12u : kInvalid;
-    }
-    f3v add[EPT];
-    const uint32_t amask = it->await_mask;
-    if (amask) {
-        // lane q of wave 0 polls segment (q, receiver)
-        const uint32_t lane = threadIdx.x & 63u;
-        uint32_t *ctr = nullptr;
-        uint32_t target = 0;
-        if (lane < 32u && ((amask >> lane) & 1u)) {
-            const int32_t s = (int32_t)lane * n_dom + it->receiver;
-            ctr = halo::counter_f(state, n_seg, s);
-            target = epoch * seg_items[s];
-        }
-        halo::wait_lanes(ctr, target, spin_limit, err_word);
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) add[j] = load3<kShared>(rf, src[j]);
-    } else {
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) add[j] = load3<kStream>(rf, src[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        if (tgt[j] == kInvalid) continue;
-        float *t = f + tgt[j] / 4u;
-        __hip_atomic_fetch_add(t + 0, add[j].x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(t + 1, add[j].y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(t + 2, add[j].z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // the targets of a pulse p > 0 may be the sources of an earlier pulse
-    if (it->flags & halo::kItemFStoreShared)
-        halo::signal_done(halo::counter_f(state, n_seg, it->seg), it->seg == withhold);
-}
-
-// ---- kernels -----------------------------------------------------------------
-
-// Fused coordinate exchange: ONE launch for all pulses, one item per
-// workgroup, items in pulse-major order of the workgroup index. An item only
-// waits on items of earlier pulses, i.e. on workgroups with smaller indices.
-// The hardware hands workgroups of a grid to the XCDs round-robin and each
-// XCD dispatches its share in increasing index order, so the smallest
-// unfinished item is always resident or next in line: every wait ends. The
-// spin limit turns a violation of that order into HALO_ERR_TIMEOUT, not a
-// hang. (No atomic ticket: 2560 same-address device atomics serialise for
-// about 20 us on MI355X; and no cooperative launch, which idles the GPU for
-// about 20 us before each launch.)
-template <int EPT>
-__global__ __launch_bounds__(kThreads) void k_pack_fused(
-    float *x, uint32_t x_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
-    const WorkItem *__restrict__ items, const int32_t *__restrict__ recv_from,
-    const uint32_t *__restrict__ seg_items, uint32_t *state, int32_t n_dom, uint32_t epoch,
-    uint32_t spin_limit, uint32_t *err_word, int32_t withhold)
-{
-    pack_item_fused<EPT>(items + blockIdx.x, make_rsrc(x, x_bytes), make_rsrc(idx, idx_bytes),
-                         recv_from, seg_items, state, n_dom, epoch, spin_limit, err_word,
-                         withhold);
-}
-
-// Fused force exchange: ONE launch, workgroup b takes item n_items-1-b, so
-// the last pulse comes first; same progress argument.
-template <int EPT>
-__global__ __launch_bounds__(kThreads) void k_unpack_fused(
-    float *f, uint32_t f_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
-    const WorkItem *__restrict__ items, const uint32_t *__restrict__ seg_items, uint32_t *state,
-    int32_t n_seg, uint32_t n_items, uint32_t epoch, uint32_t spin_limit, uint32_t *err_word,
-    int32_t withhold)
-{
-    unpack_item_fused<EPT>(items + (n_items - 1u - blockIdx.x), make_rsrc(f, f_bytes),
-                           make_rsrc(idx, idx_bytes), seg_items, state, n_seg, epoch, spin_limit,
-                           err_word, withhold);
-}
-
-// Fused force exchange with atomic adds: ONE launch, last pulse first; an item
-// waits only on segments of later pulses, i.e. on smaller workgroup indices.
-template <int EPT>
-__global__ __launch_bounds__(kThreads) void k_unpack_atomic(
-    float *f, uint32_t f_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
-    const WorkItem *__restrict__ items, const uint32_t *__restrict__ seg_items, uint32_t *state,
-    int32_t n_seg, int32_t n_dom, uint32_t n_items, uint32_t epoch, uint32_t spin_limit,
-    uint32_t *err_word, int32_t withhold)
-{
-    unpack_item_atomic<EPT>(items + (n_items - 1u - blockIdx.x), f, make_rsrc(f, f_bytes),
-                            make_rsrc(idx, idx_bytes), seg_items, state, n_seg, n_dom, epoch,
-                            spin_limit, err_word, withhold);
-}
-
-// ---- transposed form: per-slot pulse masks --------------------------------
-
-// Pulse ranks of one chunk. Thread t owns slots first + t + j*256 (j < EPT),
-// i.e. slot order is row-major over (j, wave, lane). For pulse p the slot's
-// entry of indexMap_p is chunk.rank[p] plus the number of earlier slots of
-// the chunk with bit p: a wave ballot gives the count within the wave, and an
-// exclusive prefix over (row, wave) in LDS, built once per pulse, the rest.
-template <int EPT>
-struct Ranks {
-    uint32_t cnt[halo::kMaxMaskPulses][EPT * 4];
-    uint32_t off[halo::kMaxMaskPulses][EPT * 4];
-};
-
-// Count, per pulse and (row, wave), the slots with the pulse's bit, then turn
-// the counts into exclusive prefixes (thread k computes entry k of pulse
-// k / (EPT*4) from up to EPT*4 independent LDS reads). Ends with a workgroup
-// barrier.
-template <int EPT>
-__device__ __forceinline__ void build_ranks(Ranks<EPT> &sh, const uint32_t *m, uint32_t umask,
-                                            int32_t n_pulse)
-{
-    constexpr int kRow = EPT * 4;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int32_t p = 0; p < n_pulse; ++p) {
-        if (!((umask >> p) & 1u)) continue;
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const uint64_t b = __ballot((m[j] >> p) & 1u);
-            if (lane == 0) sh.cnt[p][j * 4 + wave] = (uint32_t)__popcll(b);
-        }
-    }
-    __syncthreads();
-    for (int k = threadIdx.x; k < n_pulse * kRow; k += kThreads) {
-        const int p = k / kRow, e = k % kRow;
-        if (!((umask >> p) & 1u)) continue;
-        uint32_t acc = 0;
-#pragma unroll
-        for (int q = 0; q < kRow; ++q)
-            if (q < e) acc += sh.cnt[p][q];
-        sh.off[p][e] = acc;
-    }
-    __syncthreads();
-}
-
-// Position among the chunk's bit-p slots of this thread's row-j slot.
-template <int EPT>
-__device__ __forceinline__ uint32_t rank_in_chunk(const Ranks<EPT> &sh, int32_t p, int j, bool bit)
-{
-    const uint64_t b = __ballot(bit);
-    return sh.off[p][j * 4 + (threadIdx.x >> 6)] +
-           __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
-                                     __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-}
-
-// Fused coordinate exchange, transposed form (Algorithms 3 and 4): one
-// workgroup per chunk, chunks in zone order (home slots of every domain,
-// then the region of pulse 0, pulse 1, ...). A home chunk never waits (its
-// entries are the independent ones below depOffset); a region chunk waits for
-// the arrival of its region, then forwards it. Each slot is read once and
-// stored, plus coordShift, to every pulse whose bit it carries.
-template <int EPT>
-__global__ __launch_bounds__(kThreads) void k_push_x(
-    float *x, uint32_t x_bytes, const uint8_t *__restrict__ slot_mask,
-    const halo::Chunk *__restrict__ chunks, const int32_t *__restrict__ dest_start,
-    const float4 *__restrict__ shift4, const uint32_t *__restrict__ x_arrivals, uint32_t *state,
-    int32_t n_dom, int32_t n_pulse, uint32_t epoch, uint32_t spin_limit, uint32_t *err_word,
-    int32_t withhold)
-{
-    __shared__ Ranks<EPT> sh;
-    const halo::Chunk *c = chunks + blockIdx.x;
-    const int32_t first = c->first, count = c->count, D = c->domain;
-    const uint32_t umask = c->mask;
-    const auto rx = make_rsrc(x, x_bytes);
-
-    uint32_t m[EPT], off[EPT];
-    f3v v[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
-        m[j] = e < count ? (uint32_t)slot_mask[first + e] : 0u;
-        off[j] = e < count ? (uint32_t)(first + e) * 12u : kInvalid;
-    }
-    if (c->zone < 0) {
-        // home slots are final before the launch: load them with the masks
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) v[j] = load3<kStream>(rx, off[j]);
-    }
-    build_ranks<EPT>(sh, m, umask, n_pulse);
-    if (c->zone >= 0) {
-        // region slots are filled by another domain in this launch
-        halo::wait_one(c->xwait, x_arrivals, state, n_dom * n_pulse, false, epoch, spin_limit,
-                       err_word);
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) v[j] = load3<kShared>(rx, m[j] ? off[j] : kInvalid);
-    }
-    for (int32_t p = 0; p < n_pulse; ++p) {
-        if (!((umask >> p) & 1u)) continue;
-        const int32_t base = dest_start[p * n_dom + D] + c->rank[p];
-        const float4 sh4 = shift4[p * n_dom + D];
-        const f3v s3 = {sh4.x, sh4.y, sh4.z};
-        uint32_t dst[EPT];
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const bool bit = (m[j] >> p) & 1u;
-            const uint32_t r = rank_in_chunk<EPT>(sh, p, j, bit);
-            dst[j] = bit ? (uint32_t)(base + (int32_t)r) * 12u : kInvalid;
-        }
-        if (p + 1 < n_pulse) {
-            // the region may be forwarded by a later pulse of this launch:
-            // store coherently and signal its arrival as soon as it is
-            // complete, before the stores of later pulses
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) store3<kShared>(rx, dst[j], v[j] + s3);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            halo::wait_vmem();
-            __syncthreads();
-            const int32_t seg = p * n_dom + D;
-            if (threadIdx.x == 0 && seg != withhold)
-                __hip_atomic_fetch_add(halo::counter_x(state, seg), 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            // last pulse: nobody forwards this region, nobody waits on it
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) store3<kStream>(rx, dst[j], v[j] + s3);
-        }
-    }
-}
-
-// Fused force exchange, transposed form (Algorithm 6): one workgroup per
-// chunk, regions of later pulses first, home slots last. Every thread keeps
-// the running sum of its target slot in registers and adds the sources of
-// its pulses in strict reverse order; before pulse p it waits until the
-// sources (the receiver's region of pulse p) hold their final sums. Each
-// target slot is read once and written once.
-template <int EPT>
-__global__ __launch_bounds__(kThreads) void k_pull_f(
-    float *f, uint32_t f_bytes, const uint8_t *__restrict__ slot_mask,
-    const halo::Chunk *__restrict__ chunks, const int32_t *__restrict__ forder,
-    const int32_t *__restrict__ dest_start, const int32_t *__restrict__ send_to,
-    const uint32_t *__restrict__ zone_chunks, uint32_t *state, int32_t n_dom, int32_t n_pulse,
-    uint32_t epoch, uint32_t spin_limit, uint32_t *err_word, int32_t withhold)
-{
-    __shared__ Ranks<EPT> sh;
-    const halo::Chunk *c = chunks + forder[blockIdx.x];
-    const int32_t first = c->first, count = c->count, D = c->domain, zone = c->zone;
-    const uint32_t umask = c->mask;
-    const auto rf = make_rsrc(f, f_bytes);
-    const int32_t n_seg = n_dom * n_pulse;
-
-    uint32_t m[EPT], off[EPT];
-    f3v v[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
-        m[j] = e < count ? (uint32_t)slot_mask[first + e] : 0u;
-        off[j] = e < count ? (uint32_t)(first + e) * 12u : kInvalid;
-    }
-    // Only this workgroup writes these slots, and nobody before it in this
-    // launch: cached loads, issued together with the masks.
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) v[j] = load3<kStream>(rf, off[j]);
-    build_ranks<EPT>(sh, m, umask, n_pulse);
-    for (int32_t p = n_pulse - 1; p >= 0; --p) {
-        if (!((umask >> p) & 1u)) continue;
-        const int32_t R = send_to[p * n_dom + D];
-        const int32_t zseg = p * n_dom + R;
-        if (zone_chunks[zseg] > 0)
-            halo::wait_one(zseg, zone_chunks, state, n_seg, true, epoch, spin_limit, err_word);
-        const int32_t base = dest_start[p * n_dom + D] + c->rank[p];
-        uint32_t src[EPT];
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const bool bit = (m[j] >> p) & 1u;
-            const uint32_t r = rank_in_chunk<EPT>(sh, p, j, bit);
-            src[j] = bit ? (uint32_t)(base + (int32_t)r) * 12u : kInvalid;
-        }
-        f3v add[EPT];
-        if (zone_chunks[zseg] > 0) {
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) add[j] = load3<kShared>(rf, src[j]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) add[j] = load3<kStream>(rf, src[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < EPT; ++j)
-            if (src[j] != kInvalid) v[j] = v[j] + add[j];
-    }
-    uint32_t dst[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) dst[j] = m[j] ? off[j] : kInvalid;
-    if (zone >= 0) {
-        // region sums are read by another domain in this launch
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) store3<kShared>(rf, dst[j], v[j]);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        halo::wait_vmem();
-        __syncthreads();
-        const int32_t seg = zone * n_dom + D;
-        if (threadIdx.x == 0 && seg != withhold)
-            __hip_atomic_fetch_add(halo::counter_f(state, n_seg, seg), 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) store3<kStream>(rf, dst[j], v[j]);
-    }
-}
-
-// Per-pulse baseline: one launch per pulse, one item per workgroup, no
-// counters; the kernel boundary orders the pulses, so every access is cached.
-template <int EPT>
-__global__ __launch_bounds__(kThreads) void k_pack_pulse(float *x, uint32_t x_bytes,
-                                                         const int32_t *__restrict__ idx,
-                                                         uint32_t idx_bytes,
-                                                         const WorkItem *__restrict__ items,
-                                                         int32_t item_base)
-{
-    const WorkItem *it = items + item_base + blockIdx.x;
-    const f3v shift = {it->shift[0], it->shift[1], it->shift[2]};
-    pack_span<EPT, kPlain, kPlain>(make_rsrc(x, x_bytes), make_rsrc(idx, idx_bytes),
-                                   it->map_begin, it->region_begin, 0, it->n_total, shift);
-}
-
-template <int EPT>
-__global__ __launch_bounds__(kThreads) void k_unpack_pulse(float *f, uint32_t f_bytes,
-                                                           const int32_t *__restrict__ idx,
-                                                           uint32_t idx_bytes,
-                                                           const WorkItem *__restrict__ items,
-                                                           int32_t item_base)
-{
-    const WorkItem *it = items + item_base + blockIdx.x;
-    uint32_t tgt[EPT];
-    load_targets<EPT>(make_rsrc(idx, idx_bytes), it->map_begin, it->n_total, tgt);
-    unpack_span<EPT, kPlain, kPlain>(make_rsrc(f, f_bytes), tgt, it->region_begin, it->n_total);
-}
-
-// Staged baseline (the message-passing design the pages compare against): a
-// pulse first packs into a staging buffer, entry e of the concatenated
-// indexMap at stage[e], and a second launch moves the staged run into the
-// receiver's region; forces go the other way round (region -> stage, then
-// the scatter-add from stage). Two launches per pulse and 24 bytes more per
-// entry than the zero-copy store.
-template <int EPT>
-__global__ __launch_bounds__(kThreads) void k_stage_pack(
-    float *x, uint32_t x_bytes, float *stage, uint32_t stage_bytes,
-    const int32_t *__restrict__ idx, uint32_t idx_bytes, const WorkItem *__restrict__ items,
-    int32_t item_base)
-{
-    const WorkItem *it = items + item_base + blockIdx.x;
-    const f3v shift = {it->shift[0], it->shift[1], it->shift[2]};
-    const auto rx = make_rsrc(x, x_bytes), rs = make_rsrc(stage, stage_bytes);
-    const auto ridx = make_rsrc(idx, idx_bytes);
-    uint32_t src[EPT], dst[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
-        const bool ok = e < it->n_total;
-        src[j] = load_index(ridx, it->map_begin + e, ok) * 12u;
-        dst[j] = ok ? (uint32_t)(it->map_begin + e) * 12u : kInvalid;
-    }
-    f3v v[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) v[j] = load3<kPlain>(rx, src[j]);
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) store3<kPlain>(rs, dst[j], v[j] + shift);
-}
-
-// to_region != 0: buf[region_begin + e] = stage[map_begin + e] (coordinates);
-// to_region == 0: stage[map_begin + e] = buf[region_begin + e] (forces).
-template <int EPT>
-__global__ __launch_bounds__(kThreads) void k_stage_move(float *buf, uint32_t buf_bytes,
-                                                         float *stage, uint32_t stage_bytes,
-                                                         const WorkItem *__restrict__ items,
-                                                         int32_t item_base, int32_t to_region)
-{
-    const WorkItem *it = items + item_base + blockIdx.x;
-    const auto rb = make_rsrc(buf, buf_bytes), rs = make_rsrc(stage, stage_bytes);
-    const auto rsrc = to_region ? rs : rb, rdst = to_region ? rb : rs;
-    uint32_t src[EPT], dst[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
-        const bool ok = e < it->n_total;
-        const uint32_t so = ok ? (uint32_t)(it->map_begin + e) * 12u : kInvalid;
-        const uint32_t ro = ok ? (uint32_t)(it->region_begin + e) * 12u : kInvalid;
-        src[j] = to_region ? so : ro;
-        dst[j] = to_region ? ro : so;
-    }
-    f3v v[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) v[j] = load3<kPlain>(rsrc, src[j]);
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) store3<kPlain>(rdst, dst[j], v[j]);
-}
-
-template <int EPT>
-__global__ __launch_bounds__(kThreads) void k_stage_unpack(
-    float *f, uint32_t f_bytes, float *stage, uint32_t stage_bytes,
-    const int32_t *__restrict__ idx, uint32_t idx_bytes, const WorkItem *__restrict__ items,
-    int32_t item_base)
-{
-    const WorkItem *it = items + item_base + blockIdx.x;
-    const auto rf = make_rsrc(f, f_bytes), rs = make_rsrc(stage, stage_bytes);
-    uint32_t tgt[EPT];
-    load_targets<EPT>(make_rsrc(idx, idx_bytes), it->map_begin, it->n_total, tgt);
-    f3v add[EPT], cur[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
-        add[j] = load3<kPlain>(rs, e < it->n_total ? (uint32_t)(it->map_begin + e) * 12u
-                                                   : kInvalid);
-        cur[j] = load3<kPlain>(rf, tgt[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) store3<kPlain>(rf, tgt[j], cur[j] + add[j]);
-}
+// Device code; included here, inside this anonymous namespace, after the
+// HIP runtime, plan.hpp and sync.hpp.
+#include "exchange_kernels.hpp"
 
 }  // namespace
-
 
 namespace {
 
@@ -931,6 +275,18 @@ halo_status check_exchange(halo_plan *p, float *buf, const char *what)
     return HALO_OK;
 }
 
+// The fused forms pass a new epoch to every launch; a captured graph would
+// replay a stale one. They refuse to run while `stream` is being captured.
+halo_status refuse_capture(hipStream_t stream, const char *what)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+        return fail(HALO_ERR_ARG, std::string(what) +
+                                      ": cannot be captured in a graph (every call passes a new "
+                                      "epoch); use the per-pulse form there");
+    return HALO_OK;
+}
+
 int32_t item_entries_from_env()
 {
     const char *v = std::getenv("HALO_ITEM_ENTRIES");
@@ -1143,6 +499,8 @@ halo_status halo_exchange_x_transposed(halo_plan *p, float *x, void *stream)
 {
     halo_status st = check_exchange(p, x, "halo_exchange_x_transposed");
     if (st != HALO_OK) return st;
+    if ((st = refuse_capture((hipStream_t)stream, "halo_exchange_x_transposed")) != HALO_OK)
+        return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
     if (!p->h.has_chunks)
         return fail(HALO_ERR_ARG, "halo_exchange_x_transposed: plan has more than 8 pulses");
@@ -1156,6 +514,8 @@ halo_status halo_exchange_f_transposed(halo_plan *p, float *f, void *stream)
 {
     halo_status st = check_exchange(p, f, "halo_exchange_f_transposed");
     if (st != HALO_OK) return st;
+    if ((st = refuse_capture((hipStream_t)stream, "halo_exchange_f_transposed")) != HALO_OK)
+        return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
     if (!p->h.has_chunks)
         return fail(HALO_ERR_ARG, "halo_exchange_f_transposed: plan has more than 8 pulses");
@@ -1169,6 +529,8 @@ halo_status halo_exchange_x_indexmap(halo_plan *p, float *x, void *stream)
 {
     halo_status st = check_exchange(p, x, "halo_exchange_x_indexmap");
     if (st != HALO_OK) return st;
+    if ((st = refuse_capture((hipStream_t)stream, "halo_exchange_x_indexmap")) != HALO_OK)
+        return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
     p->epoch_x += 1;
     hipError_t e = launch_fused(p, false, x, (hipStream_t)stream);
@@ -1179,6 +541,8 @@ halo_status halo_exchange_f_indexmap(halo_plan *p, float *f, void *stream)
 {
     halo_status st = check_exchange(p, f, "halo_exchange_f_indexmap");
     if (st != HALO_OK) return st;
+    if ((st = refuse_capture((hipStream_t)stream, "halo_exchange_f_indexmap")) != HALO_OK)
+        return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
     p->epoch_f += 1;
     hipError_t e = launch_fused(p, true, f, (hipStream_t)stream);
@@ -1215,6 +579,8 @@ halo_status halo_exchange_f_atomic(halo_plan *p, float *f, void *stream)
 {
     halo_status st = check_exchange(p, f, "halo_exchange_f_atomic");
     if (st != HALO_OK) return st;
+    if ((st = refuse_capture((hipStream_t)stream, "halo_exchange_f_atomic")) != HALO_OK)
+        return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
     // shares the index-list force counters: both kernels advance the same
     // counters by the same counts per exchange
@@ -1231,6 +597,7 @@ static halo_status exchange_staged(halo_plan *p, bool force_dir, float *buf, voi
     const halo::HostPlan &h = p->h;
     if (h.total_slots == 0 || h.n_entries == 0) return HALO_OK;
     if (!p->d_stage) {
+        if ((st = refuse_capture((hipStream_t)stream, what)) != HALO_OK) return st;
         hipError_t e = hipMalloc((void **)&p->d_stage, h.n_entries * 12);
         if (e != hipSuccess) {
             p->d_stage = nullptr;

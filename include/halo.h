@@ -161,7 +161,11 @@ halo_status halo_plan_upload(halo_plan *plan);
  * read. Runs the index-list form (halo_exchange_x_indexmap).
  *   x : device, total_slots*3 float32, 4-byte aligned. Home slots are read;
  *       every halo slot is overwritten with x[indexMap[i]] + coordShift.
- * Asynchronous; exchanges of one plan must be ordered on one stream. */
+ * Asynchronous; exchanges of one plan must be ordered on one stream.
+ * Every fused call (this one, halo_exchange_f and the _indexmap, _transposed
+ * and _atomic forms) passes its launch a new epoch, so it cannot be captured
+ * into a HIP graph: called while `stream` is capturing it returns
+ * HALO_ERR_ARG. The per-pulse form can be captured. */
 halo_status halo_exchange_x(halo_plan *plan, float *x, void *stream);
 
 /* Force exchange, Algorithm 6 in ONE kernel launch: pulses from last to

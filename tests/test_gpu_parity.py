@@ -261,3 +261,73 @@ def test_parity_cell_sorted_input(torch, oracle_mod, wid):
     plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
     for impl in ("fused", "transposed"):
         check_both(torch, oracle_mod, plan, o, w.seed, impl, f"{w.name} cell-sorted")
+
+
+def test_fused_refuses_graph_capture_pulsewise_replays(torch, oracle_mod):
+    """Fused calls refuse a capturing stream; the per-pulse form captured in a
+    graph replays exactly, with eager work between the replays."""
+    w = W.WORKLOADS[2]
+    pos = W.workload_positions(w)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    plan.upload()
+    x0 = o.home_filled(np.nan)
+    want = o.exchange_x(x0.copy())
+    x = torch.from_numpy(x0.copy()).cuda()
+    dummy = torch.zeros(4, device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("graph capture: fused refuses, per-pulse is captured")
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        try:
+            for name in ("exchange_x", "exchange_x_indexmap", "exchange_x_transposed"):
+                with pytest.raises(HaloError) as e:
+                    getattr(plan, name)(x, s)
+                assert e.value.code == -1
+            plan.exchange_x_pulsewise(x, s)
+            dummy.add_(1.0)
+        finally:
+            g.capture_end()
+    torch.cuda.synchronize()
+    for r in range(3):
+        x.copy_(torch.from_numpy(x0))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bitwise(x.cpu().numpy(), want, f"replay {r}")
+        plan.exchange_x(x)  # eager fused exchange between the replays
+        torch.cuda.synchronize()
+        assert_bitwise(x.cpu().numpy(), want, f"eager after replay {r}")
+    plan.sync()
+
+
+def test_exchange_beside_a_gemm(torch, oracle_mod):
+    """Fused exchanges while a GEMM occupies the GPU from a second stream:
+    every in-kernel wait still ends and the results stay exact."""
+    w = W.WORKLOADS[5]
+    pos = W.workload_positions(w)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    x0 = o.home_filled(np.nan)
+    want_x = o.exchange_x(x0.copy())
+    base, n_home, n_halo = o.domains()
+    f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, w.seed)
+    want_f = o.exchange_f(f0.copy())
+    a = torch.randn(4096, 4096, device="cuda")
+    b = torch.randn(4096, 4096, device="cuda")
+    loc = torch.cuda.Stream()
+    x = torch.from_numpy(x0).cuda()
+    f_init = torch.from_numpy(f0).cuda()
+    f = torch.empty_like(f_init)
+    say("exchanges beside a GEMM on another stream")
+    for r in range(5):
+        with torch.cuda.stream(loc):
+            c = a @ b
+        f.copy_(f_init)
+        plan.exchange_x(x)
+        plan.exchange_f(f)
+        torch.cuda.synchronize()
+        assert_bitwise(x.cpu().numpy(), want_x, f"round {r} x")
+        assert_bitwise(f.cpu().numpy(), want_f, f"round {r} f")
+    del c
+    plan.sync()
