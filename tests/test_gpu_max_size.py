@@ -1,0 +1,96 @@
+"""Plans near the largest size the library addresses.
+
+Slots are addressed with 32-bit byte offsets of float triples, so a plan holds
+at most 178,956,969 slots (2 GiB of coordinates). These tests build a plan of
+about 95 % of that on the GPU (100 M atoms, 16x16x16 domains) and check the
+exchanges through properties that hold at any size, on the oracle-free path:
+- coordinates: every sampled region entry equals its source slot plus
+  coordShift (the stored value of a forwarded atom is the forwarded one);
+- forces: with small-integer forces on the halo slots and zero on the home
+  slots, every halo force reaches exactly one home slot, so the home slots'
+  total equals the halo slots' initial total, exactly (all partial sums are
+  integers well below 2^24 per slot; totals are summed in float64).
+A plan just above the limit is refused with HALO_ERR_RANGE.
+"""
+import numpy as np
+import pytest
+
+from domain_decomposition_halo_fusedpackx_amd import HaloError, HaloPlan
+
+from .test_gpu_parity import say, torch  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+BOX = (100.0, 100.0, 100.0)
+GRID = (16, 16, 16)
+CUTOFF = 1.2
+MAX_SLOTS = (1 << 31) // 12 - 1
+
+
+def device_positions(torch, n, seed):
+    """Uniform positions in [0, L), drawn on the GPU from a seeded generator."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    pos = torch.rand(n, 3, generator=g, device="cuda") * torch.tensor(BOX, device="cuda")
+    top = torch.nextafter(torch.tensor(BOX, device="cuda"), torch.zeros(3, device="cuda"))
+    return torch.minimum(pos, top).contiguous()
+
+
+def test_near_maximum_plan(torch):
+    n = 100_000_000
+    say(f"near-maximum plan: {n} atoms, {GRID} domains, device build")
+    pos = device_positions(torch, n, 21)
+    plan = HaloPlan.on_device(pos, BOX, GRID, CUTOFF)
+    say(f"slots {plan.total_slots} ({plan.total_slots / MAX_SLOTS:.3f} of the maximum), "
+        f"entries {plan.num_entries}")
+    assert 0.9 * MAX_SLOTS < plan.total_slots <= MAX_SLOTS
+    slots = torch.from_numpy(plan.home_slots()).cuda()
+    x = torch.full((plan.total_slots, 3), float("nan"), device="cuda")
+    x[slots] = pos
+    plan.exchange_x(x)
+    torch.cuda.synchronize()
+    plan.sync()
+    xh = x.cpu().numpy()
+    base, _, _ = plan.domains()
+    nd, npl = plan.num_domains, plan.num_pulses
+    rng = np.random.default_rng(5)
+    doms = sorted(set(range(nd - 24, nd)) | set(rng.choice(nd, 24, replace=False).tolist()))
+    checked = 0
+    for p in range(npl):
+        for d in doms:
+            q = plan.pulse(p, d)
+            r = q["send_to"]
+            dst0 = base[r] + plan.pulse(p, r)["atom_offset"]
+            src = base[d] + q["index_map"].astype(np.int64)
+            dst = dst0 + np.arange(q["send_size"], dtype=np.int64)
+            want = xh[src] + q["shift"]
+            assert np.array_equal(xh[dst].view(np.uint32), want.view(np.uint32)), (p, d)
+            checked += q["send_size"]
+    assert not np.isnan(xh).any()
+    say(f"coordinates: {checked} sampled entries match; no slot left unwritten")
+    del xh, x
+
+    # forces: conservation with small integers
+    _, n_home, n_halo = plan.domains()
+    halo = torch.ones(plan.total_slots, dtype=torch.bool, device="cuda")
+    halo[slots] = False
+    g = torch.Generator(device="cuda")
+    g.manual_seed(22)
+    f = torch.randint(-8, 9, (plan.total_slots, 3), generator=g, device="cuda").float()
+    f[~halo] = 0.0
+    total_in = f[halo].double().sum(0)
+    plan.exchange_f(f)
+    torch.cuda.synchronize()
+    plan.sync()
+    total_home = f[slots].double().sum(0)
+    assert torch.equal(total_home, total_in), (total_home, total_in)
+    say(f"forces: home total {total_home.tolist()} equals the halo input total")
+
+
+def test_just_above_maximum_is_refused(torch):
+    n = 110_000_000
+    say(f"plan above the maximum: {n} atoms")
+    pos = device_positions(torch, n, 23)
+    with pytest.raises(HaloError) as e:
+        HaloPlan.on_device(pos, BOX, GRID, CUTOFF)
+    assert e.value.code == -3
