@@ -512,7 +512,8 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
         off[j] = e < count ? (uint32_t)(first + e) * 12u : kInvalid;
     }
     // Only this workgroup writes these slots, and nobody before it in this
-    // launch: cached loads, issued together with the masks.
+    // launch: plain loads (streamed, read once), issued together with the
+    // masks.
 #pragma unroll
     for (int j = 0; j < EPT; ++j) v[j] = load3<kStream>(rf, off[j]);
     build_ranks<EPT>(sh, m, umask, n_pulse);
