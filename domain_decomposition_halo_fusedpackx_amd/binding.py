@@ -25,6 +25,7 @@ _st = ctypes.c_int
 SIGNATURES = {
     "halo_plan_create": (_st, [_vp, _i64, _vp, _vp, _f32, _P(_vp)]),
     "halo_plan_create_device": (_st, [_vp, _i64, _vp, _vp, _f32, _vp, _P(_vp)]),
+    "halo_plan_rebuild_device": (_st, [_vp, _vp, _i64, _vp, _vp]),
     "halo_plan_destroy": (None, [_vp]),
     "halo_last_error": (ctypes.c_char_p, []),
     "halo_plan_total_slots": (_i64, [_vp]),
@@ -152,6 +153,34 @@ class HaloPlan:
             _stream_handle(stream, positions.get_device()), ctypes.byref(h)))
         self._finish(h, n)
         return self
+
+    def rebuild_on_device(self, positions, box=None, stream=None):
+        """Rebuild this plan on the GPU for new positions (halo_plan_rebuild_device);
+        grid and cutoff stay, box may change."""
+        import torch
+        if not isinstance(positions, torch.Tensor) or not positions.is_cuda:
+            raise TypeError("positions must be a torch.cuda tensor")
+        if positions.dtype != torch.float32 or not positions.is_contiguous():
+            raise TypeError("positions must be contiguous float32")
+        if positions.numel() % 3:
+            raise ValueError("positions must hold 3 floats per atom")
+        if box is not None:
+            b = np.ascontiguousarray(box, dtype=np.float32)
+            if b.shape != (3,):
+                raise ValueError("box needs three entries")
+        else:
+            b = self._box
+        n = positions.numel() // 3
+        try:
+            _check(load_library().halo_plan_rebuild_device(
+                self._h, ctypes.c_void_p(positions.data_ptr()) if n else None, n, _np_ptr(b),
+                _stream_handle(stream, positions.get_device())))
+        except HaloError as e:
+            if e.code not in (-1, -2):  # the plan is now empty
+                self.n_atoms = self.total_slots = self.num_entries = self.num_items = 0
+            raise
+        self._box = b
+        self._finish(self._h, n)
 
     def _finish(self, h, n_atoms):
         lib = load_library()

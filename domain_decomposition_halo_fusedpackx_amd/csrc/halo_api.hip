@@ -44,6 +44,7 @@ halo_status hip_fail(hipError_t e, const char *what)
 
 void free_device(halo_plan *p)
 {
+    halo::free_device_build(p);  // arenas first: the pointers into them become null
     for (void *q : {(void *)p->d_idx, (void *)p->d_items, (void *)p->d_recv_from,
                     (void *)p->d_send_to, (void *)p->d_stage, (void *)p->d_seg_items,
                     (void *)p->d_state, (void *)p->d_mask, (void *)p->d_chunks,
@@ -260,6 +261,9 @@ namespace {
 halo_status check_exchange(halo_plan *p, float *buf, const char *what)
 {
     if (!p) return fail(HALO_ERR_ARG, std::string(what) + ": NULL plan");
+    if (p->invalid)
+        return fail(HALO_ERR_STATE, std::string(what) +
+                                        ": the plan's last rebuild failed; rebuild it again");
     if (!buf && p->h.total_slots > 0) return fail(HALO_ERR_ARG, std::string(what) + ": NULL buffer");
     if (p->uploaded && p->h_err && __atomic_load_n(p->h_err, __ATOMIC_ACQUIRE) != 0)
         p->poisoned = true;
@@ -358,6 +362,56 @@ halo_status halo_plan_create_device(const float *positions, int64_t n_atoms, con
         return msg.empty() ? (halo_status)rc : fail((halo_status)rc, msg);
     }
     *out = p;
+    return HALO_OK;
+}
+
+halo_status halo_plan_rebuild_device(halo_plan *p, const float *positions, int64_t n_atoms,
+                                     const float *box, void *stream)
+{
+    if (!p || !box) return fail(HALO_ERR_ARG, "halo_plan_rebuild_device: NULL argument");
+    const int32_t grid[3] = {p->h.grid[0], p->h.grid[1], p->h.grid[2]};
+    const float cutoff = p->h.cutoff;
+    {
+        // argument and geometry errors leave the plan as it was
+        halo::HostPlan probe;
+        std::string msg;
+        if (n_atoms < 0 || (n_atoms > 0 && !positions))
+            return fail(HALO_ERR_ARG, "halo_plan_rebuild_device: NULL pointer or negative count");
+        const int rc = halo::plan_geometry(n_atoms, box, grid, cutoff, probe, msg);
+        if (rc != halo::kOk) return fail((halo_status)rc, msg);
+    }
+    if (!p->built_on_device) {
+        free_device(p);  // the host-built device copy is replaced
+    } else if (p->d_stage) {
+        (void)hipFree(p->d_stage);
+        p->d_stage = nullptr;
+    }
+    p->uploaded = false;
+    std::string msg;
+    int rc;
+    g_last_error.clear();
+    try {
+        rc = halo::build_plan_device(p, positions, n_atoms, box, grid, cutoff,
+                                     item_entries_from_env(), (hipStream_t)stream, msg);
+    } catch (const std::bad_alloc &) {
+        rc = halo::kErrNoMem;
+        msg = "halo_plan_rebuild_device: out of host memory";
+    } catch (const std::exception &ex) {
+        rc = halo::kErrArg;
+        msg = std::string("halo_plan_rebuild_device: internal error: ") + ex.what();
+    }
+    if (rc != halo::kOk) {
+        free_device(p);
+        p->h = halo::HostPlan();
+        p->h.grid[0] = grid[0];
+        p->h.grid[1] = grid[1];
+        p->h.grid[2] = grid[2];
+        p->h.cutoff = cutoff;
+        p->built_on_device = false;
+        p->invalid = true;
+        return msg.empty() ? (halo_status)rc : fail((halo_status)rc, msg);
+    }
+    p->invalid = false;
     return HALO_OK;
 }
 

@@ -32,6 +32,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <limits>
 #include <string>
@@ -39,6 +40,7 @@
 
 #include "plan.hpp"
 #include "plan_state.hpp"
+#include "sync.hpp"
 
 namespace halo {
 namespace {
@@ -216,9 +218,17 @@ __global__ __launch_bounds__(kBT) void k_home_scatter(const int32_t *__restrict_
     }
 }
 
-// Device copy of the segment table, [pulse][domain] arrays.
+// Device copy of the segment table: per pulse, five rows of n_dom int32
+// (sendSize, send count from home slots, recvSize, atomOffset, map offset),
+// so that a pulse's counts come back, and its offsets go out, in one copy.
+enum { kSendSize = 0, kDepStart = 1, kRecvSize = 2, kAtomOffset = 3, kMapOff = 4, kSegRows = 5 };
 struct SegTable {
-    int32_t *send_size, *dep_start, *recv_size, *atom_offset, *map_off;
+    int32_t *t;
+    int32_t nd;
+    __host__ __device__ int32_t *row(int32_t p, int f) const
+    {
+        return t + ((size_t)p * kSegRows + f) * nd;
+    }
 };
 
 // Selection of pulse p for domain D = blockIdx.x. Candidates in ascending
@@ -247,8 +257,8 @@ __global__ __launch_bounds__(kBT) void k_select(
         c_r = R / (g.grid[0] * g.grid[1]);
     const double face = (double)(c_r + 1);
     const double ncell = (double)g.grid[dim];
-    const int32_t out0 = WRITE ? seg.map_off[p * n_dom + D] : 0;
-    const int32_t limit = WRITE ? seg.send_size[p * n_dom + D] : 0;
+    const int32_t out0 = WRITE ? seg.row(p, kMapOff)[D] : 0;
+    const int32_t limit = WRITE ? seg.row(p, kSendSize)[D] : 0;
     uint32_t count = 0, dep = 0;
     const int32_t zfirst = k == 0 ? -1 : p - 1;
     for (int32_t z = zfirst; z < p; ++z) {
@@ -260,9 +270,9 @@ __global__ __launch_bounds__(kBT) void k_select(
             gids = home_gid + home_start[D];
         } else {
             const int32_t S = recv_from[z * n_dom + D];
-            len = seg.recv_size[z * n_dom + D];
-            slot0 = seg.atom_offset[z * n_dom + D];
-            gids = entry_gid + seg.map_off[z * n_dom + S];
+            len = seg.row(z, kRecvSize)[D];
+            slot0 = seg.row(z, kAtomOffset)[D];
+            gids = entry_gid + seg.row(z, kMapOff)[S];
         }
         for (int32_t b = 0; b < len; b += kBT) {
             const int32_t i = b + (int32_t)threadIdx.x;
@@ -285,8 +295,8 @@ __global__ __launch_bounds__(kBT) void k_select(
         }
     }
     if (!WRITE && threadIdx.x == 0) {
-        seg.send_size[p * n_dom + D] = (int32_t)count;
-        seg.dep_start[p * n_dom + D] = (int32_t)dep;
+        seg.row(p, kSendSize)[D] = (int32_t)count;
+        seg.row(p, kDepStart)[D] = (int32_t)dep;
     }
 }
 
@@ -297,8 +307,8 @@ __global__ __launch_bounds__(kBT) void k_abs_map(const int32_t *__restrict__ loc
                                                  int32_t *__restrict__ abs_map)
 {
     const int32_t s = blockIdx.x;
-    const int32_t D = s % n_dom;
-    const int32_t m0 = seg.map_off[s], n = seg.send_size[s];
+    const int32_t p = s / n_dom, D = s % n_dom;
+    const int32_t m0 = seg.row(p, kMapOff)[D], n = seg.row(p, kSendSize)[D];
     const int64_t b = base[D];
     for (int32_t i = threadIdx.x; i < n; i += kBT) abs_map[m0 + i] = (int32_t)(b + local_map[m0 + i]);
 }
@@ -341,8 +351,8 @@ __global__ __launch_bounds__(kBT) void k_item_masks(WorkItem *__restrict__ items
     for (int32_t i = it->n_indep + (int32_t)threadIdx.x; i < it->n_total; i += kBT) {
         const int32_t slot = local_map[it->map_begin + i];
         for (int32_t r = 0; r < p; ++r) {
-            const int32_t lo = seg.atom_offset[r * n_dom + D];
-            if (slot >= lo && slot < lo + seg.recv_size[r * n_dom + D]) {
+            const int32_t lo = seg.row(r, kAtomOffset)[D];
+            if (slot >= lo && slot < lo + seg.row(r, kRecvSize)[D]) {
                 mine |= 1u << r;
                 break;
             }
@@ -350,13 +360,13 @@ __global__ __launch_bounds__(kBT) void k_item_masks(WorkItem *__restrict__ items
     }
     if (mine) atomicOr(&xm, mine);
     // the item's sources: R's region of pulse p
-    const int32_t lo = seg.atom_offset[p * n_dom + R];
-    const int32_t hi = lo + seg.recv_size[p * n_dom + R];
+    const int32_t lo = seg.row(p, kAtomOffset)[R];
+    const int32_t hi = lo + seg.row(p, kRecvSize)[R];
     uint32_t am = 0;
     const int32_t q = p + 1 + (int32_t)threadIdx.x;
     if (q < n_pulse && lo < hi) {
-        const int32_t *m = local_map + seg.map_off[q * n_dom + R];
-        int32_t a = 0, b = seg.send_size[q * n_dom + R];
+        const int32_t *m = local_map + seg.row(q, kMapOff)[R];
+        int32_t a = 0, b = seg.row(q, kSendSize)[R];
         while (a < b) {  // first entry >= lo
             const int32_t mid = a + (b - a) / 2;
             if (m[mid] < lo)
@@ -364,7 +374,7 @@ __global__ __launch_bounds__(kBT) void k_item_masks(WorkItem *__restrict__ items
             else
                 b = mid;
         }
-        if (a < seg.send_size[q * n_dom + R] && m[a] < hi) am = 1u << q;
+        if (a < seg.row(q, kSendSize)[R] && m[a] < hi) am = 1u << q;
     }
     __shared__ uint32_t amask;
     if (threadIdx.x == 0) amask = 0;
@@ -409,32 +419,98 @@ __global__ __launch_bounds__(kBT) void k_piece_stats(const Piece *__restrict__ p
     }
 }
 
-// Device arrays of one build; freed on every exit unless released.
-struct DevArrays {
-    std::vector<void *> owned;
-    template <class T>
-    hipError_t alloc(T **p, size_t n)
-    {
-        *p = nullptr;
-        hipError_t e = hipMalloc((void **)p, std::max<size_t>(n, 1) * sizeof(T));
-        if (e == hipSuccess) owned.push_back((void *)*p);
-        return e;
-    }
-    void release(void *p)
-    {
-        for (auto &q : owned)
-            if (q == p) q = nullptr;
-    }
-    ~DevArrays()
-    {
-        for (void *p : owned)
-            if (p) (void)hipFree(p);
-    }
-};
-
 unsigned grid_for(int64_t n, int per_block) { return (unsigned)((n + per_block - 1) / per_block); }
 
+constexpr size_t kAlign = 256;
+
+size_t aligned(size_t bytes) { return (bytes + kAlign - 1) & ~(kAlign - 1); }
+
+// Make the arena hold at least `bytes` (contents are not kept; 1/8 slack so
+// that rebuilds of a slightly larger system reuse it) and start carving from
+// its beginning.
+hipError_t arena_reserve(Arena &a, size_t bytes)
+{
+    a.used = 0;
+    if (bytes <= a.cap && a.base) return hipSuccess;
+    if (a.base) (void)hipFree(a.base);
+    a.base = nullptr;
+    a.cap = 0;
+    const size_t want = std::max<size_t>(aligned(bytes + bytes / 8), kAlign);
+    hipError_t e = hipMalloc((void **)&a.base, want);
+    if (e == hipSuccess) a.cap = want;
+    return e;
+}
+
+template <class T>
+T *arena_take(Arena &a, size_t n)
+{
+    T *p = (T *)(a.base + a.used);
+    a.used += aligned(std::max<size_t>(n, 1) * sizeof(T));
+    return p;
+}
+
+void arena_free(Arena &a)
+{
+    if (a.base) (void)hipFree(a.base);
+    a = Arena();
+}
+
+hipError_t pinned_reserve(DeviceBuild &B, size_t bytes)
+{
+    if (bytes <= B.pinned_cap && B.pinned) return hipSuccess;
+    if (B.pinned) (void)hipHostFree(B.pinned);
+    B.pinned = nullptr;
+    B.pinned_cap = 0;
+    const size_t want = std::max<size_t>(aligned(bytes + bytes / 8), kAlign);
+    hipError_t e = hipHostMalloc((void **)&B.pinned, want, hipHostMallocDefault);
+    if (e == hipSuccess) B.pinned_cap = want;
+    return e;
+}
+
+// The entries arena holds the local-slot indexMap and the sent atoms' ids,
+// `cap` entries each; grown (keeping the first `used` entries) when a pulse
+// needs more.
+hipError_t entries_reserve(DeviceBuild &B, size_t need, size_t used, hipStream_t st)
+{
+    if (need <= B.entry_cap && B.entries.base) return hipSuccess;
+    Arena old = B.entries;
+    const size_t old_cap = B.entry_cap;
+    B.entries = Arena();
+    B.entry_cap = 0;
+    const size_t cap = std::max<size_t>(need, old_cap * 2);
+    hipError_t e = arena_reserve(B.entries, 2 * aligned(cap * 4));
+    if (e == hipSuccess && used > 0) {
+        e = hipMemcpyAsync(B.entries.base, old.base, used * 4, hipMemcpyDeviceToDevice, st);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(B.entries.base + aligned(cap * 4), old.base + aligned(old_cap * 4),
+                               used * 4, hipMemcpyDeviceToDevice, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+    }
+    arena_free(old);
+    if (e == hipSuccess) B.entry_cap = cap;
+    return e;
+}
+
 }  // namespace
+
+void free_device_build(halo_plan *pl)
+{
+    if (!pl->dev) return;
+    DeviceBuild &B = *pl->dev;
+    for (Arena *a : {&B.work, &B.entries, &B.maps, &B.pieces, &B.tables}) arena_free(*a);
+    if (B.pinned) (void)hipHostFree(B.pinned);
+    delete pl->dev;
+    pl->dev = nullptr;
+    // these pointed into the arenas
+    pl->d_idx = pl->d_local_map = pl->d_recv_from = pl->d_send_to = nullptr;
+    pl->d_forder = pl->d_dest_start = nullptr;
+    pl->d_home_slot = nullptr;
+    pl->d_mask = nullptr;
+    pl->d_items = nullptr;
+    pl->d_seg_items = pl->d_x_arrivals = pl->d_zone_chunks = nullptr;
+    pl->d_chunks = nullptr;
+    pl->d_shift4 = nullptr;
+}
 
 int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const float *box,
                       const int32_t *grid, float cutoff, int32_t item_entries, hipStream_t st,
@@ -456,7 +532,10 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         msg = "halo_plan_create_device: too many atoms for one plan";
         return kErrRange;
     }
+    if (!pl->dev) pl->dev = new DeviceBuild();
+    DeviceBuild &B = *pl->dev;
     const int32_t nd = P.n_dom, np = P.n_pulse;
+    const size_t nseg = (size_t)np * nd;
     Geom g;
     for (int d = 0; d < 3; ++d) {
         g.width[d] = P.width[d];
@@ -464,7 +543,6 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         g.box[d] = box[d];
         g.grid[d] = grid[d];
     }
-    DevArrays A;
     hipError_t e = hipSuccess;
     auto hip_err = [&](const char *what) {
         msg = std::string("halo_plan_create_device: ") + what + ": " + hipGetErrorString(e);
@@ -476,45 +554,66 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
             return hip_err(what);       \
     } while (0)
 
-    // -- domains and home order ------------------------------------------------
+    // -- build temporaries in one arena ------------------------------------------
     const int32_t n_tiles = (int32_t)std::max<int64_t>(1, (n_atoms + kTile - 1) / kTile);
-    int32_t *owner, *home_rank, *home_gid, *d_n_home, *d_home_start;
-    uint32_t *tile_hist;
-    unsigned long long *bad;
-    HALO_TRY(A.alloc(&owner, n_atoms), "hipMalloc");
-    HALO_TRY(A.alloc(&home_rank, n_atoms), "hipMalloc");
-    HALO_TRY(A.alloc(&home_gid, n_atoms), "hipMalloc");
-    HALO_TRY(A.alloc(&d_n_home, nd), "hipMalloc");
-    HALO_TRY(A.alloc(&d_home_start, nd), "hipMalloc");
-    HALO_TRY(A.alloc(&tile_hist, (size_t)nd * n_tiles), "hipMalloc");
-    HALO_TRY(A.alloc(&bad, 1), "hipMalloc");
-    const unsigned long long none = ~0ull;
-    HALO_TRY(hipMemcpyAsync(bad, &none, sizeof(none), hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+    const size_t N = (size_t)n_atoms;
+    HALO_TRY(arena_reserve(B.work, 3 * aligned(std::max<size_t>(N, 1) * 4) +
+                                       aligned((size_t)nd * n_tiles * 4) + aligned(8 + 4 * nd) +
+                                       aligned(4 * nd) + aligned(std::max<size_t>(nseg, 1) * 20) +
+                                       aligned(std::max<size_t>(nseg, 1) * 8) + aligned(8 * nd)),
+             "device memory");
+    int32_t *owner = arena_take<int32_t>(B.work, N);
+    int32_t *home_rank = arena_take<int32_t>(B.work, N);
+    int32_t *home_gid = arena_take<int32_t>(B.work, N);
+    uint32_t *tile_hist = arena_take<uint32_t>(B.work, (size_t)nd * n_tiles);
+    char *xfer = arena_take<char>(B.work, 8 + 4 * (size_t)nd);  // first bad atom, home counts
+    unsigned long long *bad = (unsigned long long *)xfer;
+    int32_t *d_n_home = (int32_t *)(xfer + 8);
+    int32_t *d_home_start = arena_take<int32_t>(B.work, nd);
+    SegTable sg{arena_take<int32_t>(B.work, nseg * kSegRows), nd};
+    int32_t *w_send_to = arena_take<int32_t>(B.work, 2 * nseg);
+    int32_t *w_recv_from = w_send_to + nseg;
+    int64_t *d_base = arena_take<int64_t>(B.work, nd);
+
+    // host staging: fixed part of the build
+    const size_t h_down0 = 0, h_start = aligned(8 + 4 * nd), h_pdown = h_start + aligned(4 * nd),
+                 h_pup = h_pdown + aligned(8 * (size_t)nd), h_tab = h_pup + aligned(12 * (size_t)nd),
+                 h_base = h_tab + aligned(8 * std::max<size_t>(nseg, 1)),
+                 h_fixed = h_base + aligned(8 * (size_t)nd);
+    HALO_TRY(pinned_reserve(B, h_fixed), "pinned host memory");
+    char *hp = B.pinned;
+    std::memcpy(hp + h_tab, P.send_to.data(), nseg * 4);
+    std::memcpy(hp + h_tab + nseg * 4, P.recv_from.data(), nseg * 4);
+    if (nseg > 0)
+        HALO_TRY(hipMemcpyAsync(w_send_to, hp + h_tab, 2 * nseg * 4, hipMemcpyHostToDevice, st),
+                 "hipMemcpyAsync");
+
+    // -- domains and home order ------------------------------------------------
+    HALO_TRY(hipMemsetAsync(bad, 0xff, 8, st), "hipMemsetAsync");
     const size_t lds = (size_t)nd * sizeof(uint32_t);
-    if (n_atoms > 0) {
+    if (n_atoms > 0)
         k_owner<<<n_tiles, kBT, lds, st>>>(pos, n_atoms, g, nd, n_tiles, owner, tile_hist, bad);
-    } else {
+    else
         HALO_TRY(hipMemsetAsync(tile_hist, 0, (size_t)nd * n_tiles * 4, st), "hipMemsetAsync");
-    }
     k_tile_scan<<<nd, kBT, 0, st>>>(tile_hist, n_tiles, d_n_home);
     HALO_TRY(hipGetLastError(), "launch");
-    unsigned long long first_bad = 0;
-    P.n_home.assign(nd, 0);
-    HALO_TRY(hipMemcpyAsync(&first_bad, bad, sizeof(first_bad), hipMemcpyDeviceToHost, st),
-             "hipMemcpyAsync");
-    HALO_TRY(hipMemcpyAsync(P.n_home.data(), d_n_home, (size_t)nd * 4, hipMemcpyDeviceToHost, st),
+    HALO_TRY(hipMemcpyAsync(hp + h_down0, xfer, 8 + 4 * (size_t)nd, hipMemcpyDeviceToHost, st),
              "hipMemcpyAsync");
     HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
-    if (first_bad != none) {
+    unsigned long long first_bad;
+    std::memcpy(&first_bad, hp + h_down0, 8);
+    if (first_bad != ~0ull) {
         msg = "halo_plan_create: atom " + std::to_string(first_bad) +
               " lies outside [0, L) or is not finite";
         return kErrRange;
     }
-    std::vector<int32_t> home_start(nd, 0);
+    P.n_home.assign(nd, 0);
+    std::memcpy(P.n_home.data(), hp + h_down0 + 8, 4 * (size_t)nd);
     {
+        int32_t *hs = (int32_t *)(hp + h_start);
         int64_t acc = 0;
         for (int32_t d = 0; d < nd; ++d) {
-            home_start[d] = (int32_t)acc;
+            hs[d] = (int32_t)acc;
             acc += P.n_home[d];
         }
         if (acc != n_atoms) {
@@ -522,50 +621,35 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
             return kErrArg;
         }
     }
-    HALO_TRY(hipMemcpyAsync(d_home_start, home_start.data(), (size_t)nd * 4,
-                            hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+    HALO_TRY(hipMemcpyAsync(d_home_start, hp + h_start, 4 * (size_t)nd, hipMemcpyHostToDevice, st),
+             "hipMemcpyAsync");
     if (n_atoms > 0)
         k_home_scatter<<<n_tiles, kBT, lds, st>>>(owner, n_atoms, nd, n_tiles, tile_hist,
                                                   d_home_start, home_gid, home_rank);
     HALO_TRY(hipGetLastError(), "launch");
 
     // -- pulses -------------------------------------------------------------------
-    const size_t nseg = (size_t)np * nd;
     P.seg.assign(nseg, Segment());
-    SegTable sg;
-    int32_t *d_send_to, *d_recv_from, *local_map, *entry_gid;
-    HALO_TRY(A.alloc(&sg.send_size, nseg), "hipMalloc");
-    HALO_TRY(A.alloc(&sg.dep_start, nseg), "hipMalloc");
-    HALO_TRY(A.alloc(&sg.recv_size, nseg), "hipMalloc");
-    HALO_TRY(A.alloc(&sg.atom_offset, nseg), "hipMalloc");
-    HALO_TRY(A.alloc(&sg.map_off, nseg), "hipMalloc");
-    HALO_TRY(A.alloc(&d_send_to, nseg), "hipMalloc");
-    HALO_TRY(A.alloc(&d_recv_from, nseg), "hipMalloc");
-    HALO_TRY(hipMemcpyAsync(d_send_to, P.send_to.data(), nseg * 4, hipMemcpyHostToDevice, st),
-             "hipMemcpyAsync");
-    HALO_TRY(hipMemcpyAsync(d_recv_from, P.recv_from.data(), nseg * 4, hipMemcpyHostToDevice, st),
-             "hipMemcpyAsync");
-    // entry arrays grow with the pulses (sizes become known pulse by pulse)
-    size_t cap = std::max<size_t>(1024, (size_t)n_atoms * 2);
-    HALO_TRY(A.alloc(&local_map, cap), "hipMalloc");
-    HALO_TRY(A.alloc(&entry_gid, cap), "hipMalloc");
+    HALO_TRY(entries_reserve(B, std::max<size_t>(1024, 2 * N), 0, st), "device memory");
     std::vector<int32_t> cur(P.n_home.begin(), P.n_home.end());
-    std::vector<int32_t> send_size(nd), dep_start(nd), row_map(nd), row_recv(nd), row_off(nd);
     int64_t entries = 0;
     for (int32_t p = 0; p < np; ++p) {
         const int dim = P.pulse_dim[p];
         const int32_t k = P.pulse_k[p];
         const size_t r0 = (size_t)p * nd;
-        k_select<false><<<nd, kBT, 0, st>>>(pos, p, dim, k, nd, g, P.reach[dim], d_send_to,
-                                            d_recv_from, d_n_home, d_home_start, home_gid, sg,
-                                            entry_gid, local_map, entry_gid);
+        int32_t *lmap = (int32_t *)B.entries.base;
+        int32_t *egid = (int32_t *)(B.entries.base + aligned(B.entry_cap * 4));
+        k_select<false><<<nd, kBT, 0, st>>>(pos, p, dim, k, nd, g, P.reach[dim], w_send_to,
+                                            w_recv_from, d_n_home, d_home_start, home_gid, sg,
+                                            egid, lmap, egid);
         HALO_TRY(hipGetLastError(), "launch");
-        HALO_TRY(hipMemcpyAsync(send_size.data(), sg.send_size + r0, (size_t)nd * 4,
-                                hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
-        HALO_TRY(hipMemcpyAsync(dep_start.data(), sg.dep_start + r0, (size_t)nd * 4,
+        // send counts and home-slot counts of this pulse: two adjacent rows
+        HALO_TRY(hipMemcpyAsync(hp + h_pdown, sg.row(p, kSendSize), 8 * (size_t)nd,
                                 hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
         HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
-        // map offsets (pulse-major, then domain) and the receivers' regions
+        const int32_t *send_size = (const int32_t *)(hp + h_pdown);
+        const int32_t *dep_start = send_size + nd;
+        int32_t *up = (int32_t *)(hp + h_pup);  // recvSize, atomOffset, map offset rows
         const int64_t entries_before = entries;
         for (int32_t D = 0; D < nd; ++D) {
             Segment &s = P.seg[r0 + D];
@@ -573,7 +657,7 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
             s.send_size = send_size[D];
             s.dep_start = dep_start[D];
             s.map_off = entries;
-            row_map[D] = (int32_t)entries;
+            up[2 * nd + D] = (int32_t)entries;
             entries += send_size[D];
             const int32_t cd = dim == 0   ? D % grid[0]
                                : dim == 1 ? (D / grid[0]) % grid[1]
@@ -594,43 +678,22 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
             cur[R] += send_size[D];
         }
         for (int32_t D = 0; D < nd; ++D) {
-            row_recv[D] = P.seg[r0 + D].recv_size;
-            row_off[D] = P.seg[r0 + D].atom_offset;
+            up[D] = P.seg[r0 + D].recv_size;
+            up[nd + D] = P.seg[r0 + D].atom_offset;
         }
-        HALO_TRY(hipMemcpyAsync(sg.map_off + r0, row_map.data(), (size_t)nd * 4,
-                                hipMemcpyHostToDevice, st), "hipMemcpyAsync");
-        HALO_TRY(hipMemcpyAsync(sg.recv_size + r0, row_recv.data(), (size_t)nd * 4,
-                                hipMemcpyHostToDevice, st), "hipMemcpyAsync");
-        HALO_TRY(hipMemcpyAsync(sg.atom_offset + r0, row_off.data(), (size_t)nd * 4,
-                                hipMemcpyHostToDevice, st), "hipMemcpyAsync");
-        if ((size_t)entries > cap) {
-            const size_t ncap = std::max<size_t>((size_t)entries, cap * 2);
-            int32_t *nl, *ng;
-            HALO_TRY(A.alloc(&nl, ncap), "hipMalloc");
-            HALO_TRY(A.alloc(&ng, ncap), "hipMalloc");
-            const size_t used = (size_t)entries_before;
-            if (used > 0) {
-                HALO_TRY(hipMemcpyAsync(nl, local_map, used * 4, hipMemcpyDeviceToDevice, st),
-                         "hipMemcpyAsync");
-                HALO_TRY(hipMemcpyAsync(ng, entry_gid, used * 4, hipMemcpyDeviceToDevice, st),
-                         "hipMemcpyAsync");
-            }
-            HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
-            A.release(local_map);
-            A.release(entry_gid);
-            (void)hipFree(local_map);
-            (void)hipFree(entry_gid);
-            local_map = nl;
-            entry_gid = ng;
-            cap = ncap;
-        }
-        k_select<true><<<nd, kBT, 0, st>>>(pos, p, dim, k, nd, g, P.reach[dim], d_send_to,
-                                           d_recv_from, d_n_home, d_home_start, home_gid, sg,
-                                           entry_gid, local_map, entry_gid);
+        HALO_TRY(hipMemcpyAsync(sg.row(p, kRecvSize), up, 12 * (size_t)nd, hipMemcpyHostToDevice,
+                                st), "hipMemcpyAsync");
+        HALO_TRY(entries_reserve(B, (size_t)entries, (size_t)entries_before, st), "device memory");
+        lmap = (int32_t *)B.entries.base;
+        egid = (int32_t *)(B.entries.base + aligned(B.entry_cap * 4));
+        k_select<true><<<nd, kBT, 0, st>>>(pos, p, dim, k, nd, g, P.reach[dim], w_send_to,
+                                           w_recv_from, d_n_home, d_home_start, home_gid, sg,
+                                           egid, lmap, egid);
         HALO_TRY(hipGetLastError(), "launch");
     }
+    int32_t *local_map = (int32_t *)B.entries.base;
 
-    // -- layout ---------------------------------------------------------------------
+    // -- layout, then everything the host derives from the sizes -----------------------
     P.base.assign(nd, 0);
     P.n_halo.assign(nd, 0);
     int64_t acc = 0;
@@ -646,57 +709,80 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         return kErrRange;
     }
     P.n_entries = entries;
-    int64_t *d_base, *home_slot;
-    int32_t *abs_map;
-    HALO_TRY(A.alloc(&d_base, nd), "hipMalloc");
-    HALO_TRY(A.alloc(&home_slot, n_atoms), "hipMalloc");
-    HALO_TRY(A.alloc(&abs_map, entries), "hipMalloc");
-    HALO_TRY(hipMemcpyAsync(d_base, P.base.data(), (size_t)nd * 8, hipMemcpyHostToDevice, st),
+    P.has_chunks = plan_has_chunks(P);
+    P.chunk_slots = item_entries;
+    make_items(P, item_entries, false);
+    const std::vector<Piece> pieces =
+        P.has_chunks ? chunk_pieces(P, item_entries) : std::vector<Piece>();
+    const size_t npc = pieces.size();
+    // host staging for the rest: base, pieces, their statistics, the tables
+    const size_t n_items = P.items.size();
+    // items; seg_items, send_to, recv_from, dest_start, x_arrivals, zone_chunks;
+    // shift4; chunks; chunk order
+    const size_t tab_bytes = aligned(std::max<size_t>(n_items, 1) * sizeof(WorkItem)) +
+                             6 * aligned(std::max<size_t>(nseg, 1) * 4) +
+                             aligned(std::max<size_t>(nseg, 1) * 16) +
+                             aligned(std::max<size_t>(npc, 1) * sizeof(Chunk)) +
+                             aligned(std::max<size_t>(npc, 1) * 4);
+    const size_t h_pieces = h_fixed, h_stats = h_pieces + aligned(std::max<size_t>(npc, 1) * 16),
+                 h_tables = h_stats + aligned(std::max<size_t>(npc, 1) * sizeof(PieceStats)),
+                 h_total = h_tables + tab_bytes;
+    if (h_total > B.pinned_cap) {
+        HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");  // no copy from it in flight
+        char *keep = (char *)std::malloc(h_fixed);
+        if (!keep) {
+            msg = "halo_plan_create_device: out of host memory";
+            return kErrNoMem;
+        }
+        std::memcpy(keep, B.pinned, h_fixed);
+        e = pinned_reserve(B, h_total);
+        if (e == hipSuccess) std::memcpy(B.pinned, keep, h_fixed);
+        std::free(keep);
+        if (e != hipSuccess) return hip_err("pinned host memory");
+        hp = B.pinned;
+    }
+    std::memcpy(hp + h_base, P.base.data(), 8 * (size_t)nd);
+    HALO_TRY(hipMemcpyAsync(d_base, hp + h_base, 8 * (size_t)nd, hipMemcpyHostToDevice, st),
              "hipMemcpyAsync");
+
+    // -- maps: absolute indexMap, home slots, pulse masks ------------------------------
+    const size_t S = (size_t)P.total_slots;
+    HALO_TRY(arena_reserve(B.maps, aligned(std::max<int64_t>(entries, 1) * 4) +
+                                       aligned(std::max<size_t>(N, 1) * 8) +
+                                       (P.has_chunks ? aligned(S) : 0)),
+             "device memory");
+    int32_t *abs_map = arena_take<int32_t>(B.maps, (size_t)entries);
+    int64_t *home_slot = arena_take<int64_t>(B.maps, N);
+    uint8_t *mask = P.has_chunks ? arena_take<uint8_t>(B.maps, S) : nullptr;
     if (nseg > 0) k_abs_map<<<(unsigned)nseg, kBT, 0, st>>>(local_map, sg, nd, d_base, abs_map);
     if (n_atoms > 0)
         k_home_slot<<<grid_for(n_atoms, kBT), kBT, 0, st>>>(owner, home_rank, d_base, n_atoms,
                                                             home_slot);
     HALO_TRY(hipGetLastError(), "launch");
-
-    // -- work items (host order, device wait masks) -----------------------------------
-    make_items(P, item_entries, false);
-    WorkItem *items;
-    HALO_TRY(A.alloc(&items, P.items.size()), "hipMalloc");
-    if (!P.items.empty()) {
-        HALO_TRY(hipMemcpyAsync(items, P.items.data(), P.items.size() * sizeof(WorkItem),
-                                hipMemcpyHostToDevice, st), "hipMemcpyAsync");
-        k_item_masks<<<(unsigned)P.items.size(), kBT, 0, st>>>(items, local_map, sg, nd, np);
-        HALO_TRY(hipGetLastError(), "launch");
-    }
-
-    // -- transposed form -----------------------------------------------------------------
-    uint8_t *mask = nullptr;
-    P.has_chunks = plan_has_chunks(P);
-    P.chunk_slots = item_entries;
+    std::vector<PieceStats> stats(npc);
     if (P.has_chunks) {
-        HALO_TRY(A.alloc(&mask, (size_t)P.total_slots), "hipMalloc");
-        HALO_TRY(hipMemsetAsync(mask, 0, (size_t)P.total_slots, st), "hipMemsetAsync");
+        HALO_TRY(hipMemsetAsync(mask, 0, S, st), "hipMemsetAsync");
         for (int32_t p = 0; p < np; ++p) {
             const int32_t e0 = (int32_t)P.at(p, 0).map_off;
             const int32_t e1 = p + 1 < np ? (int32_t)P.at(p + 1, 0).map_off : (int32_t)entries;
             if (e1 > e0) k_mask<<<grid_for(e1 - e0, kBT), kBT, 0, st>>>(abs_map, e0, e1, p, mask);
         }
-        const std::vector<Piece> pieces = chunk_pieces(P, item_entries);
-        std::vector<PieceStats> stats(pieces.size());
-        if (!pieces.empty()) {
-            Piece *d_pieces;
-            PieceStats *d_stats;
-            HALO_TRY(A.alloc(&d_pieces, pieces.size()), "hipMalloc");
-            HALO_TRY(A.alloc(&d_stats, pieces.size()), "hipMalloc");
-            HALO_TRY(hipMemcpyAsync(d_pieces, pieces.data(), pieces.size() * sizeof(Piece),
+        if (npc > 0) {
+            HALO_TRY(arena_reserve(B.pieces, aligned(npc * sizeof(Piece)) +
+                                                 aligned(npc * sizeof(PieceStats))),
+                     "device memory");
+            Piece *d_pieces = arena_take<Piece>(B.pieces, npc);
+            PieceStats *d_stats = arena_take<PieceStats>(B.pieces, npc);
+            std::memcpy(hp + h_pieces, pieces.data(), npc * sizeof(Piece));
+            HALO_TRY(hipMemcpyAsync(d_pieces, hp + h_pieces, npc * sizeof(Piece),
                                     hipMemcpyHostToDevice, st), "hipMemcpyAsync");
-            k_piece_stats<<<(unsigned)pieces.size(), kBT, 0, st>>>(d_pieces, mask, np, d_stats);
+            k_piece_stats<<<(unsigned)npc, kBT, 0, st>>>(d_pieces, mask, np, d_stats);
             HALO_TRY(hipGetLastError(), "launch");
-            HALO_TRY(hipMemcpyAsync(stats.data(), d_stats, stats.size() * sizeof(PieceStats),
+            HALO_TRY(hipMemcpyAsync(hp + h_stats, d_stats, npc * sizeof(PieceStats),
                                     hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
         }
         HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
+        std::memcpy(stats.data(), hp + h_stats, npc * sizeof(PieceStats));
         try {
             finish_chunks(P, item_entries, pieces, stats);
         } catch (const std::exception &ex) {
@@ -704,22 +790,83 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
             return kErrArg;
         }
     }
-    HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
 
-    // hand the device arrays to the plan
+    // -- tables: items, segment tables, chunks; one copy ---------------------------------
+    HALO_TRY(arena_reserve(B.tables, tab_bytes), "device memory");
+    char *tp = hp + h_tables;
+    size_t off = 0;
+    auto put = [&](const void *src, size_t bytes, size_t reserve_bytes) {
+        if (bytes) std::memcpy(tp + off, src, bytes);
+        void *dst = B.tables.base + off;
+        off += aligned(std::max<size_t>(reserve_bytes, 1));
+        return dst;
+    };
+    const size_t ns4 = std::max<size_t>(nseg, 1) * 4;
+    WorkItem *items = (WorkItem *)put(P.items.data(), n_items * sizeof(WorkItem),
+                                      n_items * sizeof(WorkItem));
+    uint32_t *seg_items = (uint32_t *)put(P.seg_items.data(), nseg * 4, ns4);
+    int32_t *send_to = (int32_t *)put(P.send_to.data(), nseg * 4, ns4);
+    int32_t *recv_from = (int32_t *)put(P.recv_from.data(), nseg * 4, ns4);
+    Chunk *chunks = nullptr;
+    int32_t *forder = nullptr, *dest_start = nullptr;
+    float *shift4 = nullptr;
+    uint32_t *x_arrivals = nullptr, *zone_chunks = nullptr;
+    if (P.has_chunks) {
+        const size_t nc = P.chunks.size();
+        chunks = (Chunk *)put(P.chunks.data(), nc * sizeof(Chunk), npc * sizeof(Chunk));
+        forder = (int32_t *)put(P.chunk_forder.data(), nc * 4, npc * 4);
+        dest_start = (int32_t *)put(P.dest_start.data(), nseg * 4, ns4);
+        shift4 = (float *)put(P.shift4.data(), nseg * 16, std::max<size_t>(nseg, 1) * 16);
+        x_arrivals = (uint32_t *)put(P.x_arrivals.data(), nseg * 4, ns4);
+        zone_chunks = (uint32_t *)put(P.zone_chunks.data(), nseg * 4, ns4);
+    }
+    if (off > tab_bytes) {
+        msg = "halo_plan_create_device: internal error: table layout";
+        return kErrArg;
+    }
+    HALO_TRY(hipMemcpyAsync(B.tables.base, tp, off, hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+    if (n_items > 0) {
+        k_item_masks<<<(unsigned)n_items, kBT, 0, st>>>(items, local_map, sg, nd, np);
+        HALO_TRY(hipGetLastError(), "launch");
+    }
+
+    // -- counters and the error word --------------------------------------------------------
+    const size_t words = 4 * nseg * kCounterStride + kCounterStride;
+    if (pl->d_state && pl->state_words != words) {
+        (void)hipFree(pl->d_state);
+        pl->d_state = nullptr;
+    }
+    if (!pl->d_state) HALO_TRY(hipMalloc((void **)&pl->d_state, words * 4), "device memory");
+    pl->state_words = words;
+    HALO_TRY(hipMemsetAsync(pl->d_state, 0, words * 4, st), "hipMemsetAsync");
+    if (!pl->h_err) {
+        HALO_TRY(hipHostMalloc((void **)&pl->h_err, 64, hipHostMallocMapped), "pinned memory");
+        HALO_TRY(hipHostGetDevicePointer((void **)&pl->d_err, pl->h_err, 0), "pinned memory");
+    }
+    HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
+    std::memset(pl->h_err, 0, 64);
+    HALO_TRY(hipGetDevice(&pl->device), "hipGetDevice");
+
     pl->d_idx = abs_map;
-    pl->d_items = items;
-    pl->d_mask = mask;
     pl->d_local_map = local_map;
     pl->d_home_slot = home_slot;
-    pl->d_send_to = d_send_to;
-    pl->d_recv_from = d_recv_from;
-    for (void *q : {(void *)abs_map, (void *)items, (void *)mask, (void *)local_map,
-                    (void *)home_slot, (void *)d_send_to, (void *)d_recv_from})
-        A.release(q);
+    pl->d_mask = mask;
+    pl->d_items = items;
+    pl->d_seg_items = seg_items;
+    pl->d_send_to = send_to;
+    pl->d_recv_from = recv_from;
+    pl->d_chunks = chunks;
+    pl->d_forder = forder;
+    pl->d_dest_start = dest_start;
+    pl->d_shift4 = shift4;
+    pl->d_x_arrivals = x_arrivals;
+    pl->d_zone_chunks = zone_chunks;
+    pl->epoch_x = pl->epoch_f = pl->epoch_xc = pl->epoch_fc = 0;
+    pl->poisoned = false;
     pl->built_on_device = true;
+    pl->uploaded = true;
 #undef HALO_TRY
-    return plan_upload(pl);
+    return kOk;
 }
 
 }  // namespace halo

@@ -5,8 +5,33 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <string>
 
 #include "plan.hpp"
+
+namespace halo {
+
+// One device allocation carved into 256-byte aligned arrays.
+struct Arena {
+    char *base = nullptr;
+    size_t cap = 0;
+    size_t used = 0;
+};
+
+// Device memory of a plan built on the GPU, kept across rebuilds and grown
+// only when a rebuild needs more.
+struct DeviceBuild {
+    Arena work;               // build temporaries
+    Arena entries;            // local-slot indexMap and sent atom ids
+    size_t entry_cap = 0;     // entries each array of `entries` holds
+    Arena maps;               // absolute indexMap, home slots, pulse masks
+    Arena pieces;             // chunk candidates and their statistics
+    Arena tables;             // work items, segment tables, chunks
+    char *pinned = nullptr;   // host staging for the small copies
+    size_t pinned_cap = 0;
+};
+
+}  // namespace halo
 
 struct halo_plan {
     halo::HostPlan h;
@@ -14,6 +39,8 @@ struct halo_plan {
     bool uploaded = false;
     bool poisoned = false;
     bool built_on_device = false;  // host copies of the maps are fetched on first use
+    bool invalid = false;          // a rebuild failed: empty until rebuilt
+    halo::DeviceBuild *dev = nullptr;  // arenas of a device-built plan
     int32_t *d_idx = nullptr;      // concatenated indexMap, absolute slots
     halo::WorkItem *d_items = nullptr;
     int32_t *d_recv_from = nullptr;
@@ -50,8 +77,12 @@ namespace halo {
 // Returns a halo_status code; the message goes to halo_last_error.
 int plan_upload(halo_plan *p);
 
+// Free the arenas of a device-built plan and clear the pointers into them.
+void free_device_build(halo_plan *p);
+
 // Build p->h and its device arrays on the GPU from device-resident positions
-// (plan_device.hip). Returns a status code and a message on failure.
+// (plan_device.hip), reusing p's arenas from an earlier device build.
+// Returns a status code and a message on failure.
 int build_plan_device(halo_plan *p, const float *pos, int64_t n_atoms, const float *box,
                       const int32_t *grid, float cutoff, int32_t item_entries, hipStream_t stream,
                       std::string &msg);

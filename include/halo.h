@@ -96,6 +96,22 @@ halo_status halo_plan_create_device(const float *positions, int64_t n_atoms, con
                                     const int32_t *grid, float cutoff, void *stream,
                                     halo_plan **out);
 
+/* Rebuild an existing plan on the GPU for new positions (a repartitioning
+ * step), keeping its domain grid and cutoff; `box` may change (pressure
+ * coupling). The result is the plan halo_plan_create_device would build, and
+ * a plan built on the device keeps its device memory (grown only when the new
+ * plan needs more), so a rebuild allocates nothing in the steady state.
+ *   positions, n_atoms, stream : as halo_plan_create_device
+ *   box : host, 3 float32
+ * The counters restart (no exchange of this plan may be in flight on any
+ * stream); total_slots, the layout and the home slots change, so x and f must
+ * be re-laid out by the caller. Argument and geometry errors leave the plan
+ * unchanged; any other error (HALO_ERR_RANGE for a position out of range, a
+ * HIP failure) leaves it empty, and exchanges return HALO_ERR_STATE until a
+ * rebuild succeeds. */
+halo_status halo_plan_rebuild_device(halo_plan *plan, const float *positions, int64_t n_atoms,
+                                     const float *box, void *stream);
+
 /* Free the plan and its device metadata (NULL is accepted). Waits for nothing:
  * the caller must make sure no exchange on the plan is still running. */
 void halo_plan_destroy(halo_plan *plan);

@@ -125,3 +125,67 @@ def test_device_plan_geometry_errors(torch, oracle_mod, args):
     with pytest.raises(HaloError) as e:
         device_plan(torch, pos, *args)
     assert e.value.code == want
+
+
+def test_rebuild_in_place(torch, oracle_mod):
+    """A device-built plan rebuilt for new positions (smaller, then larger
+    systems, then a slightly changed box) is each time the plan of those
+    positions, and its exchanges are exact."""
+    w = W.WORKLOADS[3]
+    dp = device_plan(torch, W.workload_positions(w), w.box, w.grid, w.cutoff)
+    cases = [(w.box, 200_000, 31), (w.box, 337_500, 32), (w.box, 420_000, 33),
+             ((15.2, 14.9, 15.0), 337_500, 34)]
+    for box, n, seed in cases:
+        pos = W.positions(box, n, seed)
+        say(f"rebuild: {n} atoms, box {box}")
+        dp.rebuild_on_device(torch.from_numpy(pos).cuda(), box)
+        o = oracle_mod.Oracle(pos, box, w.grid, w.cutoff)
+        compare_plans(dp, o)
+        np.testing.assert_array_equal(dp.item_waits(), HaloPlan(pos, box, w.grid,
+                                                                 w.cutoff).item_waits())
+        x0 = o.home_filled(np.nan)
+        x = torch.from_numpy(x0.copy()).cuda()
+        dp.exchange_x(x)
+        base, n_home, n_halo = o.domains()
+        f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, seed)
+        f = torch.from_numpy(f0.copy()).cuda()
+        dp.exchange_f(f)
+        torch.cuda.synchronize()
+        dp.sync()
+        assert_bitwise(x.cpu().numpy(), o.exchange_x(x0.copy()), f"rebuild {n} x")
+        assert_bitwise(f.cpu().numpy(), o.exchange_f(f0.copy()), f"rebuild {n} f")
+
+
+def test_rebuild_of_a_host_plan_and_failure(torch, oracle_mod):
+    """A host-built plan can be rebuilt on the device; a rebuild with a bad
+    position leaves the plan empty and refusing exchanges until the next
+    successful rebuild; geometry errors leave it unchanged."""
+    w = W.WORKLOADS[2]
+    pos = W.workload_positions(w)
+    hp = HaloPlan(pos, w.box, w.grid, w.cutoff)
+    hp.upload()
+    pos2 = W.positions(w.box, w.n_atoms, 77)
+    hp.rebuild_on_device(torch.from_numpy(pos2).cuda())
+    compare_plans(hp, oracle_mod.Oracle(pos2, w.box, w.grid, w.cutoff))
+    with pytest.raises(HaloError) as e:
+        hp.rebuild_on_device(torch.from_numpy(pos2).cuda(), (0.5, 6.0, 6.0))
+    assert e.value.code == -2
+    compare_plans(hp, oracle_mod.Oracle(pos2, w.box, w.grid, w.cutoff))
+    bad = pos2.copy()
+    bad[5, 1] = np.float32(7.0)
+    with pytest.raises(HaloError) as e:
+        hp.rebuild_on_device(torch.from_numpy(bad).cuda())
+    assert e.value.code == -3
+    assert hp.total_slots == 0
+    with pytest.raises(HaloError) as e:
+        hp.exchange_x(torch.zeros((0, 3), device="cuda"))
+    assert e.value.code == -6
+    hp.rebuild_on_device(torch.from_numpy(pos).cuda())
+    o = oracle_mod.Oracle(pos, w.box, w.grid, w.cutoff)
+    compare_plans(hp, o)
+    x0 = o.home_filled(np.nan)
+    xt = torch.from_numpy(x0.copy()).cuda()
+    hp.exchange_x(xt)
+    torch.cuda.synchronize()
+    hp.sync()
+    assert_bitwise(xt.cpu().numpy(), o.exchange_x(x0.copy()), "after a failed rebuild")
