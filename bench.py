@@ -164,8 +164,9 @@ def cold_exchange_us(torch, plan, x, f, f_init, suffix, reps):
 
 def plan_build_ms(torch, HaloPlan, w, pos, reps):
     """Wall time of building the plan on the host (halo_plan_create from host
-    positions, then the upload) and on the GPU (halo_plan_create_device from
-    device positions), median of reps, after one warm-up build each."""
+    positions, then the upload), on the GPU (halo_plan_create_device from
+    device positions) and of rebuilding a device plan in place
+    (halo_plan_rebuild_device), median of reps, after one warm-up each."""
     pos_d = torch.from_numpy(pos).cuda()
 
     def host():
@@ -190,6 +191,18 @@ def plan_build_ms(torch, HaloPlan, w, pos, reps):
             ts.append((time.perf_counter() - t0) * 1e3)
             p.close()
         out[name] = float(np.median(ts))
+    # rebuild in place (a repartitioning step: the plan keeps its device memory)
+    p = dev()
+    p.rebuild_on_device(pos_d)
+    ts = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        p.rebuild_on_device(pos_d)
+        torch.cuda.synchronize()
+        ts.append((time.perf_counter() - t0) * 1e3)
+    p.close()
+    out["device_rebuild_ms"] = float(np.median(ts))
     out["speedup"] = out["host_ms"] / out["device_ms"]
     out["reps"] = reps
     out["host_threads"] = min(os.cpu_count() or 1, 16)

@@ -305,21 +305,31 @@ static void xcd_order(std::vector<WorkItem> &items, size_t begin, int32_t n_dom)
 {
     constexpr int kXcds = 8;
     const size_t n = items.size() - begin;
-    std::vector<std::vector<WorkItem>> bucket(kXcds);
-    for (size_t i = begin; i < items.size(); ++i)
-        bucket[(items[i].seg % n_dom) % kXcds].push_back(items[i]);
-    std::vector<size_t> head(kXcds, 0);
+    if (n == 0) return;
+    // stable buckets by XCD (domain mod 8), as index lists over a copy
+    thread_local std::vector<WorkItem> copy;
+    thread_local std::vector<uint32_t> order;
+    copy.assign(items.begin() + (std::ptrdiff_t)begin, items.end());
+    order.resize(n);
+    size_t off[kXcds + 1] = {0}, head[kXcds], end[kXcds];
+    for (const WorkItem &it : copy) ++off[(it.seg % n_dom) % kXcds + 1];
+    for (int c = 0; c < kXcds; ++c) {
+        off[c + 1] += off[c];
+        head[c] = off[c];
+        end[c] = off[c];
+    }
+    for (size_t i = 0; i < n; ++i) order[end[(copy[i].seg % n_dom) % kXcds]++] = (uint32_t)i;
     for (size_t k = 0; k < n; ++k) {
         int want = (int)((begin + k) % kXcds);
-        if (head[want] == bucket[want].size()) {
+        if (head[want] == end[want]) {  // that XCD's bucket is empty: the fullest one
             size_t best = 0;
             for (int c = 0; c < kXcds; ++c)
-                if (bucket[c].size() - head[c] > best) {
-                    best = bucket[c].size() - head[c];
+                if (end[c] - head[c] > best) {
+                    best = end[c] - head[c];
                     want = c;
                 }
         }
-        items[begin + k] = bucket[want][head[want]++];
+        items[begin + k] = copy[order[head[want]++]];
     }
 }
 
@@ -407,6 +417,12 @@ void make_items(HostPlan &P, int32_t item_entries, bool with_masks)
 {
     P.item_entries = item_entries;
     P.items.clear();
+    {
+        size_t est = 0;
+        for (const Segment &sg : P.seg)
+            est += 2 + (size_t)(sg.send_size / std::max<int32_t>(item_entries, 1));
+        P.items.reserve(est);
+    }
     P.seg_items.assign(P.seg.size(), 0);
     P.pulse_item_off.assign(P.n_pulse + 1, 0);
     for (auto &s : P.seg) {
@@ -482,7 +498,11 @@ void finish_chunks(HostPlan &P, int32_t chunk_slots, const std::vector<Piece> &p
         }
     // Pieces come per domain in slot order (home, then the region of each
     // pulse); a chunk's rank[q] counts the bit-q slots of its domain before it.
-    std::vector<std::vector<Chunk>> by_zone(np + 1);
+    // Kept chunks are then placed zone-major (stable within a zone).
+    thread_local std::vector<Chunk> kept;
+    kept.clear();
+    kept.reserve(pieces.size());
+    std::vector<int32_t> zone_count(np + 2, 0);
     int32_t rank[kMaxMaskPulses] = {0};
     int32_t cur = -1;
     for (size_t i = 0; i < pieces.size(); ++i) {
@@ -495,36 +515,40 @@ void finish_chunks(HostPlan &P, int32_t chunk_slots, const std::vector<Piece> &p
             cur = pc.domain;
             for (int32_t q = 0; q < kMaxMaskPulses; ++q) rank[q] = 0;
         }
-        Chunk c{};
-        c.first = pc.first;
-        c.count = pc.count;
-        c.domain = pc.domain;
-        c.zone = pc.zone;
-        c.mask = stats[i].mask;
-        for (int32_t q = 0; q < kMaxMaskPulses; ++q) c.rank[q] = rank[q];
+        const uint32_t m = stats[i].mask;
+        if (m != 0) {  // else nothing to send from or add into
+            Chunk c{};
+            c.first = pc.first;
+            c.count = pc.count;
+            c.domain = pc.domain;
+            c.zone = pc.zone;
+            c.mask = m;
+            for (int32_t q = 0; q < kMaxMaskPulses; ++q) c.rank[q] = rank[q];
+            c.xwait = pc.zone < 0 ? -1 : pc.zone * nd + P.at(pc.zone, pc.domain).recv_from;
+            kept.push_back(c);
+            zone_count[pc.zone + 2] += 1;
+        }
         for (int32_t q = 0; q < np; ++q) rank[q] += stats[i].count[q];
-        c.xwait = pc.zone < 0 ? -1 : pc.zone * nd + P.at(pc.zone, pc.domain).recv_from;
-        if (c.mask == 0) continue;  // nothing to send from or add into
-        by_zone[pc.zone + 1].push_back(c);
     }
     if (cur >= 0)
         for (int32_t q = 0; q < np; ++q)
             if (rank[q] != P.at(q, cur).send_size) throw std::logic_error("mask ranks disagree");
-    P.chunks.clear();
-    P.chunk_forder.clear();
-    for (int32_t z = 0; z <= np; ++z)
-        for (const Chunk &c : by_zone[z]) {
-            P.chunks.push_back(c);
-            for (int32_t q = 0; q < np; ++q)
-                if ((c.mask >> q) & 1u) P.x_arrivals[(size_t)q * nd + c.domain] += 1;
-            if (c.zone >= 0) P.zone_chunks[(size_t)c.zone * nd + c.domain] += 1;
-        }
+    // zone_count[z + 1] = first chunk of zone z (z = -1 .. np-1)
+    for (int32_t z = 0; z <= np; ++z) zone_count[z + 1] += zone_count[z];
+    P.chunks.resize(kept.size());
+    std::vector<int32_t> fill(zone_count.begin(), zone_count.end() - 1);
+    for (const Chunk &c : kept) {
+        P.chunks[fill[c.zone + 1]++] = c;
+        for (int32_t q = 0; q < np; ++q)
+            if ((c.mask >> q) & 1u) P.x_arrivals[(size_t)q * nd + c.domain] += 1;
+        if (c.zone >= 0) P.zone_chunks[(size_t)c.zone * nd + c.domain] += 1;
+    }
     // Force direction: regions of later pulses first (their sums feed earlier
     // pulses), home slots last.
-    std::vector<int32_t> zone_off(np + 2, 0);
-    for (int32_t z = 0; z <= np; ++z) zone_off[z + 1] = zone_off[z] + (int32_t)by_zone[z].size();
+    P.chunk_forder.clear();
+    P.chunk_forder.reserve(kept.size());
     for (int32_t z = np; z >= 0; --z)
-        for (int32_t i = zone_off[z]; i < zone_off[z + 1]; ++i) P.chunk_forder.push_back(i);
+        for (int32_t i = zone_count[z]; i < zone_count[z + 1]; ++i) P.chunk_forder.push_back(i);
 }
 
 void make_chunks(HostPlan &P, int32_t chunk_slots)

@@ -13,10 +13,12 @@
 // The work that grows with the atoms and the entries runs in kernels:
 //   k_owner          domain of every atom, range check, per-tile histogram
 //   k_tile_scan      per domain, exclusive scan of the tile histogram
+//   k_home_start     first home slot of every domain; slot cursors
 //   k_home_scatter   stable counting sort: home atoms of every domain in
 //                    ascending id (wave-level key grouping, waves in order)
 //   k_select<false>  per (pulse, domain): how many candidates are sent, and
 //                    how many of them are home slots (depOffset split)
+//   k_pulse_scan     the pulse's map offsets and the receivers' regions
 //   k_select<true>   the same selection writing the indexMap (local slots)
 //                    and the id of every sent atom, by stable compaction
 //   k_abs_map        indexMap entries as absolute slots
@@ -24,10 +26,10 @@
 //   k_mask           per-slot pulse masks of the transposed form
 //   k_item_masks     wait masks of the work items
 //   k_piece_stats    union mask and per-pulse counts of every chunk candidate
-// and the host keeps the O(domains x pulses + items + chunks) bookkeeping:
-// prefix sums over domains, the receivers' region offsets, the layout, the
-// work items and the chunk order. The host reads back a few small tables
-// (one synchronisation per pulse, one for the layout, one for the chunks).
+// and the host keeps the O(domains x pulses + items + chunks) bookkeeping
+// that needs the sizes: the layout, the work items and the chunk order. The
+// host synchronises three times: after the pulses (sizes), after the chunk
+// statistics, and at the end.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -46,7 +48,10 @@ namespace halo {
 namespace {
 
 constexpr int kBT = 256;                 // threads per block
-constexpr int kTile = 2048;              // atoms per histogram tile (8 per thread)
+// Atoms per histogram tile: 512 (two per thread) while the tile histogram
+// (domains x tiles) stays below 16 M counters, else 2048.
+constexpr int kTileSmall = 512, kTileLarge = 2048;
+constexpr int64_t kMaxTileCounters = (int64_t)1 << 24;
 constexpr int32_t kMaxDeviceDomains = 8192;  // LDS histogram of 32 KiB
 
 struct Geom {
@@ -92,18 +97,19 @@ __device__ __forceinline__ uint64_t lanes_below(int lane)
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Position of the thread among the block's threads with flag set (thread
+// Position of the thread among the block's NT threads with flag set (thread
 // order); total receives their number.
+template <int NT>
 __device__ uint32_t block_rank(bool flag, uint32_t &total)
 {
-    __shared__ uint32_t wc[kBT / 64];
+    __shared__ uint32_t wc[NT / 64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const uint64_t b = __ballot(flag);
     if (lane == 0) wc[w] = (uint32_t)__popcll(b);
     __syncthreads();
     uint32_t off = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kBT / 64; ++i) {
+    for (int i = 0; i < NT / 64; ++i) {
         if (i < w) off += wc[i];
         tot += wc[i];
     }
@@ -114,6 +120,7 @@ __device__ uint32_t block_rank(bool flag, uint32_t &total)
 
 // Domain of every atom (0 for an atom out of range, whose smallest index goes
 // to *bad) and the tile's histogram over domains, stored domain-major.
+template <int kTile>
 __global__ __launch_bounds__(kBT) void k_owner(const float *__restrict__ pos, int64_t n_atoms,
                                                Geom g, int32_t n_dom, int32_t n_tiles,
                                                int32_t *__restrict__ owner,
@@ -164,17 +171,20 @@ __global__ __launch_bounds__(kBT) void k_tile_scan(uint32_t *__restrict__ tile_h
     if (threadIdx.x == 0) n_home[blockIdx.x] = (int32_t)carry;
 }
 
-// Stable counting sort of the atoms by domain. Block = tile; LDS counters
+// Stable counting sort of the atoms by domain, carrying their coordinates
+// (one array per dimension, home order). Block = tile; LDS counters
 // start at the tile's offsets within each domain. In each round of 256 atoms
 // a wave groups its lanes by domain (a lane's rank = lanes below it with the
 // same domain), then the waves add their group sizes to the counters one
 // after the other, so that lower ids get lower ranks.
+template <int kTile>
 __global__ __launch_bounds__(kBT) void k_home_scatter(const int32_t *__restrict__ owner,
                                                       int64_t n_atoms, int32_t n_dom,
                                                       int32_t n_tiles,
                                                       const uint32_t *__restrict__ tile_off,
                                                       const int32_t *__restrict__ home_start,
-                                                      int32_t *__restrict__ home_gid,
+                                                      const float *__restrict__ pos,
+                                                      float *__restrict__ home_c,
                                                       int32_t *__restrict__ home_rank)
 {
     extern __shared__ uint32_t cnt[];
@@ -182,10 +192,18 @@ __global__ __launch_bounds__(kBT) void k_home_scatter(const int32_t *__restrict_
         cnt[d] = tile_off[(size_t)d * n_tiles + blockIdx.x];
     __syncthreads();
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // all of the tile's domain ids are loaded up front
+    int32_t keys[kTile / kBT];
+#pragma unroll
+    for (int j = 0; j < kTile / kBT; ++j) {
+        const int64_t a = (int64_t)blockIdx.x * kTile + j * kBT + threadIdx.x;
+        keys[j] = a < n_atoms ? owner[a] : -1;
+    }
+#pragma unroll
     for (int j = 0; j < kTile / kBT; ++j) {
         const int64_t a = (int64_t)blockIdx.x * kTile + j * kBT + threadIdx.x;
         const bool valid = a < n_atoms;
-        const int32_t key = valid ? owner[a] : -1;
+        const int32_t key = keys[j];
         uint64_t todo = __ballot(valid);
         uint32_t my_rank = 0, grp = 0;
         int my_leader = 0;
@@ -212,7 +230,9 @@ __global__ __launch_bounds__(kBT) void k_home_scatter(const int32_t *__restrict_
         base = (uint32_t)__shfl((int)base, my_leader, 64);
         if (valid) {
             const uint32_t r = base + my_rank;
-            home_gid[home_start[key] + (int32_t)r] = (int32_t)a;
+            const int64_t h = home_start[key] + (int64_t)r;
+#pragma unroll
+            for (int d = 0; d < 3; ++d) home_c[d * n_atoms + h] = pos[3 * a + d];
             home_rank[a] = (int32_t)r;
         }
     }
@@ -237,16 +257,53 @@ struct SegTable {
 // atom's original position lies less than reach above the receiver's upper
 // face. WRITE == false: store the send count and how many candidates were
 // home slots; WRITE == true: store the indexMap (local slots) and the sent
-// atoms' ids from map_off on, in candidate order.
+// atoms' coordinates (entry_c, one row of `cap` per dimension) from map_off
+// on, in candidate order.
+constexpr int kSelectThreads = 1024;  // one block per domain: 16 waves
+
 template <bool WRITE>
-__global__ __launch_bounds__(kBT) void k_select(
-    const float *__restrict__ pos, int32_t p, int32_t dim, int32_t k, int32_t n_dom, Geom g,
+__global__ __launch_bounds__(kSelectThreads) void k_select(
+    int32_t p, int32_t dim, int32_t k, int32_t n_dom, Geom g,
     double reach, const int32_t *__restrict__ send_to, const int32_t *__restrict__ recv_from,
     const int32_t *__restrict__ n_home, const int32_t *__restrict__ home_start,
-    const int32_t *__restrict__ home_gid, SegTable seg, const int32_t *entry_gid,
-    int32_t *__restrict__ local_map, int32_t *gid_out)
+    const float *__restrict__ home_c, int64_t n_atoms, SegTable seg, float *entry_c,
+    int32_t *__restrict__ local_map, int32_t cap)
 {
+    constexpr int NT = kSelectThreads;
+    constexpr int kRows = 4;  // rows of NT candidates whose loads go out together
+    // The candidate zones in slot order ([home,] regions), laid end to end:
+    // candidate i of the domain is entry i - zbeg[z] of zone z.
+    __shared__ int32_t zbeg[kMaxPulses + 2], zslot[kMaxPulses + 1], zoff[kMaxPulses + 1];
+    __shared__ uint32_t dep_lds;
     const int32_t D = blockIdx.x;
+    const int32_t zfirst = k == 0 ? -1 : p - 1;
+    const int32_t nz = p - zfirst;
+    if (threadIdx.x == 0) {
+        int32_t acc = 0;
+        for (int32_t j = 0; j < nz; ++j) {
+            const int32_t z = zfirst + j;
+            int32_t len;
+            if (z < 0) {
+                len = n_home[D];
+                zslot[j] = 0;
+                zoff[j] = home_start[D];
+            } else {
+                const int32_t S = recv_from[z * n_dom + D];
+                len = seg.row(z, kRecvSize)[D];
+                zslot[j] = seg.row(z, kAtomOffset)[D];
+                zoff[j] = seg.row(z, kMapOff)[S];
+                // an earlier pulse overflowed the entry arrays: the host
+                // rebuilds with more room; read nothing past them meanwhile
+                if (zoff[j] > cap - len) len = 0;
+            }
+            zbeg[j] = acc;
+            acc += len;
+        }
+        zbeg[nz] = acc;
+        dep_lds = 0;
+    }
+    __syncthreads();
+    const int32_t total = zbeg[nz];
     const int32_t R = send_to[p * n_dom + D];
     int32_t c_r;  // receiver's cell index along dim
     if (dim == 0)
@@ -259,45 +316,118 @@ __global__ __launch_bounds__(kBT) void k_select(
     const double ncell = (double)g.grid[dim];
     const int32_t out0 = WRITE ? seg.row(p, kMapOff)[D] : 0;
     const int32_t limit = WRITE ? seg.row(p, kSendSize)[D] : 0;
-    uint32_t count = 0, dep = 0;
-    const int32_t zfirst = k == 0 ? -1 : p - 1;
-    for (int32_t z = zfirst; z < p; ++z) {
-        int32_t len, slot0;
-        const int32_t *gids;
-        if (z < 0) {
-            len = n_home[D];
-            slot0 = 0;
-            gids = home_gid + home_start[D];
-        } else {
-            const int32_t S = recv_from[z * n_dom + D];
-            len = seg.row(z, kRecvSize)[D];
-            slot0 = seg.row(z, kAtomOffset)[D];
-            gids = entry_gid + seg.row(z, kMapOff)[S];
+    const bool home_first = zfirst < 0;
+    uint32_t count = 0;
+    for (int32_t b = 0; b < total; b += kRows * NT) {
+        // candidate coordinates come from per-dimension arrays in slot order
+        // (home order, or the order the entries were sent in): contiguous
+        const float *src[kRows];
+        int32_t slot[kRows];
+        int64_t stride[kRows];
+        float v[kRows];
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) {
+            const int32_t i = b + j * NT + (int32_t)threadIdx.x;
+            src[j] = nullptr;
+            slot[j] = 0;
+            stride[j] = 0;
+            if (i < total) {
+                int32_t z = 0;
+                while (i >= zbeg[z + 1]) ++z;
+                const int32_t e = i - zbeg[z];
+                const bool from_home = home_first && z == 0;
+                src[j] = (from_home ? home_c : entry_c) + zoff[z] + e;
+                stride[j] = from_home ? n_atoms : (int64_t)cap;
+                slot[j] = zslot[z] + e;
+            }
         }
-        for (int32_t b = 0; b < len; b += kBT) {
-            const int32_t i = b + (int32_t)threadIdx.x;
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) v[j] = src[j] ? src[j][dim * stride[j]] : 0.f;
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) {
             bool flag = false;
-            int32_t gid = 0;
-            if (i < len) {
-                gid = gids[i];
-                double above = scaled(pos[3 * (int64_t)gid + dim], g.width[dim], g.top[dim]) - face;
+            if (src[j]) {
+                double above = scaled(v[j], g.width[dim], g.top[dim]) - face;
                 if (above < 0.0) above += ncell;
                 flag = above < reach;
             }
+            if (!WRITE) {
+                // sends from home slots (the depOffset split)
+                const bool home = home_first && b + j * NT + (int32_t)threadIdx.x < zbeg[1];
+                const uint64_t hb = __ballot(flag && home);
+                if ((threadIdx.x & 63) == 0 && hb) atomicAdd(&dep_lds, (uint32_t)__popcll(hb));
+            }
             uint32_t tot;
-            const uint32_t r = block_rank(flag, tot);
-            if (WRITE && flag && (int32_t)(count + r) < limit) {
-                local_map[out0 + (int32_t)(count + r)] = slot0 + i;
-                gid_out[out0 + (int32_t)(count + r)] = gid;
+            const uint32_t r = block_rank<NT>(flag, tot);
+            if (WRITE && flag && (int32_t)(count + r) < limit &&
+                out0 + (int32_t)(count + r) < cap) {
+                const int32_t o = out0 + (int32_t)(count + r);
+                local_map[o] = slot[j];
+#pragma unroll
+                for (int d = 0; d < 3; ++d) entry_c[d * (int64_t)cap + o] = src[j][d * stride[j]];
             }
             count += tot;
-            if (z < 0) dep += tot;
         }
     }
-    if (!WRITE && threadIdx.x == 0) {
-        seg.row(p, kSendSize)[D] = (int32_t)count;
-        seg.row(p, kDepStart)[D] = (int32_t)dep;
+    if (!WRITE) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            seg.row(p, kSendSize)[D] = (int32_t)count;
+            seg.row(p, kDepStart)[D] = (int32_t)dep_lds;
+        }
     }
+}
+
+// One block: home_start = exclusive scan of the home counts; every domain's
+// slot cursor starts at its home count; no entries yet.
+__global__ __launch_bounds__(kBT) void k_home_start(const int32_t *__restrict__ n_home,
+                                                    int32_t nd, int32_t *__restrict__ home_start,
+                                                    int32_t *__restrict__ cur,
+                                                    int32_t *__restrict__ count)
+{
+    uint32_t carry = 0;
+    for (int32_t b = 0; b < nd; b += kBT) {
+        const int32_t d = b + (int32_t)threadIdx.x;
+        const uint32_t v = d < nd ? (uint32_t)n_home[d] : 0u;
+        uint32_t tot;
+        const uint32_t ex = block_scan_excl(v, tot);
+        if (d < nd) {
+            home_start[d] = (int32_t)(carry + ex);
+            cur[d] = (int32_t)v;
+        }
+        carry += tot;
+    }
+    if (threadIdx.x == 0) count[0] = 0;
+}
+
+// One block, between the two selection passes of pulse p: the map offsets of
+// the pulse's segments (pulse-major, then domain, after all earlier entries),
+// and every receiver's region: recvSize = its sender's count, atomOffset =
+// the receiver's slot count so far (each domain receives from exactly one
+// sender per pulse, so the cursor updates do not collide).
+__global__ __launch_bounds__(kBT) void k_pulse_scan(SegTable seg, int32_t p, int32_t nd,
+                                                    const int32_t *__restrict__ send_to,
+                                                    int32_t *__restrict__ cur,
+                                                    int32_t *__restrict__ count)
+{
+    const int32_t base = count[0];
+    uint32_t carry = 0;
+    for (int32_t b = 0; b < nd; b += kBT) {
+        const int32_t D = b + (int32_t)threadIdx.x;
+        const uint32_t v = D < nd ? (uint32_t)seg.row(p, kSendSize)[D] : 0u;
+        uint32_t tot;
+        const uint32_t ex = block_scan_excl(v, tot);
+        if (D < nd) {
+            seg.row(p, kMapOff)[D] = base + (int32_t)(carry + ex);
+            const int32_t R = send_to[p * nd + D];
+            seg.row(p, kRecvSize)[R] = (int32_t)v;
+            seg.row(p, kAtomOffset)[R] = cur[R];
+            cur[R] += (int32_t)v;
+        }
+        carry += tot;
+    }
+    __syncthreads();  // every thread has read count[0]
+    if (threadIdx.x == 0) count[0] = base + (int32_t)carry;
 }
 
 // Block = segment (pulse-major): absolute slots of its indexMap entries.
@@ -467,27 +597,36 @@ hipError_t pinned_reserve(DeviceBuild &B, size_t bytes)
     return e;
 }
 
-// The entries arena holds the local-slot indexMap and the sent atoms' ids,
-// `cap` entries each; grown (keeping the first `used` entries) when a pulse
-// needs more.
-hipError_t entries_reserve(DeviceBuild &B, size_t need, size_t used, hipStream_t st)
+// The entries arena holds the local-slot indexMap and the sent atoms'
+// coordinates (three rows), `cap` entries each; its contents are not kept
+// when it grows (the pulses then run again).
+hipError_t entries_reserve(DeviceBuild &B, size_t need)
 {
     if (need <= B.entry_cap && B.entries.base) return hipSuccess;
-    Arena old = B.entries;
-    const size_t old_cap = B.entry_cap;
-    B.entries = Arena();
+    const size_t cap = std::max<size_t>(need, B.entry_cap * 2);
     B.entry_cap = 0;
-    const size_t cap = std::max<size_t>(need, old_cap * 2);
-    hipError_t e = arena_reserve(B.entries, 2 * aligned(cap * 4));
-    if (e == hipSuccess && used > 0) {
-        e = hipMemcpyAsync(B.entries.base, old.base, used * 4, hipMemcpyDeviceToDevice, st);
-        if (e == hipSuccess)
-            e = hipMemcpyAsync(B.entries.base + aligned(cap * 4), old.base + aligned(old_cap * 4),
-                               used * 4, hipMemcpyDeviceToDevice, st);
-        if (e == hipSuccess) e = hipStreamSynchronize(st);
-    }
-    arena_free(old);
+    hipError_t e = arena_reserve(B.entries, aligned(cap * 4) + 3 * cap * 4);
     if (e == hipSuccess) B.entry_cap = cap;
+    return e;
+}
+
+// Wait for the work queued on `st` so far. The runtime's stream wait can
+// sleep and take far longer to return than the GPU takes to finish short
+// work; the build waits often for little, so it records an event and polls
+// it instead.
+hipError_t wait_stream(DeviceBuild &B, hipStream_t st)
+{
+    hipError_t e;
+    if (!B.done) {
+        e = hipEventCreateWithFlags(&B.done, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            B.done = nullptr;
+            return e;
+        }
+    }
+    if ((e = hipEventRecord(B.done, st)) != hipSuccess) return e;
+    while ((e = hipEventQuery(B.done)) == hipErrorNotReady) {
+    }
     return e;
 }
 
@@ -499,6 +638,7 @@ void free_device_build(halo_plan *pl)
     DeviceBuild &B = *pl->dev;
     for (Arena *a : {&B.work, &B.entries, &B.maps, &B.pieces, &B.tables}) arena_free(*a);
     if (B.pinned) (void)hipHostFree(B.pinned);
+    if (B.done) (void)hipEventDestroy(B.done);
     delete pl->dev;
     pl->dev = nullptr;
     // these pointed into the arenas
@@ -555,20 +695,28 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     } while (0)
 
     // -- build temporaries in one arena ------------------------------------------
+    const bool small_tiles =
+        (int64_t)nd * ((n_atoms + kTileSmall - 1) / kTileSmall) <= kMaxTileCounters;
+    const int kTile = small_tiles ? kTileSmall : kTileLarge;
     const int32_t n_tiles = (int32_t)std::max<int64_t>(1, (n_atoms + kTile - 1) / kTile);
     const size_t N = (size_t)n_atoms;
-    HALO_TRY(arena_reserve(B.work, 3 * aligned(std::max<size_t>(N, 1) * 4) +
-                                       aligned((size_t)nd * n_tiles * 4) + aligned(8 + 4 * nd) +
+    // summary read back once: first bad atom, entry count, home counts, cursors
+    const size_t xfer_bytes = 16 + 8 * (size_t)nd;
+    HALO_TRY(arena_reserve(B.work, 2 * aligned(std::max<size_t>(N, 1) * 4) +
+                                       aligned(std::max<size_t>(N, 1) * 12) +
+                                       aligned((size_t)nd * n_tiles * 4) + aligned(xfer_bytes) +
                                        aligned(4 * nd) + aligned(std::max<size_t>(nseg, 1) * 20) +
                                        aligned(std::max<size_t>(nseg, 1) * 8) + aligned(8 * nd)),
              "device memory");
     int32_t *owner = arena_take<int32_t>(B.work, N);
     int32_t *home_rank = arena_take<int32_t>(B.work, N);
-    int32_t *home_gid = arena_take<int32_t>(B.work, N);
+    float *home_c = arena_take<float>(B.work, 3 * N);  // home coordinates, per dimension
     uint32_t *tile_hist = arena_take<uint32_t>(B.work, (size_t)nd * n_tiles);
-    char *xfer = arena_take<char>(B.work, 8 + 4 * (size_t)nd);  // first bad atom, home counts
+    char *xfer = arena_take<char>(B.work, xfer_bytes);
     unsigned long long *bad = (unsigned long long *)xfer;
-    int32_t *d_n_home = (int32_t *)(xfer + 8);
+    int32_t *d_count = (int32_t *)(xfer + 8);
+    int32_t *d_n_home = (int32_t *)(xfer + 16);
+    int32_t *d_cur = d_n_home + nd;
     int32_t *d_home_start = arena_take<int32_t>(B.work, nd);
     SegTable sg{arena_take<int32_t>(B.work, nseg * kSegRows), nd};
     int32_t *w_send_to = arena_take<int32_t>(B.work, 2 * nseg);
@@ -576,8 +724,8 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     int64_t *d_base = arena_take<int64_t>(B.work, nd);
 
     // host staging: fixed part of the build
-    const size_t h_down0 = 0, h_start = aligned(8 + 4 * nd), h_pdown = h_start + aligned(4 * nd),
-                 h_pup = h_pdown + aligned(8 * (size_t)nd), h_tab = h_pup + aligned(12 * (size_t)nd),
+    const size_t h_sum = 0, h_seg = aligned(xfer_bytes),
+                 h_tab = h_seg + aligned(std::max<size_t>(nseg, 1) * 20),
                  h_base = h_tab + aligned(8 * std::max<size_t>(nseg, 1)),
                  h_fixed = h_base + aligned(8 * (size_t)nd);
     HALO_TRY(pinned_reserve(B, h_fixed), "pinned host memory");
@@ -591,105 +739,117 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     // -- domains and home order ------------------------------------------------
     HALO_TRY(hipMemsetAsync(bad, 0xff, 8, st), "hipMemsetAsync");
     const size_t lds = (size_t)nd * sizeof(uint32_t);
-    if (n_atoms > 0)
-        k_owner<<<n_tiles, kBT, lds, st>>>(pos, n_atoms, g, nd, n_tiles, owner, tile_hist, bad);
+    if (n_atoms > 0 && small_tiles)
+        k_owner<kTileSmall>
+            <<<n_tiles, kBT, lds, st>>>(pos, n_atoms, g, nd, n_tiles, owner, tile_hist, bad);
+    else if (n_atoms > 0)
+        k_owner<kTileLarge>
+            <<<n_tiles, kBT, lds, st>>>(pos, n_atoms, g, nd, n_tiles, owner, tile_hist, bad);
     else
         HALO_TRY(hipMemsetAsync(tile_hist, 0, (size_t)nd * n_tiles * 4, st), "hipMemsetAsync");
     k_tile_scan<<<nd, kBT, 0, st>>>(tile_hist, n_tiles, d_n_home);
+    k_home_start<<<1, kBT, 0, st>>>(d_n_home, nd, d_home_start, d_cur, d_count);
+    if (n_atoms > 0 && small_tiles)
+        k_home_scatter<kTileSmall><<<n_tiles, kBT, lds, st>>>(owner, n_atoms, nd, n_tiles,
+                                                              tile_hist, d_home_start, pos,
+                                                              home_c, home_rank);
+    else if (n_atoms > 0)
+        k_home_scatter<kTileLarge><<<n_tiles, kBT, lds, st>>>(owner, n_atoms, nd, n_tiles,
+                                                              tile_hist, d_home_start, pos,
+                                                              home_c, home_rank);
     HALO_TRY(hipGetLastError(), "launch");
-    HALO_TRY(hipMemcpyAsync(hp + h_down0, xfer, 8 + 4 * (size_t)nd, hipMemcpyDeviceToHost, st),
-             "hipMemcpyAsync");
-    HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
-    unsigned long long first_bad;
-    std::memcpy(&first_bad, hp + h_down0, 8);
-    if (first_bad != ~0ull) {
-        msg = "halo_plan_create: atom " + std::to_string(first_bad) +
-              " lies outside [0, L) or is not finite";
-        return kErrRange;
+
+    // -- pulses, all on the device; one read-back at the end -------------------------
+    // Room for the entries: what the previous build used, else the halo
+    // volume expected at uniform density, with a margin. If a pulse does not
+    // fit, the pulses run again with the count that came back.
+    size_t want = std::max<size_t>(1024, 2 * N);
+    {
+        double vol = 1.0;
+        for (int d = 0; d < 3; ++d)
+            if (grid[d] > 1) vol *= 1.0 + P.reach[d];
+        want = std::max(want, (size_t)((vol - 1.0) * 1.25 * (double)N) + 1024);
+    }
+    HALO_TRY(entries_reserve(B, want), "device memory");
+    int64_t entries = 0;
+    for (int attempt = 0;; ++attempt) {
+        const int32_t cap = (int32_t)std::min<size_t>(B.entry_cap, (size_t)INT32_MAX);
+        int32_t *lmap = (int32_t *)B.entries.base;
+        float *ecoord = (float *)(B.entries.base + aligned(B.entry_cap * 4));
+        if (attempt > 0) k_home_start<<<1, kBT, 0, st>>>(d_n_home, nd, d_home_start, d_cur, d_count);
+        for (int32_t p = 0; p < np; ++p) {
+            const int dim = P.pulse_dim[p];
+            const int32_t k = P.pulse_k[p];
+            k_select<false><<<nd, kSelectThreads, 0, st>>>(p, dim, k, nd, g, P.reach[dim], w_send_to,
+                                                w_recv_from, d_n_home, d_home_start, home_c,
+                                                n_atoms, sg, ecoord, lmap, cap);
+            k_pulse_scan<<<1, kBT, 0, st>>>(sg, p, nd, w_send_to, d_cur, d_count);
+            k_select<true><<<nd, kSelectThreads, 0, st>>>(p, dim, k, nd, g, P.reach[dim], w_send_to,
+                                               w_recv_from, d_n_home, d_home_start, home_c,
+                                               n_atoms, sg, ecoord, lmap, cap);
+        }
+        HALO_TRY(hipGetLastError(), "launch");
+        HALO_TRY(hipMemcpyAsync(hp + h_sum, xfer, xfer_bytes, hipMemcpyDeviceToHost, st),
+                 "hipMemcpyAsync");
+        if (nseg > 0)
+            HALO_TRY(hipMemcpyAsync(hp + h_seg, sg.t, nseg * kSegRows * 4, hipMemcpyDeviceToHost,
+                                    st), "hipMemcpyAsync");
+        HALO_TRY(wait_stream(B, st), "waiting for the stream");
+        unsigned long long first_bad;
+        std::memcpy(&first_bad, hp + h_sum, 8);
+        if (first_bad != ~0ull) {
+            msg = "halo_plan_create: atom " + std::to_string(first_bad) +
+                  " lies outside [0, L) or is not finite";
+            return kErrRange;
+        }
+        int32_t count;
+        std::memcpy(&count, hp + h_sum + 8, 4);
+        entries = (uint32_t)count;
+        if (entries > kMaxSlots) {
+            msg = "halo_plan_create_device: too many halo entries for one plan";
+            return kErrRange;
+        }
+        if ((size_t)entries <= B.entry_cap) break;
+        if (attempt > 0) {
+            msg = "halo_plan_create_device: internal error: entry count not stable";
+            return kErrArg;
+        }
+        HALO_TRY(entries_reserve(B, (size_t)entries), "device memory");
     }
     P.n_home.assign(nd, 0);
-    std::memcpy(P.n_home.data(), hp + h_down0 + 8, 4 * (size_t)nd);
+    std::memcpy(P.n_home.data(), hp + h_sum + 16, 4 * (size_t)nd);
+    std::vector<int32_t> cur(nd);
+    std::memcpy(cur.data(), hp + h_sum + 16 + 4 * (size_t)nd, 4 * (size_t)nd);
     {
-        int32_t *hs = (int32_t *)(hp + h_start);
         int64_t acc = 0;
-        for (int32_t d = 0; d < nd; ++d) {
-            hs[d] = (int32_t)acc;
-            acc += P.n_home[d];
-        }
+        for (int32_t d = 0; d < nd; ++d) acc += P.n_home[d];
         if (acc != n_atoms) {
             msg = "halo_plan_create_device: internal error: home counts do not add up";
             return kErrArg;
         }
     }
-    HALO_TRY(hipMemcpyAsync(d_home_start, hp + h_start, 4 * (size_t)nd, hipMemcpyHostToDevice, st),
-             "hipMemcpyAsync");
-    if (n_atoms > 0)
-        k_home_scatter<<<n_tiles, kBT, lds, st>>>(owner, n_atoms, nd, n_tiles, tile_hist,
-                                                  d_home_start, home_gid, home_rank);
-    HALO_TRY(hipGetLastError(), "launch");
-
-    // -- pulses -------------------------------------------------------------------
     P.seg.assign(nseg, Segment());
-    HALO_TRY(entries_reserve(B, std::max<size_t>(1024, 2 * N), 0, st), "device memory");
-    std::vector<int32_t> cur(P.n_home.begin(), P.n_home.end());
-    int64_t entries = 0;
-    for (int32_t p = 0; p < np; ++p) {
-        const int dim = P.pulse_dim[p];
-        const int32_t k = P.pulse_k[p];
-        const size_t r0 = (size_t)p * nd;
-        int32_t *lmap = (int32_t *)B.entries.base;
-        int32_t *egid = (int32_t *)(B.entries.base + aligned(B.entry_cap * 4));
-        k_select<false><<<nd, kBT, 0, st>>>(pos, p, dim, k, nd, g, P.reach[dim], w_send_to,
-                                            w_recv_from, d_n_home, d_home_start, home_gid, sg,
-                                            egid, lmap, egid);
-        HALO_TRY(hipGetLastError(), "launch");
-        // send counts and home-slot counts of this pulse: two adjacent rows
-        HALO_TRY(hipMemcpyAsync(hp + h_pdown, sg.row(p, kSendSize), 8 * (size_t)nd,
-                                hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
-        HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
-        const int32_t *send_size = (const int32_t *)(hp + h_pdown);
-        const int32_t *dep_start = send_size + nd;
-        int32_t *up = (int32_t *)(hp + h_pup);  // recvSize, atomOffset, map offset rows
-        const int64_t entries_before = entries;
-        for (int32_t D = 0; D < nd; ++D) {
-            Segment &s = P.seg[r0 + D];
-            s.send_to = P.send_to[r0 + D];
-            s.send_size = send_size[D];
-            s.dep_start = dep_start[D];
-            s.map_off = entries;
-            up[2 * nd + D] = (int32_t)entries;
-            entries += send_size[D];
-            const int32_t cd = dim == 0   ? D % grid[0]
-                               : dim == 1 ? (D / grid[0]) % grid[1]
-                                          : D / (grid[0] * grid[1]);
-            s.shift[0] = s.shift[1] = s.shift[2] = 0.f;
-            if (cd == 0) s.shift[dim] = box[dim];
+    {
+        const int32_t *t = (const int32_t *)(hp + h_seg);
+        for (int32_t p = 0; p < np; ++p) {
+            const int dim = P.pulse_dim[p];
+            const int32_t *row = t + (size_t)p * kSegRows * nd;
+            for (int32_t D = 0; D < nd; ++D) {
+                Segment &s = P.seg[(size_t)p * nd + D];
+                s.send_to = P.send_to[(size_t)p * nd + D];
+                s.recv_from = P.recv_from[(size_t)p * nd + D];
+                s.send_size = row[kSendSize * nd + D];
+                s.dep_start = row[kDepStart * nd + D];
+                s.recv_size = row[kRecvSize * nd + D];
+                s.atom_offset = row[kAtomOffset * nd + D];
+                s.map_off = row[kMapOff * nd + D];
+                const int32_t cd = dim == 0   ? D % grid[0]
+                                   : dim == 1 ? (D / grid[0]) % grid[1]
+                                              : D / (grid[0] * grid[1]);
+                s.shift[0] = s.shift[1] = s.shift[2] = 0.f;
+                if (cd == 0) s.shift[dim] = box[dim];
+            }
         }
-        if (entries > kMaxSlots) {
-            msg = "halo_plan_create_device: too many halo entries for one plan";
-            return kErrRange;
-        }
-        for (int32_t D = 0; D < nd; ++D) {
-            const int32_t R = P.send_to[r0 + D];
-            Segment &r = P.seg[r0 + R];
-            r.recv_from = D;
-            r.recv_size = send_size[D];
-            r.atom_offset = cur[R];
-            cur[R] += send_size[D];
-        }
-        for (int32_t D = 0; D < nd; ++D) {
-            up[D] = P.seg[r0 + D].recv_size;
-            up[nd + D] = P.seg[r0 + D].atom_offset;
-        }
-        HALO_TRY(hipMemcpyAsync(sg.row(p, kRecvSize), up, 12 * (size_t)nd, hipMemcpyHostToDevice,
-                                st), "hipMemcpyAsync");
-        HALO_TRY(entries_reserve(B, (size_t)entries, (size_t)entries_before, st), "device memory");
-        lmap = (int32_t *)B.entries.base;
-        egid = (int32_t *)(B.entries.base + aligned(B.entry_cap * 4));
-        k_select<true><<<nd, kBT, 0, st>>>(pos, p, dim, k, nd, g, P.reach[dim], w_send_to,
-                                           w_recv_from, d_n_home, d_home_start, home_gid, sg,
-                                           egid, lmap, egid);
-        HALO_TRY(hipGetLastError(), "launch");
     }
     int32_t *local_map = (int32_t *)B.entries.base;
 
@@ -728,7 +888,7 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
                  h_tables = h_stats + aligned(std::max<size_t>(npc, 1) * sizeof(PieceStats)),
                  h_total = h_tables + tab_bytes;
     if (h_total > B.pinned_cap) {
-        HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");  // no copy from it in flight
+        HALO_TRY(wait_stream(B, st), "waiting for the stream");  // no copy from it in flight
         char *keep = (char *)std::malloc(h_fixed);
         if (!keep) {
             msg = "halo_plan_create_device: out of host memory";
@@ -781,7 +941,7 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
             HALO_TRY(hipMemcpyAsync(hp + h_stats, d_stats, npc * sizeof(PieceStats),
                                     hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
         }
-        HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
+        HALO_TRY(wait_stream(B, st), "waiting for the stream");
         std::memcpy(stats.data(), hp + h_stats, npc * sizeof(PieceStats));
         try {
             finish_chunks(P, item_entries, pieces, stats);
@@ -843,7 +1003,7 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         HALO_TRY(hipHostMalloc((void **)&pl->h_err, 64, hipHostMallocMapped), "pinned memory");
         HALO_TRY(hipHostGetDevicePointer((void **)&pl->d_err, pl->h_err, 0), "pinned memory");
     }
-    HALO_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
+    HALO_TRY(wait_stream(B, st), "waiting for the stream");
     std::memset(pl->h_err, 0, 64);
     HALO_TRY(hipGetDevice(&pl->device), "hipGetDevice");
 

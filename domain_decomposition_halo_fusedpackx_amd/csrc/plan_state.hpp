@@ -29,6 +29,7 @@ struct DeviceBuild {
     Arena tables;             // work items, segment tables, chunks
     char *pinned = nullptr;   // host staging for the small copies
     size_t pinned_cap = 0;
+    hipEvent_t done = nullptr;  // polled for the build's waits
 };
 
 }  // namespace halo
