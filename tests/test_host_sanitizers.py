@@ -1,0 +1,37 @@
+"""Host code under AddressSanitizer and UndefinedBehaviorSanitizer (CPU).
+
+The library's host plan builder (plan.cpp) and the serial C oracle are built
+with -fsanitize=address,undefined into one driver (tests/native), which runs
+them on small boxes and compares their PulseData. Any out-of-bounds access,
+leak or undefined behaviour aborts the driver; GPU code is not involved.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "domain_decomposition_halo_fusedpackx_amd", "csrc")
+SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+       "-g", "-O1"]
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or shutil.which("gcc") is None,
+                    reason="no host compiler")
+def test_plan_builder_and_oracle_under_sanitizers(tmp_path):
+    d = str(tmp_path)
+    subprocess.check_call(["gcc", *SAN, "-std=c99", "-ffp-contract=off", "-c",
+                           os.path.join(ROOT, "oracle", "halo_oracle.c"),
+                           "-o", os.path.join(d, "oracle.o")])
+    subprocess.check_call(["g++", *SAN, "-std=c++17", "-ffp-contract=off", "-pthread",
+                           "-I", CSRC, os.path.join(ROOT, "tests", "native", "sanitize_driver.cpp"),
+                           os.path.join(CSRC, "plan.cpp"), os.path.join(d, "oracle.o"),
+                           "-o", os.path.join(d, "driver"), "-lm"])
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    env.pop("LD_PRELOAD", None)
+    r = subprocess.run([os.path.join(d, "driver")], capture_output=True, text=True, env=env,
+                       timeout=300)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert "0 case(s) differ" in r.stdout
