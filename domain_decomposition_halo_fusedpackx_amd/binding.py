@@ -55,6 +55,7 @@ SIGNATURES = {
     "halo_plan_reset": (_st, [_vp]),
     "halo_plan_set_spin_limit": (_st, [_vp, _u32]),
     "halo_plan_debug_withhold": (_st, [_vp, _i32]),
+    "halo_plan_debug_stress": (_st, [_vp, _u32]),
 }
 
 _lib = None
@@ -319,6 +320,9 @@ class HaloPlan:
 
     def debug_withhold(self, segment: int):
         _check(load_library().halo_plan_debug_withhold(self._h, segment))
+
+    def debug_stress(self, seed: int):
+        _check(load_library().halo_plan_debug_stress(self._h, seed))
 
     # -- inputs in this layout ----------------------------------------------------
     def home_filled(self, positions, fill=float("nan")) -> np.ndarray:

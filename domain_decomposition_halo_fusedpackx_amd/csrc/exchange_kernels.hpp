@@ -30,6 +30,25 @@
 
 constexpr int kThreads = 256;  // 4 waves of 64 per workgroup
 
+// Testing mode for the fused kernels (halo_plan_debug_stress): workgroup b
+// takes work unit order[b] instead of its usual one (the host reverses the
+// order inside every group of mutually independent units), and every unit
+// first sleeps a pseudo-random while. Results must not change. order ==
+// nullptr and seed == 0 in normal runs.
+struct Stress {
+    const int32_t *order;
+    uint32_t seed;
+};
+
+__device__ __forceinline__ void stress_delay(uint32_t seed, uint32_t unit)
+{
+    uint32_t h = (unit + 1u) * 0x9E3779B1u ^ seed;
+    h ^= h >> 15;
+    h *= 0x85EBCA77u;
+    h ^= h >> 13;
+    for (uint32_t i = 0; i < (h & 31u); ++i) __builtin_amdgcn_s_sleep(127);
+}
+
 // ---- buffer addressing ----------------------------------------------------
 // x, f and the indexMap are read and written through buffer descriptors: one
 // 12-byte float triple per buffer_load/store_dwordx3, 32-bit byte offsets, and
@@ -319,11 +338,12 @@ __global__ __launch_bounds__(kThreads) void k_pack_fused(
     float *x, uint32_t x_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
     const WorkItem *__restrict__ items, const int32_t *__restrict__ recv_from,
     const uint32_t *__restrict__ seg_items, uint32_t *state, int32_t n_dom, uint32_t epoch,
-    uint32_t spin_limit, uint32_t *err_word, int32_t withhold)
+    uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Stress st)
 {
-    pack_item_fused<EPT>(items + blockIdx.x, make_rsrc(x, x_bytes), make_rsrc(idx, idx_bytes),
-                         recv_from, seg_items, state, n_dom, epoch, spin_limit, err_word,
-                         withhold);
+    const uint32_t u = st.order ? (uint32_t)st.order[blockIdx.x] : blockIdx.x;
+    if (st.seed) stress_delay(st.seed, u);
+    pack_item_fused<EPT>(items + u, make_rsrc(x, x_bytes), make_rsrc(idx, idx_bytes), recv_from,
+                         seg_items, state, n_dom, epoch, spin_limit, err_word, withhold);
 }
 
 // Fused force exchange: ONE launch, workgroup b takes item n_items-1-b, so
@@ -333,11 +353,12 @@ __global__ __launch_bounds__(kThreads) void k_unpack_fused(
     float *f, uint32_t f_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
     const WorkItem *__restrict__ items, const uint32_t *__restrict__ seg_items, uint32_t *state,
     int32_t n_seg, uint32_t n_items, uint32_t epoch, uint32_t spin_limit, uint32_t *err_word,
-    int32_t withhold)
+    int32_t withhold, Stress st)
 {
-    unpack_item_fused<EPT>(items + (n_items - 1u - blockIdx.x), make_rsrc(f, f_bytes),
-                           make_rsrc(idx, idx_bytes), seg_items, state, n_seg, epoch, spin_limit,
-                           err_word, withhold);
+    const uint32_t u = st.order ? (uint32_t)st.order[blockIdx.x] : n_items - 1u - blockIdx.x;
+    if (st.seed) stress_delay(st.seed, u);
+    unpack_item_fused<EPT>(items + u, make_rsrc(f, f_bytes), make_rsrc(idx, idx_bytes), seg_items,
+                           state, n_seg, epoch, spin_limit, err_word, withhold);
 }
 
 // Fused force exchange with atomic adds: ONE launch, last pulse first; an item
@@ -347,11 +368,12 @@ __global__ __launch_bounds__(kThreads) void k_unpack_atomic(
     float *f, uint32_t f_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
     const WorkItem *__restrict__ items, const uint32_t *__restrict__ seg_items, uint32_t *state,
     int32_t n_seg, int32_t n_dom, uint32_t n_items, uint32_t epoch, uint32_t spin_limit,
-    uint32_t *err_word, int32_t withhold)
+    uint32_t *err_word, int32_t withhold, Stress st)
 {
-    unpack_item_atomic<EPT>(items + (n_items - 1u - blockIdx.x), f, make_rsrc(f, f_bytes),
-                            make_rsrc(idx, idx_bytes), seg_items, state, n_seg, n_dom, epoch,
-                            spin_limit, err_word, withhold);
+    const uint32_t u = st.order ? (uint32_t)st.order[blockIdx.x] : n_items - 1u - blockIdx.x;
+    if (st.seed) stress_delay(st.seed, u);
+    unpack_item_atomic<EPT>(items + u, f, make_rsrc(f, f_bytes), make_rsrc(idx, idx_bytes),
+                            seg_items, state, n_seg, n_dom, epoch, spin_limit, err_word, withhold);
 }
 
 // ---- transposed form: per-slot pulse masks --------------------------------
@@ -420,10 +442,12 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
     const halo::Chunk *__restrict__ chunks, const int32_t *__restrict__ dest_start,
     const float4 *__restrict__ shift4, const uint32_t *__restrict__ x_arrivals, uint32_t *state,
     int32_t n_dom, int32_t n_pulse, uint32_t epoch, uint32_t spin_limit, uint32_t *err_word,
-    int32_t withhold)
+    int32_t withhold, Stress st)
 {
     __shared__ Ranks<EPT> sh;
-    const halo::Chunk *c = chunks + blockIdx.x;
+    const uint32_t u = st.order ? (uint32_t)st.order[blockIdx.x] : blockIdx.x;
+    if (st.seed) stress_delay(st.seed, u);
+    const halo::Chunk *c = chunks + u;
     const int32_t first = c->first, count = c->count, D = c->domain;
     const uint32_t umask = c->mask;
     const auto rx = make_rsrc(x, x_bytes);
@@ -494,10 +518,12 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
     const halo::Chunk *__restrict__ chunks, const int32_t *__restrict__ forder,
     const int32_t *__restrict__ dest_start, const int32_t *__restrict__ send_to,
     const uint32_t *__restrict__ zone_chunks, uint32_t *state, int32_t n_dom, int32_t n_pulse,
-    uint32_t epoch, uint32_t spin_limit, uint32_t *err_word, int32_t withhold)
+    uint32_t epoch, uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Stress st)
 {
     __shared__ Ranks<EPT> sh;
-    const halo::Chunk *c = chunks + forder[blockIdx.x];
+    const int32_t u = st.order ? st.order[blockIdx.x] : forder[blockIdx.x];
+    if (st.seed) stress_delay(st.seed, (uint32_t)u);
+    const halo::Chunk *c = chunks + u;
     const int32_t first = c->first, count = c->count, D = c->domain, zone = c->zone;
     const uint32_t umask = c->mask;
     const auto rf = make_rsrc(f, f_bytes);

@@ -50,10 +50,12 @@ void free_device(halo_plan *p)
                     (void *)p->d_state, (void *)p->d_mask, (void *)p->d_chunks,
                     (void *)p->d_forder, (void *)p->d_dest_start, (void *)p->d_shift4,
                     (void *)p->d_x_arrivals, (void *)p->d_zone_chunks, (void *)p->d_local_map,
-                    (void *)p->d_home_slot})
+                    (void *)p->d_home_slot, (void *)p->d_stress})
         if (q) (void)hipFree(q);
     if (p->h_err) (void)hipHostFree(p->h_err);
     p->d_idx = p->d_recv_from = p->d_send_to = p->d_forder = p->d_dest_start = nullptr;
+    p->d_stress = nullptr;
+    p->stress_seed = 0;
     p->d_local_map = nullptr;
     p->d_home_slot = nullptr;
     p->d_items = nullptr;
@@ -110,6 +112,18 @@ Kernels kernels(int32_t item_entries)
     }
 }
 
+// Stress-mode order of one kernel family (see halo_plan_debug_stress):
+// [items X | items F | chunks X | chunks F] in p->d_stress.
+enum StressOrder { kOrderItemsX = 0, kOrderItemsF = 1, kOrderChunksX = 2, kOrderChunksF = 3 };
+
+Stress stress_of(const halo_plan *p, StressOrder which)
+{
+    if (!p->stress_seed || !p->d_stress) return Stress{nullptr, 0u};
+    const size_t ni = p->h.items.size(), nc = p->h.chunks.size();
+    const size_t off[4] = {0, ni, 2 * ni, 2 * ni + nc};
+    return Stress{p->d_stress + off[which], p->stress_seed};
+}
+
 hipError_t launch_fused(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
 {
     const halo::HostPlan &h = p->h;
@@ -120,15 +134,17 @@ hipError_t launch_fused(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
     uint32_t epoch = force_dir ? p->epoch_f : p->epoch_x;
     const Kernels k = kernels(h.item_entries);
     if (force_dir) {
+        Stress st = stress_of(p, kOrderItemsF);
         void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_seg_items,
                         &p->d_state, &n_seg, &n_items, &epoch, &p->spin_limit, &p->d_err,
-                        &p->withhold};
+                        &p->withhold, &st};
         return hipLaunchKernel(k.unpack_fused, dim3(n_items), dim3(kThreads), args, 0, s);
     }
     int32_t n_dom = h.n_dom;
+    Stress st = stress_of(p, kOrderItemsX);
     void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_recv_from,
                     &p->d_seg_items, &p->d_state, &n_dom, &epoch, &p->spin_limit, &p->d_err,
-                    &p->withhold};
+                    &p->withhold, &st};
     return hipLaunchKernel(k.pack_fused, dim3(n_items), dim3(kThreads), args, 0, s);
 }
 
@@ -143,15 +159,17 @@ hipError_t launch_chunks(halo_plan *p, bool force_dir, float *buf, hipStream_t s
     const Kernels k = kernels(h.chunk_slots);
     if (force_dir) {
         uint32_t epoch = p->epoch_fc;
+        Stress st = stress_of(p, kOrderChunksF);
         void *args[] = {&buf, &bytes, &p->d_mask, &p->d_chunks, &p->d_forder, &p->d_dest_start,
                         &p->d_send_to, &p->d_zone_chunks, &state, &n_dom, &n_pulse, &epoch,
-                        &p->spin_limit, &p->d_err, &p->withhold};
+                        &p->spin_limit, &p->d_err, &p->withhold, &st};
         return hipLaunchKernel(k.pull_f, dim3(n), dim3(kThreads), args, 0, s);
     }
     uint32_t epoch = p->epoch_xc;
+    Stress st = stress_of(p, kOrderChunksX);
     void *args[] = {&buf, &bytes, &p->d_mask, &p->d_chunks, &p->d_dest_start, &p->d_shift4,
                     &p->d_x_arrivals, &state, &n_dom, &n_pulse, &epoch, &p->spin_limit,
-                    &p->d_err, &p->withhold};
+                    &p->d_err, &p->withhold, &st};
     return hipLaunchKernel(k.push_x, dim3(n), dim3(kThreads), args, 0, s);
 }
 
@@ -178,9 +196,10 @@ hipError_t launch_atomic(halo_plan *p, float *buf, hipStream_t s)
     uint32_t epoch = p->epoch_f;
     const Kernels k = kernels(h.item_entries);
     int32_t n_dom = h.n_dom;
+    Stress st = stress_of(p, kOrderItemsF);
     void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_seg_items,
                     &p->d_state, &n_seg, &n_dom, &n_items, &epoch, &p->spin_limit, &p->d_err,
-                    &p->withhold};
+                    &p->withhold, &st};
     return hipLaunchKernel(k.unpack_atomic, dim3(n_items), dim3(kThreads), args, 0, s);
 }
 
@@ -711,6 +730,70 @@ halo_status halo_plan_set_spin_limit(halo_plan *p, uint32_t polls)
 {
     if (!p || polls == 0) return fail(HALO_ERR_ARG, "halo_plan_set_spin_limit: bad argument");
     p->spin_limit = polls;
+    return HALO_OK;
+}
+
+halo_status halo_plan_debug_stress(halo_plan *p, uint32_t seed)
+{
+    if (!p) return fail(HALO_ERR_ARG, "halo_plan_debug_stress: NULL plan");
+    if (p->invalid) return fail(HALO_ERR_STATE, "halo_plan_debug_stress: invalid plan");
+    halo_status st = ensure_uploaded(p);
+    if (st != HALO_OK) return st;
+    if (p->d_stress) {
+        hipError_t e = hipDeviceSynchronize();  // no launch still reads the old orders
+        if (e != hipSuccess) return hip_fail(e, "halo_plan_debug_stress");
+        (void)hipFree(p->d_stress);
+        p->d_stress = nullptr;
+    }
+    p->stress_seed = 0;
+    if (seed == 0) return HALO_OK;
+    const halo::HostPlan &h = p->h;
+    const int32_t ni = (int32_t)h.items.size(), nc = (int32_t)h.chunks.size();
+    // Work units that never wait on each other, in launch order: the items of
+    // one pulse; the chunks of one zone. Each such group runs reversed.
+    std::vector<int32_t> order((size_t)2 * ni + 2 * nc);
+    auto reverse_groups = [](int32_t *dst, const std::vector<int32_t> &seq,
+                             const std::vector<int32_t> &key) {
+        const int32_t n = (int32_t)seq.size();
+        for (int32_t lo = 0; lo < n;) {
+            int32_t hi = lo;
+            while (hi < n && key[hi] == key[lo]) ++hi;
+            for (int32_t i = lo; i < hi; ++i) dst[i] = seq[lo + hi - 1 - i];
+            lo = hi;
+        }
+    };
+    std::vector<int32_t> seq(ni), key(ni);
+    for (int32_t i = 0; i < ni; ++i) {
+        seq[i] = i;
+        key[i] = h.items[i].seg / h.n_dom;  // pulse
+    }
+    reverse_groups(order.data(), seq, key);
+    for (int32_t b = 0; b < ni; ++b) {  // force direction: last pulse first
+        seq[b] = ni - 1 - b;
+        key[b] = h.items[ni - 1 - b].seg / h.n_dom;
+    }
+    reverse_groups(order.data() + ni, seq, key);
+    seq.resize(nc);
+    key.resize(nc);
+    for (int32_t i = 0; i < nc; ++i) {
+        seq[i] = i;
+        key[i] = h.chunks[i].zone;
+    }
+    reverse_groups(order.data() + 2 * ni, seq, key);
+    for (int32_t b = 0; b < nc; ++b) {
+        seq[b] = h.chunk_forder[b];
+        key[b] = h.chunks[h.chunk_forder[b]].zone;
+    }
+    reverse_groups(order.data() + 2 * ni + nc, seq, key);
+    hipError_t e = hipMalloc((void **)&p->d_stress, std::max<size_t>(order.size(), 1) * 4);
+    if (e == hipSuccess && !order.empty())
+        e = hipMemcpy(p->d_stress, order.data(), order.size() * 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        if (p->d_stress) (void)hipFree(p->d_stress);
+        p->d_stress = nullptr;
+        return hip_fail(e, "halo_plan_debug_stress");
+    }
+    p->stress_seed = seed;
     return HALO_OK;
 }
 

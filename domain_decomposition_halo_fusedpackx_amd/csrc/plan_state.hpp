@@ -69,6 +69,9 @@ struct halo_plan {
     uint32_t epoch_x = 0, epoch_f = 0, epoch_xc = 0, epoch_fc = 0;
     uint32_t spin_limit = 1u << 20;
     int32_t withhold = -1;
+    // testing: stress mode (seed 0 = off) and its launch orders
+    uint32_t stress_seed = 0;
+    int32_t *d_stress = nullptr;
 };
 
 namespace halo {
