@@ -165,8 +165,11 @@ halo_status halo_plan_pulse(const halo_plan *plan, int32_t p, int32_t d, int32_t
 halo_status halo_plan_item_waits(const halo_plan *plan, int32_t item, int32_t *segment,
                                  uint32_t *xwait_mask, uint32_t *await_mask);
 
-/* Allocate and upload the device metadata on the current HIP device (blocking).
- * Called implicitly by the first exchange. */
+/* Allocate and upload the device metadata on the current HIP device (blocking:
+ * it synchronises the device). The first exchange on a plan built by
+ * halo_plan_create calls it implicitly, and is then the only exchange call
+ * that synchronises; call it up front to keep every exchange asynchronous.
+ * Plans built on the device are uploaded when they are built. */
 halo_status halo_plan_upload(halo_plan *plan);
 
 /* Coordinate exchange, Algorithms 3-5 fused into ONE kernel launch on
