@@ -55,29 +55,38 @@ def domain_cells(grid):
     return np.stack([ids % nx, (ids // nx) % ny, ids // (nx * ny)], axis=1)
 
 
-def halo_sets(pos, box, grid, cutoff):
+def halo_sets(pos, box, grid, cutoff, criterion="slab"):
     """For every domain, the sorted global ids that its halo must hold.
 
     An atom belongs to the halo of domain D when it is not a home atom of D and,
     in every decomposed dimension d, it lies either in D's own slab of cells or
     within the cutoff above D's upper face: 0 <= (t_d - (c_d(D) + 1)) mod n_d
-    < rc / w_d. This is the set definition, evaluated atom by atom.
+    < rc / w_d. With criterion "corner" its Euclidean distance to D's box must
+    also be below the cutoff: sum_d (delta_d * w_d)^2 < rc^2 over d = x, y, z,
+    delta_d = 0 where it lies in D's slab. This is the set definition,
+    evaluated atom by atom.
     """
     grid = np.asarray(grid, np.int64)
-    _, u, _ = geometry(box, grid, cutoff)
+    w, u, _ = geometry(box, grid, cutoff)
     t, c = cells(pos, box, grid)
+    rc2 = float(np.float32(cutoff)) * float(np.float32(cutoff))
     out = []
     for cd in domain_cells(grid):
         ok = np.ones(len(t), dtype=bool)
         home = np.ones(len(t), dtype=bool)
+        dist2 = np.zeros(len(t))
         for d in range(3):
             same = c[:, d] == cd[d]
             home &= same
-            if grid[d] == 1:
-                continue
             delta = t[:, d] - float(cd[d] + 1)
             delta = np.where(delta < 0.0, delta + float(grid[d]), delta)
+            dist = np.where(same, 0.0, delta) * w[d]
+            dist2 = dist2 + dist * dist
+            if grid[d] == 1:
+                continue
             ok &= same | (delta < u[d])
+        if criterion == "corner":
+            ok &= dist2 < rc2
         out.append(np.flatnonzero(ok & ~home))
     return out
 

@@ -44,6 +44,14 @@
  *     one after another in id order, id = cx + nx*(cy + ny*cz).
  *  R5 depOffset = number of home atoms: entries below it are independent.
  *  R6 force order: pulses strictly in reverse, one fp32 add per component.
+ *  R7 corner selection (an option; the pages do not spell the test out): an
+ *     atom belongs to the halo of domain D only if its Euclidean distance to
+ *     D's box, over the upper faces it lies beyond, is below the cutoff:
+ *       sum_d (delta_d * w_d)^2 < rc^2,  delta_d = 0 where the atom's cell
+ *     equals D's along d, else its distance above D's upper face (as in R3),
+ *     summed over d = x, y, z in that order, in double. In the pulses the
+ *     test is made against each receiver; the partial sums only grow along
+ *     the forwarding path, so the final receiver's test decides.
  *
  * Build: gcc -O2 -std=c99 -fPIC -shared -ffp-contract=off (no -ffast-math).
  */
@@ -84,6 +92,7 @@ typedef struct {
 
 typedef struct oracle {
     int64_t n_atoms;
+    int32_t criterion;    /* 0 slab (R3), 1 corner (R7) */
     float box[3];
     int32_t grid[3];
     float cutoff;
@@ -194,16 +203,46 @@ static int in_slab(const oracle *o, int64_t a, int dim, int32_t cr)
     return delta < o->u[dim];
 }
 
+int oracle_build_ex(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,
+                    float cutoff, int32_t criterion, oracle **out);
+
+/* Corner test of reading R7 for atom a sent towards the receiver of cell cr
+ * in a pulse along dim: the slab test, and the squared distance to the
+ * receiver's box over the faces the atom lies beyond below rc^2. */
+static int in_corner(const oracle *o, int64_t a, int dim, const int32_t cr[3])
+{
+    if (!in_slab(o, a, dim, cr[dim])) return 0;
+    double s = 0.0;
+    for (int d = 0; d < 3; ++d) {
+        double delta = 0.0;
+        if (d == dim || o->c[3 * a + d] != cr[d]) {
+            delta = o->t[3 * a + d] - (double)(cr[d] + 1);
+            if (delta < 0.0) delta += (double)o->grid[d];
+        }
+        const double dist = delta * o->w[d];
+        s += dist * dist;
+    }
+    return s < (double)o->cutoff * (double)o->cutoff;
+}
+
 int oracle_build(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,
                  float cutoff, oracle **out)
+{
+    return oracle_build_ex(pos, n_atoms, box, grid, cutoff, 0, out);
+}
+
+int oracle_build_ex(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,
+                    float cutoff, int32_t criterion, oracle **out)
 {
     if (!out) return OR_ERR_ARG;
     *out = NULL;
     if (n_atoms < 0 || !box || !grid || (n_atoms > 0 && !pos)) return OR_ERR_ARG;
+    if (criterion != 0 && criterion != 1) return OR_ERR_ARG;
 
     oracle *o = (oracle *)calloc(1, sizeof(oracle));
     if (!o) return OR_ERR_NOMEM;
     o->n_atoms = n_atoms;
+    o->criterion = criterion;
     for (int d = 0; d < 3; ++d) {
         o->box[d] = box[d];
         o->grid[d] = grid[d];
@@ -291,9 +330,11 @@ int oracle_build(const float *pos, int64_t n_atoms, const float *box, const int3
                 goto fail;
             }
             q->send_size = 0;
-            for (int32_t s = lo; s < hi; ++s)
-                if (in_slab(o, o->slots[D].gid[s], dim, cr[dim]))
+            for (int32_t s = lo; s < hi; ++s) {
+                const int64_t a = o->slots[D].gid[s];
+                if (o->criterion ? in_corner(o, a, dim, cr) : in_slab(o, a, dim, cr[dim]))
                     q->index_map[q->send_size++] = s;
+            }
 
             /* depOffset split, [REV] Algorithm 4 (R5) */
             q->dep_start = 0;

@@ -41,6 +41,8 @@ def lib():
         P = ctypes.POINTER
         L.oracle_build.argtypes = [vp, i64, vp, vp, ctypes.c_float, P(vp)]
         L.oracle_build.restype = ctypes.c_int
+        L.oracle_build_ex.argtypes = [vp, i64, vp, vp, ctypes.c_float, i32, P(vp)]
+        L.oracle_build_ex.restype = ctypes.c_int
         L.oracle_free.argtypes = [vp]
         L.oracle_free.restype = None
         L.oracle_total_slots.argtypes = [vp]
@@ -82,16 +84,20 @@ class OracleError(RuntimeError):
 class Oracle:
     """The plan and both exchanges, computed serially on the CPU."""
 
-    def __init__(self, pos, box, grid, cutoff):
+    CRITERIA = {"slab": 0, "corner": 1}
+
+    def __init__(self, pos, box, grid, cutoff, criterion="slab"):
         L = lib()
         pos = np.ascontiguousarray(pos, dtype=np.float32).reshape(-1, 3)
         self.pos = pos
         self.box = np.ascontiguousarray(box, dtype=np.float32)
         self.grid = np.ascontiguousarray(grid, dtype=np.int32)
         self.cutoff = np.float32(cutoff)
+        self.criterion = criterion
         h = ctypes.c_void_p()
-        rc = L.oracle_build(_ptr(pos) if pos.size else None, pos.shape[0], _ptr(self.box),
-                            _ptr(self.grid), ctypes.c_float(self.cutoff), ctypes.byref(h))
+        rc = L.oracle_build_ex(_ptr(pos) if pos.size else None, pos.shape[0], _ptr(self.box),
+                               _ptr(self.grid), ctypes.c_float(self.cutoff),
+                               self.CRITERIA[criterion], ctypes.byref(h))
         if rc != 0:
             raise OracleError(rc)
         self._h = h
@@ -180,10 +186,10 @@ class Oracle:
         return f
 
 
-def try_build(pos, box, grid, cutoff) -> int:
+def try_build(pos, box, grid, cutoff, criterion="slab") -> int:
     """Return the oracle's status code for these inputs (0 when it builds)."""
     try:
-        Oracle(pos, box, grid, cutoff)
+        Oracle(pos, box, grid, cutoff, criterion)
     except OracleError as e:
         return e.code
     return 0

@@ -401,3 +401,68 @@ def test_cell_sorted_is_a_renumbering():
     c = np.minimum((sp.astype(np.float64) / 0.5).astype(np.int64), 11)
     key = (c[:, 2] * 12 + c[:, 1]) * 12 + c[:, 0]
     assert np.all(np.diff(key) >= 0)
+
+
+# ---- the corner selection option (Euclidean distance to the receiving box) ----
+
+@pytest.mark.parametrize("case", TINY, ids=lambda c: "x".join(map(str, c[1])))
+@pytest.mark.parametrize("seed", [11, 12])
+def test_corner_halo_set_is_bruteforce_set_exactly_once(oracle_mod, case, seed):
+    box, grid, rc, n = case
+    pos = W.positions(box, n, seed)
+    o = oracle_mod.Oracle(pos, box, grid, rc, "corner")
+    gids = o.slot_gids()
+    want = BF.halo_sets(pos, box, grid, rc, "corner")
+    for d, (lo, hi) in enumerate(_halo_slices(o)):
+        got = np.sort(gids[lo:hi])
+        assert len(np.unique(got)) == len(got), f"domain {d}: an atom appears twice"
+        np.testing.assert_array_equal(got, want[d], err_msg=f"domain {d}")
+
+
+@pytest.mark.parametrize("case", TINY, ids=lambda c: "x".join(map(str, c[1])))
+def test_corner_halo_is_the_slab_halo_within_the_cutoff(oracle_mod, case):
+    """Corner halo = the slab halo's atoms whose Euclidean distance to the
+    domain's box is below the cutoff; strictly smaller wherever two
+    dimensions are decomposed (edges and corners get trimmed)."""
+    box, grid, rc, n = case
+    pos = W.positions(box, n, 5)
+    slab = BF.halo_sets(pos, box, grid, rc)
+    corner = BF.halo_sets(pos, box, grid, rc, "corner")
+    t, c = BF.cells(pos, box, grid)
+    w, _, _ = BF.geometry(box, grid, rc)
+    for dom, cd in enumerate(BF.domain_cells(np.asarray(grid))):
+        s, k = set(slab[dom].tolist()), set(corner[dom].tolist())
+        assert k <= s
+        for a in s - k:  # every trimmed atom lies at least rc away
+            dist2 = 0.0
+            for d in range(3):
+                if c[a, d] != cd[d]:
+                    delta = t[a, d] - (cd[d] + 1)
+                    delta = delta + grid[d] if delta < 0 else delta
+                    dist2 += (delta * w[d]) ** 2
+            assert dist2 >= float(np.float32(rc)) ** 2 * (1 - 1e-12)
+    if sum(g > 1 for g in grid) >= 2:
+        assert sum(map(len, corner)) < sum(map(len, slab))
+
+
+@pytest.mark.parametrize("case", TINY[:6], ids=lambda c: "x".join(map(str, c[1])))
+def test_corner_coordinates_and_force_adjoint(oracle_mod, case):
+    box, grid, rc, n = case
+    pos = W.positions(box, n, 23)
+    o = oracle_mod.Oracle(pos, box, grid, rc, "corner")
+    x = o.home_filled(np.nan)
+    o.exchange_x(x)
+    gids = o.slot_gids()
+    dos = _dom_of_slot(o)
+    halo = np.ones(o.total_slots, bool)
+    halo[o.home_slots()] = False
+    want = BF.halo_coords(pos, box, grid, gids[halo], dos[halo])
+    np.testing.assert_array_equal(x[halo].view(np.uint32), want.view(np.uint32))
+    base, n_home, n_halo = o.domains()
+    f = W.small_int_forces(o.total_slots, base, n_home, n_halo, 3)
+    f0 = f.copy()
+    o.exchange_f(f)
+    hs = o.home_slots()
+    want_f = np.zeros((len(pos), 3))
+    np.add.at(want_f, gids[halo], f0[halo].astype(np.float64))
+    np.testing.assert_array_equal(f[hs].astype(np.float64), want_f)
