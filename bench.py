@@ -165,7 +165,7 @@ def cold_exchange_us(torch, plan, x, f, f_init, suffix, reps):
 def plan_build_ms(torch, HaloPlan, w, pos, reps):
     """Wall time of building the plan on the host (halo_plan_create from host
     positions, then the upload), on the GPU (halo_plan_create_device from
-    device positions) and of rebuilding a device plan in place
+    device positions, with either selection) and of rebuilding a device plan in place
     (halo_plan_rebuild_device), median of reps, after one warm-up each."""
     pos_d = torch.from_numpy(pos).cuda()
 
@@ -180,8 +180,13 @@ def plan_build_ms(torch, HaloPlan, w, pos, reps):
         torch.cuda.synchronize()
         return p
 
+    def dev_corner():
+        p = HaloPlan.on_device(pos_d, w.box, w.grid, w.cutoff, selection="corner")
+        torch.cuda.synchronize()
+        return p
+
     out = {}
-    for name, fn in (("host_ms", host), ("device_ms", dev)):
+    for name, fn in (("host_ms", host), ("device_ms", dev), ("device_corner_ms", dev_corner)):
         fn().close()
         ts = []
         for _ in range(reps):
@@ -442,6 +447,32 @@ def main():
         for p in splans:
             p.sync()
         del splans, sx, sf
+        # The corner selection: the same atoms, edge and corner zones trimmed
+        # to the cutoff sphere; fewer entries, same kernels.
+        log("corner selection")
+        cplans = [HaloPlan(pos, w.box, w.grid, w.cutoff, selection="corner") for _ in range(R)]
+        cS = cplans[0].total_slots
+        cx = [torch.from_numpy(cplans[0].home_filled(pos, 0.0)).cuda() for _ in range(R)]
+        cbase, ch, cm = cplans[0].domains()
+        cf = [torch.from_numpy(W.halo_forces(cS, cbase, ch, cm, w.seed)).cuda() for _ in range(R)]
+        for p in cplans:
+            p.upload()
+
+        def cstep(i):
+            cplans[i % R].exchange_x(cx[i % R])
+            cplans[i % R].exchange_f(cf[i % R])
+        cms = time_loop(torch, cstep, args.steps)
+        out["corner_selection"] = {
+            "halo_entries": cplans[0].num_entries, "slots": cS,
+            "ms_per_step": cms,
+            "us_x": time_loop(torch, lambda i: cplans[i % R].exchange_x(cx[i % R]),
+                              args.steps) * 1e3,
+            "us_f": time_loop(torch, lambda i: cplans[i % R].exchange_f(cf[i % R]),
+                              args.steps) * 1e3,
+            "step_speedup_vs_slab": ms_step / cms}
+        for p in cplans:
+            p.sync()
+        del cplans, cx, cf
         log("plan builds")
         out["plan_build"] = plan_build_ms(torch, HaloPlan, w, pos, args.build_reps)
         if not args.no_overlap:

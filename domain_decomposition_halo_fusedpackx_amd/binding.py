@@ -24,7 +24,9 @@ _P = ctypes.POINTER
 _st = ctypes.c_int
 SIGNATURES = {
     "halo_plan_create": (_st, [_vp, _i64, _vp, _vp, _f32, _P(_vp)]),
+    "halo_plan_create_ex": (_st, [_vp, _i64, _vp, _vp, _f32, _i32, _P(_vp)]),
     "halo_plan_create_device": (_st, [_vp, _i64, _vp, _vp, _f32, _vp, _P(_vp)]),
+    "halo_plan_create_device_ex": (_st, [_vp, _i64, _vp, _vp, _f32, _i32, _vp, _P(_vp)]),
     "halo_plan_rebuild_device": (_st, [_vp, _vp, _i64, _vp, _vp]),
     "halo_plan_destroy": (None, [_vp]),
     "halo_last_error": (ctypes.c_char_p, []),
@@ -33,6 +35,7 @@ SIGNATURES = {
     "halo_plan_num_pulses": (_i32, [_vp]),
     "halo_plan_num_entries": (_i64, [_vp]),
     "halo_plan_num_items": (_i32, [_vp]),
+    "halo_plan_selection": (_i32, [_vp]),
     "halo_plan_pulse_dim": (_st, [_vp, _i32, _P(_i32), _P(_i32)]),
     "halo_plan_domain": (_st, [_vp, _i32, _P(_i64), _P(_i32), _P(_i32)]),
     "halo_plan_home_slots": (_st, [_vp, _vp]),
@@ -113,10 +116,23 @@ def _stream_handle(stream, device: int = -1):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-class HaloPlan:
-    """An exchange plan (halo_plan_create) and its two exchanges."""
+# halo_selection values of include/halo.h
+SELECTIONS = {"slab": 0, "corner": 1}
 
-    def __init__(self, positions, box, grid, cutoff):
+
+def _selection(name):
+    if name not in SELECTIONS:
+        raise ValueError(f"selection must be one of {sorted(SELECTIONS)}")
+    return SELECTIONS[name]
+
+
+class HaloPlan:
+    """An exchange plan (halo_plan_create_ex) and its two exchanges.
+    `selection` is "slab" (the per-dimension test) or "corner" (also the
+    Euclidean distance to the receiving domain's box below the cutoff)."""
+
+    def __init__(self, positions, box, grid, cutoff, selection="slab"):
+        sel = _selection(selection)
         lib = load_library()
         pos = np.ascontiguousarray(np.asarray(positions, dtype=np.float32).reshape(-1, 3))
         self._box = np.ascontiguousarray(box, dtype=np.float32)
@@ -124,16 +140,17 @@ class HaloPlan:
         if self._box.shape != (3,) or self._grid.shape != (3,):
             raise ValueError("box and grid need three entries")
         h = ctypes.c_void_p()
-        _check(lib.halo_plan_create(_np_ptr(pos) if pos.size else None, pos.shape[0],
-                                    _np_ptr(self._box), _np_ptr(self._grid),
-                                    ctypes.c_float(cutoff), ctypes.byref(h)))
+        _check(lib.halo_plan_create_ex(_np_ptr(pos) if pos.size else None, pos.shape[0],
+                                       _np_ptr(self._box), _np_ptr(self._grid),
+                                       ctypes.c_float(cutoff), sel, ctypes.byref(h)))
         self._finish(h, pos.shape[0])
 
     @classmethod
-    def on_device(cls, positions, box, grid, cutoff, stream=None):
-        """Build the plan on the GPU (halo_plan_create_device) from a
+    def on_device(cls, positions, box, grid, cutoff, stream=None, selection="slab"):
+        """Build the plan on the GPU (halo_plan_create_device_ex) from a
         contiguous float32 torch.cuda tensor of shape (n_atoms, 3)."""
         import torch
+        sel = _selection(selection)
         if not isinstance(positions, torch.Tensor) or not positions.is_cuda:
             raise TypeError("positions must be a torch.cuda tensor")
         if positions.dtype != torch.float32 or not positions.is_contiguous():
@@ -148,16 +165,16 @@ class HaloPlan:
             raise ValueError("box and grid need three entries")
         n = positions.numel() // 3
         h = ctypes.c_void_p()
-        _check(lib.halo_plan_create_device(
+        _check(lib.halo_plan_create_device_ex(
             ctypes.c_void_p(positions.data_ptr()) if n else None, n, _np_ptr(self._box),
-            _np_ptr(self._grid), ctypes.c_float(cutoff),
+            _np_ptr(self._grid), ctypes.c_float(cutoff), sel,
             _stream_handle(stream, positions.get_device()), ctypes.byref(h)))
         self._finish(h, n)
         return self
 
     def rebuild_on_device(self, positions, box=None, stream=None):
         """Rebuild this plan on the GPU for new positions (halo_plan_rebuild_device);
-        grid and cutoff stay, box may change."""
+        grid, cutoff and selection stay, box may change."""
         import torch
         if not isinstance(positions, torch.Tensor) or not positions.is_cuda:
             raise TypeError("positions must be a torch.cuda tensor")
@@ -192,6 +209,7 @@ class HaloPlan:
         self.num_pulses = lib.halo_plan_num_pulses(h)
         self.num_entries = lib.halo_plan_num_entries(h)
         self.num_items = lib.halo_plan_num_items(h)
+        self.selection = {v: k for k, v in SELECTIONS.items()}[lib.halo_plan_selection(h)]
 
     def close(self):
         h = getattr(self, "_h", None)

@@ -15,6 +15,9 @@
 #include "plan_state.hpp"
 #include "sync.hpp"
 
+static_assert(HALO_SELECT_SLAB == halo::kSelectSlab && HALO_SELECT_CORNER == halo::kSelectCorner,
+              "selection codes");
+
 using halo::WorkItem;
 
 namespace {
@@ -329,6 +332,13 @@ const char *halo_last_error(void) { return g_last_error.c_str(); }
 halo_status halo_plan_create(const float *positions, int64_t n_atoms, const float *box,
                              const int32_t *grid, float cutoff, halo_plan **out)
 {
+    return halo_plan_create_ex(positions, n_atoms, box, grid, cutoff, HALO_SELECT_SLAB, out);
+}
+
+halo_status halo_plan_create_ex(const float *positions, int64_t n_atoms, const float *box,
+                                const int32_t *grid, float cutoff, int32_t selection,
+                                halo_plan **out)
+{
     if (!out) return fail(HALO_ERR_ARG, "halo_plan_create: NULL output pointer");
     *out = nullptr;
     halo_plan *p = new (std::nothrow) halo_plan();
@@ -336,8 +346,8 @@ halo_status halo_plan_create(const float *positions, int64_t n_atoms, const floa
     std::string msg;
     int rc;
     try {
-        rc = halo::build_plan(positions, n_atoms, box, grid, cutoff, item_entries_from_env(), p->h,
-                              msg);
+        rc = halo::build_plan(positions, n_atoms, box, grid, cutoff, selection,
+                              item_entries_from_env(), p->h, msg);
     } catch (const std::bad_alloc &) {
         rc = halo::kErrNoMem;
         msg = "halo_plan_create: out of host memory";
@@ -357,6 +367,14 @@ halo_status halo_plan_create_device(const float *positions, int64_t n_atoms, con
                                     const int32_t *grid, float cutoff, void *stream,
                                     halo_plan **out)
 {
+    return halo_plan_create_device_ex(positions, n_atoms, box, grid, cutoff, HALO_SELECT_SLAB,
+                                      stream, out);
+}
+
+halo_status halo_plan_create_device_ex(const float *positions, int64_t n_atoms, const float *box,
+                                       const int32_t *grid, float cutoff, int32_t selection,
+                                       void *stream, halo_plan **out)
+{
     if (!out) return fail(HALO_ERR_ARG, "halo_plan_create_device: NULL output pointer");
     *out = nullptr;
     halo_plan *p = new (std::nothrow) halo_plan();
@@ -365,7 +383,7 @@ halo_status halo_plan_create_device(const float *positions, int64_t n_atoms, con
     int rc;
     g_last_error.clear();
     try {
-        rc = halo::build_plan_device(p, positions, n_atoms, box, grid, cutoff,
+        rc = halo::build_plan_device(p, positions, n_atoms, box, grid, cutoff, selection,
                                      item_entries_from_env(), (hipStream_t)stream, msg);
     } catch (const std::bad_alloc &) {
         rc = halo::kErrNoMem;
@@ -390,13 +408,14 @@ halo_status halo_plan_rebuild_device(halo_plan *p, const float *positions, int64
     if (!p || !box) return fail(HALO_ERR_ARG, "halo_plan_rebuild_device: NULL argument");
     const int32_t grid[3] = {p->h.grid[0], p->h.grid[1], p->h.grid[2]};
     const float cutoff = p->h.cutoff;
+    const int32_t selection = p->h.selection;
     {
         // argument and geometry errors leave the plan as it was
         halo::HostPlan probe;
         std::string msg;
         if (n_atoms < 0 || (n_atoms > 0 && !positions))
             return fail(HALO_ERR_ARG, "halo_plan_rebuild_device: NULL pointer or negative count");
-        const int rc = halo::plan_geometry(n_atoms, box, grid, cutoff, probe, msg);
+        const int rc = halo::plan_geometry(n_atoms, box, grid, cutoff, selection, probe, msg);
         if (rc != halo::kOk) return fail((halo_status)rc, msg);
     }
     if (!p->built_on_device) {
@@ -410,7 +429,7 @@ halo_status halo_plan_rebuild_device(halo_plan *p, const float *positions, int64
     int rc;
     g_last_error.clear();
     try {
-        rc = halo::build_plan_device(p, positions, n_atoms, box, grid, cutoff,
+        rc = halo::build_plan_device(p, positions, n_atoms, box, grid, cutoff, selection,
                                      item_entries_from_env(), (hipStream_t)stream, msg);
     } catch (const std::bad_alloc &) {
         rc = halo::kErrNoMem;
@@ -426,6 +445,7 @@ halo_status halo_plan_rebuild_device(halo_plan *p, const float *positions, int64
         p->h.grid[1] = grid[1];
         p->h.grid[2] = grid[2];
         p->h.cutoff = cutoff;
+        p->h.selection = selection;
         p->built_on_device = false;
         p->invalid = true;
         return msg.empty() ? (halo_status)rc : fail((halo_status)rc, msg);
@@ -446,6 +466,7 @@ int32_t halo_plan_num_domains(const halo_plan *p) { return p ? p->h.n_dom : -1; 
 int32_t halo_plan_num_pulses(const halo_plan *p) { return p ? p->h.n_pulse : -1; }
 int64_t halo_plan_num_entries(const halo_plan *p) { return p ? (int64_t)p->h.n_entries : -1; }
 int32_t halo_plan_num_items(const halo_plan *p) { return p ? (int32_t)p->h.items.size() : -1; }
+int32_t halo_plan_selection(const halo_plan *p) { return p ? p->h.selection : -1; }
 
 halo_status halo_plan_pulse_dim(const halo_plan *p, int32_t pulse, int32_t *dim, int32_t *k)
 {

@@ -9,7 +9,9 @@
 // pulses per dimension ceil(cutoff / w); data flows to the lower neighbour
 // with +L on a periodic wrap; an atom is sent when its original position,
 // in units of w and in double precision, lies less than cutoff / w above the
-// receiver's upper face; home atoms in ascending id; indexMap ascending;
+// receiver's upper face (with the corner selection also when its Euclidean
+// distance to the receiver's box is below the cutoff); home atoms in
+// ascending id; indexMap ascending;
 // slots of a domain = [home | region per pulse], domains in id order.
 //
 // The build runs the pulses on index lists only (no coordinates are moved):
@@ -82,11 +84,16 @@ inline int32_t domain_of_cell(const int32_t *grid, const int32_t *c)
 }  // namespace
 
 int plan_geometry(int64_t n_atoms, const float *box, const int32_t *grid, float cutoff,
-                  HostPlan &P, std::string &msg)
+                  int32_t selection, HostPlan &P, std::string &msg)
 {
     P = HostPlan();
     P.n_atoms = n_atoms;
     P.cutoff = cutoff;
+    if (selection != kSelectSlab && selection != kSelectCorner) {
+        msg = "halo_plan_create: selection must be HALO_SELECT_SLAB or HALO_SELECT_CORNER";
+        return kErrArg;
+    }
+    P.selection = selection;
     for (int d = 0; d < 3; ++d) {
         P.box[d] = box[d];
         P.grid[d] = grid[d];
@@ -150,13 +157,14 @@ int plan_geometry(int64_t n_atoms, const float *box, const int32_t *grid, float 
 }
 
 int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,
-               float cutoff, int32_t item_entries, HostPlan &P, std::string &msg)
+               float cutoff, int32_t selection, int32_t item_entries, HostPlan &P,
+               std::string &msg)
 {
     if (n_atoms < 0 || !box || !grid || (n_atoms > 0 && !pos)) {
         msg = "halo_plan_create: NULL pointer or negative atom count";
         return kErrArg;
     }
-    int rc = plan_geometry(n_atoms, box, grid, cutoff, P, msg);
+    int rc = plan_geometry(n_atoms, box, grid, cutoff, selection, P, msg);
     if (rc != kOk) return rc;
     for (int64_t a = 0; a < n_atoms; ++a)
         for (int d = 0; d < 3; ++d) {
@@ -172,6 +180,8 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
     // back below n so that the cell index stays in range.
     std::vector<double> scaled((size_t)n_atoms * 3);
     std::vector<int32_t> owner((size_t)n_atoms);
+    const bool corner = selection == kSelectCorner;
+    const double rc2 = (double)cutoff * (double)cutoff;
     {
         double top[3];
         for (int d = 0; d < 3; ++d) top[d] = std::nextafter((double)grid[d], 0.0);
@@ -211,7 +221,8 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
             Cell3 cd = cell_of_domain(grid, D);
             Segment &s = row[D];
             s.send_to = P.send_to[(size_t)p * P.n_dom + D];
-            const int32_t c_recv = cell_of_domain(grid, s.send_to).c[dim];
+            const Cell3 cr = cell_of_domain(grid, s.send_to);
+            const int32_t c_recv = cr.c[dim];
             s.shift[0] = s.shift[1] = s.shift[2] = 0.f;
             if (cd.c[dim] == 0) s.shift[dim] = box[dim];
             // Candidate slots: all of them on the first pulse of a dimension,
@@ -228,9 +239,27 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
             mv.clear();
             const std::vector<int64_t> &sa = slot_atom[D];
             for (int32_t slot = first; slot < last; ++slot) {
-                double above = scaled[3 * sa[slot] + dim] - face;
+                const double *t = &scaled[3 * sa[slot]];
+                double above = t[dim] - face;
                 if (above < 0.0) above += (double)n;
-                if (above < reach) {
+                bool send = above < reach;
+                if (send && corner) {
+                    // squared distance to the receiver's box, x + y + z in
+                    // this order; dimensions where the atom lies in the
+                    // receiver's slab add nothing
+                    double dist2 = 0.0;
+                    for (int d = 0; d < 3; ++d) {
+                        double delta = 0.0;
+                        if (d == dim || (int32_t)std::floor(t[d]) != cr.c[d]) {
+                            delta = t[d] - (double)(cr.c[d] + 1);
+                            if (delta < 0.0) delta += (double)grid[d];
+                        }
+                        const double dist = delta * P.width[d];
+                        dist2 += dist * dist;
+                    }
+                    send = dist2 < rc2;
+                }
+                if (send) {
                     out.push_back(slot);
                     mv.push_back(sa[slot]);
                 }

@@ -80,6 +80,7 @@ struct HostPlan {
     float box[3] = {0, 0, 0};
     int32_t grid[3] = {1, 1, 1};
     float cutoff = 0;
+    int32_t selection = 0;        // kSelectSlab or kSelectCorner
     // geometry
     double width[3] = {0, 0, 0};
     double reach[3] = {0, 0, 0};  // cutoff / width
@@ -127,6 +128,11 @@ constexpr int32_t kMaxPulses = 32;
 // 0x80000000 as an always-out-of-range offset.
 constexpr int64_t kMaxSlots = ((int64_t)1 << 31) / 12 - 1;
 
+// Halo selection tests, shared with halo.h: the slab test alone, or the slab
+// test and the atom's Euclidean distance to the receiver's box below the
+// cutoff.
+enum : int32_t { kSelectSlab = 0, kSelectCorner = 1 };
+
 // Status codes shared with halo.h.
 enum : int { kOk = 0, kErrArg = -1, kErrGeometry = -2, kErrRange = -3, kErrHip = -4, kErrNoMem = -7 };
 
@@ -161,11 +167,12 @@ void finish_chunks(HostPlan &plan, int32_t chunk_slots, const std::vector<Piece>
 // Geometry of a plan: validates box, grid and cutoff and fills widths,
 // reaches, the pulse list and the send/receive tables.
 int plan_geometry(int64_t n_atoms, const float *box, const int32_t *grid, float cutoff,
-                  HostPlan &plan, std::string &msg);
+                  int32_t selection, HostPlan &plan, std::string &msg);
 
 // Build the plan; returns a status code and a message on failure.
 int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,
-               float cutoff, int32_t item_entries, HostPlan &out, std::string &msg);
+               float cutoff, int32_t selection, int32_t item_entries, HostPlan &out,
+               std::string &msg);
 
 // Cut every segment into work items of at most item_entries entries and,
 // with with_masks, compute their wait masks from the indexMaps (without, the

@@ -57,8 +57,10 @@ constexpr int32_t kMaxDeviceDomains = 8192;  // LDS histogram of 32 KiB
 struct Geom {
     double width[3];
     double top[3];  // nextafter(n_d, 0): scaled positions are clamped below n_d
+    double rc2;     // cutoff^2, for the corner selection
     float box[3];
     int32_t grid[3];
+    int32_t corner; // 1: corner selection, 0: slab selection
 };
 
 __device__ __forceinline__ double scaled(float v, double width, double top)
@@ -251,11 +253,34 @@ struct SegTable {
     }
 };
 
+// Corner selection: the squared distance from the atom at src (coordinates
+// `stride` apart) to the box of the receiver in cell cr, summed over x, y, z
+// in this order in double, is below cutoff^2. A dimension where the atom lies
+// in the receiver's slab (other than the pulse's own) adds nothing.
+__device__ __forceinline__ bool corner_test(const float *src, int64_t stride, int32_t dim,
+                                         const int32_t cr[3], const Geom &g)
+{
+    double dist2 = 0.0;
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+        const double t = scaled(src[d * stride], g.width[d], g.top[d]);
+        double delta = 0.0;
+        if (d == dim || (int32_t)floor(t) != cr[d]) {
+            delta = t - (double)(cr[d] + 1);
+            if (delta < 0.0) delta += (double)g.grid[d];
+        }
+        const double dist = delta * g.width[d];
+        dist2 += dist * dist;
+    }
+    return dist2 < g.rc2;
+}
+
 // Selection of pulse p for domain D = blockIdx.x. Candidates in ascending
 // local slot: the home slots and every region received so far (k == 0), or
 // the region of the previous pulse (k > 0). A candidate is sent when its
 // atom's original position lies less than reach above the receiver's upper
-// face. WRITE == false: store the send count and how many candidates were
+// face and, with the corner selection, its Euclidean distance to the
+// receiver's box is below the cutoff. WRITE == false: store the send count and how many candidates were
 // home slots; WRITE == true: store the indexMap (local slots) and the sent
 // atoms' coordinates (entry_c, one row of `cap` per dimension) from map_off
 // on, in candidate order.
@@ -305,14 +330,9 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     __syncthreads();
     const int32_t total = zbeg[nz];
     const int32_t R = send_to[p * n_dom + D];
-    int32_t c_r;  // receiver's cell index along dim
-    if (dim == 0)
-        c_r = R % g.grid[0];
-    else if (dim == 1)
-        c_r = (R / g.grid[0]) % g.grid[1];
-    else
-        c_r = R / (g.grid[0] * g.grid[1]);
-    const double face = (double)(c_r + 1);
+    const int32_t cr[3] = {R % g.grid[0], (R / g.grid[0]) % g.grid[1],
+                           R / (g.grid[0] * g.grid[1])};  // receiver's cell
+    const double face = (double)(cr[dim] + 1);
     const double ncell = (double)g.grid[dim];
     const int32_t out0 = WRITE ? seg.row(p, kMapOff)[D] : 0;
     const int32_t limit = WRITE ? seg.row(p, kSendSize)[D] : 0;
@@ -350,6 +370,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
                 double above = scaled(v[j], g.width[dim], g.top[dim]) - face;
                 if (above < 0.0) above += ncell;
                 flag = above < reach;
+                if (flag && g.corner) flag = corner_test(src[j], stride[j], dim, cr, g);
             }
             if (!WRITE) {
                 // sends from home slots (the depOffset split)
@@ -653,15 +674,15 @@ void free_device_build(halo_plan *pl)
 }
 
 int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const float *box,
-                      const int32_t *grid, float cutoff, int32_t item_entries, hipStream_t st,
-                      std::string &msg)
+                      const int32_t *grid, float cutoff, int32_t selection, int32_t item_entries,
+                      hipStream_t st, std::string &msg)
 {
     if (n_atoms < 0 || !box || !grid || (n_atoms > 0 && !pos)) {
         msg = "halo_plan_create_device: NULL pointer or negative atom count";
         return kErrArg;
     }
     HostPlan &P = pl->h;
-    int rc = plan_geometry(n_atoms, box, grid, cutoff, P, msg);
+    int rc = plan_geometry(n_atoms, box, grid, cutoff, selection, P, msg);
     if (rc != kOk) return rc;
     if (P.n_dom > kMaxDeviceDomains) {
         msg = "halo_plan_create_device: at most " + std::to_string(kMaxDeviceDomains) +
@@ -683,6 +704,8 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         g.box[d] = box[d];
         g.grid[d] = grid[d];
     }
+    g.rc2 = (double)cutoff * (double)cutoff;
+    g.corner = selection == kSelectCorner ? 1 : 0;
     hipError_t e = hipSuccess;
     auto hip_err = [&](const char *what) {
         msg = std::string("halo_plan_create_device: ") + what + ": " + hipGetErrorString(e);

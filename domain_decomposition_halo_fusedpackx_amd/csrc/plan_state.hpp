@@ -88,7 +88,7 @@ void free_device_build(halo_plan *p);
 // (plan_device.hip), reusing p's arenas from an earlier device build.
 // Returns a status code and a message on failure.
 int build_plan_device(halo_plan *p, const float *pos, int64_t n_atoms, const float *box,
-                      const int32_t *grid, float cutoff, int32_t item_entries, hipStream_t stream,
-                      std::string &msg);
+                      const int32_t *grid, float cutoff, int32_t selection, int32_t item_entries,
+                      hipStream_t stream, std::string &msg);
 
 }  // namespace halo

@@ -77,6 +77,33 @@ typedef enum {
 halo_status halo_plan_create(const float *positions, int64_t n_atoms, const float *box,
                              const int32_t *grid, float cutoff, halo_plan **out);
 
+/* Halo selection tests. The pages define the halo as the atoms within the
+ * cutoff of a domain ("Redesigning GROMACS Halo Exchange", s.3), without
+ * spelling out the per-pulse test; this library offers two readings:
+ *   HALO_SELECT_SLAB   : the per-dimension slab test above (the default of
+ *                        halo_plan_create); edge and corner zones of the
+ *                        eighth shell are full boxes;
+ *   HALO_SELECT_CORNER : the slab test and, in addition, the atom's Euclidean
+ *                        distance to the receiver's box below the cutoff:
+ *                        sum_d (delta_d * w_d)^2 < cutoff^2 in double over
+ *                        d = x, y, z in this order, delta_d = 0 where the
+ *                        atom's cell equals the receiver's along d (d other
+ *                        than the pulse's dimension), else its distance in
+ *                        units of w_d above the receiver's upper face as in
+ *                        the slab test. It trims the edge and corner zones to
+ *                        their rounded shape (about 5% fewer halo slots on an
+ *                        8x8x8 grid at cutoff/w = 0.66). Distances only grow
+ *                        along a forwarding path, so the set equals the
+ *                        direct definition for the final receiver. */
+typedef enum { HALO_SELECT_SLAB = 0, HALO_SELECT_CORNER = 1 } halo_selection;
+
+/* halo_plan_create with a selection test (a halo_selection value; anything
+ * else gives HALO_ERR_ARG). halo_plan_create is this call with
+ * HALO_SELECT_SLAB. */
+halo_status halo_plan_create_ex(const float *positions, int64_t n_atoms, const float *box,
+                                const int32_t *grid, float cutoff, int32_t selection,
+                                halo_plan **out);
+
 /* Build the same plan on the GPU from device-resident positions, for
  * repartitioning steps of a GPU-resident simulation (the pages rebuild the
  * halo metadata at every domain-decomposition / neighbour-search step; see
@@ -96,8 +123,13 @@ halo_status halo_plan_create_device(const float *positions, int64_t n_atoms, con
                                     const int32_t *grid, float cutoff, void *stream,
                                     halo_plan **out);
 
+/* halo_plan_create_device with a selection test, as halo_plan_create_ex. */
+halo_status halo_plan_create_device_ex(const float *positions, int64_t n_atoms, const float *box,
+                                       const int32_t *grid, float cutoff, int32_t selection,
+                                       void *stream, halo_plan **out);
+
 /* Rebuild an existing plan on the GPU for new positions (a repartitioning
- * step), keeping its domain grid and cutoff; `box` may change (pressure
+ * step), keeping its domain grid, cutoff and selection test; `box` may change (pressure
  * coupling). The result is the plan halo_plan_create_device would build, and
  * a plan built on the device keeps its device memory (grown only when the new
  * plan needs more), so a rebuild allocates nothing in the steady state.
@@ -126,6 +158,7 @@ int32_t halo_plan_num_domains(const halo_plan *plan);  /* nx*ny*nz; -1 on NULL  
 int32_t halo_plan_num_pulses(const halo_plan *plan);   /* np(x)+np(y)+np(z); -1 on NULL */
 int64_t halo_plan_num_entries(const halo_plan *plan);  /* indexMap entries, all pulses */
 int32_t halo_plan_num_items(const halo_plan *plan);    /* work items (workgroups) per exchange */
+int32_t halo_plan_selection(const halo_plan *plan);    /* a halo_selection value; -1 on NULL */
 
 /* Dimension (0 = x, 1 = y, 2 = z) and number within that dimension of pulse p. */
 halo_status halo_plan_pulse_dim(const halo_plan *plan, int32_t p, int32_t *dim, int32_t *k);

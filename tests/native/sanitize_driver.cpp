@@ -1,6 +1,7 @@
 // Host-code check under AddressSanitizer and UndefinedBehaviorSanitizer: the
 // library's host plan builder (plan.cpp, items and chunks included) and the
-// serial C oracle run on small boxes, and their PulseData are compared. Built
+// serial C oracle run on small boxes with both selection tests, and their
+// PulseData are compared. Built
 // and run by tests/test_host_sanitizers.py; exits non-zero on a mismatch, and
 // the sanitizers abort on any memory or UB error.
 #include <cmath>
@@ -13,8 +14,8 @@
 
 extern "C" {
 struct oracle;
-int oracle_build(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,
-                 float cutoff, oracle **out);
+int oracle_build_ex(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,
+                    float cutoff, int32_t criterion, oracle **out);
 void oracle_free(oracle *o);
 int64_t oracle_total_slots(const oracle *o);
 int oracle_pulse(const oracle *o, int32_t p, int32_t d, int32_t *send_to, int32_t *send_size,
@@ -42,7 +43,7 @@ struct Case {
     int64_t n;
 };
 
-int run(const Case &c, uint64_t seed)
+int run(const Case &c, uint64_t seed, int32_t selection)
 {
     std::vector<float> pos(3 * (size_t)c.n);
     uint64_t s = seed;
@@ -55,9 +56,9 @@ int run(const Case &c, uint64_t seed)
         }
     halo::HostPlan P;
     std::string msg;
-    int rc = halo::build_plan(pos.data(), c.n, c.box, c.grid, c.cutoff, 64, P, msg);
+    int rc = halo::build_plan(pos.data(), c.n, c.box, c.grid, c.cutoff, selection, 64, P, msg);
     oracle *o = nullptr;
-    int orc = oracle_build(pos.data(), c.n, c.box, c.grid, c.cutoff, &o);
+    int orc = oracle_build_ex(pos.data(), c.n, c.box, c.grid, c.cutoff, selection, &o);
     if (rc != orc) {
         std::printf("status differs: plan %d oracle %d (%s)\n", rc, orc, msg.c_str());
         oracle_free(o);
@@ -105,7 +106,9 @@ int main()
     };
     int fails = 0;
     for (const Case &c : cases)
-        for (uint64_t seed = 1; seed <= 2; ++seed) fails += run(c, seed);
+        for (uint64_t seed = 1; seed <= 2; ++seed)
+            for (int32_t sel = halo::kSelectSlab; sel <= halo::kSelectCorner; ++sel)
+                fails += run(c, seed, sel);
     std::printf("%d case(s) differ\n", fails);
     return fails ? 1 : 0;
 }

@@ -55,6 +55,12 @@ def test_create_errors_are_synchronous_and_clean():
     assert lib.halo_plan_create(P(pos), 4, P(box), P(grid), 1.5, ctypes.byref(h)) == -2
     assert b"pulses" in lib.halo_last_error()
     assert lib.halo_plan_create(P(pos), 4, P(box), P(grid), -1.0, ctypes.byref(h)) == -2
+    for bad_sel in (-1, 2):
+        assert lib.halo_plan_create_ex(P(pos), 4, P(box), P(grid), 0.5, bad_sel,
+                                       ctypes.byref(h)) == -1
+        assert b"selection" in lib.halo_last_error()
+    assert h.value is None
+    assert lib.halo_plan_selection(None) == -1
     pos[2, 0] = 2.0
     assert lib.halo_plan_create(P(pos), 4, P(box), P(grid), 0.5, ctypes.byref(h)) == -3
     assert h.value is None

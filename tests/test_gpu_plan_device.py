@@ -19,17 +19,18 @@ from .test_plan_host import compare_plans
 pytestmark = pytest.mark.gpu
 
 
-def device_plan(torch, pos, box, grid, rc):
+def device_plan(torch, pos, box, grid, rc, selection="slab"):
     t = torch.from_numpy(np.ascontiguousarray(pos, np.float32).reshape(-1, 3)).cuda()
-    return HaloPlan.on_device(t, box, grid, rc)
+    return HaloPlan.on_device(t, box, grid, rc, selection=selection)
 
 
-def check_same_plan(torch, oracle_mod, pos, box, grid, rc, tag):
-    say(f"{tag}: device plan build")
-    dp = device_plan(torch, pos, box, grid, rc)
-    o = oracle_mod.Oracle(pos, box, grid, rc)
+def check_same_plan(torch, oracle_mod, pos, box, grid, rc, tag, selection="slab"):
+    say(f"{tag}: device plan build ({selection})")
+    dp = device_plan(torch, pos, box, grid, rc, selection)
+    assert dp.selection == selection
+    o = oracle_mod.Oracle(pos, box, grid, rc, selection)
     compare_plans(dp, o)
-    hp = HaloPlan(pos, box, grid, rc)
+    hp = HaloPlan(pos, box, grid, rc, selection=selection)
     assert dp.num_items == hp.num_items
     for p in range(o.n_pulse):
         for d in range(o.n_dom):

@@ -63,6 +63,54 @@ def test_plan_edge_cases(oracle_mod):
         compare_plans(HaloPlan(pos, box, grid, rc), oracle_mod.Oracle(pos, box, grid, rc))
 
 
+def lattice_positions(box, step):
+    """Atoms on a regular lattice of spacing `step` (exact in float32): many
+    sit exactly on cell faces and at distances that tie with the cutoff."""
+    axes = [np.arange(0.0, b, step, dtype=np.float64) for b in box]
+    g = np.stack(np.meshgrid(*axes, indexing="ij"), axis=-1).reshape(-1, 3)
+    return g.astype(np.float32)
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_corner_plan_equals_oracle_on_workloads(oracle_mod, wid):
+    w = W.WORKLOADS[wid]
+    pos = W.workload_positions(w)
+    plan = HaloPlan(pos, w.box, w.grid, w.cutoff, selection="corner")
+    assert plan.selection == "corner"
+    o = oracle_mod.Oracle(pos, w.box, w.grid, w.cutoff, "corner")
+    compare_plans(plan, o)
+    if min(w.grid) > 1:
+        assert plan.total_slots < HaloPlan(pos, w.box, w.grid, w.cutoff).total_slots
+
+
+@pytest.mark.parametrize("case", TINY, ids=lambda c: "x".join(map(str, c[1])))
+def test_corner_plan_equals_oracle_on_tiny_boxes(oracle_mod, case):
+    box, grid, rc, n = case
+    for seed in (1, 2):
+        pos = W.positions(box, n, seed)
+        compare_plans(HaloPlan(pos, box, grid, rc, selection="corner"),
+                      oracle_mod.Oracle(pos, box, grid, rc, "corner"))
+
+
+@pytest.mark.parametrize("box,grid,rc,step", [
+    ((4.0, 4.0, 4.0), (2, 2, 2), 1.0, 0.125),
+    ((6.0, 6.0, 6.0), (3, 3, 3), 1.25, 0.25),
+    ((4.0, 4.0, 8.0), (2, 2, 4), 1.5, 0.25),
+])
+def test_plans_equal_oracle_on_lattices(oracle_mod, box, grid, rc, step):
+    pos = lattice_positions(box, step)
+    for sel in ("slab", "corner"):
+        compare_plans(HaloPlan(pos, box, grid, rc, selection=sel),
+                      oracle_mod.Oracle(pos, box, grid, rc, sel))
+
+
+def test_selection_is_checked():
+    pos = W.positions((2.0, 2.0, 2.0), 10, 1)
+    with pytest.raises(ValueError):
+        HaloPlan(pos, (2.0, 2.0, 2.0), (2, 2, 2), 0.5, selection="sphere")
+    assert HaloPlan(pos, (2.0, 2.0, 2.0), (2, 2, 2), 0.5).selection == "slab"
+
+
 @pytest.mark.parametrize("args", [
     ((2.0, 2.0, 2.0), (2, 2, 2), 1.5),
     ((2.0, 2.0, 2.0), (1, 1, 1), 0.0),
