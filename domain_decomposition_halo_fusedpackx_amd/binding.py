@@ -53,6 +53,7 @@ SIGNATURES = {
     "halo_exchange_f_pulsewise": (_st, [_vp, _vp, _vp]),
     "halo_exchange_f_atomic": (_st, [_vp, _vp, _vp]),
     "halo_exchange_x_staged": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_x_direct": (_st, [_vp, _vp, _vp]),
     "halo_exchange_f_staged": (_st, [_vp, _vp, _vp]),
     "halo_plan_sync": (_st, [_vp, _vp]),
     "halo_plan_reset": (_st, [_vp]),
@@ -326,6 +327,9 @@ class HaloPlan:
 
     def exchange_f_staged(self, f, stream=None):
         self._call("halo_exchange_f_staged", f, stream)
+
+    def exchange_x_direct(self, x, stream=None):
+        self._call("halo_exchange_x_direct", x, stream)
 
     def sync(self, stream=None):
         _check(load_library().halo_plan_sync(self._h, _stream_handle(stream)))

@@ -698,3 +698,84 @@ __global__ __launch_bounds__(kThreads) void k_stage_unpack(
     for (int j = 0; j < EPT; ++j) store3<kPlain>(rf, tgt[j], cur[j] + add[j]);
 }
 
+
+// ---- direct coordinate form (halo_exchange_x_direct) -----------------------
+// With every domain in one buffer, the value the forwarding chain delivers to
+// a halo slot can be gathered straight from its atom's home slot: it is the
+// home value plus the coordShift of every pulse on the atom's path. An atom
+// wraps at most once per dimension (a dimension has at most n_d - 1 pulses,
+// which start from distinct cells), so each component receives at most one
+// non-zero shift and one IEEE add per component gives the chain's bits (the
+// zero adds change nothing but -0 into +0, which both forms do on their first
+// add). origin[e] = home slot of entry e's atom | wrap bits << kOriginShift
+// (bit d: +L_d); slots stay below 2^28.
+constexpr uint32_t kOriginShift = 28;
+constexpr uint32_t kOriginSlot = (1u << kOriginShift) - 1u;
+
+// slot_origin[s] = s for every slot (home slots are their own origin; halo
+// slots are overwritten pulse by pulse before anything reads them).
+__global__ __launch_bounds__(kThreads) void k_origin_init(uint32_t *__restrict__ slot_origin,
+                                                          int32_t n_slots)
+{
+    const int32_t s = (int32_t)(blockIdx.x * kThreads + threadIdx.x);
+    if (s < n_slots) slot_origin[s] = (uint32_t)s;
+}
+
+// One pulse's items: each entry takes the origin of the slot it reads plus
+// the segment's wrap bit and passes it on to the slot it fills. A pulse reads
+// only slots filled before it, so one launch per pulse in stream order is
+// race-free.
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_origin_pulse(const int32_t *__restrict__ idx,
+                                                           const WorkItem *__restrict__ items,
+                                                           int32_t item_base,
+                                                           uint32_t *__restrict__ slot_origin,
+                                                           uint32_t *__restrict__ origin)
+{
+    const WorkItem *it = items + item_base + blockIdx.x;
+    const uint32_t bits = (it->shift[0] != 0.f ? 1u : 0u) | (it->shift[1] != 0.f ? 2u : 0u) |
+                          (it->shift[2] != 0.f ? 4u : 0u);
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        if (e < it->n_total) {
+            const uint32_t o = slot_origin[idx[it->map_begin + e]] | (bits << kOriginShift);
+            origin[it->map_begin + e] = o;
+            slot_origin[it->region_begin + e] = o;
+        }
+    }
+}
+
+// x[region_begin + e] = x[origin slot] + (L_d where the wrap bit d is set,
+// else 0), every item independently: no waits, no counters, one launch.
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_gather_x(float *x, uint32_t x_bytes,
+                                                       const uint32_t *origin,
+                                                       uint32_t origin_bytes,
+                                                       const WorkItem *__restrict__ items,
+                                                       float lx, float ly, float lz)
+{
+    const WorkItem *it = items + blockIdx.x;
+    const auto rx = make_rsrc(x, x_bytes), ro = make_rsrc(origin, origin_bytes);
+    const int32_t n = it->n_total;
+    uint32_t o[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        o[j] = __builtin_amdgcn_raw_buffer_load_b32(
+            ro, e < n ? (uint32_t)(it->map_begin + e) * 4u : kInvalid, 0, kStream);
+    }
+    f3v v[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        v[j] = load3<kPlain>(rx, e < n ? (o[j] & kOriginSlot) * 12u : kInvalid);
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        const uint32_t b = o[j] >> kOriginShift;
+        const f3v s = {(b & 1u) ? lx : 0.f, (b & 2u) ? ly : 0.f, (b & 4u) ? lz : 0.f};
+        store3<kStream>(rx, e < n ? (uint32_t)(it->region_begin + e) * 12u : kInvalid, v[j] + s);
+    }
+}

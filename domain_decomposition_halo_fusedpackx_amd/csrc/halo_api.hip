@@ -53,7 +53,7 @@ void free_device(halo_plan *p)
                     (void *)p->d_state, (void *)p->d_mask, (void *)p->d_chunks,
                     (void *)p->d_forder, (void *)p->d_dest_start, (void *)p->d_shift4,
                     (void *)p->d_x_arrivals, (void *)p->d_zone_chunks, (void *)p->d_local_map,
-                    (void *)p->d_home_slot, (void *)p->d_stress})
+                    (void *)p->d_home_slot, (void *)p->d_stress, (void *)p->d_origin})
         if (q) (void)hipFree(q);
     if (p->h_err) (void)hipHostFree(p->h_err);
     p->d_idx = p->d_recv_from = p->d_send_to = p->d_forder = p->d_dest_start = nullptr;
@@ -63,6 +63,7 @@ void free_device(halo_plan *p)
     p->d_home_slot = nullptr;
     p->d_items = nullptr;
     p->d_stage = p->d_shift4 = nullptr;
+    p->d_origin = nullptr;
     p->d_seg_items = p->d_state = p->d_x_arrivals = p->d_zone_chunks = nullptr;
     p->d_mask = nullptr;
     p->d_chunks = nullptr;
@@ -92,7 +93,7 @@ int ept_for(int32_t item_entries)
 // Kernel entry points for the plan's items-per-thread.
 struct Kernels {
     const void *pack_fused, *unpack_fused, *pack_pulse, *unpack_pulse, *push_x, *pull_f,
-        *unpack_atomic, *stage_pack, *stage_move, *stage_unpack;
+        *unpack_atomic, *stage_pack, *stage_move, *stage_unpack, *origin_pulse, *gather_x;
 };
 
 template <int EPT>
@@ -102,7 +103,8 @@ Kernels kernels_for()
             (const void *)&k_pack_pulse<EPT>,    (const void *)&k_unpack_pulse<EPT>,
             (const void *)&k_push_x<EPT>,        (const void *)&k_pull_f<EPT>,
             (const void *)&k_unpack_atomic<EPT>, (const void *)&k_stage_pack<EPT>,
-            (const void *)&k_stage_move<EPT>,    (const void *)&k_stage_unpack<EPT>};
+            (const void *)&k_stage_move<EPT>,    (const void *)&k_stage_unpack<EPT>,
+            (const void *)&k_origin_pulse<EPT>,  (const void *)&k_gather_x<EPT>};
 }
 
 Kernels kernels(int32_t item_entries)
@@ -420,9 +422,11 @@ halo_status halo_plan_rebuild_device(halo_plan *p, const float *positions, int64
     }
     if (!p->built_on_device) {
         free_device(p);  // the host-built device copy is replaced
-    } else if (p->d_stage) {
-        (void)hipFree(p->d_stage);
+    } else {
+        if (p->d_stage) (void)hipFree(p->d_stage);
+        if (p->d_origin) (void)hipFree(p->d_origin);
         p->d_stage = nullptr;
+        p->d_origin = nullptr;
     }
     p->uploaded = false;
     std::string msg;
@@ -704,6 +708,59 @@ static halo_status exchange_staged(halo_plan *p, bool force_dir, float *buf, voi
         if (e != hipSuccess) return hip_fail(e, what);
     }
     return HALO_OK;
+}
+
+static_assert(halo::kMaxSlots <= (int64_t)kOriginSlot, "origin slots need 28 bits");
+
+halo_status halo_exchange_x_direct(halo_plan *p, float *x, void *stream)
+{
+    const char *what = "halo_exchange_x_direct";
+    halo_status st = check_exchange(p, x, what);
+    if (st != HALO_OK) return st;
+    const halo::HostPlan &h = p->h;
+    if (h.total_slots == 0 || h.n_entries == 0) return HALO_OK;
+    const hipStream_t s = (hipStream_t)stream;
+    const Kernels k = kernels(h.item_entries);
+    hipError_t e;
+    if (!p->d_origin) {
+        // first call: derive the origin map from the indexMaps, pulse by pulse
+        if ((st = refuse_capture(s, what)) != HALO_OK) return st;
+        uint32_t *slot_origin = nullptr;
+        if ((e = hipMalloc((void **)&p->d_origin, h.n_entries * 4)) != hipSuccess) {
+            p->d_origin = nullptr;
+            return hip_fail(e, what);
+        }
+        if ((e = hipMalloc((void **)&slot_origin, h.total_slots * 4)) != hipSuccess) {
+            (void)hipFree(p->d_origin);
+            p->d_origin = nullptr;
+            return hip_fail(e, what);
+        }
+        int32_t n_slots = (int32_t)h.total_slots;
+        void *a0[] = {&slot_origin, &n_slots};
+        e = hipLaunchKernel((const void *)&k_origin_init,
+                            dim3((uint32_t)((h.total_slots + kThreads - 1) / kThreads)),
+                            dim3(kThreads), a0, 0, s);
+        for (int32_t q = 0; q < h.n_pulse && e == hipSuccess; ++q) {
+            int32_t base = h.pulse_item_off[q];
+            const uint32_t n = (uint32_t)(h.pulse_item_off[q + 1] - base);
+            if (n == 0) continue;
+            void *a1[] = {&p->d_idx, &p->d_items, &base, &slot_origin, &p->d_origin};
+            e = hipLaunchKernel(k.origin_pulse, dim3(n), dim3(kThreads), a1, 0, s);
+        }
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        (void)hipFree(slot_origin);
+        if (e != hipSuccess) {
+            (void)hipFree(p->d_origin);
+            p->d_origin = nullptr;
+            return hip_fail(e, what);
+        }
+    }
+    uint32_t bytes = (uint32_t)(h.total_slots * 12);
+    uint32_t obytes = (uint32_t)(h.n_entries * 4);
+    float lx = h.box[0], ly = h.box[1], lz = h.box[2];
+    void *args[] = {&x, &bytes, &p->d_origin, &obytes, &p->d_items, &lx, &ly, &lz};
+    e = hipLaunchKernel(k.gather_x, dim3((uint32_t)h.items.size()), dim3(kThreads), args, 0, s);
+    return e == hipSuccess ? HALO_OK : hip_fail(e, what);
 }
 
 halo_status halo_exchange_x_staged(halo_plan *p, float *x, void *stream)

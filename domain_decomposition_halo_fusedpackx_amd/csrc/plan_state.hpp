@@ -61,6 +61,7 @@ struct halo_plan {
     uint32_t *d_zone_chunks = nullptr;
     // staged baseline: one float triple per indexMap entry, allocated on first use
     float *d_stage = nullptr;
+    uint32_t *d_origin = nullptr;  // direct form: home slot | wrap bits per entry (lazy)
     // device-built plans: local-slot indexMap and home slot of every atom
     int32_t *d_local_map = nullptr;
     int64_t *d_home_slot = nullptr;

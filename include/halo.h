@@ -285,6 +285,23 @@ halo_status halo_exchange_f_atomic(halo_plan *plan, float *f, void *stream);
 halo_status halo_exchange_x_staged(halo_plan *plan, float *x, void *stream);
 halo_status halo_exchange_f_staged(halo_plan *plan, float *f, void *stream);
 
+/* Direct coordinate exchange, a one-GPU form of the same result: every halo
+ * slot is gathered straight from its atom's home slot, adding +L_d for each
+ * dimension in which the atom's forwarding path wraps, in one launch with no
+ * waits and no counters. Because an atom wraps at most once per dimension,
+ * one add per component gives the bits of the pulse-by-pulse chain
+ * (x[indexMap[i]] + coordShift per pulse), so results are bitwise identical to
+ * halo_exchange_x. The forwarding of the pages ("Redesigning GROMACS Halo
+ * Exchange", Algorithm 4) is what a decomposition over several GPUs needs;
+ * on one GPU it is a choice, and this form measures what it costs.
+ * The first call on a plan derives the origin map (num_entries * 4 bytes,
+ * plus total_slots * 4 bytes of temporary memory) from the indexMaps and
+ * synchronises `stream`; it refuses a capturing stream (HALO_ERR_ARG) and
+ * reports HALO_ERR_HIP if an allocation fails. Later calls are one
+ * asynchronous launch and can be captured into a HIP graph. A rebuild
+ * discards the map. Same arguments as halo_exchange_x. */
+halo_status halo_exchange_x_direct(halo_plan *plan, float *x, void *stream);
+
 /* Wait for the plan's work on `stream` and report a timeout raised inside a
  * kernel (HALO_ERR_TIMEOUT); poisons the plan in that case. */
 halo_status halo_plan_sync(halo_plan *plan, void *stream);

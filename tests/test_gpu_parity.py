@@ -54,16 +54,19 @@ def setup_case(oracle_mod, pos, box, grid, rc):
     return plan, o
 
 
-IMPLS = ["fused", "indexmap", "transposed", "pulsewise", "staged"]
+IMPLS = ["fused", "indexmap", "transposed", "pulsewise", "staged", "direct"]
 
 
 def exchange(plan, impl, direction, buf, stream=None):
     if impl == "transposed" and plan.num_pulses > 8:
         impl = "indexmap"  # the transposed form refuses plans with more than 8 pulses
+    if impl == "direct" and direction == "f":
+        impl = "fused"  # the direct form exists for coordinates only
     name = {"fused": "exchange_{}", "indexmap": "exchange_{}_indexmap",
             "transposed": "exchange_{}_transposed",
             "pulsewise": "exchange_{}_pulsewise",
-            "staged": "exchange_{}_staged"}[impl].format(direction)
+            "staged": "exchange_{}_staged",
+            "direct": "exchange_{}_direct"}[impl].format(direction)
     getattr(plan, name)(buf, stream)
 
 
@@ -299,6 +302,58 @@ def test_fused_refuses_graph_capture_pulsewise_replays(torch, oracle_mod):
         plan.exchange_x(x)  # eager fused exchange between the replays
         torch.cuda.synchronize()
         assert_bitwise(x.cpu().numpy(), want, f"eager after replay {r}")
+    plan.sync()
+
+
+def test_direct_form_capture(torch, oracle_mod):
+    """The direct form's first call derives its origin map and refuses a
+    capturing stream; afterwards it is one launch that a graph replays
+    exactly, with eager work between the replays."""
+    w = W.WORKLOADS[4]
+    pos = W.workload_positions(w)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    plan.upload()
+    x0 = o.home_filled(np.nan)
+    want = o.exchange_x(x0.copy())
+    x = torch.from_numpy(x0.copy()).cuda()
+    dummy = torch.zeros(4, device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    say("direct form: first call under capture is refused")
+    g0 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        g0.capture_begin()
+        try:
+            with pytest.raises(HaloError) as e:
+                plan.exchange_x_direct(x, s)
+            assert e.value.code == -1
+            dummy.add_(1.0)
+        finally:
+            g0.capture_end()
+    torch.cuda.synchronize()
+    plan.exchange_x_direct(x)
+    torch.cuda.synchronize()
+    assert_bitwise(x.cpu().numpy(), want, "direct, first call")
+    say("direct form: captured and replayed")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        try:
+            plan.exchange_x_direct(x, s)
+            dummy.add_(1.0)
+        finally:
+            g.capture_end()
+    torch.cuda.synchronize()
+    for r in range(3):
+        x.copy_(torch.from_numpy(x0))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bitwise(x.cpu().numpy(), want, f"direct replay {r}")
+        x.copy_(torch.from_numpy(x0))
+        plan.exchange_x(x)  # eager fused exchange between the replays
+        torch.cuda.synchronize()
+        assert_bitwise(x.cpu().numpy(), want, f"eager after direct replay {r}")
     plan.sync()
 
 

@@ -147,13 +147,17 @@ def test_rebuild_in_place(torch, oracle_mod):
         x0 = o.home_filled(np.nan)
         x = torch.from_numpy(x0.copy()).cuda()
         dp.exchange_x(x)
+        xd = torch.from_numpy(x0.copy()).cuda()
+        dp.exchange_x_direct(xd)  # its origin map is derived again after every rebuild
         base, n_home, n_halo = o.domains()
         f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, seed)
         f = torch.from_numpy(f0.copy()).cuda()
         dp.exchange_f(f)
         torch.cuda.synchronize()
         dp.sync()
-        assert_bitwise(x.cpu().numpy(), o.exchange_x(x0.copy()), f"rebuild {n} x")
+        want_x = o.exchange_x(x0.copy())
+        assert_bitwise(x.cpu().numpy(), want_x, f"rebuild {n} x")
+        assert_bitwise(xd.cpu().numpy(), want_x, f"rebuild {n} x direct")
         assert_bitwise(f.cpu().numpy(), o.exchange_f(f0.copy()), f"rebuild {n} f")
 
 
