@@ -28,9 +28,11 @@ def test_plan_builder_and_oracle_under_sanitizers(tmp_path):
                            "-I", CSRC, os.path.join(ROOT, "tests", "native", "sanitize_driver.cpp"),
                            os.path.join(CSRC, "plan.cpp"), os.path.join(d, "oracle.o"),
                            "-o", os.path.join(d, "driver"), "-lm"])
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
+    # verify_asan_link_order=0: the environment may preload a library ahead of
+    # the ASan runtime; the driver is left to run with it
+    env = dict(os.environ,
+               ASAN_OPTIONS="detect_leaks=1:abort_on_error=1:verify_asan_link_order=0",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
-    env.pop("LD_PRELOAD", None)
     r = subprocess.run([os.path.join(d, "driver")], capture_output=True, text=True, env=env,
                        timeout=300)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
