@@ -1,0 +1,224 @@
+/* The C ABI from plain C, with no Python and no torch: HIP memory and a HIP
+ * stream of the caller's own, plans built on the host and on the device, every
+ * exchange form, compared bit for bit with the serial C oracle (test
+ * infrastructure, linked only into this test program). Built by
+ * __graft_entry__.build() and run by tests/test_gpu_c_abi.py on a GPU; exits
+ * non-zero on the first difference or unexpected status.
+ */
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "halo.h"
+
+typedef struct oracle oracle;
+int oracle_build_ex(const float *pos, int64_t n_atoms, const float *box, const int32_t *grid,
+                    float cutoff, int32_t criterion, oracle **out);
+void oracle_free(oracle *o);
+int64_t oracle_total_slots(const oracle *o);
+int oracle_home_slots(const oracle *o, int64_t *slot_of_atom);
+int oracle_exchange_x(const oracle *o, float *x);
+int oracle_exchange_f(const oracle *o, float *f);
+
+#define CHECK_HIP(call)                                                                  \
+    do {                                                                                 \
+        hipError_t e_ = (call);                                                          \
+        if (e_ != hipSuccess) {                                                          \
+            printf("HIP error %s at %s:%d\n", hipGetErrorString(e_), __FILE__, __LINE__); \
+            exit(2);                                                                     \
+        }                                                                                \
+    } while (0)
+
+#define CHECK_HALO(call)                                                                  \
+    do {                                                                                  \
+        halo_status s_ = (call);                                                          \
+        if (s_ != HALO_OK) {                                                              \
+            printf("halo status %d (%s) at %s:%d\n", (int)s_, halo_last_error(), __FILE__, \
+                   __LINE__);                                                             \
+            exit(3);                                                                      \
+        }                                                                                 \
+    } while (0)
+
+/* splitmix64: reproducible inputs without a library generator */
+static uint64_t next_u64(uint64_t *s)
+{
+    uint64_t z = (*s += 0x9e3779b97f4a7c15ull);
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+
+static double next_unit(uint64_t *s) { return (double)(next_u64(s) >> 11) * (1.0 / 9007199254740992.0); }
+
+typedef struct {
+    float box[3];
+    int32_t grid[3];
+    float cutoff;
+    int64_t n;
+    int32_t selection;
+} Case;
+
+typedef halo_status (*exchange_fn)(halo_plan *, float *, void *);
+
+static int same_bits(const float *a, const float *b, int64_t n, const char *what)
+{
+    if (n == 0 || memcmp(a, b, (size_t)n * sizeof(float)) == 0) return 1;
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u, v;
+        memcpy(&u, a + i, 4);
+        memcpy(&v, b + i, 4);
+        if (u != v) {
+            printf("%s: first difference at float %lld: %.9g vs %.9g\n", what, (long long)i,
+                   (double)a[i], (double)b[i]);
+            break;
+        }
+    }
+    return 0;
+}
+
+/* Run one exchange form on a fresh copy of `init` and compare with `want`. */
+static int run_form(halo_plan *plan, exchange_fn fn, const char *name, float *dev, const float *init,
+                    const float *want, float *host, int64_t nf, hipStream_t stream)
+{
+    const size_t bytes = (size_t)nf * sizeof(float);
+    CHECK_HIP(hipMemcpyAsync(dev, init, bytes, hipMemcpyHostToDevice, stream));
+    CHECK_HALO(fn(plan, dev, stream));
+    CHECK_HIP(hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    CHECK_HALO(halo_plan_sync(plan, stream));
+    return same_bits(host, want, nf, name);
+}
+
+static int run_case(const Case *c, uint64_t seed, hipStream_t stream)
+{
+    uint64_t s = seed;
+    const int64_t n = c->n;
+    float *pos = (float *)malloc((size_t)(3 * n + 1) * sizeof(float));
+    for (int64_t a = 0; a < n; ++a)
+        for (int d = 0; d < 3; ++d) {
+            float v = (float)(next_unit(&s) * c->box[d]);
+            if (!(v < c->box[d])) v = nextafterf(c->box[d], 0.f);
+            pos[3 * a + d] = v;
+        }
+
+    oracle *o = NULL;
+    if (oracle_build_ex(pos, n, c->box, c->grid, c->cutoff, c->selection, &o) != 0) {
+        printf("oracle build failed\n");
+        exit(4);
+    }
+    halo_plan *hp = NULL, *dp = NULL;
+    CHECK_HALO(halo_plan_create_ex(pos, n, c->box, c->grid, c->cutoff, c->selection, &hp));
+    float *pos_dev = NULL;
+    CHECK_HIP(hipMalloc((void **)&pos_dev, (size_t)(3 * n + 1) * sizeof(float)));
+    CHECK_HIP(hipMemcpy(pos_dev, pos, (size_t)(3 * n) * sizeof(float), hipMemcpyHostToDevice));
+    CHECK_HALO(halo_plan_create_device_ex(n ? pos_dev : NULL, n, c->box, c->grid, c->cutoff,
+                                          c->selection, stream, &dp));
+
+    const int64_t slots = oracle_total_slots(o);
+    int ok = halo_plan_total_slots(hp) == slots && halo_plan_total_slots(dp) == slots &&
+             halo_plan_selection(hp) == c->selection && halo_plan_selection(dp) == c->selection;
+    int64_t *hs_o = (int64_t *)malloc((size_t)(n + 1) * 8), *hs_h = (int64_t *)malloc((size_t)(n + 1) * 8),
+            *hs_d = (int64_t *)malloc((size_t)(n + 1) * 8);
+    oracle_home_slots(o, hs_o);
+    CHECK_HALO(halo_plan_home_slots(hp, hs_h));
+    CHECK_HALO(halo_plan_home_slots(dp, hs_d));
+    ok = ok && memcmp(hs_o, hs_h, (size_t)n * 8) == 0 && memcmp(hs_o, hs_d, (size_t)n * 8) == 0;
+    if (!ok) printf("plan layout differs from the oracle\n");
+
+    /* coordinates: home slots hold the positions, halo slots NaN */
+    const int64_t nf = 3 * slots;
+    float *x0 = (float *)malloc((size_t)(nf + 3) * sizeof(float));
+    float *want = (float *)malloc((size_t)(nf + 3) * sizeof(float));
+    float *host = (float *)malloc((size_t)(nf + 3) * sizeof(float));
+    for (int64_t i = 0; i < nf; ++i) x0[i] = NAN;
+    for (int64_t a = 0; a < n; ++a)
+        for (int d = 0; d < 3; ++d) x0[3 * hs_o[a] + d] = pos[3 * a + d];
+    memcpy(want, x0, (size_t)nf * sizeof(float));
+    oracle_exchange_x(o, want);
+    float *dev = NULL;
+    CHECK_HIP(hipMalloc((void **)&dev, (size_t)(nf + 3) * sizeof(float)));
+
+    const int32_t pulses = halo_plan_num_pulses(hp);
+    struct {
+        exchange_fn fn;
+        const char *name;
+    } xf[] = {{halo_exchange_x, "x"},
+              {halo_exchange_x_indexmap, "x_indexmap"},
+              {halo_exchange_x_transposed, "x_transposed"},
+              {halo_exchange_x_pulsewise, "x_pulsewise"},
+              {halo_exchange_x_staged, "x_staged"},
+              {halo_exchange_x_direct, "x_direct"}},
+      ff[] = {{halo_exchange_f, "f"},
+              {halo_exchange_f_indexmap, "f_indexmap"},
+              {halo_exchange_f_transposed, "f_transposed"},
+              {halo_exchange_f_pulsewise, "f_pulsewise"},
+              {halo_exchange_f_staged, "f_staged"},
+              {halo_exchange_f_atomic, "f_atomic"}};
+    halo_plan *plans[2] = {hp, dp};
+    for (int k = 0; k < 2 && ok; ++k)
+        for (size_t i = 0; i < sizeof(xf) / sizeof(xf[0]) && ok; ++i) {
+            if (xf[i].fn == halo_exchange_x_transposed && pulses > 8) continue;
+            ok = run_form(plans[k], xf[i].fn, xf[i].name, dev, x0, want, host, nf, stream);
+        }
+
+    /* forces: small integers on halo slots, 0 on home slots, so that every
+     * partial sum is exact and the atomic form is bitwise too */
+    for (int64_t i = 0; i < nf; ++i) x0[i] = (float)((int)(next_u64(&s) % 17u) - 8);
+    for (int64_t a = 0; a < n; ++a)
+        for (int d = 0; d < 3; ++d) x0[3 * hs_o[a] + d] = 0.f;
+    memcpy(want, x0, (size_t)nf * sizeof(float));
+    oracle_exchange_f(o, want);
+    for (int k = 0; k < 2 && ok; ++k)
+        for (size_t i = 0; i < sizeof(ff) / sizeof(ff[0]) && ok; ++i) {
+            if (ff[i].fn == halo_exchange_f_transposed && pulses > 8) continue;
+            ok = run_form(plans[k], ff[i].fn, ff[i].name, dev, x0, want, host, nf, stream);
+        }
+
+    /* an argument error is synchronous and leaves a message */
+    if (ok && slots > 0) {
+        ok = halo_exchange_x(hp, NULL, stream) == HALO_ERR_ARG && halo_last_error()[0] != '\0';
+        if (!ok) printf("NULL buffer was not refused\n");
+    }
+
+    printf("case grid %dx%dx%d n=%lld selection=%d pulses=%d slots=%lld: %s\n", c->grid[0],
+           c->grid[1], c->grid[2], (long long)n, c->selection, pulses, (long long)slots,
+           ok ? "bitwise equal" : "DIFFERS");
+    fflush(stdout);
+    CHECK_HIP(hipFree(dev));
+    CHECK_HIP(hipFree(pos_dev));
+    halo_plan_destroy(hp);
+    halo_plan_destroy(dp);
+    oracle_free(o);
+    free(pos);
+    free(hs_o);
+    free(hs_h);
+    free(hs_d);
+    free(x0);
+    free(want);
+    free(host);
+    return ok;
+}
+
+int main(void)
+{
+    const Case cases[] = {
+        {{6.f, 6.f, 6.f}, {2, 2, 2}, 1.0f, 21600, HALO_SELECT_SLAB},
+        {{8.f, 8.f, 8.f}, {4, 4, 8}, 1.2f, 51200, HALO_SELECT_SLAB},
+        {{8.f, 8.f, 8.f}, {4, 4, 8}, 1.2f, 51200, HALO_SELECT_CORNER},
+        {{6.f, 6.f, 6.f}, {3, 3, 3}, 2.5f, 20000, HALO_SELECT_CORNER},
+        {{4.f, 4.f, 4.f}, {2, 2, 2}, 1.0f, 0, HALO_SELECT_SLAB},
+    };
+    hipStream_t stream;
+    CHECK_HIP(hipSetDevice(0));
+    CHECK_HIP(hipStreamCreate(&stream));
+    int ok = 1;
+    for (size_t i = 0; i < sizeof(cases) / sizeof(cases[0]) && ok; ++i)
+        ok = run_case(&cases[i], 100 + i, stream);
+    CHECK_HIP(hipStreamDestroy(stream));
+    printf(ok ? "c_abi_driver: all cases bitwise equal to the oracle\n"
+              : "c_abi_driver: FAILED\n");
+    return ok ? 0 : 1;
+}
