@@ -224,6 +224,42 @@ def plan_build_ms(torch, HaloPlan, w, pos, reps):
     return out
 
 
+def graph_replays(torch, plans, xs, fs, steps):
+    """The default exchanges captured in HIP graphs (one graph of X over all
+    replicas, one of F, one of whole steps) and replayed: us per exchange and
+    ms per step as a graph-launched MD loop would see them. Capturing switches
+    the plans to inferring their epochs on the device, so this runs last."""
+    R = len(plans)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            g.capture_begin()
+            try:
+                fn()
+            finally:
+                g.capture_end()
+        torch.cuda.synchronize()
+        return g
+
+    gx = capture(lambda: [plans[r].exchange_x(xs[r], s) for r in range(R)])
+    gf = capture(lambda: [plans[r].exchange_f(fs[r], s) for r in range(R)])
+    gs = capture(lambda: [(plans[r].exchange_x(xs[r], s), plans[r].exchange_f(fs[r], s))
+                          for r in range(R)])
+    n = max(2, steps // R)
+    out = {}
+    for name, g in (("us_x", gx), ("us_f", gf), ("ms_per_step", gs)):
+        g.replay()
+        ms = time_loop(torch, lambda i: g.replay(), n) / R
+        out[name] = ms if name == "ms_per_step" else ms * 1e3
+    for p in plans:
+        p.sync()
+    out["exchanges_per_graph"] = R
+    return out
+
+
 def overlap(torch, plan, x, f, reps):
     """The pages' overlap measurement with a synthetic local workload.
 
@@ -500,6 +536,8 @@ def main():
         if not args.no_overlap:
             log("overlap with local work")
             out["overlap"] = overlap(torch, plans[0], xs[0], fs[0], args.overlap_reps)
+        log("graph replays")
+        out["graph"] = graph_replays(torch, plans, xs, fs, args.steps)
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

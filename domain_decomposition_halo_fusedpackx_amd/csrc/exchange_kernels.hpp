@@ -125,8 +125,9 @@ __device__ __forceinline__ void pack_item_fused_st(const WorkItem *it, __amdgpu_
                                                    __amdgpu_buffer_rsrc_t ridx,
                                                    const int32_t *recv_from,
                                                    const uint32_t *seg_items, uint32_t *state,
-                                                   int32_t n_dom, uint32_t epoch,
-                                                   uint32_t spin_limit, uint32_t *err_word)
+                                                   int32_t n_dom, const halo::LaunchGroup &lg,
+                                                   uint32_t &epoch, uint32_t spin_limit,
+                                                   uint32_t *err_word)
 {
     const int32_t n_indep = it->n_indep;
     const int32_t n_total = it->n_total;
@@ -154,15 +155,15 @@ __device__ __forceinline__ void pack_item_fused_st(const WorkItem *it, __amdgpu_
     if (n_total > n_indep) {
         // lane r of wave 0 polls the arrival of the region the sender
         // received in pulse r, if the dependent entries read it
-        const uint32_t lane = threadIdx.x & 63u, wmask = it->xwait_mask;
+        const uint32_t lane = threadIdx.x, wmask = it->xwait_mask;
         uint32_t *ctr = nullptr;
-        uint32_t target = 0;
+        uint32_t mult = 0;
         if (lane < 32u && ((wmask >> lane) & 1u)) {
             const int32_t s = (int32_t)lane * n_dom + recv_from[(int32_t)lane * n_dom + it->domain];
             ctr = halo::counter_x(state, s);
-            target = epoch * seg_items[s];
+            mult = seg_items[s];
         }
-        halo::wait_lanes(ctr, target, spin_limit, err_word);
+        halo::wait_lanes(ctr, mult, lg, epoch, spin_limit, err_word);
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
             const bool dep = (int32_t)threadIdx.x + j * kThreads >= n_indep;
@@ -181,18 +182,18 @@ __device__ __forceinline__ void pack_item_fused(const WorkItem *it, __amdgpu_buf
                                                 __amdgpu_buffer_rsrc_t ridx,
                                                 const int32_t *recv_from,
                                                 const uint32_t *seg_items, uint32_t *state,
-                                                int32_t n_dom, uint32_t epoch,
-                                                uint32_t spin_limit, uint32_t *err_word,
-                                                int32_t withhold)
+                                                int32_t n_dom, const halo::LaunchGroup &lg,
+                                                uint32_t &epoch, uint32_t spin_limit,
+                                                uint32_t *err_word, int32_t withhold)
 {
     if (it->flags & halo::kItemXStoreShared) {
-        pack_item_fused_st<EPT, kShared>(it, rx, ridx, recv_from, seg_items, state, n_dom, epoch,
-                                         spin_limit, err_word);
+        pack_item_fused_st<EPT, kShared>(it, rx, ridx, recv_from, seg_items, state, n_dom, lg,
+                                         epoch, spin_limit, err_word);
         halo::signal_done(halo::counter_x(state, it->seg), it->seg == withhold);
     } else {
         // last pulse: no later pulse forwards its region, nobody waits on it
-        pack_item_fused_st<EPT, kStream>(it, rx, ridx, recv_from, seg_items, state, n_dom, epoch,
-                                        spin_limit, err_word);
+        pack_item_fused_st<EPT, kStream>(it, rx, ridx, recv_from, seg_items, state, n_dom, lg,
+                                        epoch, spin_limit, err_word);
     }
 }
 
@@ -232,9 +233,9 @@ template <int EPT>
 __device__ __forceinline__ void unpack_item_fused(const WorkItem *it, __amdgpu_buffer_rsrc_t rf,
                                                   __amdgpu_buffer_rsrc_t ridx,
                                                   const uint32_t *seg_items, uint32_t *state,
-                                                  int32_t n_seg, uint32_t epoch,
-                                                  uint32_t spin_limit, uint32_t *err_word,
-                                                  int32_t withhold)
+                                                  int32_t n_seg, const halo::LaunchGroup &lg,
+                                                  uint32_t &epoch, uint32_t spin_limit,
+                                                  uint32_t *err_word, int32_t withhold)
 {
     const int32_t n_total = it->n_total;
     const int32_t region_begin = it->region_begin;
@@ -243,7 +244,7 @@ __device__ __forceinline__ void unpack_item_fused(const WorkItem *it, __amdgpu_b
     load_targets<EPT>(ridx, it->map_begin, n_total, tgt);
     if (it->fwait[0] >= 0) {
         const int32_t nw = it->fwait[1] >= 0 && it->fwait[1] != it->fwait[0] ? 2 : 1;
-        halo::wait_segments(it->fwait, nw, seg_items, state, n_seg, true, epoch, spin_limit,
+        halo::wait_segments(it->fwait, nw, seg_items, state, n_seg, true, lg, epoch, spin_limit,
                             err_word);
     }
     const int32_t fl = it->flags;
@@ -276,7 +277,8 @@ __device__ __forceinline__ void unpack_item_atomic(const WorkItem *it, float *f,
                                                    __amdgpu_buffer_rsrc_t rf,
                                                    __amdgpu_buffer_rsrc_t ridx,
                                                    const uint32_t *seg_items, uint32_t *state,
-                                                   int32_t n_seg, int32_t n_dom, uint32_t epoch,
+                                                   int32_t n_seg, int32_t n_dom,
+                                                   const halo::LaunchGroup &lg, uint32_t &epoch,
                                                    uint32_t spin_limit, uint32_t *err_word,
                                                    int32_t withhold)
 {
@@ -293,15 +295,15 @@ __device__ __forceinline__ void unpack_item_atomic(const WorkItem *it, float *f,
     const uint32_t amask = it->await_mask;
     if (amask) {
         // lane q of wave 0 polls segment (q, receiver)
-        const uint32_t lane = threadIdx.x & 63u;
+        const uint32_t lane = threadIdx.x;
         uint32_t *ctr = nullptr;
-        uint32_t target = 0;
+        uint32_t mult = 0;
         if (lane < 32u && ((amask >> lane) & 1u)) {
             const int32_t s = (int32_t)lane * n_dom + it->receiver;
             ctr = halo::counter_f(state, n_seg, s);
-            target = epoch * seg_items[s];
+            mult = seg_items[s];
         }
-        halo::wait_lanes(ctr, target, spin_limit, err_word);
+        halo::wait_lanes(ctr, mult, lg, epoch, spin_limit, err_word);
 #pragma unroll
         for (int j = 0; j < EPT; ++j) add[j] = load3<kShared>(rf, src[j]);
     } else {
@@ -337,13 +339,19 @@ template <int EPT>
 __global__ __launch_bounds__(kThreads) void k_pack_fused(
     float *x, uint32_t x_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
     const WorkItem *__restrict__ items, const int32_t *__restrict__ recv_from,
-    const uint32_t *__restrict__ seg_items, uint32_t *state, int32_t n_dom, uint32_t epoch,
-    uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Stress st)
+    const uint32_t *__restrict__ seg_items, uint32_t *state, int32_t n_dom, uint32_t *groups,
+    const uint32_t *__restrict__ members, uint32_t host_epoch, uint32_t spin_limit,
+    uint32_t *err_word, int32_t withhold, Stress st)
 {
     const uint32_t u = st.order ? (uint32_t)st.order[blockIdx.x] : blockIdx.x;
     if (st.seed) stress_delay(st.seed, u);
-    pack_item_fused<EPT>(items + u, make_rsrc(x, x_bytes), make_rsrc(idx, idx_bytes), recv_from,
-                         seg_items, state, n_dom, epoch, spin_limit, err_word, withhold);
+    halo::LaunchState ls = halo::launch_state(groups, members, u, host_epoch);
+    const WorkItem *it = items + u;
+    const bool member = it->n_total > it->n_indep;  // the item waits
+    halo::count_early(ls, member);
+    pack_item_fused<EPT>(it, make_rsrc(x, x_bytes), make_rsrc(idx, idx_bytes), recv_from,
+                         seg_items, state, n_dom, ls.lg, ls.epoch, spin_limit, err_word, withhold);
+    halo::count_late(ls, member);
 }
 
 // Fused force exchange: ONE launch, workgroup b takes item n_items-1-b, so
@@ -352,13 +360,18 @@ template <int EPT>
 __global__ __launch_bounds__(kThreads) void k_unpack_fused(
     float *f, uint32_t f_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
     const WorkItem *__restrict__ items, const uint32_t *__restrict__ seg_items, uint32_t *state,
-    int32_t n_seg, uint32_t n_items, uint32_t epoch, uint32_t spin_limit, uint32_t *err_word,
-    int32_t withhold, Stress st)
+    int32_t n_seg, uint32_t n_items, uint32_t *groups, const uint32_t *__restrict__ members,
+    uint32_t host_epoch, uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Stress st)
 {
     const uint32_t u = st.order ? (uint32_t)st.order[blockIdx.x] : n_items - 1u - blockIdx.x;
     if (st.seed) stress_delay(st.seed, u);
-    unpack_item_fused<EPT>(items + u, make_rsrc(f, f_bytes), make_rsrc(idx, idx_bytes), seg_items,
-                           state, n_seg, epoch, spin_limit, err_word, withhold);
+    halo::LaunchState ls = halo::launch_state(groups, members, u, host_epoch);
+    const WorkItem *it = items + u;
+    const bool member = it->fwait[0] >= 0;  // the item waits
+    halo::count_early(ls, member);
+    unpack_item_fused<EPT>(it, make_rsrc(f, f_bytes), make_rsrc(idx, idx_bytes), seg_items,
+                           state, n_seg, ls.lg, ls.epoch, spin_limit, err_word, withhold);
+    halo::count_late(ls, member);
 }
 
 // Fused force exchange with atomic adds: ONE launch, last pulse first; an item
@@ -367,13 +380,19 @@ template <int EPT>
 __global__ __launch_bounds__(kThreads) void k_unpack_atomic(
     float *f, uint32_t f_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
     const WorkItem *__restrict__ items, const uint32_t *__restrict__ seg_items, uint32_t *state,
-    int32_t n_seg, int32_t n_dom, uint32_t n_items, uint32_t epoch, uint32_t spin_limit,
+    int32_t n_seg, int32_t n_dom, uint32_t n_items, uint32_t *groups,
+    const uint32_t *__restrict__ members, uint32_t host_epoch, uint32_t spin_limit,
     uint32_t *err_word, int32_t withhold, Stress st)
 {
     const uint32_t u = st.order ? (uint32_t)st.order[blockIdx.x] : n_items - 1u - blockIdx.x;
     if (st.seed) stress_delay(st.seed, u);
+    halo::LaunchState ls = halo::launch_state(groups, members, u, host_epoch);
+    // every item is a member here (which items wait is known on the device only)
+    halo::count_early(ls, true);
     unpack_item_atomic<EPT>(items + u, f, make_rsrc(f, f_bytes), make_rsrc(idx, idx_bytes),
-                            seg_items, state, n_seg, n_dom, epoch, spin_limit, err_word, withhold);
+                            seg_items, state, n_seg, n_dom, ls.lg, ls.epoch, spin_limit, err_word,
+                            withhold);
+    halo::count_late(ls, true);
 }
 
 // ---- transposed form: per-slot pulse masks --------------------------------
@@ -441,13 +460,15 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
     float *x, uint32_t x_bytes, const uint8_t *__restrict__ slot_mask,
     const halo::Chunk *__restrict__ chunks, const int32_t *__restrict__ dest_start,
     const float4 *__restrict__ shift4, const uint32_t *__restrict__ x_arrivals, uint32_t *state,
-    int32_t n_dom, int32_t n_pulse, uint32_t epoch, uint32_t spin_limit, uint32_t *err_word,
-    int32_t withhold, Stress st)
+    int32_t n_dom, int32_t n_pulse, uint32_t *groups, const uint32_t *__restrict__ members,
+    uint32_t host_epoch, uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Stress st)
 {
     __shared__ Ranks<EPT> sh;
     const uint32_t u = st.order ? (uint32_t)st.order[blockIdx.x] : blockIdx.x;
     if (st.seed) stress_delay(st.seed, u);
+    halo::LaunchState ls = halo::launch_state(groups, members, u, host_epoch);
     const halo::Chunk *c = chunks + u;
+    halo::count_early(ls, c->zone >= 0);  // region chunks wait
     const int32_t first = c->first, count = c->count, D = c->domain;
     const uint32_t umask = c->mask;
     const auto rx = make_rsrc(x, x_bytes);
@@ -468,8 +489,8 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
     build_ranks<EPT>(sh, m, umask, n_pulse);
     if (c->zone >= 0) {
         // region slots are filled by another domain in this launch
-        halo::wait_one(c->xwait, x_arrivals, state, n_dom * n_pulse, false, epoch, spin_limit,
-                       err_word);
+        halo::wait_one(c->xwait, x_arrivals, state, n_dom * n_pulse, false, ls.lg, ls.epoch,
+                       spin_limit, err_word);
 #pragma unroll
         for (int j = 0; j < EPT; ++j) v[j] = load3<kShared>(rx, m[j] ? off[j] : kInvalid);
     }
@@ -504,6 +525,7 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
             for (int j = 0; j < EPT; ++j) store3<kStream>(rx, dst[j], v[j] + s3);
         }
     }
+    halo::count_late(ls, c->zone >= 0);
 }
 
 // Fused force exchange, transposed form (Algorithm 6): one workgroup per
@@ -518,11 +540,13 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
     const halo::Chunk *__restrict__ chunks, const int32_t *__restrict__ forder,
     const int32_t *__restrict__ dest_start, const int32_t *__restrict__ send_to,
     const uint32_t *__restrict__ zone_chunks, uint32_t *state, int32_t n_dom, int32_t n_pulse,
-    uint32_t epoch, uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Stress st)
+    uint32_t *groups, const uint32_t *__restrict__ members, uint32_t host_epoch,
+    uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Stress st)
 {
     __shared__ Ranks<EPT> sh;
     const int32_t u = st.order ? st.order[blockIdx.x] : forder[blockIdx.x];
     if (st.seed) stress_delay(st.seed, (uint32_t)u);
+    halo::LaunchState ls = halo::launch_state(groups, members, (uint32_t)u, host_epoch);
     const halo::Chunk *c = chunks + u;
     const int32_t first = c->first, count = c->count, D = c->domain, zone = c->zone;
     const uint32_t umask = c->mask;
@@ -543,12 +567,17 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
 #pragma unroll
     for (int j = 0; j < EPT; ++j) v[j] = load3<kStream>(rf, off[j]);
     build_ranks<EPT>(sh, m, umask, n_pulse);
+    bool waited = false;
     for (int32_t p = n_pulse - 1; p >= 0; --p) {
         if (!((umask >> p) & 1u)) continue;
         const int32_t R = send_to[p * n_dom + D];
         const int32_t zseg = p * n_dom + R;
-        if (zone_chunks[zseg] > 0)
-            halo::wait_one(zseg, zone_chunks, state, n_seg, true, epoch, spin_limit, err_word);
+        if (zone_chunks[zseg] > 0) {
+            halo::count_early(ls, true);  // the chunk waits
+            halo::wait_one(zseg, zone_chunks, state, n_seg, true, ls.lg, ls.epoch, spin_limit,
+                           err_word);
+            waited = true;
+        }
         const int32_t base = dest_start[p * n_dom + D] + c->rank[p];
         uint32_t src[EPT];
 #pragma unroll
@@ -587,6 +616,7 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
 #pragma unroll
         for (int j = 0; j < EPT; ++j) store3<kStream>(rf, dst[j], v[j]);
     }
+    halo::count_late(ls, waited);
 }
 
 // Per-pulse baseline: one launch per pulse, one item per workgroup, no

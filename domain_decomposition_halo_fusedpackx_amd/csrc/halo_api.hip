@@ -53,7 +53,8 @@ void free_device(halo_plan *p)
                     (void *)p->d_state, (void *)p->d_mask, (void *)p->d_chunks,
                     (void *)p->d_forder, (void *)p->d_dest_start, (void *)p->d_shift4,
                     (void *)p->d_x_arrivals, (void *)p->d_zone_chunks, (void *)p->d_local_map,
-                    (void *)p->d_home_slot, (void *)p->d_stress, (void *)p->d_origin})
+                    (void *)p->d_home_slot, (void *)p->d_stress, (void *)p->d_origin,
+                    (void *)p->d_members})
         if (q) (void)hipFree(q);
     if (p->h_err) (void)hipHostFree(p->h_err);
     p->d_idx = p->d_recv_from = p->d_send_to = p->d_forder = p->d_dest_start = nullptr;
@@ -64,6 +65,7 @@ void free_device(halo_plan *p)
     p->d_items = nullptr;
     p->d_stage = p->d_shift4 = nullptr;
     p->d_origin = nullptr;
+    p->d_members = nullptr;
     p->d_seg_items = p->d_state = p->d_x_arrivals = p->d_zone_chunks = nullptr;
     p->d_mask = nullptr;
     p->d_chunks = nullptr;
@@ -129,6 +131,32 @@ Stress stress_of(const halo_plan *p, StressOrder which)
     return Stress{p->d_stress + off[which], p->stress_seed};
 }
 
+// Launch counts of a kernel family and their group sizes (the fused kernels
+// infer their epoch from them).
+uint32_t *launch_groups(halo_plan *p, int family)
+{
+    return p->d_state + halo::launch_groups_offset(p->h.seg.size(), family);
+}
+
+const uint32_t *launch_members(halo_plan *p, int family)
+{
+    return p->d_members + (size_t)family * halo::kLaunchGroups;
+}
+
+// The epoch argument of a fused launch: the host's count for eager calls; 0
+// (inferred on the device) for calls being captured and for every call after
+// the first capture, since replays then advance the counts unseen.
+uint32_t launch_epoch_arg(halo_plan *p, int family, hipStream_t s)
+{
+    if (!p->device_epochs) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+            p->device_epochs = true;
+    }
+    if (p->device_epochs) return 0u;
+    return ++p->epochs[family];  // a wrap to 0 only asks for inference once
+}
+
 hipError_t launch_fused(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
 {
     const halo::HostPlan &h = p->h;
@@ -136,20 +164,25 @@ hipError_t launch_fused(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
     uint32_t n_items = (uint32_t)h.items.size();
     uint32_t bytes = (uint32_t)(h.total_slots * 12);
     uint32_t idx_bytes = (uint32_t)(h.n_entries * 4);
-    uint32_t epoch = force_dir ? p->epoch_f : p->epoch_x;
     const Kernels k = kernels(h.item_entries);
     if (force_dir) {
         Stress st = stress_of(p, kOrderItemsF);
+        uint32_t *groups = launch_groups(p, halo::kFamItemsF);
+        const uint32_t *members = launch_members(p, halo::kFamItemsF);
+        uint32_t epoch = launch_epoch_arg(p, halo::kFamItemsF, s);
         void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_seg_items,
-                        &p->d_state, &n_seg, &n_items, &epoch, &p->spin_limit, &p->d_err,
-                        &p->withhold, &st};
+                        &p->d_state, &n_seg, &n_items, &groups, &members, &epoch,
+                        &p->spin_limit, &p->d_err, &p->withhold, &st};
         return hipLaunchKernel(k.unpack_fused, dim3(n_items), dim3(kThreads), args, 0, s);
     }
     int32_t n_dom = h.n_dom;
     Stress st = stress_of(p, kOrderItemsX);
+    uint32_t *groups = launch_groups(p, halo::kFamItemsX);
+    const uint32_t *members = launch_members(p, halo::kFamItemsX);
+    uint32_t epoch = launch_epoch_arg(p, halo::kFamItemsX, s);
     void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_recv_from,
-                    &p->d_seg_items, &p->d_state, &n_dom, &epoch, &p->spin_limit, &p->d_err,
-                    &p->withhold, &st};
+                    &p->d_seg_items, &p->d_state, &n_dom, &groups, &members, &epoch,
+                    &p->spin_limit, &p->d_err, &p->withhold, &st};
     return hipLaunchKernel(k.pack_fused, dim3(n_items), dim3(kThreads), args, 0, s);
 }
 
@@ -163,18 +196,22 @@ hipError_t launch_chunks(halo_plan *p, bool force_dir, float *buf, hipStream_t s
     const uint32_t n = (uint32_t)h.chunks.size();
     const Kernels k = kernels(h.chunk_slots);
     if (force_dir) {
-        uint32_t epoch = p->epoch_fc;
+        uint32_t *groups = launch_groups(p, halo::kFamChunksF);
+        const uint32_t *members = launch_members(p, halo::kFamChunksF);
+        uint32_t epoch = launch_epoch_arg(p, halo::kFamChunksF, s);
         Stress st = stress_of(p, kOrderChunksF);
         void *args[] = {&buf, &bytes, &p->d_mask, &p->d_chunks, &p->d_forder, &p->d_dest_start,
-                        &p->d_send_to, &p->d_zone_chunks, &state, &n_dom, &n_pulse, &epoch,
-                        &p->spin_limit, &p->d_err, &p->withhold, &st};
+                        &p->d_send_to, &p->d_zone_chunks, &state, &n_dom, &n_pulse, &groups,
+                        &members, &epoch, &p->spin_limit, &p->d_err, &p->withhold, &st};
         return hipLaunchKernel(k.pull_f, dim3(n), dim3(kThreads), args, 0, s);
     }
-    uint32_t epoch = p->epoch_xc;
+    uint32_t *groups = launch_groups(p, halo::kFamChunksX);
+    const uint32_t *members = launch_members(p, halo::kFamChunksX);
+    uint32_t epoch = launch_epoch_arg(p, halo::kFamChunksX, s);
     Stress st = stress_of(p, kOrderChunksX);
     void *args[] = {&buf, &bytes, &p->d_mask, &p->d_chunks, &p->d_dest_start, &p->d_shift4,
-                    &p->d_x_arrivals, &state, &n_dom, &n_pulse, &epoch, &p->spin_limit,
-                    &p->d_err, &p->withhold, &st};
+                    &p->d_x_arrivals, &state, &n_dom, &n_pulse, &groups, &members, &epoch,
+                    &p->spin_limit, &p->d_err, &p->withhold, &st};
     return hipLaunchKernel(k.push_x, dim3(n), dim3(kThreads), args, 0, s);
 }
 
@@ -198,13 +235,18 @@ hipError_t launch_atomic(halo_plan *p, float *buf, hipStream_t s)
     uint32_t n_items = (uint32_t)h.items.size();
     uint32_t bytes = (uint32_t)(h.total_slots * 12);
     uint32_t idx_bytes = (uint32_t)(h.n_entries * 4);
-    uint32_t epoch = p->epoch_f;
     const Kernels k = kernels(h.item_entries);
     int32_t n_dom = h.n_dom;
     Stress st = stress_of(p, kOrderItemsF);
+    // its own counters and launch counts: which items wait differs from the
+    // ordered force kernel
+    uint32_t *state = p->d_state + halo::atomic_state_offset(h.seg.size());
+    uint32_t *groups = launch_groups(p, halo::kFamAtomicF);
+    const uint32_t *members = launch_members(p, halo::kFamAtomicF);
+    uint32_t epoch = launch_epoch_arg(p, halo::kFamAtomicF, s);
     void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_seg_items,
-                    &p->d_state, &n_seg, &n_dom, &n_items, &epoch, &p->spin_limit, &p->d_err,
-                    &p->withhold, &st};
+                    &state, &n_seg, &n_dom, &n_items, &groups, &members, &epoch,
+                    &p->spin_limit, &p->d_err, &p->withhold, &st};
     return hipLaunchKernel(k.unpack_atomic, dim3(n_items), dim3(kThreads), args, 0, s);
 }
 
@@ -245,7 +287,8 @@ halo_status ensure_uploaded(halo_plan *p)
         (e = upload_vec(&p->d_items, h.items)) != hipSuccess ||
         (e = upload_vec(&p->d_recv_from, h.recv_from)) != hipSuccess ||
         (e = upload_vec(&p->d_send_to, h.send_to)) != hipSuccess ||
-        (e = upload_vec(&p->d_seg_items, h.seg_items)) != hipSuccess) {
+        (e = upload_vec(&p->d_seg_items, h.seg_items)) != hipSuccess ||
+        (e = upload_vec(&p->d_members, h.launch_members)) != hipSuccess) {
         free_device(p);
         return hip_fail(e, "halo_plan_upload");
     }
@@ -260,8 +303,9 @@ halo_status ensure_uploaded(halo_plan *p)
         free_device(p);
         return hip_fail(e, "halo_plan_upload");
     }
-    // two counter blocks (work items, chunks), each X then F, 128 B per counter
-    p->state_words = 4 * h.seg.size() * halo::kCounterStride + halo::kCounterStride;
+    // two counter blocks (work items, chunks), each X then F, and the launch
+    // counts; 128 B per counter
+    p->state_words = halo::state_words_for(h.seg.size());
     if ((e = hipMalloc((void **)&p->d_state, p->state_words * 4)) != hipSuccess ||
         (e = hipMemset(p->d_state, 0, p->state_words * 4)) != hipSuccess ||
         (e = hipHostMalloc((void **)&p->h_err, 64, hipHostMallocMapped)) != hipSuccess ||
@@ -271,7 +315,7 @@ halo_status ensure_uploaded(halo_plan *p)
         return hip_fail(e, "halo_plan_upload");
     }
     std::memset(p->h_err, 0, 64);
-    p->epoch_x = p->epoch_f = p->epoch_xc = p->epoch_fc = 0;
+    for (uint32_t &e : p->epochs) e = 0;
     p->uploaded = true;
     return HALO_OK;
 }
@@ -282,7 +326,20 @@ int halo::plan_upload(halo_plan *p) { return ensure_uploaded(p); }
 
 namespace {
 
-halo_status check_exchange(halo_plan *p, float *buf, const char *what)
+// Calls whose first use allocates or synchronises (the upload, staging
+// buffers, origin maps) refuse a stream that is being captured.
+halo_status refuse_capture(hipStream_t stream, const char *what)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+        return fail(HALO_ERR_ARG, std::string(what) +
+                                      ": its first call on a plan allocates and synchronises, "
+                                      "so it cannot be captured; call it (or halo_plan_upload) "
+                                      "once before capturing");
+    return HALO_OK;
+}
+
+halo_status check_exchange(halo_plan *p, float *buf, const char *what, void *stream)
 {
     if (!p) return fail(HALO_ERR_ARG, std::string(what) + ": NULL plan");
     if (p->invalid)
@@ -295,23 +352,13 @@ halo_status check_exchange(halo_plan *p, float *buf, const char *what)
         return fail(HALO_ERR_STATE, std::string(what) +
                                         ": plan poisoned by an in-kernel wait timeout; call "
                                         "halo_plan_reset");
-    halo_status st = ensure_uploaded(p);
+    halo_status st;
+    if (!p->uploaded && (st = refuse_capture((hipStream_t)stream, what)) != HALO_OK) return st;
+    st = ensure_uploaded(p);
     if (st != HALO_OK) return st;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != p->device)
         return fail(HALO_ERR_ARG, std::string(what) + ": current device differs from the plan's");
-    return HALO_OK;
-}
-
-// The fused forms pass a new epoch to every launch; a captured graph would
-// replay a stale one. They refuse to run while `stream` is being captured.
-halo_status refuse_capture(hipStream_t stream, const char *what)
-{
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
-        return fail(HALO_ERR_ARG, std::string(what) +
-                                      ": cannot be captured in a graph (every call passes a new "
-                                      "epoch); use the per-pulse form there");
     return HALO_OK;
 }
 
@@ -595,61 +642,49 @@ halo_status halo_exchange_f(halo_plan *p, float *f, void *stream)
 
 halo_status halo_exchange_x_transposed(halo_plan *p, float *x, void *stream)
 {
-    halo_status st = check_exchange(p, x, "halo_exchange_x_transposed");
+    halo_status st = check_exchange(p, x, "halo_exchange_x_transposed", stream);
     if (st != HALO_OK) return st;
-    if ((st = refuse_capture((hipStream_t)stream, "halo_exchange_x_transposed")) != HALO_OK)
-        return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
     if (!p->h.has_chunks)
         return fail(HALO_ERR_ARG, "halo_exchange_x_transposed: plan has more than 8 pulses");
     if (p->h.chunks.empty()) return HALO_OK;
-    p->epoch_xc += 1;
     hipError_t e = launch_chunks(p, false, x, (hipStream_t)stream);
     return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_x_transposed launch");
 }
 
 halo_status halo_exchange_f_transposed(halo_plan *p, float *f, void *stream)
 {
-    halo_status st = check_exchange(p, f, "halo_exchange_f_transposed");
+    halo_status st = check_exchange(p, f, "halo_exchange_f_transposed", stream);
     if (st != HALO_OK) return st;
-    if ((st = refuse_capture((hipStream_t)stream, "halo_exchange_f_transposed")) != HALO_OK)
-        return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
     if (!p->h.has_chunks)
         return fail(HALO_ERR_ARG, "halo_exchange_f_transposed: plan has more than 8 pulses");
     if (p->h.chunks.empty()) return HALO_OK;
-    p->epoch_fc += 1;
     hipError_t e = launch_chunks(p, true, f, (hipStream_t)stream);
     return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_f_transposed launch");
 }
 
 halo_status halo_exchange_x_indexmap(halo_plan *p, float *x, void *stream)
 {
-    halo_status st = check_exchange(p, x, "halo_exchange_x_indexmap");
+    halo_status st = check_exchange(p, x, "halo_exchange_x_indexmap", stream);
     if (st != HALO_OK) return st;
-    if ((st = refuse_capture((hipStream_t)stream, "halo_exchange_x_indexmap")) != HALO_OK)
-        return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
-    p->epoch_x += 1;
     hipError_t e = launch_fused(p, false, x, (hipStream_t)stream);
     return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_x_indexmap launch");
 }
 
 halo_status halo_exchange_f_indexmap(halo_plan *p, float *f, void *stream)
 {
-    halo_status st = check_exchange(p, f, "halo_exchange_f_indexmap");
+    halo_status st = check_exchange(p, f, "halo_exchange_f_indexmap", stream);
     if (st != HALO_OK) return st;
-    if ((st = refuse_capture((hipStream_t)stream, "halo_exchange_f_indexmap")) != HALO_OK)
-        return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
-    p->epoch_f += 1;
     hipError_t e = launch_fused(p, true, f, (hipStream_t)stream);
     return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_f_indexmap launch");
 }
 
 halo_status halo_exchange_x_pulsewise(halo_plan *p, float *x, void *stream)
 {
-    halo_status st = check_exchange(p, x, "halo_exchange_x_pulsewise");
+    halo_status st = check_exchange(p, x, "halo_exchange_x_pulsewise", stream);
     if (st != HALO_OK) return st;
     const halo::HostPlan &h = p->h;
     if (h.total_slots == 0) return HALO_OK;
@@ -662,7 +697,7 @@ halo_status halo_exchange_x_pulsewise(halo_plan *p, float *x, void *stream)
 
 halo_status halo_exchange_f_pulsewise(halo_plan *p, float *f, void *stream)
 {
-    halo_status st = check_exchange(p, f, "halo_exchange_f_pulsewise");
+    halo_status st = check_exchange(p, f, "halo_exchange_f_pulsewise", stream);
     if (st != HALO_OK) return st;
     const halo::HostPlan &h = p->h;
     if (h.total_slots == 0) return HALO_OK;
@@ -675,14 +710,9 @@ halo_status halo_exchange_f_pulsewise(halo_plan *p, float *f, void *stream)
 
 halo_status halo_exchange_f_atomic(halo_plan *p, float *f, void *stream)
 {
-    halo_status st = check_exchange(p, f, "halo_exchange_f_atomic");
+    halo_status st = check_exchange(p, f, "halo_exchange_f_atomic", stream);
     if (st != HALO_OK) return st;
-    if ((st = refuse_capture((hipStream_t)stream, "halo_exchange_f_atomic")) != HALO_OK)
-        return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
-    // shares the index-list force counters: both kernels advance the same
-    // counters by the same counts per exchange
-    p->epoch_f += 1;
     hipError_t e = launch_atomic(p, f, (hipStream_t)stream);
     return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_f_atomic launch");
 }
@@ -690,7 +720,7 @@ halo_status halo_exchange_f_atomic(halo_plan *p, float *f, void *stream)
 static halo_status exchange_staged(halo_plan *p, bool force_dir, float *buf, void *stream,
                                    const char *what)
 {
-    halo_status st = check_exchange(p, buf, what);
+    halo_status st = check_exchange(p, buf, what, stream);
     if (st != HALO_OK) return st;
     const halo::HostPlan &h = p->h;
     if (h.total_slots == 0 || h.n_entries == 0) return HALO_OK;
@@ -715,7 +745,7 @@ static_assert(halo::kMaxSlots <= (int64_t)kOriginSlot, "origin slots need 28 bit
 halo_status halo_exchange_x_direct(halo_plan *p, float *x, void *stream)
 {
     const char *what = "halo_exchange_x_direct";
-    halo_status st = check_exchange(p, x, what);
+    halo_status st = check_exchange(p, x, what, stream);
     if (st != HALO_OK) return st;
     const halo::HostPlan &h = p->h;
     if (h.total_slots == 0 || h.n_entries == 0) return HALO_OK;
@@ -799,7 +829,7 @@ halo_status halo_plan_reset(halo_plan *p)
         (e = hipDeviceSynchronize()) != hipSuccess)
         return hip_fail(e, "halo_plan_reset");
     std::memset(p->h_err, 0, 64);
-    p->epoch_x = p->epoch_f = p->epoch_xc = p->epoch_fc = 0;
+    for (uint32_t &e : p->epochs) e = 0;
     p->poisoned = false;
     return HALO_OK;
 }

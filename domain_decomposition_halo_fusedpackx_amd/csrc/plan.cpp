@@ -322,7 +322,37 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
         }
     make_items(P, item_entries);
     make_chunks(P, item_entries);
+    make_launch_members(P);
     return kOk;
+}
+
+// The members of each launch-count group: exactly the units for which the
+// kernel of the family executes a wait (the conditions below mirror the
+// kernels').
+void make_launch_members(HostPlan &P)
+{
+    P.launch_members.assign((size_t)kFamilies * kLaunchGroups, 0u);
+    auto add = [&](int family, size_t unit) {
+        P.launch_members[(size_t)family * kLaunchGroups + unit % kLaunchGroups] += 1u;
+    };
+    for (size_t u = 0; u < P.items.size(); ++u) {
+        const WorkItem &it = P.items[u];
+        if (it.n_total > it.n_indep) add(kFamItemsX, u);
+        if (it.fwait[0] >= 0) add(kFamItemsF, u);
+        add(kFamAtomicF, u);
+    }
+    if (!P.has_chunks) return;
+    for (size_t u = 0; u < P.chunks.size(); ++u) {
+        const Chunk &c = P.chunks[u];
+        if (c.zone >= 0) add(kFamChunksX, u);
+        bool waits = false;
+        for (int32_t p = 0; p < P.n_pulse; ++p) {
+            if (!((c.mask >> p) & 1u)) continue;
+            const int32_t R = P.send_to[(size_t)p * P.n_dom + c.domain];
+            if (P.zone_chunks[(size_t)p * P.n_dom + R] > 0) waits = true;
+        }
+        if (waits) add(kFamChunksF, u);
+    }
 }
 
 // Reorder the items of one pulse so that the items of domain D sit at

@@ -115,6 +115,8 @@ struct HostPlan {
     std::vector<float> shift4;             // [p][D][4]: coordShift of (p, D)
     std::vector<uint32_t> x_arrivals;      // [p][D]: chunks of D that send in pulse p
     std::vector<uint32_t> zone_chunks;     // [r][D]: chunks in region zone r of D
+    // launch counts: members of each group of each kernel family
+    std::vector<uint32_t> launch_members;  // [family][kLaunchGroups]
 
     const Segment &at(int32_t p, int32_t d) const { return seg[(size_t)p * n_dom + d]; }
 };
@@ -135,6 +137,25 @@ enum : int32_t { kSelectSlab = 0, kSelectCorner = 1 };
 
 // Status codes shared with halo.h.
 enum : int { kOk = 0, kErrArg = -1, kErrGeometry = -2, kErrRange = -3, kErrHip = -4, kErrNoMem = -7 };
+
+// Launch counts, from which the fused kernels infer the epoch of a launch
+// (the number of this family's launches so far, plus one) without a kernel
+// argument: the work units of a launch (work items, chunks) fall into
+// kLaunchGroups groups by unit index, and per kernel family the units that
+// wait on a counter are the members of their group. Each member adds 1 to its
+// group's count once per launch.
+constexpr int kLaunchGroups = 512;
+enum : int {
+    kFamItemsX = 0,   // k_pack_fused: items with dependent entries
+    kFamItemsF = 1,   // k_unpack_fused: items of every pulse but the last
+    kFamChunksX = 2,  // k_push_x: region chunks
+    kFamChunksF = 3,  // k_pull_f: chunks that pull a region summed in the launch
+    kFamAtomicF = 4,  // k_unpack_atomic: every item
+    kFamilies = 5
+};
+
+// Fill plan.launch_members from the items and chunks.
+void make_launch_members(HostPlan &plan);
 
 // Whether make_items places the items of one domain on one XCD.
 bool xcd_ordering_enabled();

@@ -669,6 +669,7 @@ void free_device_build(halo_plan *pl)
     pl->d_mask = nullptr;
     pl->d_items = nullptr;
     pl->d_seg_items = pl->d_x_arrivals = pl->d_zone_chunks = nullptr;
+    pl->d_members = nullptr;
     pl->d_chunks = nullptr;
     pl->d_shift4 = nullptr;
 }
@@ -906,7 +907,8 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
                              6 * aligned(std::max<size_t>(nseg, 1) * 4) +
                              aligned(std::max<size_t>(nseg, 1) * 16) +
                              aligned(std::max<size_t>(npc, 1) * sizeof(Chunk)) +
-                             aligned(std::max<size_t>(npc, 1) * 4);
+                             aligned(std::max<size_t>(npc, 1) * 4) +
+                             aligned((size_t)kFamilies * kLaunchGroups * 4);
     const size_t h_pieces = h_fixed, h_stats = h_pieces + aligned(std::max<size_t>(npc, 1) * 16),
                  h_tables = h_stats + aligned(std::max<size_t>(npc, 1) * sizeof(PieceStats)),
                  h_total = h_tables + tab_bytes;
@@ -974,6 +976,8 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         }
     }
 
+    make_launch_members(P);
+
     // -- tables: items, segment tables, chunks; one copy ---------------------------------
     HALO_TRY(arena_reserve(B.tables, tab_bytes), "device memory");
     char *tp = hp + h_tables;
@@ -990,6 +994,8 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     uint32_t *seg_items = (uint32_t *)put(P.seg_items.data(), nseg * 4, ns4);
     int32_t *send_to = (int32_t *)put(P.send_to.data(), nseg * 4, ns4);
     int32_t *recv_from = (int32_t *)put(P.recv_from.data(), nseg * 4, ns4);
+    uint32_t *members = (uint32_t *)put(P.launch_members.data(), P.launch_members.size() * 4,
+                                        P.launch_members.size() * 4);
     Chunk *chunks = nullptr;
     int32_t *forder = nullptr, *dest_start = nullptr;
     float *shift4 = nullptr;
@@ -1014,7 +1020,7 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     }
 
     // -- counters and the error word --------------------------------------------------------
-    const size_t words = 4 * nseg * kCounterStride + kCounterStride;
+    const size_t words = state_words_for(nseg);
     if (pl->d_state && pl->state_words != words) {
         (void)hipFree(pl->d_state);
         pl->d_state = nullptr;
@@ -1044,7 +1050,8 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     pl->d_shift4 = shift4;
     pl->d_x_arrivals = x_arrivals;
     pl->d_zone_chunks = zone_chunks;
-    pl->epoch_x = pl->epoch_f = pl->epoch_xc = pl->epoch_fc = 0;
+    pl->d_members = members;
+    for (uint32_t &e : pl->epochs) e = 0;
     pl->poisoned = false;
     pl->built_on_device = true;
     pl->uploaded = true;

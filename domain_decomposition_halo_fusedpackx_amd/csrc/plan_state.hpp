@@ -62,12 +62,16 @@ struct halo_plan {
     // staged baseline: one float triple per indexMap entry, allocated on first use
     float *d_stage = nullptr;
     uint32_t *d_origin = nullptr;  // direct form: home slot | wrap bits per entry (lazy)
+    uint32_t *d_members = nullptr;  // launch-count group sizes [family][group]
+    // epochs of the fused kernel families as the host counts them; passed to
+    // eager launches. Once a fused exchange of the plan has been captured in a
+    // graph, the host no longer sees every launch and passes 0 (the kernels
+    // then infer the epoch from the launch counts).
+    uint32_t epochs[halo::kFamilies] = {};
+    bool device_epochs = false;
     // device-built plans: local-slot indexMap and home slot of every atom
     int32_t *d_local_map = nullptr;
     int64_t *d_home_slot = nullptr;
-    // epochs: work-item kernels (x, f) and chunk kernels (xc, fc); each family
-    // counts in its own block of state
-    uint32_t epoch_x = 0, epoch_f = 0, epoch_xc = 0, epoch_fc = 0;
     uint32_t spin_limit = 1u << 20;
     int32_t withhold = -1;
     // testing: stress mode (seed 0 = off) and its launch orders

@@ -26,18 +26,50 @@
 // into m_s work items, each adds 1 when it is done, so after exchange number
 // e (the epoch) the counter holds e * m_s (mod 2^32). A waiter compares with
 // wrap-around arithmetic; nothing is reset between exchanges.
+//
+// A captured HIP graph replays its kernel arguments unchanged, so a replayed
+// launch cannot be handed its epoch; it infers it from launch counts on the
+// device (eager calls pass the epoch the host counted, and keep the counts
+// up to date for later replays). Work unit u of a launch (an item or a chunk) belongs to group
+// u mod kLaunchGroups; the units that wait are the group's members, and each
+// adds 1 to the group's 64-bit count once per launch, as its last action.
+// With m_g members, the count holds k * m_g + j while launch k + 1 runs,
+// j < m_g being the members of this launch already done; a member reads it
+// (with its first poll) before its own add, so k = count / m_g and the epoch
+// is k + 1, the same for every unit of the launch. 64 bits never wrap.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+#include "plan.hpp"
+
 namespace halo {
 
 constexpr int kCounterStride = 32;  // uint32 words: one 128-byte line per counter
 
+// Device state of a plan with n_seg segments, in uint32 words: segment
+// counters of the work-item kernels (X, then F), of the chunk kernels (X,
+// then F), of the atomic force kernel (F only), the launch counts of the
+// kernel families (kLaunchGroups each), one spare line.
+inline size_t state_words_for(size_t n_seg)
+{
+    return (5 * n_seg + (size_t)kFamilies * kLaunchGroups + 1) * kCounterStride;
+}
+
+// Base for counter_f() of the atomic force kernel's own block.
+inline size_t atomic_state_offset(size_t n_seg) { return 3 * n_seg * kCounterStride; }
+
+// First launch count of a family.
+inline size_t launch_groups_offset(size_t n_seg, int family)
+{
+    return (5 * n_seg + (size_t)family * kLaunchGroups) * kCounterStride;
+}
+
 // A counter block holds n_seg counters of the coordinate direction, then
-// n_seg of the force direction. The plan keeps one block per kernel family,
-// each with its own epochs, so that the families never mix their counts.
+// n_seg of the force direction. The plan keeps one block per kernel form
+// (work items, chunks), each with its own launch counts, so that the forms
+// never mix their counts.
 __device__ __forceinline__ uint32_t *counter_x(uint32_t *state, int32_t seg)
 {
     return state + (size_t)seg * kCounterStride;
@@ -48,11 +80,87 @@ __device__ __forceinline__ uint32_t *counter_f(uint32_t *state, int32_t n_seg, i
     return state + ((size_t)n_seg + seg) * kCounterStride;
 }
 
+// A unit's launch-count group: its count and its number of members.
+struct LaunchGroup {
+    uint64_t *count;
+    const uint32_t *members;
+};
+
+__device__ __forceinline__ LaunchGroup launch_group(uint32_t *groups, const uint32_t *members,
+                                                   uint32_t unit)
+{
+    const uint32_t g = unit % kLaunchGroups;
+    return LaunchGroup{reinterpret_cast<uint64_t *>(groups + (size_t)g * kCounterStride),
+                       members + g};
+}
+
+// Start of a member's first wait when the epoch is not known yet (0): read
+// its group's count and size, completed by finish_epoch after the first poll
+// has been issued.
+struct EpochRead {
+    uint64_t count;
+    uint32_t members;
+};
+
+__device__ __forceinline__ EpochRead start_epoch(const LaunchGroup &lg, uint32_t epoch)
+{
+    if (epoch != 0) return EpochRead{0, 1};
+    return EpochRead{__hip_atomic_load(lg.count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                     *lg.members};
+}
+
+__device__ __forceinline__ void finish_epoch(const EpochRead &r, uint32_t &epoch)
+{
+    if (epoch == 0) epoch = (uint32_t)(r.count / r.members) + 1u;
+}
+
+// A unit's launch-count bookkeeping: its group, its epoch (the host's, or 0
+// until a wait infers it), and whether its add has been made.
+struct LaunchState {
+    LaunchGroup lg;
+    uint32_t epoch;
+    bool eager;    // the host passed the epoch: this launch reads no count
+    bool counted;
+};
+
+__device__ __forceinline__ LaunchState launch_state(uint32_t *groups, const uint32_t *members,
+                                                    uint32_t unit, uint32_t host_epoch)
+{
+    return LaunchState{launch_group(groups, members, unit), host_epoch, host_epoch != 0, false};
+}
+
+__device__ __forceinline__ void count_unit(LaunchState &ls)
+{
+    if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(ls.lg.count, (uint64_t)1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    ls.counted = true;
+}
+
+// A member's add, as early as possible when nothing in the launch reads the
+// counts (its latency then overlaps the unit's work)...
+__device__ __forceinline__ void count_early(LaunchState &ls, bool member)
+{
+    if (ls.eager && member && !ls.counted) count_unit(ls);
+}
+
+// ... else as the unit's last action, after its read of the count (same
+// address, same thread or an earlier instruction of its wave), where the adds
+// do not compete with the reads of the units still starting.
+__device__ __forceinline__ void count_late(LaunchState &ls, bool member)
+{
+    if (member && !ls.counted) count_unit(ls);
+}
+
 // s_waitcnt with vmcnt(0) only (gfx9 encoding: expcnt and lgkmcnt left at max).
 __device__ __forceinline__ void wait_vmem()
 {
     __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
 }
+
+// The waits below take the unit's launch-count group and an epoch cache (0:
+// not known yet). On the first wait of a unit the polling lanes read the
+// launch count together with their first poll and fill the cache.
 
 // Wave 0 polls the counters of the listed segments (lane i the i-th) until
 // every one shows this epoch's completion; the workgroup then meets at a
@@ -60,27 +168,28 @@ __device__ __forceinline__ void wait_vmem()
 // up, so that the kernel always drains.
 __device__ __forceinline__ void wait_segments(const int32_t *list, int32_t n, const uint32_t *seg_items,
                                               uint32_t *state, int32_t n_seg, bool force_dir,
-                                              uint32_t epoch, uint32_t spin_limit,
-                                              uint32_t *err_word)
+                                              const LaunchGroup &lg, uint32_t &epoch,
+                                              uint32_t spin_limit, uint32_t *err_word)
 {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         for (int32_t base = 0; base < n; base += 64) {
             const bool mine = base + lane < n;
             uint32_t *ctr = nullptr;
-            uint32_t target = 0;
+            uint32_t mult = 0;
             if (mine) {
                 const int32_t s = list[base + lane];
                 ctr = force_dir ? counter_f(state, n_seg, s) : counter_x(state, s);
-                target = epoch * seg_items[s];
+                mult = seg_items[s];
             }
+            const EpochRead er = start_epoch(lg, epoch);
+            uint32_t c = mine ? __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : 0u;
+            finish_epoch(er, epoch);
+            const uint32_t target = epoch * mult;
             uint32_t polls = 0;
             while (true) {
-                bool ok = true;
-                if (mine) {
-                    uint32_t c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    ok = (int32_t)(c - target) >= 0;
-                }
+                const bool ok = !mine || (int32_t)(c - target) >= 0;
                 if (__all(ok)) break;
                 if (++polls > spin_limit) {
                     if (lane == 0)
@@ -89,6 +198,7 @@ __device__ __forceinline__ void wait_segments(const int32_t *list, int32_t n, co
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
+                if (mine) c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         wait_vmem();
@@ -99,20 +209,23 @@ __device__ __forceinline__ void wait_segments(const int32_t *list, int32_t n, co
 
 // The same wait for one segment, polled by lane 0 of wave 0.
 __device__ __forceinline__ void wait_one(int32_t s, const uint32_t *seg_items, uint32_t *state,
-                                         int32_t n_seg, bool force_dir, uint32_t epoch,
-                                         uint32_t spin_limit, uint32_t *err_word)
+                                         int32_t n_seg, bool force_dir, const LaunchGroup &lg,
+                                         uint32_t &epoch, uint32_t spin_limit, uint32_t *err_word)
 {
     if (threadIdx.x == 0) {
         uint32_t *ctr = force_dir ? counter_f(state, n_seg, s) : counter_x(state, s);
+        const EpochRead er = start_epoch(lg, epoch);
+        uint32_t c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        finish_epoch(er, epoch);
         const uint32_t target = epoch * seg_items[s];
         uint32_t polls = 0;
-        while ((int32_t)(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                         target) < 0) {
+        while ((int32_t)(c - target) < 0) {
             if (++polls > spin_limit) {
                 __hip_atomic_store(err_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
+            c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         wait_vmem();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -121,19 +234,20 @@ __device__ __forceinline__ void wait_one(int32_t s, const uint32_t *seg_items, u
 }
 
 // Wave 0 waits until the counter that each of its lanes names (ctr; nullptr:
-// none) reaches that lane's target; the workgroup then meets at a barrier.
-// One round of polls covers up to 64 counters.
-__device__ __forceinline__ void wait_lanes(uint32_t *ctr, uint32_t target, uint32_t spin_limit,
+// none) reaches mult times this launch's epoch; the workgroup then meets at a
+// barrier. One round of polls covers up to 64 counters.
+__device__ __forceinline__ void wait_lanes(uint32_t *ctr, uint32_t mult, const LaunchGroup &lg,
+                                           uint32_t &epoch, uint32_t spin_limit,
                                            uint32_t *err_word)
 {
     if (threadIdx.x < 64) {
+        const EpochRead er = start_epoch(lg, epoch);
+        uint32_t c = ctr ? __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+        finish_epoch(er, epoch);
+        const uint32_t target = epoch * mult;
         uint32_t polls = 0;
         while (true) {
-            bool ok = true;
-            if (ctr) {
-                const uint32_t c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ok = (int32_t)(c - target) >= 0;
-            }
+            const bool ok = !ctr || (int32_t)(c - target) >= 0;
             if (__all(ok)) break;
             if (++polls > spin_limit) {
                 if (threadIdx.x == 0)
@@ -141,6 +255,7 @@ __device__ __forceinline__ void wait_lanes(uint32_t *ctr, uint32_t target, uint3
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
+            if (ctr) c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         wait_vmem();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");

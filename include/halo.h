@@ -214,10 +214,14 @@ halo_status halo_plan_upload(halo_plan *plan);
  *   x : device, total_slots*3 float32, 4-byte aligned. Home slots are read;
  *       every halo slot is overwritten with x[indexMap[i]] + coordShift.
  * Asynchronous; exchanges of one plan must be ordered on one stream.
- * Every fused call (this one, halo_exchange_f and the _indexmap, _transposed
- * and _atomic forms) passes its launch a new epoch, so it cannot be captured
- * into a HIP graph: called while `stream` is capturing it returns
- * HALO_ERR_ARG. The per-pulse form can be captured. */
+ * HIP graphs: every exchange form can be captured once the plan is uploaded
+ * (halo_plan_upload, or any earlier exchange). The fused kernels take no
+ * per-call argument: each launch infers its epoch (Algorithm 5's signal
+ * value) from launch counters in the plan's device memory, so replays of
+ * captured exchanges and eager calls of the same plan may follow one another
+ * in any order, as long as they are ordered on one stream. Before the upload,
+ * a call on a capturing stream returns HALO_ERR_ARG (the upload allocates and
+ * synchronises). */
 halo_status halo_exchange_x(halo_plan *plan, float *x, void *stream);
 
 /* Force exchange, Algorithm 6 in ONE kernel launch: pulses from last to
@@ -269,8 +273,8 @@ halo_status halo_exchange_f_pulsewise(halo_plan *plan, float *f, void *stream);
  * 2 * (n - 1) * 2^-24 * (sum of |terms|) apart, n being the number of values
  * summed into the slot; it is bitwise equal whenever every partial sum is
  * exact (small integers, for example). Same arguments, ownership and errors
- * as halo_exchange_f. Shares the index-list force counters; do not overlap it
- * with halo_exchange_f on the same plan. */
+ * as halo_exchange_f. Like every exchange of one plan, order it on one
+ * stream with the plan's other exchanges. */
 halo_status halo_exchange_f_atomic(halo_plan *plan, float *f, void *stream);
 
 /* Staged baseline (the message-passing design that the pages measure the

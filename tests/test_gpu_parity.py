@@ -266,42 +266,107 @@ def test_parity_cell_sorted_input(torch, oracle_mod, wid):
         check_both(torch, oracle_mod, plan, o, w.seed, impl, f"{w.name} cell-sorted")
 
 
-def test_fused_refuses_graph_capture_pulsewise_replays(torch, oracle_mod):
-    """Fused calls refuse a capturing stream; the per-pulse form captured in a
-    graph replays exactly, with eager work between the replays."""
+def _capture(torch, fn, stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        g.capture_begin()
+        try:
+            fn()
+        finally:
+            g.capture_end()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_capture_before_upload_is_refused(torch, oracle_mod):
+    """The first exchange on a plan uploads it (allocations and a device
+    synchronisation): under capture it is refused with HALO_ERR_ARG."""
     w = W.WORKLOADS[2]
+    pos = W.workload_positions(w)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    x = torch.from_numpy(o.home_filled(np.nan)).cuda()
+    dummy = torch.zeros(4, device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    say("capture before upload")
+
+    def body():
+        with pytest.raises(HaloError) as e:
+            plan.exchange_x(x, s)
+        assert e.value.code == -1 and "capture" in str(e.value)
+        dummy.add_(1.0)
+    _capture(torch, body, s)
+    plan.upload()
+
+
+@pytest.mark.parametrize("form", ["fused", "indexmap", "transposed", "pulsewise"])
+@pytest.mark.parametrize("wid", [2, 4, 5])
+def test_graph_replays_of_every_form(torch, oracle_mod, wid, form):
+    """Both exchanges captured in one HIP graph, replayed three times, with
+    eager exchanges of the same plan between the replays: every replay and
+    every eager call is bitwise equal to the oracle (the fused kernels infer
+    their epoch on the device, so replays and eager calls share the counts)."""
+    w = W.WORKLOADS[wid]
     pos = W.workload_positions(w)
     plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
     plan.upload()
     x0 = o.home_filled(np.nan)
-    want = o.exchange_x(x0.copy())
-    x = torch.from_numpy(x0.copy()).cuda()
-    dummy = torch.zeros(4, device="cuda")
+    want_x = o.exchange_x(x0.copy())
+    base, n_home, n_halo = o.domains()
+    f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, w.seed)
+    want_f = o.exchange_f(f0.copy())
+    x0d, f0d = torch.from_numpy(x0).cuda(), torch.from_numpy(f0).cuda()
+    x, f = x0d.clone(), f0d.clone()
     s = torch.cuda.Stream()
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    say("graph capture: fused refuses, per-pulse is captured")
-    with torch.cuda.stream(s):
-        g.capture_begin()
-        try:
-            for name in ("exchange_x", "exchange_x_indexmap", "exchange_x_transposed"):
-                with pytest.raises(HaloError) as e:
-                    getattr(plan, name)(x, s)
-                assert e.value.code == -1
-            plan.exchange_x_pulsewise(x, s)
-            dummy.add_(1.0)
-        finally:
-            g.capture_end()
-    torch.cuda.synchronize()
+    say(f"{w.name} {form}: capture X and F")
+    g = _capture(torch, lambda: (exchange(plan, form, "x", x, s), exchange(plan, form, "f", f, s)),
+                 s)
     for r in range(3):
-        x.copy_(torch.from_numpy(x0))
+        x.copy_(x0d)
+        f.copy_(f0d)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert_bitwise(x.cpu().numpy(), want, f"replay {r}")
-        plan.exchange_x(x)  # eager fused exchange between the replays
+        assert_bitwise(x.cpu().numpy(), want_x, f"{form} replay {r} x")
+        assert_bitwise(f.cpu().numpy(), want_f, f"{form} replay {r} f")
+        x.copy_(x0d)
+        f.copy_(f0d)
+        exchange(plan, form, "x", x)
+        exchange(plan, form, "f", f)
         torch.cuda.synchronize()
-        assert_bitwise(x.cpu().numpy(), want, f"eager after replay {r}")
+        assert_bitwise(x.cpu().numpy(), want_x, f"{form} eager {r} x")
+        assert_bitwise(f.cpu().numpy(), want_f, f"{form} eager {r} f")
+    plan.sync()
+
+
+def test_graph_replays_share_counts_with_the_atomic_form(torch, oracle_mod):
+    """The ordered and the atomic force kernels share their counters: graphs of
+    each, replayed alternately and mixed with eager calls, stay exact (small
+    integer forces, so that the atomic sums are exact too)."""
+    w = W.WORKLOADS[4]
+    pos = W.workload_positions(w)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    plan.upload()
+    base, n_home, n_halo = o.domains()
+    f0 = W.small_int_forces(o.total_slots, base, n_home, n_halo, 5)
+    want = o.exchange_f(f0.copy())
+    f0d = torch.from_numpy(f0).cuda()
+    f = f0d.clone()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    say("atomic and ordered force graphs")
+    g_ord = _capture(torch, lambda: plan.exchange_f_indexmap(f, s), s)
+    g_atm = _capture(torch, lambda: plan.exchange_f_atomic(f, s), s)
+    for r, g in enumerate([g_ord, g_atm, g_atm, g_ord, None, g_atm, None, g_ord]):
+        f.copy_(f0d)
+        torch.cuda.synchronize()
+        if g is None:
+            plan.exchange_f_atomic(f) if r % 2 else plan.exchange_f_indexmap(f)
+        else:
+            g.replay()
+        torch.cuda.synchronize()
+        assert_bitwise(f.cpu().numpy(), want, f"step {r}")
     plan.sync()
 
 
