@@ -49,3 +49,55 @@ def test_stress_fused_forms(torch, oracle_mod, wid):
     torch.cuda.synchronize()
     plan.sync()
     assert_bitwise(x.cpu().numpy(), want_x, "after stress off")
+
+
+@pytest.mark.parametrize("wid", [3, 4])
+def test_stress_in_graph_replays(torch, oracle_mod, wid):
+    """The same stress with the epoch inferred on the device: exchanges
+    captured in a graph (with the stress orders and delays) and replayed,
+    mixed with eager calls; every result stays bitwise equal."""
+    w = W.WORKLOADS[wid]
+    pos = W.workload_positions(w)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    plan.upload()
+    x0 = o.home_filled(np.nan)
+    want_x = o.exchange_x(x0.copy())
+    base, n_home, n_halo = o.domains()
+    f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, w.seed)
+    want_f = o.exchange_f(f0.copy())
+    x0d, f0d = torch.from_numpy(x0).cuda(), torch.from_numpy(f0).cuda()
+    x, f = x0d.clone(), f0d.clone()
+    plan.debug_stress(7)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graphs = {}
+    for impl in ("indexmap", "transposed"):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            g.capture_begin()
+            try:
+                exchange(plan, impl, "x", x, s)
+                exchange(plan, impl, "f", f, s)
+            finally:
+                g.capture_end()
+        torch.cuda.synchronize()
+        graphs[impl] = g
+    for r, impl in enumerate(["indexmap", "transposed", "transposed", "indexmap"]):
+        say(f"{w.name} stressed replay {r} {impl}")
+        x.copy_(x0d)
+        f.copy_(f0d)
+        torch.cuda.synchronize()
+        graphs[impl].replay()
+        torch.cuda.synchronize()
+        plan.sync()
+        assert_bitwise(x.cpu().numpy(), want_x, f"stressed replay {r} {impl} x")
+        assert_bitwise(f.cpu().numpy(), want_f, f"stressed replay {r} {impl} f")
+        x.copy_(x0d)
+        f.copy_(f0d)
+        exchange(plan, impl, "x", x)
+        exchange(plan, impl, "f", f)
+        torch.cuda.synchronize()
+        plan.sync()
+        assert_bitwise(x.cpu().numpy(), want_x, f"stressed eager {r} {impl} x")
+        assert_bitwise(f.cpu().numpy(), want_f, f"stressed eager {r} {impl} f")
+    plan.debug_stress(0)
