@@ -300,7 +300,7 @@ def test_capture_before_upload_is_refused(torch, oracle_mod):
 
 
 @pytest.mark.parametrize("form", ["fused", "indexmap", "transposed", "pulsewise"])
-@pytest.mark.parametrize("wid", [2, 4, 5])
+@pytest.mark.parametrize("wid", [1, 2, 4, 5])
 def test_graph_replays_of_every_form(torch, oracle_mod, wid, form):
     """Both exchanges captured in one HIP graph, replayed three times, with
     eager exchanges of the same plan between the replays: every replay and
