@@ -221,7 +221,9 @@ halo_status halo_plan_upload(halo_plan *plan);
  * captured exchanges and eager calls of the same plan may follow one another
  * in any order, as long as they are ordered on one stream. Before the upload,
  * a call on a capturing stream returns HALO_ERR_ARG (the upload allocates and
- * synchronises). */
+ * synchronises). A graph holds the plan's device addresses: after
+ * halo_plan_rebuild_device, halo_plan_reset or halo_plan_debug_stress,
+ * capture it again. */
 halo_status halo_exchange_x(halo_plan *plan, float *x, void *stream);
 
 /* Force exchange, Algorithm 6 in ONE kernel launch: pulses from last to
