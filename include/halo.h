@@ -222,8 +222,8 @@ halo_status halo_plan_upload(halo_plan *plan);
  * in any order, as long as they are ordered on one stream. Before the upload,
  * a call on a capturing stream returns HALO_ERR_ARG (the upload allocates and
  * synchronises). A graph holds the plan's device addresses: after
- * halo_plan_rebuild_device, halo_plan_reset or halo_plan_debug_stress,
- * capture it again. */
+ * halo_plan_rebuild_device or halo_plan_debug_stress, capture it again
+ * (halo_plan_reset keeps them). */
 halo_status halo_exchange_x(halo_plan *plan, float *x, void *stream);
 
 /* Force exchange, Algorithm 6 in ONE kernel launch: pulses from last to
