@@ -340,6 +340,42 @@ def test_graph_replays_of_every_form(torch, oracle_mod, wid, form):
     plan.sync()
 
 
+def test_graph_replays_after_reset(torch, oracle_mod):
+    """halo_plan_reset zeroes the counts and the host's epochs: a graph captured
+    before it replays exactly afterwards, and so do eager calls."""
+    w = W.WORKLOADS[3]
+    pos = W.workload_positions(w)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    plan.upload()
+    x0 = o.home_filled(np.nan)
+    want_x = o.exchange_x(x0.copy())
+    base, n_home, n_halo = o.domains()
+    f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, w.seed)
+    want_f = o.exchange_f(f0.copy())
+    x0d, f0d = torch.from_numpy(x0).cuda(), torch.from_numpy(f0).cuda()
+    x, f = x0d.clone(), f0d.clone()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = _capture(torch, lambda: (plan.exchange_x(x, s), plan.exchange_f(f, s)), s)
+    for r, mode in enumerate(["replay", "reset", "replay", "eager", "reset", "eager", "replay"]):
+        say(f"graph and reset: {mode}")
+        if mode == "reset":
+            plan.reset()
+            continue
+        x.copy_(x0d)
+        f.copy_(f0d)
+        torch.cuda.synchronize()
+        if mode == "replay":
+            g.replay()
+        else:
+            plan.exchange_x(x)
+            plan.exchange_f(f)
+        torch.cuda.synchronize()
+        assert_bitwise(x.cpu().numpy(), want_x, f"{mode} {r} x")
+        assert_bitwise(f.cpu().numpy(), want_f, f"{mode} {r} f")
+    plan.sync()
+
+
 def test_graph_replays_share_counts_with_the_atomic_form(torch, oracle_mod):
     """The ordered and the atomic force kernels share their counters: graphs of
     each, replayed alternately and mixed with eager calls, stay exact (small
