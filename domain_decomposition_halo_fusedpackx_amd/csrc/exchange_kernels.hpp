@@ -19,7 +19,11 @@
 // per-slot pulse masks. "GPU-Initiated Halo Exchange Cuts CPU Bottlenecks in
 // GROMACS", "Fusing pack, put, and wait into one kernel": the per-pulse first
 // design is kept as k_pack_pulse / k_unpack_pulse, one launch per pulse in
-// stream order, and the staged design as k_stage_*.
+// stream order, and the staged design as k_stage_*. k_gather_x is the
+// one-GPU direct coordinate form (every halo slot from its atom's home slot).
+// The fused kernels take the epoch (the pages' sigVal) from the host, or
+// infer it from launch counts on the device when replayed from a graph
+// (sync.hpp).
 //
 // Everything is float32 and every add is a single IEEE add (no FMA, no flush
 // of subnormals: the build passes -ffp-contract=off and keeps denormals).
