@@ -189,6 +189,36 @@ def test_layout_and_pulsedata_conventions(oracle_mod, case):
     assert np.all(nxt == n_home + n_halo)
 
 
+def _check_halos(oracle_mod, pos, g, want, selection):
+    o = oracle_mod.Oracle(pos, g["box"], g["grid"], g["cutoff"], selection)
+    x = o.home_filled(np.nan)
+    o.exchange_x(x)
+    gids = o.slot_gids()
+    base, n_home, n_halo = o.domains()
+    assert o.n_pulse == g["n_pulses"]
+    for d_s, items in want["halo"].items():
+        d = int(d_s)
+        lo, hi = base[d] + n_home[d], base[d] + n_home[d] + n_halo[d]
+        got = sorted((int(gids[s]), *map(float, x[s])) for s in range(lo, hi))
+        exp = sorted((int(v[0]), *(float(np.float32(c)) for c in v[1:])) for v in items)
+        assert got == exp, f"{selection}: domain {d}"
+    f = np.zeros((o.total_slots, 3), np.float32)
+    halo = np.ones(o.total_slots, bool)
+    halo[o.home_slots()] = False
+    f[halo] = 1.0
+    o.exchange_f(f)
+    hs = o.home_slots()
+    for a_s, v in want["home_force_after_unit_halo_forces"].items():
+        assert np.all(f[hs[int(a_s)]] == v), f"{selection}: atom {a_s}"
+
+
+def test_golden_selection_example(oracle_mod):
+    g = json.load(open(os.path.join(GOLDEN, "corner_selection_2x2x2.json")))
+    pos = np.array(g["positions"], np.float32)
+    for selection, want in g["selections"].items():
+        _check_halos(oracle_mod, pos, g, want, selection)
+
+
 @pytest.mark.parametrize("name", ["slab_1x1x2.json", "corner_2x2x2.json"])
 def test_golden_worked_examples(oracle_mod, name):
     g = json.load(open(os.path.join(GOLDEN, name)))
