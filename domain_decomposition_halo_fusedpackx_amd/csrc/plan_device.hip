@@ -15,7 +15,7 @@
 //   k_tile_scan      per domain, exclusive scan of the tile histogram
 //   k_home_start     first home slot of every domain; slot cursors
 //   k_home_scatter   stable counting sort: home atoms of every domain in
-//                    ascending id (wave-level key grouping, waves in order)
+//                    ascending id (wave-level radix sort by domain, waves in order)
 //   k_select<false>  per (pulse, domain): how many candidates are sent, and
 //                    how many of them are home slots (depOffset split)
 //   k_pulse_scan     the pulse's map offsets and the receivers' regions
@@ -173,12 +173,30 @@ __global__ __launch_bounds__(kBT) void k_tile_scan(uint32_t *__restrict__ tile_h
     if (threadIdx.x == 0) n_home[blockIdx.x] = (int32_t)carry;
 }
 
+// Stable sort of the wave's 64 values by their key bits (value = key << 6 |
+// lane): LSD radix, one key bit per pass, each lane pushing its value to its
+// new position. Every lane of the wave must take part.
+__device__ __forceinline__ uint32_t wave_sort_by_key(uint32_t v, int key_bits)
+{
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = lanes_below(lane);
+    for (int b = 0; b < key_bits; ++b) {
+        const bool one = (v >> (6 + b)) & 1u;
+        const uint64_t ones = __ballot(one);
+        const uint32_t zeros_total = 64u - (uint32_t)__popcll(ones);
+        const uint32_t pos = one ? zeros_total + (uint32_t)__popcll(ones & below)
+                                 : (uint32_t)__popcll(~ones & below);
+        v = (uint32_t)__builtin_amdgcn_ds_permute((int)(pos * 4u), (int)v);
+    }
+    return v;
+}
+
 // Stable counting sort of the atoms by domain, carrying their coordinates
 // (one array per dimension, home order). Block = tile; LDS counters
 // start at the tile's offsets within each domain. In each round of 256 atoms
-// a wave groups its lanes by domain (a lane's rank = lanes below it with the
-// same domain), then the waves add their group sizes to the counters one
-// after the other, so that lower ids get lower ranks.
+// a wave sorts its lanes by domain (stable), so that lanes with one domain
+// form a run in id order; the waves then add their run lengths to the
+// counters one after the other, so that lower ids get lower ranks.
 template <int kTile>
 __global__ __launch_bounds__(kBT) void k_home_scatter(const int32_t *__restrict__ owner,
                                                       int64_t n_atoms, int32_t n_dom,
@@ -194,44 +212,46 @@ __global__ __launch_bounds__(kBT) void k_home_scatter(const int32_t *__restrict_
         cnt[d] = tile_off[(size_t)d * n_tiles + blockIdx.x];
     __syncthreads();
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // keys of up to n_dom (n_dom marks lanes past the last atom)
+    int key_bits = 1;
+    while ((1 << key_bits) <= n_dom) ++key_bits;
     // all of the tile's domain ids are loaded up front
     int32_t keys[kTile / kBT];
 #pragma unroll
     for (int j = 0; j < kTile / kBT; ++j) {
         const int64_t a = (int64_t)blockIdx.x * kTile + j * kBT + threadIdx.x;
-        keys[j] = a < n_atoms ? owner[a] : -1;
+        keys[j] = a < n_atoms ? owner[a] : n_dom;
     }
+    const uint64_t le = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);  // lanes <= this one
 #pragma unroll
     for (int j = 0; j < kTile / kBT; ++j) {
         const int64_t a = (int64_t)blockIdx.x * kTile + j * kBT + threadIdx.x;
         const bool valid = a < n_atoms;
-        const int32_t key = keys[j];
-        uint64_t todo = __ballot(valid);
-        uint32_t my_rank = 0, grp = 0;
-        int my_leader = 0;
-        while (todo) {
-            const int leader = __ffsll((unsigned long long)todo) - 1;
-            const int32_t k = __shfl(key, leader, 64);
-            const bool mine = valid && key == k;
-            const uint64_t m = __ballot(mine);
-            if (mine) {
-                my_rank = (uint32_t)__popcll(m & lanes_below(lane));
-                my_leader = leader;
-                grp = (uint32_t)__popcll(m);
-            }
-            todo &= ~m;
-        }
+        // after the sort, sorted lane i holds (key, original lane) of the
+        // i-th value in (key, lane) order
+        const uint32_t sv = wave_sort_by_key(((uint32_t)keys[j] << 6) | (uint32_t)lane, key_bits);
+        const int32_t skey = (int32_t)(sv >> 6);
+        const int32_t prev = __shfl_up((int)skey, 1, 64);
+        const bool head = lane == 0 || prev != skey;
+        const uint64_t heads = __ballot(head);
+        const int run_start = 63 - __clzll((long long)(heads & le));
+        const uint64_t after = heads & ~le;
+        const int run_end = after ? __ffsll((long long)after) - 1 : 64;
         uint32_t base = 0;
         for (int t = 0; t < kBT / 64; ++t) {
-            if (w == t && valid && lane == my_leader) {
-                base = cnt[key];
-                cnt[key] = base + grp;
+            if (w == t && head && skey < n_dom) {
+                base = cnt[skey];
+                cnt[skey] = base + (uint32_t)(run_end - lane);
             }
             __syncthreads();
         }
-        base = (uint32_t)__shfl((int)base, my_leader, 64);
+        base = (uint32_t)__shfl((int)base, run_start, 64);
+        const uint32_t r_sorted = base + (uint32_t)(lane - run_start);
+        // back to the lane that holds the atom
+        const uint32_t r = (uint32_t)__builtin_amdgcn_ds_permute((int)((sv & 63u) * 4u),
+                                                                 (int)r_sorted);
         if (valid) {
-            const uint32_t r = base + my_rank;
+            const int32_t key = keys[j];
             const int64_t h = home_start[key] + (int64_t)r;
 #pragma unroll
             for (int d = 0; d < 3; ++d) home_c[d * n_atoms + h] = pos[3 * a + d];
@@ -298,34 +318,41 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     constexpr int kRows = 4;  // rows of NT candidates whose loads go out together
     // The candidate zones in slot order ([home,] regions), laid end to end:
     // candidate i of the domain is entry i - zbeg[z] of zone z.
-    __shared__ int32_t zbeg[kMaxPulses + 2], zslot[kMaxPulses + 1], zoff[kMaxPulses + 1];
+    __shared__ int32_t zbeg[kMaxPulses + 2], zslot[kMaxPulses + 1], zoff[kMaxPulses + 1],
+        zlen[kMaxPulses + 1];
     __shared__ uint32_t dep_lds;
     const int32_t D = blockIdx.x;
     const int32_t zfirst = k == 0 ? -1 : p - 1;
     const int32_t nz = p - zfirst;
+    // thread j reads zone j's sizes (one round of loads for all zones)
+    if ((int32_t)threadIdx.x < nz) {
+        const int32_t j = threadIdx.x, z = zfirst + j;
+        int32_t len;
+        if (z < 0) {
+            len = n_home[D];
+            zslot[j] = 0;
+            zoff[j] = home_start[D];
+        } else {
+            const int32_t S = recv_from[z * n_dom + D];
+            len = seg.row(z, kRecvSize)[D];
+            zslot[j] = seg.row(z, kAtomOffset)[D];
+            const int32_t off = seg.row(z, kMapOff)[S];
+            zoff[j] = off;
+            // an earlier pulse overflowed the entry arrays: the host
+            // rebuilds with more room; read nothing past them meanwhile
+            if (off > cap - len) len = 0;
+        }
+        zlen[j] = len;
+    }
+    if (threadIdx.x == 0) dep_lds = 0;
+    __syncthreads();
     if (threadIdx.x == 0) {
         int32_t acc = 0;
         for (int32_t j = 0; j < nz; ++j) {
-            const int32_t z = zfirst + j;
-            int32_t len;
-            if (z < 0) {
-                len = n_home[D];
-                zslot[j] = 0;
-                zoff[j] = home_start[D];
-            } else {
-                const int32_t S = recv_from[z * n_dom + D];
-                len = seg.row(z, kRecvSize)[D];
-                zslot[j] = seg.row(z, kAtomOffset)[D];
-                zoff[j] = seg.row(z, kMapOff)[S];
-                // an earlier pulse overflowed the entry arrays: the host
-                // rebuilds with more room; read nothing past them meanwhile
-                if (zoff[j] > cap - len) len = 0;
-            }
             zbeg[j] = acc;
-            acc += len;
+            acc += zlen[j];
         }
         zbeg[nz] = acc;
-        dep_lds = 0;
     }
     __syncthreads();
     const int32_t total = zbeg[nz];
