@@ -470,10 +470,15 @@ halo_status halo_plan_rebuild_device(halo_plan *p, const float *positions, int64
     if (!p->built_on_device) {
         free_device(p);  // the host-built device copy is replaced
     } else {
+        // derived arrays sized for the old plan: staging, origin map and the
+        // stress orders (the stress mode ends with the plan it was set for)
         if (p->d_stage) (void)hipFree(p->d_stage);
         if (p->d_origin) (void)hipFree(p->d_origin);
+        if (p->d_stress) (void)hipFree(p->d_stress);
         p->d_stage = nullptr;
         p->d_origin = nullptr;
+        p->d_stress = nullptr;
+        p->stress_seed = 0;
     }
     p->uploaded = false;
     std::string msg;

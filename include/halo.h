@@ -332,7 +332,7 @@ halo_status halo_plan_debug_withhold(halo_plan *plan, int32_t segment);
  * unit first sleeps a pseudo-random while (up to about 100 us) derived from
  * the seed. Results must not change: this exposes missing waits or orderings.
  * seed = 0 (the default) turns it off. Synchronises the device when it
- * changes an existing setting. */
+ * changes an existing setting. A rebuild turns it off. */
 halo_status halo_plan_debug_stress(halo_plan *plan, uint32_t seed);
 
 #ifdef __cplusplus

@@ -101,3 +101,28 @@ def test_stress_in_graph_replays(torch, oracle_mod, wid):
         assert_bitwise(x.cpu().numpy(), want_x, f"stressed eager {r} {impl} x")
         assert_bitwise(f.cpu().numpy(), want_f, f"stressed eager {r} {impl} f")
     plan.debug_stress(0)
+
+
+def test_rebuild_ends_stress_mode(torch, oracle_mod):
+    """A rebuild changes the number of work units; the stress orders of the
+    old plan are dropped with it, and the rebuilt plan's exchanges are exact."""
+    from .test_gpu_plan_device import device_plan
+    w = W.WORKLOADS[3]
+    dp = device_plan(torch, W.positions(w.box, 200_000, 41), w.box, w.grid, w.cutoff)
+    dp.debug_stress(5)
+    pos = W.positions(w.box, 420_000, 42)  # more atoms: more items and chunks
+    say("rebuild with stress set")
+    dp.rebuild_on_device(torch.from_numpy(pos).cuda())
+    o = oracle_mod.Oracle(pos, w.box, w.grid, w.cutoff)
+    x0 = o.home_filled(np.nan)
+    base, n_home, n_halo = o.domains()
+    f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, 42)
+    for impl in ("indexmap", "transposed"):
+        x = torch.from_numpy(x0.copy()).cuda()
+        exchange(dp, impl, "x", x)
+        f = torch.from_numpy(f0.copy()).cuda()
+        exchange(dp, impl, "f", f)
+        torch.cuda.synchronize()
+        dp.sync()
+        assert_bitwise(x.cpu().numpy(), o.exchange_x(x0.copy()), f"{impl} x")
+        assert_bitwise(f.cpu().numpy(), o.exchange_f(f0.copy()), f"{impl} f")
