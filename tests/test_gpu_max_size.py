@@ -5,7 +5,8 @@ at most 178,956,969 slots (2 GiB of coordinates). These tests build a plan of
 about 95 % of that on the GPU (100 M atoms, 16x16x16 domains) and check the
 exchanges through properties that hold at any size, on the oracle-free path:
 - coordinates: every sampled region entry equals its source slot plus
-  coordShift (the stored value of a forwarded atom is the forwarded one);
+  coordShift (the stored value of a forwarded atom is the forwarded one), and
+  the direct form gives the same bits;
 - forces: with small-integer forces on the halo slots and zero on the home
   slots, every halo force reaches exactly one home slot, so the home slots'
   total equals the halo slots' initial total, exactly (all partial sums are
@@ -68,7 +69,15 @@ def test_near_maximum_plan(torch):
             checked += q["send_size"]
     assert not np.isnan(xh).any()
     say(f"coordinates: {checked} sampled entries match; no slot left unwritten")
-    del xh, x
+    del xh
+    # the direct form (28-bit origin slots) gives the same bits at this size
+    xd = torch.full((plan.total_slots, 3), float("nan"), device="cuda")
+    xd[slots] = pos
+    plan.exchange_x_direct(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(xd.view(torch.int32), x.view(torch.int32))
+    say("direct form: bitwise equal to the fused exchange")
+    del xd, x
 
     # forces: conservation with small integers
     _, n_home, n_halo = plan.domains()
