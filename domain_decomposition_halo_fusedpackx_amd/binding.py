@@ -54,6 +54,8 @@ SIGNATURES = {
     "halo_exchange_f_atomic": (_st, [_vp, _vp, _vp]),
     "halo_exchange_x_staged": (_st, [_vp, _vp, _vp]),
     "halo_exchange_x_direct": (_st, [_vp, _vp, _vp]),
+    "halo_scatter_home": (_st, [_vp, _vp, _vp, _vp]),
+    "halo_gather_home": (_st, [_vp, _vp, _vp, _vp]),
     "halo_exchange_f_staged": (_st, [_vp, _vp, _vp]),
     "halo_plan_sync": (_st, [_vp, _vp]),
     "halo_plan_reset": (_st, [_vp]),
@@ -330,6 +332,29 @@ class HaloPlan:
 
     def exchange_x_direct(self, x, stream=None):
         self._call("halo_exchange_x_direct", x, stream)
+
+    def _atoms(self, t):
+        import torch
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("per-atom arrays must be torch.cuda tensors")
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError("per-atom arrays must be contiguous float32")
+        if t.numel() != 3 * self.n_atoms:
+            raise ValueError(f"per-atom array holds {t.numel()} floats, the plan needs "
+                             f"{3 * self.n_atoms} (n_atoms x 3)")
+        return ctypes.c_void_p(t.data_ptr())
+
+    def scatter_home(self, values, slots, stream=None):
+        """slots[home_slot[a]] = values[a] (halo_scatter_home)."""
+        v = self._atoms(values)
+        ptr, dev = self._buf(slots)
+        _check(load_library().halo_scatter_home(self._h, v, ptr, _stream_handle(stream, dev)))
+
+    def gather_home(self, slots, values, stream=None):
+        """values[a] = slots[home_slot[a]] (halo_gather_home)."""
+        v = self._atoms(values)
+        ptr, dev = self._buf(slots)
+        _check(load_library().halo_gather_home(self._h, ptr, v, _stream_handle(stream, dev)))
 
     def sync(self, stream=None):
         _check(load_library().halo_plan_sync(self._h, _stream_handle(stream)))

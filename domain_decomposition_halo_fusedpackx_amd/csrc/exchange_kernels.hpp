@@ -813,3 +813,32 @@ __global__ __launch_bounds__(kThreads) void k_gather_x(float *x, uint32_t x_byte
         store3<kStream>(rx, e < n ? (uint32_t)(it->region_begin + e) * 12u : kInvalid, v[j] + s);
     }
 }
+
+// ---- home slots and per-atom arrays (halo_scatter_home, halo_gather_home) ----
+// Atom a's values live at slot home_slot[a]: scatter copies a per-atom array
+// of float triples into the home slots, gather copies them back out.
+__global__ __launch_bounds__(kThreads) void k_scatter_home(const float *values, uint32_t value_bytes,
+                                                           float *slots, uint32_t slot_bytes,
+                                                           const int64_t *__restrict__ home_slot,
+                                                           int64_t n_atoms)
+{
+    const int64_t a = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const bool ok = a < n_atoms;
+    const uint32_t hs = (uint32_t)home_slot[ok ? a : 0];  // n_atoms >= 1
+    const uint32_t s = ok ? hs * 12u : kInvalid;
+    const f3v v = load3<kStream>(make_rsrc(values, value_bytes), ok ? (uint32_t)a * 12u : kInvalid);
+    store3<kPlain>(make_rsrc(slots, slot_bytes), s, v);
+}
+
+__global__ __launch_bounds__(kThreads) void k_gather_home(const float *slots, uint32_t slot_bytes,
+                                                          float *values, uint32_t value_bytes,
+                                                          const int64_t *__restrict__ home_slot,
+                                                          int64_t n_atoms)
+{
+    const int64_t a = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const bool ok = a < n_atoms;
+    const uint32_t hs = (uint32_t)home_slot[ok ? a : 0];  // n_atoms >= 1
+    const uint32_t s = ok ? hs * 12u : kInvalid;
+    const f3v v = load3<kPlain>(make_rsrc(slots, slot_bytes), s);
+    store3<kStream>(make_rsrc(values, value_bytes), ok ? (uint32_t)a * 12u : kInvalid, v);
+}

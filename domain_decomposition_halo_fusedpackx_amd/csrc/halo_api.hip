@@ -798,6 +798,56 @@ halo_status halo_exchange_x_direct(halo_plan *p, float *x, void *stream)
     return e == hipSuccess ? HALO_OK : hip_fail(e, what);
 }
 
+// Device copy of the home slots (built on the device already for device-built
+// plans; uploaded on the first call for host-built ones).
+static halo_status ensure_home_slots(halo_plan *p, hipStream_t s, const char *what)
+{
+    if (p->d_home_slot || p->h.n_atoms == 0) return HALO_OK;
+    halo_status st = refuse_capture(s, what);
+    if (st != HALO_OK) return st;
+    if ((st = ensure_host_maps(p)) != HALO_OK) return st;
+    hipError_t e = hipMalloc((void **)&p->d_home_slot, (size_t)p->h.n_atoms * 8);
+    if (e == hipSuccess)
+        e = hipMemcpy(p->d_home_slot, p->h.home_slot.data(), (size_t)p->h.n_atoms * 8,
+                      hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        if (p->d_home_slot) (void)hipFree(p->d_home_slot);
+        p->d_home_slot = nullptr;
+        return hip_fail(e, what);
+    }
+    return HALO_OK;
+}
+
+static halo_status home_copy(halo_plan *p, const float *src, float *dst, void *stream,
+                             bool scatter, const char *what)
+{
+    halo_status st = check_exchange(p, scatter ? dst : const_cast<float *>(src), what, stream);
+    if (st != HALO_OK) return st;
+    const int64_t n = p->h.n_atoms;
+    if (n == 0) return HALO_OK;
+    if (!src || !dst) return fail(HALO_ERR_ARG, std::string(what) + ": NULL buffer");
+    const hipStream_t s = (hipStream_t)stream;
+    if ((st = ensure_home_slots(p, s, what)) != HALO_OK) return st;
+    uint32_t slot_bytes = (uint32_t)(p->h.total_slots * 12);
+    uint32_t value_bytes = (uint32_t)(n * 12);
+    const void *kernel = scatter ? (const void *)&k_scatter_home : (const void *)&k_gather_home;
+    uint32_t b0 = scatter ? value_bytes : slot_bytes, b1 = scatter ? slot_bytes : value_bytes;
+    void *args[] = {&src, &b0, &dst, &b1, &p->d_home_slot, (void *)&n};
+    hipError_t e = hipLaunchKernel(kernel, dim3((uint32_t)((n + kThreads - 1) / kThreads)),
+                                   dim3(kThreads), args, 0, s);
+    return e == hipSuccess ? HALO_OK : hip_fail(e, what);
+}
+
+halo_status halo_scatter_home(halo_plan *p, const float *values, float *slots, void *stream)
+{
+    return home_copy(p, values, slots, stream, true, "halo_scatter_home");
+}
+
+halo_status halo_gather_home(halo_plan *p, const float *slots, float *values, void *stream)
+{
+    return home_copy(p, slots, values, stream, false, "halo_gather_home");
+}
+
 halo_status halo_exchange_x_staged(halo_plan *p, float *x, void *stream)
 {
     return exchange_staged(p, false, x, stream, "halo_exchange_x_staged");

@@ -308,6 +308,20 @@ halo_status halo_exchange_f_staged(halo_plan *plan, float *f, void *stream);
  * discards the map. Same arguments as halo_exchange_x. */
 halo_status halo_exchange_x_direct(halo_plan *plan, float *x, void *stream);
 
+/* Copy a per-atom array of float triples into the home slots of a slot
+ * buffer (slots[home_slot[a]] = values[a]), or back out of them
+ * (values[a] = slots[home_slot[a]]), home_slot being halo_plan_home_slots.
+ * Fills x before halo_exchange_x, or collects the forces after
+ * halo_exchange_f, from or into the caller's atom order.
+ *   values : device, n_atoms*3 float32 (the positions' order at creation)
+ *   slots  : device, total_slots*3 float32; only home slots are touched
+ * One asynchronous launch on `stream`. For a plan built on the host, the
+ * first call uploads the home slots (n_atoms*8 bytes), synchronises and
+ * refuses a capturing stream; later calls can be captured. HALO_ERR_ARG for
+ * NULL buffers. */
+halo_status halo_scatter_home(halo_plan *plan, const float *values, float *slots, void *stream);
+halo_status halo_gather_home(halo_plan *plan, const float *slots, float *values, void *stream);
+
 /* Wait for the plan's work on `stream` and report a timeout raised inside a
  * kernel (HALO_ERR_TIMEOUT); poisons the plan in that case. */
 halo_status halo_plan_sync(halo_plan *plan, void *stream);

@@ -164,6 +164,21 @@ static int run_case(const Case *c, uint64_t seed, hipStream_t stream)
             ok = run_form(plans[k], xf[i].fn, xf[i].name, dev, x0, want, host, nf, stream);
         }
 
+    /* the same coordinates through halo_scatter_home from the atom order */
+    for (int k = 0; k < 2 && ok && n > 0; ++k) {
+        float *nan_fill = (float *)malloc((size_t)(nf + 3) * sizeof(float));
+        for (int64_t i = 0; i < nf; ++i) nan_fill[i] = NAN;
+        CHECK_HIP(hipMemcpyAsync(dev, nan_fill, (size_t)nf * sizeof(float), hipMemcpyHostToDevice,
+                                 stream));
+        CHECK_HALO(halo_scatter_home(plans[k], pos_dev, dev, stream));
+        CHECK_HALO(halo_exchange_x(plans[k], dev, stream));
+        CHECK_HIP(hipMemcpyAsync(host, dev, (size_t)nf * sizeof(float), hipMemcpyDeviceToHost,
+                                 stream));
+        CHECK_HIP(hipStreamSynchronize(stream));
+        ok = same_bits(host, want, nf, "scatter_home + x");
+        free(nan_fill);
+    }
+
     /* forces: small integers on halo slots, 0 on home slots, so that every
      * partial sum is exact and the atomic form is bitwise too */
     for (int64_t i = 0; i < nf; ++i) x0[i] = (float)((int)(next_u64(&s) % 17u) - 8);
@@ -176,6 +191,23 @@ static int run_case(const Case *c, uint64_t seed, hipStream_t stream)
             if (ff[i].fn == halo_exchange_f_transposed && pulses > 8) continue;
             ok = run_form(plans[k], ff[i].fn, ff[i].name, dev, x0, want, host, nf, stream);
         }
+
+    /* every atom's force back in atom order through halo_gather_home */
+    for (int k = 0; k < 2 && ok && n > 0; ++k) {
+        float *atoms_dev = NULL, *atoms = (float *)malloc((size_t)(3 * n) * sizeof(float));
+        CHECK_HIP(hipMalloc((void **)&atoms_dev, (size_t)(3 * n) * sizeof(float)));
+        CHECK_HIP(hipMemcpyAsync(dev, x0, (size_t)nf * sizeof(float), hipMemcpyHostToDevice,
+                                 stream));
+        CHECK_HALO(halo_exchange_f(plans[k], dev, stream));
+        CHECK_HALO(halo_gather_home(plans[k], dev, atoms_dev, stream));
+        CHECK_HIP(hipMemcpyAsync(atoms, atoms_dev, (size_t)(3 * n) * sizeof(float),
+                                 hipMemcpyDeviceToHost, stream));
+        CHECK_HIP(hipStreamSynchronize(stream));
+        for (int64_t a = 0; a < n && ok; ++a)
+            ok = same_bits(atoms + 3 * a, want + 3 * hs_o[a], 3, "gather_home");
+        CHECK_HIP(hipFree(atoms_dev));
+        free(atoms);
+    }
 
     /* an argument error is synchronous and leaves a message */
     if (ok && slots > 0) {

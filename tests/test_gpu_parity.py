@@ -487,3 +487,32 @@ def test_exchange_beside_a_gemm(torch, oracle_mod):
         assert_bitwise(f.cpu().numpy(), want_f, f"round {r} f")
     del c
     plan.sync()
+
+
+@pytest.mark.parametrize("built", ["host", "device"])
+def test_scatter_and_gather_home(torch, oracle_mod, built):
+    """halo_scatter_home fills exactly the home slots from the atom order;
+    after the exchanges, halo_gather_home returns every atom's force."""
+    w = W.WORKLOADS[3]
+    pos = W.workload_positions(w)
+    plan, o = setup_case(oracle_mod, pos, w.box, w.grid, w.cutoff)
+    if built == "device":
+        from .test_gpu_plan_device import device_plan
+        plan = device_plan(torch, pos, w.box, w.grid, w.cutoff)
+    say(f"scatter/gather home ({built} plan)")
+    x = torch.full((plan.total_slots, 3), float("nan"), device="cuda")
+    plan.scatter_home(torch.from_numpy(pos).cuda(), x)
+    plan.exchange_x(x)
+    base, n_home, n_halo = o.domains()
+    f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, 4)
+    f = torch.from_numpy(f0.copy()).cuda()
+    plan.exchange_f(f)
+    out = torch.empty(len(pos), 3, device="cuda")
+    plan.gather_home(f, out)
+    torch.cuda.synchronize()
+    plan.sync()
+    assert_bitwise(x.cpu().numpy(), o.exchange_x(o.home_filled(np.nan)), "x after scatter")
+    want_f = o.exchange_f(f0.copy())
+    assert_bitwise(out.cpu().numpy(), want_f[o.home_slots()], "gathered forces")
+    with pytest.raises(ValueError):
+        plan.scatter_home(torch.zeros(3, device="cuda"), x)
