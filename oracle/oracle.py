@@ -109,7 +109,10 @@ class Oracle:
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            lib().oracle_free(h)
+            try:
+                lib().oracle_free(h)
+            except Exception:  # interpreter shutdown: the module may be gone
+                pass
             self._h = None
 
     # -- plan read-out -------------------------------------------------------
