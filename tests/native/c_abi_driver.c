@@ -3,14 +3,18 @@
  * exchange form, compared bit for bit with the serial C oracle (test
  * infrastructure, linked only into this test program). Built by
  * __graft_entry__.build() and run by tests/test_gpu_c_abi.py on a GPU; exits
- * non-zero on the first difference or unexpected status.
+ * non-zero on the first difference or unexpected status. With --time it
+ * instead prints how long back-to-back exchanges take when a C caller issues
+ * them (GPU time and host time per call).
  */
+#define _POSIX_C_SOURCE 199309L  /* clock_gettime */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+#include <time.h>
 
 #include "halo.h"
 
@@ -234,8 +238,71 @@ static int run_case(const Case *c, uint64_t seed, hipStream_t stream)
     return ok;
 }
 
-int main(void)
+/* Host cost of issuing exchanges from C: back-to-back calls of the default
+ * exchanges on a plan of the given shape, timed with HIP events and with the
+ * host clock (printed, not checked). */
+static void time_case(const Case *c, hipStream_t stream)
 {
+    uint64_t s = 7;
+    const int64_t n = c->n;
+    float *pos = (float *)malloc((size_t)(3 * n) * sizeof(float));
+    for (int64_t a = 0; a < 3 * n; ++a) pos[a] = (float)(next_unit(&s) * c->box[a % 3]);
+    for (int64_t a = 0; a < n; ++a)
+        for (int d = 0; d < 3; ++d)
+            if (!(pos[3 * a + d] < c->box[d])) pos[3 * a + d] = nextafterf(c->box[d], 0.f);
+    halo_plan *p = NULL;
+    CHECK_HALO(halo_plan_create(pos, n, c->box, c->grid, c->cutoff, &p));
+    CHECK_HALO(halo_plan_upload(p));
+    const int64_t nf = 3 * halo_plan_total_slots(p);
+    float *x = NULL, *f = NULL;
+    CHECK_HIP(hipMalloc((void **)&x, (size_t)nf * sizeof(float)));
+    CHECK_HIP(hipMalloc((void **)&f, (size_t)nf * sizeof(float)));
+    CHECK_HIP(hipMemsetAsync(x, 0, (size_t)nf * sizeof(float), stream));
+    CHECK_HIP(hipMemsetAsync(f, 0, (size_t)nf * sizeof(float), stream));
+    const int reps = 2000;
+    hipEvent_t e0, e1;
+    CHECK_HIP(hipEventCreate(&e0));
+    CHECK_HIP(hipEventCreate(&e1));
+    for (int which = 0; which < 2; ++which) {
+        for (int i = 0; i < 50; ++i)
+            CHECK_HALO(which ? halo_exchange_f(p, f, stream) : halo_exchange_x(p, x, stream));
+        CHECK_HIP(hipStreamSynchronize(stream));
+        struct timespec t0, t1;
+        clock_gettime(CLOCK_MONOTONIC, &t0);
+        CHECK_HIP(hipEventRecord(e0, stream));
+        for (int i = 0; i < reps; ++i)
+            CHECK_HALO(which ? halo_exchange_f(p, f, stream) : halo_exchange_x(p, x, stream));
+        clock_gettime(CLOCK_MONOTONIC, &t1);
+        CHECK_HIP(hipEventRecord(e1, stream));
+        CHECK_HIP(hipEventSynchronize(e1));
+        float ms = 0.f;
+        CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
+        const double host_us = ((t1.tv_sec - t0.tv_sec) * 1e9 + (t1.tv_nsec - t0.tv_nsec)) / 1e3;
+        printf("time grid %dx%dx%d n=%lld %s: %.2f us per exchange on the GPU, %.2f us per "
+               "call on the host\n", c->grid[0], c->grid[1], c->grid[2], (long long)n,
+               which ? "f" : "x", ms * 1e3 / reps, host_us / reps);
+    }
+    CHECK_HALO(halo_plan_sync(p, stream));
+    CHECK_HIP(hipEventDestroy(e0));
+    CHECK_HIP(hipEventDestroy(e1));
+    CHECK_HIP(hipFree(x));
+    CHECK_HIP(hipFree(f));
+    halo_plan_destroy(p);
+    free(pos);
+}
+
+int main(int argc, char **argv)
+{
+    if (argc > 1 && strcmp(argv[1], "--time") == 0) {
+        const Case tc[] = {{{3.f, 3.f, 6.f}, {1, 1, 2}, 1.0f, 5400, HALO_SELECT_SLAB},
+                           {{6.f, 6.f, 6.f}, {2, 2, 2}, 1.0f, 21600, HALO_SELECT_SLAB}};
+        hipStream_t stream;
+        CHECK_HIP(hipSetDevice(0));
+        CHECK_HIP(hipStreamCreate(&stream));
+        for (size_t i = 0; i < sizeof(tc) / sizeof(tc[0]); ++i) time_case(&tc[i], stream);
+        CHECK_HIP(hipStreamDestroy(stream));
+        return 0;
+    }
     const Case cases[] = {
         {{6.f, 6.f, 6.f}, {2, 2, 2}, 1.0f, 21600, HALO_SELECT_SLAB},
         {{8.f, 8.f, 8.f}, {4, 4, 8}, 1.2f, 51200, HALO_SELECT_SLAB},
