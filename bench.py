@@ -343,8 +343,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; the exchange over several GPUs is a "
-              "design (peer-mapped stores over xGMI), not built. Use --gpus 1.", file=sys.stderr)
+        print("bench.py: the library exchanges halos between virtual domains on one GPU; the "
+              "exchange over several GPUs (peer-mapped stores over xGMI) is not implemented. "
+              "Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
