@@ -135,6 +135,10 @@ def test_edge_cases(torch, oracle_mod):
         ("all-in-one-domain", W.positions((1.0, 1.0, 1.0), 64, 4) + np.float32(2.5),
          (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
         ("one-atom", np.array([[0.1, 0.1, 0.1]], np.float32), (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
+        # -0 and the largest float below L in every coordinate, and atoms on faces
+        ("signed-zero-and-top", np.array(
+            [[-0.0, -0.0, -0.0], [np.nextafter(np.float32(4), np.float32(0))] * 3,
+             [2.0, -0.0, 2.0], [0.5, 3.5, -0.0]], np.float32), (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
     ]
     for name, pos, box, grid, rc in cases:
         plan, o = setup_case(oracle_mod, pos, box, grid, rc)

@@ -58,6 +58,9 @@ def test_plan_edge_cases(oracle_mod):
         (np.zeros((0, 3), np.float32), (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
         (W.positions((2.0, 2.0, 2.0), 50, 3), (2.0, 2.0, 2.0), (1, 1, 1), 0.9),
         (W.positions((1.0, 1.0, 1.0), 64, 4) + np.float32(2.5), (4.0, 4.0, 4.0), (2, 2, 2), 1.0),
+        (np.array([[-0.0, -0.0, -0.0], [np.nextafter(np.float32(4), np.float32(0))] * 3,
+                   [2.0, -0.0, 2.0], [0.5, 3.5, -0.0]], np.float32), (4.0, 4.0, 4.0),
+         (2, 2, 2), 1.0),
     ]
     for pos, box, grid, rc in cases:
         compare_plans(HaloPlan(pos, box, grid, rc), oracle_mod.Oracle(pos, box, grid, rc))
