@@ -201,6 +201,39 @@ def test_side_stream(torch, oracle_mod):
     assert_bitwise(x.cpu().numpy(), want, "side stream x")
 
 
+def test_independent_plans_on_concurrent_streams(torch, oracle_mod):
+    """Plans share no state: four plans (two workloads, two selections)
+    exchange on four streams at once, several times, and stay exact."""
+    cases = []
+    for wid, sel in ((3, "slab"), (3, "corner"), (4, "slab"), (5, "corner")):
+        w = W.WORKLOADS[wid]
+        pos = W.workload_positions(w)
+        plan = HaloPlan(pos, w.box, w.grid, w.cutoff, selection=sel)
+        o = oracle_mod.Oracle(pos, w.box, w.grid, w.cutoff, sel)
+        x0 = o.home_filled(np.nan)
+        base, n_home, n_halo = o.domains()
+        f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, wid)
+        plan.upload()
+        cases.append((plan, torch.cuda.Stream(), x0, o.exchange_x(x0.copy()), f0,
+                      o.exchange_f(f0.copy())))
+    torch.cuda.synchronize()
+    say("four plans on four streams")
+    for r in range(3):
+        bufs = []
+        for plan, s, x0, _, f0, _ in cases:
+            with torch.cuda.stream(s):
+                x = torch.from_numpy(x0.copy()).cuda()
+                f = torch.from_numpy(f0.copy()).cuda()
+                plan.exchange_x(x, s)
+                plan.exchange_f(f, s)
+            bufs.append((x, f))
+        torch.cuda.synchronize()
+        for (plan, s, _, want_x, _, want_f), (x, f) in zip(cases, bufs):
+            plan.sync(s)
+            assert_bitwise(x.cpu().numpy(), want_x, f"round {r} x")
+            assert_bitwise(f.cpu().numpy(), want_f, f"round {r} f")
+
+
 @pytest.mark.parametrize("impl", ["indexmap", "transposed"])
 def test_forced_timeout_poisons_and_reset_recovers(torch, oracle_mod, impl):
     """A withheld completion signal makes its dependents hit a tiny spin limit.
