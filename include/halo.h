@@ -213,7 +213,10 @@ halo_status halo_plan_upload(halo_plan *plan);
  * read. Runs the index-list form (halo_exchange_x_indexmap).
  *   x : device, total_slots*3 float32, 4-byte aligned. Home slots are read;
  *       every halo slot is overwritten with x[indexMap[i]] + coordShift.
- * Asynchronous; exchanges of one plan must be ordered on one stream.
+ * Asynchronous; exchanges of one plan must be ordered on one stream. Fused
+ * exchanges of different plans may run at once on different streams; their
+ * in-kernel waits then compete for the same compute units, and an
+ * interleaving that starves a producer ends in HALO_ERR_TIMEOUT, not a hang.
  * HIP graphs: every exchange form can be captured once the plan is uploaded
  * (halo_plan_upload, or any earlier exchange). The fused kernels take no
  * per-call argument: each launch infers its epoch (Algorithm 5's signal
