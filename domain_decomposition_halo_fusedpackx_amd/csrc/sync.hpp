@@ -30,13 +30,15 @@
 // A captured HIP graph replays its kernel arguments unchanged, so a replayed
 // launch cannot be handed its epoch; it infers it from launch counts on the
 // device (eager calls pass the epoch the host counted, and keep the counts
-// up to date for later replays). Work unit u of a launch (an item or a chunk) belongs to group
-// u mod kLaunchGroups; the units that wait are the group's members, and each
-// adds 1 to the group's 64-bit count once per launch, as its last action.
-// With m_g members, the count holds k * m_g + j while launch k + 1 runs,
-// j < m_g being the members of this launch already done; a member reads it
-// (with its first poll) before its own add, so k = count / m_g and the epoch
-// is k + 1, the same for every unit of the launch. 64 bits never wrap.
+// up to date for later replays). Work unit u of a launch (an item or a
+// chunk) belongs to group u mod kLaunchGroups; the units that wait are the
+// group's members, and each adds 1 to the group's 64-bit count once per
+// launch. With m_g members, the count holds k * m_g + j while launch k + 1
+// runs, j < m_g being the members of this launch that have added. A launch
+// that infers its epoch adds as each member's last action, after the member
+// read the count (with its first poll), so k = count / m_g and the epoch is
+// k + 1, the same for every unit of the launch. A launch that was handed
+// its epoch reads no count and adds early. 64 bits never wrap.
 #pragma once
 
 #include <hip/hip_runtime.h>
