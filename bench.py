@@ -88,15 +88,34 @@ def cpu_baseline(w, pos, seconds: float):
             if (el >= budget and reps >= 3) or reps >= 10000:
                 return reps, el
 
-    rx, tx = timed(lambda: o.exchange_x(x), seconds / 2)
-    rf, tf = timed(lambda: o.exchange_f(f), seconds / 2)
+    # one thread, pinned to one of the cores this process may use
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
+    try:
+        rx, tx = timed(lambda: o.exchange_x(x), seconds / 2)
+        rf, tf = timed(lambda: o.exchange_f(f), seconds / 2)
+    finally:
+        os.sched_setaffinity(0, allowed)
     us_x, us_f = tx / rx * 1e6, tf / rf * 1e6
     return {"value": entries / ((us_x + us_f) * 1e-6), "unit": "halo atoms/s", "cores": 1,
             "kind": "oracle", "us_per_exchange": {"x": us_x, "f": us_f},
             "sample": f"whole {w.name} workload ({entries} halo entries): {rx} coordinate "
                       f"exchanges in {tx:.2f} s, then {rf} force exchanges in {tf:.2f} s; "
-                      f"serial C (gcc -O2), 1 thread",
-            "host_cpus": os.cpu_count(), "host_cpu": platform.processor() or platform.machine()}
+                      f"serial C (gcc -O2), 1 thread pinned to core {core}",
+            "host_cpus": os.cpu_count(), "host_cpus_allowed": len(allowed),
+            "host_cpu": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def time_loop(torch, fn, n):
