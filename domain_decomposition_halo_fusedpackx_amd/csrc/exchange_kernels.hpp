@@ -536,8 +536,11 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
 // chunk, regions of later pulses first, home slots last. Every thread keeps
 // the running sum of its target slot in registers and adds the sources of
 // its pulses in strict reverse order; before pulse p it waits until the
-// sources (the receiver's region of pulse p) hold their final sums. Each
-// target slot is read once and written once.
+// sources (the receiver's region of pulse p) hold their final sums. Every
+// slot of the chunk is read once and written once, the ones no pulse sends
+// with the value they were read with: no other work unit writes them, and
+// whole-line stores cost less than the byte-masked stores that leaving them
+// out would make.
 template <int EPT>
 __global__ __launch_bounds__(kThreads) void k_pull_f(
     float *f, uint32_t f_bytes, const uint8_t *__restrict__ slot_mask,
@@ -602,13 +605,10 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
         for (int j = 0; j < EPT; ++j)
             if (src[j] != kInvalid) v[j] = v[j] + add[j];
     }
-    uint32_t dst[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) dst[j] = m[j] ? off[j] : kInvalid;
     if (zone >= 0) {
         // region sums are read by another domain in this launch
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) store3<kShared>(rf, dst[j], v[j]);
+        for (int j = 0; j < EPT; ++j) store3<kShared>(rf, off[j], v[j]);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         halo::wait_vmem();
         __syncthreads();
@@ -618,7 +618,7 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
                                    __HIP_MEMORY_SCOPE_AGENT);
     } else {
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) store3<kStream>(rf, dst[j], v[j]);
+        for (int j = 0; j < EPT; ++j) store3<kStream>(rf, off[j], v[j]);
     }
     halo::count_late(ls, waited);
 }
