@@ -90,7 +90,7 @@ def cpu_baseline(w, pos, seconds: float):
 
     # one thread, pinned to one of the cores this process may use
     allowed = os.sched_getaffinity(0)
-    core = min(allowed)
+    core = max(allowed)  # the last one: core 0 also takes the host's interrupts
     os.sched_setaffinity(0, {core})
     try:
         rx, tx = timed(lambda: o.exchange_x(x), seconds / 2)
