@@ -921,6 +921,11 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     }
     P.n_entries = entries;
     P.has_chunks = plan_has_chunks(P);
+    if (!P.has_chunks) {  // a rebuild may have left those of the previous plan
+        P.chunks.clear();
+        P.chunk_forder.clear();
+        P.slot_mask.clear();
+    }
     P.chunk_slots = item_entries;
     make_items(P, item_entries, false);
     const std::vector<Piece> pieces =

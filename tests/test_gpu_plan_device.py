@@ -194,3 +194,42 @@ def test_rebuild_of_a_host_plan_and_failure(torch, oracle_mod):
     torch.cuda.synchronize()
     hp.sync()
     assert_bitwise(xt.cpu().numpy(), o.exchange_x(x0.copy()), "after a failed rebuild")
+
+
+def test_rebuild_across_the_transposed_pulse_limit(torch, oracle_mod):
+    """A box change can take a plan past the 8 pulses the transposed form
+    handles and back: the rebuilt plan drops its chunks (the force exchange
+    falls back to the index-list kernel, stress mode included) and gets them
+    again, with exchanges exact throughout."""
+    grid, rc = (10, 1, 1), 1.0
+    boxes = [(3.0, 2.0, 2.0), (1.2, 2.0, 2.0), (3.0, 2.0, 2.0)]  # 4, then 9, then 4 pulses
+    dp = None
+    for i, box in enumerate(boxes):
+        pos = W.positions(box, 600, 90 + i)
+        o = oracle_mod.Oracle(pos, box, grid, rc)
+        say(f"rebuild {i}: box {box}, {o.n_pulse} pulses")
+        if dp is None:
+            dp = device_plan(torch, pos, box, grid, rc)
+        else:
+            dp.rebuild_on_device(torch.from_numpy(pos).cuda(), box)
+        compare_plans(dp, o)
+        base, n_home, n_halo = o.domains()
+        f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, 7 + i)
+        want = o.exchange_f(f0.copy())
+        for seed in (0, 11):
+            dp.debug_stress(seed)
+            f = torch.from_numpy(f0.copy()).cuda()
+            dp.exchange_f(f)
+            torch.cuda.synchronize()
+            dp.sync()
+            assert_bitwise(f.cpu().numpy(), want, f"rebuild {i} f (stress seed {seed})")
+        dp.debug_stress(0)
+        f = torch.from_numpy(f0.copy()).cuda()
+        if o.n_pulse > 8:
+            with pytest.raises(HaloError):
+                dp.exchange_f_transposed(f)
+        else:
+            dp.exchange_f_transposed(f)
+            torch.cuda.synchronize()
+            dp.sync()
+            assert_bitwise(f.cpu().numpy(), want, f"rebuild {i} f transposed")
