@@ -492,11 +492,12 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
     }
     build_ranks<EPT>(sh, m, umask, n_pulse);
     if (c->zone >= 0) {
-        // region slots are filled by another domain in this launch
+        // region slots are filled by another domain in this launch; every
+        // slot is loaded, sent or not, so that the loads cover whole lines
         halo::wait_one(c->xwait, x_arrivals, state, n_dom * n_pulse, false, ls.lg, ls.epoch,
                        spin_limit, err_word);
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) v[j] = load3<kShared>(rx, m[j] ? off[j] : kInvalid);
+        for (int j = 0; j < EPT; ++j) v[j] = load3<kShared>(rx, off[j]);
     }
     for (int32_t p = 0; p < n_pulse; ++p) {
         if (!((umask >> p) & 1u)) continue;
