@@ -433,8 +433,10 @@ def main():
     gbs_f = E * BYTES_F / (ms_f * 1e-3) / 1e9
     dom = "f" if ms_f >= ms_x else "x"
     sha = kernel_source_sha()
+    # the kernels the default exchanges run (halo_exchange_x / _f choose by size)
+    x_default = "push_x" if E >= (1 << 20) else "pack_fused"
     f_default = "pull_f" if E >= (1 << 18) else "unpack_fused"
-    kernel_of = {("fused", "x"): "pack_fused", ("fused", "f"): f_default,
+    kernel_of = {("fused", "x"): x_default, ("fused", "f"): f_default,
                  ("indexmap", "x"): "pack_fused", ("indexmap", "f"): "unpack_fused",
                  ("transposed", "x"): "push_x", ("transposed", "f"): "pull_f",
                  ("pulsewise", "x"): "pack_pulse", ("pulsewise", "f"): "unpack_pulse"}

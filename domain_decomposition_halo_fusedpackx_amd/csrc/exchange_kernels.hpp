@@ -402,53 +402,70 @@ __global__ __launch_bounds__(kThreads) void k_unpack_atomic(
 // ---- transposed form: per-slot pulse masks --------------------------------
 
 // Pulse ranks of one chunk. Thread t owns slots first + t + j*256 (j < EPT),
-// i.e. slot order is row-major over (j, wave, lane). For pulse p the slot's
-// entry of indexMap_p is chunk.rank[p] plus the number of earlier slots of
-// the chunk with bit p: a wave ballot gives the count within the wave, and an
-// exclusive prefix over (row, wave) in LDS, built once per pulse, the rest.
-template <int EPT>
-struct Ranks {
-    uint32_t cnt[halo::kMaxMaskPulses][EPT * 4];
-    uint32_t off[halo::kMaxMaskPulses][EPT * 4];
-};
+// i.e. slot order is row-major over rows (j, wave) of 64 slots. For pulse p
+// the slot's entry of indexMap_p is chunk.rank[p], plus the chunk's bit-p
+// slots in earlier rows, plus those earlier in its own row (a wave ballot).
+// The middle term depends on the masks only; the plan keeps it in a table
+// built once by k_chunk_rows (uint16, since a chunk holds at most 2048
+// slots): rows[((chunk * 4 + wave) * n_pulse + p) * EPT + j].
+__device__ __forceinline__ size_t chunk_rows_at(int32_t chunk, int wave, int32_t n_pulse, int ept)
+{
+    return ((size_t)chunk * 4 + (size_t)wave) * (size_t)n_pulse * (size_t)ept;
+}
 
-// Count, per pulse and (row, wave), the slots with the pulse's bit, then turn
-// the counts into exclusive prefixes (thread k computes entry k of pulse
-// k / (EPT*4) from up to EPT*4 independent LDS reads). Ends with a workgroup
-// barrier.
+// Builds the row table of every chunk: per pulse and row, the count of the
+// row's bit-p slots (ballots), then exclusive prefixes over the rows.
 template <int EPT>
-__device__ __forceinline__ void build_ranks(Ranks<EPT> &sh, const uint32_t *m, uint32_t umask,
-                                            int32_t n_pulse)
+__global__ __launch_bounds__(kThreads) void k_chunk_rows(const uint8_t *__restrict__ slot_mask,
+                                                         const halo::Chunk *__restrict__ chunks,
+                                                         int32_t n_pulse,
+                                                         uint16_t *__restrict__ rows)
 {
     constexpr int kRow = EPT * 4;
+    __shared__ uint32_t cnt[halo::kMaxMaskPulses][kRow];
+    const halo::Chunk *c = chunks + blockIdx.x;
+    const int32_t first = c->first, count = c->count;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint32_t m[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        m[j] = e < count ? (uint32_t)slot_mask[first + e] : 0u;
+    }
     for (int32_t p = 0; p < n_pulse; ++p) {
-        if (!((umask >> p) & 1u)) continue;
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
             const uint64_t b = __ballot((m[j] >> p) & 1u);
-            if (lane == 0) sh.cnt[p][j * 4 + wave] = (uint32_t)__popcll(b);
+            if (lane == 0) cnt[p][j * 4 + wave] = (uint32_t)__popcll(b);
         }
     }
     __syncthreads();
     for (int k = threadIdx.x; k < n_pulse * kRow; k += kThreads) {
-        const int p = k / kRow, e = k % kRow;
-        if (!((umask >> p) & 1u)) continue;
+        const int p = k / kRow, q = k % kRow;
         uint32_t acc = 0;
-#pragma unroll
-        for (int q = 0; q < kRow; ++q)
-            if (q < e) acc += sh.cnt[p][q];
-        sh.off[p][e] = acc;
+        for (int r = 0; r < q; ++r) acc += cnt[p][r];
+        rows[chunk_rows_at((int32_t)blockIdx.x, q % 4, n_pulse, EPT) + (size_t)p * EPT + q / 4] =
+            (uint16_t)acc;
     }
-    __syncthreads();
+}
+
+// The row table entries of this thread's wave, one per lane (lane p*EPT + j
+// holds pulse p, row j), loaded with the chunk's masks.
+template <int EPT>
+__device__ __forceinline__ uint32_t load_wave_rows(const uint16_t *rows, int32_t chunk,
+                                                   int32_t n_pulse)
+{
+    const int lane = threadIdx.x & 63;
+    const size_t at = chunk_rows_at(chunk, threadIdx.x >> 6, n_pulse, EPT);
+    return lane < n_pulse * EPT ? (uint32_t)rows[at + lane] : 0u;
 }
 
 // Position among the chunk's bit-p slots of this thread's row-j slot.
 template <int EPT>
-__device__ __forceinline__ uint32_t rank_in_chunk(const Ranks<EPT> &sh, int32_t p, int j, bool bit)
+__device__ __forceinline__ uint32_t rank_in_chunk(uint32_t wave_rows, int32_t p, int j, bool bit)
 {
     const uint64_t b = __ballot(bit);
-    return sh.off[p][j * 4 + (threadIdx.x >> 6)] +
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_rows, p * EPT + j) +
            __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
 }
@@ -462,12 +479,12 @@ __device__ __forceinline__ uint32_t rank_in_chunk(const Ranks<EPT> &sh, int32_t 
 template <int EPT>
 __global__ __launch_bounds__(kThreads) void k_push_x(
     float *x, uint32_t x_bytes, const uint8_t *__restrict__ slot_mask,
-    const halo::Chunk *__restrict__ chunks, const int32_t *__restrict__ dest_start,
-    const float4 *__restrict__ shift4, const uint32_t *__restrict__ x_arrivals, uint32_t *state,
-    int32_t n_dom, int32_t n_pulse, uint32_t *groups, const uint32_t *__restrict__ members,
-    uint32_t host_epoch, uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Stress st)
+    const halo::Chunk *__restrict__ chunks, const uint16_t *__restrict__ rows,
+    const int32_t *__restrict__ dest_start, const float4 *__restrict__ shift4,
+    const uint32_t *__restrict__ x_arrivals, uint32_t *state, int32_t n_dom, int32_t n_pulse,
+    uint32_t *groups, const uint32_t *__restrict__ members, uint32_t host_epoch,
+    uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Stress st)
 {
-    __shared__ Ranks<EPT> sh;
     const uint32_t u = st.order ? (uint32_t)st.order[blockIdx.x] : blockIdx.x;
     if (st.seed) stress_delay(st.seed, u);
     halo::LaunchState ls = halo::launch_state(groups, members, u, host_epoch);
@@ -485,12 +502,12 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
         m[j] = e < count ? (uint32_t)slot_mask[first + e] : 0u;
         off[j] = e < count ? (uint32_t)(first + e) * 12u : kInvalid;
     }
+    const uint32_t wrows = load_wave_rows<EPT>(rows, (int32_t)u, n_pulse);
     if (c->zone < 0) {
         // home slots are final before the launch: load them with the masks
 #pragma unroll
         for (int j = 0; j < EPT; ++j) v[j] = load3<kStream>(rx, off[j]);
     }
-    build_ranks<EPT>(sh, m, umask, n_pulse);
     if (c->zone >= 0) {
         // region slots are filled by another domain in this launch; every
         // slot is loaded, sent or not, so that the loads cover whole lines
@@ -508,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
             const bool bit = (m[j] >> p) & 1u;
-            const uint32_t r = rank_in_chunk<EPT>(sh, p, j, bit);
+            const uint32_t r = rank_in_chunk<EPT>(wrows, p, j, bit);
             dst[j] = bit ? (uint32_t)(base + (int32_t)r) * 12u : kInvalid;
         }
         if (p + 1 < n_pulse) {
@@ -546,12 +563,12 @@ template <int EPT>
 __global__ __launch_bounds__(kThreads) void k_pull_f(
     float *f, uint32_t f_bytes, const uint8_t *__restrict__ slot_mask,
     const halo::Chunk *__restrict__ chunks, const int32_t *__restrict__ forder,
-    const int32_t *__restrict__ dest_start, const int32_t *__restrict__ send_to,
-    const uint32_t *__restrict__ zone_chunks, uint32_t *state, int32_t n_dom, int32_t n_pulse,
-    uint32_t *groups, const uint32_t *__restrict__ members, uint32_t host_epoch,
-    uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Stress st)
+    const uint16_t *__restrict__ rows, const int32_t *__restrict__ dest_start,
+    const int32_t *__restrict__ send_to, const uint32_t *__restrict__ zone_chunks,
+    uint32_t *state, int32_t n_dom, int32_t n_pulse, uint32_t *groups,
+    const uint32_t *__restrict__ members, uint32_t host_epoch, uint32_t spin_limit,
+    uint32_t *err_word, int32_t withhold, Stress st)
 {
-    __shared__ Ranks<EPT> sh;
     const int32_t u = st.order ? st.order[blockIdx.x] : forder[blockIdx.x];
     if (st.seed) stress_delay(st.seed, (uint32_t)u);
     halo::LaunchState ls = halo::launch_state(groups, members, (uint32_t)u, host_epoch);
@@ -569,12 +586,12 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
         m[j] = e < count ? (uint32_t)slot_mask[first + e] : 0u;
         off[j] = e < count ? (uint32_t)(first + e) * 12u : kInvalid;
     }
+    const uint32_t wrows = load_wave_rows<EPT>(rows, (int32_t)u, n_pulse);
     // Only this workgroup writes these slots, and nobody before it in this
     // launch: plain loads (streamed, read once), issued together with the
     // masks.
 #pragma unroll
     for (int j = 0; j < EPT; ++j) v[j] = load3<kStream>(rf, off[j]);
-    build_ranks<EPT>(sh, m, umask, n_pulse);
     bool waited = false;
     for (int32_t p = n_pulse - 1; p >= 0; --p) {
         if (!((umask >> p) & 1u)) continue;
@@ -591,7 +608,7 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
             const bool bit = (m[j] >> p) & 1u;
-            const uint32_t r = rank_in_chunk<EPT>(sh, p, j, bit);
+            const uint32_t r = rank_in_chunk<EPT>(wrows, p, j, bit);
             src[j] = bit ? (uint32_t)(base + (int32_t)r) * 12u : kInvalid;
         }
         f3v add[EPT];

@@ -54,7 +54,7 @@ void free_device(halo_plan *p)
                     (void *)p->d_forder, (void *)p->d_dest_start, (void *)p->d_shift4,
                     (void *)p->d_x_arrivals, (void *)p->d_zone_chunks, (void *)p->d_local_map,
                     (void *)p->d_home_slot, (void *)p->d_stress, (void *)p->d_origin,
-                    (void *)p->d_members})
+                    (void *)p->d_members, (void *)p->d_rows})
         if (q) (void)hipFree(q);
     if (p->h_err) (void)hipHostFree(p->h_err);
     p->d_idx = p->d_recv_from = p->d_send_to = p->d_forder = p->d_dest_start = nullptr;
@@ -66,6 +66,8 @@ void free_device(halo_plan *p)
     p->d_stage = p->d_shift4 = nullptr;
     p->d_origin = nullptr;
     p->d_members = nullptr;
+    p->d_rows = nullptr;
+    p->rows_cap = 0;
     p->d_seg_items = p->d_state = p->d_x_arrivals = p->d_zone_chunks = nullptr;
     p->d_mask = nullptr;
     p->d_chunks = nullptr;
@@ -95,7 +97,8 @@ int ept_for(int32_t item_entries)
 // Kernel entry points for the plan's items-per-thread.
 struct Kernels {
     const void *pack_fused, *unpack_fused, *pack_pulse, *unpack_pulse, *push_x, *pull_f,
-        *unpack_atomic, *stage_pack, *stage_move, *stage_unpack, *origin_pulse, *gather_x;
+        *unpack_atomic, *stage_pack, *stage_move, *stage_unpack, *origin_pulse, *gather_x,
+        *chunk_rows;
 };
 
 template <int EPT>
@@ -106,7 +109,8 @@ Kernels kernels_for()
             (const void *)&k_push_x<EPT>,        (const void *)&k_pull_f<EPT>,
             (const void *)&k_unpack_atomic<EPT>, (const void *)&k_stage_pack<EPT>,
             (const void *)&k_stage_move<EPT>,    (const void *)&k_stage_unpack<EPT>,
-            (const void *)&k_origin_pulse<EPT>,  (const void *)&k_gather_x<EPT>};
+            (const void *)&k_origin_pulse<EPT>,  (const void *)&k_gather_x<EPT>,
+            (const void *)&k_chunk_rows<EPT>};
 }
 
 Kernels kernels(int32_t item_entries)
@@ -200,18 +204,19 @@ hipError_t launch_chunks(halo_plan *p, bool force_dir, float *buf, hipStream_t s
         const uint32_t *members = launch_members(p, halo::kFamChunksF);
         uint32_t epoch = launch_epoch_arg(p, halo::kFamChunksF, s);
         Stress st = stress_of(p, kOrderChunksF);
-        void *args[] = {&buf, &bytes, &p->d_mask, &p->d_chunks, &p->d_forder, &p->d_dest_start,
-                        &p->d_send_to, &p->d_zone_chunks, &state, &n_dom, &n_pulse, &groups,
-                        &members, &epoch, &p->spin_limit, &p->d_err, &p->withhold, &st};
+        void *args[] = {&buf, &bytes, &p->d_mask, &p->d_chunks, &p->d_forder, &p->d_rows,
+                        &p->d_dest_start, &p->d_send_to, &p->d_zone_chunks, &state, &n_dom,
+                        &n_pulse, &groups, &members, &epoch, &p->spin_limit, &p->d_err,
+                        &p->withhold, &st};
         return hipLaunchKernel(k.pull_f, dim3(n), dim3(kThreads), args, 0, s);
     }
     uint32_t *groups = launch_groups(p, halo::kFamChunksX);
     const uint32_t *members = launch_members(p, halo::kFamChunksX);
     uint32_t epoch = launch_epoch_arg(p, halo::kFamChunksX, s);
     Stress st = stress_of(p, kOrderChunksX);
-    void *args[] = {&buf, &bytes, &p->d_mask, &p->d_chunks, &p->d_dest_start, &p->d_shift4,
-                    &p->d_x_arrivals, &state, &n_dom, &n_pulse, &groups, &members, &epoch,
-                    &p->spin_limit, &p->d_err, &p->withhold, &st};
+    void *args[] = {&buf, &bytes, &p->d_mask, &p->d_chunks, &p->d_rows, &p->d_dest_start,
+                    &p->d_shift4, &p->d_x_arrivals, &state, &n_dom, &n_pulse, &groups,
+                    &members, &epoch, &p->spin_limit, &p->d_err, &p->withhold, &st};
     return hipLaunchKernel(k.push_x, dim3(n), dim3(kThreads), args, 0, s);
 }
 
@@ -303,6 +308,11 @@ halo_status ensure_uploaded(halo_plan *p)
         free_device(p);
         return hip_fail(e, "halo_plan_upload");
     }
+    if (h.has_chunks && !h.chunks.empty() &&
+        (e = halo::plan_chunk_rows(p, p->d_mask, p->d_chunks, nullptr)) != hipSuccess) {
+        free_device(p);
+        return hip_fail(e, "halo_plan_upload");
+    }
     // two counter blocks (work items, chunks), each X then F, and the launch
     // counts; 128 B per counter
     p->state_words = halo::state_words_for(h.seg.size());
@@ -323,6 +333,30 @@ halo_status ensure_uploaded(halo_plan *p)
 }  // namespace
 
 int halo::plan_upload(halo_plan *p) { return ensure_uploaded(p); }
+
+hipError_t halo::plan_chunk_rows(halo_plan *p, const uint8_t *mask, const Chunk *chunks,
+                                 hipStream_t s)
+{
+    const HostPlan &h = p->h;
+    const int ept = ept_for(h.chunk_slots);
+    const size_t need = h.chunks.size() * 4 * (size_t)h.n_pulse * (size_t)ept;
+    if (need == 0) return hipSuccess;
+    hipError_t e;
+    if (p->rows_cap < need) {
+        if (p->d_rows) (void)hipFree(p->d_rows);
+        p->d_rows = nullptr;
+        p->rows_cap = 0;
+        if ((e = hipMalloc((void **)&p->d_rows, need * sizeof(uint16_t))) != hipSuccess) {
+            p->d_rows = nullptr;
+            return e;
+        }
+        p->rows_cap = need;
+    }
+    int32_t n_pulse = h.n_pulse;
+    void *args[] = {&mask, &chunks, &n_pulse, &p->d_rows};
+    return hipLaunchKernel(kernels(h.chunk_slots).chunk_rows, dim3((uint32_t)h.chunks.size()),
+                           dim3(kThreads), args, 0, s);
+}
 
 namespace {
 
@@ -628,14 +662,17 @@ halo_status halo_plan_upload(halo_plan *p)
 }
 
 // The fused defaults take, per direction, the form that measured fastest:
-// the index-list kernel for coordinates at every size; for forces the
-// transposed kernel from 2^18 entries up (4x4x4 and 8x8x8 boxes), the
-// index-list kernel below that and for plans with more than 8 pulses.
+// the transposed kernel from 2^20 entries up for coordinates (the 8x8x8
+// box) and from 2^18 up for forces (4x4x4 and 8x8x8), the index-list kernel
+// below that and for plans with more than 8 pulses.
+constexpr int64_t kTransposedCoordMinEntries = 1 << 20;
 constexpr int64_t kTransposedForceMinEntries = 1 << 18;
 
 halo_status halo_exchange_x(halo_plan *p, float *x, void *stream)
 {
-    return halo_exchange_x_indexmap(p, x, stream);
+    if (p && (!p->h.has_chunks || (int64_t)p->h.n_entries < kTransposedCoordMinEntries))
+        return halo_exchange_x_indexmap(p, x, stream);
+    return halo_exchange_x_transposed(p, x, stream);
 }
 
 halo_status halo_exchange_f(halo_plan *p, float *f, void *stream)

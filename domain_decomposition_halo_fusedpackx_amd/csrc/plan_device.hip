@@ -1050,6 +1050,8 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         k_item_masks<<<(unsigned)n_items, kBT, 0, st>>>(items, local_map, sg, nd, np);
         HALO_TRY(hipGetLastError(), "launch");
     }
+    if (P.has_chunks && !P.chunks.empty())
+        HALO_TRY(plan_chunk_rows(pl, mask, chunks, st), "the chunks' row table");
 
     // -- counters and the error word --------------------------------------------------------
     const size_t words = state_words_for(nseg);

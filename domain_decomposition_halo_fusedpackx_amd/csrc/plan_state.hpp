@@ -55,6 +55,8 @@ struct halo_plan {
     uint8_t *d_mask = nullptr;
     halo::Chunk *d_chunks = nullptr;
     int32_t *d_forder = nullptr;
+    uint16_t *d_rows = nullptr;  // per chunk, wave, pulse and row: bit-p slots in earlier rows
+    size_t rows_cap = 0;         // entries d_rows holds
     int32_t *d_dest_start = nullptr;
     float *d_shift4 = nullptr;
     uint32_t *d_x_arrivals = nullptr;
@@ -85,6 +87,11 @@ namespace halo {
 // already on the device are kept), the counters and the error word.
 // Returns a halo_status code; the message goes to halo_last_error.
 int plan_upload(halo_plan *p);
+
+// (Re)builds the row table of the transposed kernels (d_rows) from the
+// plan's device masks and chunks, on stream s; allocates when it must grow.
+hipError_t plan_chunk_rows(halo_plan *p, const uint8_t *mask, const Chunk *chunks,
+                           hipStream_t s);
 
 // Free the arenas of a device-built plan and clear the pointers into them.
 void free_device_build(halo_plan *p);

@@ -210,7 +210,10 @@ halo_status halo_plan_upload(halo_plan *plan);
  * the entries of each indexMap below depOffset (home slots) are packed
  * immediately; entries that forward atoms received in earlier pulses wait,
  * inside the kernel, on the arrival counters of exactly the regions they
- * read. Runs the index-list form (halo_exchange_x_indexmap).
+ * read. Runs the transposed form (halo_exchange_x_transposed) for plans of
+ * at least 2^20 indexMap entries, the index-list form
+ * (halo_exchange_x_indexmap) for smaller plans and for plans with more than
+ * 8 pulses.
  *   x : device, total_slots*3 float32, 4-byte aligned. Home slots are read;
  *       every halo slot is overwritten with x[indexMap[i]] + coordShift.
  * Asynchronous; exchanges of one plan must be ordered on one stream. Fused
@@ -252,9 +255,9 @@ halo_status halo_exchange_f_indexmap(halo_plan *plan, float *f, void *stream);
 /* Transposed form of the fused exchanges: the indexMaps stored as one pulse
  * mask per slot; a workgroup takes a run of slots of one domain inside one
  * zone (home slots, or the region of one pulse). Coordinates: each slot is
- * read once and stored, plus coordShift, to every pulse it carries, at the
- * rank given by a wave-ballot prefix count; region runs wait for their
- * region to arrive. Forces: each target slot keeps its running sum in a
+ * read once and stored, plus coordShift, to every pulse it carries, at its
+ * rank among the run's slots of that pulse (a per-row count the plan keeps,
+ * plus a wave ballot); region runs wait for their region to arrive. Forces: each target slot keeps its running sum in a
  * register and adds its pulses' sources in strict reverse order, waiting
  * until each source holds its final sum; every target is read and written
  * once. HALO_ERR_ARG for plans with more than 8 pulses. */
