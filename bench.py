@@ -435,7 +435,7 @@ def main():
     sha = kernel_source_sha()
     # the kernels the default exchanges run (halo_exchange_x / _f choose by size)
     x_default = "push_x" if E >= (1 << 20) else "pack_fused"
-    f_default = "pull_f" if E >= (1 << 18) else "unpack_fused"
+    f_default = "pull_f" if E >= (1 << 14) and plan0.num_pulses <= 3 else "unpack_fused"
     kernel_of = {("fused", "x"): x_default, ("fused", "f"): f_default,
                  ("indexmap", "x"): "pack_fused", ("indexmap", "f"): "unpack_fused",
                  ("transposed", "x"): "push_x", ("transposed", "f"): "pull_f",

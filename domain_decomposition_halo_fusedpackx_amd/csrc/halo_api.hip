@@ -661,12 +661,16 @@ halo_status halo_plan_upload(halo_plan *p)
     return ensure_uploaded(p);
 }
 
-// The fused defaults take, per direction, the form that measured fastest:
-// the transposed kernel from 2^20 entries up for coordinates (the 8x8x8
-// box) and from 2^18 up for forces (4x4x4 and 8x8x8), the index-list kernel
-// below that and for plans with more than 8 pulses.
+// The fused defaults take, per direction, the form that measured fastest.
+// Coordinates: the transposed kernel from 2^20 entries up (the 8x8x8 box),
+// the index-list kernel below. Forces: the transposed kernel from 2^14
+// entries up for plans of at most 3 pulses (2x2x2, 4x4x4 and 8x8x8 boxes);
+// the index-list kernel for smaller plans, which are latency-bound, and for
+// more pulses, each of which adds a dependent stage to the transposed
+// kernel's work units (the 4x4x8 box with its two z pulses).
 constexpr int64_t kTransposedCoordMinEntries = 1 << 20;
-constexpr int64_t kTransposedForceMinEntries = 1 << 18;
+constexpr int64_t kTransposedForceMinEntries = 1 << 14;
+constexpr int32_t kTransposedForceMaxPulses = 3;
 
 halo_status halo_exchange_x(halo_plan *p, float *x, void *stream)
 {
@@ -677,7 +681,8 @@ halo_status halo_exchange_x(halo_plan *p, float *x, void *stream)
 
 halo_status halo_exchange_f(halo_plan *p, float *f, void *stream)
 {
-    if (p && (!p->h.has_chunks || (int64_t)p->h.n_entries < kTransposedForceMinEntries))
+    if (p && (!p->h.has_chunks || (int64_t)p->h.n_entries < kTransposedForceMinEntries ||
+              p->h.n_pulse > kTransposedForceMaxPulses))
         return halo_exchange_f_indexmap(p, f, stream);
     return halo_exchange_f_transposed(p, f, stream);
 }
