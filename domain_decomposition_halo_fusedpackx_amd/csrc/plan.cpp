@@ -166,48 +166,86 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
     }
     int rc = plan_geometry(n_atoms, box, grid, cutoff, selection, P, msg);
     if (rc != kOk) return rc;
-    for (int64_t a = 0; a < n_atoms; ++a)
-        for (int d = 0; d < 3; ++d) {
-            float v = pos[3 * a + d];
-            if (!std::isfinite(v) || !(v >= 0.f) || !(v < box[d])) {
-                msg = "halo_plan_create: atom " + std::to_string((long long)a) +
-                      " lies outside [0, L) or is not finite";
-                return kErrRange;
-            }
-        }
 
+    // Atoms in blocks of kBlock, processed in parallel. Per block: the range
+    // check (the first bad atom of the lowest block is reported, as a serial
+    // scan would), the owner, and the block's count per domain.
+    constexpr int64_t kBlock = 1 << 15;
+    const int32_t n_blocks = (int32_t)((n_atoms + kBlock - 1) / kBlock);
+    std::vector<int32_t> owner((size_t)n_atoms);
+    std::vector<int64_t> bad(n_blocks, -1);
+    std::vector<int32_t> block_count((size_t)n_blocks * P.n_dom, 0);
     // Position in units of the domain width; a rounding up to n is pulled
     // back below n so that the cell index stays in range.
-    std::vector<double> scaled((size_t)n_atoms * 3);
-    std::vector<int32_t> owner((size_t)n_atoms);
+    double top[3];
+    for (int d = 0; d < 3; ++d) top[d] = std::nextafter((double)grid[d], 0.0);
+    auto scaled = [&](float v, int d) {
+        const double t = (double)v / P.width[d];
+        return t > top[d] ? top[d] : t;
+    };
+    {
+        parallel_for(n_blocks, [&](int32_t b) {
+            const int64_t a0 = (int64_t)b * kBlock, a1 = std::min(n_atoms, a0 + kBlock);
+            int32_t *cnt = &block_count[(size_t)b * P.n_dom];
+            for (int64_t a = a0; a < a1; ++a) {
+                int32_t c[3];
+                for (int d = 0; d < 3; ++d) {
+                    const float v = pos[3 * a + d];
+                    if (!std::isfinite(v) || !(v >= 0.f) || !(v < box[d])) {
+                        bad[b] = a;
+                        return;
+                    }
+                    c[d] = (int32_t)std::floor(scaled(v, d));
+                }
+                owner[a] = domain_of_cell(grid, c);
+                cnt[owner[a]] += 1;
+            }
+        });
+    }
+    for (int32_t b = 0; b < n_blocks; ++b)
+        if (bad[b] >= 0) {
+            msg = "halo_plan_create: atom " + std::to_string((long long)bad[b]) +
+                  " lies outside [0, L) or is not finite";
+            return kErrRange;
+        }
     const bool corner = selection == kSelectCorner;
     const double rc2 = (double)cutoff * (double)cutoff;
-    {
-        double top[3];
-        for (int d = 0; d < 3; ++d) top[d] = std::nextafter((double)grid[d], 0.0);
-        for (int64_t a = 0; a < n_atoms; ++a) {
-            int32_t c[3];
-            for (int d = 0; d < 3; ++d) {
-                double s = (double)pos[3 * a + d] / P.width[d];
-                if (s > top[d]) s = top[d];
-                scaled[3 * a + d] = s;
-                c[d] = (int32_t)std::floor(s);
-            }
-            owner[a] = domain_of_cell(grid, c);
-        }
-    }
 
     // Home atoms by stable counting sort: ascending id within each domain.
+    // Every slot also carries its atom's position (slot_pos), so that the
+    // pulses read their candidates' positions in slot order.
     std::vector<std::vector<int64_t>> slot_atom(P.n_dom);
+    std::vector<std::vector<float>> slot_pos(P.n_dom);
     P.n_home.assign(P.n_dom, 0);
-    for (int64_t a = 0; a < n_atoms; ++a) P.n_home[owner[a]] += 1;
-    for (int32_t d = 0; d < P.n_dom; ++d) slot_atom[d].reserve((size_t)P.n_home[d] * 2 + 8);
-    for (int64_t a = 0; a < n_atoms; ++a) slot_atom[owner[a]].push_back(a);
+    for (int32_t b = 0; b < n_blocks; ++b)
+        for (int32_t d = 0; d < P.n_dom; ++d) {
+            int32_t &c = block_count[(size_t)b * P.n_dom + d];
+            const int32_t start = P.n_home[d];
+            P.n_home[d] += c;
+            c = start;  // now the block's first slot in domain d
+        }
+    for (int32_t d = 0; d < P.n_dom; ++d) {
+        slot_atom[d].reserve((size_t)P.n_home[d] * 2 + 8);
+        slot_atom[d].resize((size_t)P.n_home[d]);
+        slot_pos[d].reserve(((size_t)P.n_home[d] * 2 + 8) * 3);
+        slot_pos[d].resize((size_t)P.n_home[d] * 3);
+    }
+    parallel_for(n_blocks, [&](int32_t b) {
+        const int64_t a0 = (int64_t)b * kBlock, a1 = std::min(n_atoms, a0 + kBlock);
+        int32_t *next = &block_count[(size_t)b * P.n_dom];
+        for (int64_t a = a0; a < a1; ++a) {
+            const int32_t d = owner[a];
+            const int32_t sl = next[d]++;
+            slot_atom[d][sl] = a;
+            for (int k = 0; k < 3; ++k) slot_pos[d][3 * (size_t)sl + k] = pos[3 * a + k];
+        }
+    });
 
     // Pulses.
     P.seg.assign((size_t)P.n_pulse * P.n_dom, Segment());
     std::vector<std::vector<int32_t>> picks((size_t)P.n_pulse * P.n_dom);
     std::vector<std::vector<int64_t>> moving(P.n_dom);
+    std::vector<std::vector<float>> moving_pos(P.n_dom);
     for (int32_t p = 0; p < P.n_pulse; ++p) {
         const int dim = P.pulse_dim[p];
         const int32_t k = P.pulse_k[p];
@@ -234,16 +272,24 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
                 last = prev.atom_offset + prev.recv_size;
             }
             const double face = (double)(c_recv + 1);
-            std::vector<int32_t> &out = prow[D];
-            std::vector<int64_t> &mv = moving[D];
-            mv.clear();
+            // Appends go to local vectors, handed over at the end: the
+            // shared arrays of vectors would have neighbouring domains'
+            // headers, written by other threads, in one cache line.
+            std::vector<int32_t> out;
+            std::vector<int64_t> mv;
+            std::vector<float> mp;
+            out.reserve((size_t)(last - first));
+            mv.reserve((size_t)(last - first));
+            mp.reserve((size_t)(last - first) * 3);
             const std::vector<int64_t> &sa = slot_atom[D];
+            const float *sp = slot_pos[D].data();
             for (int32_t slot = first; slot < last; ++slot) {
-                const double *t = &scaled[3 * sa[slot]];
-                double above = t[dim] - face;
+                const float *ps = sp + 3 * (size_t)slot;
+                double above = scaled(ps[dim], dim) - face;
                 if (above < 0.0) above += (double)n;
                 bool send = above < reach;
                 if (send && corner) {
+                    const double t[3] = {scaled(ps[0], 0), scaled(ps[1], 1), scaled(ps[2], 2)};
                     // squared distance to the receiver's box, x + y + z in
                     // this order; dimensions where the atom lies in the
                     // receiver's slab add nothing
@@ -262,11 +308,15 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
                 if (send) {
                     out.push_back(slot);
                     mv.push_back(sa[slot]);
+                    mp.insert(mp.end(), ps, ps + 3);
                 }
             }
             s.send_size = (int32_t)out.size();
             s.dep_start = (int32_t)(std::lower_bound(out.begin(), out.end(), P.n_home[D]) -
                                     out.begin());
+            prow[D] = std::move(out);
+            moving[D] = std::move(mv);
+            moving_pos[D] = std::move(mp);
         });
 
         // Phase 2 writes only the receiver's slots; each receiver has exactly
@@ -279,6 +329,8 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
             r.recv_size = s.send_size;
             r.atom_offset = (int32_t)dst.size();
             dst.insert(dst.end(), moving[D].begin(), moving[D].end());
+            std::vector<float> &dst_p = slot_pos[s.send_to];
+            dst_p.insert(dst_p.end(), moving_pos[D].begin(), moving_pos[D].end());
         });
     }
 
@@ -298,8 +350,9 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
         return kErrRange;
     }
     P.home_slot.assign((size_t)n_atoms, 0);
-    for (int32_t d = 0; d < P.n_dom; ++d)
+    parallel_for(P.n_dom, [&](int32_t d) {  // each atom is a home atom of one domain
         for (int32_t s = 0; s < P.n_home[d]; ++s) P.home_slot[slot_atom[d][s]] = P.base[d] + s;
+    });
 
     // Concatenated indexMap, pulse-major then domain.
     int64_t entries = 0;
@@ -311,15 +364,15 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
     P.local_map.resize((size_t)entries);
     P.abs_map.resize((size_t)entries);
 
-    for (int32_t p = 0; p < P.n_pulse; ++p)
-        for (int32_t D = 0; D < P.n_dom; ++D) {
-            const Segment &s = P.seg[(size_t)p * P.n_dom + D];
-            const std::vector<int32_t> &pk = picks[(size_t)p * P.n_dom + D];
-            for (int32_t i = 0; i < s.send_size; ++i) {
-                P.local_map[s.map_off + i] = pk[i];
-                P.abs_map[s.map_off + i] = (int32_t)(P.base[D] + pk[i]);
-            }
+    parallel_for(P.n_pulse * P.n_dom, [&](int32_t sg) {
+        const Segment &s = P.seg[(size_t)sg];
+        const int32_t D = sg % P.n_dom;
+        const std::vector<int32_t> &pk = picks[(size_t)sg];
+        for (int32_t i = 0; i < s.send_size; ++i) {
+            P.local_map[s.map_off + i] = pk[i];
+            P.abs_map[s.map_off + i] = (int32_t)(P.base[D] + pk[i]);
         }
+    });
     make_items(P, item_entries);
     make_chunks(P, item_entries);
     make_launch_members(P);
@@ -618,15 +671,16 @@ void make_chunks(HostPlan &P, int32_t chunk_slots)
     P.has_chunks = plan_has_chunks(P);
     if (!P.has_chunks) return;
     P.slot_mask.assign((size_t)P.total_slots, 0);
-    for (int32_t p = 0; p < P.n_pulse; ++p)
-        for (int32_t D = 0; D < P.n_dom; ++D) {
+    parallel_for(P.n_dom, [&](int32_t D) {  // a domain's indexMaps name its own slots
+        for (int32_t p = 0; p < P.n_pulse; ++p) {
             const Segment &s = P.at(p, D);
             for (int32_t i = 0; i < s.send_size; ++i)
                 P.slot_mask[(size_t)(P.base[D] + P.local_map[s.map_off + i])] |= (uint8_t)(1u << p);
         }
+    });
     const std::vector<Piece> pieces = chunk_pieces(P, chunk_slots);
     std::vector<PieceStats> stats(pieces.size());
-    for (size_t i = 0; i < pieces.size(); ++i) {
+    parallel_for((int32_t)pieces.size(), [&](int32_t i) {
         PieceStats &st = stats[i];
         st.mask = 0;
         for (int32_t q = 0; q < kMaxMaskPulses; ++q) st.count[q] = 0;
@@ -635,7 +689,7 @@ void make_chunks(HostPlan &P, int32_t chunk_slots)
             st.mask |= m;
             for (int32_t q = 0; q < P.n_pulse; ++q) st.count[q] += (int32_t)((m >> q) & 1u);
         }
-    }
+    });
     finish_chunks(P, chunk_slots, pieces, stats);
 }
 
