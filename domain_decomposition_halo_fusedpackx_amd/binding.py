@@ -65,6 +65,16 @@ SIGNATURES = {
 }
 
 _lib = None
+_FUNCS = {}
+_TORCH = None
+
+
+def _torch():
+    global _TORCH
+    if _TORCH is None:
+        import torch
+        _TORCH = torch
+    return _TORCH
 
 
 class HaloError(RuntimeError):
@@ -277,22 +287,34 @@ class HaloPlan:
     # -- device side ------------------------------------------------------------
     def _buf(self, t):
         """Validate an exchange buffer; returns (pointer, device index)."""
-        import torch
+        torch = _torch()
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise TypeError("exchange buffers must be torch.cuda tensors")
-        if t.dtype != torch.float32 or not t.is_contiguous():
+        if t.dtype is not torch.float32 or not t.is_contiguous():
             raise TypeError("exchange buffers must be contiguous float32")
         if t.numel() != 3 * self.total_slots:
             raise ValueError(f"buffer holds {t.numel()} floats, the plan needs "
                              f"{3 * self.total_slots} (total_slots x 3)")
         ptr = t.data_ptr()
-        if ptr % 4:
+        if ptr & 3:
             raise ValueError("buffer must be 4-byte aligned")
-        return ctypes.c_void_p(ptr), t.get_device()
+        return ptr, t.get_device()
 
     def _call(self, name, t, stream):
+        # The per-call path stays lean (small exchanges take a few us on the
+        # GPU): plain ints for the pointers, the library's function objects
+        # looked up once.
         ptr, dev = self._buf(t)
-        _check(getattr(load_library(), name)(self._h, ptr, _stream_handle(stream, dev)))
+        fn = _FUNCS.get(name)
+        if fn is None:
+            fn = _FUNCS[name] = getattr(load_library(), name)
+        if stream is None:
+            s = _torch()._C._cuda_getCurrentRawStream(dev)
+        else:
+            s = _stream_handle(stream, dev)
+        code = fn(self._h, ptr, s)
+        if code:
+            _check(code)
 
     def upload(self):
         _check(load_library().halo_plan_upload(self._h))
