@@ -560,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
 // whole-line stores cost less than the byte-masked stores that leaving them
 // out would make.
 template <int EPT>
-__global__ __launch_bounds__(kThreads) void k_pull_f(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_pull_f(
     float *f, uint32_t f_bytes, const uint8_t *__restrict__ slot_mask,
     const halo::Chunk *__restrict__ chunks, const int32_t *__restrict__ forder,
     const uint16_t *__restrict__ rows, const int32_t *__restrict__ dest_start,
@@ -578,6 +578,26 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
     const auto rf = make_rsrc(f, f_bytes);
     const int32_t n_seg = n_dom * n_pulse;
 
+    // The last pulse's regions are summed by nobody in this launch, so its
+    // sources need no wait: they are the dense run of the receiver's region
+    // from this chunk's rank on. They are loaded at once, with the masks,
+    // straight into LDS (buffer-to-LDS loads: lane l of a load writes its
+    // 12 bytes at 16 * l from the wave's base), and read there by rank.
+    __shared__ float top_src[4 * EPT * kThreads];
+    const int32_t top = n_pulse - 1;
+    const bool has_top = (umask >> top) & 1u;
+    const int32_t top_n = has_top ? c->top_sends : 0;
+    if (has_top) {
+        const int32_t tbase = dest_start[top * n_dom + D] + c->rank[top];
+        const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rf, (__attribute__((address_space(3))) void *)(top_src + 4 * (j * kThreads + wave * 64)),
+                12, e < top_n ? (uint32_t)(tbase + e) * 12u : kInvalid, 0, 0, kStream);
+        }
+    }
     uint32_t m[EPT], off[EPT];
     f3v v[EPT];
 #pragma unroll
@@ -592,8 +612,21 @@ __global__ __launch_bounds__(kThreads) void k_pull_f(
     // masks.
 #pragma unroll
     for (int j = 0; j < EPT; ++j) v[j] = load3<kStream>(rf, off[j]);
+    if (has_top) {
+        halo::wait_vmem();  // this wave's loads into LDS are done
+        __syncthreads();    // and every other wave's
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const bool bit = (m[j] >> top) & 1u;
+            const uint32_t r = rank_in_chunk<EPT>(wrows, top, j, bit);
+            if (bit) {
+                const f3v a = {top_src[4 * r], top_src[4 * r + 1], top_src[4 * r + 2]};
+                v[j] = v[j] + a;
+            }
+        }
+    }
     bool waited = false;
-    for (int32_t p = n_pulse - 1; p >= 0; --p) {
+    for (int32_t p = n_pulse - 2; p >= 0; --p) {
         if (!((umask >> p) & 1u)) continue;
         const int32_t R = send_to[p * n_dom + D];
         const int32_t zseg = p * n_dom + R;

@@ -637,6 +637,7 @@ void finish_chunks(HostPlan &P, int32_t chunk_slots, const std::vector<Piece> &p
             c.mask = m;
             for (int32_t q = 0; q < kMaxMaskPulses; ++q) c.rank[q] = rank[q];
             c.xwait = pc.zone < 0 ? -1 : pc.zone * nd + P.at(pc.zone, pc.domain).recv_from;
+            c.top_sends = np > 0 ? stats[i].count[np - 1] : 0;
             kept.push_back(c);
             zone_count[pc.zone + 2] += 1;
         }

@@ -56,7 +56,8 @@ struct alignas(16) Chunk {
     int32_t zone;         // -1: home slots; r >= 0: region received in pulse r
     uint32_t mask;        // union of the pulse masks of the chunk's slots
     int32_t xwait;        // X: segment (r * n_dom + sender) that fills this region; -1 for home
-    int32_t pad[2];
+    int32_t top_sends;    // slots of the chunk sent in the last pulse
+    int32_t pad;
     int32_t rank[kMaxMaskPulses];  // entries of indexMap_p(domain) before the chunk
 };
 static_assert(sizeof(Chunk) == 64, "Chunk layout");
