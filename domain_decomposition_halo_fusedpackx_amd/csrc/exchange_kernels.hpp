@@ -626,7 +626,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         }
     }
     bool waited = false;
-    for (int32_t p = n_pulse - 2; p >= 0; --p) {
+    int32_t p_next = n_pulse - 2;
+    // The two pulses below the last one: when the regions both read already
+    // hold their final sums (one poll of both; with the epoch known), their
+    // loads go out together; otherwise each waits in turn in the loop below.
+    if (n_pulse >= 3 && ls.epoch != 0 && ((umask >> (n_pulse - 3)) & 3u) == 3u) {
+        const int32_t hi = n_pulse - 2, lo = n_pulse - 3;
+        const int32_t zh = hi * n_dom + send_to[hi * n_dom + D];
+        const int32_t zl = lo * n_dom + send_to[lo * n_dom + D];
+        if (zone_chunks[zh] > 0 && zone_chunks[zl] > 0) {
+            halo::count_early(ls, true);  // the chunk waits
+            if (halo::poll_both(halo::counter_f(state, n_seg, zh), zone_chunks[zh],
+                                halo::counter_f(state, n_seg, zl), zone_chunks[zl], ls.epoch)) {
+                waited = true;
+                p_next = lo - 1;
+                const int32_t bh = dest_start[hi * n_dom + D] + c->rank[hi];
+                const int32_t bl = dest_start[lo * n_dom + D] + c->rank[lo];
+                uint32_t sh[EPT], sl[EPT];
+#pragma unroll
+                for (int j = 0; j < EPT; ++j) {
+                    const bool bit_h = (m[j] >> hi) & 1u;
+                    const uint32_t rh = rank_in_chunk<EPT>(wrows, hi, j, bit_h);
+                    sh[j] = bit_h ? (uint32_t)(bh + (int32_t)rh) * 12u : kInvalid;
+                    const bool bit_l = (m[j] >> lo) & 1u;
+                    const uint32_t rl = rank_in_chunk<EPT>(wrows, lo, j, bit_l);
+                    sl[j] = bit_l ? (uint32_t)(bl + (int32_t)rl) * 12u : kInvalid;
+                }
+                f3v ah[EPT], al[EPT];
+#pragma unroll
+                for (int j = 0; j < EPT; ++j) ah[j] = load3<kShared>(rf, sh[j]);
+#pragma unroll
+                for (int j = 0; j < EPT; ++j) al[j] = load3<kShared>(rf, sl[j]);
+#pragma unroll
+                for (int j = 0; j < EPT; ++j) {
+                    if (sh[j] != kInvalid) v[j] = v[j] + ah[j];
+                    if (sl[j] != kInvalid) v[j] = v[j] + al[j];
+                }
+            }
+        }
+    }
+    for (int32_t p = p_next; p >= 0; --p) {
         if (!((umask >> p) & 1u)) continue;
         const int32_t R = send_to[p * n_dom + D];
         const int32_t zseg = p * n_dom + R;

@@ -265,6 +265,32 @@ __device__ __forceinline__ void wait_lanes(uint32_t *ctr, uint32_t mult, const L
     __syncthreads();
 }
 
+// One poll, without waiting, of two counters (lanes 0 and 1 of wave 0):
+// whether both already show this epoch's completion (targets m0 and m1
+// times the epoch). The workgroup then meets at a barrier, so that loads
+// issued after a true answer are ordered after the poll.
+__device__ __forceinline__ bool poll_both(uint32_t *c0, uint32_t m0, uint32_t *c1, uint32_t m1,
+                                          uint32_t epoch)
+{
+    __shared__ uint32_t ready;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        bool ok = true;
+        if (lane < 2) {
+            uint32_t *c = lane == 0 ? c0 : c1;
+            const uint32_t target = epoch * (lane == 0 ? m0 : m1);
+            ok = (int32_t)(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                           target) >= 0;
+        }
+        const bool all = __all(ok);
+        wait_vmem();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        if (lane == 0) ready = all ? 1u : 0u;
+    }
+    __syncthreads();
+    return ready != 0;
+}
+
 // Completion of one work item: every wave waits until its stores are
 // complete, the workgroup meets at a barrier, and one thread adds 1 to the
 // segment's counter.
