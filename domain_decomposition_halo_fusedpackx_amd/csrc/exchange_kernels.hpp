@@ -628,16 +628,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     bool waited = false;
     int32_t p_next = n_pulse - 2;
     // The two pulses below the last one: when the regions both read already
-    // hold their final sums (one poll of both; with the epoch known), their
-    // loads go out together; otherwise each waits in turn in the loop below.
-    if (n_pulse >= 3 && ls.epoch != 0 && ((umask >> (n_pulse - 3)) & 3u) == 3u) {
+    // hold their final sums (one poll of both), their loads go out together;
+    // otherwise each waits in turn in the loop below.
+    if (n_pulse >= 3 && ((umask >> (n_pulse - 3)) & 3u) == 3u) {
         const int32_t hi = n_pulse - 2, lo = n_pulse - 3;
         const int32_t zh = hi * n_dom + send_to[hi * n_dom + D];
         const int32_t zl = lo * n_dom + send_to[lo * n_dom + D];
         if (zone_chunks[zh] > 0 && zone_chunks[zl] > 0) {
             halo::count_early(ls, true);  // the chunk waits
             if (halo::poll_both(halo::counter_f(state, n_seg, zh), zone_chunks[zh],
-                                halo::counter_f(state, n_seg, zl), zone_chunks[zl], ls.epoch)) {
+                                halo::counter_f(state, n_seg, zl), zone_chunks[zl], ls.lg,
+                                ls.epoch)) {
                 waited = true;
                 p_next = lo - 1;
                 const int32_t bh = dest_start[hi * n_dom + D] + c->rank[hi];

@@ -267,10 +267,11 @@ __device__ __forceinline__ void wait_lanes(uint32_t *ctr, uint32_t mult, const L
 
 // One poll, without waiting, of two counters (lanes 0 and 1 of wave 0):
 // whether both already show this epoch's completion (targets m0 and m1
-// times the epoch). The workgroup then meets at a barrier, so that loads
-// issued after a true answer are ordered after the poll.
+// times the epoch; an epoch not known yet is read with the poll, as in the
+// waits below). The workgroup then meets at a barrier, so that loads issued
+// after a true answer are ordered after the poll.
 __device__ __forceinline__ bool poll_both(uint32_t *c0, uint32_t m0, uint32_t *c1, uint32_t m1,
-                                          uint32_t epoch)
+                                          const LaunchGroup &lg, uint32_t &epoch)
 {
     __shared__ uint32_t ready;
     if (threadIdx.x < 64) {
@@ -278,9 +279,10 @@ __device__ __forceinline__ bool poll_both(uint32_t *c0, uint32_t m0, uint32_t *c
         bool ok = true;
         if (lane < 2) {
             uint32_t *c = lane == 0 ? c0 : c1;
-            const uint32_t target = epoch * (lane == 0 ? m0 : m1);
-            ok = (int32_t)(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                           target) >= 0;
+            const EpochRead er = start_epoch(lg, epoch);
+            const uint32_t now = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            finish_epoch(er, epoch);
+            ok = (int32_t)(now - epoch * (lane == 0 ? m0 : m1)) >= 0;
         }
         const bool all = __all(ok);
         wait_vmem();
