@@ -28,6 +28,11 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 METRIC = "halo atoms/s and HBM GB/s (% of peak); µs per coord+force exchange"
+# The library's rule for the default exchanges (halo_exchange_x / _f in
+# csrc/halo_api.hip): the transposed kernels from these sizes on.
+TRANSPOSED_X_MIN_ENTRIES = 1 << 20
+TRANSPOSED_F_MIN_ENTRIES = 1 << 14
+TRANSPOSED_F_MAX_PULSES = 3
 HBM_PEAK_GBS = 8000.0
 BYTES_X = 28  # per entry: 4 B index + 12 B gathered source + 12 B store
 BYTES_F = 40  # per entry: 4 B index + 12 B region read + 12 B target read + 12 B target write
@@ -434,8 +439,9 @@ def main():
     dom = "f" if ms_f >= ms_x else "x"
     sha = kernel_source_sha()
     # the kernels the default exchanges run (halo_exchange_x / _f choose by size)
-    x_default = "push_x" if E >= (1 << 20) else "pack_fused"
-    f_default = "pull_f" if E >= (1 << 14) and plan0.num_pulses <= 3 else "unpack_fused"
+    x_default = "push_x" if E >= TRANSPOSED_X_MIN_ENTRIES else "pack_fused"
+    f_default = ("pull_f" if E >= TRANSPOSED_F_MIN_ENTRIES and
+                 plan0.num_pulses <= TRANSPOSED_F_MAX_PULSES else "unpack_fused")
     kernel_of = {("fused", "x"): x_default, ("fused", "f"): f_default,
                  ("indexmap", "x"): "pack_fused", ("indexmap", "f"): "unpack_fused",
                  ("transposed", "x"): "push_x", ("transposed", "f"): "pull_f",
