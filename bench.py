@@ -136,6 +136,19 @@ def time_loop(torch, fn, n):
     return e0.elapsed_time(e1) / n  # ms
 
 
+def time_loops(torch, fn, n, loops):
+    """`loops` timed loops of n back-to-back calls (call i of a loop gets i,
+    so every loop walks the replicas the same way): the median loop's time
+    per call in ms, and every loop's, so that the spread is visible."""
+    per = [time_loop(torch, fn, n) for _ in range(loops)]
+    return float(np.median(per)), per
+
+
+def spread(per):
+    return {"min": min(per), "median": float(np.median(per)), "max": max(per),
+            "loops": len(per)}
+
+
 def launch_floor_us(torch, n):
     """Back-to-back launches of a one-element kernel on the same stream
     (after a warm-up that loads the kernel)."""
@@ -145,17 +158,20 @@ def launch_floor_us(torch, n):
     return time_loop(torch, lambda i: t.add_(1.0), n) * 1e3
 
 
-def host_call_us(torch, fn, n):
-    """Host time to issue one call (no synchronisation inside the loop): when
-    it exceeds the GPU time of the call, back-to-back timings measure the
-    host, not the kernel."""
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(n):
-        fn(i)
-    el = time.perf_counter() - t0
-    torch.cuda.synchronize()
-    return el / n * 1e6
+def host_call_us(torch, fn, n, loops=5):
+    """Host time to issue one call (no synchronisation inside a loop), median
+    over loops of n calls: when it exceeds the GPU time of the call,
+    back-to-back timings measure the host, not the kernel."""
+    per = []
+    for _ in range(loops):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        el = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        per.append(el / n * 1e6)
+    return float(np.median(per))
 
 
 def cold_exchange_us(torch, plan, x, f, f_init, suffix, reps, clean=True):
@@ -342,11 +358,97 @@ def overlap(torch, plan, x, f, reps):
             **both, "reps": reps}
 
 
+STAGE_FIELDS = ("start", "wait_begin", "wait_end", "signal", "end")
+
+
+def stage_profile(torch, HaloPlan, W, w, pos, launches, reps):
+    """Where the time of one exchange goes, per kernel: every work unit's
+    clock stamps (halo_plan_debug_timing) from the last of `launches`
+    back-to-back launches, grouped by stage of the forwarding chain (pulse and
+    whether the unit waits for the index-list and direct forms; zone for the
+    transposed form). Per group: median and latest time, in us from the first
+    unit's start, of the units' start, first wait begin, last wait end, first
+    completion signal and end; medians over `reps` repetitions. The kernel's
+    duration per launch from HIP events over the same loop is given with it."""
+    plan = HaloPlan(pos, w.box, w.grid, w.cutoff)
+    plan.upload()
+    x = torch.from_numpy(plan.home_filled(pos, 0.0)).cuda()
+    base, n_home, n_halo = plan.domains()
+    f = torch.from_numpy(W.halo_forces(plan.total_slots, base, n_home, n_halo, w.seed)).cuda()
+    plan.debug_timing(True)
+    waits = plan.item_waits()
+    pulse_of_item = waits[:, 0] // plan.num_domains
+    chunks = plan.chunks()
+    runs = [("x", "indexmap"), ("x", "transposed"), ("x", "direct"), ("f", "indexmap"),
+            ("f", "transposed")]
+    out = {"workload": w.describe(), "halo_entries": plan.num_entries,
+           "items": plan.num_items, "chunks": len(chunks), "launches": launches, "reps": reps}
+    for d, form in runs:
+        if form == "transposed" and len(chunks) == 0:
+            continue
+        fn = getattr(plan, f"exchange_{d}_{form}")
+        buf = x if d == "x" else f
+        fn(buf)  # first call (origin map) untimed
+        per_rep, ev_us = [], []
+        for _ in range(reps):
+            ev_us.append(time_loop(torch, lambda i: fn(buf), launches) * 1e3)
+            st, khz = plan.debug_timing_read()
+            tick_us = 1e3 / khz
+            n_units = len(chunks) if form == "transposed" else plan.num_items
+            st = st[:n_units]
+            t0 = st[:, 0].min()
+            rel = {k: (st[:, i] - t0) * tick_us for i, k in enumerate(STAGE_FIELDS)}
+            reached = {k: st[:, i] != 0 for i, k in enumerate(STAGE_FIELDS)}
+            if form == "transposed":
+                keys = ["home" if z < 0 else f"region{z}" for z in chunks[:, 1]]
+            elif d == "x" and form == "indexmap":
+                keys = [f"pulse{p}:{'forwards' if wm else 'home'}"
+                        for p, wm in zip(pulse_of_item, waits[:, 1])]
+            else:
+                keys = [f"pulse{p}:{'waits' if wb else 'no wait'}" if form != "direct"
+                        else f"pulse{p}" for p, wb in zip(pulse_of_item, reached["wait_begin"])]
+            groups = {}
+            for k in dict.fromkeys(keys):
+                sel = np.array([kk == k for kk in keys])
+                g = {"units": int(sel.sum())}
+                for fld in STAGE_FIELDS:
+                    m = sel & reached[fld]
+                    if m.any():
+                        g[fld] = (float(np.median(rel[fld][m])), float(rel[fld][m].max()))
+                groups[k] = g
+            per_rep.append({"span_us": float(rel["end"][reached["end"]].max()),
+                            "groups": groups})
+        med = {"us_per_launch_events": float(np.median(ev_us)),
+               "span_us": float(np.median([r["span_us"] for r in per_rep])), "groups": {}}
+        for k, g in per_rep[0]["groups"].items():
+            mg = {"units": g["units"]}
+            for fld in STAGE_FIELDS:
+                vals = [r["groups"][k][fld] for r in per_rep if fld in r["groups"].get(k, {})]
+                if vals:
+                    mg[fld] = [round(float(np.median([v[0] for v in vals])), 3),
+                               round(float(np.median([v[1] for v in vals])), 3)]
+            med["groups"][k] = mg
+        out[f"{d}_{form}"] = med
+        log(f"stages {d} {form}: {med['us_per_launch_events']:.2f} us per launch (events), "
+            f"first start to last end {med['span_us']:.2f} us")
+        for k, g in med["groups"].items():
+            cols = "  ".join(f"{fld} {g[fld][0]:6.2f}/{g[fld][1]:6.2f}" for fld in STAGE_FIELDS
+                             if fld in g)
+            log(f"   {k:22s} n={g['units']:5d}  {cols}")
+    plan.sync()
+    plan.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--loops", type=int, default=7,
+                    help="timed loops of --steps steps; ms_per_step is the median loop's")
+    ap.add_argument("--kernel-launches", type=int, default=240,
+                    help="launches per loop of the per-direction timings (at least --steps)")
     ap.add_argument("--config", type=int, default=5, help="workload 1..5 (default 5: 8x8x8)")
     ap.add_argument("--replicas", type=int, default=0,
                     help="rotated copies of plan/x/f (0: enough to exceed 2x the 256 MB cache)")
@@ -361,6 +463,9 @@ def main():
     ap.add_argument("--no-overlap", action="store_true")
     ap.add_argument("--build-reps", type=int, default=5)
     ap.add_argument("--overlap-reps", type=int, default=50)
+    ap.add_argument("--stages", action="store_true",
+                    help="only the per-stage clock profile of every fused kernel on --config "
+                         "(halo_plan_debug_timing; medians over 5 repetitions of 20 launches)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device 3 times (a plain copy kernel of "
                          "known size, for scaling hardware byte counters)")
@@ -391,6 +496,10 @@ def main():
     w = W.WORKLOADS[args.config]
     pos = W.workload_positions(w)
     log(f"workload {w.describe()}")
+    if args.stages:
+        print(json.dumps({"stages": stage_profile(torch, HaloPlan, W, w, pos, 20, 5)}),
+              flush=True)
+        return
 
     plan0 = HaloPlan(pos, w.box, w.grid, w.cutoff)
     E = plan0.num_entries
@@ -425,14 +534,17 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    log(f"timed {args.steps} steps")
-    ms_step = time_loop(torch, step, args.steps)
-    # Per-kernel launch durations on the launch stream, same replicas.
-    ms_x = time_loop(torch, lambda i: ex_x(plans[i % R], xs[i % R]), args.steps)
-    ms_f = time_loop(torch, lambda i: ex_f(plans[i % R], fs[i % R]), args.steps)
+    log(f"timed {args.loops} loops of {args.steps} steps")
+    ms_step, step_loops = time_loops(torch, step, args.steps, args.loops)
+    # Per-kernel launch durations on the launch stream, same replicas: the
+    # median of 5 loops of back-to-back launches of one direction.
+    nk = max(args.steps, args.kernel_launches)
+    ms_x, x_loops = time_loops(torch, lambda i: ex_x(plans[i % R], xs[i % R]), nk, 5)
+    ms_f, f_loops = time_loops(torch, lambda i: ex_f(plans[i % R], fs[i % R]), nk, 5)
     for p in plans:
         p.sync()
-    log(f"ms/step={ms_step:.4f} x={ms_x * 1e3:.2f}us f={ms_f * 1e3:.2f}us")
+    log(f"ms/step={ms_step:.4f} (loops {min(step_loops):.4f}..{max(step_loops):.4f}) "
+        f"x={ms_x * 1e3:.2f}us f={ms_f * 1e3:.2f}us")
 
     gbs_x = E * BYTES_X / (ms_x * 1e-3) / 1e9
     gbs_f = E * BYTES_F / (ms_f * 1e-3) / 1e9
@@ -474,6 +586,12 @@ def main():
                      "kernel_source_sha": sha},
         "us_per_exchange": {"x": ms_x * 1e3, "f": ms_f * 1e3},
         "gbs": {"x": gbs_x, "f": gbs_f},
+        "spread": {"ms_per_step": spread(step_loops),
+                   "us_x": spread([t * 1e3 for t in x_loops]),
+                   "us_f": spread([t * 1e3 for t in f_loops]),
+                   "method": f"ms_per_step: median of {args.loops} loops of {args.steps} steps "
+                             f"after {args.warmup} warm-up steps; us_x, us_f: median of 5 loops "
+                             f"of {nk} launches; HIP events on the launch stream"},
     }
 
     if fused and not args.no_ablation:
@@ -489,9 +607,9 @@ def main():
                 if ff:
                     ff(plans[r], fs[r])
             torch.cuda.synchronize()
-            ux = (time_loop(torch, lambda i: fx(plans[i % R], xs[i % R]), args.steps) * 1e3
+            ux = (time_loops(torch, lambda i: fx(plans[i % R], xs[i % R]), nk, 3)[0] * 1e3
                   if fx else None)
-            uf = (time_loop(torch, lambda i: ff(plans[i % R], fs[i % R]), args.steps) * 1e3
+            uf = (time_loops(torch, lambda i: ff(plans[i % R], fs[i % R]), nk, 3)[0] * 1e3
                   if ff else None)
             launches = {"pulsewise": plan0.num_pulses, "staged": 2 * plan0.num_pulses}
             forms[form] = {"us_x": ux, "us_f": uf, "launches_per_exchange": launches.get(form, 1)}
@@ -503,8 +621,8 @@ def main():
                                 speedup_fused_f=forms["pulsewise"]["us_f"] / (ms_f * 1e3))
         out["launch_floor_us"] = launch_floor_us(torch, args.steps)
         out["host_us_per_call"] = {
-            "x": host_call_us(torch, lambda i: ex_x(plans[i % R], xs[i % R]), args.steps),
-            "f": host_call_us(torch, lambda i: ex_f(plans[i % R], fs[i % R]), args.steps)}
+            "x": host_call_us(torch, lambda i: ex_x(plans[i % R], xs[i % R]), nk),
+            "f": host_call_us(torch, lambda i: ex_f(plans[i % R], fs[i % R]), nk)}
         log("cold exchanges")
         out["cold"] = {form: cold_exchange_us(torch, plans[0], xs[0], fs[0], f_init, suffix,
                                               args.cold_reps)
@@ -527,8 +645,8 @@ def main():
         for p in splans:
             p.upload()
         out["cell_sorted_input"] = {
-            "us_x": time_loop(torch, lambda i: splans[i % R].exchange_x(sx[i % R]), args.steps) * 1e3,
-            "us_f": time_loop(torch, lambda i: splans[i % R].exchange_f(sf[i % R]), args.steps) * 1e3,
+            "us_x": time_loops(torch, lambda i: splans[i % R].exchange_x(sx[i % R]), nk, 3)[0] * 1e3,
+            "us_f": time_loops(torch, lambda i: splans[i % R].exchange_f(sf[i % R]), nk, 3)[0] * 1e3,
             "order": "atoms renumbered by 0.5 nm cell (z, y, x), same positions"}
         for p in splans:
             p.sync()
@@ -547,14 +665,14 @@ def main():
         def cstep(i):
             cplans[i % R].exchange_x(cx[i % R])
             cplans[i % R].exchange_f(cf[i % R])
-        cms = time_loop(torch, cstep, args.steps)
+        cms = time_loops(torch, cstep, args.steps, args.loops)[0]
         out["corner_selection"] = {
             "halo_entries": cplans[0].num_entries, "slots": cS,
             "ms_per_step": cms,
-            "us_x": time_loop(torch, lambda i: cplans[i % R].exchange_x(cx[i % R]),
-                              args.steps) * 1e3,
-            "us_f": time_loop(torch, lambda i: cplans[i % R].exchange_f(cf[i % R]),
-                              args.steps) * 1e3,
+            "us_x": time_loops(torch, lambda i: cplans[i % R].exchange_x(cx[i % R]),
+                               nk, 3)[0] * 1e3,
+            "us_f": time_loops(torch, lambda i: cplans[i % R].exchange_f(cf[i % R]),
+                               nk, 3)[0] * 1e3,
             "step_speedup_vs_slab": ms_step / cms}
         for p in cplans:
             p.sync()
@@ -566,6 +684,11 @@ def main():
             out["overlap"] = overlap(torch, plans[0], xs[0], fs[0], args.overlap_reps)
         log("graph replays")
         out["graph"] = graph_replays(torch, plans, xs, fs, args.steps)
+
+    torch.cuda.synchronize()
+    for p in plans:
+        p.close()
+    log("plans released")
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

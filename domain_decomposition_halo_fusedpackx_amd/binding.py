@@ -6,8 +6,10 @@ library has not been built, every call raises: there is no CPU fallback.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import weakref
 
 import numpy as np
 
@@ -42,6 +44,8 @@ SIGNATURES = {
     "halo_plan_pulse": (_st, [_vp, _i32, _i32, _P(_i32), _P(_i32), _P(_i32), _P(_i32), _P(_i32),
                               _P(_i32), _P(_i32), _vp, _vp]),
     "halo_plan_item_waits": (_st, [_vp, _i32, _P(_i32), _P(_u32), _P(_u32)]),
+    "halo_plan_num_chunks": (_i32, [_vp]),
+    "halo_plan_chunk": (_st, [_vp, _i32, _P(_i32), _P(_i32), _P(_i64), _P(_i32), _P(_u32)]),
     "halo_plan_upload": (_st, [_vp]),
     "halo_exchange_x": (_st, [_vp, _vp, _vp]),
     "halo_exchange_f": (_st, [_vp, _vp, _vp]),
@@ -62,11 +66,25 @@ SIGNATURES = {
     "halo_plan_set_spin_limit": (_st, [_vp, _u32]),
     "halo_plan_debug_withhold": (_st, [_vp, _i32]),
     "halo_plan_debug_stress": (_st, [_vp, _u32]),
+    "halo_plan_debug_timing": (_st, [_vp, _i32]),
+    "halo_plan_debug_timing_read": (_st, [_vp, _vp, _i64, _P(_i64), _P(_i32)]),
 }
 
 _lib = None
 _FUNCS = {}
 _TORCH = None
+# Plans still open. At interpreter exit they are destroyed by an atexit hook,
+# which runs before the process's C-level exit handlers tear down the HIP
+# runtime (and any profiler attached to it); a plan left to the garbage
+# collector of a finishing interpreter would free its device memory at an
+# unspecified point of that teardown.
+_LIVE = weakref.WeakSet()
+
+
+@atexit.register
+def _close_live_plans():
+    for plan in list(_LIVE):
+        plan.close()
 
 
 def _torch():
@@ -216,6 +234,8 @@ class HaloPlan:
     def _finish(self, h, n_atoms):
         lib = load_library()
         self._h = h
+        self._destroy = lib.halo_plan_destroy
+        _LIVE.add(self)
         self.n_atoms = n_atoms
         self.total_slots = lib.halo_plan_total_slots(h)
         self.num_domains = lib.halo_plan_num_domains(h)
@@ -225,16 +245,16 @@ class HaloPlan:
         self.selection = {v: k for k, v in SELECTIONS.items()}[lib.halo_plan_selection(h)]
 
     def close(self):
+        """Destroy the plan (halo_plan_destroy); exchanges on it must have
+        finished. Called by __del__ and, for plans still open at interpreter
+        exit, by an atexit hook."""
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            load_library().halo_plan_destroy(h)
+            self._destroy(h)
         self._h = None
 
     def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
+        self.close()
 
     # -- read-out -------------------------------------------------------------
     def pulse_dim(self, p: int):
@@ -282,6 +302,20 @@ class HaloPlan:
             _check(lib.halo_plan_item_waits(self._h, i, ctypes.byref(sg), ctypes.byref(xm),
                                             ctypes.byref(am)))
             out[i] = (sg.value, xm.value, am.value)
+        return out
+
+    def chunks(self):
+        """(domain, zone, first, count, mask) of every chunk of the transposed
+        form, in its coordinate kernel's launch order."""
+        lib = load_library()
+        n = lib.halo_plan_num_chunks(self._h)
+        out = np.zeros((max(n, 0), 5), np.int64)
+        d, z, c, m = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_uint32()
+        f = ctypes.c_int64()
+        for i in range(n):
+            _check(lib.halo_plan_chunk(self._h, i, ctypes.byref(d), ctypes.byref(z),
+                                       ctypes.byref(f), ctypes.byref(c), ctypes.byref(m)))
+            out[i] = (d.value, z.value, f.value, c.value, m.value)
         return out
 
     # -- device side ------------------------------------------------------------
@@ -392,6 +426,21 @@ class HaloPlan:
 
     def debug_stress(self, seed: int):
         _check(load_library().halo_plan_debug_stress(self._h, seed))
+
+    def debug_timing(self, enable: bool = True):
+        _check(load_library().halo_plan_debug_timing(self._h, 1 if enable else 0))
+
+    def debug_timing_read(self):
+        """(stamps, clock_khz): stamps is an int64 array [units, 8] (start,
+        first wait begins, last wait ends, first signal, end, workgroup index,
+        HW_ID, XCC_ID) as halo_plan_debug_timing_read returns it."""
+        lib = load_library()
+        n, khz = ctypes.c_int64(), ctypes.c_int32()
+        _check(lib.halo_plan_debug_timing_read(self._h, None, 0, ctypes.byref(n),
+                                               ctypes.byref(khz)))
+        out = np.zeros((max(n.value, 1), 8), np.uint64)
+        _check(lib.halo_plan_debug_timing_read(self._h, _np_ptr(out), n.value, None, None))
+        return out[:n.value].astype(np.int64), khz.value
 
     # -- inputs in this layout ----------------------------------------------------
     def home_filled(self, positions, fill=float("nan")) -> np.ndarray:

@@ -34,14 +34,32 @@
 
 constexpr int kThreads = 256;  // 4 waves of 64 per workgroup
 
-// Testing mode for the fused kernels (halo_plan_debug_stress): workgroup b
-// takes work unit order[b] instead of its usual one (the host reverses the
-// order inside every group of mutually independent units), and every unit
-// first sleeps a pseudo-random while. Results must not change. order ==
-// nullptr and seed == 0 in normal runs.
-struct Stress {
+// Debugging modes of the fused kernels, both off in normal runs:
+//  - stress (halo_plan_debug_stress): workgroup b takes work unit order[b]
+//    instead of its usual one (the host reverses the order inside every group
+//    of mutually independent units), and every unit first sleeps a
+//    pseudo-random while. Results must not change. order == nullptr and
+//    seed == 0 when off.
+//  - timing (halo_plan_debug_timing): wave 0 of every unit records the
+//    device's constant-rate clock at the steps of the unit (start, first
+//    wait, end of the last wait, first completion signal, end) and where it
+//    ran, kStampWords words per unit. stamps == nullptr when off.
+struct Debug {
     const int32_t *order;
     uint32_t seed;
+    uint64_t *stamps;
+};
+
+constexpr int kStampWords = 8;
+enum : int {
+    kStampStart = 0,      // the unit's first instruction
+    kStampWaitBegin = 1,  // its first dependency wait begins (0: it never waits)
+    kStampWaitEnd = 2,    // its last dependency wait has ended
+    kStampSignal = 3,     // its first completion signal is sent (stores complete)
+    kStampEnd = 4,        // its last instruction
+    kStampBlock = 5,      // workgroup index
+    kStampHwId = 6,       // HW_ID register (wave, SIMD, CU, shader array, engine)
+    kStampXcc = 7         // XCC_ID register (the XCD the unit ran on)
 };
 
 __device__ __forceinline__ void stress_delay(uint32_t seed, uint32_t unit)
@@ -51,6 +69,36 @@ __device__ __forceinline__ void stress_delay(uint32_t seed, uint32_t unit)
     h *= 0x85EBCA77u;
     h ^= h >> 13;
     for (uint32_t i = 0; i < (h & 31u); ++i) __builtin_amdgcn_s_sleep(127);
+}
+
+// s_getreg_b32 operands: register id, bit offset 0, 32 bits.
+constexpr int kHwRegHwId = 4 | (31 << 11);
+constexpr int kHwRegXccId = 20 | (31 << 11);
+
+// The unit's first stamp: its start, where it runs, and zeros for the steps
+// it may not reach.
+__device__ __forceinline__ void stamp_start(const Debug &d, uint32_t unit)
+{
+    if (d.stamps && threadIdx.x == 0) {
+        uint64_t *s = d.stamps + (size_t)unit * kStampWords;
+        s[kStampStart] = __builtin_amdgcn_s_memrealtime();
+        s[kStampWaitBegin] = 0;
+        s[kStampWaitEnd] = 0;
+        s[kStampSignal] = 0;
+        s[kStampEnd] = 0;
+        s[kStampBlock] = blockIdx.x;
+        s[kStampHwId] = (uint32_t)__builtin_amdgcn_s_getreg(kHwRegHwId);
+        s[kStampXcc] = (uint32_t)__builtin_amdgcn_s_getreg(kHwRegXccId) & 0xfu;
+    }
+}
+
+// Stamp k of the unit; with first_only, only if it is still 0.
+__device__ __forceinline__ void stamp(const Debug &d, uint32_t unit, int k, bool first_only = false)
+{
+    if (d.stamps && threadIdx.x == 0) {
+        uint64_t *s = d.stamps + (size_t)unit * kStampWords + k;
+        if (!first_only || *s == 0) *s = __builtin_amdgcn_s_memrealtime();
+    }
 }
 
 // ---- buffer addressing ----------------------------------------------------
@@ -131,7 +179,8 @@ __device__ __forceinline__ void pack_item_fused_st(const WorkItem *it, __amdgpu_
                                                    const uint32_t *seg_items, uint32_t *state,
                                                    int32_t n_dom, const halo::LaunchGroup &lg,
                                                    uint32_t &epoch, uint32_t spin_limit,
-                                                   uint32_t *err_word)
+                                                   uint32_t *err_word, const Debug &dbg,
+                                                   uint32_t unit)
 {
     const int32_t n_indep = it->n_indep;
     const int32_t n_total = it->n_total;
@@ -167,7 +216,9 @@ __device__ __forceinline__ void pack_item_fused_st(const WorkItem *it, __amdgpu_
             ctr = halo::counter_x(state, s);
             mult = seg_items[s];
         }
+        stamp(dbg, unit, kStampWaitBegin);
         halo::wait_lanes(ctr, mult, lg, epoch, spin_limit, err_word);
+        stamp(dbg, unit, kStampWaitEnd);
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
             const bool dep = (int32_t)threadIdx.x + j * kThreads >= n_indep;
@@ -188,16 +239,18 @@ __device__ __forceinline__ void pack_item_fused(const WorkItem *it, __amdgpu_buf
                                                 const uint32_t *seg_items, uint32_t *state,
                                                 int32_t n_dom, const halo::LaunchGroup &lg,
                                                 uint32_t &epoch, uint32_t spin_limit,
-                                                uint32_t *err_word, int32_t withhold)
+                                                uint32_t *err_word, int32_t withhold,
+                                                const Debug &dbg, uint32_t unit)
 {
     if (it->flags & halo::kItemXStoreShared) {
         pack_item_fused_st<EPT, kShared>(it, rx, ridx, recv_from, seg_items, state, n_dom, lg,
-                                         epoch, spin_limit, err_word);
+                                         epoch, spin_limit, err_word, dbg, unit);
         halo::signal_done(halo::counter_x(state, it->seg), it->seg == withhold);
+        stamp(dbg, unit, kStampSignal);
     } else {
         // last pulse: no later pulse forwards its region, nobody waits on it
         pack_item_fused_st<EPT, kStream>(it, rx, ridx, recv_from, seg_items, state, n_dom, lg,
-                                        epoch, spin_limit, err_word);
+                                        epoch, spin_limit, err_word, dbg, unit);
     }
 }
 
@@ -239,7 +292,8 @@ __device__ __forceinline__ void unpack_item_fused(const WorkItem *it, __amdgpu_b
                                                   const uint32_t *seg_items, uint32_t *state,
                                                   int32_t n_seg, const halo::LaunchGroup &lg,
                                                   uint32_t &epoch, uint32_t spin_limit,
-                                                  uint32_t *err_word, int32_t withhold)
+                                                  uint32_t *err_word, int32_t withhold,
+                                                  const Debug &dbg, uint32_t unit)
 {
     const int32_t n_total = it->n_total;
     const int32_t region_begin = it->region_begin;
@@ -248,8 +302,10 @@ __device__ __forceinline__ void unpack_item_fused(const WorkItem *it, __amdgpu_b
     load_targets<EPT>(ridx, it->map_begin, n_total, tgt);
     if (it->fwait[0] >= 0) {
         const int32_t nw = it->fwait[1] >= 0 && it->fwait[1] != it->fwait[0] ? 2 : 1;
+        stamp(dbg, unit, kStampWaitBegin);
         halo::wait_segments(it->fwait, nw, seg_items, state, n_seg, true, lg, epoch, spin_limit,
                             err_word);
+        stamp(dbg, unit, kStampWaitEnd);
     }
     const int32_t fl = it->flags;
     if (fl & halo::kItemFLoadShared) {
@@ -264,8 +320,10 @@ __device__ __forceinline__ void unpack_item_fused(const WorkItem *it, __amdgpu_b
             unpack_span<EPT, kStream, kStream>(rf, tgt, region_begin, n_total);
     }
     // pulse 0 runs last: nobody waits on its completion
-    if (fl & halo::kItemFStoreShared)
+    if (fl & halo::kItemFStoreShared) {
         halo::signal_done(halo::counter_f(state, n_seg, it->seg), it->seg == withhold);
+        stamp(dbg, unit, kStampSignal);
+    }
 }
 
 // One force-direction item with atomic accumulation: Algorithm 6 as the
@@ -345,17 +403,20 @@ __global__ __launch_bounds__(kThreads) void k_pack_fused(
     const WorkItem *__restrict__ items, const int32_t *__restrict__ recv_from,
     const uint32_t *__restrict__ seg_items, uint32_t *state, int32_t n_dom, uint32_t *groups,
     const uint32_t *__restrict__ members, uint32_t host_epoch, uint32_t spin_limit,
-    uint32_t *err_word, int32_t withhold, Stress st)
+    uint32_t *err_word, int32_t withhold, Debug dbg)
 {
-    const uint32_t u = st.order ? (uint32_t)st.order[blockIdx.x] : blockIdx.x;
-    if (st.seed) stress_delay(st.seed, u);
+    const uint32_t u = dbg.order ? (uint32_t)dbg.order[blockIdx.x] : blockIdx.x;
+    stamp_start(dbg, u);
+    if (dbg.seed) stress_delay(dbg.seed, u);
     halo::LaunchState ls = halo::launch_state(groups, members, u, host_epoch);
     const WorkItem *it = items + u;
     const bool member = it->n_total > it->n_indep;  // the item waits
     halo::count_early(ls, member);
     pack_item_fused<EPT>(it, make_rsrc(x, x_bytes), make_rsrc(idx, idx_bytes), recv_from,
-                         seg_items, state, n_dom, ls.lg, ls.epoch, spin_limit, err_word, withhold);
+                         seg_items, state, n_dom, ls.lg, ls.epoch, spin_limit, err_word, withhold,
+                         dbg, u);
     halo::count_late(ls, member);
+    stamp(dbg, u, kStampEnd);
 }
 
 // Fused force exchange: ONE launch, workgroup b takes item n_items-1-b, so
@@ -365,17 +426,19 @@ __global__ __launch_bounds__(kThreads) void k_unpack_fused(
     float *f, uint32_t f_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
     const WorkItem *__restrict__ items, const uint32_t *__restrict__ seg_items, uint32_t *state,
     int32_t n_seg, uint32_t n_items, uint32_t *groups, const uint32_t *__restrict__ members,
-    uint32_t host_epoch, uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Stress st)
+    uint32_t host_epoch, uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Debug dbg)
 {
-    const uint32_t u = st.order ? (uint32_t)st.order[blockIdx.x] : n_items - 1u - blockIdx.x;
-    if (st.seed) stress_delay(st.seed, u);
+    const uint32_t u = dbg.order ? (uint32_t)dbg.order[blockIdx.x] : n_items - 1u - blockIdx.x;
+    stamp_start(dbg, u);
+    if (dbg.seed) stress_delay(dbg.seed, u);
     halo::LaunchState ls = halo::launch_state(groups, members, u, host_epoch);
     const WorkItem *it = items + u;
     const bool member = it->fwait[0] >= 0;  // the item waits
     halo::count_early(ls, member);
     unpack_item_fused<EPT>(it, make_rsrc(f, f_bytes), make_rsrc(idx, idx_bytes), seg_items,
-                           state, n_seg, ls.lg, ls.epoch, spin_limit, err_word, withhold);
+                           state, n_seg, ls.lg, ls.epoch, spin_limit, err_word, withhold, dbg, u);
     halo::count_late(ls, member);
+    stamp(dbg, u, kStampEnd);
 }
 
 // Fused force exchange with atomic adds: ONE launch, last pulse first; an item
@@ -386,10 +449,11 @@ __global__ __launch_bounds__(kThreads) void k_unpack_atomic(
     const WorkItem *__restrict__ items, const uint32_t *__restrict__ seg_items, uint32_t *state,
     int32_t n_seg, int32_t n_dom, uint32_t n_items, uint32_t *groups,
     const uint32_t *__restrict__ members, uint32_t host_epoch, uint32_t spin_limit,
-    uint32_t *err_word, int32_t withhold, Stress st)
+    uint32_t *err_word, int32_t withhold, Debug dbg)
 {
-    const uint32_t u = st.order ? (uint32_t)st.order[blockIdx.x] : n_items - 1u - blockIdx.x;
-    if (st.seed) stress_delay(st.seed, u);
+    const uint32_t u = dbg.order ? (uint32_t)dbg.order[blockIdx.x] : n_items - 1u - blockIdx.x;
+    stamp_start(dbg, u);
+    if (dbg.seed) stress_delay(dbg.seed, u);
     halo::LaunchState ls = halo::launch_state(groups, members, u, host_epoch);
     // every item is a member here (which items wait is known on the device only)
     halo::count_early(ls, true);
@@ -397,6 +461,7 @@ __global__ __launch_bounds__(kThreads) void k_unpack_atomic(
                             seg_items, state, n_seg, n_dom, ls.lg, ls.epoch, spin_limit, err_word,
                             withhold);
     halo::count_late(ls, true);
+    stamp(dbg, u, kStampEnd);
 }
 
 // ---- transposed form: per-slot pulse masks --------------------------------
@@ -483,10 +548,11 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
     const int32_t *__restrict__ dest_start, const float4 *__restrict__ shift4,
     const uint32_t *__restrict__ x_arrivals, uint32_t *state, int32_t n_dom, int32_t n_pulse,
     uint32_t *groups, const uint32_t *__restrict__ members, uint32_t host_epoch,
-    uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Stress st)
+    uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Debug dbg)
 {
-    const uint32_t u = st.order ? (uint32_t)st.order[blockIdx.x] : blockIdx.x;
-    if (st.seed) stress_delay(st.seed, u);
+    const uint32_t u = dbg.order ? (uint32_t)dbg.order[blockIdx.x] : blockIdx.x;
+    stamp_start(dbg, u);
+    if (dbg.seed) stress_delay(dbg.seed, u);
     halo::LaunchState ls = halo::launch_state(groups, members, u, host_epoch);
     const halo::Chunk *c = chunks + u;
     halo::count_early(ls, c->zone >= 0);  // region chunks wait
@@ -511,8 +577,10 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
     if (c->zone >= 0) {
         // region slots are filled by another domain in this launch; every
         // slot is loaded, sent or not, so that the loads cover whole lines
+        stamp(dbg, u, kStampWaitBegin);
         halo::wait_one(c->xwait, x_arrivals, state, n_dom * n_pulse, false, ls.lg, ls.epoch,
                        spin_limit, err_word);
+        stamp(dbg, u, kStampWaitEnd);
 #pragma unroll
         for (int j = 0; j < EPT; ++j) v[j] = load3<kShared>(rx, off[j]);
     }
@@ -541,6 +609,7 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
             if (threadIdx.x == 0 && seg != withhold)
                 __hip_atomic_fetch_add(halo::counter_x(state, seg), 1u, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
+            stamp(dbg, u, kStampSignal, true);
         } else {
             // last pulse: nobody forwards this region, nobody waits on it
 #pragma unroll
@@ -548,6 +617,7 @@ __global__ __launch_bounds__(kThreads) void k_push_x(
         }
     }
     halo::count_late(ls, c->zone >= 0);
+    stamp(dbg, u, kStampEnd);
 }
 
 // Fused force exchange, transposed form (Algorithm 6): one workgroup per
@@ -567,10 +637,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     const int32_t *__restrict__ send_to, const uint32_t *__restrict__ zone_chunks,
     uint32_t *state, int32_t n_dom, int32_t n_pulse, uint32_t *groups,
     const uint32_t *__restrict__ members, uint32_t host_epoch, uint32_t spin_limit,
-    uint32_t *err_word, int32_t withhold, Stress st)
+    uint32_t *err_word, int32_t withhold, Debug dbg)
 {
-    const int32_t u = st.order ? st.order[blockIdx.x] : forder[blockIdx.x];
-    if (st.seed) stress_delay(st.seed, (uint32_t)u);
+    const int32_t u = dbg.order ? dbg.order[blockIdx.x] : forder[blockIdx.x];
+    stamp_start(dbg, (uint32_t)u);
+    if (dbg.seed) stress_delay(dbg.seed, (uint32_t)u);
     halo::LaunchState ls = halo::launch_state(groups, members, (uint32_t)u, host_epoch);
     const halo::Chunk *c = chunks + u;
     const int32_t first = c->first, count = c->count, D = c->domain, zone = c->zone;
@@ -636,9 +707,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         const int32_t zl = lo * n_dom + send_to[lo * n_dom + D];
         if (zone_chunks[zh] > 0 && zone_chunks[zl] > 0) {
             halo::count_early(ls, true);  // the chunk waits
-            if (halo::poll_both(halo::counter_f(state, n_seg, zh), zone_chunks[zh],
-                                halo::counter_f(state, n_seg, zl), zone_chunks[zl], ls.lg,
-                                ls.epoch)) {
+            stamp(dbg, (uint32_t)u, kStampWaitBegin);
+            const bool both = halo::poll_both(halo::counter_f(state, n_seg, zh), zone_chunks[zh],
+                                              halo::counter_f(state, n_seg, zl), zone_chunks[zl],
+                                              ls.lg, ls.epoch);
+            stamp(dbg, (uint32_t)u, kStampWaitEnd);
+            if (both) {
                 waited = true;
                 p_next = lo - 1;
                 const int32_t bh = dest_start[hi * n_dom + D] + c->rank[hi];
@@ -672,8 +746,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         const int32_t zseg = p * n_dom + R;
         if (zone_chunks[zseg] > 0) {
             halo::count_early(ls, true);  // the chunk waits
+            stamp(dbg, (uint32_t)u, kStampWaitBegin, true);
             halo::wait_one(zseg, zone_chunks, state, n_seg, true, ls.lg, ls.epoch, spin_limit,
                            err_word);
+            stamp(dbg, (uint32_t)u, kStampWaitEnd);
             waited = true;
         }
         const int32_t base = dest_start[p * n_dom + D] + c->rank[p];
@@ -707,11 +783,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         if (threadIdx.x == 0 && seg != withhold)
             __hip_atomic_fetch_add(halo::counter_f(state, n_seg, seg), 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
+        stamp(dbg, (uint32_t)u, kStampSignal);
     } else {
 #pragma unroll
         for (int j = 0; j < EPT; ++j) store3<kStream>(rf, off[j], v[j]);
     }
     halo::count_late(ls, waited);
+    stamp(dbg, (uint32_t)u, kStampEnd);
 }
 
 // Per-pulse baseline: one launch per pulse, one item per workgroup, no
@@ -878,8 +956,9 @@ __global__ __launch_bounds__(kThreads) void k_gather_x(float *x, uint32_t x_byte
                                                        const uint32_t *origin,
                                                        uint32_t origin_bytes,
                                                        const WorkItem *__restrict__ items,
-                                                       float lx, float ly, float lz)
+                                                       float lx, float ly, float lz, Debug dbg)
 {
+    stamp_start(dbg, blockIdx.x);
     const WorkItem *it = items + blockIdx.x;
     const auto rx = make_rsrc(x, x_bytes), ro = make_rsrc(origin, origin_bytes);
     const int32_t n = it->n_total;
@@ -903,6 +982,7 @@ __global__ __launch_bounds__(kThreads) void k_gather_x(float *x, uint32_t x_byte
         const f3v s = {(b & 1u) ? lx : 0.f, (b & 2u) ? ly : 0.f, (b & 4u) ? lz : 0.f};
         store3<kStream>(rx, e < n ? (uint32_t)(it->region_begin + e) * 12u : kInvalid, v[j] + s);
     }
+    stamp(dbg, blockIdx.x, kStampEnd);
 }
 
 // ---- home slots and per-atom arrays (halo_scatter_home, halo_gather_home) ----

@@ -54,12 +54,14 @@ void free_device(halo_plan *p)
                     (void *)p->d_forder, (void *)p->d_dest_start, (void *)p->d_shift4,
                     (void *)p->d_x_arrivals, (void *)p->d_zone_chunks, (void *)p->d_local_map,
                     (void *)p->d_home_slot, (void *)p->d_stress, (void *)p->d_origin,
-                    (void *)p->d_members, (void *)p->d_rows})
+                    (void *)p->d_members, (void *)p->d_rows, (void *)p->d_stamps})
         if (q) (void)hipFree(q);
     if (p->h_err) (void)hipHostFree(p->h_err);
     p->d_idx = p->d_recv_from = p->d_send_to = p->d_forder = p->d_dest_start = nullptr;
     p->d_stress = nullptr;
     p->stress_seed = 0;
+    p->d_stamps = nullptr;
+    p->stamp_units = 0;
     p->d_local_map = nullptr;
     p->d_home_slot = nullptr;
     p->d_items = nullptr;
@@ -123,16 +125,20 @@ Kernels kernels(int32_t item_entries)
     }
 }
 
-// Stress-mode order of one kernel family (see halo_plan_debug_stress):
-// [items X | items F | chunks X | chunks F] in p->d_stress.
+// Debugging modes of a kernel family: the stress-mode order (see
+// halo_plan_debug_stress; [items X | items F | chunks X | chunks F] in
+// p->d_stress) and the timing stamps (halo_plan_debug_timing).
 enum StressOrder { kOrderItemsX = 0, kOrderItemsF = 1, kOrderChunksX = 2, kOrderChunksF = 3 };
 
-Stress stress_of(const halo_plan *p, StressOrder which)
+Debug debug_of(const halo_plan *p, StressOrder which)
 {
-    if (!p->stress_seed || !p->d_stress) return Stress{nullptr, 0u};
+    Debug d{nullptr, 0u, p->d_stamps};
+    if (!p->stress_seed || !p->d_stress) return d;
     const size_t ni = p->h.items.size(), nc = p->h.chunks.size();
     const size_t off[4] = {0, ni, 2 * ni, 2 * ni + nc};
-    return Stress{p->d_stress + off[which], p->stress_seed};
+    d.order = p->d_stress + off[which];
+    d.seed = p->stress_seed;
+    return d;
 }
 
 // Launch counts of a kernel family and their group sizes (the fused kernels
@@ -149,16 +155,22 @@ const uint32_t *launch_members(halo_plan *p, int family)
 
 // The epoch argument of a fused launch: the host's count for eager calls; 0
 // (inferred on the device) for calls being captured and for every call after
-// the first capture, since replays then advance the counts unseen.
+// the first capture, since replays then advance the counts unseen. The count
+// moves only when the launch is enqueued (epoch_launched).
 uint32_t launch_epoch_arg(halo_plan *p, int family, hipStream_t s)
 {
-    if (!p->device_epochs) {
+    bool capturing = false;
+    if (!p->epochs.on_device) {
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
-            p->device_epochs = true;
+        capturing = hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
     }
-    if (p->device_epochs) return 0u;
-    return ++p->epochs[family];  // a wrap to 0 only asks for inference once
+    return p->epochs.next(family, capturing);
+}
+
+hipError_t epoch_launched(halo_plan *p, int family, hipError_t e)
+{
+    p->epochs.launched(family, e == hipSuccess);
+    return e;
 }
 
 hipError_t launch_fused(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
@@ -170,24 +182,27 @@ hipError_t launch_fused(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
     uint32_t idx_bytes = (uint32_t)(h.n_entries * 4);
     const Kernels k = kernels(h.item_entries);
     if (force_dir) {
-        Stress st = stress_of(p, kOrderItemsF);
+        Debug st = debug_of(p, kOrderItemsF);
         uint32_t *groups = launch_groups(p, halo::kFamItemsF);
         const uint32_t *members = launch_members(p, halo::kFamItemsF);
         uint32_t epoch = launch_epoch_arg(p, halo::kFamItemsF, s);
         void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_seg_items,
                         &p->d_state, &n_seg, &n_items, &groups, &members, &epoch,
                         &p->spin_limit, &p->d_err, &p->withhold, &st};
-        return hipLaunchKernel(k.unpack_fused, dim3(n_items), dim3(kThreads), args, 0, s);
+        return epoch_launched(p, halo::kFamItemsF,
+                              hipLaunchKernel(k.unpack_fused, dim3(n_items), dim3(kThreads), args,
+                                              0, s));
     }
     int32_t n_dom = h.n_dom;
-    Stress st = stress_of(p, kOrderItemsX);
+    Debug st = debug_of(p, kOrderItemsX);
     uint32_t *groups = launch_groups(p, halo::kFamItemsX);
     const uint32_t *members = launch_members(p, halo::kFamItemsX);
     uint32_t epoch = launch_epoch_arg(p, halo::kFamItemsX, s);
     void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_recv_from,
                     &p->d_seg_items, &p->d_state, &n_dom, &groups, &members, &epoch,
                     &p->spin_limit, &p->d_err, &p->withhold, &st};
-    return hipLaunchKernel(k.pack_fused, dim3(n_items), dim3(kThreads), args, 0, s);
+    return epoch_launched(p, halo::kFamItemsX,
+                          hipLaunchKernel(k.pack_fused, dim3(n_items), dim3(kThreads), args, 0, s));
 }
 
 // Transposed-form kernels: counters in the second block of state.
@@ -203,21 +218,23 @@ hipError_t launch_chunks(halo_plan *p, bool force_dir, float *buf, hipStream_t s
         uint32_t *groups = launch_groups(p, halo::kFamChunksF);
         const uint32_t *members = launch_members(p, halo::kFamChunksF);
         uint32_t epoch = launch_epoch_arg(p, halo::kFamChunksF, s);
-        Stress st = stress_of(p, kOrderChunksF);
+        Debug st = debug_of(p, kOrderChunksF);
         void *args[] = {&buf, &bytes, &p->d_mask, &p->d_chunks, &p->d_forder, &p->d_rows,
                         &p->d_dest_start, &p->d_send_to, &p->d_zone_chunks, &state, &n_dom,
                         &n_pulse, &groups, &members, &epoch, &p->spin_limit, &p->d_err,
                         &p->withhold, &st};
-        return hipLaunchKernel(k.pull_f, dim3(n), dim3(kThreads), args, 0, s);
+        return epoch_launched(p, halo::kFamChunksF,
+                              hipLaunchKernel(k.pull_f, dim3(n), dim3(kThreads), args, 0, s));
     }
     uint32_t *groups = launch_groups(p, halo::kFamChunksX);
     const uint32_t *members = launch_members(p, halo::kFamChunksX);
     uint32_t epoch = launch_epoch_arg(p, halo::kFamChunksX, s);
-    Stress st = stress_of(p, kOrderChunksX);
+    Debug st = debug_of(p, kOrderChunksX);
     void *args[] = {&buf, &bytes, &p->d_mask, &p->d_chunks, &p->d_rows, &p->d_dest_start,
                     &p->d_shift4, &p->d_x_arrivals, &state, &n_dom, &n_pulse, &groups,
                     &members, &epoch, &p->spin_limit, &p->d_err, &p->withhold, &st};
-    return hipLaunchKernel(k.push_x, dim3(n), dim3(kThreads), args, 0, s);
+    return epoch_launched(p, halo::kFamChunksX,
+                          hipLaunchKernel(k.push_x, dim3(n), dim3(kThreads), args, 0, s));
 }
 
 hipError_t launch_pulse(halo_plan *p, bool force_dir, float *buf, hipStream_t s, int32_t q)
@@ -242,7 +259,7 @@ hipError_t launch_atomic(halo_plan *p, float *buf, hipStream_t s)
     uint32_t idx_bytes = (uint32_t)(h.n_entries * 4);
     const Kernels k = kernels(h.item_entries);
     int32_t n_dom = h.n_dom;
-    Stress st = stress_of(p, kOrderItemsF);
+    Debug st = debug_of(p, kOrderItemsF);
     // its own counters and launch counts: which items wait differs from the
     // ordered force kernel
     uint32_t *state = p->d_state + halo::atomic_state_offset(h.seg.size());
@@ -252,7 +269,9 @@ hipError_t launch_atomic(halo_plan *p, float *buf, hipStream_t s)
     void *args[] = {&buf, &bytes, &p->d_idx, &idx_bytes, &p->d_items, &p->d_seg_items,
                     &state, &n_seg, &n_dom, &n_items, &groups, &members, &epoch,
                     &p->spin_limit, &p->d_err, &p->withhold, &st};
-    return hipLaunchKernel(k.unpack_atomic, dim3(n_items), dim3(kThreads), args, 0, s);
+    return epoch_launched(p, halo::kFamAtomicF,
+                          hipLaunchKernel(k.unpack_atomic, dim3(n_items), dim3(kThreads), args, 0,
+                                          s));
 }
 
 // One pulse of the staged baseline: two launches.
@@ -325,7 +344,7 @@ halo_status ensure_uploaded(halo_plan *p)
         return hip_fail(e, "halo_plan_upload");
     }
     std::memset(p->h_err, 0, 64);
-    for (uint32_t &e : p->epochs) e = 0;
+    p->epochs.reset();
     p->uploaded = true;
     return HALO_OK;
 }
@@ -361,17 +380,22 @@ hipError_t halo::plan_chunk_rows(halo_plan *p, const uint8_t *mask, const Chunk 
 namespace {
 
 // Calls whose first use allocates or synchronises (the upload, staging
-// buffers, origin maps) refuse a stream that is being captured.
-halo_status refuse_capture(hipStream_t stream, const char *what)
+// buffers, origin maps) refuse a stream that is being captured, and so do the
+// device plan builds, which queue clears and copies and then wait. The check
+// comes before anything is queued or freed.
+halo_status refuse_capture(hipStream_t stream, const char *what,
+                           const char *why = "its first call on a plan allocates and "
+                                             "synchronises, so it cannot be captured; call it "
+                                             "(or halo_plan_upload) once before capturing")
 {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
-        return fail(HALO_ERR_ARG, std::string(what) +
-                                      ": its first call on a plan allocates and synchronises, "
-                                      "so it cannot be captured; call it (or halo_plan_upload) "
-                                      "once before capturing");
+        return fail(HALO_ERR_ARG, std::string(what) + ": " + why);
     return HALO_OK;
 }
+
+constexpr const char *kBuildUncapturable =
+    "a plan build allocates, queues copies and waits for them, so it cannot be captured";
 
 halo_status check_exchange(halo_plan *p, float *buf, const char *what, void *stream)
 {
@@ -460,6 +484,10 @@ halo_status halo_plan_create_device_ex(const float *positions, int64_t n_atoms, 
 {
     if (!out) return fail(HALO_ERR_ARG, "halo_plan_create_device: NULL output pointer");
     *out = nullptr;
+    if (halo_status st = refuse_capture((hipStream_t)stream, "halo_plan_create_device",
+                                        kBuildUncapturable);
+        st != HALO_OK)
+        return st;
     halo_plan *p = new (std::nothrow) halo_plan();
     if (!p) return fail(HALO_ERR_NOMEM, "halo_plan_create_device: out of host memory");
     std::string msg;
@@ -489,6 +517,11 @@ halo_status halo_plan_rebuild_device(halo_plan *p, const float *positions, int64
                                      const float *box, void *stream)
 {
     if (!p || !box) return fail(HALO_ERR_ARG, "halo_plan_rebuild_device: NULL argument");
+    // before anything is freed or queued: a refused rebuild leaves the plan as it was
+    if (halo_status st = refuse_capture((hipStream_t)stream, "halo_plan_rebuild_device",
+                                        kBuildUncapturable);
+        st != HALO_OK)
+        return st;
     const int32_t grid[3] = {p->h.grid[0], p->h.grid[1], p->h.grid[2]};
     const float cutoff = p->h.cutoff;
     const int32_t selection = p->h.selection;
@@ -509,10 +542,13 @@ halo_status halo_plan_rebuild_device(halo_plan *p, const float *positions, int64
         if (p->d_stage) (void)hipFree(p->d_stage);
         if (p->d_origin) (void)hipFree(p->d_origin);
         if (p->d_stress) (void)hipFree(p->d_stress);
+        if (p->d_stamps) (void)hipFree(p->d_stamps);
         p->d_stage = nullptr;
         p->d_origin = nullptr;
         p->d_stress = nullptr;
         p->stress_seed = 0;
+        p->d_stamps = nullptr;
+        p->stamp_units = 0;
     }
     p->uploaded = false;
     std::string msg;
@@ -652,6 +688,22 @@ halo_status halo_plan_item_waits(const halo_plan *p, int32_t item, int32_t *segm
     if (segment) *segment = it.seg;
     if (xwait_mask) *xwait_mask = it.xwait_mask;
     if (await_mask) *await_mask = it.await_mask;
+    return HALO_OK;
+}
+
+int32_t halo_plan_num_chunks(const halo_plan *p) { return p ? (int32_t)p->h.chunks.size() : -1; }
+
+halo_status halo_plan_chunk(const halo_plan *p, int32_t chunk, int32_t *domain, int32_t *zone,
+                            int64_t *first, int32_t *count, uint32_t *mask)
+{
+    if (!p || chunk < 0 || chunk >= (int32_t)p->h.chunks.size())
+        return fail(HALO_ERR_ARG, "halo_plan_chunk: no such chunk");
+    const halo::Chunk &c = p->h.chunks[chunk];
+    if (domain) *domain = c.domain;
+    if (zone) *zone = c.zone;
+    if (first) *first = c.first;
+    if (count) *count = c.count;
+    if (mask) *mask = c.mask;
     return HALO_OK;
 }
 
@@ -835,7 +887,8 @@ halo_status halo_exchange_x_direct(halo_plan *p, float *x, void *stream)
     uint32_t bytes = (uint32_t)(h.total_slots * 12);
     uint32_t obytes = (uint32_t)(h.n_entries * 4);
     float lx = h.box[0], ly = h.box[1], lz = h.box[2];
-    void *args[] = {&x, &bytes, &p->d_origin, &obytes, &p->d_items, &lx, &ly, &lz};
+    Debug dbg{nullptr, 0u, p->d_stamps};
+    void *args[] = {&x, &bytes, &p->d_origin, &obytes, &p->d_items, &lx, &ly, &lz, &dbg};
     e = hipLaunchKernel(k.gather_x, dim3((uint32_t)h.items.size()), dim3(kThreads), args, 0, s);
     return e == hipSuccess ? HALO_OK : hip_fail(e, what);
 }
@@ -926,7 +979,7 @@ halo_status halo_plan_reset(halo_plan *p)
         (e = hipDeviceSynchronize()) != hipSuccess)
         return hip_fail(e, "halo_plan_reset");
     std::memset(p->h_err, 0, 64);
-    for (uint32_t &e : p->epochs) e = 0;
+    p->epochs.reset();
     p->poisoned = false;
     return HALO_OK;
 }
@@ -1000,6 +1053,57 @@ halo_status halo_plan_debug_stress(halo_plan *p, uint32_t seed)
     }
     p->stress_seed = seed;
     return HALO_OK;
+}
+
+halo_status halo_plan_debug_timing(halo_plan *p, int32_t enable)
+{
+    if (!p) return fail(HALO_ERR_ARG, "halo_plan_debug_timing: NULL plan");
+    if (p->invalid) return fail(HALO_ERR_STATE, "halo_plan_debug_timing: invalid plan");
+    halo_status st = ensure_uploaded(p);
+    if (st != HALO_OK) return st;
+    if (p->d_stamps) {
+        hipError_t e = hipDeviceSynchronize();  // no launch still writes the old buffer
+        if (e != hipSuccess) return hip_fail(e, "halo_plan_debug_timing");
+        (void)hipFree(p->d_stamps);
+        p->d_stamps = nullptr;
+        p->stamp_units = 0;
+    }
+    if (!enable) return HALO_OK;
+    const size_t units = std::max<size_t>({p->h.items.size(), p->h.chunks.size(), 1});
+    const size_t bytes = units * kStampWords * sizeof(uint64_t);
+    hipError_t e = hipMalloc((void **)&p->d_stamps, bytes);
+    if (e == hipSuccess) e = hipMemset(p->d_stamps, 0, bytes);
+    if (e != hipSuccess) {
+        if (p->d_stamps) (void)hipFree(p->d_stamps);
+        p->d_stamps = nullptr;
+        return hip_fail(e, "halo_plan_debug_timing");
+    }
+    p->stamp_units = units;
+    return HALO_OK;
+}
+
+halo_status halo_plan_debug_timing_read(halo_plan *p, uint64_t *stamps, int64_t max_units,
+                                        int64_t *units, int32_t *clock_khz)
+{
+    if (!p || !p->d_stamps)
+        return fail(HALO_ERR_ARG, "halo_plan_debug_timing_read: timing is not enabled");
+    const int64_t n = (int64_t)p->stamp_units;
+    if (units) *units = n;
+    if (clock_khz) {
+        int rate = 0;
+        hipError_t e = hipDeviceGetAttribute(&rate, hipDeviceAttributeWallClockRate, p->device);
+        if (e != hipSuccess) return hip_fail(e, "halo_plan_debug_timing_read");
+        *clock_khz = rate;
+    }
+    if (!stamps) return HALO_OK;
+    if (max_units < n)
+        return fail(HALO_ERR_ARG, "halo_plan_debug_timing_read: the buffer holds fewer units "
+                                  "than the plan's");
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess)
+        e = hipMemcpy(stamps, p->d_stamps, (size_t)n * kStampWords * sizeof(uint64_t),
+                      hipMemcpyDeviceToHost);
+    return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_plan_debug_timing_read");
 }
 
 halo_status halo_plan_debug_withhold(halo_plan *p, int32_t segment)

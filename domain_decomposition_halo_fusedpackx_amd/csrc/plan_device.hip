@@ -1085,7 +1085,7 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     pl->d_x_arrivals = x_arrivals;
     pl->d_zone_chunks = zone_chunks;
     pl->d_members = members;
-    for (uint32_t &e : pl->epochs) e = 0;
+    pl->epochs.reset();
     pl->poisoned = false;
     pl->built_on_device = true;
     pl->uploaded = true;

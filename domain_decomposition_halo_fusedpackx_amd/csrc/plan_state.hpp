@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <string>
 
+#include "epochs.hpp"
 #include "plan.hpp"
 
 namespace halo {
@@ -66,11 +67,8 @@ struct halo_plan {
     uint32_t *d_origin = nullptr;  // direct form: home slot | wrap bits per entry (lazy)
     uint32_t *d_members = nullptr;  // launch-count group sizes [family][group]
     // epochs of the fused kernel families as the host counts them; passed to
-    // eager launches. Once a fused exchange of the plan has been captured in a
-    // graph, the host no longer sees every launch and passes 0 (the kernels
-    // then infer the epoch from the launch counts).
-    uint32_t epochs[halo::kFamilies] = {};
-    bool device_epochs = false;
+    // eager launches (0 once a fused exchange of the plan has been captured)
+    halo::EpochBook<halo::kFamilies> epochs;
     // device-built plans: local-slot indexMap and home slot of every atom
     int32_t *d_local_map = nullptr;
     int64_t *d_home_slot = nullptr;
@@ -79,6 +77,9 @@ struct halo_plan {
     // testing: stress mode (seed 0 = off) and its launch orders
     uint32_t stress_seed = 0;
     int32_t *d_stress = nullptr;
+    // tuning: per-unit clock stamps of the fused kernels (nullptr = off)
+    uint64_t *d_stamps = nullptr;
+    size_t stamp_units = 0;
 };
 
 namespace halo {

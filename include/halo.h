@@ -54,8 +54,10 @@ typedef struct halo_plan halo_plan; /* opaque; created and freed by the library 
 typedef enum {
     HALO_OK = 0,
     HALO_ERR_ARG = -1,      /* NULL pointer, negative count, index out of range   */
-    HALO_ERR_GEOMETRY = -2, /* box/grid/cutoff not positive and finite, or more
-                               pulses in a dimension than n_d - 1                */
+    HALO_ERR_GEOMETRY = -2, /* box/grid/cutoff not positive and finite, more
+                               pulses in a dimension than n_d - 1, or more than
+                               32 pulses in all (the work items keep their
+                               per-pulse wait sets as 32-bit masks)              */
     HALO_ERR_RANGE = -3,    /* a position not finite or outside [0, L); more
                                slots than fit a 32-bit index                      */
     HALO_ERR_HIP = -4,      /* a HIP runtime call failed                          */
@@ -113,7 +115,9 @@ halo_status halo_plan_create_ex(const float *positions, int64_t n_atoms, const f
  *   positions : DEVICE, n_atoms*3 float32 on the current device, read on
  *               `stream` (so work queued there before the call is seen)
  *   stream    : a hipStream_t; the call synchronises it a few times (it reads
- *               back per-pulse sizes) and returns with the plan uploaded
+ *               back per-pulse sizes) and returns with the plan uploaded. A
+ *               stream that is being captured into a HIP graph gives
+ *               HALO_ERR_ARG before anything is queued.
  *   others    : as halo_plan_create.
  * Limits: at most 8192 domains (HALO_ERR_GEOMETRY beyond). A position not
  * finite or outside [0, L) gives HALO_ERR_RANGE naming the first such atom.
@@ -137,8 +141,9 @@ halo_status halo_plan_create_device_ex(const float *positions, int64_t n_atoms, 
  *   box : host, 3 float32
  * The counters restart (no exchange of this plan may be in flight on any
  * stream); total_slots, the layout and the home slots change, so x and f must
- * be re-laid out by the caller. Argument and geometry errors leave the plan
- * unchanged; any other error (HALO_ERR_RANGE for a position out of range, a
+ * be re-laid out by the caller. Argument and geometry errors, and a stream
+ * that is being captured (HALO_ERR_ARG, checked before anything is freed or
+ * queued), leave the plan unchanged; any other error (HALO_ERR_RANGE for a position out of range, a
  * HIP failure) leaves it empty, and exchanges return HALO_ERR_STATE until a
  * rebuild succeeds. */
 halo_status halo_plan_rebuild_device(halo_plan *plan, const float *positions, int64_t n_atoms,
@@ -197,6 +202,17 @@ halo_status halo_plan_pulse(const halo_plan *plan, int32_t p, int32_t d, int32_t
  * Any output may be NULL. A read-out for tests and tools. */
 halo_status halo_plan_item_waits(const halo_plan *plan, int32_t item, int32_t *segment,
                                  uint32_t *xwait_mask, uint32_t *await_mask);
+
+/* Chunks of the transposed form (0 for plans of more than 8 pulses), in
+ * launch order of its coordinate kernel: the home slots of every domain, then
+ * the region received in pulse 0, pulse 1, ... Chunk c is a run of `count`
+ * consecutive slots from absolute slot `first` of `domain`, inside its home
+ * slots (zone -1) or its region of pulse `zone`; bit p of `mask` is set when
+ * one of its slots is sent in pulse p. Outputs may be NULL. A read-out for
+ * tests and tools. */
+int32_t halo_plan_num_chunks(const halo_plan *plan);  /* -1 on NULL */
+halo_status halo_plan_chunk(const halo_plan *plan, int32_t chunk, int32_t *domain, int32_t *zone,
+                            int64_t *first, int32_t *count, uint32_t *mask);
 
 /* Allocate and upload the device metadata on the current HIP device (blocking:
  * it synchronises the device). The first exchange on a plan built by
@@ -354,6 +370,32 @@ halo_status halo_plan_debug_withhold(halo_plan *plan, int32_t segment);
  * seed = 0 (the default) turns it off. Synchronises the device when it
  * changes an existing setting. A rebuild turns it off. */
 halo_status halo_plan_debug_stress(halo_plan *plan, uint32_t seed);
+
+/* Tuning aid (where an exchange's time goes along the forwarding chain of
+ * "Redesigning GROMACS Halo Exchange", Algorithms 4-6): with enable != 0, the
+ * fused kernels of every form and halo_exchange_x_direct record, for every
+ * work unit (work item or chunk) they run, the device's constant-rate clock
+ * at the unit's start, when its first dependency wait begins, when its last
+ * wait ends, when its first completion signal is sent (its stores complete)
+ * and at its end, plus where it ran. Each launch overwrites the records of
+ * the units it runs. enable == 0 frees the record buffer. The call allocates
+ * and synchronises the device (not under graph capture); a rebuild turns the
+ * recording off. Results of the exchanges do not change. */
+halo_status halo_plan_debug_timing(halo_plan *plan, int32_t enable);
+
+/* Copy the records of halo_plan_debug_timing (blocking: synchronises the
+ * device). Unit u (a work item of the index-list and direct forms, a chunk of
+ * the transposed form, in the plan's unit numbering) occupies words
+ * [8u, 8u + 8) of `stamps` (host memory of max_units * 8 uint64):
+ *   0 start, 1 first wait begins, 2 last wait ends, 3 first signal sent,
+ *   4 end (clock ticks; 0 = the unit did not reach that step),
+ *   5 workgroup index, 6 HW_ID register, 7 XCC_ID register.
+ *   units     : receives the number of units recorded (may be NULL)
+ *   clock_khz : receives the clock's rate in kHz (may be NULL)
+ * stamps may be NULL to query units and clock_khz only; HALO_ERR_ARG if the
+ * recording is off or max_units is below the unit count. */
+halo_status halo_plan_debug_timing_read(halo_plan *plan, uint64_t *stamps, int64_t max_units,
+                                        int64_t *units, int32_t *clock_khz);
 
 #ifdef __cplusplus
 }

@@ -5,9 +5,11 @@ CPU-baseline leg of bench.py. It shares no code with the HIP library.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 import subprocess
+import weakref
 
 import numpy as np
 
@@ -29,6 +31,14 @@ def build(force: bool = False) -> str:
 
 
 _lib = None
+# Oracles still open are freed by an atexit hook, while the module is intact.
+_LIVE = weakref.WeakSet()
+
+
+@atexit.register
+def _close_live():
+    for o in list(_LIVE):
+        o.close()
 
 
 def lib():
@@ -101,19 +111,22 @@ class Oracle:
         if rc != 0:
             raise OracleError(rc)
         self._h = h
+        self._free = L.oracle_free
+        _LIVE.add(self)
         self.n_atoms = pos.shape[0]
         self.total_slots = L.oracle_total_slots(h)
         self.n_dom = L.oracle_num_domains(h)
         self.n_pulse = L.oracle_num_pulses(h)
 
-    def __del__(self):
+    def close(self):
+        """Free the C oracle (also done by __del__ and at interpreter exit)."""
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            try:
-                lib().oracle_free(h)
-            except Exception:  # interpreter shutdown: the module may be gone
-                pass
-            self._h = None
+            self._free(h)
+        self._h = None
+
+    def __del__(self):
+        self.close()
 
     # -- plan read-out -------------------------------------------------------
     def geometry(self):

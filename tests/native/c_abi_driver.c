@@ -121,8 +121,29 @@ static int run_case(const Case *c, uint64_t seed, hipStream_t stream)
     CHECK_HALO(halo_plan_create_device_ex(n ? pos_dev : NULL, n, c->box, c->grid, c->cutoff,
                                           c->selection, stream, &dp));
 
+    /* A device build on a stream that is being captured is refused before
+     * anything is queued or freed: both calls return HALO_ERR_ARG, the graph
+     * stays empty, and dp still exchanges bit for bit below. */
+    int capture_ok = 1;
+    {
+        hipGraph_t g = NULL;
+        halo_plan *q = dp;
+        size_t nodes = 1;
+        CHECK_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeRelaxed));
+        const halo_status s1 = halo_plan_create_device_ex(n ? pos_dev : NULL, n, c->box, c->grid,
+                                                          c->cutoff, c->selection, stream, &q);
+        const halo_status s2 = halo_plan_rebuild_device(dp, n ? pos_dev : NULL, n, c->box, stream);
+        CHECK_HIP(hipStreamEndCapture(stream, &g));
+        CHECK_HIP(hipGraphGetNodes(g, NULL, &nodes));
+        CHECK_HIP(hipGraphDestroy(g));
+        capture_ok = s1 == HALO_ERR_ARG && q == NULL && s2 == HALO_ERR_ARG && nodes == 0;
+        if (!capture_ok)
+            printf("device build under capture: create %d rebuild %d, %zu graph node(s)\n",
+                   (int)s1, (int)s2, nodes);
+    }
+
     const int64_t slots = oracle_total_slots(o);
-    int ok = halo_plan_total_slots(hp) == slots && halo_plan_total_slots(dp) == slots &&
+    int ok = capture_ok && halo_plan_total_slots(hp) == slots && halo_plan_total_slots(dp) == slots &&
              halo_plan_selection(hp) == c->selection && halo_plan_selection(dp) == c->selection;
     int64_t *hs_o = (int64_t *)malloc((size_t)(n + 1) * 8), *hs_h = (int64_t *)malloc((size_t)(n + 1) * 8),
             *hs_d = (int64_t *)malloc((size_t)(n + 1) * 8);
@@ -295,11 +316,25 @@ int main(int argc, char **argv)
 {
     if (argc > 1 && strcmp(argv[1], "--time") == 0) {
         const Case tc[] = {{{3.f, 3.f, 6.f}, {1, 1, 2}, 1.0f, 5400, HALO_SELECT_SLAB},
-                           {{6.f, 6.f, 6.f}, {2, 2, 2}, 1.0f, 21600, HALO_SELECT_SLAB}};
+                           {{6.f, 6.f, 6.f}, {2, 2, 2}, 1.0f, 21600, HALO_SELECT_SLAB},
+                           {{15.f, 15.f, 15.f}, {4, 4, 4}, 1.2f, 337500, HALO_SELECT_SLAB},
+                           {{8.f, 8.f, 8.f}, {4, 4, 8}, 1.2f, 51200, HALO_SELECT_SLAB},
+                           {{22.f, 22.f, 22.f}, {8, 8, 8}, 1.2f, 1064800, HALO_SELECT_SLAB}};
         hipStream_t stream;
         CHECK_HIP(hipSetDevice(0));
         CHECK_HIP(hipStreamCreate(&stream));
         for (size_t i = 0; i < sizeof(tc) / sizeof(tc[0]); ++i) time_case(&tc[i], stream);
+        {
+            /* the capture query every eager fused launch makes */
+            const int reps = 100000;
+            hipStreamCaptureStatus cs;
+            struct timespec t0, t1;
+            clock_gettime(CLOCK_MONOTONIC, &t0);
+            for (int i = 0; i < reps; ++i) CHECK_HIP(hipStreamIsCapturing(stream, &cs));
+            clock_gettime(CLOCK_MONOTONIC, &t1);
+            printf("time hipStreamIsCapturing: %.3f us per call\n",
+                   ((t1.tv_sec - t0.tv_sec) * 1e9 + (t1.tv_nsec - t0.tv_nsec)) / 1e3 / reps);
+        }
         CHECK_HIP(hipStreamDestroy(stream));
         return 0;
     }

@@ -37,3 +37,17 @@ def test_plan_builder_and_oracle_under_sanitizers(tmp_path):
                        timeout=300)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
     assert "0 case(s) differ" in r.stdout
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="no host compiler")
+def test_epoch_bookkeeping_under_sanitizers(tmp_path):
+    """The host's epoch count per kernel family moves only for launches that
+    were enqueued, and a capture switches the plan to inferred epochs."""
+    exe = os.path.join(str(tmp_path), "epoch_check")
+    subprocess.check_call(["g++", *SAN, "-std=c++17", "-I", CSRC,
+                           os.path.join(ROOT, "tests", "native", "epoch_check.cpp"), "-o", exe])
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1:verify_asan_link_order=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "0 epoch check(s) failed" in r.stdout

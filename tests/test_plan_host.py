@@ -198,3 +198,23 @@ def test_item_wait_masks(oracle_mod, wid):
                 want_am |= 1 << qq
         for _, am in lst:
             assert int(am) == want_am, (p, d)
+
+
+def test_more_than_32_pulses_is_a_geometry_error(oracle_mod):
+    """The library caps a plan at 32 pulses (its work items keep per-pulse wait
+    sets as 32-bit masks); the oracle has no such cap. A 12x12x12 grid of 1 nm
+    domains with a 10.5 nm cutoff needs 11 pulses per dimension, 33 in all:
+    the oracle builds it, the library refuses it with HALO_ERR_GEOMETRY and
+    says why. With 1.1 nm domains in z (10 pulses there) the plan has 32
+    pulses and builds."""
+    pos = np.zeros((0, 3), np.float32)
+    grid = (12, 12, 12)
+    assert oracle_mod.try_build(pos, (12.0, 12.0, 12.0), grid, 10.5) == 0
+    with pytest.raises(HaloError) as e:
+        HaloPlan(pos, (12.0, 12.0, 12.0), grid, 10.5)
+    assert e.value.code == -2
+    assert "33 pulses" in str(e.value) and "at most 32" in str(e.value)
+    plan = HaloPlan(pos, (12.0, 12.0, 13.2), grid, 10.5)
+    assert plan.num_pulses == 32
+    o = oracle_mod.Oracle(pos, (12.0, 12.0, 13.2), grid, 10.5)
+    assert o.n_pulse == 32
