@@ -379,6 +379,8 @@ def stage_profile(torch, HaloPlan, W, w, pos, launches, reps):
     waits = plan.item_waits()
     pulse_of_item = waits[:, 0] // plan.num_domains
     chunks = plan.chunks()
+    # plans built on the host run the index-list exchanges on XCD-local units
+    lunits = plan.local_units()
     runs = [("x", "indexmap"), ("x", "transposed"), ("x", "direct"), ("f", "indexmap"),
             ("f", "transposed")]
     out = {"workload": w.describe(), "halo_entries": plan.num_entries,
@@ -394,12 +396,22 @@ def stage_profile(torch, HaloPlan, W, w, pos, launches, reps):
             ev_us.append(time_loop(torch, lambda i: fn(buf), launches) * 1e3)
             st, khz = plan.debug_timing_read()
             tick_us = 1e3 / khz
-            n_units = len(chunks) if form == "transposed" else plan.num_items
+            local = form == "indexmap" and len(lunits) > 0
+            n_units = (len(chunks) if form == "transposed" else
+                       len(lunits) if local else plan.num_items)
             st = st[:n_units]
+            if local:  # empty positions only record their start and end
+                st = st[lunits[:, 2] > 0]
             t0 = st[:, 0].min()
             rel = {k: (st[:, i] - t0) * tick_us for i, k in enumerate(STAGE_FIELDS)}
             reached = {k: st[:, i] != 0 for i, k in enumerate(STAGE_FIELDS)}
-            if form == "transposed":
+            if local:
+                lu = lunits[lunits[:, 2] > 0]
+                nw = lu[:, 3] if d == "x" else lu[:, 4]
+                keys = [f"pulse{sg // plan.num_domains}:"
+                        f"{('forwards' if d == 'x' else 'waits') if w else ('home' if d == 'x' else 'no wait')}"
+                        for sg, w in zip(lu[:, 0], nw)]
+            elif form == "transposed":
                 keys = ["home" if z < 0 else f"region{z}" for z in chunks[:, 1]]
             elif d == "x" and form == "indexmap":
                 keys = [f"pulse{p}:{'forwards' if wm else 'home'}"
@@ -417,9 +429,13 @@ def stage_profile(torch, HaloPlan, W, w, pos, launches, reps):
                         g[fld] = (float(np.median(rel[fld][m])), float(rel[fld][m].max()))
                 groups[k] = g
             per_rep.append({"span_us": float(rel["end"][reached["end"]].max()),
-                            "groups": groups})
+                            "groups": groups,
+                            "xcc_round_robin": float(np.mean(
+                                (st[:, 7] - st[:, 5]) % 8 ==
+                                np.bincount((st[:, 7] - st[:, 5]) % 8).argmax()))})
         med = {"us_per_launch_events": float(np.median(ev_us)),
-               "span_us": float(np.median([r["span_us"] for r in per_rep])), "groups": {}}
+               "span_us": float(np.median([r["span_us"] for r in per_rep])),
+               "xcc_round_robin": min(r["xcc_round_robin"] for r in per_rep), "groups": {}}
         for k, g in per_rep[0]["groups"].items():
             mg = {"units": g["units"]}
             for fld in STAGE_FIELDS:
@@ -430,7 +446,8 @@ def stage_profile(torch, HaloPlan, W, w, pos, launches, reps):
             med["groups"][k] = mg
         out[f"{d}_{form}"] = med
         log(f"stages {d} {form}: {med['us_per_launch_events']:.2f} us per launch (events), "
-            f"first start to last end {med['span_us']:.2f} us")
+            f"first start to last end {med['span_us']:.2f} us, workgroups on XCD "
+            f"(index + r) mod 8: {100 * med['xcc_round_robin']:.1f} %")
         for k, g in med["groups"].items():
             cols = "  ".join(f"{fld} {g[fld][0]:6.2f}/{g[fld][1]:6.2f}" for fld in STAGE_FIELDS
                              if fld in g)

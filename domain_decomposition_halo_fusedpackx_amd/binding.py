@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libhalo.so")
 
 STATUS = {0: "HALO_OK", -1: "HALO_ERR_ARG", -2: "HALO_ERR_GEOMETRY", -3: "HALO_ERR_RANGE",
-          -4: "HALO_ERR_HIP", -5: "HALO_ERR_TIMEOUT", -6: "HALO_ERR_STATE", -7: "HALO_ERR_NOMEM"}
+          -4: "HALO_ERR_HIP", -5: "HALO_ERR_TIMEOUT", -6: "HALO_ERR_STATE", -7: "HALO_ERR_NOMEM", -8: "HALO_ERR_PLACEMENT"}
 
 # Every symbol include/halo.h declares, with (restype, argtypes).
 _vp, _i32, _i64, _u32, _f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
@@ -45,6 +45,8 @@ SIGNATURES = {
                               _P(_i32), _P(_i32), _vp, _vp]),
     "halo_plan_item_waits": (_st, [_vp, _i32, _P(_i32), _P(_u32), _P(_u32)]),
     "halo_plan_num_chunks": (_i32, [_vp]),
+    "halo_plan_num_local_units": (_i32, [_vp]),
+    "halo_plan_local_unit": (_st, [_vp, _i32, _P(_i32), _P(_i32), _P(_i32), _P(_i32), _P(_i32)]),
     "halo_plan_chunk": (_st, [_vp, _i32, _P(_i32), _P(_i32), _P(_i64), _P(_i32), _P(_u32)]),
     "halo_plan_upload": (_st, [_vp]),
     "halo_exchange_x": (_st, [_vp, _vp, _vp]),
@@ -316,6 +318,18 @@ class HaloPlan:
             _check(lib.halo_plan_chunk(self._h, i, ctypes.byref(d), ctypes.byref(z),
                                        ctypes.byref(f), ctypes.byref(c), ctypes.byref(m)))
             out[i] = (d.value, z.value, f.value, c.value, m.value)
+        return out
+
+    def local_units(self):
+        """(segment, origin, entries, x_waits, f_waits) of every XCD-local
+        unit position (empty positions: segment and origin -1)."""
+        lib = load_library()
+        n = lib.halo_plan_num_local_units(self._h)
+        out = np.zeros((max(n, 0), 5), np.int64)
+        v = [ctypes.c_int32() for _ in range(5)]
+        for i in range(n):
+            _check(lib.halo_plan_local_unit(self._h, i, *[ctypes.byref(x) for x in v]))
+            out[i] = [x.value for x in v]
         return out
 
     # -- device side ------------------------------------------------------------

@@ -464,6 +464,147 @@ __global__ __launch_bounds__(kThreads) void k_unpack_atomic(
     stamp(dbg, u, kStampEnd);
 }
 
+// ---- index-list form, XCD-local units (plans built on the host) -------------
+// The same exchanges as k_pack_fused / k_unpack_fused, with the units of
+// plan.hpp's LocalUnit: runs of one origin, placed so that every dependency
+// stays on one XCD. Data written in the launch and read by another unit
+// stays in that XCD's L2 (plain stores, reads past the CU cache); the
+// signals are per-unit flag words (sync.hpp, wait_flags / set_local_flag).
+// Unit position b is workgroup b of the coordinate kernel and workgroup
+// n - 1 - b of the force kernel; empty positions exit at once.
+
+// Coordinates (Algorithms 3 and 4): x[region_begin + e] = x[idx[map_begin +
+// e]] + shift; a unit that reads a region first waits for its writers.
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_pack_local(
+    float *x, uint32_t x_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
+    const halo::LocalUnit *__restrict__ units, const int32_t *__restrict__ waits,
+    uint64_t *flags, int32_t kp, uint32_t *groups, const uint32_t *__restrict__ members,
+    uint32_t host_epoch, uint32_t spin_limit, uint32_t *err_word, int32_t withhold, Debug dbg)
+{
+    const int32_t b = dbg.order ? dbg.order[blockIdx.x] : (int32_t)blockIdx.x;
+    stamp_start(dbg, (uint32_t)b);
+    const halo::LocalUnit *un = units + b;
+    const int32_t n = un->n_total;
+    if (n == 0) {  // an empty position
+        stamp(dbg, (uint32_t)b, kStampEnd);
+        return;
+    }
+    if (dbg.seed) stress_delay(dbg.seed, (uint32_t)b);
+    halo::LaunchState ls = halo::launch_state(groups, members, (uint32_t)b, host_epoch);
+    const int32_t nw = un->wx_n;
+    const bool flagged = (un->flags & halo::kLocalXWaited) != 0;
+    const bool member = nw > 0 || flagged;
+    halo::count_early(ls, member);
+    const auto rx = make_rsrc(x, x_bytes), ridx = make_rsrc(idx, idx_bytes);
+    const f3v shift = {un->shift[0], un->shift[1], un->shift[2]};
+    const int32_t map_begin = un->map_begin, region_begin = un->region_begin;
+    uint32_t src[EPT], dst[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        const bool ok = e < n;
+        src[j] = load_index(ridx, map_begin + e, ok) * 12u;
+        dst[j] = ok ? (uint32_t)(region_begin + e) * 12u : kInvalid;
+    }
+    f3v v[EPT];
+    if (nw == 0) {
+        // home slots: final before the launch
+        if (flagged) halo::learn_epoch(ls.lg, ls.epoch);
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) v[j] = load3<kPlain>(rx, src[j]);
+    } else {
+        stamp(dbg, (uint32_t)b, kStampWaitBegin);
+        halo::wait_flags(waits + un->wx_off, nw, flags, kp, ls.lg, ls.epoch, spin_limit,
+                         err_word);
+        stamp(dbg, (uint32_t)b, kStampWaitEnd);
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) v[j] = load3<kShared>(rx, src[j]);
+    }
+    if (flagged) {
+        // a later unit of this XCD forwards these slots
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) store3<kPlain>(rx, dst[j], v[j] + shift);
+        halo::set_local_flag(flags, kp, b, ls.epoch, un->seg == withhold);
+        stamp(dbg, (uint32_t)b, kStampSignal);
+    } else {
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) store3<kStream>(rx, dst[j], v[j] + shift);
+    }
+    halo::count_late(ls, member);
+    stamp(dbg, (uint32_t)b, kStampEnd);
+}
+
+// Forces (Algorithm 6, pulses in reverse): f[idx[map_begin + e]] +=
+// f[region_begin + e], after every later unit that adds into either slot.
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void k_unpack_local(
+    float *f, uint32_t f_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
+    const halo::LocalUnit *__restrict__ units, int32_t n_units,
+    const int32_t *__restrict__ waits, uint64_t *flags, int32_t kp, uint32_t *groups,
+    const uint32_t *__restrict__ members, uint32_t host_epoch, uint32_t spin_limit,
+    uint32_t *err_word, int32_t withhold, Debug dbg)
+{
+    const int32_t b = dbg.order ? dbg.order[blockIdx.x] : n_units - 1 - (int32_t)blockIdx.x;
+    stamp_start(dbg, (uint32_t)b);
+    const halo::LocalUnit *un = units + b;
+    const int32_t n = un->n_total;
+    if (n == 0) {  // an empty position
+        stamp(dbg, (uint32_t)b, kStampEnd);
+        return;
+    }
+    if (dbg.seed) stress_delay(dbg.seed, (uint32_t)b);
+    halo::LaunchState ls = halo::launch_state(groups, members, (uint32_t)b, host_epoch);
+    const int32_t nw = un->wf_n;
+    const bool flagged = (un->flags & halo::kLocalFWaited) != 0;
+    const bool member = nw > 0 || flagged;
+    halo::count_early(ls, member);
+    const auto rf = make_rsrc(f, f_bytes), ridx = make_rsrc(idx, idx_bytes);
+    const int32_t map_begin = un->map_begin, region_begin = un->region_begin;
+    // the indexMap is read-only in the launch: its loads go out before the wait
+    uint32_t tgt[EPT], src[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        const bool ok = e < n;
+        const uint32_t t = load_index(ridx, map_begin + e, ok) * 12u;
+        tgt[j] = ok ? t : kInvalid;
+        src[j] = ok ? (uint32_t)(region_begin + e) * 12u : kInvalid;
+    }
+    f3v add[EPT], cur[EPT];
+    if (nw == 0) {
+        // no unit of this launch has touched these slots yet
+        if (flagged) halo::learn_epoch(ls.lg, ls.epoch);
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            add[j] = load3<kStream>(rf, src[j]);
+            cur[j] = load3<kStream>(rf, tgt[j]);
+        }
+    } else {
+        stamp(dbg, (uint32_t)b, kStampWaitBegin);
+        halo::wait_flags(waits + un->wf_off, nw, flags, kp, ls.lg, ls.epoch, spin_limit,
+                         err_word);
+        stamp(dbg, (uint32_t)b, kStampWaitEnd);
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            add[j] = load3<kShared>(rf, src[j]);
+            cur[j] = load3<kShared>(rf, tgt[j]);
+        }
+    }
+    if (flagged) {
+        // an earlier pulse reads or adds into these targets in this launch
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) store3<kPlain>(rf, tgt[j], cur[j] + add[j]);
+        halo::set_local_flag(flags, kp, b, ls.epoch, un->seg == withhold);
+        stamp(dbg, (uint32_t)b, kStampSignal);
+    } else {
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) store3<kStream>(rf, tgt[j], cur[j] + add[j]);
+    }
+    halo::count_late(ls, member);
+    stamp(dbg, (uint32_t)b, kStampEnd);
+}
+
 // ---- transposed form: per-slot pulse masks --------------------------------
 
 // Pulse ranks of one chunk. Thread t owns slots first + t + j*256 (j < EPT),

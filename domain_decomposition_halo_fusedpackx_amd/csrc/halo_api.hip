@@ -54,7 +54,8 @@ void free_device(halo_plan *p)
                     (void *)p->d_forder, (void *)p->d_dest_start, (void *)p->d_shift4,
                     (void *)p->d_x_arrivals, (void *)p->d_zone_chunks, (void *)p->d_local_map,
                     (void *)p->d_home_slot, (void *)p->d_stress, (void *)p->d_origin,
-                    (void *)p->d_members, (void *)p->d_rows, (void *)p->d_stamps})
+                    (void *)p->d_members, (void *)p->d_rows, (void *)p->d_stamps,
+                    (void *)p->d_lunits, (void *)p->d_lwaits, (void *)p->d_lflags})
         if (q) (void)hipFree(q);
     if (p->h_err) (void)hipHostFree(p->h_err);
     p->d_idx = p->d_recv_from = p->d_send_to = p->d_forder = p->d_dest_start = nullptr;
@@ -62,6 +63,10 @@ void free_device(halo_plan *p)
     p->stress_seed = 0;
     p->d_stamps = nullptr;
     p->stamp_units = 0;
+    p->d_lunits = nullptr;
+    p->d_lwaits = nullptr;
+    p->d_lflags = nullptr;
+    p->lflag_words = 0;
     p->d_local_map = nullptr;
     p->d_home_slot = nullptr;
     p->d_items = nullptr;
@@ -100,7 +105,7 @@ int ept_for(int32_t item_entries)
 struct Kernels {
     const void *pack_fused, *unpack_fused, *pack_pulse, *unpack_pulse, *push_x, *pull_f,
         *unpack_atomic, *stage_pack, *stage_move, *stage_unpack, *origin_pulse, *gather_x,
-        *chunk_rows;
+        *chunk_rows, *pack_local, *unpack_local;
 };
 
 template <int EPT>
@@ -112,7 +117,8 @@ Kernels kernels_for()
             (const void *)&k_unpack_atomic<EPT>, (const void *)&k_stage_pack<EPT>,
             (const void *)&k_stage_move<EPT>,    (const void *)&k_stage_unpack<EPT>,
             (const void *)&k_origin_pulse<EPT>,  (const void *)&k_gather_x<EPT>,
-            (const void *)&k_chunk_rows<EPT>};
+            (const void *)&k_chunk_rows<EPT>,    (const void *)&k_pack_local<EPT>,
+            (const void *)&k_unpack_local<EPT>};
 }
 
 Kernels kernels(int32_t item_entries)
@@ -126,16 +132,24 @@ Kernels kernels(int32_t item_entries)
 }
 
 // Debugging modes of a kernel family: the stress-mode order (see
-// halo_plan_debug_stress; [items X | items F | chunks X | chunks F] in
-// p->d_stress) and the timing stamps (halo_plan_debug_timing).
-enum StressOrder { kOrderItemsX = 0, kOrderItemsF = 1, kOrderChunksX = 2, kOrderChunksF = 3 };
+// halo_plan_debug_stress; [items X | items F | chunks X | chunks F | local
+// units X | local units F] in p->d_stress) and the timing stamps
+// (halo_plan_debug_timing).
+enum StressOrder {
+    kOrderItemsX = 0,
+    kOrderItemsF = 1,
+    kOrderChunksX = 2,
+    kOrderChunksF = 3,
+    kOrderLocalX = 4,
+    kOrderLocalF = 5
+};
 
 Debug debug_of(const halo_plan *p, StressOrder which)
 {
     Debug d{nullptr, 0u, p->d_stamps};
     if (!p->stress_seed || !p->d_stress) return d;
-    const size_t ni = p->h.items.size(), nc = p->h.chunks.size();
-    const size_t off[4] = {0, ni, 2 * ni, 2 * ni + nc};
+    const size_t ni = p->h.items.size(), nc = p->h.chunks.size(), nl = p->h.lunits.size();
+    const size_t off[6] = {0, ni, 2 * ni, 2 * ni + nc, 2 * ni + 2 * nc, 2 * ni + 2 * nc + nl};
     d.order = p->d_stress + off[which];
     d.seed = p->stress_seed;
     return d;
@@ -274,6 +288,38 @@ hipError_t launch_atomic(halo_plan *p, float *buf, hipStream_t s)
                                           s));
 }
 
+// XCD-local index-list kernels (plans built on the host): one launch, one
+// unit position per workgroup; the flags of the coordinate direction, then
+// of the force direction.
+hipError_t launch_local(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
+{
+    const halo::HostPlan &h = p->h;
+    uint32_t bytes = (uint32_t)(h.total_slots * 12);
+    uint32_t idx_bytes = (uint32_t)(h.n_entries * 4);
+    int32_t n_units = (int32_t)h.lunits.size();
+    int32_t kp = halo::local_flag_stride(h.local_k);
+    const Kernels k = kernels(h.item_entries);
+    const int fam = force_dir ? halo::kFamItemsF : halo::kFamItemsX;
+    uint32_t *groups = launch_groups(p, fam);
+    const uint32_t *members = launch_members(p, fam);
+    uint32_t epoch = launch_epoch_arg(p, fam, s);
+    Debug dbg = debug_of(p, force_dir ? kOrderLocalF : kOrderLocalX);
+    uint64_t *flags = p->d_lflags + (force_dir ? (size_t)kp * halo::kXcdClasses : 0);
+    hipError_t e;
+    if (force_dir) {
+        void *args[] = {&buf,  &bytes,  &p->d_idx, &idx_bytes, &p->d_lunits, &n_units,
+                        &p->d_lwaits, &flags, &kp, &groups, &members, &epoch,
+                        &p->spin_limit, &p->d_err, &p->withhold, &dbg};
+        e = hipLaunchKernel(k.unpack_local, dim3((uint32_t)n_units), dim3(kThreads), args, 0, s);
+    } else {
+        void *args[] = {&buf,   &bytes, &p->d_idx, &idx_bytes, &p->d_lunits, &p->d_lwaits,
+                        &flags, &kp,    &groups,   &members,   &epoch,       &p->spin_limit,
+                        &p->d_err, &p->withhold, &dbg};
+        e = hipLaunchKernel(k.pack_local, dim3((uint32_t)n_units), dim3(kThreads), args, 0, s);
+    }
+    return epoch_launched(p, fam, e);
+}
+
 // One pulse of the staged baseline: two launches.
 hipError_t launch_staged(halo_plan *p, bool force_dir, float *buf, hipStream_t s, int32_t q)
 {
@@ -331,6 +377,16 @@ halo_status ensure_uploaded(halo_plan *p)
         (e = halo::plan_chunk_rows(p, p->d_mask, p->d_chunks, nullptr)) != hipSuccess) {
         free_device(p);
         return hip_fail(e, "halo_plan_upload");
+    }
+    if (h.has_local) {
+        p->lflag_words = 2 * (size_t)halo::kXcdClasses * halo::local_flag_stride(h.local_k);
+        if ((e = upload_vec(&p->d_lunits, h.lunits)) != hipSuccess ||
+            (e = upload_vec(&p->d_lwaits, h.lwaits)) != hipSuccess ||
+            (e = hipMalloc((void **)&p->d_lflags, p->lflag_words * 8)) != hipSuccess ||
+            (e = hipMemset(p->d_lflags, 0, p->lflag_words * 8)) != hipSuccess) {
+            free_device(p);
+            return hip_fail(e, "halo_plan_upload");
+        }
     }
     // two counter blocks (work items, chunks), each X then F, and the launch
     // counts; 128 B per counter
@@ -408,8 +464,8 @@ halo_status check_exchange(halo_plan *p, float *buf, const char *what, void *str
         p->poisoned = true;
     if (p->poisoned)
         return fail(HALO_ERR_STATE, std::string(what) +
-                                        ": plan poisoned by an in-kernel wait timeout; call "
-                                        "halo_plan_reset");
+                                        ": plan poisoned by an in-kernel wait timeout or "
+                                        "placement error; call halo_plan_reset");
     halo_status st;
     if (!p->uploaded && (st = refuse_capture((hipStream_t)stream, what)) != HALO_OK) return st;
     st = ensure_uploaded(p);
@@ -693,6 +749,26 @@ halo_status halo_plan_item_waits(const halo_plan *p, int32_t item, int32_t *segm
 
 int32_t halo_plan_num_chunks(const halo_plan *p) { return p ? (int32_t)p->h.chunks.size() : -1; }
 
+int32_t halo_plan_num_local_units(const halo_plan *p)
+{
+    return p ? (int32_t)p->h.lunits.size() : -1;
+}
+
+halo_status halo_plan_local_unit(const halo_plan *p, int32_t position, int32_t *segment,
+                                 int32_t *origin, int32_t *entries, int32_t *x_waits,
+                                 int32_t *f_waits)
+{
+    if (!p || position < 0 || position >= (int32_t)p->h.lunits.size())
+        return fail(HALO_ERR_ARG, "halo_plan_local_unit: no such unit position");
+    const halo::LocalUnit &u = p->h.lunits[(size_t)position];
+    if (segment) *segment = u.n_total > 0 ? u.seg : -1;
+    if (origin) *origin = u.n_total > 0 ? u.origin : -1;
+    if (entries) *entries = u.n_total;
+    if (x_waits) *x_waits = u.wx_n;
+    if (f_waits) *f_waits = u.wf_n;
+    return HALO_OK;
+}
+
 halo_status halo_plan_chunk(const halo_plan *p, int32_t chunk, int32_t *domain, int32_t *zone,
                             int64_t *first, int32_t *count, uint32_t *mask)
 {
@@ -768,7 +844,8 @@ halo_status halo_exchange_x_indexmap(halo_plan *p, float *x, void *stream)
     halo_status st = check_exchange(p, x, "halo_exchange_x_indexmap", stream);
     if (st != HALO_OK) return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
-    hipError_t e = launch_fused(p, false, x, (hipStream_t)stream);
+    hipError_t e = p->h.has_local ? launch_local(p, false, x, (hipStream_t)stream)
+                                  : launch_fused(p, false, x, (hipStream_t)stream);
     return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_x_indexmap launch");
 }
 
@@ -777,7 +854,8 @@ halo_status halo_exchange_f_indexmap(halo_plan *p, float *f, void *stream)
     halo_status st = check_exchange(p, f, "halo_exchange_f_indexmap", stream);
     if (st != HALO_OK) return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
-    hipError_t e = launch_fused(p, true, f, (hipStream_t)stream);
+    hipError_t e = p->h.has_local ? launch_local(p, true, f, (hipStream_t)stream)
+                                  : launch_fused(p, true, f, (hipStream_t)stream);
     return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_f_indexmap launch");
 }
 
@@ -959,7 +1037,15 @@ halo_status halo_plan_sync(halo_plan *p, void *stream)
     if (!p->uploaded) return HALO_OK;
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "halo_plan_sync");
-    if (__atomic_load_n(p->h_err, __ATOMIC_ACQUIRE) != 0) {
+    const uint32_t word = __atomic_load_n(p->h_err, __ATOMIC_ACQUIRE);
+    if (word == halo::kErrWordPlacement) {
+        p->poisoned = true;
+        return fail(HALO_ERR_PLACEMENT,
+                    "halo_plan_sync: a work unit ran on another XCD than the units it waits "
+                    "for (the grid's workgroups did not go to the XCDs round-robin); the "
+                    "results of that exchange are not valid");
+    }
+    if (word != 0) {
         p->poisoned = true;
         return fail(HALO_ERR_TIMEOUT, "halo_plan_sync: an in-kernel dependency wait timed out");
     }
@@ -976,6 +1062,7 @@ halo_status halo_plan_reset(halo_plan *p)
     hipError_t e;
     if ((e = hipDeviceSynchronize()) != hipSuccess ||
         (e = hipMemset(p->d_state, 0, p->state_words * 4)) != hipSuccess ||
+        (p->d_lflags && (e = hipMemset(p->d_lflags, 0, p->lflag_words * 8)) != hipSuccess) ||
         (e = hipDeviceSynchronize()) != hipSuccess)
         return hip_fail(e, "halo_plan_reset");
     std::memset(p->h_err, 0, 64);
@@ -1007,9 +1094,12 @@ halo_status halo_plan_debug_stress(halo_plan *p, uint32_t seed)
     if (seed == 0) return HALO_OK;
     const halo::HostPlan &h = p->h;
     const int32_t ni = (int32_t)h.items.size(), nc = (int32_t)h.chunks.size();
+    const int32_t nl = (int32_t)h.lunits.size();
     // Work units that never wait on each other, in launch order: the items of
-    // one pulse; the chunks of one zone. Each such group runs reversed.
-    std::vector<int32_t> order((size_t)2 * ni + 2 * nc);
+    // one pulse; the chunks of one zone; the XCD-local units of one class and
+    // one pulse (reversed among the positions of their class, so that every
+    // unit stays on its XCD). Each such group runs reversed.
+    std::vector<int32_t> order((size_t)2 * ni + 2 * nc + 2 * nl);
     auto reverse_groups = [](int32_t *dst, const std::vector<int32_t> &seq,
                              const std::vector<int32_t> &key) {
         const int32_t n = (int32_t)seq.size();
@@ -1043,6 +1133,36 @@ halo_status halo_plan_debug_stress(halo_plan *p, uint32_t seed)
         key[b] = h.chunks[h.chunk_forder[b]].zone;
     }
     reverse_groups(order.data() + 2 * ni + nc, seq, key);
+    if (nl > 0) {
+        // class c holds positions c, c + 8, ...; its units in launch order
+        int32_t *ox = order.data() + 2 * ni + 2 * nc, *of = ox + nl;
+        for (int32_t b = 0; b < nl; ++b) {
+            ox[b] = b;
+            of[b] = nl - 1 - b;
+        }
+        const int32_t K = h.local_k;
+        for (int c = 0; c < halo::kXcdClasses; ++c) {
+            int32_t lo = 0;
+            while (lo < K) {
+                const halo::LocalUnit &u0 = h.lunits[(size_t)lo * halo::kXcdClasses + c];
+                if (u0.n_total == 0) break;  // the class's empty tail
+                const int32_t pulse = u0.seg / h.n_dom;
+                int32_t hi = lo;
+                while (hi < K) {
+                    const halo::LocalUnit &u = h.lunits[(size_t)hi * halo::kXcdClasses + c];
+                    if (u.n_total == 0 || u.seg / h.n_dom != pulse) break;
+                    ++hi;
+                }
+                for (int32_t k = lo; k < hi; ++k) {
+                    const int32_t pos = k * halo::kXcdClasses + c;
+                    const int32_t partner = (lo + hi - 1 - k) * halo::kXcdClasses + c;
+                    ox[pos] = partner;
+                    of[nl - 1 - pos] = partner;
+                }
+                lo = hi;
+            }
+        }
+    }
     hipError_t e = hipMalloc((void **)&p->d_stress, std::max<size_t>(order.size(), 1) * 4);
     if (e == hipSuccess && !order.empty())
         e = hipMemcpy(p->d_stress, order.data(), order.size() * 4, hipMemcpyHostToDevice);
@@ -1069,7 +1189,8 @@ halo_status halo_plan_debug_timing(halo_plan *p, int32_t enable)
         p->stamp_units = 0;
     }
     if (!enable) return HALO_OK;
-    const size_t units = std::max<size_t>({p->h.items.size(), p->h.chunks.size(), 1});
+    const size_t units =
+        std::max<size_t>({p->h.items.size(), p->h.chunks.size(), p->h.lunits.size(), 1});
     const size_t bytes = units * kStampWords * sizeof(uint64_t);
     hipError_t e = hipMalloc((void **)&p->d_stamps, bytes);
     if (e == hipSuccess) e = hipMemset(p->d_stamps, 0, bytes);

@@ -375,6 +375,7 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
     });
     make_items(P, item_entries);
     make_chunks(P, item_entries);
+    make_local_units(P, item_entries);
     make_launch_members(P);
     return kOk;
 }
@@ -390,9 +391,19 @@ void make_launch_members(HostPlan &P)
     };
     for (size_t u = 0; u < P.items.size(); ++u) {
         const WorkItem &it = P.items[u];
-        if (it.n_total > it.n_indep) add(kFamItemsX, u);
-        if (it.fwait[0] >= 0) add(kFamItemsF, u);
+        if (!P.has_local) {
+            if (it.n_total > it.n_indep) add(kFamItemsX, u);
+            if (it.fwait[0] >= 0) add(kFamItemsF, u);
+        }
         add(kFamAtomicF, u);
+    }
+    // The XCD-local index-list kernels take the same two families; a unit
+    // that waits, or that writes a flag another unit waits for, takes part
+    // (in a replayed graph it reads the count to learn the epoch).
+    for (size_t b = 0; b < P.lunits.size(); ++b) {
+        const LocalUnit &un = P.lunits[b];
+        if (un.wx_n > 0 || (un.flags & kLocalXWaited)) add(kFamItemsX, b);
+        if (un.wf_n > 0 || (un.flags & kLocalFWaited)) add(kFamItemsF, b);
     }
     if (!P.has_chunks) return;
     for (size_t u = 0; u < P.chunks.size(); ++u) {
@@ -561,6 +572,168 @@ void make_items(HostPlan &P, int32_t item_entries, bool with_masks)
         }
     }
     P.pulse_item_off[P.n_pulse] = (int32_t)P.items.size();
+}
+
+// XCD-local units. A unit is a run of consecutive entries of one indexMap
+// (pulse p, sender D) whose source slots lie in one zone of D (its home
+// slots or the region it received in one pulse) and hold atoms of one home
+// domain, the run's origin; runs longer than unit_entries are cut into
+// near-equal pieces. All images of an atom in one domain arrive by the same
+// path, so each origin occupies one contiguous stretch of one zone.
+//
+// Dependencies, all among units of one origin:
+//  - coordinates (Algorithm 4): a unit reading region q of D waits for the
+//    units of segment (q, sender to D) that wrote the stretch it reads;
+//  - forces (Algorithm 6, pulses in reverse): a unit of pulse p adds its
+//    receiver's region slots onto its source slots, so it waits for every
+//    unit of a later pulse that adds into those region slots (they must be
+//    final) or into its own source slots (their adds come first).
+// Placement: the units of origin o form class o mod kXcdClasses; a class
+// lists its units pulse by pulse (roots, which read home slots, before the
+// others; in the last pulse the others first, as the index-list items),
+// and the k-th unit of class c sits at position 8k + c. Unused positions
+// hold empty units. A unit then waits only for units of its own class at
+// smaller positions (coordinates) or larger positions (forces, launched in
+// reverse).
+void make_local_units(HostPlan &P, int32_t unit_entries)
+{
+    P.has_local = false;
+    P.local_k = 0;
+    P.lunits.clear();
+    P.lwaits.clear();
+    if (P.n_pulse == 0 || P.n_entries == 0 || P.total_slots == 0) return;
+    const int32_t nd = P.n_dom, np = P.n_pulse;
+    unit_entries = std::max<int32_t>(unit_entries, 1);
+
+    // origin of every slot, pulse by pulse
+    std::vector<int32_t> origin((size_t)P.total_slots, -1);
+    for (int32_t D = 0; D < nd; ++D)
+        for (int32_t l = 0; l < P.n_home[D]; ++l) origin[(size_t)(P.base[D] + l)] = D;
+    for (int32_t p = 0; p < np; ++p)
+        for (int32_t D = 0; D < nd; ++D) {
+            const Segment &g = P.at(p, D);
+            const int64_t dst = P.base[g.send_to] + P.at(p, g.send_to).atom_offset;
+            for (int32_t i = 0; i < g.send_size; ++i)
+                origin[(size_t)(dst + i)] = origin[(size_t)P.abs_map[(size_t)g.map_off + i]];
+        }
+
+    struct Raw {
+        int32_t pulse, sender, e0, n, zone, origin;
+        int32_t src_lo, src_hi;  // absolute slots of the first and last source
+    };
+    std::vector<Raw> raw;
+    auto zone_of = [&](int32_t D, int32_t l) {
+        if (l < P.n_home[D]) return -1;
+        for (int32_t q = 0; q < np; ++q) {
+            const Segment &r = P.at(q, D);
+            if (l >= r.atom_offset && l < r.atom_offset + r.recv_size) return q;
+        }
+        return np;  // not reached: every local slot is home or in a region
+    };
+    for (int32_t p = 0; p < np; ++p)
+        for (int32_t D = 0; D < nd; ++D) {
+            const Segment &g = P.at(p, D);
+            int32_t i = 0;
+            while (i < g.send_size) {
+                const int32_t l0 = P.local_map[(size_t)g.map_off + i];
+                const int32_t z = zone_of(D, l0);
+                const int32_t o = origin[(size_t)(P.base[D] + l0)];
+                int32_t j = i + 1;
+                while (j < g.send_size) {
+                    const int32_t l = P.local_map[(size_t)g.map_off + j];
+                    if (origin[(size_t)(P.base[D] + l)] != o || zone_of(D, l) != z) break;
+                    ++j;
+                }
+                const int32_t len = j - i, pieces = (len + unit_entries - 1) / unit_entries;
+                for (int32_t k = 0; k < pieces; ++k) {
+                    const int32_t a = i + (int32_t)((int64_t)len * k / pieces);
+                    const int32_t b = i + (int32_t)((int64_t)len * (k + 1) / pieces);
+                    raw.push_back(Raw{p, D, a, b - a, z, o,
+                                      P.abs_map[(size_t)g.map_off + a],
+                                      P.abs_map[(size_t)g.map_off + b - 1]});
+                }
+                i = j;
+            }
+        }
+
+    // classes and positions
+    std::vector<std::vector<int32_t>> cls(kXcdClasses);
+    for (int32_t p = 0; p < np; ++p) {
+        const bool last = p + 1 == np;
+        for (int pass = 0; pass < 2; ++pass) {
+            const bool roots = (pass == 0) != last;
+            for (int32_t r = 0; r < (int32_t)raw.size(); ++r)
+                if (raw[r].pulse == p && (raw[r].zone < 0) == roots)
+                    cls[raw[r].origin % kXcdClasses].push_back(r);
+        }
+    }
+    size_t k_max = 0;
+    for (const auto &c : cls) k_max = std::max(k_max, c.size());
+    P.local_k = (int32_t)k_max;
+    P.lunits.assign(k_max * kXcdClasses, LocalUnit{});
+    std::vector<int32_t> pos_of(raw.size(), -1);
+    for (int c = 0; c < kXcdClasses; ++c)
+        for (size_t k = 0; k < cls[c].size(); ++k)
+            pos_of[(size_t)cls[c][k]] = (int32_t)(k * kXcdClasses + (size_t)c);
+
+    // units by sending domain, for the wait lists
+    std::vector<std::vector<int32_t>> by_sender(nd);
+    for (int32_t r = 0; r < (int32_t)raw.size(); ++r) by_sender[raw[r].sender].push_back(r);
+
+    std::vector<std::vector<int32_t>> wx(raw.size()), wf(raw.size());
+    for (int32_t r = 0; r < (int32_t)raw.size(); ++r) {
+        const Raw &u = raw[r];
+        const Segment &g = P.at(u.pulse, u.sender);
+        // coordinates: the writers of the stretch of region `zone` it reads
+        if (u.zone >= 0) {
+            const int32_t q = u.zone, Dq = P.recv_from[(size_t)q * nd + u.sender];
+            const int64_t r0 = P.base[u.sender] + P.at(q, u.sender).atom_offset;
+            const int64_t i_lo = u.src_lo - r0, i_hi = u.src_hi - r0;
+            for (int32_t v : by_sender[Dq]) {
+                const Raw &w = raw[v];
+                if (w.pulse == q && w.e0 <= i_hi && w.e0 + w.n - 1 >= i_lo) wx[r].push_back(v);
+            }
+        }
+        // forces: later units adding into the region slots it reads or into
+        // its own source slots
+        const int64_t reg_lo = P.base[g.send_to] + P.at(u.pulse, g.send_to).atom_offset + u.e0;
+        const int64_t reg_hi = reg_lo + u.n - 1;
+        for (int32_t v : by_sender[g.send_to]) {
+            const Raw &w = raw[v];
+            if (w.pulse > u.pulse && w.src_lo <= reg_hi && w.src_hi >= reg_lo) wf[r].push_back(v);
+        }
+        for (int32_t v : by_sender[u.sender]) {
+            const Raw &w = raw[v];
+            if (w.pulse > u.pulse && w.src_lo <= u.src_hi && w.src_hi >= u.src_lo &&
+                (g.send_to != u.sender || std::find(wf[r].begin(), wf[r].end(), v) == wf[r].end()))
+                wf[r].push_back(v);
+        }
+    }
+
+    for (int32_t r = 0; r < (int32_t)raw.size(); ++r) {
+        const Raw &u = raw[r];
+        const Segment &g = P.at(u.pulse, u.sender);
+        LocalUnit &L = P.lunits[(size_t)pos_of[r]];
+        L.map_begin = (int32_t)(g.map_off + u.e0);
+        L.n_total = u.n;
+        L.region_begin = (int32_t)(P.base[g.send_to] + P.at(u.pulse, g.send_to).atom_offset + u.e0);
+        L.seg = u.pulse * nd + u.sender;
+        for (int c = 0; c < 3; ++c) L.shift[c] = g.shift[c];
+        L.origin = u.origin;
+        L.wx_off = (int32_t)P.lwaits.size();
+        L.wx_n = (int32_t)wx[r].size();
+        for (int32_t v : wx[r]) {
+            P.lwaits.push_back(pos_of[(size_t)v]);
+            P.lunits[(size_t)pos_of[(size_t)v]].flags |= kLocalXWaited;
+        }
+        L.wf_off = (int32_t)P.lwaits.size();
+        L.wf_n = (int32_t)wf[r].size();
+        for (int32_t v : wf[r]) {
+            P.lwaits.push_back(pos_of[(size_t)v]);
+            P.lunits[(size_t)pos_of[(size_t)v]].flags |= kLocalFWaited;
+        }
+    }
+    P.has_local = true;
 }
 
 bool plan_has_chunks(const HostPlan &P)

@@ -62,6 +62,42 @@ struct alignas(16) Chunk {
 };
 static_assert(sizeof(Chunk) == 64, "Chunk layout");
 
+// XCD-local units of the index-list kernels (plans built on the host). The
+// entries of every indexMap are cut into runs whose atoms share one home
+// domain (their "origin"); a run reads either home slots or a stretch of one
+// region written by the runs of the same origin in earlier pulses. Every
+// dependency of both exchanges therefore stays among the runs of one origin,
+// and the units of an origin all run on one XCD: unit position b (the
+// workgroup index of the coordinate kernel) belongs to class b mod
+// kXcdClasses, and a grid's workgroups go to the XCDs round-robin. Data that
+// one unit writes and another reads then stays in that XCD's L2: written
+// with plain stores, read past the CU cache, and signalled by a per-unit flag
+// word instead of a device-wide counter.
+constexpr int kXcdClasses = 8;
+
+struct alignas(16) LocalUnit {
+    int32_t map_begin;     // first entry (index into the concatenated indexMap)
+    int32_t n_total;       // entries (0: an empty position)
+    int32_t region_begin;  // receiver-region slot of the first entry
+    int32_t seg;           // pulse * n_domains + sending domain
+    float shift[3];        // coordShift of the segment
+    int32_t origin;        // home domain of the run's atoms
+    int32_t wx_off, wx_n;  // coordinates: the units (positions) whose stores it reads
+    int32_t wf_off, wf_n;  // forces: the units (positions) that must add before it
+    int32_t flags;         // kLocal* bits
+    int32_t pad[3];
+};
+static_assert(sizeof(LocalUnit) == 64, "LocalUnit layout");
+
+// Flag words per class of the XCD-local kernels: positions per class rounded
+// up to whole 128-byte lines of 8-byte flags.
+inline int32_t local_flag_stride(int32_t local_k) { return (local_k + 15) / 16 * 16 + 16; }
+
+enum : int32_t {
+    kLocalXWaited = 1,  // coordinates: a later unit reads what this one stores
+    kLocalFWaited = 2,  // forces: a unit waits until this one has added
+};
+
 struct Segment {
     int32_t send_to = 0;
     int32_t send_size = 0;
@@ -116,6 +152,11 @@ struct HostPlan {
     std::vector<float> shift4;             // [p][D][4]: coordShift of (p, D)
     std::vector<uint32_t> x_arrivals;      // [p][D]: chunks of D that send in pulse p
     std::vector<uint32_t> zone_chunks;     // [r][D]: chunks in region zone r of D
+    // XCD-local units of the index-list kernels (host-built plans only)
+    bool has_local = false;
+    int32_t local_k = 0;                   // positions per class
+    std::vector<LocalUnit> lunits;         // [kXcdClasses * local_k]; position b: class b % 8
+    std::vector<int32_t> lwaits;           // wait lists (positions)
     // launch counts: members of each group of each kernel family
     std::vector<uint32_t> launch_members;  // [family][kLaunchGroups]
 
@@ -160,6 +201,10 @@ void make_launch_members(HostPlan &plan);
 
 // Whether make_items places the items of one domain on one XCD.
 bool xcd_ordering_enabled();
+
+// Build the XCD-local units (runs of one origin, at most unit_entries
+// entries each), their placement and their wait lists.
+void make_local_units(HostPlan &plan, int32_t unit_entries);
 
 // Build the transposed form (masks and chunks of at most chunk_slots slots).
 void make_chunks(HostPlan &plan, int32_t chunk_slots);

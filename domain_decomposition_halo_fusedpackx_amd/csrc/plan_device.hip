@@ -712,6 +712,12 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     HostPlan &P = pl->h;
     int rc = plan_geometry(n_atoms, box, grid, cutoff, selection, P, msg);
     if (rc != kOk) return rc;
+    // a device-built plan runs the index-list kernels with segment counters
+    // (no XCD-local units)
+    P.has_local = false;
+    P.local_k = 0;
+    P.lunits.clear();
+    P.lwaits.clear();
     if (P.n_dom > kMaxDeviceDomains) {
         msg = "halo_plan_create_device: at most " + std::to_string(kMaxDeviceDomains) +
               " domains (use halo_plan_create)";

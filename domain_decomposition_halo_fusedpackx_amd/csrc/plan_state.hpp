@@ -77,6 +77,12 @@ struct halo_plan {
     // testing: stress mode (seed 0 = off) and its launch orders
     uint32_t stress_seed = 0;
     int32_t *d_stress = nullptr;
+    // XCD-local index-list kernels: units, wait lists, and per-unit flags
+    // (coordinates, then forces; 8 bytes each, class-major)
+    halo::LocalUnit *d_lunits = nullptr;
+    int32_t *d_lwaits = nullptr;
+    uint64_t *d_lflags = nullptr;
+    size_t lflag_words = 0;
     // tuning: per-unit clock stamps of the fused kernels (nullptr = off)
     uint64_t *d_stamps = nullptr;
     size_t stamp_units = 0;

@@ -50,6 +50,11 @@ namespace halo {
 
 constexpr int kCounterStride = 32;  // uint32 words: one 128-byte line per counter
 
+// Values of the plan's error word (0: no error): a dependency wait exceeded
+// its spin limit; a flag came from another XCD than the waiting unit's.
+constexpr uint32_t kErrWordTimeout = 1;
+constexpr uint32_t kErrWordPlacement = 2;
+
 // Device state of a plan with n_seg segments, in uint32 words: segment
 // counters of the work-item kernels (X, then F), of the chunk kernels (X,
 // then F), of the atomic force kernel (F only), the launch counts of the
@@ -195,7 +200,7 @@ __device__ __forceinline__ void wait_segments(const int32_t *list, int32_t n, co
                 if (__all(ok)) break;
                 if (++polls > spin_limit) {
                     if (lane == 0)
-                        __hip_atomic_store(err_word, 1u, __ATOMIC_RELAXED,
+                        __hip_atomic_store(err_word, kErrWordTimeout, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_SYSTEM);
                     break;
                 }
@@ -223,7 +228,8 @@ __device__ __forceinline__ void wait_one(int32_t s, const uint32_t *seg_items, u
         uint32_t polls = 0;
         while ((int32_t)(c - target) < 0) {
             if (++polls > spin_limit) {
-                __hip_atomic_store(err_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                __hip_atomic_store(err_word, kErrWordTimeout, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -253,7 +259,8 @@ __device__ __forceinline__ void wait_lanes(uint32_t *ctr, uint32_t mult, const L
             if (__all(ok)) break;
             if (++polls > spin_limit) {
                 if (threadIdx.x == 0)
-                    __hip_atomic_store(err_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    __hip_atomic_store(err_word, kErrWordTimeout, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -263,6 +270,98 @@ __device__ __forceinline__ void wait_lanes(uint32_t *ctr, uint32_t mult, const L
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
     __syncthreads();
+}
+
+// ---- XCD-local flags (the index-list kernels on plans built on the host) ----
+// The units of one origin run on one XCD (plan.hpp, LocalUnit), so a unit's
+// stores reach the consumer through that XCD's L2: the producer writes its
+// data with plain stores, waits for them (s_waitcnt vmcnt(0): the L2 has
+// acknowledged them), meets its workgroup at a barrier and then stores its
+// flag word, also plainly: {epoch, 0x100 | its XCC}. The consumer polls the
+// flag words with loads that bypass the CU cache and are served by the L2
+// (agent-scope relaxed loads), waits for them (s_waitcnt), meets at a
+// barrier, and reads the data with the same kind of load. A flag from
+// another XCD (the grid's workgroups did not go to the XCDs round-robin)
+// would not be seen there in time, or, if seen, is reported: the error word
+// becomes kErrWordPlacement.
+__device__ __forceinline__ uint32_t xcc_id()
+{
+    return (uint32_t)__builtin_amdgcn_s_getreg(20 | (31 << 11)) & 0xfu;  // HW_REG_XCC_ID
+}
+
+// Flag word of unit position b: class-major, kp words per class (a multiple
+// of 16, so that no 128-byte line holds flags of two classes).
+__device__ __forceinline__ uint64_t *local_flag(uint64_t *flags, int32_t kp, int32_t b)
+{
+    return flags + (size_t)(b % kXcdClasses) * (size_t)kp + (size_t)(b / kXcdClasses);
+}
+
+// Wave 0 polls the flags of the listed unit positions (lane i the i-th)
+// until every one shows this epoch; the workgroup then meets at a barrier.
+// The epoch, if not known yet (0), is inferred with the first poll.
+__device__ __forceinline__ void wait_flags(const int32_t *list, int32_t n, uint64_t *flags,
+                                           int32_t kp, const LaunchGroup &lg, uint32_t &epoch,
+                                           uint32_t spin_limit, uint32_t *err_word)
+{
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const uint32_t mine_xcc = xcc_id() | 0x100u;
+        for (int32_t base = 0; base < n; base += 64) {
+            const bool mine = base + lane < n;
+            uint64_t *fp = mine ? local_flag(flags, kp, list[base + lane]) : nullptr;
+            const EpochRead er = start_epoch(lg, epoch);
+            uint64_t f = mine ? __hip_atomic_load(fp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : 0u;
+            finish_epoch(er, epoch);
+            uint32_t polls = 0;
+            while (true) {
+                const bool ok = !mine || (int32_t)((uint32_t)f - epoch) >= 0;
+                if (__all(ok)) break;
+                if (++polls > spin_limit) {
+                    if (lane == 0)
+                        __hip_atomic_store(err_word, kErrWordTimeout, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_SYSTEM);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                if (mine) f = __hip_atomic_load(fp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            // a flag of this epoch written on another XCD (a flag never
+            // written, after a timeout, is not a placement error)
+            const bool seen = mine && (int32_t)((uint32_t)f - epoch) >= 0;
+            if (__any(seen && (uint32_t)(f >> 32) != mine_xcc) && lane == 0)
+                __hip_atomic_store(err_word, kErrWordPlacement, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+        wait_vmem();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+    __syncthreads();
+}
+
+// The unit's stores are complete in every wave (they reached the XCD's L2),
+// the workgroup meets at a barrier, and thread 0 stores the flag word
+// (plain store: it stays in the L2, where the consumers on this XCD poll).
+__device__ __forceinline__ void set_local_flag(uint64_t *flags, int32_t kp, int32_t b,
+                                               uint32_t epoch, bool withhold)
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0 && !withhold)
+        __hip_atomic_store(local_flag(flags, kp, b),
+                           (uint64_t)epoch | ((uint64_t)(xcc_id() | 0x100u) << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
+
+// The epoch of a unit that writes a flag without waiting first, in a launch
+// that was not handed its epoch (thread 0, which stores the flag).
+__device__ __forceinline__ void learn_epoch(const LaunchGroup &lg, uint32_t &epoch)
+{
+    if (threadIdx.x == 0 && epoch == 0) {
+        const EpochRead er = start_epoch(lg, epoch);
+        finish_epoch(er, epoch);
+    }
 }
 
 // One poll, without waiting, of two counters (lanes 0 and 1 of wave 0):

@@ -63,7 +63,10 @@ typedef enum {
     HALO_ERR_HIP = -4,      /* a HIP runtime call failed                          */
     HALO_ERR_TIMEOUT = -5,  /* an in-kernel dependency wait exceeded its limit    */
     HALO_ERR_STATE = -6,    /* plan poisoned by an earlier timeout                */
-    HALO_ERR_NOMEM = -7     /* host allocation failed                             */
+    HALO_ERR_NOMEM = -7,    /* host allocation failed                             */
+    HALO_ERR_PLACEMENT = -8 /* a work unit of the XCD-local index-list kernels ran
+                               on another XCD than the units it waits for; the
+                               exchange's results are not valid (plan poisoned)   */
 } halo_status;
 
 /* Build the exchange plan (the pages' PulseData per pulse and domain,
@@ -213,6 +216,21 @@ halo_status halo_plan_item_waits(const halo_plan *plan, int32_t item, int32_t *s
 int32_t halo_plan_num_chunks(const halo_plan *plan);  /* -1 on NULL */
 halo_status halo_plan_chunk(const halo_plan *plan, int32_t chunk, int32_t *domain, int32_t *zone,
                             int64_t *first, int32_t *count, uint32_t *mask);
+
+/* XCD-local units of the index-list kernels (plans built by
+ * halo_plan_create; 0 for plans built on the device, whose index-list
+ * kernels use the work items above). A unit is a run of one indexMap whose
+ * atoms share one home domain (their origin); it sits at a position of the
+ * coordinate kernel's grid whose index mod 8 is its origin mod 8, so that all
+ * units of an origin, and with them every dependency of both exchanges, run
+ * on one XCD. Unit `position`: its segment (pulse * num_domains + sending
+ * domain; -1 for an empty position), origin (-1 if empty), entries, and the
+ * number of units it waits for in the coordinate and in the force exchange.
+ * Outputs may be NULL. A read-out for tests and tools. */
+int32_t halo_plan_num_local_units(const halo_plan *plan);  /* -1 on NULL */
+halo_status halo_plan_local_unit(const halo_plan *plan, int32_t position, int32_t *segment,
+                                 int32_t *origin, int32_t *entries, int32_t *x_waits,
+                                 int32_t *f_waits);
 
 /* Allocate and upload the device metadata on the current HIP device (blocking:
  * it synchronises the device). The first exchange on a plan built by

@@ -27,6 +27,109 @@ int oracle_exchange_f(const oracle *o, float *f);
 
 namespace {
 
+// The XCD-local units of a host plan (plan.hpp, LocalUnit), checked against
+// the plan's indexMaps entry by entry: every entry is in exactly one unit;
+// a unit's atoms share one origin, whose class is the unit's position mod 8;
+// every coordinate dependency (an entry reads a slot another entry wrote)
+// and every force dependency (a later pulse adds into a slot the unit reads
+// or adds into) is on the unit's wait list, on its own class, at a smaller
+// (coordinates) or larger (forces) position; the flag bits mark exactly the
+// units on some list. Returns the number of violations.
+int check_local_units(const halo::HostPlan &P, int32_t unit_entries)
+{
+    if (!P.has_local) return P.n_entries > 0 && P.n_pulse > 0;
+    int bad = 0;
+    const int32_t nd = P.n_dom;
+    const size_t nl = P.lunits.size();
+    if (nl != (size_t)P.local_k * halo::kXcdClasses) return 1;
+    // entry -> position
+    std::vector<int32_t> unit_of((size_t)P.n_entries, -1);
+    for (size_t b = 0; b < nl; ++b) {
+        const halo::LocalUnit &u = P.lunits[b];
+        if (u.n_total == 0) continue;
+        if (u.n_total > unit_entries) ++bad;
+        for (int32_t e = 0; e < u.n_total; ++e) {
+            int32_t &o = unit_of[(size_t)u.map_begin + e];
+            if (o != -1) ++bad;
+            o = (int32_t)b;
+        }
+    }
+    for (int32_t o : unit_of) bad += o < 0;
+    // writer entry of every halo slot, and origins (recomputed here)
+    std::vector<int64_t> writer((size_t)P.total_slots, -1);
+    std::vector<int32_t> origin((size_t)P.total_slots, -1);
+    for (int32_t D = 0; D < nd; ++D)
+        for (int32_t l = 0; l < P.n_home[D]; ++l) origin[(size_t)(P.base[D] + l)] = D;
+    for (int32_t p = 0; p < P.n_pulse; ++p)
+        for (int32_t D = 0; D < nd; ++D) {
+            const halo::Segment &g = P.at(p, D);
+            const int64_t dst = P.base[g.send_to] + P.at(p, g.send_to).atom_offset;
+            for (int32_t i = 0; i < g.send_size; ++i) {
+                writer[(size_t)(dst + i)] = g.map_off + i;
+                origin[(size_t)(dst + i)] = origin[(size_t)P.abs_map[(size_t)g.map_off + i]];
+            }
+        }
+    auto on_list = [&](int32_t off, int32_t n, int32_t pos) {
+        for (int32_t i = 0; i < n; ++i)
+            if (P.lwaits[(size_t)off + i] == pos) return true;
+        return false;
+    };
+    std::vector<char> xw(nl, 0), fw(nl, 0);
+    for (size_t b = 0; b < nl; ++b) {
+        const halo::LocalUnit &u = P.lunits[b];
+        for (int32_t i = 0; i < u.wx_n; ++i) {
+            const int32_t v = P.lwaits[(size_t)u.wx_off + i];
+            xw[(size_t)v] = 1;
+            bad += v >= (int32_t)b || v % 8 != (int32_t)b % 8;
+        }
+        for (int32_t i = 0; i < u.wf_n; ++i) {
+            const int32_t v = P.lwaits[(size_t)u.wf_off + i];
+            fw[(size_t)v] = 1;
+            bad += v <= (int32_t)b || v % 8 != (int32_t)b % 8;
+        }
+    }
+    for (size_t b = 0; b < nl; ++b) {
+        const halo::LocalUnit &u = P.lunits[b];
+        bad += ((u.flags & halo::kLocalXWaited) != 0) != (xw[b] != 0);
+        bad += ((u.flags & halo::kLocalFWaited) != 0) != (fw[b] != 0);
+    }
+    // per entry: origin class, coordinate writer on the wait list
+    std::vector<std::vector<int64_t>> readers((size_t)P.total_slots);
+    std::vector<int32_t> pulse_of((size_t)P.n_entries);
+    for (int32_t p = 0; p < P.n_pulse; ++p)
+        for (int32_t D = 0; D < nd; ++D) {
+            const halo::Segment &g = P.at(p, D);
+            for (int32_t i = 0; i < g.send_size; ++i) pulse_of[(size_t)g.map_off + i] = p;
+        }
+    for (int64_t e = 0; e < P.n_entries; ++e) {
+        const int32_t b = unit_of[(size_t)e];
+        const halo::LocalUnit &u = P.lunits[(size_t)b];
+        const int32_t src = P.abs_map[(size_t)e];
+        bad += origin[(size_t)src] != u.origin || u.origin % 8 != b % 8;
+        readers[(size_t)src].push_back(e);
+        if (writer[(size_t)src] >= 0 &&
+            !on_list(u.wx_off, u.wx_n, unit_of[(size_t)writer[(size_t)src]]))
+            ++bad;
+    }
+    // forces: every later-pulse reader of the entry's source slot or of the
+    // region slot it fills
+    for (int32_t p = 0; p < P.n_pulse; ++p)
+        for (int32_t D = 0; D < nd; ++D) {
+            const halo::Segment &g = P.at(p, D);
+            const int64_t dst = P.base[g.send_to] + P.at(p, g.send_to).atom_offset;
+            for (int32_t i = 0; i < g.send_size; ++i) {
+                const int64_t e = g.map_off + i;
+                const halo::LocalUnit &u = P.lunits[(size_t)unit_of[(size_t)e]];
+                for (int64_t slot : {(int64_t)P.abs_map[(size_t)e], dst + i})
+                    for (int64_t r : readers[(size_t)slot])
+                        if (pulse_of[(size_t)r] > p &&
+                            !on_list(u.wf_off, u.wf_n, unit_of[(size_t)r]))
+                            ++bad;
+            }
+        }
+    return bad;
+}
+
 // splitmix64: reproducible positions without any library generator
 uint64_t next(uint64_t &s)
 {
@@ -57,6 +160,13 @@ int run(const Case &c, uint64_t seed, int32_t selection)
     halo::HostPlan P;
     std::string msg;
     int rc = halo::build_plan(pos.data(), c.n, c.box, c.grid, c.cutoff, selection, 64, P, msg);
+    if (rc == 0) {
+        const int lb = check_local_units(P, 64);
+        if (lb) {
+            std::printf("XCD-local units: %d violation(s)\n", lb);
+            return 1;
+        }
+    }
     oracle *o = nullptr;
     int orc = oracle_build_ex(pos.data(), c.n, c.box, c.grid, c.cutoff, selection, &o);
     if (rc != orc) {

@@ -40,6 +40,8 @@ def test_timing_records_and_results(torch, oracle_mod, wid):
         f0[base[d]:base[d] + n_home[d]] = 0
     want_f = o.exchange_f(f0.copy())
     n_items, n_chunks = plan.num_items, len(plan.chunks())
+    lunits = plan.local_units()
+    assert len(lunits) > 0  # a host-built plan runs the index-list form on XCD-local units
     for d, name in FORMS:
         buf = torch.from_numpy((x0 if d == "x" else f0).copy()).cuda()
         getattr(plan, name)(buf)
@@ -48,8 +50,13 @@ def test_timing_records_and_results(torch, oracle_mod, wid):
         assert_bitwise(buf.cpu().numpy(), want_x if d == "x" else want_f, name)
         st, khz = plan.debug_timing_read()
         assert khz > 0
-        n = n_chunks if "transposed" in name else n_items
+        n = (n_chunks if "transposed" in name else len(lunits) if "indexmap" in name
+             else n_items)
         st = st[:n]
+        # the workgroups of a launch go to the XCDs round-robin (starting at
+        # whichever XCD is next): workgroup b on XCD (b + r) mod 8 for one r.
+        # The XCD-local units rely on workgroups b and b + 8 sharing an XCD.
+        assert len(np.unique((st[:, 7] - st[:, 5]) % 8)) == 1, name
         start, wb, we, sig, end = (st[:, k] for k in range(5))
         assert (start > 0).all() and (end >= start).all(), name
         waited = wb != 0
@@ -61,8 +68,14 @@ def test_timing_records_and_results(torch, oracle_mod, wid):
         assert sorted(st[:, 5].tolist()) == list(range(n)), name
         assert ((st[:, 7] >= 0) & (st[:, 7] < 8)).all(), name
         if name == "exchange_x_indexmap":
-            # an item waits exactly when its dependent entries read a region
-            np.testing.assert_array_equal(waited, plan.item_waits()[:, 1] != 0)
+            # a unit waits exactly when it reads a region
+            np.testing.assert_array_equal(waited, lunits[:, 3] > 0)
+        if name == "exchange_f_indexmap":
+            np.testing.assert_array_equal(waited, lunits[:, 4] > 0)
+        if "indexmap" in name:
+            # units of one origin on one XCD
+            for og in np.unique(lunits[:, 1][lunits[:, 2] > 0]):
+                assert len(np.unique(st[:, 7][lunits[:, 1] == og])) == 1
         if name == "exchange_x_direct":
             assert not waited.any()
     plan.debug_timing(False)
