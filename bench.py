@@ -31,7 +31,7 @@ METRIC = "halo atoms/s and HBM GB/s (% of peak); µs per coord+force exchange"
 # The library's rule for the default exchanges (halo_exchange_x / _f in
 # csrc/halo_api.hip): the transposed kernels from these sizes on.
 TRANSPOSED_X_MIN_ENTRIES = 1 << 20
-TRANSPOSED_F_MIN_ENTRIES = 1 << 14
+TRANSPOSED_F_MIN_ENTRIES = 1 << 18
 TRANSPOSED_F_MAX_PULSES = 3
 HBM_PEAK_GBS = 8000.0
 BYTES_X = 28  # per entry: 4 B index + 12 B gathered source + 12 B store
@@ -121,6 +121,15 @@ def _cpu_model() -> str:
     except OSError:
         pass
     return platform.processor() or platform.machine()
+
+
+def replica_count(slots, entries):
+    """Copies of plan, x and f the timed loops rotate over: enough to exceed
+    twice the 256 MB Infinity Cache, so that every exchange streams its data
+    from HBM; at most MAX_REPLICAS (the two smallest workloads then stay in
+    the cache)."""
+    per_rep_bytes = slots * 12 + entries * 4
+    return min(MAX_REPLICAS, max(1, -(-2 * MALL_BYTES // per_rep_bytes)))
 
 
 def time_loop(torch, fn, n):
@@ -361,7 +370,7 @@ def overlap(torch, plan, x, f, reps):
 STAGE_FIELDS = ("start", "wait_begin", "wait_end", "signal", "end")
 
 
-def stage_profile(torch, HaloPlan, W, w, pos, launches, reps):
+def stage_profile(torch, HaloPlan, W, w, pos, launches, reps, replicas=1):
     """Where the time of one exchange goes, per kernel: every work unit's
     clock stamps (halo_plan_debug_timing) from the last of `launches`
     back-to-back launches, grouped by stage of the forwarding chain (pulse and
@@ -369,13 +378,19 @@ def stage_profile(torch, HaloPlan, W, w, pos, launches, reps):
     transposed form). Per group: median and latest time, in us from the first
     unit's start, of the units' start, first wait begin, last wait end, first
     completion signal and end; medians over `reps` repetitions. The kernel's
-    duration per launch from HIP events over the same loop is given with it."""
-    plan = HaloPlan(pos, w.box, w.grid, w.cutoff)
-    plan.upload()
-    x = torch.from_numpy(plan.home_filled(pos, 0.0)).cuda()
+    duration per launch from HIP events over the same loop is given with it.
+    With replicas > 1 the launches rotate over that many copies of plan and
+    buffers (as the bench's timed loops do), so that their data come from
+    HBM rather than from the caches."""
+    plans = [HaloPlan(pos, w.box, w.grid, w.cutoff) for _ in range(replicas)]
+    plan = plans[0]
+    for p in plans:
+        p.upload()
+        p.debug_timing(True)
+    xs = [torch.from_numpy(plan.home_filled(pos, 0.0)).cuda() for _ in range(replicas)]
     base, n_home, n_halo = plan.domains()
-    f = torch.from_numpy(W.halo_forces(plan.total_slots, base, n_home, n_halo, w.seed)).cuda()
-    plan.debug_timing(True)
+    f0 = W.halo_forces(plan.total_slots, base, n_home, n_halo, w.seed)
+    fs = [torch.from_numpy(f0).cuda() for _ in range(replicas)]
     waits = plan.item_waits()
     pulse_of_item = waits[:, 0] // plan.num_domains
     chunks = plan.chunks()
@@ -384,17 +399,21 @@ def stage_profile(torch, HaloPlan, W, w, pos, launches, reps):
     runs = [("x", "indexmap"), ("x", "transposed"), ("x", "direct"), ("f", "indexmap"),
             ("f", "transposed")]
     out = {"workload": w.describe(), "halo_entries": plan.num_entries,
-           "items": plan.num_items, "chunks": len(chunks), "launches": launches, "reps": reps}
+           "items": plan.num_items, "chunks": len(chunks), "local_units": len(lunits),
+           "launches": launches, "reps": reps, "replicas": replicas}
     for d, form in runs:
         if form == "transposed" and len(chunks) == 0:
             continue
-        fn = getattr(plan, f"exchange_{d}_{form}")
-        buf = x if d == "x" else f
-        fn(buf)  # first call (origin map) untimed
+        name = f"exchange_{d}_{form}"
+        bufs = xs if d == "x" else fs
+        for r in range(replicas):
+            getattr(plans[r], name)(bufs[r])  # first calls (origin maps) untimed
         per_rep, ev_us = [], []
         for _ in range(reps):
-            ev_us.append(time_loop(torch, lambda i: fn(buf), launches) * 1e3)
-            st, khz = plan.debug_timing_read()
+            ev_us.append(time_loop(
+                torch, lambda i: getattr(plans[i % replicas], name)(bufs[i % replicas]),
+                launches) * 1e3)
+            st, khz = plans[(launches - 1) % replicas].debug_timing_read()
             tick_us = 1e3 / khz
             local = form == "indexmap" and len(lunits) > 0
             n_units = (len(chunks) if form == "transposed" else
@@ -452,8 +471,9 @@ def stage_profile(torch, HaloPlan, W, w, pos, launches, reps):
             cols = "  ".join(f"{fld} {g[fld][0]:6.2f}/{g[fld][1]:6.2f}" for fld in STAGE_FIELDS
                              if fld in g)
             log(f"   {k:22s} n={g['units']:5d}  {cols}")
-    plan.sync()
-    plan.close()
+    for p in plans:
+        p.sync()
+        p.close()
     return out
 
 
@@ -483,6 +503,9 @@ def main():
     ap.add_argument("--stages", action="store_true",
                     help="only the per-stage clock profile of every fused kernel on --config "
                          "(halo_plan_debug_timing; medians over 5 repetitions of 20 launches)")
+    ap.add_argument("--stage-replicas", type=int, default=1,
+                    help="copies of plan and buffers the --stages launches rotate over "
+                         "(1: data stay in the caches; 0: as many as the timed loops use)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device 3 times (a plain copy kernel of "
                          "known size, for scaling hardware byte counters)")
@@ -514,17 +537,19 @@ def main():
     pos = W.workload_positions(w)
     log(f"workload {w.describe()}")
     if args.stages:
-        print(json.dumps({"stages": stage_profile(torch, HaloPlan, W, w, pos, 20, 5)}),
+        reps = args.stage_replicas
+        if reps == 0:
+            p0 = HaloPlan(pos, w.box, w.grid, w.cutoff)
+            reps = replica_count(p0.total_slots, p0.num_entries)
+            p0.close()
+        print(json.dumps({"stages": stage_profile(torch, HaloPlan, W, w, pos, 20, 5, reps)}),
               flush=True)
         return
 
     plan0 = HaloPlan(pos, w.box, w.grid, w.cutoff)
     E = plan0.num_entries
     S = plan0.total_slots
-    per_rep_bytes = S * 12 + E * 4
-    # Small workloads are capped at MAX_REPLICAS: their whole footprint then
-    # stays in the 256 MB cache, as it would in a real run.
-    R = args.replicas or min(MAX_REPLICAS, max(1, -(-2 * MALL_BYTES // per_rep_bytes)))
+    R = args.replicas or replica_count(S, E)
     log(f"entries={E} slots={S} items={plan0.num_items} replicas={R}")
     plans = [plan0] + [HaloPlan(pos, w.box, w.grid, w.cutoff) for _ in range(R - 1)]
     x_home = torch.from_numpy(plan0.home_filled(pos, 0.0)).cuda()
@@ -568,11 +593,14 @@ def main():
     dom = "f" if ms_f >= ms_x else "x"
     sha = kernel_source_sha()
     # the kernels the default exchanges run (halo_exchange_x / _f choose by size)
-    x_default = "push_x" if E >= TRANSPOSED_X_MIN_ENTRIES else "pack_fused"
+    # plans built on the host run the index-list form on XCD-local units
+    idx_x, idx_f = (("pack_local", "unpack_local") if len(plan0.local_units()) else
+                    ("pack_fused", "unpack_fused"))
+    x_default = "push_x" if E >= TRANSPOSED_X_MIN_ENTRIES else idx_x
     f_default = ("pull_f" if E >= TRANSPOSED_F_MIN_ENTRIES and
-                 plan0.num_pulses <= TRANSPOSED_F_MAX_PULSES else "unpack_fused")
+                 plan0.num_pulses <= TRANSPOSED_F_MAX_PULSES else idx_f)
     kernel_of = {("fused", "x"): x_default, ("fused", "f"): f_default,
-                 ("indexmap", "x"): "pack_fused", ("indexmap", "f"): "unpack_fused",
+                 ("indexmap", "x"): idx_x, ("indexmap", "f"): idx_f,
                  ("transposed", "x"): "push_x", ("transposed", "f"): "pull_f",
                  ("pulsewise", "x"): "pack_pulse", ("pulsewise", "f"): "unpack_pulse"}
     kname = kernel_of[(args.impl, dom)]

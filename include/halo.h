@@ -270,7 +270,7 @@ halo_status halo_exchange_x(halo_plan *plan, float *x, void *stream);
  * first; for every sender d of pulse p, f[indexMap[i]] += f[receiver's region
  * of pulse p][i], with the per-slot order of additions of the serial
  * reverse-pulse loop, so results are bitwise deterministic. Runs the
- * transposed form (halo_exchange_f_transposed) for plans of at least 2^14
+ * transposed form (halo_exchange_f_transposed) for plans of at least 2^18
  * indexMap entries and at most 3 pulses, the index-list form
  * (halo_exchange_f_indexmap) for the others.
  *   f : device, total_slots*3 float32, updated in place. On return home slots
@@ -278,11 +278,17 @@ halo_status halo_exchange_x(halo_plan *plan, float *x, void *stream);
  * Asynchronous; exchanges of one plan must be ordered on one stream. */
 halo_status halo_exchange_f(halo_plan *plan, float *f, void *stream);
 
-/* Index-list form of the fused exchanges: one work item (workgroup) per run
- * of an indexMap, in pulse-major order (reverse for forces); entries below
- * depOffset first, the rest after a wait on the (pulse, sender) counters of
- * the regions they read; forces added with one read-modify-write per entry,
- * an item waiting until pulse p+1 is finished for its sender and receiver. */
+/* Index-list form of the fused exchanges (Algorithms 3-6): one work unit
+ * (workgroup) per run of an indexMap, in pulse-major order (reverse for
+ * forces); entries below depOffset go at once, the others after a wait on
+ * the units that wrote the region stretch they read; forces added with one
+ * read-modify-write per entry, after every later pulse that adds into the
+ * same slots. On plans built by halo_plan_create the units are XCD-local
+ * (halo_plan_local_unit): runs of one origin, placed so that each forwarding
+ * stage stays in one XCD's L2, with per-unit flags; an exchange whose units
+ * find their producers on another XCD reports HALO_ERR_PLACEMENT from
+ * halo_plan_sync. On plans built on the device the units are the work items
+ * (halo_plan_item_waits) with per-(pulse, sender) counters. */
 halo_status halo_exchange_x_indexmap(halo_plan *plan, float *x, void *stream);
 halo_status halo_exchange_f_indexmap(halo_plan *plan, float *f, void *stream);
 
