@@ -63,6 +63,7 @@ SIGNATURES = {
     "halo_scatter_home": (_st, [_vp, _vp, _vp, _vp]),
     "halo_gather_home": (_st, [_vp, _vp, _vp, _vp]),
     "halo_exchange_f_staged": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_x_staged_noalloc": (_st, [_vp, _vp, _vp]),
     "halo_plan_sync": (_st, [_vp, _vp]),
     "halo_plan_reset": (_st, [_vp]),
     "halo_plan_set_spin_limit": (_st, [_vp, _u32]),
@@ -399,6 +400,9 @@ class HaloPlan:
 
     def exchange_f_staged(self, f, stream=None):
         self._call("halo_exchange_f_staged", f, stream)
+
+    def exchange_x_staged_noalloc(self, x, stream=None):
+        self._call("halo_exchange_x_staged_noalloc", x, stream)
 
     def exchange_x_direct(self, x, stream=None):
         self._call("halo_exchange_x_direct", x, stream)

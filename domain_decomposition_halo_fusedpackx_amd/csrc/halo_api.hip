@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -321,7 +322,8 @@ hipError_t launch_local(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
 }
 
 // One pulse of the staged baseline: two launches.
-hipError_t launch_staged(halo_plan *p, bool force_dir, float *buf, hipStream_t s, int32_t q)
+hipError_t launch_staged(halo_plan *p, bool force_dir, float *buf, float *stage, hipStream_t s,
+                         int32_t q)
 {
     const halo::HostPlan &h = p->h;
     uint32_t bytes = (uint32_t)(h.total_slots * 12);
@@ -331,9 +333,9 @@ hipError_t launch_staged(halo_plan *p, bool force_dir, float *buf, hipStream_t s
     const uint32_t n = (uint32_t)(h.pulse_item_off[q + 1] - base);
     const Kernels k = kernels(h.item_entries);
     int32_t to_region = force_dir ? 0 : 1;
-    void *args_io[] = {&buf, &bytes, &p->d_stage, &stage_bytes, &p->d_idx, &idx_bytes,
-                       &p->d_items, &base};
-    void *args_mv[] = {&buf, &bytes, &p->d_stage, &stage_bytes, &p->d_items, &base, &to_region};
+    void *args_io[] = {&buf, &bytes, &stage, &stage_bytes, &p->d_idx, &idx_bytes, &p->d_items,
+                       &base};
+    void *args_mv[] = {&buf, &bytes, &stage, &stage_bytes, &p->d_items, &base, &to_region};
     hipError_t e;
     if (!force_dir) {
         e = hipLaunchKernel(k.stage_pack, dim3(n), dim3(kThreads), args_io, 0, s);
@@ -912,7 +914,7 @@ static halo_status exchange_staged(halo_plan *p, bool force_dir, float *buf, voi
     }
     for (int32_t i = 0; i < h.n_pulse; ++i) {
         const int32_t q = force_dir ? h.n_pulse - 1 - i : i;
-        hipError_t e = launch_staged(p, force_dir, buf, (hipStream_t)stream, q);
+        hipError_t e = launch_staged(p, force_dir, buf, p->d_stage, (hipStream_t)stream, q);
         if (e != hipSuccess) return hip_fail(e, what);
     }
     return HALO_OK;
@@ -1025,6 +1027,68 @@ halo_status halo_gather_home(halo_plan *p, const float *slots, float *values, vo
 halo_status halo_exchange_x_staged(halo_plan *p, float *x, void *stream)
 {
     return exchange_staged(p, false, x, stream, "halo_exchange_x_staged");
+}
+
+}  // extern "C"
+
+// ---- the staged coordinate exchange without allocation ---------------------
+// For callers that cannot allocate (graph capture, tight loops, harnesses
+// that forbid it): the staging area is a static device array, one per GPU
+// the library runs on, held until the process ends. Its device address is
+// looked up once per device (with that device current) and used from then
+// on; the array's name itself is a host-side stand-in.
+constexpr size_t kScratchBytes = (size_t)32 << 20;  // 12 bytes per indexMap entry
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+float *g_scratch_ptr[kMaxScratchDevices] = {};
+
+halo_status scratch_of_device(int dev, float **out, const char *what)
+{
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(HALO_ERR_ARG, std::string(what) + ": device index out of range");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return hip_fail(e, what);
+        g_scratch_ptr[dev] = static_cast<float *>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return HALO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+halo_status halo_exchange_x_staged_noalloc(halo_plan *p, float *x, void *stream)
+{
+    const char *what = "halo_exchange_x_staged_noalloc";
+    if (!p) return fail(HALO_ERR_ARG, std::string(what) + ": NULL plan");
+    if (!p->uploaded && !p->invalid)
+        return fail(HALO_ERR_STATE, std::string(what) +
+                                        ": the plan is not on the device yet; call "
+                                        "halo_plan_upload (or any exchange) first");
+    halo_status st = check_exchange(p, x, what, stream);  // uploaded: allocates nothing
+    if (st != HALO_OK) return st;
+    const halo::HostPlan &h = p->h;
+    if (h.total_slots == 0 || h.n_entries == 0) return HALO_OK;
+    if ((size_t)h.n_entries * 12 > kScratchBytes)
+        return fail(HALO_ERR_ARG, std::string(what) + ": the plan has " +
+                                      std::to_string((long long)h.n_entries) +
+                                      " indexMap entries; the static staging area holds " +
+                                      std::to_string((long long)(kScratchBytes / 12)));
+    float *stage = nullptr;
+    if ((st = scratch_of_device(p->device, &stage, what)) != HALO_OK) return st;
+    for (int32_t q = 0; q < h.n_pulse; ++q) {
+        const hipError_t e = launch_staged(p, false, x, stage, (hipStream_t)stream, q);
+        if (e != hipSuccess) return hip_fail(e, what);
+    }
+    return HALO_OK;
 }
 
 halo_status halo_exchange_f_staged(halo_plan *p, float *f, void *stream)

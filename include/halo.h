@@ -337,6 +337,17 @@ halo_status halo_exchange_f_atomic(halo_plan *plan, float *f, void *stream);
 halo_status halo_exchange_x_staged(halo_plan *plan, float *x, void *stream);
 halo_status halo_exchange_f_staged(halo_plan *plan, float *f, void *stream);
 
+/* halo_exchange_x_staged for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight loops, harnesses that forbid it): the
+ * same launches and results, staging in a static device array of 32 MiB per
+ * GPU (held until the process ends) instead of a buffer the plan allocates.
+ * The plan must already be on the device (halo_plan_upload or any earlier
+ * exchange; HALO_ERR_STATE otherwise); plans of more than 2,796,202 indexMap
+ * entries (12 bytes each) get HALO_ERR_ARG. Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (other streams, other plans)
+ * race and must be ordered by the caller. Asynchronous on `stream`. */
+halo_status halo_exchange_x_staged_noalloc(halo_plan *plan, float *x, void *stream);
+
 /* Direct coordinate exchange, a one-GPU form of the same result: every halo
  * slot is gathered straight from its atom's home slot, adding +L_d for each
  * dimension in which the atom's forwarding path wraps, in one launch with no
