@@ -396,13 +396,14 @@ def stage_profile(torch, HaloPlan, W, w, pos, launches, reps, replicas=1):
     chunks = plan.chunks()
     # plans built on the host run the index-list exchanges on XCD-local units
     lunits = plan.local_units()
-    runs = [("x", "indexmap"), ("x", "transposed"), ("x", "direct"), ("f", "indexmap"),
-            ("f", "transposed")]
+    runs = [("x", "indexmap"), ("x", "indexmap_lds"), ("x", "transposed"), ("x", "direct"),
+            ("f", "indexmap"), ("f", "transposed")]
     out = {"workload": w.describe(), "halo_entries": plan.num_entries,
            "items": plan.num_items, "chunks": len(chunks), "local_units": len(lunits),
            "launches": launches, "reps": reps, "replicas": replicas}
     for d, form in runs:
-        if form == "transposed" and len(chunks) == 0:
+        if (form == "transposed" and len(chunks) == 0) or (form == "indexmap_lds" and
+                                                            len(lunits) == 0):
             continue
         name = f"exchange_{d}_{form}"
         bufs = xs if d == "x" else fs
@@ -415,7 +416,7 @@ def stage_profile(torch, HaloPlan, W, w, pos, launches, reps, replicas=1):
                 launches) * 1e3)
             st, khz = plans[(launches - 1) % replicas].debug_timing_read()
             tick_us = 1e3 / khz
-            local = form == "indexmap" and len(lunits) > 0
+            local = form.startswith("indexmap") and len(lunits) > 0
             n_units = (len(chunks) if form == "transposed" else
                        len(lunits) if local else plan.num_items)
             st = st[:n_units]
@@ -642,7 +643,8 @@ def main():
     if fused and not args.no_ablation:
         # the other forms of the same two exchanges, same replicas
         forms = {}
-        for form in ("indexmap", "transposed", "pulsewise", "staged", "atomic", "direct"):
+        for form in ("indexmap", "indexmap_lds", "transposed", "pulsewise", "staged", "atomic",
+                     "direct"):
             log(f"form {form}")
             fx = getattr(HaloPlan, "exchange_x_" + form, None)
             ff = getattr(HaloPlan, "exchange_f_" + form, None)

@@ -53,6 +53,7 @@ SIGNATURES = {
     "halo_exchange_f": (_st, [_vp, _vp, _vp]),
     "halo_exchange_x_indexmap": (_st, [_vp, _vp, _vp]),
     "halo_exchange_f_indexmap": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_x_indexmap_lds": (_st, [_vp, _vp, _vp]),
     "halo_exchange_x_transposed": (_st, [_vp, _vp, _vp]),
     "halo_exchange_f_transposed": (_st, [_vp, _vp, _vp]),
     "halo_exchange_x_pulsewise": (_st, [_vp, _vp, _vp]),
@@ -379,6 +380,9 @@ class HaloPlan:
 
     def exchange_f_indexmap(self, f, stream=None):
         self._call("halo_exchange_f_indexmap", f, stream)
+
+    def exchange_x_indexmap_lds(self, x, stream=None):
+        self._call("halo_exchange_x_indexmap_lds", x, stream)
 
     def exchange_x_transposed(self, x, stream=None):
         self._call("halo_exchange_x_transposed", x, stream)

@@ -473,9 +473,56 @@ __global__ __launch_bounds__(kThreads) void k_unpack_atomic(
 // Unit position b is workgroup b of the coordinate kernel and workgroup
 // n - 1 - b of the force kernel; empty positions exit at once.
 
+// Store a unit's n consecutive float triples (v[j] of thread t is entry
+// t + j * kThreads) at slots region_begin, region_begin + 1, ... through LDS:
+// the triples are written to LDS, then the run's bytes go out as 16-byte
+// stores on 16-byte boundaries (a head and a tail of up to three 4-byte
+// stores). The form the pages' design names for float3 coordinates; kept as
+// an ablation beside the 12-byte stores.
+template <int EPT, int ST>
+__device__ __forceinline__ void store_run_lds4(__amdgpu_buffer_rsrc_t rx, int32_t region_begin,
+                                               int32_t n, const f3v *v, float *lds)
+{
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int32_t e = (int32_t)threadIdx.x + j * kThreads;
+        if (e < n) {
+            lds[3 * e] = v[j].x;
+            lds[3 * e + 1] = v[j].y;
+            lds[3 * e + 2] = v[j].z;
+        }
+    }
+    __syncthreads();
+    // words k < words of the run sit at byte b0 + 4k; the body [a0, a1) is
+    // 16-byte aligned, the head (before a0) and the tail (from the body's
+    // end) have at most three words each
+    const uint32_t words = (uint32_t)n * 3u;
+    const uint32_t b0 = (uint32_t)region_begin * 12u, b1 = b0 + words * 4u;
+    const uint32_t a0 = (b0 + 15u) & ~15u, a1 = b1 & ~15u;
+    const uint32_t head = min(words, (a0 - b0) / 4u);
+    const uint32_t body_end = a1 > a0 ? (a1 - b0) / 4u : head;
+    // (the 4-byte store takes the word's bits, not a converted value)
+    if (threadIdx.x < head)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lds[threadIdx.x]), rx,
+                                              b0 + 4u * threadIdx.x, 0, ST);
+    if (threadIdx.x < words - body_end) {
+        const uint32_t w = body_end + threadIdx.x;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lds[w]), rx, b0 + 4u * w, 0, ST);
+    }
+    if (a1 > a0) {
+        typedef float f4v __attribute__((ext_vector_type(4)));
+        for (uint32_t q = threadIdx.x; q < (a1 - a0) / 16u; q += kThreads) {
+            const uint32_t w = head + 4u * q;
+            const f4v d = {lds[w], lds[w + 1], lds[w + 2], lds[w + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(d, rx, a0 + 16u * q, 0, ST);
+        }
+    }
+}
+
 // Coordinates (Algorithms 3 and 4): x[region_begin + e] = x[idx[map_begin +
 // e]] + shift; a unit that reads a region first waits for its writers.
-template <int EPT>
+// LDS4: the stores go through LDS as 16-byte stores (store_run_lds4).
+template <int EPT, bool LDS4 = false>
 __global__ __launch_bounds__(kThreads) void k_pack_local(
     float *x, uint32_t x_bytes, const int32_t *__restrict__ idx, uint32_t idx_bytes,
     const halo::LocalUnit *__restrict__ units, const int32_t *__restrict__ waits,
@@ -521,7 +568,18 @@ __global__ __launch_bounds__(kThreads) void k_pack_local(
 #pragma unroll
         for (int j = 0; j < EPT; ++j) v[j] = load3<kShared>(rx, src[j]);
     }
-    if (flagged) {
+    if constexpr (LDS4) {
+        __shared__ float lds[3 * EPT * kThreads];
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) v[j] = v[j] + shift;
+        if (flagged) {
+            store_run_lds4<EPT, kPlain>(rx, region_begin, n, v, lds);
+            halo::set_local_flag(flags, kp, b, ls.epoch, un->seg == withhold);
+            stamp(dbg, (uint32_t)b, kStampSignal);
+        } else {
+            store_run_lds4<EPT, kStream>(rx, region_begin, n, v, lds);
+        }
+    } else if (flagged) {
         // a later unit of this XCD forwards these slots
 #pragma unroll
         for (int j = 0; j < EPT; ++j) store3<kPlain>(rx, dst[j], v[j] + shift);

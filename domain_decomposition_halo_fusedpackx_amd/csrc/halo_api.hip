@@ -106,7 +106,7 @@ int ept_for(int32_t item_entries)
 struct Kernels {
     const void *pack_fused, *unpack_fused, *pack_pulse, *unpack_pulse, *push_x, *pull_f,
         *unpack_atomic, *stage_pack, *stage_move, *stage_unpack, *origin_pulse, *gather_x,
-        *chunk_rows, *pack_local, *unpack_local;
+        *chunk_rows, *pack_local, *unpack_local, *pack_local_lds4;
 };
 
 template <int EPT>
@@ -119,7 +119,7 @@ Kernels kernels_for()
             (const void *)&k_stage_move<EPT>,    (const void *)&k_stage_unpack<EPT>,
             (const void *)&k_origin_pulse<EPT>,  (const void *)&k_gather_x<EPT>,
             (const void *)&k_chunk_rows<EPT>,    (const void *)&k_pack_local<EPT>,
-            (const void *)&k_unpack_local<EPT>};
+            (const void *)&k_unpack_local<EPT>,  (const void *)&k_pack_local<EPT, true>};
 }
 
 Kernels kernels(int32_t item_entries)
@@ -292,7 +292,8 @@ hipError_t launch_atomic(halo_plan *p, float *buf, hipStream_t s)
 // XCD-local index-list kernels (plans built on the host): one launch, one
 // unit position per workgroup; the flags of the coordinate direction, then
 // of the force direction.
-hipError_t launch_local(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
+hipError_t launch_local(halo_plan *p, bool force_dir, float *buf, hipStream_t s,
+                        bool lds4 = false)
 {
     const halo::HostPlan &h = p->h;
     uint32_t bytes = (uint32_t)(h.total_slots * 12);
@@ -316,7 +317,8 @@ hipError_t launch_local(halo_plan *p, bool force_dir, float *buf, hipStream_t s)
         void *args[] = {&buf,   &bytes, &p->d_idx, &idx_bytes, &p->d_lunits, &p->d_lwaits,
                         &flags, &kp,    &groups,   &members,   &epoch,       &p->spin_limit,
                         &p->d_err, &p->withhold, &dbg};
-        e = hipLaunchKernel(k.pack_local, dim3((uint32_t)n_units), dim3(kThreads), args, 0, s);
+        e = hipLaunchKernel(lds4 ? k.pack_local_lds4 : k.pack_local, dim3((uint32_t)n_units),
+                            dim3(kThreads), args, 0, s);
     }
     return epoch_launched(p, fam, e);
 }
@@ -850,6 +852,20 @@ halo_status halo_exchange_x_indexmap(halo_plan *p, float *x, void *stream)
     hipError_t e = p->h.has_local ? launch_local(p, false, x, (hipStream_t)stream)
                                   : launch_fused(p, false, x, (hipStream_t)stream);
     return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_x_indexmap launch");
+}
+
+halo_status halo_exchange_x_indexmap_lds(halo_plan *p, float *x, void *stream)
+{
+    const char *what = "halo_exchange_x_indexmap_lds";
+    halo_status st = check_exchange(p, x, what, stream);
+    if (st != HALO_OK) return st;
+    if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
+    if (!p->h.has_local)
+        return fail(HALO_ERR_ARG, std::string(what) +
+                                      ": needs the XCD-local units of a plan built by "
+                                      "halo_plan_create");
+    hipError_t e = launch_local(p, false, x, (hipStream_t)stream, true);
+    return e == hipSuccess ? HALO_OK : hip_fail(e, what);
 }
 
 halo_status halo_exchange_f_indexmap(halo_plan *p, float *f, void *stream)

@@ -292,6 +292,14 @@ halo_status halo_exchange_f(halo_plan *plan, float *f, void *stream);
 halo_status halo_exchange_x_indexmap(halo_plan *plan, float *x, void *stream);
 halo_status halo_exchange_f_indexmap(halo_plan *plan, float *f, void *stream);
 
+/* Ablation of the coordinate store ("Redesigning GROMACS Halo Exchange",
+ * s.4 on the coalescing of float3 coordinates into aligned stores): the
+ * index-list coordinate exchange on XCD-local units with each unit's
+ * contiguous run of destination slots staged in LDS and written as 16-byte
+ * stores on 16-byte boundaries, instead of one 12-byte store per slot. Same
+ * results. Plans built by halo_plan_create only (HALO_ERR_ARG otherwise). */
+halo_status halo_exchange_x_indexmap_lds(halo_plan *plan, float *x, void *stream);
+
 /* Transposed form of the fused exchanges: the indexMaps stored as one pulse
  * mask per slot; a workgroup takes a run of slots of one domain inside one
  * zone (home slots, or the region of one pulse). Coordinates: each slot is

@@ -54,7 +54,7 @@ def setup_case(oracle_mod, pos, box, grid, rc):
     return plan, o
 
 
-IMPLS = ["fused", "indexmap", "transposed", "pulsewise", "staged", "direct"]
+IMPLS = ["fused", "indexmap", "transposed", "pulsewise", "staged", "direct", "indexmap_lds"]
 
 
 def exchange(plan, impl, direction, buf, stream=None):
@@ -62,11 +62,14 @@ def exchange(plan, impl, direction, buf, stream=None):
         impl = "indexmap"  # the transposed form refuses plans with more than 8 pulses
     if impl == "direct" and direction == "f":
         impl = "fused"  # the direct form exists for coordinates only
+    if impl == "indexmap_lds" and (direction == "f" or len(plan.local_units()) == 0):
+        impl = "indexmap"  # coordinates only, on the XCD-local units of host-built plans
     name = {"fused": "exchange_{}", "indexmap": "exchange_{}_indexmap",
             "transposed": "exchange_{}_transposed",
             "pulsewise": "exchange_{}_pulsewise",
             "staged": "exchange_{}_staged",
-            "direct": "exchange_{}_direct"}[impl].format(direction)
+            "direct": "exchange_{}_direct",
+            "indexmap_lds": "exchange_{}_indexmap_lds"}[impl].format(direction)
     getattr(plan, name)(buf, stream)
 
 
