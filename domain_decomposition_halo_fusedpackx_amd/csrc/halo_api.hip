@@ -300,7 +300,7 @@ hipError_t launch_local(halo_plan *p, bool force_dir, float *buf, hipStream_t s,
     uint32_t idx_bytes = (uint32_t)(h.n_entries * 4);
     int32_t n_units = (int32_t)h.lunits.size();
     int32_t kp = halo::local_flag_stride(h.local_k);
-    const Kernels k = kernels(h.item_entries);
+    const Kernels k = kernels(h.local_entries);
     const int fam = force_dir ? halo::kFamItemsF : halo::kFamItemsX;
     uint32_t *groups = launch_groups(p, fam);
     const uint32_t *members = launch_members(p, fam);
@@ -802,7 +802,8 @@ halo_status halo_plan_upload(halo_plan *p)
 // for more pulses, each of which adds a dependent stage to the transposed
 // kernel's work units (the 4x4x8 box with its two z pulses).
 constexpr int64_t kTransposedCoordMinEntries = 1 << 20;
-constexpr int64_t kTransposedForceMinEntries = 1 << 18;
+constexpr int64_t kTransposedForceMinEntries = 1 << 18;       // plans with work items
+constexpr int64_t kTransposedForceMinEntriesLocal = 1 << 20;  // plans with XCD-local units
 constexpr int32_t kTransposedForceMaxPulses = 3;
 
 halo_status halo_exchange_x(halo_plan *p, float *x, void *stream)
@@ -814,7 +815,9 @@ halo_status halo_exchange_x(halo_plan *p, float *x, void *stream)
 
 halo_status halo_exchange_f(halo_plan *p, float *f, void *stream)
 {
-    if (p && (!p->h.has_chunks || (int64_t)p->h.n_entries < kTransposedForceMinEntries ||
+    const int64_t min_entries =
+        p && p->h.has_local ? kTransposedForceMinEntriesLocal : kTransposedForceMinEntries;
+    if (p && (!p->h.has_chunks || (int64_t)p->h.n_entries < min_entries ||
               p->h.n_pulse > kTransposedForceMaxPulses))
         return halo_exchange_f_indexmap(p, f, stream);
     return halo_exchange_f_transposed(p, f, stream);

@@ -375,7 +375,7 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
     });
     make_items(P, item_entries);
     make_chunks(P, item_entries);
-    make_local_units(P, item_entries);
+    make_local_units(P, local_unit_entries(P.n_entries, item_entries));
     make_launch_members(P);
     return kOk;
 }
@@ -595,10 +595,23 @@ void make_items(HostPlan &P, int32_t item_entries, bool with_masks)
 // hold empty units. A unit then waits only for units of its own class at
 // smaller positions (coordinates) or larger positions (forces, launched in
 // reverse).
+// A unit's entries are one stage of the forwarding chain for that stretch:
+// smaller units start their dependants sooner and run fewer entries per
+// thread, larger ones cost fewer waits and workgroups. Measured over the five
+// workloads, about two units per compute unit is where the two balance (the
+// chip has 256 compute units).
+int32_t local_unit_entries(int64_t n_entries, int32_t item_entries)
+{
+    int32_t u = 1024;
+    while (u > 128 && (int64_t)u * 512 > n_entries) u /= 2;
+    return std::max<int32_t>(1, std::min(u, item_entries));
+}
+
 void make_local_units(HostPlan &P, int32_t unit_entries)
 {
     P.has_local = false;
     P.local_k = 0;
+    P.local_entries = 0;
     P.lunits.clear();
     P.lwaits.clear();
     if (P.n_pulse == 0 || P.n_entries == 0 || P.total_slots == 0) return;
@@ -733,6 +746,7 @@ void make_local_units(HostPlan &P, int32_t unit_entries)
             P.lunits[(size_t)pos_of[(size_t)v]].flags |= kLocalFWaited;
         }
     }
+    for (const LocalUnit &u : P.lunits) P.local_entries = std::max(P.local_entries, u.n_total);
     P.has_local = true;
 }
 

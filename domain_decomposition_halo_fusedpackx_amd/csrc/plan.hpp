@@ -155,6 +155,7 @@ struct HostPlan {
     // XCD-local units of the index-list kernels (host-built plans only)
     bool has_local = false;
     int32_t local_k = 0;                   // positions per class
+    int32_t local_entries = 0;             // most entries of a unit (sets the kernels' width)
     std::vector<LocalUnit> lunits;         // [kXcdClasses * local_k]; position b: class b % 8
     std::vector<int32_t> lwaits;           // wait lists (positions)
     // launch counts: members of each group of each kernel family
@@ -205,6 +206,11 @@ bool xcd_ordering_enabled();
 // Build the XCD-local units (runs of one origin, at most unit_entries
 // entries each), their placement and their wait lists.
 void make_local_units(HostPlan &plan, int32_t unit_entries);
+
+// The size bound of the XCD-local units: the largest power of two from 128 to
+// 1024 entries (and at most item_entries) at which the plan still has about
+// two units per compute unit of the chip (512 units' worth of entries).
+int32_t local_unit_entries(int64_t n_entries, int32_t item_entries);
 
 // Build the transposed form (masks and chunks of at most chunk_slots slots).
 void make_chunks(HostPlan &plan, int32_t chunk_slots);

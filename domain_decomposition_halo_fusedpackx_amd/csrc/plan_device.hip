@@ -716,6 +716,7 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     // (no XCD-local units)
     P.has_local = false;
     P.local_k = 0;
+    P.local_entries = 0;
     P.lunits.clear();
     P.lwaits.clear();
     if (P.n_dom > kMaxDeviceDomains) {

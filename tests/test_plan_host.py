@@ -218,3 +218,25 @@ def test_more_than_32_pulses_is_a_geometry_error(oracle_mod):
     assert plan.num_pulses == 32
     o = oracle_mod.Oracle(pos, (12.0, 12.0, 13.2), grid, 10.5)
     assert o.n_pulse == 32
+
+
+@pytest.mark.parametrize("wid,bound", [(1, 128), (2, 128), (3, 512), (4, 256), (5, 1024)])
+def test_local_unit_size_follows_plan_size(wid, bound):
+    """The XCD-local units are cut at the largest power of two from 128 to
+    1024 entries at which the plan keeps 512 units' worth of entries: 128 for
+    the two smallest workloads, 512 / 256 / 1024 for workloads 3 / 4 / 5. A
+    unit never exceeds its bound, and on workloads 3 and 5 some unit is longer
+    than half of it (the bound is not smaller than the rule says)."""
+    w = W.WORKLOADS[wid]
+    pos = W.workload_positions(w)
+    plan = HaloPlan(pos, w.box, w.grid, w.cutoff)
+    size = 1024
+    while size > 128 and size * 512 > plan.num_entries:
+        size //= 2
+    assert size == bound
+    lu = plan.local_units()
+    n = lu[:, 2][lu[:, 2] > 0]
+    assert n.sum() == plan.num_entries
+    assert n.max() <= bound
+    if wid in (3, 5):
+        assert n.max() > bound // 2
