@@ -270,8 +270,9 @@ halo_status halo_exchange_x(halo_plan *plan, float *x, void *stream);
  * first; for every sender d of pulse p, f[indexMap[i]] += f[receiver's region
  * of pulse p][i], with the per-slot order of additions of the serial
  * reverse-pulse loop, so results are bitwise deterministic. Runs the
- * transposed form (halo_exchange_f_transposed) for plans of at least 2^18
- * indexMap entries and at most 3 pulses, the index-list form
+ * transposed form (halo_exchange_f_transposed) for plans of at most 3 pulses
+ * and at least 2^20 indexMap entries (plans built by halo_plan_create) or
+ * 2^18 (plans built on the device), the index-list form
  * (halo_exchange_f_indexmap) for the others.
  *   f : device, total_slots*3 float32, updated in place. On return home slots
  *       hold the accumulated forces; forwarding halo slots hold partial sums.
