@@ -78,7 +78,12 @@ typedef enum {
  *   grid      : host, 3 int32, domains per dimension nx, ny, nz >= 1
  *   cutoff    : > 0, in the units of box
  *   out       : receives the plan; set to NULL on error
- * The caller keeps ownership of every input; the plan copies what it needs. */
+ * The caller keeps ownership of every input; the plan copies what it needs.
+ * Work units: work items and transposed runs of at most 1024 entries (the
+ * environment variable HALO_ITEM_ENTRIES, read at plan creation, sets another
+ * bound from 1 to 2048, for tuning); XCD-local units of the largest power of
+ * two from 128 to 1024 entries (never above that bound) at which the plan
+ * keeps at least 512 units' worth of entries. */
 halo_status halo_plan_create(const float *positions, int64_t n_atoms, const float *box,
                              const int32_t *grid, float cutoff, halo_plan **out);
 
