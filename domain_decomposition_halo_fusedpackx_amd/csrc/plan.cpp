@@ -373,9 +373,12 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
             P.abs_map[s.map_off + i] = (int32_t)(P.base[D] + pk[i]);
         }
     });
-    make_items(P, item_entries);
+    // work items and XCD-local units take the plan-sized bound; the
+    // transposed runs keep item_entries
+    const int32_t unit_entries = local_unit_entries(P.n_entries, item_entries);
+    make_items(P, unit_entries);
     make_chunks(P, item_entries);
-    make_local_units(P, local_unit_entries(P.n_entries, item_entries));
+    make_local_units(P, unit_entries);
     make_launch_members(P);
     return kOk;
 }

@@ -934,7 +934,7 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         P.slot_mask.clear();
     }
     P.chunk_slots = item_entries;
-    make_items(P, item_entries, false);
+    make_items(P, local_unit_entries(P.n_entries, item_entries), false);
     const std::vector<Piece> pieces =
         P.has_chunks ? chunk_pieces(P, item_entries) : std::vector<Piece>();
     const size_t npc = pieces.size();

@@ -139,14 +139,26 @@ def test_position_errors_match_oracle(oracle_mod, bad):
     assert e.value.code == want == -3
 
 
+def _unit_bound(n_entries, item_entries=1024):
+    """The work-unit size rule: the largest power of two from 128 to 1024 at
+    which the plan keeps 512 units' worth of entries, at most item_entries."""
+    size = 1024
+    while size > 128 and size * 512 > n_entries:
+        size //= 2
+    return min(size, item_entries)
+
+
 def test_item_cutting(monkeypatch):
     """Work items cut the independent and the dependent span of every
-    (pulse, domain) separately, with at least one item per (pulse, domain)."""
+    (pulse, domain) separately, with at least one item per (pulse, domain),
+    into items of at most the plan-sized bound (256 entries on workload 4,
+    or less when HALO_ITEM_ENTRIES says so)."""
     w = W.WORKLOADS[4]
     pos = W.workload_positions(w)
-    for n in (64, 300, 1024, 2048):
-        monkeypatch.setenv("HALO_ITEM_ENTRIES", str(n))
+    for env, n in ((64, 64), (200, 200), (300, 256), (1024, 256), (2048, 256)):
+        monkeypatch.setenv("HALO_ITEM_ENTRIES", str(env))
         plan = HaloPlan(pos, w.box, w.grid, w.cutoff)
+        assert _unit_bound(plan.num_entries, env) == n
         tot = 0
         for p in range(plan.num_pulses):
             for d in range(plan.num_domains):
@@ -222,21 +234,24 @@ def test_more_than_32_pulses_is_a_geometry_error(oracle_mod):
 
 @pytest.mark.parametrize("wid,bound", [(1, 128), (2, 128), (3, 512), (4, 256), (5, 1024)])
 def test_local_unit_size_follows_plan_size(wid, bound):
-    """The XCD-local units are cut at the largest power of two from 128 to
-    1024 entries at which the plan keeps 512 units' worth of entries: 128 for
-    the two smallest workloads, 512 / 256 / 1024 for workloads 3 / 4 / 5. A
-    unit never exceeds its bound, and on workloads 3 and 5 some unit is longer
-    than half of it (the bound is not smaller than the rule says)."""
+    """The XCD-local units and the work items are cut at the largest power of
+    two from 128 to 1024 entries at which the plan keeps 512 units' worth of
+    entries: 128 for the two smallest workloads, 512 / 256 / 1024 for
+    workloads 3 / 4 / 5. No unit or item exceeds the bound, and on workloads
+    3 and 5 some unit is longer than half of it (the bound is not smaller than
+    the rule says)."""
     w = W.WORKLOADS[wid]
     pos = W.workload_positions(w)
     plan = HaloPlan(pos, w.box, w.grid, w.cutoff)
-    size = 1024
-    while size > 128 and size * 512 > plan.num_entries:
-        size //= 2
-    assert size == bound
+    assert _unit_bound(plan.num_entries) == bound
     lu = plan.local_units()
     n = lu[:, 2][lu[:, 2] > 0]
     assert n.sum() == plan.num_entries
     assert n.max() <= bound
     if wid in (3, 5):
         assert n.max() > bound // 2
+    for p in range(plan.num_pulses):
+        for d in range(plan.num_domains):
+            q = plan.pulse(p, d)
+            dep = q["send_size"] - q["dep_start"]
+            assert q["items"] == max(1, -(-q["dep_start"] // bound) + -(-dep // bound))
