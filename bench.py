@@ -31,8 +31,7 @@ METRIC = "halo atoms/s and HBM GB/s (% of peak); µs per coord+force exchange"
 # The library's rule for the default exchanges (halo_exchange_x / _f in
 # csrc/halo_api.hip): the transposed kernels from these sizes on.
 TRANSPOSED_X_MIN_ENTRIES = 1 << 20
-TRANSPOSED_F_MIN_ENTRIES = 1 << 18        # plans with work items (built on the device)
-TRANSPOSED_F_MIN_ENTRIES_LOCAL = 1 << 20  # plans with XCD-local units (built on the host)
+TRANSPOSED_F_MIN_ENTRIES = 1 << 20
 TRANSPOSED_F_MAX_PULSES = 3
 HBM_PEAK_GBS = 8000.0
 BYTES_X = 28  # per entry: 4 B index + 12 B gathered source + 12 B store
@@ -596,11 +595,9 @@ def main():
     sha = kernel_source_sha()
     # the kernels the default exchanges run (halo_exchange_x / _f choose by size)
     # plans built on the host run the index-list form on XCD-local units
-    local = len(plan0.local_units()) > 0
-    idx_x, idx_f = ("pack_local", "unpack_local") if local else ("pack_fused", "unpack_fused")
-    f_min = TRANSPOSED_F_MIN_ENTRIES_LOCAL if local else TRANSPOSED_F_MIN_ENTRIES
+    idx_x, idx_f = "pack_local", "unpack_local"
     x_default = "push_x" if E >= TRANSPOSED_X_MIN_ENTRIES else idx_x
-    f_default = ("pull_f" if E >= f_min and
+    f_default = ("pull_f" if E >= TRANSPOSED_F_MIN_ENTRIES and
                  plan0.num_pulses <= TRANSPOSED_F_MAX_PULSES else idx_f)
     kernel_of = {("fused", "x"): x_default, ("fused", "f"): f_default,
                  ("indexmap", "x"): idx_x, ("indexmap", "f"): idx_f,
@@ -645,8 +642,8 @@ def main():
     if fused and not args.no_ablation:
         # the other forms of the same two exchanges, same replicas
         forms = {}
-        for form in ("indexmap", "indexmap_lds", "transposed", "pulsewise", "staged", "atomic",
-                     "direct"):
+        for form in ("indexmap", "indexmap_lds", "items", "transposed", "pulsewise", "staged",
+                     "atomic", "direct"):
             log(f"form {form}")
             fx = getattr(HaloPlan, "exchange_x_" + form, None)
             ff = getattr(HaloPlan, "exchange_f_" + form, None)

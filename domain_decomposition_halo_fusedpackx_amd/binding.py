@@ -51,6 +51,8 @@ SIGNATURES = {
     "halo_plan_upload": (_st, [_vp]),
     "halo_exchange_x": (_st, [_vp, _vp, _vp]),
     "halo_exchange_f": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_x_items": (_st, [_vp, _vp, _vp]),
+    "halo_exchange_f_items": (_st, [_vp, _vp, _vp]),
     "halo_exchange_x_indexmap": (_st, [_vp, _vp, _vp]),
     "halo_exchange_f_indexmap": (_st, [_vp, _vp, _vp]),
     "halo_exchange_x_indexmap_lds": (_st, [_vp, _vp, _vp]),
@@ -380,6 +382,12 @@ class HaloPlan:
 
     def exchange_f_indexmap(self, f, stream=None):
         self._call("halo_exchange_f_indexmap", f, stream)
+
+    def exchange_x_items(self, x, stream=None):
+        self._call("halo_exchange_x_items", x, stream)
+
+    def exchange_f_items(self, f, stream=None):
+        self._call("halo_exchange_f_items", f, stream)
 
     def exchange_x_indexmap_lds(self, x, stream=None):
         self._call("halo_exchange_x_indexmap_lds", x, stream)

@@ -301,7 +301,7 @@ hipError_t launch_local(halo_plan *p, bool force_dir, float *buf, hipStream_t s,
     int32_t n_units = (int32_t)h.lunits.size();
     int32_t kp = halo::local_flag_stride(h.local_k);
     const Kernels k = kernels(h.local_entries);
-    const int fam = force_dir ? halo::kFamItemsF : halo::kFamItemsX;
+    const int fam = force_dir ? halo::kFamLocalF : halo::kFamLocalX;
     uint32_t *groups = launch_groups(p, fam);
     const uint32_t *members = launch_members(p, fam);
     uint32_t epoch = launch_epoch_arg(p, fam, s);
@@ -802,8 +802,7 @@ halo_status halo_plan_upload(halo_plan *p)
 // for more pulses, each of which adds a dependent stage to the transposed
 // kernel's work units (the 4x4x8 box with its two z pulses).
 constexpr int64_t kTransposedCoordMinEntries = 1 << 20;
-constexpr int64_t kTransposedForceMinEntries = 1 << 18;       // plans with work items
-constexpr int64_t kTransposedForceMinEntriesLocal = 1 << 20;  // plans with XCD-local units
+constexpr int64_t kTransposedForceMinEntries = 1 << 20;
 constexpr int32_t kTransposedForceMaxPulses = 3;
 
 halo_status halo_exchange_x(halo_plan *p, float *x, void *stream)
@@ -815,9 +814,7 @@ halo_status halo_exchange_x(halo_plan *p, float *x, void *stream)
 
 halo_status halo_exchange_f(halo_plan *p, float *f, void *stream)
 {
-    const int64_t min_entries =
-        p && p->h.has_local ? kTransposedForceMinEntriesLocal : kTransposedForceMinEntries;
-    if (p && (!p->h.has_chunks || (int64_t)p->h.n_entries < min_entries ||
+    if (p && (!p->h.has_chunks || (int64_t)p->h.n_entries < kTransposedForceMinEntries ||
               p->h.n_pulse > kTransposedForceMaxPulses))
         return halo_exchange_f_indexmap(p, f, stream);
     return halo_exchange_f_transposed(p, f, stream);
@@ -857,6 +854,24 @@ halo_status halo_exchange_x_indexmap(halo_plan *p, float *x, void *stream)
     return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_x_indexmap launch");
 }
 
+halo_status halo_exchange_x_items(halo_plan *p, float *x, void *stream)
+{
+    halo_status st = check_exchange(p, x, "halo_exchange_x_items", stream);
+    if (st != HALO_OK) return st;
+    if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
+    hipError_t e = launch_fused(p, false, x, (hipStream_t)stream);
+    return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_x_items launch");
+}
+
+halo_status halo_exchange_f_items(halo_plan *p, float *f, void *stream)
+{
+    halo_status st = check_exchange(p, f, "halo_exchange_f_items", stream);
+    if (st != HALO_OK) return st;
+    if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
+    hipError_t e = launch_fused(p, true, f, (hipStream_t)stream);
+    return e == hipSuccess ? HALO_OK : hip_fail(e, "halo_exchange_f_items launch");
+}
+
 halo_status halo_exchange_x_indexmap_lds(halo_plan *p, float *x, void *stream)
 {
     const char *what = "halo_exchange_x_indexmap_lds";
@@ -864,9 +879,7 @@ halo_status halo_exchange_x_indexmap_lds(halo_plan *p, float *x, void *stream)
     if (st != HALO_OK) return st;
     if (p->h.items.empty() || p->h.total_slots == 0) return HALO_OK;
     if (!p->h.has_local)
-        return fail(HALO_ERR_ARG, std::string(what) +
-                                      ": needs the XCD-local units of a plan built by "
-                                      "halo_plan_create");
+        return fail(HALO_ERR_ARG, std::string(what) + ": the plan has no XCD-local units");
     hipError_t e = launch_local(p, false, x, (hipStream_t)stream, true);
     return e == hipSuccess ? HALO_OK : hip_fail(e, what);
 }

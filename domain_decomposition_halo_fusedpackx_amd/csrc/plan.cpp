@@ -394,19 +394,17 @@ void make_launch_members(HostPlan &P)
     };
     for (size_t u = 0; u < P.items.size(); ++u) {
         const WorkItem &it = P.items[u];
-        if (!P.has_local) {
-            if (it.n_total > it.n_indep) add(kFamItemsX, u);
-            if (it.fwait[0] >= 0) add(kFamItemsF, u);
-        }
+        if (it.n_total > it.n_indep) add(kFamItemsX, u);
+        if (it.fwait[0] >= 0) add(kFamItemsF, u);
         add(kFamAtomicF, u);
     }
-    // The XCD-local index-list kernels take the same two families; a unit
-    // that waits, or that writes a flag another unit waits for, takes part
-    // (in a replayed graph it reads the count to learn the epoch).
+    // The XCD-local index-list kernels: a unit that waits, or that writes a
+    // flag another unit waits for, takes part (in a replayed graph it reads
+    // the count to learn the epoch).
     for (size_t b = 0; b < P.lunits.size(); ++b) {
         const LocalUnit &un = P.lunits[b];
-        if (un.wx_n > 0 || (un.flags & kLocalXWaited)) add(kFamItemsX, b);
-        if (un.wf_n > 0 || (un.flags & kLocalFWaited)) add(kFamItemsF, b);
+        if (un.wx_n > 0 || (un.flags & kLocalXWaited)) add(kFamLocalX, b);
+        if (un.wf_n > 0 || (un.flags & kLocalFWaited)) add(kFamLocalF, b);
     }
     if (!P.has_chunks) return;
     for (size_t u = 0; u < P.chunks.size(); ++u) {
@@ -633,11 +631,7 @@ void make_local_units(HostPlan &P, int32_t unit_entries)
                 origin[(size_t)(dst + i)] = origin[(size_t)P.abs_map[(size_t)g.map_off + i]];
         }
 
-    struct Raw {
-        int32_t pulse, sender, e0, n, zone, origin;
-        int32_t src_lo, src_hi;  // absolute slots of the first and last source
-    };
-    std::vector<Raw> raw;
+    std::vector<LocalRun> raw;
     auto zone_of = [&](int32_t D, int32_t l) {
         if (l < P.n_home[D]) return -1;
         for (int32_t q = 0; q < np; ++q) {
@@ -664,14 +658,24 @@ void make_local_units(HostPlan &P, int32_t unit_entries)
                 for (int32_t k = 0; k < pieces; ++k) {
                     const int32_t a = i + (int32_t)((int64_t)len * k / pieces);
                     const int32_t b = i + (int32_t)((int64_t)len * (k + 1) / pieces);
-                    raw.push_back(Raw{p, D, a, b - a, z, o,
-                                      P.abs_map[(size_t)g.map_off + a],
-                                      P.abs_map[(size_t)g.map_off + b - 1]});
+                    raw.push_back(LocalRun{p, D, a, b - a, z, o,
+                                           P.abs_map[(size_t)g.map_off + a],
+                                           P.abs_map[(size_t)g.map_off + b - 1]});
                 }
                 i = j;
             }
         }
+    place_local_units(P, raw);
+}
 
+void place_local_units(HostPlan &P, const std::vector<LocalRun> &raw)
+{
+    P.has_local = false;
+    P.local_k = 0;
+    P.local_entries = 0;
+    P.lunits.clear();
+    P.lwaits.clear();
+    const int32_t nd = P.n_dom, np = P.n_pulse;
     // classes and positions
     std::vector<std::vector<int32_t>> cls(kXcdClasses);
     for (int32_t p = 0; p < np; ++p) {
@@ -692,42 +696,21 @@ void make_local_units(HostPlan &P, int32_t unit_entries)
         for (size_t k = 0; k < cls[c].size(); ++k)
             pos_of[(size_t)cls[c][k]] = (int32_t)(k * kXcdClasses + (size_t)c);
 
-    // units by sending domain, for the wait lists
-    std::vector<std::vector<int32_t>> by_sender(nd);
-    for (int32_t r = 0; r < (int32_t)raw.size(); ++r) by_sender[raw[r].sender].push_back(r);
-
-    std::vector<std::vector<int32_t>> wx(raw.size()), wf(raw.size());
-    for (int32_t r = 0; r < (int32_t)raw.size(); ++r) {
-        const Raw &u = raw[r];
-        const Segment &g = P.at(u.pulse, u.sender);
-        // coordinates: the writers of the stretch of region `zone` it reads
-        if (u.zone >= 0) {
-            const int32_t q = u.zone, Dq = P.recv_from[(size_t)q * nd + u.sender];
-            const int64_t r0 = P.base[u.sender] + P.at(q, u.sender).atom_offset;
-            const int64_t i_lo = u.src_lo - r0, i_hi = u.src_hi - r0;
-            for (int32_t v : by_sender[Dq]) {
-                const Raw &w = raw[v];
-                if (w.pulse == q && w.e0 <= i_hi && w.e0 + w.n - 1 >= i_lo) wx[r].push_back(v);
-            }
-        }
-        // forces: later units adding into the region slots it reads or into
-        // its own source slots
-        const int64_t reg_lo = P.base[g.send_to] + P.at(u.pulse, g.send_to).atom_offset + u.e0;
-        const int64_t reg_hi = reg_lo + u.n - 1;
-        for (int32_t v : by_sender[g.send_to]) {
-            const Raw &w = raw[v];
-            if (w.pulse > u.pulse && w.src_lo <= reg_hi && w.src_hi >= reg_lo) wf[r].push_back(v);
-        }
-        for (int32_t v : by_sender[u.sender]) {
-            const Raw &w = raw[v];
-            if (w.pulse > u.pulse && w.src_lo <= u.src_hi && w.src_hi >= u.src_lo &&
-                (g.send_to != u.sender || std::find(wf[r].begin(), wf[r].end(), v) == wf[r].end()))
-                wf[r].push_back(v);
-        }
+    // units by sending domain (in piece order), for the wait lists
+    std::vector<int32_t> sender_off((size_t)nd + 1, 0), by_sender(raw.size());
+    for (const LocalRun &u : raw) ++sender_off[(size_t)u.sender + 1];
+    for (int32_t D = 0; D < nd; ++D) sender_off[(size_t)D + 1] += sender_off[(size_t)D];
+    {
+        std::vector<int32_t> fill(sender_off.begin(), sender_off.end() - 1);
+        for (int32_t r = 0; r < (int32_t)raw.size(); ++r) by_sender[(size_t)fill[raw[r].sender]++] = r;
     }
-
+    auto senders = [&](int32_t D) {
+        return std::make_pair(by_sender.data() + sender_off[(size_t)D],
+                              by_sender.data() + sender_off[(size_t)D + 1]);
+    };
+    P.lwaits.reserve(raw.size() * 4);
     for (int32_t r = 0; r < (int32_t)raw.size(); ++r) {
-        const Raw &u = raw[r];
+        const LocalRun &u = raw[r];
         const Segment &g = P.at(u.pulse, u.sender);
         LocalUnit &L = P.lunits[(size_t)pos_of[r]];
         L.map_begin = (int32_t)(g.map_off + u.e0);
@@ -736,18 +719,42 @@ void make_local_units(HostPlan &P, int32_t unit_entries)
         L.seg = u.pulse * nd + u.sender;
         for (int c = 0; c < 3; ++c) L.shift[c] = g.shift[c];
         L.origin = u.origin;
+        // coordinates: the writers of the stretch of region `zone` it reads
         L.wx_off = (int32_t)P.lwaits.size();
-        L.wx_n = (int32_t)wx[r].size();
-        for (int32_t v : wx[r]) {
-            P.lwaits.push_back(pos_of[(size_t)v]);
-            P.lunits[(size_t)pos_of[(size_t)v]].flags |= kLocalXWaited;
+        if (u.zone >= 0) {
+            const int32_t q = u.zone, Dq = P.recv_from[(size_t)q * nd + u.sender];
+            const int64_t r0 = P.base[u.sender] + P.at(q, u.sender).atom_offset;
+            const int64_t i_lo = u.src_lo - r0, i_hi = u.src_hi - r0;
+            for (auto [it, end] = senders(Dq); it != end; ++it) {
+                const LocalRun &w = raw[(size_t)*it];
+                if (w.pulse == q && w.e0 <= i_hi && w.e0 + w.n - 1 >= i_lo) {
+                    P.lwaits.push_back(pos_of[(size_t)*it]);
+                    P.lunits[(size_t)pos_of[(size_t)*it]].flags |= kLocalXWaited;
+                }
+            }
         }
+        L.wx_n = (int32_t)P.lwaits.size() - L.wx_off;
+        // forces: later units adding into the region slots it reads or into
+        // its own source slots
         L.wf_off = (int32_t)P.lwaits.size();
-        L.wf_n = (int32_t)wf[r].size();
-        for (int32_t v : wf[r]) {
-            P.lwaits.push_back(pos_of[(size_t)v]);
-            P.lunits[(size_t)pos_of[(size_t)v]].flags |= kLocalFWaited;
+        const int64_t reg_lo = L.region_begin, reg_hi = reg_lo + u.n - 1;
+        for (auto [it, end] = senders(g.send_to); it != end; ++it) {
+            const LocalRun &w = raw[(size_t)*it];
+            if (w.pulse > u.pulse && w.src_lo <= reg_hi && w.src_hi >= reg_lo)
+                P.lwaits.push_back(pos_of[(size_t)*it]);
         }
+        const size_t first_own = P.lwaits.size();
+        for (auto [it, end] = senders(u.sender); it != end; ++it) {
+            const LocalRun &w = raw[(size_t)*it];
+            if (w.pulse > u.pulse && w.src_lo <= u.src_hi && w.src_hi >= u.src_lo &&
+                (g.send_to != u.sender ||
+                 std::find(P.lwaits.begin() + L.wf_off, P.lwaits.begin() + (ptrdiff_t)first_own,
+                           pos_of[(size_t)*it]) == P.lwaits.begin() + (ptrdiff_t)first_own))
+                P.lwaits.push_back(pos_of[(size_t)*it]);
+        }
+        L.wf_n = (int32_t)P.lwaits.size() - L.wf_off;
+        for (int32_t k = L.wf_off; k < L.wf_off + L.wf_n; ++k)
+            P.lunits[(size_t)P.lwaits[(size_t)k]].flags |= kLocalFWaited;
     }
     for (const LocalUnit &u : P.lunits) P.local_entries = std::max(P.local_entries, u.n_total);
     P.has_local = true;

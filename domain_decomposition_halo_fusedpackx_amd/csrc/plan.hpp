@@ -194,7 +194,9 @@ enum : int {
     kFamChunksX = 2,  // k_push_x: region chunks
     kFamChunksF = 3,  // k_pull_f: chunks that pull a region summed in the launch
     kFamAtomicF = 4,  // k_unpack_atomic: every item
-    kFamilies = 5
+    kFamLocalX = 5,   // k_pack_local: units that wait or are waited for
+    kFamLocalF = 6,   // k_unpack_local: the same in the force direction
+    kFamilies = 7
 };
 
 // Fill plan.launch_members from the items and chunks.
@@ -206,6 +208,20 @@ bool xcd_ordering_enabled();
 // Build the XCD-local units (runs of one origin, at most unit_entries
 // entries each), their placement and their wait lists.
 void make_local_units(HostPlan &plan, int32_t unit_entries);
+
+// One piece of a run of entries of segment (pulse, sender) whose sources lie
+// in one zone of the sender and hold atoms of one origin; entries e0 .. e0+n-1
+// of the segment. The input of the placement below, from the host build
+// (make_local_units) or the device build.
+struct LocalRun {
+    int32_t pulse, sender, e0, n, zone, origin;
+    int32_t src_lo, src_hi;  // absolute slots of the first and last source
+};
+static_assert(sizeof(LocalRun) == 32, "LocalRun layout");
+
+// Classes, positions, wait lists and flags of the XCD-local units from their
+// pieces, given in segment order (pulse-major, then sender, then entry).
+void place_local_units(HostPlan &plan, const std::vector<LocalRun> &runs);
 
 // The size bound of the XCD-local units: the largest power of two from 128 to
 // 1024 entries (and at most item_entries) at which the plan still has about

@@ -597,6 +597,198 @@ __global__ __launch_bounds__(kBT) void k_piece_stats(const Piece *__restrict__ p
     }
 }
 
+// ---- XCD-local units (plan.cpp, make_local_units, does the same on the host) ----
+
+// The origin (home domain of the atom) of every home slot.
+__global__ __launch_bounds__(kBT) void k_origin_home(const int32_t *__restrict__ owner,
+                                                     const int64_t *__restrict__ home_slot,
+                                                     int64_t n_atoms, int32_t *__restrict__ origin)
+{
+    const int64_t a = (int64_t)blockIdx.x * kBT + threadIdx.x;
+    if (a < n_atoms) origin[home_slot[a]] = owner[a];
+}
+
+// Block = sender D of pulse p: the origins of the receiver's region of pulse p
+// are those of the slots D sends (home slots or regions of earlier pulses,
+// set by earlier launches).
+__global__ __launch_bounds__(kBT) void k_origin_pulse(SegTable seg, int32_t p, int32_t n_dom,
+                                                      const int32_t *__restrict__ send_to,
+                                                      const int64_t *__restrict__ base,
+                                                      const int32_t *__restrict__ abs_map,
+                                                      int32_t *__restrict__ origin)
+{
+    const int32_t D = blockIdx.x;
+    const int32_t m0 = seg.row(p, kMapOff)[D], n = seg.row(p, kSendSize)[D];
+    const int32_t R = send_to[(size_t)p * n_dom + D];
+    const int64_t dst = base[R] + seg.row(p, kAtomOffset)[R];
+    for (int32_t i = threadIdx.x; i < n; i += kBT) origin[dst + i] = origin[abs_map[m0 + i]];
+}
+
+// Origin and zone (-1: home slots; q: the region of pulse q) of the source of
+// entry i of segment (p, D), packed as origin * 64 + zone + 1.
+__device__ __forceinline__ int32_t unit_key(SegTable seg, int32_t p, int32_t D, int32_t m0,
+                                            int32_t i, const int32_t *__restrict__ local_map,
+                                            const int32_t *__restrict__ abs_map,
+                                            const int32_t *__restrict__ origin,
+                                            const int32_t *__restrict__ n_home)
+{
+    const int32_t l = local_map[m0 + i];
+    int32_t z = -1;
+    if (l >= n_home[D])
+        for (int32_t q = 0; q < p; ++q) {
+            const int32_t lo = seg.row(q, kAtomOffset)[D];
+            if (l >= lo && l < lo + seg.row(q, kRecvSize)[D]) z = q;
+        }
+    return origin[abs_map[m0 + i]] * 64 + z + 1;
+}
+
+// Block = segment (pulse-major): the first entry of every run of entries
+// whose sources share origin and zone (in runs[m0 ...]), the run count, and
+// the number of pieces of at most unit_entries entries the runs are cut into.
+__global__ __launch_bounds__(kBT) void k_unit_runs(SegTable seg, int32_t n_dom,
+                                                   const int32_t *__restrict__ local_map,
+                                                   const int32_t *__restrict__ abs_map,
+                                                   const int32_t *__restrict__ origin,
+                                                   const int32_t *__restrict__ n_home,
+                                                   int32_t unit_entries, int32_t *__restrict__ runs,
+                                                   int32_t *__restrict__ seg_runs,
+                                                   int32_t *__restrict__ seg_pieces)
+{
+    constexpr int kWaves = kBT / 64;
+    __shared__ int32_t wave_n[kWaves];
+    __shared__ int32_t carry;
+    const int32_t s = blockIdx.x, p = s / n_dom, D = s % n_dom;
+    const int32_t m0 = seg.row(p, kMapOff)[D], n = seg.row(p, kSendSize)[D];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    for (int32_t t0 = 0; t0 < n; t0 += kBT) {
+        const int32_t i = t0 + (int32_t)threadIdx.x;
+        bool brk = false;
+        if (i < n)
+            brk = i == 0 || unit_key(seg, p, D, m0, i, local_map, abs_map, origin, n_home) !=
+                                unit_key(seg, p, D, m0, i - 1, local_map, abs_map, origin, n_home);
+        const uint64_t b = __ballot(brk);
+        if (lane == 0) wave_n[w] = __popcll(b);
+        __syncthreads();
+        int32_t at = carry;
+        for (int k = 0; k < w; ++k) at += wave_n[k];
+        at += (int32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+        if (brk) runs[m0 + at] = i;  // at < n: one run start per entry at most
+        __syncthreads();
+        if (threadIdx.x == 0)
+            for (int k = 0; k < kWaves; ++k) carry += wave_n[k];
+        __syncthreads();
+    }
+    const int32_t n_runs = carry;
+    int32_t pieces = 0;
+    for (int32_t k = threadIdx.x; k < n_runs; k += kBT) {
+        const int32_t a = runs[m0 + k], e = k + 1 < n_runs ? runs[m0 + k + 1] : n;
+        pieces += (e - a + unit_entries - 1) / unit_entries;
+    }
+    __shared__ int32_t total;
+    if (threadIdx.x == 0) total = 0;
+    __syncthreads();
+    if (pieces) atomicAdd(&total, pieces);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        seg_runs[s] = n_runs;
+        seg_pieces[s] = total;
+    }
+}
+
+// One block: exclusive prefix of the segments' piece counts; the total at
+// out[n_seg].
+__global__ __launch_bounds__(kBT) void k_unit_scan(const int32_t *__restrict__ seg_pieces,
+                                                   int32_t n_seg, int32_t *__restrict__ out)
+{
+    constexpr int kWaves = kBT / 64;
+    __shared__ int32_t wave_sum[kWaves];
+    __shared__ int32_t carry;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    for (int32_t t0 = 0; t0 < n_seg; t0 += kBT) {
+        const int32_t i = t0 + (int32_t)threadIdx.x;
+        const int32_t v = i < n_seg ? seg_pieces[i] : 0;
+        int32_t x = v;  // inclusive scan within the wave
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t y = __shfl_up(x, d, 64);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) wave_sum[w] = x;
+        __syncthreads();
+        int32_t at = carry;
+        for (int k = 0; k < w; ++k) at += wave_sum[k];
+        if (i < n_seg) out[i] = at + x - v;
+        __syncthreads();
+        if (threadIdx.x == 0)
+            for (int k = 0; k < kWaves; ++k) carry += wave_sum[k];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[n_seg] = carry;
+}
+
+// Block = segment: its runs cut into near-equal pieces of at most
+// unit_entries entries, written from out[piece_off[s]] on (pieces at or past
+// `cap` are counted but not written).
+__global__ __launch_bounds__(kBT) void k_unit_write(SegTable seg, int32_t n_dom,
+                                                    const int32_t *__restrict__ local_map,
+                                                    const int32_t *__restrict__ abs_map,
+                                                    const int32_t *__restrict__ origin,
+                                                    const int32_t *__restrict__ n_home,
+                                                    int32_t unit_entries,
+                                                    const int32_t *__restrict__ runs,
+                                                    const int32_t *__restrict__ seg_runs,
+                                                    const int32_t *__restrict__ piece_off,
+                                                    int64_t cap, LocalRun *__restrict__ out)
+{
+    constexpr int kWaves = kBT / 64;
+    __shared__ int32_t wave_sum[kWaves];
+    __shared__ int32_t carry;
+    const int32_t s = blockIdx.x, p = s / n_dom, D = s % n_dom;
+    const int32_t m0 = seg.row(p, kMapOff)[D], n = seg.row(p, kSendSize)[D];
+    const int32_t n_runs = seg_runs[s];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    for (int32_t t0 = 0; t0 < n_runs; t0 += kBT) {
+        const int32_t k = t0 + (int32_t)threadIdx.x;
+        int32_t a = 0, len = 0, np_ = 0;
+        if (k < n_runs) {
+            a = runs[m0 + k];
+            len = (k + 1 < n_runs ? runs[m0 + k + 1] : n) - a;
+            np_ = (len + unit_entries - 1) / unit_entries;
+        }
+        int32_t x = np_;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t y = __shfl_up(x, d, 64);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) wave_sum[w] = x;
+        __syncthreads();
+        int32_t at = carry;
+        for (int c = 0; c < w; ++c) at += wave_sum[c];
+        at += x - np_;
+        if (np_ > 0) {
+            const int32_t key = unit_key(seg, p, D, m0, a, local_map, abs_map, origin, n_home);
+            for (int32_t j = 0; j < np_; ++j) {
+                const int64_t o = (int64_t)piece_off[s] + at + j;
+                if (o >= cap) break;
+                const int32_t e0 = a + (int32_t)((int64_t)len * j / np_);
+                const int32_t e1 = a + (int32_t)((int64_t)len * (j + 1) / np_);
+                out[o] = LocalRun{p, D, e0, e1 - e0, (key & 63) - 1, key >> 6,
+                                  abs_map[m0 + e0], abs_map[m0 + e1 - 1]};
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x == 0)
+            for (int c = 0; c < kWaves; ++c) carry += wave_sum[c];
+        __syncthreads();
+    }
+}
+
 unsigned grid_for(int64_t n, int per_block) { return (unsigned)((n + per_block - 1) / per_block); }
 
 constexpr size_t kAlign = 256;
@@ -662,6 +854,20 @@ hipError_t entries_reserve(DeviceBuild &B, size_t need)
 // sleep and take far longer to return than the GPU takes to finish short
 // work; the build waits often for little, so it records an event and polls
 // it instead.
+// Bytes of the tables copy: items; seg_items, send_to, recv_from, dest_start,
+// x_arrivals, zone_chunks; shift4; chunks; chunk order; launch members; the
+// XCD-local units, their wait lists and their flags.
+size_t tables_bytes(size_t n_items, size_t nseg, size_t npc, size_t n_lunits, size_t n_lwaits,
+                    size_t lflag_words)
+{
+    return aligned(std::max<size_t>(n_items, 1) * sizeof(WorkItem)) +
+           6 * aligned(std::max<size_t>(nseg, 1) * 4) + aligned(std::max<size_t>(nseg, 1) * 16) +
+           aligned(std::max<size_t>(npc, 1) * sizeof(Chunk)) +
+           aligned(std::max<size_t>(npc, 1) * 4) + aligned((size_t)kFamilies * kLaunchGroups * 4) +
+           aligned(std::max<size_t>(n_lunits, 1) * sizeof(LocalUnit)) +
+           aligned(std::max<size_t>(n_lwaits, 1) * 4) + aligned(std::max<size_t>(lflag_words, 1) * 8);
+}
+
 hipError_t wait_stream(DeviceBuild &B, hipStream_t st)
 {
     hipError_t e;
@@ -684,7 +890,8 @@ void free_device_build(halo_plan *pl)
 {
     if (!pl->dev) return;
     DeviceBuild &B = *pl->dev;
-    for (Arena *a : {&B.work, &B.entries, &B.maps, &B.pieces, &B.tables}) arena_free(*a);
+    for (Arena *a : {&B.work, &B.entries, &B.maps, &B.pieces, &B.tables, &B.units_more})
+        arena_free(*a);
     if (B.pinned) (void)hipHostFree(B.pinned);
     if (B.done) (void)hipEventDestroy(B.done);
     delete pl->dev;
@@ -699,6 +906,10 @@ void free_device_build(halo_plan *pl)
     pl->d_members = nullptr;
     pl->d_chunks = nullptr;
     pl->d_shift4 = nullptr;
+    pl->d_lunits = nullptr;
+    pl->d_lwaits = nullptr;
+    pl->d_lflags = nullptr;
+    pl->lflag_words = 0;
 }
 
 int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const float *box,
@@ -712,8 +923,7 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     HostPlan &P = pl->h;
     int rc = plan_geometry(n_atoms, box, grid, cutoff, selection, P, msg);
     if (rc != kOk) return rc;
-    // a device-built plan runs the index-list kernels with segment counters
-    // (no XCD-local units)
+    // the XCD-local units are made after the pulses
     P.has_local = false;
     P.local_k = 0;
     P.local_entries = 0;
@@ -934,23 +1144,27 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         P.slot_mask.clear();
     }
     P.chunk_slots = item_entries;
-    make_items(P, local_unit_entries(P.n_entries, item_entries), false);
+    const int32_t unit_entries = local_unit_entries(P.n_entries, item_entries);
+    make_items(P, unit_entries, false);
     const std::vector<Piece> pieces =
         P.has_chunks ? chunk_pieces(P, item_entries) : std::vector<Piece>();
     const size_t npc = pieces.size();
-    // host staging for the rest: base, pieces, their statistics, the tables
     const size_t n_items = P.items.size();
-    // items; seg_items, send_to, recv_from, dest_start, x_arrivals, zone_chunks;
-    // shift4; chunks; chunk order
-    const size_t tab_bytes = aligned(std::max<size_t>(n_items, 1) * sizeof(WorkItem)) +
-                             6 * aligned(std::max<size_t>(nseg, 1) * 4) +
-                             aligned(std::max<size_t>(nseg, 1) * 16) +
-                             aligned(std::max<size_t>(npc, 1) * sizeof(Chunk)) +
-                             aligned(std::max<size_t>(npc, 1) * 4) +
-                             aligned((size_t)kFamilies * kLaunchGroups * 4);
+    // host staging for the rest: base, pieces, their statistics, the pieces
+    // of the XCD-local units (their count, then at most lr_cap of them; a
+    // plan with more fetches them again), then the tables
+    const int64_t lr_cap = std::max<int64_t>(
+        1, std::min<int64_t>(entries, entries / unit_entries + 4 * (int64_t)nseg + 1024));
+    // the tables are staged from the buffer's start once the rest has been
+    // read: room for them too, with an estimate of the units' part (about
+    // one unit position per piece)
+    const size_t tab_est = tables_bytes(n_items, nseg, npc, (size_t)lr_cap, (size_t)lr_cap * 4,
+                                        2 * (size_t)kXcdClasses *
+                                            local_flag_stride((int32_t)(lr_cap / 8 + 1)));
     const size_t h_pieces = h_fixed, h_stats = h_pieces + aligned(std::max<size_t>(npc, 1) * 16),
-                 h_tables = h_stats + aligned(std::max<size_t>(npc, 1) * sizeof(PieceStats)),
-                 h_total = h_tables + tab_bytes;
+                 h_lruns = h_stats + aligned(std::max<size_t>(npc, 1) * sizeof(PieceStats)),
+                 h_total = std::max(h_lruns + aligned(16 + (size_t)lr_cap * sizeof(LocalRun)),
+                                    tab_est);
     if (h_total > B.pinned_cap) {
         HALO_TRY(wait_stream(B, st), "waiting for the stream");  // no copy from it in flight
         char *keep = (char *)std::malloc(h_fixed);
@@ -971,9 +1185,14 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
 
     // -- maps: absolute indexMap, home slots, pulse masks ------------------------------
     const size_t S = (size_t)P.total_slots;
+    // (then the XCD-local units' temporaries: slot origins, runs, pieces)
+    const size_t units_tmp = entries > 0 ? aligned(S * 4) + aligned((size_t)entries * 4) +
+                                               3 * aligned(nseg * 4 + 4) +
+                                               aligned((size_t)lr_cap * sizeof(LocalRun))
+                                         : 0;
     HALO_TRY(arena_reserve(B.maps, aligned(std::max<int64_t>(entries, 1) * 4) +
                                        aligned(std::max<size_t>(N, 1) * 8) +
-                                       (P.has_chunks ? aligned(S) : 0)),
+                                       (P.has_chunks ? aligned(S) : 0) + units_tmp),
              "device memory");
     int32_t *abs_map = arena_take<int32_t>(B.maps, (size_t)entries);
     int64_t *home_slot = arena_take<int64_t>(B.maps, N);
@@ -983,6 +1202,39 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         k_home_slot<<<grid_for(n_atoms, kBT), kBT, 0, st>>>(owner, home_rank, d_base, n_atoms,
                                                             home_slot);
     HALO_TRY(hipGetLastError(), "launch");
+    // XCD-local units: the origin of every slot, pulse by pulse; per segment
+    // the runs of one origin and zone and their pieces; the pieces come back
+    // with the chunk statistics
+    int32_t *u_origin = nullptr, *u_runs = nullptr, *u_seg_runs = nullptr, *u_piece_off = nullptr;
+    if (entries > 0) {
+        int32_t *origin = arena_take<int32_t>(B.maps, S);
+        int32_t *runs = arena_take<int32_t>(B.maps, (size_t)entries);
+        int32_t *seg_runs = arena_take<int32_t>(B.maps, nseg + 1);
+        int32_t *seg_pieces = arena_take<int32_t>(B.maps, nseg + 1);
+        int32_t *piece_off = arena_take<int32_t>(B.maps, nseg + 1);
+        LocalRun *lruns = arena_take<LocalRun>(B.maps, (size_t)lr_cap);
+        u_origin = origin;
+        u_runs = runs;
+        u_seg_runs = seg_runs;
+        u_piece_off = piece_off;
+        if (n_atoms > 0)
+            k_origin_home<<<grid_for(n_atoms, kBT), kBT, 0, st>>>(owner, home_slot, n_atoms,
+                                                                  origin);
+        for (int32_t p = 0; p < np; ++p)
+            k_origin_pulse<<<(unsigned)nd, kBT, 0, st>>>(sg, p, nd, w_send_to, d_base, abs_map,
+                                                         origin);
+        k_unit_runs<<<(unsigned)nseg, kBT, 0, st>>>(sg, nd, local_map, abs_map, origin, d_n_home,
+                                                    unit_entries, runs, seg_runs, seg_pieces);
+        k_unit_scan<<<1, kBT, 0, st>>>(seg_pieces, (int32_t)nseg, piece_off);
+        k_unit_write<<<(unsigned)nseg, kBT, 0, st>>>(sg, nd, local_map, abs_map, origin,
+                                                     d_n_home, unit_entries, runs, seg_runs,
+                                                     piece_off, lr_cap, lruns);
+        HALO_TRY(hipGetLastError(), "launch");
+        HALO_TRY(hipMemcpyAsync(hp + h_lruns, piece_off + nseg, 4, hipMemcpyDeviceToHost, st),
+                 "hipMemcpyAsync");
+        HALO_TRY(hipMemcpyAsync(hp + h_lruns + 16, lruns, (size_t)lr_cap * sizeof(LocalRun),
+                                hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
+    }
     std::vector<PieceStats> stats(npc);
     if (P.has_chunks) {
         HALO_TRY(hipMemsetAsync(mask, 0, S, st), "hipMemsetAsync");
@@ -1015,11 +1267,51 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         }
     }
 
+    if (entries > 0) {
+        if (!P.has_chunks) HALO_TRY(wait_stream(B, st), "waiting for the stream");
+        int32_t n_lr;
+        std::memcpy(&n_lr, hp + h_lruns, 4);
+        if (n_lr < 1 || n_lr > entries) {
+            msg = "halo_plan_create_device: internal error: unit count";
+            return kErrArg;
+        }
+        std::vector<LocalRun> lr((size_t)n_lr);
+        if (n_lr <= lr_cap) {
+            std::memcpy(lr.data(), hp + h_lruns + 16, (size_t)n_lr * sizeof(LocalRun));
+        } else {
+            // more pieces than the first copy held: write them again, all of
+            // them, into an arena of their own, and fetch them
+            HALO_TRY(arena_reserve(B.units_more, (size_t)n_lr * sizeof(LocalRun)),
+                     "device memory");
+            LocalRun *more = arena_take<LocalRun>(B.units_more, (size_t)n_lr);
+            k_unit_write<<<(unsigned)nseg, kBT, 0, st>>>(sg, nd, local_map, abs_map, u_origin,
+                                                         d_n_home, unit_entries, u_runs,
+                                                         u_seg_runs, u_piece_off, n_lr, more);
+            HALO_TRY(hipGetLastError(), "launch");
+            HALO_TRY(pinned_reserve(B, (size_t)n_lr * sizeof(LocalRun)), "pinned host memory");
+            hp = B.pinned;
+            HALO_TRY(hipMemcpyAsync(hp, more, (size_t)n_lr * sizeof(LocalRun),
+                                    hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
+            HALO_TRY(wait_stream(B, st), "waiting for the stream");
+            std::memcpy(lr.data(), hp, (size_t)n_lr * sizeof(LocalRun));
+        }
+        place_local_units(P, lr);
+    }
     make_launch_members(P);
 
-    // -- tables: items, segment tables, chunks; one copy ---------------------------------
+    // -- tables: items, segment tables, chunks, XCD-local units and their
+    // (cleared) flags; one copy -------------------------------------------------------
+    // items; seg_items, send_to, recv_from, dest_start, x_arrivals, zone_chunks;
+    // shift4; chunks; chunk order; launch members; units, wait lists, flags
+    const size_t n_lunits = P.lunits.size(), n_lwaits = P.lwaits.size();
+    const size_t lflag_words =
+        P.has_local ? 2 * (size_t)kXcdClasses * local_flag_stride(P.local_k) : 0;
+    const size_t tab_bytes = tables_bytes(n_items, nseg, npc, n_lunits, n_lwaits, lflag_words);
+    // nothing is in flight from the staging buffer here: it may be regrown
+    HALO_TRY(pinned_reserve(B, tab_bytes), "pinned host memory");
+    hp = B.pinned;
     HALO_TRY(arena_reserve(B.tables, tab_bytes), "device memory");
-    char *tp = hp + h_tables;
+    char *tp = hp;
     size_t off = 0;
     auto put = [&](const void *src, size_t bytes, size_t reserve_bytes) {
         if (bytes) std::memcpy(tp + off, src, bytes);
@@ -1047,6 +1339,16 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         shift4 = (float *)put(P.shift4.data(), nseg * 16, std::max<size_t>(nseg, 1) * 16);
         x_arrivals = (uint32_t *)put(P.x_arrivals.data(), nseg * 4, ns4);
         zone_chunks = (uint32_t *)put(P.zone_chunks.data(), nseg * 4, ns4);
+    }
+    LocalUnit *lunits = nullptr;
+    int32_t *lwaits = nullptr;
+    uint64_t *lflags = nullptr;
+    if (P.has_local) {
+        lunits = (LocalUnit *)put(P.lunits.data(), n_lunits * sizeof(LocalUnit),
+                                  n_lunits * sizeof(LocalUnit));
+        lwaits = (int32_t *)put(P.lwaits.data(), n_lwaits * 4, n_lwaits * 4);
+        std::memset(tp + off, 0, lflag_words * 8);
+        lflags = (uint64_t *)put(nullptr, 0, lflag_words * 8);
     }
     if (off > tab_bytes) {
         msg = "halo_plan_create_device: internal error: table layout";
@@ -1092,6 +1394,10 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     pl->d_x_arrivals = x_arrivals;
     pl->d_zone_chunks = zone_chunks;
     pl->d_members = members;
+    pl->d_lunits = lunits;
+    pl->d_lwaits = lwaits;
+    pl->d_lflags = lflags;
+    pl->lflag_words = lflag_words;
     pl->epochs.reset();
     pl->poisoned = false;
     pl->built_on_device = true;

@@ -25,9 +25,11 @@ struct DeviceBuild {
     Arena work;               // build temporaries
     Arena entries;            // local-slot indexMap and sent atom ids
     size_t entry_cap = 0;     // entries each array of `entries` holds
-    Arena maps;               // absolute indexMap, home slots, pulse masks
+    Arena maps;               // absolute indexMap, home slots, pulse masks; build
+                              // temporaries of the XCD-local units
     Arena pieces;             // chunk candidates and their statistics
-    Arena tables;             // work items, segment tables, chunks
+    Arena tables;             // work items, segment tables, chunks, XCD-local units
+    Arena units_more;         // XCD-local unit pieces, when more than the first copy held
     char *pinned = nullptr;   // host staging for the small copies
     size_t pinned_cap = 0;
     hipEvent_t done = nullptr;  // polled for the build's waits

@@ -222,9 +222,8 @@ int32_t halo_plan_num_chunks(const halo_plan *plan);  /* -1 on NULL */
 halo_status halo_plan_chunk(const halo_plan *plan, int32_t chunk, int32_t *domain, int32_t *zone,
                             int64_t *first, int32_t *count, uint32_t *mask);
 
-/* XCD-local units of the index-list kernels (plans built by
- * halo_plan_create; 0 for plans built on the device, whose index-list
- * kernels use the work items above). A unit is a run of one indexMap whose
+/* XCD-local units of the index-list kernels (both builds make the same
+ * units). A unit is a run of one indexMap whose
  * atoms share one home domain (their origin); it sits at a position of the
  * coordinate kernel's grid whose index mod 8 is its origin mod 8, so that all
  * units of an origin, and with them every dependency of both exchanges, run
@@ -276,8 +275,7 @@ halo_status halo_exchange_x(halo_plan *plan, float *x, void *stream);
  * of pulse p][i], with the per-slot order of additions of the serial
  * reverse-pulse loop, so results are bitwise deterministic. Runs the
  * transposed form (halo_exchange_f_transposed) for plans of at most 3 pulses
- * and at least 2^20 indexMap entries (plans built by halo_plan_create) or
- * 2^18 (plans built on the device), the index-list form
+ * and at least 2^20 indexMap entries, the index-list form
  * (halo_exchange_f_indexmap) for the others.
  *   f : device, total_slots*3 float32, updated in place. On return home slots
  *       hold the accumulated forces; forwarding halo slots hold partial sums.
@@ -289,21 +287,26 @@ halo_status halo_exchange_f(halo_plan *plan, float *f, void *stream);
  * forces); entries below depOffset go at once, the others after a wait on
  * the units that wrote the region stretch they read; forces added with one
  * read-modify-write per entry, after every later pulse that adds into the
- * same slots. On plans built by halo_plan_create the units are XCD-local
- * (halo_plan_local_unit): runs of one origin, placed so that each forwarding
- * stage stays in one XCD's L2, with per-unit flags; an exchange whose units
- * find their producers on another XCD reports HALO_ERR_PLACEMENT from
- * halo_plan_sync. On plans built on the device the units are the work items
- * (halo_plan_item_waits) with per-(pulse, sender) counters. */
+ * same slots. The units are XCD-local (halo_plan_local_unit): runs of one
+ * origin, placed so that each forwarding stage stays in one XCD's L2, with
+ * per-unit flags; an exchange whose units find their producers on another
+ * XCD reports HALO_ERR_PLACEMENT from halo_plan_sync. */
 halo_status halo_exchange_x_indexmap(halo_plan *plan, float *x, void *stream);
 halo_status halo_exchange_f_indexmap(halo_plan *plan, float *f, void *stream);
+
+/* The index-list form on the plan's work items (halo_plan_item_waits) with
+ * one completion counter per (pulse, sender) segment at the device-coherent
+ * level instead of the XCD-local units and their flags: the same results,
+ * kept as an ablation of the XCD-local placement. */
+halo_status halo_exchange_x_items(halo_plan *plan, float *x, void *stream);
+halo_status halo_exchange_f_items(halo_plan *plan, float *f, void *stream);
 
 /* Ablation of the coordinate store ("Redesigning GROMACS Halo Exchange",
  * s.4 on the coalescing of float3 coordinates into aligned stores): the
  * index-list coordinate exchange on XCD-local units with each unit's
  * contiguous run of destination slots staged in LDS and written as 16-byte
  * stores on 16-byte boundaries, instead of one 12-byte store per slot. Same
- * results. Plans built by halo_plan_create only (HALO_ERR_ARG otherwise). */
+ * results. */
 halo_status halo_exchange_x_indexmap_lds(halo_plan *plan, float *x, void *stream);
 
 /* Transposed form of the fused exchanges: the indexMaps stored as one pulse

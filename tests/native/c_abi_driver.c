@@ -175,13 +175,16 @@ static int run_case(const Case *c, uint64_t seed, hipStream_t stream)
               {halo_exchange_x_transposed, "x_transposed"},
               {halo_exchange_x_pulsewise, "x_pulsewise"},
               {halo_exchange_x_staged, "x_staged"},
-              {halo_exchange_x_direct, "x_direct"}},
+              {halo_exchange_x_direct, "x_direct"},
+              {halo_exchange_x_items, "x_items"},
+              {halo_exchange_x_indexmap_lds, "x_indexmap_lds"}},
       ff[] = {{halo_exchange_f, "f"},
               {halo_exchange_f_indexmap, "f_indexmap"},
               {halo_exchange_f_transposed, "f_transposed"},
               {halo_exchange_f_pulsewise, "f_pulsewise"},
               {halo_exchange_f_staged, "f_staged"},
-              {halo_exchange_f_atomic, "f_atomic"}};
+              {halo_exchange_f_atomic, "f_atomic"},
+              {halo_exchange_f_items, "f_items"}};
     halo_plan *plans[2] = {hp, dp};
     for (int k = 0; k < 2 && ok; ++k)
         for (size_t i = 0; i < sizeof(xf) / sizeof(xf[0]) && ok; ++i) {

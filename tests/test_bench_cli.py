@@ -30,5 +30,4 @@ def test_bench_names_the_kernels_the_library_defaults_run():
 
     assert const("kTransposedCoordMinEntries") == bench.TRANSPOSED_X_MIN_ENTRIES
     assert const("kTransposedForceMinEntries") == bench.TRANSPOSED_F_MIN_ENTRIES
-    assert const("kTransposedForceMinEntriesLocal") == bench.TRANSPOSED_F_MIN_ENTRIES_LOCAL
     assert const("kTransposedForceMaxPulses") == bench.TRANSPOSED_F_MAX_PULSES

@@ -54,7 +54,8 @@ def setup_case(oracle_mod, pos, box, grid, rc):
     return plan, o
 
 
-IMPLS = ["fused", "indexmap", "transposed", "pulsewise", "staged", "direct", "indexmap_lds"]
+IMPLS = ["fused", "indexmap", "transposed", "pulsewise", "staged", "direct", "indexmap_lds",
+         "items"]
 
 
 def exchange(plan, impl, direction, buf, stream=None):
@@ -63,13 +64,14 @@ def exchange(plan, impl, direction, buf, stream=None):
     if impl == "direct" and direction == "f":
         impl = "fused"  # the direct form exists for coordinates only
     if impl == "indexmap_lds" and (direction == "f" or len(plan.local_units()) == 0):
-        impl = "indexmap"  # coordinates only, on the XCD-local units of host-built plans
+        impl = "indexmap"  # coordinates only, on the XCD-local units
     name = {"fused": "exchange_{}", "indexmap": "exchange_{}_indexmap",
             "transposed": "exchange_{}_transposed",
             "pulsewise": "exchange_{}_pulsewise",
             "staged": "exchange_{}_staged",
             "direct": "exchange_{}_direct",
-            "indexmap_lds": "exchange_{}_indexmap_lds"}[impl].format(direction)
+            "indexmap_lds": "exchange_{}_indexmap_lds",
+            "items": "exchange_{}_items"}[impl].format(direction)
     getattr(plan, name)(buf, stream)
 
 
@@ -237,7 +239,7 @@ def test_independent_plans_on_concurrent_streams(torch, oracle_mod):
             assert_bitwise(f.cpu().numpy(), want_f, f"round {r} f")
 
 
-@pytest.mark.parametrize("impl", ["indexmap", "transposed"])
+@pytest.mark.parametrize("impl", ["indexmap", "transposed", "items"])
 def test_forced_timeout_poisons_and_reset_recovers(torch, oracle_mod, impl):
     """A withheld completion signal makes its dependents hit a tiny spin limit.
 
@@ -339,7 +341,7 @@ def test_capture_before_upload_is_refused(torch, oracle_mod):
     plan.upload()
 
 
-@pytest.mark.parametrize("form", ["fused", "indexmap", "transposed", "pulsewise"])
+@pytest.mark.parametrize("form", ["fused", "indexmap", "transposed", "pulsewise", "items"])
 @pytest.mark.parametrize("wid", [1, 2, 4, 5])
 def test_graph_replays_of_every_form(torch, oracle_mod, wid, form):
     """Both exchanges captured in one HIP graph, replayed three times, with

@@ -3,8 +3,8 @@
 A device-built plan must be the same plan: layout, home slots, every
 PulseData field (sendSize, recvSize, atomOffset, coordShift, indexMap,
 depOffset split) equal to the oracle's, the same work items with the same
-wait masks as the host-built plan, and exchanges bitwise equal to the
-oracle's.
+wait masks and the same XCD-local units (positions, runs, origins, wait
+counts) as the host-built plan, and exchanges bitwise equal to the oracle's.
 """
 import numpy as np
 import pytest
@@ -36,6 +36,7 @@ def check_same_plan(torch, oracle_mod, pos, box, grid, rc, tag, selection="slab"
         for d in range(o.n_dom):
             assert dp.pulse(p, d)["items"] == hp.pulse(p, d)["items"]
     np.testing.assert_array_equal(dp.item_waits(), hp.item_waits())
+    np.testing.assert_array_equal(dp.local_units(), hp.local_units())
     return dp, o
 
 
@@ -142,8 +143,9 @@ def test_rebuild_in_place(torch, oracle_mod):
         dp.rebuild_on_device(torch.from_numpy(pos).cuda(), box)
         o = oracle_mod.Oracle(pos, box, w.grid, w.cutoff)
         compare_plans(dp, o)
-        np.testing.assert_array_equal(dp.item_waits(), HaloPlan(pos, box, w.grid,
-                                                                 w.cutoff).item_waits())
+        hp = HaloPlan(pos, box, w.grid, w.cutoff)
+        np.testing.assert_array_equal(dp.item_waits(), hp.item_waits())
+        np.testing.assert_array_equal(dp.local_units(), hp.local_units())
         x0 = o.home_filled(np.nan)
         x = torch.from_numpy(x0.copy()).cuda()
         dp.exchange_x(x)

@@ -27,7 +27,7 @@ def test_stress_fused_forms(torch, oracle_mod, wid):
     want_fi = o.exchange_f(fi.copy())
     for seed in (1, 2, 3):
         plan.debug_stress(seed)
-        for impl in ("indexmap", "transposed"):
+        for impl in ("indexmap", "transposed", "items"):
             say(f"{w.name} stress seed {seed} {impl}")
             x = torch.from_numpy(x0.copy()).cuda()
             exchange(plan, impl, "x", x)
@@ -71,7 +71,7 @@ def test_stress_in_graph_replays(torch, oracle_mod, wid):
     s = torch.cuda.Stream()
     torch.cuda.synchronize()
     graphs = {}
-    for impl in ("indexmap", "transposed"):
+    for impl in ("indexmap", "transposed", "items"):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(s):
             g.capture_begin()
@@ -117,7 +117,7 @@ def test_rebuild_ends_stress_mode(torch, oracle_mod):
     x0 = o.home_filled(np.nan)
     base, n_home, n_halo = o.domains()
     f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, 42)
-    for impl in ("indexmap", "transposed"):
+    for impl in ("indexmap", "transposed", "items"):
         x = torch.from_numpy(x0.copy()).cuda()
         exchange(dp, impl, "x", x)
         f = torch.from_numpy(f0.copy()).cuda()

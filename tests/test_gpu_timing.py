@@ -18,8 +18,8 @@ from .test_gpu_parity import assert_bitwise, say, setup_case, torch  # noqa: F40
 pytestmark = pytest.mark.gpu
 
 FORMS = [("x", "exchange_x_indexmap"), ("x", "exchange_x_transposed"),
-         ("x", "exchange_x_direct"), ("f", "exchange_f_indexmap"),
-         ("f", "exchange_f_transposed"), ("f", "exchange_f_atomic")]
+         ("x", "exchange_x_direct"), ("x", "exchange_x_items"), ("f", "exchange_f_indexmap"),
+         ("f", "exchange_f_transposed"), ("f", "exchange_f_atomic"), ("f", "exchange_f_items")]
 
 
 @pytest.mark.parametrize("wid", [2, 4])
