@@ -619,52 +619,57 @@ void make_local_units(HostPlan &P, int32_t unit_entries)
     const int32_t nd = P.n_dom, np = P.n_pulse;
     unit_entries = std::max<int32_t>(unit_entries, 1);
 
-    // origin of every slot, pulse by pulse
+    // origin of every slot, pulse by pulse (the senders of one pulse write
+    // disjoint regions)
     std::vector<int32_t> origin((size_t)P.total_slots, -1);
-    for (int32_t D = 0; D < nd; ++D)
+    parallel_for(nd, [&](int32_t D) {
         for (int32_t l = 0; l < P.n_home[D]; ++l) origin[(size_t)(P.base[D] + l)] = D;
+    });
     for (int32_t p = 0; p < np; ++p)
-        for (int32_t D = 0; D < nd; ++D) {
+        parallel_for(nd, [&](int32_t D) {
             const Segment &g = P.at(p, D);
             const int64_t dst = P.base[g.send_to] + P.at(p, g.send_to).atom_offset;
             for (int32_t i = 0; i < g.send_size; ++i)
                 origin[(size_t)(dst + i)] = origin[(size_t)P.abs_map[(size_t)g.map_off + i]];
-        }
+        });
 
-    std::vector<LocalRun> raw;
-    auto zone_of = [&](int32_t D, int32_t l) {
-        if (l < P.n_home[D]) return -1;
-        for (int32_t q = 0; q < np; ++q) {
-            const Segment &r = P.at(q, D);
-            if (l >= r.atom_offset && l < r.atom_offset + r.recv_size) return q;
-        }
-        return np;  // not reached: every local slot is home or in a region
-    };
-    for (int32_t p = 0; p < np; ++p)
-        for (int32_t D = 0; D < nd; ++D) {
-            const Segment &g = P.at(p, D);
-            int32_t i = 0;
-            while (i < g.send_size) {
-                const int32_t l0 = P.local_map[(size_t)g.map_off + i];
-                const int32_t z = zone_of(D, l0);
-                const int32_t o = origin[(size_t)(P.base[D] + l0)];
-                int32_t j = i + 1;
-                while (j < g.send_size) {
-                    const int32_t l = P.local_map[(size_t)g.map_off + j];
-                    if (origin[(size_t)(P.base[D] + l)] != o || zone_of(D, l) != z) break;
-                    ++j;
-                }
-                const int32_t len = j - i, pieces = (len + unit_entries - 1) / unit_entries;
-                for (int32_t k = 0; k < pieces; ++k) {
-                    const int32_t a = i + (int32_t)((int64_t)len * k / pieces);
-                    const int32_t b = i + (int32_t)((int64_t)len * (k + 1) / pieces);
-                    raw.push_back(LocalRun{p, D, a, b - a, z, o,
-                                           P.abs_map[(size_t)g.map_off + a],
-                                           P.abs_map[(size_t)g.map_off + b - 1]});
-                }
-                i = j;
+    // per segment: runs of one origin and zone, cut into pieces
+    std::vector<std::vector<LocalRun>> per_seg((size_t)np * nd);
+    parallel_for(np * nd, [&](int32_t sg) {
+        const int32_t p = sg / nd, D = sg % nd;
+        const Segment &g = P.at(p, D);
+        auto zone_of = [&](int32_t l) {
+            if (l < P.n_home[D]) return -1;
+            for (int32_t q = 0; q < np; ++q) {
+                const Segment &r = P.at(q, D);
+                if (l >= r.atom_offset && l < r.atom_offset + r.recv_size) return q;
             }
+            return np;  // not reached: every local slot is home or in a region
+        };
+        std::vector<LocalRun> &out = per_seg[(size_t)sg];
+        int32_t i = 0;
+        while (i < g.send_size) {
+            const int32_t l0 = P.local_map[(size_t)g.map_off + i];
+            const int32_t z = zone_of(l0);
+            const int32_t o = origin[(size_t)(P.base[D] + l0)];
+            int32_t j = i + 1;
+            while (j < g.send_size) {
+                const int32_t l = P.local_map[(size_t)g.map_off + j];
+                if (origin[(size_t)(P.base[D] + l)] != o || zone_of(l) != z) break;
+                ++j;
+            }
+            const int32_t len = j - i, pieces = (len + unit_entries - 1) / unit_entries;
+            for (int32_t k = 0; k < pieces; ++k) {
+                const int32_t a = i + (int32_t)((int64_t)len * k / pieces);
+                const int32_t b = i + (int32_t)((int64_t)len * (k + 1) / pieces);
+                out.push_back(LocalRun{p, D, a, b - a, z, o, P.abs_map[(size_t)g.map_off + a],
+                                       P.abs_map[(size_t)g.map_off + b - 1]});
+            }
+            i = j;
         }
+    });
+    std::vector<LocalRun> raw;
+    for (const auto &v : per_seg) raw.insert(raw.end(), v.begin(), v.end());
     place_local_units(P, raw);
 }
 
