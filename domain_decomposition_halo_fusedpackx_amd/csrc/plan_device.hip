@@ -1153,8 +1153,13 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     // host staging for the rest: base, pieces, their statistics, the pieces
     // of the XCD-local units (their count, then at most lr_cap of them; a
     // plan with more fetches them again), then the tables
-    const int64_t lr_cap = std::max<int64_t>(
+    int64_t lr_cap = std::max<int64_t>(
         1, std::min<int64_t>(entries, entries / unit_entries + 4 * (int64_t)nseg + 1024));
+    if (const char *v = std::getenv("HALO_UNIT_PIECES_CAP")) {
+        // testing: a smaller first copy, so that the second fetch runs
+        const long c = std::strtol(v, nullptr, 10);
+        if (c >= 1) lr_cap = std::min<int64_t>(lr_cap, c);
+    }
     // the tables are staged from the buffer's start once the rest has been
     // read: room for them too, with an estimate of the units' part (about
     // one unit position per piece)

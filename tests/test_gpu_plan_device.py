@@ -71,27 +71,33 @@ def test_device_plan_edge_cases(torch, oracle_mod):
         check_same_plan(torch, oracle_mod, pos, box, grid, rc, name)
 
 
+def check_exchanges(torch, dp, o, seed, impl):
+    """Both exchanges of one form on a device-built plan, bitwise against the
+    oracle."""
+    x0 = o.home_filled(np.nan)
+    want_x = o.exchange_x(x0.copy())
+    base, n_home, n_halo = o.domains()
+    f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, seed)
+    want_f = o.exchange_f(f0.copy())
+    say(f"device plan, {impl}")
+    x = torch.from_numpy(x0.copy()).cuda()
+    exchange(dp, impl, "x", x)
+    f = torch.from_numpy(f0.copy()).cuda()
+    exchange(dp, impl, "f", f)
+    torch.cuda.synchronize()
+    dp.sync()
+    assert_bitwise(x.cpu().numpy(), want_x, f"{impl} x")
+    assert_bitwise(f.cpu().numpy(), want_f, f"{impl} f")
+
+
 @pytest.mark.parametrize("wid", [2, 4, 5])
 def test_exchanges_on_device_plans(torch, oracle_mod, wid):
     w = W.WORKLOADS[wid]
     pos = W.workload_positions(w)
     dp = device_plan(torch, pos, w.box, w.grid, w.cutoff)
     o = oracle_mod.Oracle(pos, w.box, w.grid, w.cutoff)
-    x0 = o.home_filled(np.nan)
-    want_x = o.exchange_x(x0.copy())
-    base, n_home, n_halo = o.domains()
-    f0 = W.halo_forces(o.total_slots, base, n_home, n_halo, w.seed)
-    want_f = o.exchange_f(f0.copy())
     for impl in IMPLS:
-        say(f"{w.name} device plan, {impl}")
-        x = torch.from_numpy(x0.copy()).cuda()
-        exchange(dp, impl, "x", x)
-        f = torch.from_numpy(f0.copy()).cuda()
-        exchange(dp, impl, "f", f)
-        torch.cuda.synchronize()
-        dp.sync()
-        assert_bitwise(x.cpu().numpy(), want_x, f"{impl} x")
-        assert_bitwise(f.cpu().numpy(), want_f, f"{impl} f")
+        check_exchanges(torch, dp, o, w.seed, impl)
 
 
 def test_repartition_sequence(torch, oracle_mod):
@@ -235,3 +241,26 @@ def test_rebuild_across_the_transposed_pulse_limit(torch, oracle_mod):
             torch.cuda.synchronize()
             dp.sync()
             assert_bitwise(f.cpu().numpy(), want, f"rebuild {i} f transposed")
+
+
+@pytest.mark.parametrize("cap", ["1", "37"])
+def test_device_units_fetched_again_when_the_first_copy_is_short(torch, oracle_mod, monkeypatch,
+                                                                 cap):
+    """The device build fetches the pieces of the XCD-local units in one copy
+    of a size estimated up front; when there are more, it writes them again,
+    all of them, and fetches them. Forced with a first copy of 1 or 37
+    pieces (HALO_UNIT_PIECES_CAP, read at the build): the units still equal
+    the host build's, and a rebuild and the exchanges are exact."""
+    monkeypatch.setenv("HALO_UNIT_PIECES_CAP", cap)
+    w = W.WORKLOADS[4]
+    pos = W.workload_positions(w)
+    dp, o = check_same_plan(torch, oracle_mod, pos, w.box, w.grid, w.cutoff, f"cap {cap}")
+    for impl in ("indexmap", "fused"):
+        check_exchanges(torch, dp, o, w.seed, impl)
+    pos2 = W.positions(w.box, 48_000, 41)
+    dp.rebuild_on_device(torch.from_numpy(pos2).cuda())
+    o2 = oracle_mod.Oracle(pos2, w.box, w.grid, w.cutoff)
+    compare_plans(dp, o2)
+    np.testing.assert_array_equal(dp.local_units(),
+                                  HaloPlan(pos2, w.box, w.grid, w.cutoff).local_units())
+    check_exchanges(torch, dp, o2, 41, "indexmap")
