@@ -794,13 +794,11 @@ halo_status halo_plan_upload(halo_plan *p)
 }
 
 // The fused defaults take, per direction, the form that measured fastest.
-// Coordinates: the transposed kernel from 2^20 entries up (the 8x8x8 box),
-// the index-list kernel below. Forces: the transposed kernel from 2^18
-// entries up for plans of at most 3 pulses (4x4x4 and 8x8x8 boxes); the
-// index-list kernel for smaller plans, which are latency-bound (on host-built
-// plans its XCD-local units keep each forwarding stage in one XCD's L2), and
-// for more pulses, each of which adds a dependent stage to the transposed
-// kernel's work units (the 4x4x8 box with its two z pulses).
+// Both directions: the transposed kernel from 2^20 entries up (the 8x8x8
+// box; forces only for plans of at most 3 pulses), the index-list kernel on
+// XCD-local units below, where the exchanges are latency-bound and the units
+// keep each forwarding stage in one XCD's L2, and for more pulses, each of
+// which adds a dependent stage to the transposed kernel's work units.
 constexpr int64_t kTransposedCoordMinEntries = 1 << 20;
 constexpr int64_t kTransposedForceMinEntries = 1 << 20;
 constexpr int32_t kTransposedForceMaxPulses = 3;

@@ -575,6 +575,18 @@ void make_items(HostPlan &P, int32_t item_entries, bool with_masks)
     P.pulse_item_off[P.n_pulse] = (int32_t)P.items.size();
 }
 
+// A unit's entries are one stage of the forwarding chain for that stretch:
+// smaller units start their dependants sooner and run fewer entries per
+// thread, larger ones cost fewer waits and workgroups. Measured over the five
+// workloads, about two units per compute unit is where the two balance (the
+// chip has 256 compute units).
+int32_t local_unit_entries(int64_t n_entries, int32_t item_entries)
+{
+    int32_t u = 1024;
+    while (u > 128 && (int64_t)u * 512 > n_entries) u /= 2;
+    return std::max<int32_t>(1, std::min(u, item_entries));
+}
+
 // XCD-local units. A unit is a run of consecutive entries of one indexMap
 // (pulse p, sender D) whose source slots lie in one zone of D (its home
 // slots or the region it received in one pulse) and hold atoms of one home
@@ -596,18 +608,6 @@ void make_items(HostPlan &P, int32_t item_entries, bool with_masks)
 // hold empty units. A unit then waits only for units of its own class at
 // smaller positions (coordinates) or larger positions (forces, launched in
 // reverse).
-// A unit's entries are one stage of the forwarding chain for that stretch:
-// smaller units start their dependants sooner and run fewer entries per
-// thread, larger ones cost fewer waits and workgroups. Measured over the five
-// workloads, about two units per compute unit is where the two balance (the
-// chip has 256 compute units).
-int32_t local_unit_entries(int64_t n_entries, int32_t item_entries)
-{
-    int32_t u = 1024;
-    while (u > 128 && (int64_t)u * 512 > n_entries) u /= 2;
-    return std::max<int32_t>(1, std::min(u, item_entries));
-}
-
 void make_local_units(HostPlan &P, int32_t unit_entries)
 {
     P.has_local = false;
