@@ -119,7 +119,11 @@ halo_status halo_plan_create_ex(const float *positions, int64_t n_atoms, const f
  * halo metadata at every domain-decomposition / neighbour-search step; see
  * "Redesigning GROMACS Halo Exchange", s.3 and Algorithms 1 and 4). The
  * result is identical to halo_plan_create on the same positions: layout,
- * home slots, every PulseData field and the exchanges' results.
+ * home slots, every PulseData field, the work items, the XCD-local units and
+ * the exchanges' results. (The units' pieces come back in one copy of an
+ * estimated size and, when there are more, in a second one; the environment
+ * variable HALO_UNIT_PIECES_CAP, read at the build, caps the first copy, for
+ * testing that path.)
  *   positions : DEVICE, n_atoms*3 float32 on the current device, read on
  *               `stream` (so work queued there before the call is seen)
  *   stream    : a hipStream_t; the call synchronises it a few times (it reads
