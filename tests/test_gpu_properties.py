@@ -1,6 +1,7 @@
 """Property-based parity on the GPU (hypothesis): over random systems (the
 strategy of tests/test_properties.py) the device-built plan equals the
-oracle's, and every exchange form on it is bitwise equal to the oracle."""
+oracle's, its XCD-local units equal the host build's, and every exchange form
+on it is bitwise equal to the oracle."""
 import numpy as np
 import pytest
 
@@ -8,6 +9,7 @@ pytest.importorskip("hypothesis")
 from hypothesis import HealthCheck, given, settings  # noqa: E402
 from hypothesis import strategies as st  # noqa: E402
 
+from domain_decomposition_halo_fusedpackx_amd import HaloPlan  # noqa: E402
 from domain_decomposition_halo_fusedpackx_amd import workloads as W  # noqa: E402
 
 from .test_gpu_parity import IMPLS, assert_bitwise, exchange, say, torch  # noqa: E402,F401
@@ -29,6 +31,8 @@ def test_random_systems_on_the_gpu(torch, oracle_mod, system, selection):
     o = oracle_mod.Oracle(pos, box, grid, rc, selection)
     dp = device_plan(torch, pos, box, grid, rc, selection)
     compare_plans(dp, o)
+    hp = HaloPlan(pos, box, grid, rc, selection=selection)
+    np.testing.assert_array_equal(dp.local_units(), hp.local_units())
     if o.total_slots == 0:
         return
     x0 = o.home_filled(np.nan)
