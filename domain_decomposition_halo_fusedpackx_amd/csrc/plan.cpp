@@ -681,37 +681,47 @@ void place_local_units(HostPlan &P, const std::vector<LocalRun> &raw)
     P.lunits.clear();
     P.lwaits.clear();
     const int32_t nd = P.n_dom, np = P.n_pulse;
-    // classes and positions
-    std::vector<std::vector<int32_t>> cls(kXcdClasses);
+    // the pieces by (sending domain, pulse), each bucket in piece order
+    const size_t n_raw = raw.size();
+    std::vector<int32_t> bucket_off((size_t)nd * np + 1, 0), by_bucket(n_raw);
+    for (const LocalRun &u : raw) ++bucket_off[(size_t)u.sender * np + u.pulse + 1];
+    for (size_t k = 0; k + 1 < bucket_off.size(); ++k) bucket_off[k + 1] += bucket_off[k];
+    {
+        std::vector<int32_t> fill(bucket_off.begin(), bucket_off.end() - 1);
+        for (int32_t r = 0; r < (int32_t)n_raw; ++r)
+            by_bucket[(size_t)fill[(size_t)raw[r].sender * np + raw[r].pulse]++] = r;
+    }
+    // classes and positions: pulse by pulse, roots first (forwarders first in
+    // the last pulse), pieces in order
+    std::vector<int32_t> pulse_off((size_t)np + 1, 0), by_pulse(n_raw);
+    for (const LocalRun &u : raw) ++pulse_off[(size_t)u.pulse + 1];
+    for (int32_t p = 0; p < np; ++p) pulse_off[(size_t)p + 1] += pulse_off[(size_t)p];
+    {
+        std::vector<int32_t> fill(pulse_off.begin(), pulse_off.end() - 1);
+        for (int32_t r = 0; r < (int32_t)n_raw; ++r) by_pulse[(size_t)fill[raw[r].pulse]++] = r;
+    }
+    std::vector<int32_t> cls_n(kXcdClasses, 0), pos_of(n_raw, -1);
     for (int32_t p = 0; p < np; ++p) {
         const bool last = p + 1 == np;
         for (int pass = 0; pass < 2; ++pass) {
             const bool roots = (pass == 0) != last;
-            for (int32_t r = 0; r < (int32_t)raw.size(); ++r)
-                if (raw[r].pulse == p && (raw[r].zone < 0) == roots)
-                    cls[raw[r].origin % kXcdClasses].push_back(r);
+            for (int32_t k = pulse_off[(size_t)p]; k < pulse_off[(size_t)p + 1]; ++k) {
+                const int32_t r = by_pulse[(size_t)k];
+                if ((raw[r].zone < 0) != roots) continue;
+                const int c = raw[r].origin % kXcdClasses;
+                pos_of[(size_t)r] = cls_n[c]++ * kXcdClasses + c;
+            }
         }
     }
-    size_t k_max = 0;
-    for (const auto &c : cls) k_max = std::max(k_max, c.size());
-    P.local_k = (int32_t)k_max;
-    P.lunits.assign(k_max * kXcdClasses, LocalUnit{});
-    std::vector<int32_t> pos_of(raw.size(), -1);
-    for (int c = 0; c < kXcdClasses; ++c)
-        for (size_t k = 0; k < cls[c].size(); ++k)
-            pos_of[(size_t)cls[c][k]] = (int32_t)(k * kXcdClasses + (size_t)c);
+    int32_t k_max = 0;
+    for (int c = 0; c < kXcdClasses; ++c) k_max = std::max(k_max, cls_n[c]);
+    P.local_k = k_max;
+    P.lunits.assign((size_t)k_max * kXcdClasses, LocalUnit{});
 
-    // units by sending domain (in piece order), for the wait lists
-    std::vector<int32_t> sender_off((size_t)nd + 1, 0), by_sender(raw.size());
-    for (const LocalRun &u : raw) ++sender_off[(size_t)u.sender + 1];
-    for (int32_t D = 0; D < nd; ++D) sender_off[(size_t)D + 1] += sender_off[(size_t)D];
-    {
-        std::vector<int32_t> fill(sender_off.begin(), sender_off.end() - 1);
-        for (int32_t r = 0; r < (int32_t)raw.size(); ++r) by_sender[(size_t)fill[raw[r].sender]++] = r;
-    }
-    auto senders = [&](int32_t D) {
-        return std::make_pair(by_sender.data() + sender_off[(size_t)D],
-                              by_sender.data() + sender_off[(size_t)D + 1]);
+    // the pieces of sender D and pulse p
+    auto bucket = [&](int32_t D, int32_t p) {
+        return std::make_pair(by_bucket.data() + bucket_off[(size_t)D * np + p],
+                              by_bucket.data() + bucket_off[(size_t)D * np + p + 1]);
     };
     P.lwaits.reserve(raw.size() * 4);
     for (int32_t r = 0; r < (int32_t)raw.size(); ++r) {
@@ -730,9 +740,9 @@ void place_local_units(HostPlan &P, const std::vector<LocalRun> &raw)
             const int32_t q = u.zone, Dq = P.recv_from[(size_t)q * nd + u.sender];
             const int64_t r0 = P.base[u.sender] + P.at(q, u.sender).atom_offset;
             const int64_t i_lo = u.src_lo - r0, i_hi = u.src_hi - r0;
-            for (auto [it, end] = senders(Dq); it != end; ++it) {
+            for (auto [it, end] = bucket(Dq, q); it != end; ++it) {
                 const LocalRun &w = raw[(size_t)*it];
-                if (w.pulse == q && w.e0 <= i_hi && w.e0 + w.n - 1 >= i_lo) {
+                if (w.e0 <= i_hi && w.e0 + w.n - 1 >= i_lo) {
                     P.lwaits.push_back(pos_of[(size_t)*it]);
                     P.lunits[(size_t)pos_of[(size_t)*it]].flags |= kLocalXWaited;
                 }
@@ -743,20 +753,22 @@ void place_local_units(HostPlan &P, const std::vector<LocalRun> &raw)
         // its own source slots
         L.wf_off = (int32_t)P.lwaits.size();
         const int64_t reg_lo = L.region_begin, reg_hi = reg_lo + u.n - 1;
-        for (auto [it, end] = senders(g.send_to); it != end; ++it) {
-            const LocalRun &w = raw[(size_t)*it];
-            if (w.pulse > u.pulse && w.src_lo <= reg_hi && w.src_hi >= reg_lo)
-                P.lwaits.push_back(pos_of[(size_t)*it]);
-        }
+        for (int32_t q = u.pulse + 1; q < np; ++q)
+            for (auto [it, end] = bucket(g.send_to, q); it != end; ++it) {
+                const LocalRun &w = raw[(size_t)*it];
+                if (w.src_lo <= reg_hi && w.src_hi >= reg_lo) P.lwaits.push_back(pos_of[(size_t)*it]);
+            }
         const size_t first_own = P.lwaits.size();
-        for (auto [it, end] = senders(u.sender); it != end; ++it) {
-            const LocalRun &w = raw[(size_t)*it];
-            if (w.pulse > u.pulse && w.src_lo <= u.src_hi && w.src_hi >= u.src_lo &&
-                (g.send_to != u.sender ||
-                 std::find(P.lwaits.begin() + L.wf_off, P.lwaits.begin() + (ptrdiff_t)first_own,
-                           pos_of[(size_t)*it]) == P.lwaits.begin() + (ptrdiff_t)first_own))
-                P.lwaits.push_back(pos_of[(size_t)*it]);
-        }
+        for (int32_t q = u.pulse + 1; q < np; ++q)
+            for (auto [it, end] = bucket(u.sender, q); it != end; ++it) {
+                const LocalRun &w = raw[(size_t)*it];
+                if (w.src_lo <= u.src_hi && w.src_hi >= u.src_lo &&
+                    (g.send_to != u.sender ||
+                     std::find(P.lwaits.begin() + L.wf_off,
+                               P.lwaits.begin() + (ptrdiff_t)first_own,
+                               pos_of[(size_t)*it]) == P.lwaits.begin() + (ptrdiff_t)first_own))
+                    P.lwaits.push_back(pos_of[(size_t)*it]);
+            }
         L.wf_n = (int32_t)P.lwaits.size() - L.wf_off;
         for (int32_t k = L.wf_off; k < L.wf_off + L.wf_n; ++k)
             P.lunits[(size_t)P.lwaits[(size_t)k]].flags |= kLocalFWaited;
