@@ -868,20 +868,33 @@ size_t tables_bytes(size_t n_items, size_t nseg, size_t npc, size_t n_lunits, si
            aligned(std::max<size_t>(n_lwaits, 1) * 4) + aligned(std::max<size_t>(lflag_words, 1) * 8);
 }
 
-hipError_t wait_stream(DeviceBuild &B, hipStream_t st)
+// Records ev (created on first use) at the stream's current end.
+hipError_t record_event(hipEvent_t &ev, hipStream_t st)
 {
-    hipError_t e;
-    if (!B.done) {
-        e = hipEventCreateWithFlags(&B.done, hipEventDisableTiming);
+    if (!ev) {
+        const hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
         if (e != hipSuccess) {
-            B.done = nullptr;
+            ev = nullptr;
             return e;
         }
     }
-    if ((e = hipEventRecord(B.done, st)) != hipSuccess) return e;
-    while ((e = hipEventQuery(B.done)) == hipErrorNotReady) {
+    return hipEventRecord(ev, st);
+}
+
+// Waits for a recorded event by polling it: the runtime's own wait could
+// sleep far longer than the GPU needs.
+hipError_t poll_event(hipEvent_t ev)
+{
+    hipError_t e;
+    while ((e = hipEventQuery(ev)) == hipErrorNotReady) {
     }
     return e;
+}
+
+hipError_t wait_stream(DeviceBuild &B, hipStream_t st)
+{
+    const hipError_t e = record_event(B.done, st);
+    return e != hipSuccess ? e : poll_event(B.done);
 }
 
 }  // namespace
@@ -894,6 +907,7 @@ void free_device_build(halo_plan *pl)
         arena_free(*a);
     if (B.pinned) (void)hipHostFree(B.pinned);
     if (B.done) (void)hipEventDestroy(B.done);
+    if (B.units_back) (void)hipEventDestroy(B.units_back);
     delete pl->dev;
     pl->dev = nullptr;
     // these pointed into the arenas
@@ -1145,11 +1159,13 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     }
     P.chunk_slots = item_entries;
     const int32_t unit_entries = local_unit_entries(P.n_entries, item_entries);
-    make_items(P, unit_entries, false);
     const std::vector<Piece> pieces =
         P.has_chunks ? chunk_pieces(P, item_entries) : std::vector<Piece>();
     const size_t npc = pieces.size();
-    const size_t n_items = P.items.size();
+    // the work items are cut while the GPU runs; until then, a bound on
+    // their count (a segment's two spans give at most ceil(n / U) items each,
+    // an empty segment one)
+    const size_t items_bound = (size_t)(entries / unit_entries) + 3 * nseg + 1;
     // host staging for the rest: base, pieces, their statistics, the pieces
     // of the XCD-local units (their count, then at most lr_cap of them; a
     // plan with more fetches them again), then the tables
@@ -1163,7 +1179,7 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     // the tables are staged from the buffer's start once the rest has been
     // read: room for them too, with an estimate of the units' part (about
     // one unit position per piece)
-    const size_t tab_est = tables_bytes(n_items, nseg, npc, (size_t)lr_cap, (size_t)lr_cap * 4,
+    const size_t tab_est = tables_bytes(items_bound, nseg, npc, (size_t)lr_cap, (size_t)lr_cap * 4,
                                         2 * (size_t)kXcdClasses *
                                             local_flag_stride((int32_t)(lr_cap / 8 + 1)));
     const size_t h_pieces = h_fixed, h_stats = h_pieces + aligned(std::max<size_t>(npc, 1) * 16),
@@ -1239,6 +1255,7 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
                  "hipMemcpyAsync");
         HALO_TRY(hipMemcpyAsync(hp + h_lruns + 16, lruns, (size_t)lr_cap * sizeof(LocalRun),
                                 hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
+        HALO_TRY(record_event(B.units_back, st), "hipEventRecord");
     }
     std::vector<PieceStats> stats(npc);
     if (P.has_chunks) {
@@ -1262,6 +1279,31 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
             HALO_TRY(hipMemcpyAsync(hp + h_stats, d_stats, npc * sizeof(PieceStats),
                                     hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
         }
+    }
+
+    // Host work while the GPU runs: the work items, then the XCD-local
+    // units, placed as soon as their pieces are back (unless the first copy
+    // was too short; the second fetch comes after the chunk statistics)
+    make_items(P, unit_entries, false);
+    const size_t n_items = P.items.size();
+    int32_t n_lr = 0;
+    bool units_placed = false;
+    if (entries > 0) {
+        HALO_TRY(poll_event(B.units_back), "waiting for the stream");
+        std::memcpy(&n_lr, hp + h_lruns, 4);
+        if (n_lr < 1 || n_lr > entries) {
+            (void)wait_stream(B, st);  // no copy into the staging buffer left in flight
+            msg = "halo_plan_create_device: internal error: unit count";
+            return kErrArg;
+        }
+        if (n_lr <= lr_cap) {
+            std::vector<LocalRun> lr((size_t)n_lr);
+            std::memcpy(lr.data(), hp + h_lruns + 16, (size_t)n_lr * sizeof(LocalRun));
+            place_local_units(P, lr);
+            units_placed = true;
+        }
+    }
+    if (P.has_chunks) {
         HALO_TRY(wait_stream(B, st), "waiting for the stream");
         std::memcpy(stats.data(), hp + h_stats, npc * sizeof(PieceStats));
         try {
@@ -1271,35 +1313,23 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
             return kErrArg;
         }
     }
-
-    if (entries > 0) {
-        if (!P.has_chunks) HALO_TRY(wait_stream(B, st), "waiting for the stream");
-        int32_t n_lr;
-        std::memcpy(&n_lr, hp + h_lruns, 4);
-        if (n_lr < 1 || n_lr > entries) {
-            msg = "halo_plan_create_device: internal error: unit count";
-            return kErrArg;
-        }
+    if (entries > 0 && !units_placed) {
+        // more pieces than the first copy held: write them again, all of
+        // them, into an arena of their own, and fetch them
         std::vector<LocalRun> lr((size_t)n_lr);
-        if (n_lr <= lr_cap) {
-            std::memcpy(lr.data(), hp + h_lruns + 16, (size_t)n_lr * sizeof(LocalRun));
-        } else {
-            // more pieces than the first copy held: write them again, all of
-            // them, into an arena of their own, and fetch them
-            HALO_TRY(arena_reserve(B.units_more, (size_t)n_lr * sizeof(LocalRun)),
-                     "device memory");
-            LocalRun *more = arena_take<LocalRun>(B.units_more, (size_t)n_lr);
-            k_unit_write<<<(unsigned)nseg, kBT, 0, st>>>(sg, nd, local_map, abs_map, u_origin,
-                                                         d_n_home, unit_entries, u_runs,
-                                                         u_seg_runs, u_piece_off, n_lr, more);
-            HALO_TRY(hipGetLastError(), "launch");
-            HALO_TRY(pinned_reserve(B, (size_t)n_lr * sizeof(LocalRun)), "pinned host memory");
-            hp = B.pinned;
-            HALO_TRY(hipMemcpyAsync(hp, more, (size_t)n_lr * sizeof(LocalRun),
-                                    hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
-            HALO_TRY(wait_stream(B, st), "waiting for the stream");
-            std::memcpy(lr.data(), hp, (size_t)n_lr * sizeof(LocalRun));
-        }
+        HALO_TRY(arena_reserve(B.units_more, (size_t)n_lr * sizeof(LocalRun)), "device memory");
+        LocalRun *more = arena_take<LocalRun>(B.units_more, (size_t)n_lr);
+        k_unit_write<<<(unsigned)nseg, kBT, 0, st>>>(sg, nd, local_map, abs_map, u_origin, d_n_home,
+                                                     unit_entries, u_runs, u_seg_runs, u_piece_off,
+                                                     n_lr, more);
+        HALO_TRY(hipGetLastError(), "launch");
+        // no copy into the staging buffer is in flight here: it may be regrown
+        HALO_TRY(pinned_reserve(B, (size_t)n_lr * sizeof(LocalRun)), "pinned host memory");
+        hp = B.pinned;
+        HALO_TRY(hipMemcpyAsync(hp, more, (size_t)n_lr * sizeof(LocalRun), hipMemcpyDeviceToHost,
+                                st), "hipMemcpyAsync");
+        HALO_TRY(wait_stream(B, st), "waiting for the stream");
+        std::memcpy(lr.data(), hp, (size_t)n_lr * sizeof(LocalRun));
         place_local_units(P, lr);
     }
     make_launch_members(P);

@@ -32,7 +32,8 @@ struct DeviceBuild {
     Arena units_more;         // XCD-local unit pieces, when more than the first copy held
     char *pinned = nullptr;   // host staging for the small copies
     size_t pinned_cap = 0;
-    hipEvent_t done = nullptr;  // polled for the build's waits
+    hipEvent_t done = nullptr;        // polled for the build's waits
+    hipEvent_t units_back = nullptr;  // the XCD-local units' pieces are on the host
 };
 
 }  // namespace halo
