@@ -22,14 +22,19 @@
 //   k_select<true>   the same selection writing the indexMap (local slots)
 //                    and the id of every sent atom, by stable compaction
 //   k_abs_map        indexMap entries as absolute slots
-//   k_home_slot      slot of every atom
+//   k_home_slot      slot of every atom, and the origin (home domain) of
+//                    every home slot
+//   k_origin_pulse   per pulse, the origins of the regions received
+//   k_unit_runs      per segment, the runs of entries whose sources share
+//   k_unit_scan        origin and zone, cut into pieces (the XCD-local
+//   k_unit_write       units' pieces), with their offsets
 //   k_mask           per-slot pulse masks of the transposed form
 //   k_item_masks     wait masks of the work items
 //   k_piece_stats    union mask and per-pulse counts of every chunk candidate
-// and the host keeps the O(domains x pulses + items + chunks) bookkeeping
-// that needs the sizes: the layout, the work items and the chunk order. The
-// host synchronises three times: after the pulses (sizes), after the chunk
-// statistics, and at the end.
+// and the host keeps the O(domains x pulses + items + chunks + units)
+// bookkeeping that needs the sizes: the layout, the work items, the chunk
+// order and the placement of the units. The host synchronises three times:
+// after the pulses (sizes), after the chunk statistics, and at the end.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -494,10 +499,16 @@ __global__ __launch_bounds__(kBT) void k_abs_map(const int32_t *__restrict__ loc
 __global__ __launch_bounds__(kBT) void k_home_slot(const int32_t *__restrict__ owner,
                                                    const int32_t *__restrict__ home_rank,
                                                    const int64_t *__restrict__ base,
-                                                   int64_t n_atoms, int64_t *__restrict__ slot)
+                                                   int64_t n_atoms, int64_t *__restrict__ slot,
+                                                   int32_t *__restrict__ origin)
 {
     const int64_t a = (int64_t)blockIdx.x * kBT + threadIdx.x;
-    if (a < n_atoms) slot[a] = base[owner[a]] + home_rank[a];
+    if (a < n_atoms) {
+        const int32_t D = owner[a];
+        const int64_t h = base[D] + home_rank[a];
+        slot[a] = h;
+        if (origin) origin[h] = D;  // the origin (home domain) of every home slot
+    }
 }
 
 // Bit p on the slots sent in pulse p (entries [e0, e1)). A slot appears at
@@ -572,24 +583,40 @@ __global__ __launch_bounds__(kBT) void k_piece_stats(const Piece *__restrict__ p
                                                      int32_t n_pulse,
                                                      PieceStats *__restrict__ stats)
 {
+    constexpr int kRows = 8;  // slots per thread and round (a piece holds at most 8 * kBT)
     __shared__ uint32_t um;
     __shared__ int32_t cnt[kMaxMaskPulses];
     if (threadIdx.x == 0) um = 0;
     if (threadIdx.x < kMaxMaskPulses) cnt[threadIdx.x] = 0;
     __syncthreads();
     const Piece pc = pieces[blockIdx.x];
+    // per wave: the union and the per-pulse counts, from ballots
     uint32_t u = 0;
     int32_t c[kMaxMaskPulses] = {0};
-    for (int32_t i = threadIdx.x; i < pc.count; i += kBT) {
-        const uint32_t m = mask[pc.first + i];
-        u |= m;
+    for (int32_t i0 = 0; i0 < pc.count; i0 += kRows * kBT) {
+        uint32_t m[kRows];
 #pragma unroll
-        for (int q = 0; q < kMaxMaskPulses; ++q) c[q] += (int32_t)((m >> q) & 1u);
+        for (int j = 0; j < kRows; ++j) {
+            const int32_t i = i0 + j * kBT + (int32_t)threadIdx.x;
+            m[j] = i < pc.count ? (uint32_t)mask[pc.first + i] : 0u;
+        }
+#pragma unroll
+        for (int q = 0; q < kMaxMaskPulses; ++q) {
+            if (q >= n_pulse) break;
+#pragma unroll
+            for (int j = 0; j < kRows; ++j) {
+                const uint64_t bq = __ballot((m[j] >> q) & 1u);
+                c[q] += __popcll(bq);
+                if (bq) u |= 1u << q;
+            }
+        }
     }
-    if (u) atomicOr(&um, u);
+    if ((threadIdx.x & 63) == 0) {
+        if (u) atomicOr(&um, u);
 #pragma unroll
-    for (int q = 0; q < kMaxMaskPulses; ++q)
-        if (q < n_pulse && c[q]) atomicAdd(&cnt[q], c[q]);
+        for (int q = 0; q < kMaxMaskPulses; ++q)
+            if (c[q]) atomicAdd(&cnt[q], c[q]);
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
         stats[blockIdx.x].mask = um;
@@ -598,15 +625,6 @@ __global__ __launch_bounds__(kBT) void k_piece_stats(const Piece *__restrict__ p
 }
 
 // ---- XCD-local units (plan.cpp, make_local_units, does the same on the host) ----
-
-// The origin (home domain of the atom) of every home slot.
-__global__ __launch_bounds__(kBT) void k_origin_home(const int32_t *__restrict__ owner,
-                                                     const int64_t *__restrict__ home_slot,
-                                                     int64_t n_atoms, int32_t *__restrict__ origin)
-{
-    const int64_t a = (int64_t)blockIdx.x * kBT + threadIdx.x;
-    if (a < n_atoms) origin[home_slot[a]] = owner[a];
-}
 
 // Block = sender D of pulse p: the origins of the receiver's region of pulse p
 // are those of the slots D sends (home slots or regions of earlier pulses,
@@ -1218,17 +1236,17 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     int32_t *abs_map = arena_take<int32_t>(B.maps, (size_t)entries);
     int64_t *home_slot = arena_take<int64_t>(B.maps, N);
     uint8_t *mask = P.has_chunks ? arena_take<uint8_t>(B.maps, S) : nullptr;
+    // XCD-local units: the origin of every slot (home slots with their slots,
+    // then pulse by pulse); per segment the runs of one origin and zone and
+    // their pieces; the pieces come back while the host works
+    int32_t *origin = entries > 0 ? arena_take<int32_t>(B.maps, S) : nullptr;
     if (nseg > 0) k_abs_map<<<(unsigned)nseg, kBT, 0, st>>>(local_map, sg, nd, d_base, abs_map);
     if (n_atoms > 0)
         k_home_slot<<<grid_for(n_atoms, kBT), kBT, 0, st>>>(owner, home_rank, d_base, n_atoms,
-                                                            home_slot);
+                                                            home_slot, origin);
     HALO_TRY(hipGetLastError(), "launch");
-    // XCD-local units: the origin of every slot, pulse by pulse; per segment
-    // the runs of one origin and zone and their pieces; the pieces come back
-    // with the chunk statistics
     int32_t *u_origin = nullptr, *u_runs = nullptr, *u_seg_runs = nullptr, *u_piece_off = nullptr;
     if (entries > 0) {
-        int32_t *origin = arena_take<int32_t>(B.maps, S);
         int32_t *runs = arena_take<int32_t>(B.maps, (size_t)entries);
         int32_t *seg_runs = arena_take<int32_t>(B.maps, nseg + 1);
         int32_t *seg_pieces = arena_take<int32_t>(B.maps, nseg + 1);
@@ -1238,9 +1256,6 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         u_runs = runs;
         u_seg_runs = seg_runs;
         u_piece_off = piece_off;
-        if (n_atoms > 0)
-            k_origin_home<<<grid_for(n_atoms, kBT), kBT, 0, st>>>(owner, home_slot, n_atoms,
-                                                                  origin);
         for (int32_t p = 0; p < np; ++p)
             k_origin_pulse<<<(unsigned)nd, kBT, 0, st>>>(sg, p, nd, w_send_to, d_base, abs_map,
                                                          origin);
