@@ -197,8 +197,9 @@ __device__ __forceinline__ uint32_t wave_sort_by_key(uint32_t v, int key_bits)
 }
 
 // Stable counting sort of the atoms by domain, carrying their coordinates
-// (one array per dimension, home order). Block = tile; LDS counters
-// start at the tile's offsets within each domain. In each round of 256 atoms
+// (x, y, z interleaved per home slot: one 12-byte store per atom, where
+// three scattered 4-byte stores cost twice the kernel's time). Block = tile;
+// LDS counters start at the tile's offsets within each domain. In each round of 256 atoms
 // a wave sorts its lanes by domain (stable), so that lanes with one domain
 // form a run in id order; the waves then add their run lengths to the
 // counters one after the other, so that lower ids get lower ranks.
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(kBT) void k_home_scatter(const int32_t *__restrict_
             const int32_t key = keys[j];
             const int64_t h = home_start[key] + (int64_t)r;
 #pragma unroll
-            for (int d = 0; d < 3; ++d) home_c[d * n_atoms + h] = pos[3 * a + d];
+            for (int d = 0; d < 3; ++d) home_c[3 * h + d] = pos[3 * a + d];
             home_rank[a] = (int32_t)r;
         }
     }
@@ -371,8 +372,9 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     const bool home_first = zfirst < 0;
     uint32_t count = 0;
     for (int32_t b = 0; b < total; b += kRows * NT) {
-        // candidate coordinates come from per-dimension arrays in slot order
-        // (home order, or the order the entries were sent in): contiguous
+        // candidate coordinates in slot order: the home slots' interleaved
+        // (x, y, z), the entries' one row per dimension (the order they were
+        // sent in); contiguous either way
         const float *src[kRows];
         int32_t slot[kRows];
         int64_t stride[kRows];
@@ -388,8 +390,8 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
                 while (i >= zbeg[z + 1]) ++z;
                 const int32_t e = i - zbeg[z];
                 const bool from_home = home_first && z == 0;
-                src[j] = (from_home ? home_c : entry_c) + zoff[z] + e;
-                stride[j] = from_home ? n_atoms : (int64_t)cap;
+                src[j] = from_home ? home_c + 3 * ((int64_t)zoff[z] + e) : entry_c + zoff[z] + e;
+                stride[j] = from_home ? 1 : (int64_t)cap;
                 slot[j] = zslot[z] + e;
             }
         }
@@ -1010,7 +1012,7 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
              "device memory");
     int32_t *owner = arena_take<int32_t>(B.work, N);
     int32_t *home_rank = arena_take<int32_t>(B.work, N);
-    float *home_c = arena_take<float>(B.work, 3 * N);  // home coordinates, per dimension
+    float *home_c = arena_take<float>(B.work, 3 * N);  // home coordinates, (x, y, z) per slot
     uint32_t *tile_hist = arena_take<uint32_t>(B.work, (size_t)nd * n_tiles);
     char *xfer = arena_take<char>(B.work, xfer_bytes);
     unsigned long long *bad = (unsigned long long *)xfer;
