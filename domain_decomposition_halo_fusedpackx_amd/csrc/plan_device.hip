@@ -310,7 +310,7 @@ __device__ __forceinline__ bool corner_test(const float *src, int64_t stride, in
 // home slots; WRITE == true: store the indexMap (local slots) and the sent
 // atoms' coordinates (entry_c, one row of `cap` per dimension) from map_off
 // on, in candidate order.
-constexpr int kSelectThreads = 1024;  // one block per domain: 16 waves
+constexpr int kSelectThreads = 512;  // one block per domain: 8 waves (1024 measured slower)
 
 template <bool WRITE>
 __global__ __launch_bounds__(kSelectThreads) void k_select(
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     int32_t *__restrict__ local_map, int32_t cap)
 {
     constexpr int NT = kSelectThreads;
-    constexpr int kRows = 4;  // rows of NT candidates whose loads go out together
+    constexpr int kRows = 1;  // rows of NT candidates per step (2, 4 or 8 measured slower)
     // The candidate zones in slot order ([home,] regions), laid end to end:
     // candidate i of the domain is entry i - zbeg[z] of zone z.
     __shared__ int32_t zbeg[kMaxPulses + 2], zslot[kMaxPulses + 1], zoff[kMaxPulses + 1],
@@ -677,17 +677,23 @@ __global__ __launch_bounds__(kBT) void k_unit_runs(SegTable seg, int32_t n_dom,
     constexpr int kWaves = kBT / 64;
     __shared__ int32_t wave_n[kWaves];
     __shared__ int32_t carry;
+    __shared__ int32_t keys[kBT + 1];  // keys[0]: the previous round's last key
     const int32_t s = blockIdx.x, p = s / n_dom, D = s % n_dom;
     const int32_t m0 = seg.row(p, kMapOff)[D], n = seg.row(p, kSendSize)[D];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (threadIdx.x == 0) carry = 0;
+    if (threadIdx.x == 0) {
+        carry = 0;
+        keys[0] = -1;  // no key is negative
+    }
     __syncthreads();
     for (int32_t t0 = 0; t0 < n; t0 += kBT) {
         const int32_t i = t0 + (int32_t)threadIdx.x;
-        bool brk = false;
-        if (i < n)
-            brk = i == 0 || unit_key(seg, p, D, m0, i, local_map, abs_map, origin, n_home) !=
-                                unit_key(seg, p, D, m0, i - 1, local_map, abs_map, origin, n_home);
+        // every entry's key once; a run starts where it differs from the one before
+        const int32_t key =
+            i < n ? unit_key(seg, p, D, m0, i, local_map, abs_map, origin, n_home) : -1;
+        keys[threadIdx.x + 1] = key;
+        __syncthreads();
+        const bool brk = i < n && key != keys[threadIdx.x];
         const uint64_t b = __ballot(brk);
         if (lane == 0) wave_n[w] = __popcll(b);
         __syncthreads();
@@ -697,8 +703,10 @@ __global__ __launch_bounds__(kBT) void k_unit_runs(SegTable seg, int32_t n_dom,
                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
         if (brk) runs[m0 + at] = i;  // at < n: one run start per entry at most
         __syncthreads();
-        if (threadIdx.x == 0)
+        if (threadIdx.x == 0) {
             for (int k = 0; k < kWaves; ++k) carry += wave_n[k];
+            keys[0] = keys[kBT];
+        }
         __syncthreads();
     }
     const int32_t n_runs = carry;
