@@ -21,9 +21,9 @@
 //   k_pulse_scan     the pulse's map offsets and the receivers' regions
 //   k_select<true>   the same selection writing the indexMap (local slots)
 //                    and the id of every sent atom, by stable compaction
-//   k_abs_map        indexMap entries as absolute slots
-//   k_home_slot      slot of every atom, and the origin (home domain) of
-//                    every home slot
+//   k_abs_map        indexMap entries as absolute slots; the origin (home
+//                    domain) of every home slot
+//   k_home_slot      slot of every atom
 //   k_origin_pulse   per pulse, the origins of the regions received
 //   k_unit_runs      per segment, the runs of entries whose sources share
 //   k_unit_scan        origin and zone, cut into pieces (the XCD-local
@@ -485,32 +485,32 @@ __global__ __launch_bounds__(kBT) void k_pulse_scan(SegTable seg, int32_t p, int
     if (threadIdx.x == 0) count[0] = base + (int32_t)carry;
 }
 
-// Block = segment (pulse-major): absolute slots of its indexMap entries.
+// Block = segment (pulse-major): absolute slots of its indexMap entries. The
+// blocks of pulse 0 also give the home slots of their domain its id as their
+// origin (home domain), when `origin` is not null.
 __global__ __launch_bounds__(kBT) void k_abs_map(const int32_t *__restrict__ local_map,
                                                  SegTable seg, int32_t n_dom,
                                                  const int64_t *__restrict__ base,
-                                                 int32_t *__restrict__ abs_map)
+                                                 int32_t *__restrict__ abs_map,
+                                                 const int32_t *__restrict__ n_home,
+                                                 int32_t *__restrict__ origin)
 {
     const int32_t s = blockIdx.x;
     const int32_t p = s / n_dom, D = s % n_dom;
     const int32_t m0 = seg.row(p, kMapOff)[D], n = seg.row(p, kSendSize)[D];
     const int64_t b = base[D];
     for (int32_t i = threadIdx.x; i < n; i += kBT) abs_map[m0 + i] = (int32_t)(b + local_map[m0 + i]);
+    if (origin && p == 0)
+        for (int32_t i = threadIdx.x; i < n_home[D]; i += kBT) origin[b + i] = D;
 }
 
 __global__ __launch_bounds__(kBT) void k_home_slot(const int32_t *__restrict__ owner,
                                                    const int32_t *__restrict__ home_rank,
                                                    const int64_t *__restrict__ base,
-                                                   int64_t n_atoms, int64_t *__restrict__ slot,
-                                                   int32_t *__restrict__ origin)
+                                                   int64_t n_atoms, int64_t *__restrict__ slot)
 {
     const int64_t a = (int64_t)blockIdx.x * kBT + threadIdx.x;
-    if (a < n_atoms) {
-        const int32_t D = owner[a];
-        const int64_t h = base[D] + home_rank[a];
-        slot[a] = h;
-        if (origin) origin[h] = D;  // the origin (home domain) of every home slot
-    }
+    if (a < n_atoms) slot[a] = base[owner[a]] + home_rank[a];
 }
 
 // Bit p on the slots sent in pulse p (entries [e0, e1)). A slot appears at
@@ -1246,14 +1246,16 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     int32_t *abs_map = arena_take<int32_t>(B.maps, (size_t)entries);
     int64_t *home_slot = arena_take<int64_t>(B.maps, N);
     uint8_t *mask = P.has_chunks ? arena_take<uint8_t>(B.maps, S) : nullptr;
-    // XCD-local units: the origin of every slot (home slots with their slots,
-    // then pulse by pulse); per segment the runs of one origin and zone and
-    // their pieces; the pieces come back while the host works
+    // XCD-local units: the origin of every slot (home slots with the absolute
+    // indexMap, then pulse by pulse); per segment the runs of one origin and
+    // zone and their pieces; the pieces come back while the host works
     int32_t *origin = entries > 0 ? arena_take<int32_t>(B.maps, S) : nullptr;
-    if (nseg > 0) k_abs_map<<<(unsigned)nseg, kBT, 0, st>>>(local_map, sg, nd, d_base, abs_map);
+    if (nseg > 0)
+        k_abs_map<<<(unsigned)nseg, kBT, 0, st>>>(local_map, sg, nd, d_base, abs_map, d_n_home,
+                                                  origin);
     if (n_atoms > 0)
         k_home_slot<<<grid_for(n_atoms, kBT), kBT, 0, st>>>(owner, home_rank, d_base, n_atoms,
-                                                            home_slot, origin);
+                                                            home_slot);
     HALO_TRY(hipGetLastError(), "launch");
     int32_t *u_origin = nullptr, *u_runs = nullptr, *u_seg_runs = nullptr, *u_piece_off = nullptr;
     if (entries > 0) {
