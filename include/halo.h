@@ -420,7 +420,8 @@ halo_status halo_plan_debug_withhold(halo_plan *plan, int32_t segment);
 
 /* Testing hook: with seed != 0 the fused kernels (index-list, transposed and
  * atomic forms) run every group of mutually independent work units (the
- * items of one pulse, the chunks of one zone) in reversed order, and every
+ * items of one pulse, the chunks of one zone, the XCD-local units of one class
+ * and one pulse) in reversed order, and every
  * unit first sleeps a pseudo-random while (up to about 100 us) derived from
  * the seed. Results must not change: this exposes missing waits or orderings.
  * seed = 0 (the default) turns it off. Synchronises the device when it
