@@ -38,10 +38,12 @@ BYTES_X = 28  # per entry: 4 B index + 12 B gathered source + 12 B store
 BYTES_F = 40  # per entry: 4 B index + 12 B region read + 12 B target read + 12 B target write
 MALL_BYTES = 256 << 20
 MAX_REPLICAS = 128
-# The device code of the exchange kernels (the traffic counters in profiles/
-# are valid while these files are unchanged).
+# The device code of the exchange kernels and the flags it is compiled with
+# (the traffic counters in profiles/ are valid while these files are
+# unchanged).
 KERNEL_SOURCES = ["domain_decomposition_halo_fusedpackx_amd/csrc/exchange_kernels.hpp",
-                  "domain_decomposition_halo_fusedpackx_amd/csrc/sync.hpp"]
+                  "domain_decomposition_halo_fusedpackx_amd/csrc/sync.hpp",
+                  "domain_decomposition_halo_fusedpackx_amd/build.py"]
 
 
 def log(msg):

@@ -4,7 +4,12 @@
 
 Host code (the plan builder) is compiled with g++; the kernels and the C-ABI
 with hipcc. Floating point: no FMA contraction, subnormals kept, and packed
-fp32 instructions disabled for the device code.
+fp32 instructions disabled for the device code. The first 16 dwords of every
+kernel's arguments are preloaded into SGPRs when a wave starts (gfx950
+kernel-argument preloading; the code object carries a compatible entry that
+loads them itself where the firmware does not): the transposed exchange
+kernels then start their work-unit loads without waiting for an argument load
+(the coordinate exchange on the 8x8x8 workload: 14.1 -> 13.8 us).
 """
 from __future__ import annotations
 
@@ -26,6 +31,7 @@ HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function",
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-Wall",
