@@ -603,6 +603,11 @@ __global__ __launch_bounds__(kThreads) void k_unpack_local(
     const uint32_t *__restrict__ members, uint32_t host_epoch, uint32_t spin_limit,
     uint32_t *err_word, int32_t withhold, Debug dbg)
 {
+    // Every scalar argument in SGPRs from the start: their loads go out
+    // together here instead of one by one on the way to the first wait
+    // (0.2-0.3 us per exchange on the 4x4x4 and 4x4x8 workloads).
+    asm volatile("" ::"s"(groups), "s"(members), "s"(host_epoch), "s"(spin_limit), "s"(err_word),
+                 "s"(withhold), "s"(dbg.seed), "s"(dbg.stamps), "s"(flags), "s"(kp), "s"(waits));
     const int32_t b = dbg.order ? dbg.order[blockIdx.x] : n_units - 1 - (int32_t)blockIdx.x;
     stamp_start(dbg, (uint32_t)b);
     const halo::LocalUnit *un = units + b;
