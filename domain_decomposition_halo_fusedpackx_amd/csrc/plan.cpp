@@ -386,12 +386,21 @@ int build_plan(const float *pos, int64_t n_atoms, const float *box, const int32_
 // The members of each launch-count group: exactly the units for which the
 // kernel of the family executes a wait (the conditions below mirror the
 // kernels').
+static inline void add_member(HostPlan &P, int family, size_t unit)
+{
+    P.launch_members[(size_t)family * kLaunchGroups + unit % kLaunchGroups] += 1u;
+}
+
 void make_launch_members(HostPlan &P)
 {
+    launch_members_items_units(P);
+    launch_members_chunks(P);
+}
+
+void launch_members_items_units(HostPlan &P)
+{
     P.launch_members.assign((size_t)kFamilies * kLaunchGroups, 0u);
-    auto add = [&](int family, size_t unit) {
-        P.launch_members[(size_t)family * kLaunchGroups + unit % kLaunchGroups] += 1u;
-    };
+    auto add = [&](int family, size_t unit) { add_member(P, family, unit); };
     for (size_t u = 0; u < P.items.size(); ++u) {
         const WorkItem &it = P.items[u];
         if (it.n_total > it.n_indep) add(kFamItemsX, u);
@@ -406,7 +415,12 @@ void make_launch_members(HostPlan &P)
         if (un.wx_n > 0 || (un.flags & kLocalXWaited)) add(kFamLocalX, b);
         if (un.wf_n > 0 || (un.flags & kLocalFWaited)) add(kFamLocalF, b);
     }
+}
+
+void launch_members_chunks(HostPlan &P)
+{
     if (!P.has_chunks) return;
+    auto add = [&](int family, size_t unit) { add_member(P, family, unit); };
     for (size_t u = 0; u < P.chunks.size(); ++u) {
         const Chunk &c = P.chunks[u];
         if (c.zone >= 0) add(kFamChunksX, u);
@@ -824,11 +838,15 @@ void finish_chunks(HostPlan &P, int32_t chunk_slots, const std::vector<Piece> &p
         }
     // Pieces come per domain in slot order (home, then the region of each
     // pulse); a chunk's rank[q] counts the bit-q slots of its domain before it.
-    // Kept chunks are then placed zone-major (stable within a zone).
-    thread_local std::vector<Chunk> kept;
-    kept.clear();
-    kept.reserve(pieces.size());
-    std::vector<int32_t> zone_count(np + 2, 0);
+    // Kept chunks are placed zone-major (stable within a zone): a first pass
+    // counts them per zone, the second writes each at its place.
+    // zone_first[z + 1] = first chunk of zone z (z = -1 .. np-1)
+    std::vector<int32_t> zone_first(np + 2, 0);
+    for (size_t i = 0; i < pieces.size(); ++i)
+        if (stats[i].mask != 0) ++zone_first[pieces[i].zone + 2];
+    for (int32_t z = 0; z <= np; ++z) zone_first[z + 1] += zone_first[z];
+    P.chunks.resize((size_t)zone_first[np + 1]);
+    std::vector<int32_t> fill(zone_first.begin(), zone_first.end() - 1);
     int32_t rank[kMaxMaskPulses] = {0};
     int32_t cur = -1;
     for (size_t i = 0; i < pieces.size(); ++i) {
@@ -843,39 +861,31 @@ void finish_chunks(HostPlan &P, int32_t chunk_slots, const std::vector<Piece> &p
         }
         const uint32_t m = stats[i].mask;
         if (m != 0) {  // else nothing to send from or add into
-            Chunk c{};
+            Chunk &c = P.chunks[(size_t)fill[pc.zone + 1]++];
             c.first = pc.first;
             c.count = pc.count;
             c.domain = pc.domain;
             c.zone = pc.zone;
             c.mask = m;
-            for (int32_t q = 0; q < kMaxMaskPulses; ++q) c.rank[q] = rank[q];
             c.xwait = pc.zone < 0 ? -1 : pc.zone * nd + P.at(pc.zone, pc.domain).recv_from;
             c.top_sends = np > 0 ? stats[i].count[np - 1] : 0;
-            kept.push_back(c);
-            zone_count[pc.zone + 2] += 1;
+            c.pad = 0;
+            for (int32_t q = 0; q < kMaxMaskPulses; ++q) c.rank[q] = rank[q];
+            for (int32_t q = 0; q < np; ++q)
+                if ((m >> q) & 1u) P.x_arrivals[(size_t)q * nd + pc.domain] += 1;
+            if (pc.zone >= 0) P.zone_chunks[(size_t)pc.zone * nd + pc.domain] += 1;
         }
         for (int32_t q = 0; q < np; ++q) rank[q] += stats[i].count[q];
     }
     if (cur >= 0)
         for (int32_t q = 0; q < np; ++q)
             if (rank[q] != P.at(q, cur).send_size) throw std::logic_error("mask ranks disagree");
-    // zone_count[z + 1] = first chunk of zone z (z = -1 .. np-1)
-    for (int32_t z = 0; z <= np; ++z) zone_count[z + 1] += zone_count[z];
-    P.chunks.resize(kept.size());
-    std::vector<int32_t> fill(zone_count.begin(), zone_count.end() - 1);
-    for (const Chunk &c : kept) {
-        P.chunks[fill[c.zone + 1]++] = c;
-        for (int32_t q = 0; q < np; ++q)
-            if ((c.mask >> q) & 1u) P.x_arrivals[(size_t)q * nd + c.domain] += 1;
-        if (c.zone >= 0) P.zone_chunks[(size_t)c.zone * nd + c.domain] += 1;
-    }
     // Force direction: regions of later pulses first (their sums feed earlier
     // pulses), home slots last.
     P.chunk_forder.clear();
-    P.chunk_forder.reserve(kept.size());
+    P.chunk_forder.reserve(P.chunks.size());
     for (int32_t z = np; z >= 0; --z)
-        for (int32_t i = zone_count[z]; i < zone_count[z + 1]; ++i) P.chunk_forder.push_back(i);
+        for (int32_t i = zone_first[z]; i < zone_first[z + 1]; ++i) P.chunk_forder.push_back(i);
 }
 
 void make_chunks(HostPlan &P, int32_t chunk_slots)

@@ -199,8 +199,12 @@ enum : int {
     kFamilies = 7
 };
 
-// Fill plan.launch_members from the items and chunks.
+// Fill plan.launch_members from the items, the XCD-local units and the
+// chunks; the two halves may also run apart (the first zeroes the counts),
+// once the items and units exist and once the chunks do.
 void make_launch_members(HostPlan &plan);
+void launch_members_items_units(HostPlan &plan);
+void launch_members_chunks(HostPlan &plan);
 
 // Whether make_items places the items of one domain on one XCD.
 bool xcd_ordering_enabled();

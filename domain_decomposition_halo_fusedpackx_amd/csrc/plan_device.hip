@@ -1336,6 +1336,8 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
             units_placed = true;
         }
     }
+    // the launch-count members of the items and units, still before the wait
+    if (units_placed || entries == 0) launch_members_items_units(P);
     if (P.has_chunks) {
         HALO_TRY(wait_stream(B, st), "waiting for the stream");
         std::memcpy(stats.data(), hp + h_stats, npc * sizeof(PieceStats));
@@ -1364,8 +1366,9 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
         HALO_TRY(wait_stream(B, st), "waiting for the stream");
         std::memcpy(lr.data(), hp, (size_t)n_lr * sizeof(LocalRun));
         place_local_units(P, lr);
+        launch_members_items_units(P);
     }
-    make_launch_members(P);
+    launch_members_chunks(P);
 
     // -- tables: items, segment tables, chunks, XCD-local units and their
     // (cleared) flags; one copy -------------------------------------------------------
