@@ -938,6 +938,7 @@ void free_device_build(halo_plan *pl)
     if (B.pinned) (void)hipHostFree(B.pinned);
     if (B.done) (void)hipEventDestroy(B.done);
     if (B.units_back) (void)hipEventDestroy(B.units_back);
+    if (B.stats_back) (void)hipEventDestroy(B.stats_back);
     delete pl->dev;
     pl->dev = nullptr;
     // these pointed into the arenas
@@ -1311,6 +1312,9 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
             HALO_TRY(hipGetLastError(), "launch");
             HALO_TRY(hipMemcpyAsync(hp + h_stats, d_stats, npc * sizeof(PieceStats),
                                     hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
+            // the last work queued before the host's wait: recorded now, so
+            // that a wait on a stream that has long finished costs no new marker
+            HALO_TRY(record_event(B.stats_back, st), "hipEventRecord");
         }
     }
 
@@ -1339,7 +1343,7 @@ int build_plan_device(halo_plan *pl, const float *pos, int64_t n_atoms, const fl
     // the launch-count members of the items and units, still before the wait
     if (units_placed || entries == 0) launch_members_items_units(P);
     if (P.has_chunks) {
-        HALO_TRY(wait_stream(B, st), "waiting for the stream");
+        HALO_TRY(npc > 0 ? poll_event(B.stats_back) : wait_stream(B, st), "waiting for the stream");
         std::memcpy(stats.data(), hp + h_stats, npc * sizeof(PieceStats));
         try {
             finish_chunks(P, item_entries, pieces, stats);

@@ -34,6 +34,7 @@ struct DeviceBuild {
     size_t pinned_cap = 0;
     hipEvent_t done = nullptr;        // polled for the build's waits
     hipEvent_t units_back = nullptr;  // the XCD-local units' pieces are on the host
+    hipEvent_t stats_back = nullptr;  // the chunk statistics are on the host
 };
 
 }  // namespace halo
